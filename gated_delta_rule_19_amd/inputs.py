@@ -1,0 +1,107 @@
+"""Seeded synthetic inputs for the GDN-2 token mixer (shared by tests, bench, smoke).
+
+This module holds only random-number generation and shape bookkeeping; none
+of the token mixer's arithmetic lives here, so both the GPU path and the CPU
+oracle can consume what it draws.
+
+Recipe (per workload; draw order q, k, v, alpha-logits, b-logits, w-logits, S0):
+  q, k ~ N(0, 1), each (batch, token, head) row L2-normalised along d_k in fp32
+         (the layer normalises q and k before the core -- burn-gdn2 README,
+         "Architecture" diagram -- so the core receives unit-norm rows), then
+         rounded to the I/O dtype (RNE);
+  v    ~ N(0, 1) rounded to the I/O dtype;
+  alpha = sigmoid(N(alpha_mu, 1)) per key channel, fp32;
+  b     = b_scale * sigmoid(N(0, 1)) per key channel, fp32 (b_scale = 2 is the
+          README's negative-eigenvalue option, "b x 2");
+  w     = sigmoid(N(0, 1)) per value channel, fp32;
+  S0    = N(0, s0_std) fp32 when s0_std is given, else no initial state.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    T: int
+    H: int
+    dk: int
+    dv: int
+    io_dtype: torch.dtype
+    alpha_mu: float = 3.0
+    b_scale: float = 1.0
+    s0_std: Optional[float] = None
+    mode: str = "chunk"          # "chunk" | "recurrent" | "decode"
+    note: str = field(default="", compare=False)
+
+    @property
+    def head_tokens(self) -> int:
+        return self.B * self.T * self.H
+
+
+# The five synthetic workloads the path is built and measured on.
+WORKLOADS = {
+    0: Workload("tiny-fp32", 1, 64, 2, 16, 16, torch.float32, mode="both",
+                note="oracle-size check of both modes, fp32 I/O"),
+    1: Workload("chunk-B4-H16-T2048-d128", 4, 2048, 16, 128, 128, torch.bfloat16,
+                note="chunked forward at a 1.3B-layer shape (hidden 2048)"),
+    2: Workload("decode-B256-H16-d128", 256, 1, 16, 128, 128, torch.bfloat16,
+                s0_std=0.05, mode="decode",
+                note="one fused recurrent decode step, fp32 state updated in place"),
+    3: Workload("chunk-B1-H16-T65536-d128", 1, 65536, 16, 128, 128, torch.bfloat16,
+                alpha_mu=4.0, note="long-context chunked forward, slow decay"),
+    4: Workload("chunk-B8-H16-T4096-dk128-dv256", 8, 4096, 16, 128, 256, torch.bfloat16,
+                b_scale=2.0, s0_std=0.05,
+                note="expanded values, b in (0,2), nonzero initial state"),
+}
+
+
+def make(wl: Workload, seed: int, device="cpu", B=None, T=None, H=None):
+    """Draw one input set for ``wl`` (optionally overriding B/T/H).
+
+    Returns a dict with q, k, v (io dtype), alpha, b, w (fp32), S0 (fp32 or None).
+    """
+    B = wl.B if B is None else B
+    T = wl.T if T is None else T
+    H = wl.H if H is None else H
+    return make_raw(B, T, H, wl.dk, wl.dv, wl.io_dtype, seed, device,
+                    alpha_mu=wl.alpha_mu, b_scale=wl.b_scale, s0_std=wl.s0_std)
+
+
+def make_raw(B, T, H, dk, dv, io_dtype, seed, device="cpu", alpha_mu=3.0,
+             b_scale=1.0, s0_std=None):
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(int(seed))
+    f32 = torch.float32
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=g, device=dev, dtype=f32)
+
+    def unit_rows(x):
+        n = torch.linalg.vector_norm(x, dim=-1, keepdim=True)
+        return x / torch.clamp(n, min=1e-30)
+
+    q = unit_rows(randn(B, T, H, dk)).to(io_dtype)
+    k = unit_rows(randn(B, T, H, dk)).to(io_dtype)
+    v = randn(B, T, H, dv).to(io_dtype)
+    alpha = torch.sigmoid(randn(B, T, H, dk) + alpha_mu)
+    b = b_scale * torch.sigmoid(randn(B, T, H, dk))
+    w = torch.sigmoid(randn(B, T, H, dv))
+    S0 = None
+    if s0_std is not None:
+        S0 = randn(B, H, dk, dv) * s0_std
+    return dict(q=q, k=k, v=v, alpha=alpha, b=b, w=w, S0=S0)
+
+
+def to_numpy_f32(inp):
+    """Exact float32 widening of every tensor (bf16 -> fp32 is exact), on the host."""
+    out = {}
+    for key, x in inp.items():
+        out[key] = None if x is None else x.detach().to("cpu", torch.float32).numpy()
+    return out

@@ -1,0 +1,7 @@
+"""fp64 CPU oracle of the Gated DeltaNet-2 token mixer.
+
+TEST INFRASTRUCTURE: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it.  The GPU library and its
+Python binding never import it.
+"""
+from .reference import recurrent, chunked_wy, rel_l2  # noqa: F401

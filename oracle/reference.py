@@ -1,0 +1,153 @@
+"""fp64 CPU oracle for the Gated DeltaNet-2 token mixer (TEST INFRASTRUCTURE ONLY).
+
+Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The GPU library never calls it and
+shares no code with it.
+
+What is computed
+----------------
+The per-head recurrence on a matrix state S of shape (d_k, d_v), as written in
+the burn-gdn2 0.1.9 README (docs.rs), section "Architecture" (the per-token
+recurrence block):
+
+    S_t = (I - k_t (b_t * k_t)^T) diag(alpha_t) S_{t-1} + k_t (w_t * v_t)^T
+    o_t = q_t^T S_t
+
+alpha (decay) and b (erase gate) act per key channel, w (write gate) per value
+channel; the Gated DeltaNet-2 explainer (asapai.co.kr), section on splitting
+the single gate into two knobs, describes the same three per-channel gates.
+
+Readings taken where the page leaves a step open (each also listed in the
+design notes of the repository):
+  * the output reads the state *after* this token's update (S_t);
+  * the decay is applied first, the erase reads the decayed state;
+  * the erase subtracts along k and reads with b*k (literal order of the
+    product k (b*k)^T);
+  * no 1/sqrt(d_k) query scale, no normalisation inside the core;
+  * a missing initial state means S_0 = 0 (the README's quick start starts
+    inference from an empty state).
+
+Layouts (all row-major / C-contiguous):
+  q, k, alpha, b : [B, T, H, d_k]
+  v, w           : [B, T, H, d_v]
+  S0, S          : [B, H, d_k, d_v]
+  o              : [B, T, H, d_v]
+
+Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
+hand-worked examples (``tests/golden``), the special cases the pages name
+(KDA, Gated DeltaNet, plain linear attention), exact-recall and
+Householder invariants, and against each other.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["recurrent", "chunked_wy", "rel_l2"]
+
+
+def _f64(x):
+    return None if x is None else np.asarray(x, dtype=np.float64)
+
+
+def recurrent(q, k, v, alpha, b, w, S0=None):
+    """Sequential fp64 recurrence, literal order of the README's formula.
+
+    burn-gdn2 README, "Architecture": per token, the state is decayed on the
+    key axis (diag(alpha_t)), multiplied by the erase matrix
+    E_t = I - k_t (b_t*k_t)^T, and receives the write k_t (w_t*v_t)^T; the
+    output is q_t^T applied to the updated state.
+
+    The erase matrix is formed explicitly (a d_k x d_k matrix per head and
+    token) so that the code reads as the formula; this is O(d_k^2 d_v) per
+    token and meant for small shapes.  Returns (o, S_T) in fp64.
+    """
+    q, k, v, alpha, b, w = map(_f64, (q, k, v, alpha, b, w))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    S = np.zeros((B, H, dk, dv)) if S0 is None else _f64(S0).copy()
+    o = np.zeros((B, T, H, dv))
+    eye = np.eye(dk)
+    for t in range(T):
+        kt = k[:, t]                                   # [B,H,dk]
+        E = eye - kt[..., :, None] * (b[:, t] * kt)[..., None, :]   # I - k (b*k)^T
+        D = alpha[:, t][..., :, None] * eye            # diag(alpha_t)
+        write = kt[..., :, None] * (w[:, t] * v[:, t])[..., None, :]  # k (w*v)^T
+        S = E @ (D @ S) + write
+        o[:, t] = np.einsum("bhc,bhcj->bhj", q[:, t], S)   # q_t^T S_t
+    return o, S
+
+
+def chunked_wy(q, k, v, alpha, b, w, S0=None, chunk=64, return_intermediates=False):
+    """fp64 chunked form of the same recurrence (chunk size ``chunk``).
+
+    The README (intro and "Architecture" diagram; "Configuration" gives
+    chunk_size = 64) names a chunked WY decomposition as the training-mode
+    forward.  The pages give no formulas for it, so this is the form that the
+    per-token recurrence itself implies, written per chunk of L tokens that
+    enters with state S0 (positions r, s = 1..L inside the chunk):
+
+      g_r = log alpha_r, G_r = sum_{j<=r} g_j, Gamma_r = exp(G_r)   (per key channel)
+      e_r = b_r * k_r,   u_r = w_r * v_r
+      A[r,s] = sum_c e_r[c] k_s[c] exp(G_r[c]-G_s[c])     for s <  r  (else 0)
+      P[r,s] = sum_c q_r[c] k_s[c] exp(G_r[c]-G_s[c])     for s <= r  (else 0)
+      Tm = (I + A)^{-1}
+      W  = Tm @ (Gamma * e),   U = Tm @ u
+      Delta = U - W @ S0
+      O     = (Gamma * q) @ S0 + P @ Delta
+      S_L   = diag(Gamma_L) @ S0 + Ktil^T @ Delta,   Ktil_s = k_s * exp(G_L - G_s)
+
+    Derivation: one step is S_r = D_r S_{r-1} + k_r delta_r^T with
+    delta_r = u_r - S_{r-1}^T (alpha_r * e_r); unrolling S_{r-1} and collecting
+    the delta terms gives (I + A) Delta = U - (Gamma*e) S0.  A trailing partial
+    chunk is handled at its own length.
+
+    Returns (o, S_T); with ``return_intermediates`` also a list (one dict per
+    (chunk, b, h) in that nesting order) holding G, A, P, Tm, W, U, Qh, Ktil,
+    GammaL for kernel-level checks.
+    """
+    q, k, v, alpha, b, w = map(_f64, (q, k, v, alpha, b, w))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    S = np.zeros((B, H, dk, dv)) if S0 is None else _f64(S0).copy()
+    o = np.zeros((B, T, H, dv))
+    inter = []
+    for n0 in range(0, T, chunk):
+        L = min(chunk, T - n0)
+        sl = slice(n0, n0 + L)
+        for bi in range(B):
+            for hi in range(H):
+                qc = q[bi, sl, hi]          # [L,dk]
+                kc = k[bi, sl, hi]
+                ec = b[bi, sl, hi] * kc
+                uc = w[bi, sl, hi] * v[bi, sl, hi]   # [L,dv]
+                G = np.cumsum(np.log(alpha[bi, sl, hi]), axis=0)   # [L,dk]
+                ratio = np.exp(G[:, None, :] - G[None, :, :])       # [r,s,c]
+                A = np.einsum("rc,sc,rsc->rs", ec, kc, ratio) * np.tri(L, k=-1)
+                P = np.einsum("rc,sc,rsc->rs", qc, kc, ratio) * np.tri(L, k=0)
+                Tm = np.linalg.inv(np.eye(L) + A)
+                Gam = np.exp(G)
+                W = Tm @ (Gam * ec)
+                U = Tm @ uc
+                S0c = S[bi, hi]
+                Delta = U - W @ S0c
+                Qh = Gam * qc
+                o[bi, sl, hi] = Qh @ S0c + P @ Delta
+                Ktil = kc * np.exp(G[-1][None, :] - G)
+                S[bi, hi] = Gam[-1][:, None] * S0c + Ktil.T @ Delta
+                if return_intermediates:
+                    inter.append(dict(G=G, A=A, P=P, Tm=Tm, W=W, U=U, Qh=Qh,
+                                      Ktil=Ktil, GammaL=Gam[-1]))
+    if return_intermediates:
+        return o, S, inter
+    return o, S
+
+
+def rel_l2(x, ref):
+    """||x - ref||_2 / ||ref||_2 over the whole tensor in fp64 (max-abs if ref == 0)."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref.ravel())
+    num = np.linalg.norm((x - ref).ravel())
+    if den == 0.0:
+        return float(np.max(np.abs(x - ref))) if x.size else 0.0
+    return float(num / den)
