@@ -1,0 +1,21 @@
+"""Gated DeltaNet-2 token-mixer core for AMD MI355X (gfx950).
+
+Python face of the C ABI in ``include/gdn2.h`` (``libgdn2.so`` in this
+directory): the chunked forward and the fused recurrent / decode step of the
+GDN-2 recurrence, with hand-written HIP kernels doing all the arithmetic.
+The library is loaded on first use; a missing library raises.
+"""
+from ._binding import (  # noqa: F401
+    Gdn2Error,
+    Problem,
+    abi_version,
+    alloc_workspace,
+    chunk_fwd,
+    chunk_fwd_workspace_size,
+    chunk_prep,
+    chunk_state,
+    lib,
+    problem,
+    recurrent_step,
+    status_str,
+)

@@ -1,0 +1,192 @@
+"""ctypes binding of ``libgdn2.so`` (argument marshalling only).
+
+Every computation runs in the library's gfx950 kernels; this module checks
+tensor shapes/dtypes/devices, allocates outputs and workspace with torch, and
+passes raw device pointers plus torch's current HIP stream to the C ABI
+declared in ``include/gdn2.h``.  There is no fallback: if the library is
+missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn2.so")
+
+GDN2_F32, GDN2_BF16 = 0, 1
+_STATUS = {0: "GDN2_OK", 1: "GDN2_ERR_NULL", 2: "GDN2_ERR_SHAPE", 3: "GDN2_ERR_DTYPE",
+           4: "GDN2_ERR_ALIAS", 5: "GDN2_ERR_WORKSPACE", 6: "GDN2_ERR_DEVICE", 7: "GDN2_ERR_ALIGN"}
+EXPORTED = ("gdn2_abi_version", "gdn2_status_str", "gdn2_chunk_fwd_workspace_size",
+            "gdn2_chunk_fwd", "gdn2_chunk_prep", "gdn2_chunk_state", "gdn2_recurrent_step")
+
+
+class Problem(ctypes.Structure):
+    """Mirror of ``gdn2_problem`` (include/gdn2.h)."""
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("dk", ctypes.c_int64), ("dv", ctypes.c_int64), ("chunk", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("gate_dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class Gdn2Error(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(msg)
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """Load ``libgdn2.so`` once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                              "(hipcc, gfx950); there is no CPU fallback")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, P = ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(Problem)
+        L.gdn2_abi_version.restype = ctypes.c_int
+        L.gdn2_abi_version.argtypes = []
+        L.gdn2_status_str.restype = ctypes.c_char_p
+        L.gdn2_status_str.argtypes = [ctypes.c_int]
+        L.gdn2_chunk_fwd_workspace_size.restype = sz
+        L.gdn2_chunk_fwd_workspace_size.argtypes = [P]
+        L.gdn2_chunk_fwd.restype = ctypes.c_int
+        L.gdn2_chunk_fwd.argtypes = [P] + [vp] * 9 + [vp, sz, vp]
+        L.gdn2_chunk_prep.restype = ctypes.c_int
+        L.gdn2_chunk_prep.argtypes = [P] + [vp] * 6 + [vp, sz, vp]
+        L.gdn2_chunk_state.restype = ctypes.c_int
+        L.gdn2_chunk_state.argtypes = [P, vp, vp, vp, vp, sz, vp]
+        L.gdn2_recurrent_step.restype = ctypes.c_int
+        L.gdn2_recurrent_step.argtypes = [P] + [vp] * 9 + [vp]
+        _lib = L
+    return _lib
+
+
+def abi_version() -> int:
+    return int(lib().gdn2_abi_version())
+
+
+def status_str(code: int) -> str:
+    return lib().gdn2_status_str(int(code)).decode()
+
+
+def _check(code: int):
+    if code != 0:
+        raise Gdn2Error(code, status_str(code))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def problem(B, T, H, dk, dv, io_dtype: torch.dtype, chunk: int = 64) -> Problem:
+    io = {torch.float32: GDN2_F32, torch.bfloat16: GDN2_BF16}.get(io_dtype, -1)
+    return Problem(B, T, H, dk, dv, chunk, io, GDN2_F32, 0)
+
+
+def _problem_from(q, k, v, alpha, b, w) -> Tuple[Problem, torch.device]:
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q/k/alpha/b must be [B,T,H,dk] and v/w [B,T,H,dv]")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    for name, x, last in (("k", k, dk), ("alpha", alpha, dk), ("b", b, dk), ("v", v, dv), ("w", w, dv)):
+        if tuple(x.shape) != (B, T, H, last):
+            raise ValueError(f"{name} has shape {tuple(x.shape)}, expected {(B, T, H, last)}")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("q, k, v must share one dtype: float32 or bfloat16")
+    for name, x in (("alpha", alpha), ("b", b), ("w", w)):
+        if x.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    dev = q.device
+    for name, x in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("b", b), ("w", w)):
+        if x.device != dev or dev.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor on {dev}")
+        if not x.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    return problem(B, T, H, dk, dv, q.dtype), dev
+
+
+def _check_state(S, p: Problem, dev, name):
+    if S is None:
+        return
+    if tuple(S.shape) != (p.B, p.H, p.dk, p.dv) or S.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32 [{p.B},{p.H},{p.dk},{p.dv}]")
+    if S.device != dev or not S.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous tensor on {dev}")
+
+
+def chunk_fwd_workspace_size(B, T, H, dk, dv, io_dtype: torch.dtype) -> int:
+    return int(lib().gdn2_chunk_fwd_workspace_size(ctypes.byref(problem(B, T, H, dk, dv, io_dtype))))
+
+
+def alloc_workspace(nbytes: int, device) -> torch.Tensor:
+    # torch's caching allocator returns blocks aligned to at least 512 bytes
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def chunk_fwd(q, k, v, alpha, b, w, S0=None, *, out_state: bool = True, o=None, S_out=None,
+              workspace=None):
+    """Chunked forward (``gdn2_chunk_fwd``).  Returns (o, S_final or None)."""
+    p, dev = _problem_from(q, k, v, alpha, b, w)
+    _check_state(S0, p, dev, "S0")
+    if o is None:
+        o = torch.empty(v.shape, dtype=v.dtype, device=dev)
+    if S_out is None and out_state:
+        S_out = torch.empty((p.B, p.H, p.dk, p.dv), dtype=torch.float32, device=dev)
+    _check_state(S_out, p, dev, "S_out")
+    need = int(lib().gdn2_chunk_fwd_workspace_size(ctypes.byref(p)))
+    if workspace is None:
+        workspace = alloc_workspace(need, dev)
+    _check(lib().gdn2_chunk_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w),
+                                _ptr(S0), _ptr(o), _ptr(S_out), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(dev)))
+    return o, S_out
+
+
+def chunk_prep(q, k, v, alpha, b, w, workspace):
+    """First stage of the chunked forward (``gdn2_chunk_prep``): fills ``workspace``."""
+    p, dev = _problem_from(q, k, v, alpha, b, w)
+    _check(lib().gdn2_chunk_prep(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(dev)))
+
+
+def chunk_state(p: Problem, workspace, o, S0=None, S_out=None):
+    """Second stage of the chunked forward (``gdn2_chunk_state``): writes o (and S_out)."""
+    dev = workspace.device
+    _check_state(S0, p, dev, "S0")
+    _check_state(S_out, p, dev, "S_out")
+    _check(lib().gdn2_chunk_state(ctypes.byref(p), _ptr(S0), _ptr(o), _ptr(S_out), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(dev)))
+
+
+def recurrent_step(q, k, v, alpha, b, w, S_in=None, *, o=None, S_out=None, out_state: bool = True,
+                   inplace: bool = False):
+    """Fused recurrent forward (``gdn2_recurrent_step``); T == 1 is one decode step.
+
+    ``inplace=True`` writes the final state back into ``S_in``.
+    Returns (o, S_final or None).
+    """
+    p, dev = _problem_from(q, k, v, alpha, b, w)
+    _check_state(S_in, p, dev, "S_in")
+    if o is None:
+        o = torch.empty(v.shape, dtype=v.dtype, device=dev)
+    if inplace:
+        if S_in is None:
+            raise ValueError("inplace needs S_in")
+        S_out = S_in
+    elif S_out is None and out_state:
+        S_out = torch.empty((p.B, p.H, p.dk, p.dv), dtype=torch.float32, device=dev)
+    _check_state(S_out, p, dev, "S_out")
+    _check(lib().gdn2_recurrent_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w),
+                                     _ptr(S_in), _ptr(o), _ptr(S_out), _stream(dev)))
+    return o, S_out

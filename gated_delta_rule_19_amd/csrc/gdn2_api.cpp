@@ -1,0 +1,281 @@
+// C ABI of the GDN-2 token-mixer core (include/gdn2.h): argument checks on
+// the host, workspace sizing, and the kernel launches on the caller's stream.
+//
+// Everything that can be decided from the arguments is checked before the
+// first HIP call, so an invalid call never touches the device.  No function
+// here allocates, frees or synchronises.
+#include "gdn2.h"
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include <initializer_list>
+
+#include "gdn2_launch.hpp"
+#include "gdn2_layout.hpp"
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 40;   // larger sizes are rejected as shape errors
+
+struct Range {
+    uintptr_t lo, hi;   // [lo, hi); empty when lo == hi
+};
+
+Range range_of(const void* p, int64_t bytes)
+{
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, (p != nullptr && bytes > 0) ? lo + static_cast<uintptr_t>(bytes) : lo};
+}
+
+bool overlap(Range a, Range b)
+{
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+// checks shared by every entry point; `chunked` adds the chunk-length rule
+int check_problem(const gdn2_problem* p, bool chunked)
+{
+    if (p == nullptr) return GDN2_ERR_NULL;
+    if (p->B < 0 || p->T < 0 || p->H < 0 || p->B > kMaxDim || p->T > kMaxDim || p->H > kMaxDim)
+        return GDN2_ERR_SHAPE;
+    if (!(p->dk == 16 || p->dk == 32 || p->dk == 64 || p->dk == 128)) return GDN2_ERR_SHAPE;
+    if (p->dv < 16 || p->dv > 256 || p->dv % 16 != 0) return GDN2_ERR_SHAPE;
+    if (chunked && p->chunk != 64) return GDN2_ERR_SHAPE;
+    if (p->reserved != 0) return GDN2_ERR_SHAPE;
+    // element counts stay far inside int64 and every grid inside 2^31 workgroups
+    const double rows = double(p->B) * double(p->T) * double(p->H);
+    if (rows * 256.0 > 9.0e15) return GDN2_ERR_SHAPE;
+    if (double(p->B) * double(p->H) * (double((p->T + 63) / 64) + 16.0) > 2.0e9) return GDN2_ERR_SHAPE;
+    const bool f32 = p->io_dtype == GDN2_F32 && p->gate_dtype == GDN2_F32;
+    const bool bf = p->io_dtype == GDN2_BF16 && p->gate_dtype == GDN2_F32;
+    if (!f32 && !bf) return GDN2_ERR_DTYPE;
+    return GDN2_OK;
+}
+
+bool is_bf16(const gdn2_problem* p) { return p->io_dtype == GDN2_BF16; }
+int64_t io_size(const gdn2_problem* p) { return is_bf16(p) ? 2 : 4; }
+int64_t nchunks(const gdn2_problem* p) { return (p->T + 63) / 64; }
+
+int64_t ws_block_bytes(const gdn2_problem* p)
+{
+    return gdn2::ws_layout(p->dk, p->dv, io_size(p), is_bf16(p) ? 32 : 16).block;
+}
+
+int64_t ws_bytes(const gdn2_problem* p) { return p->B * p->H * nchunks(p) * ws_block_bytes(p); }
+
+struct Sizes {
+    int64_t key, val, state;   // bytes of a [B,T,H,dk] io tensor, a [B,T,H,dv] io tensor, a state
+    int64_t gk, gv;            // bytes of the fp32 gates on the key / value axis
+};
+
+Sizes sizes_of(const gdn2_problem* p)
+{
+    const int64_t rows = p->B * p->T * p->H;
+    return Sizes{rows * p->dk * io_size(p), rows * p->dv * io_size(p), p->B * p->H * p->dk * p->dv * 4,
+                 rows * p->dk * 4, rows * p->dv * 4};
+}
+
+bool rows_nonempty(const gdn2_problem* p) { return p->B * p->T * p->H > 0; }
+
+// inputs must be non-null whenever they hold any element
+int check_inputs(const gdn2_problem* p, const void* q, const void* k, const void* v,
+                 const void* alpha, const void* b, const void* w, const void* o)
+{
+    if (!rows_nonempty(p)) return GDN2_OK;
+    if (!q || !k || !v || !alpha || !b || !w || !o) return GDN2_ERR_NULL;
+    return GDN2_OK;
+}
+
+// outputs may not overlap inputs or each other; the state may be updated in
+// place only when the pointers are identical
+int check_alias(const Range* outs, int nout, const Range* ins, int nin, const void* s_in, const void* s_out,
+                int s_in_idx, int s_out_idx)
+{
+    for (int i = 0; i < nout; ++i) {
+        for (int j = 0; j < nin; ++j) {
+            if (i == s_out_idx && j == s_in_idx && s_in == s_out) continue;
+            if (overlap(outs[i], ins[j])) return GDN2_ERR_ALIAS;
+        }
+        for (int j = i + 1; j < nout; ++j)
+            if (overlap(outs[i], outs[j])) return GDN2_ERR_ALIAS;
+    }
+    return GDN2_OK;
+}
+
+int check_align(std::initializer_list<const void*> ptrs)
+{
+    for (const void* p : ptrs)
+        if ((reinterpret_cast<uintptr_t>(p) & 15u) != 0) return GDN2_ERR_ALIGN;
+    return GDN2_OK;
+}
+
+int device_ready()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GDN2_ERR_DEVICE;
+    return GDN2_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? GDN2_OK : GDN2_ERR_DEVICE; }
+
+int do_prep(const gdn2_problem* p, const void* q, const void* k, const void* v, const void* alpha,
+            const void* b, const void* w, void* ws, hipStream_t s)
+{
+    if (p->B * p->H * nchunks(p) == 0) return GDN2_OK;
+    gdn2::PrepArgs a{q, k, v, static_cast<const float*>(alpha), static_cast<const float*>(b),
+                     static_cast<const float*>(w), ws, ws_block_bytes(p), p->B, p->T, p->H,
+                     (int)p->dv, (int)nchunks(p)};
+    return launch_status(gdn2::launch_chunk_prep(a, (int)p->dk, is_bf16(p), s));
+}
+
+int do_state(const gdn2_problem* p, const float* S0, void* o, float* S_out, const void* ws, hipStream_t s)
+{
+    const int64_t nch = p->B * p->H;
+    if (nch == 0) return GDN2_OK;
+    if (nchunks(p) == 0 && S_out == S0) return GDN2_OK;   // nothing to compute or copy
+    const int vs = gdn2::chunk_state_slice(nch, (int)p->dv);
+    gdn2::StateArgs a{ws, ws_block_bytes(p), S0, o, S_out, p->B, p->T, p->H, (int)p->dv,
+                      (int)nchunks(p), (int)(p->dv / vs)};
+    return launch_status(gdn2::launch_chunk_state(a, (int)p->dk, vs, is_bf16(p), s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn2_abi_version(void) { return GDN2_ABI_VERSION; }
+
+const char* gdn2_status_str(int status)
+{
+    switch (status) {
+        case GDN2_OK: return "GDN2_OK: success";
+        case GDN2_ERR_NULL: return "GDN2_ERR_NULL: a required pointer is NULL";
+        case GDN2_ERR_SHAPE: return "GDN2_ERR_SHAPE: unsupported or inconsistent sizes";
+        case GDN2_ERR_DTYPE: return "GDN2_ERR_DTYPE: unsupported dtype pair";
+        case GDN2_ERR_ALIAS: return "GDN2_ERR_ALIAS: an output overlaps an input or another output";
+        case GDN2_ERR_WORKSPACE: return "GDN2_ERR_WORKSPACE: workspace missing or too small";
+        case GDN2_ERR_DEVICE: return "GDN2_ERR_DEVICE: no usable GPU or a launch failed";
+        case GDN2_ERR_ALIGN: return "GDN2_ERR_ALIGN: a tensor pointer is not 16-byte aligned";
+        default: return "GDN2: unknown status";
+    }
+}
+
+size_t gdn2_chunk_fwd_workspace_size(const gdn2_problem* p)
+{
+    if (check_problem(p, true) != GDN2_OK) return 0;
+    return static_cast<size_t>(ws_bytes(p));
+}
+
+int gdn2_chunk_prep(const gdn2_problem* p, const void* q, const void* k, const void* v,
+                    const void* alpha, const void* b, const void* w, void* workspace,
+                    size_t workspace_bytes, void* stream)
+{
+    int st = check_problem(p, true);
+    if (st) return st;
+    // the prep stage has no o; check inputs with a stand-in non-null output
+    st = check_inputs(p, q, k, v, alpha, b, w, q);
+    if (st) return st;
+    const int64_t need = ws_bytes(p);
+    if (need > 0 && (workspace == nullptr || static_cast<int64_t>(workspace_bytes) < need))
+        return GDN2_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_WORKSPACE;
+    const Sizes z = sizes_of(p);
+    const Range ins[6] = {range_of(q, z.key), range_of(k, z.key), range_of(v, z.val),
+                          range_of(alpha, z.gk), range_of(b, z.gk), range_of(w, z.gv)};
+    const Range outs[1] = {range_of(workspace, need)};
+    st = check_alias(outs, 1, ins, 6, nullptr, nullptr, -1, -1);
+    if (st) return st;
+    st = check_align({q, k, v, alpha, b, w});
+    if (st) return st;
+    if (need == 0) return GDN2_OK;
+    st = device_ready();
+    if (st) return st;
+    return do_prep(p, q, k, v, alpha, b, w, workspace, static_cast<hipStream_t>(stream));
+}
+
+int gdn2_chunk_state(const gdn2_problem* p, const float* S0, void* o, float* S_out,
+                     const void* workspace, size_t workspace_bytes, void* stream)
+{
+    int st = check_problem(p, true);
+    if (st) return st;
+    if (rows_nonempty(p) && o == nullptr) return GDN2_ERR_NULL;
+    const int64_t need = ws_bytes(p);
+    if (need > 0 && (workspace == nullptr || static_cast<int64_t>(workspace_bytes) < need))
+        return GDN2_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_WORKSPACE;
+    const Sizes z = sizes_of(p);
+    const Range ins[2] = {range_of(workspace, need), range_of(S0, z.state)};
+    const Range outs[2] = {range_of(o, z.val), range_of(S_out, z.state)};
+    st = check_alias(outs, 2, ins, 2, S0, S_out, 1, 1);
+    if (st) return st;
+    st = check_align({S0, o, S_out});
+    if (st) return st;
+    if (p->B * p->H == 0 || (nchunks(p) == 0 && S_out == S0)) return GDN2_OK;
+    st = device_ready();
+    if (st) return st;
+    return do_state(p, S0, o, S_out, workspace, static_cast<hipStream_t>(stream));
+}
+
+int gdn2_chunk_fwd(const gdn2_problem* p, const void* q, const void* k, const void* v,
+                   const void* alpha, const void* b, const void* w, const float* S0, void* o,
+                   float* S_out, void* workspace, size_t workspace_bytes, void* stream)
+{
+    int st = check_problem(p, true);
+    if (st) return st;
+    st = check_inputs(p, q, k, v, alpha, b, w, o);
+    if (st) return st;
+    const int64_t need = ws_bytes(p);
+    if (need > 0 && (workspace == nullptr || static_cast<int64_t>(workspace_bytes) < need))
+        return GDN2_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_WORKSPACE;
+    const Sizes z = sizes_of(p);
+    const Range ins[7] = {range_of(q, z.key),  range_of(k, z.key),  range_of(v, z.val),
+                          range_of(alpha, z.gk), range_of(b, z.gk), range_of(w, z.gv),
+                          range_of(S0, z.state)};
+    const Range outs[3] = {range_of(o, z.val), range_of(S_out, z.state), range_of(workspace, need)};
+    st = check_alias(outs, 3, ins, 7, S0, S_out, 6, 1);
+    if (st) return st;
+    st = check_align({q, k, v, alpha, b, w, S0, o, S_out});
+    if (st) return st;
+    if (p->B * p->H == 0 || (nchunks(p) == 0 && S_out == S0)) return GDN2_OK;
+    st = device_ready();
+    if (st) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    st = do_prep(p, q, k, v, alpha, b, w, workspace, s);
+    if (st) return st;
+    return do_state(p, S0, o, S_out, workspace, s);
+}
+
+int gdn2_recurrent_step(const gdn2_problem* p, const void* q, const void* k, const void* v,
+                        const void* alpha, const void* b, const void* w, const float* S_in, void* o,
+                        float* S_out, void* stream)
+{
+    int st = check_problem(p, false);
+    if (st) return st;
+    st = check_inputs(p, q, k, v, alpha, b, w, o);
+    if (st) return st;
+    const Sizes z = sizes_of(p);
+    const Range ins[7] = {range_of(q, z.key),  range_of(k, z.key),  range_of(v, z.val),
+                          range_of(alpha, z.gk), range_of(b, z.gk), range_of(w, z.gv),
+                          range_of(S_in, z.state)};
+    const Range outs[2] = {range_of(o, z.val), range_of(S_out, z.state)};
+    st = check_alias(outs, 2, ins, 7, S_in, S_out, 6, 1);
+    if (st) return st;
+    st = check_align({q, k, v, alpha, b, w, S_in, o, S_out});
+    if (st) return st;
+    const int64_t nch = p->B * p->H;
+    if (nch == 0) return GDN2_OK;
+    if (p->T == 0 && S_out == S_in) return GDN2_OK;
+    st = device_ready();
+    if (st) return st;
+    const int vs = gdn2::recurrent_slice(nch, p->T, (int)p->dv);
+    gdn2::RecArgs a{q, k, v, static_cast<const float*>(alpha), static_cast<const float*>(b),
+                    static_cast<const float*>(w), S_in, o, S_out, p->B, p->T, p->H, (int)p->dv,
+                    (int)(p->dv / vs)};
+    return launch_status(gdn2::launch_recurrent(a, (int)p->dk, vs, is_bf16(p), static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

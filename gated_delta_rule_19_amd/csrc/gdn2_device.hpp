@@ -1,0 +1,110 @@
+// Device helpers shared by the GDN-2 kernels (gfx950 / CDNA4, wave64).
+//
+// Matrix-core convention used everywhere in this library.  A 16x16 output
+// tile D = A (16 x K) * B (K x 16) is accumulated by "K-blocks".  In every
+// K-block each lane supplies 16 bytes of A and 16 bytes of B:
+//   A: row  m = lane % 16, elements k0 + EPL*(lane/16) .. +EPL-1 of that row
+//   B: col  n = lane % 16, elements k0 + EPL*(lane/16) .. +EPL-1 of that column
+// where EPL = 8 for bf16 (one v_mfma_f32_16x16x32_bf16, K-block = 32) and
+// EPL = 4 for fp32 (four v_mfma_f32_16x16x4_f32, K-block = 16; the i-th
+// instruction takes element i of every lane).  Because A and B use the same
+// lane->k assignment, the sum runs over every k of the block exactly once.
+// The accumulator holds D[4*(lane/16) + i][lane % 16], i = 0..3.
+//
+// So an operand stored with its K index contiguous (row-major A, or B stored
+// as B^T) is fetched with one 16-byte load per lane per K-block, from LDS or
+// global memory alike.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn2 {
+
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+
+constexpr int kThreads = 256;   // every kernel runs 4 waves of 64 lanes
+constexpr int kChunk = 64;      // chunk length of the chunked form
+
+__host__ __device__ constexpr int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+// ---------------------------------------------------------------------------
+// Element type traits: Tio is float (fp32 I/O) or __bf16 (bf16 I/O).
+// ---------------------------------------------------------------------------
+template <typename T> struct Io;
+
+template <> struct Io<float> {
+    static constexpr int EPL = 4;        // elements per lane per K-block
+    static constexpr int KB = 16;        // K per K-block
+    typedef f32x4 frag;                  // 16 bytes
+    typedef f32x4 vec4;                  // 4 elements
+    __device__ static inline float to_f(float x) { return x; }
+    __device__ static inline float from_f(float x) { return x; }
+    __device__ static inline vec4 pack4(f32x4 v) { return v; }
+    __device__ static inline f32x4 unpack4(vec4 v) { return v; }
+    __device__ static inline f32x4 mma(f32x4 acc, frag a, frag b) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc, 0, 0, 0);
+        return acc;
+    }
+    // multiply the EPL elements of a fragment by per-k factors f[0..EPL-1]
+    __device__ static inline frag scale(frag a, const float* f) {
+        f32x4 s = *reinterpret_cast<const f32x4*>(f);
+        return a * s;
+    }
+};
+
+template <> struct Io<__bf16> {
+    static constexpr int EPL = 8;
+    static constexpr int KB = 32;
+    typedef bf16x8 frag;
+    typedef bf16x4 vec4;
+    __device__ static inline float to_f(__bf16 x) { return (float)x; }
+    __device__ static inline __bf16 from_f(float x) { return (__bf16)x; }   // RNE (v_cvt_pk_bf16_f32)
+    __device__ static inline vec4 pack4(f32x4 v) {
+        vec4 r;
+        r[0] = (__bf16)v[0]; r[1] = (__bf16)v[1]; r[2] = (__bf16)v[2]; r[3] = (__bf16)v[3];
+        return r;
+    }
+    __device__ static inline f32x4 unpack4(vec4 v) {
+        f32x4 r = {(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+        return r;
+    }
+    __device__ static inline f32x4 mma(f32x4 acc, frag a, frag b) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    }
+    __device__ static inline frag scale(frag a, const float* f) {
+        f32x4 s0 = *reinterpret_cast<const f32x4*>(f);
+        f32x4 s1 = *reinterpret_cast<const f32x4*>(f + 4);
+        frag r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            r[i] = (__bf16)((float)a[i] * s0[i]);
+            r[4 + i] = (__bf16)((float)a[4 + i] * s1[i]);
+        }
+        return r;
+    }
+};
+
+template <typename T>
+__device__ inline typename Io<T>::frag ld_frag(const T* p) {
+    return *reinterpret_cast<const typename Io<T>::frag*>(p);
+}
+
+template <typename T>
+__device__ inline void st_vec4(T* p, f32x4 v) {
+    *reinterpret_cast<typename Io<T>::vec4*>(p) = Io<T>::pack4(v);
+}
+
+template <typename T>
+__device__ inline f32x4 ld_vec4(const T* p) {
+    return Io<T>::unpack4(*reinterpret_cast<const typename Io<T>::vec4*>(p));
+}
+
+__device__ inline float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+}  // namespace gdn2

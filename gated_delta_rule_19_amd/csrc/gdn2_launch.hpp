@@ -1,0 +1,39 @@
+// Internal launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn2 {
+
+struct PrepArgs {
+    const void* q; const void* k; const void* v;
+    const float* alpha; const float* b; const float* w;
+    void* ws; int64_t ws_block;
+    int64_t B, T, H; int dv; int nt;
+};
+
+struct StateArgs {
+    const void* ws; int64_t ws_block;
+    const float* S0; void* o; float* S_out;
+    int64_t B, T, H; int dv; int nt; int nslices;
+};
+
+struct RecArgs {
+    const void* q; const void* k; const void* v;
+    const float* alpha; const float* b; const float* w;
+    const float* S_in; void* o; float* S_out;
+    int64_t B, T, H; int dv; int nslices;
+};
+
+// Each returns hipSuccess or the launch error.  bf16 selects the I/O dtype.
+hipError_t launch_chunk_prep(const PrepArgs& a, int dk, bool bf16, hipStream_t s);
+hipError_t launch_chunk_state(const StateArgs& a, int dk, int vs, bool bf16, hipStream_t s);
+hipError_t launch_recurrent(const RecArgs& a, int dk, int vs, bool bf16, hipStream_t s);
+
+// Value-slice width the state pass uses for a problem (16, 32 or 64).
+int chunk_state_slice(int64_t nchains, int dv);
+// Value-slice width the recurrent kernel uses (16, 32, 64 or 128).
+int recurrent_slice(int64_t nchains, int64_t T, int dv);
+
+}  // namespace gdn2

@@ -1,0 +1,213 @@
+// Fused recurrent forward / decode step of the GDN-2 token mixer on gfx950.
+//
+// Per token (burn-gdn2 0.1.9 README, "Architecture" recurrence):
+//   S_t = (I - k (b*k)^T) diag(alpha) S + k (w*v)^T,   o_t = q^T S_t.
+// Rewritten so that the state is read and written once per token:
+//   X = diag(alpha) S
+//   r = X^T (b*k),  m = X^T q            (two reductions over the key axis)
+//   delta = w*v - r
+//   S_t = X + k delta^T,  o_t = m + (q.k) delta
+// since (I - k e^T) X = X - k (e^T X) and q^T k delta^T = (q.k) delta^T.
+//
+// Workgroup = (batch, head, value slice of VS columns), 256 threads.  Thread
+// (jg, rg) holds columns 4*jg..4*jg+3 of rows rg, rg+NR, ... of the fp32
+// state in registers for the whole call, so for a decode step (T = 1) the
+// state streams from HBM and back exactly once with 16-byte accesses; a wave
+// covers 64/NJ whole rows of the slice, contiguous in memory when VS == dv.
+// The key-axis vectors of token t+1 are fetched into LDS while token t is
+// reduced; one barrier per token.
+#include "gdn2_device.hpp"
+#include "gdn2_launch.hpp"
+
+namespace gdn2 {
+
+template <typename Tio, int DK, int VS>
+__global__ __launch_bounds__(kThreads) void k_recurrent(RecArgs a)
+{
+    using IO = Io<Tio>;
+    constexpr int NJ = VS / 4;                          // column groups (4 columns each)
+    constexpr int NR = (kThreads / NJ) < DK ? (kThreads / NJ) : DK;   // row groups
+    constexpr int NTH = NJ * NR;                        // threads holding state (multiple of 64)
+    constexpr int RPT = DK / NR;                        // rows per thread
+    constexpr int NW = NTH / 64;                        // waves holding state
+    static_assert(NTH % 64 == 0 && NTH <= kThreads && DK % NR == 0, "thread layout");
+
+    __shared__ __attribute__((aligned(16))) float vec[2][4][DK];   // alpha, b*k, k, q of a token
+    __shared__ float red[2][NW][NJ][9];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const bool holder = tid < NTH;
+    const int jg = tid % NJ, rg = tid / NJ;
+    const int64_t chain = blockIdx.x / a.nslices;
+    const int slice = (int)(blockIdx.x - chain * a.nslices);
+    const int64_t bb = chain / a.H, hh = chain - bb * a.H;
+    const int dv = a.dv;
+    const int jc = slice * VS + 4 * jg;                 // first column of this thread
+    const Tio* q = static_cast<const Tio*>(a.q);
+    const Tio* k = static_cast<const Tio*>(a.k);
+    const Tio* v = static_cast<const Tio*>(a.v);
+    Tio* o = static_cast<Tio*>(a.o);
+
+    f32x4 S[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (holder && a.S_in != nullptr)
+            S[i] = *reinterpret_cast<const f32x4*>(a.S_in + (chain * DK + rg + NR * i) * dv + jc);
+    }
+
+    // key-axis vectors of a token -> registers (cooperative, coalesced)
+    constexpr int VPT = (4 * DK + kThreads - 1) / kThreads;
+    auto fetch = [&](int64_t t, float (&st)[VPT]) {
+        const int64_t rowk = ((bb * a.T + t) * a.H + hh) * DK;
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const int e = tid + u * kThreads;
+            float x = 0.f;
+            if (e < 4 * DK) {
+                const int which = e / DK, c = e - which * DK;
+                if (which == 0) x = a.alpha[rowk + c];
+                else if (which == 1) x = a.b[rowk + c] * IO::to_f(k[rowk + c]);
+                else if (which == 2) x = IO::to_f(k[rowk + c]);
+                else x = IO::to_f(q[rowk + c]);
+            }
+            st[u] = x;
+        }
+    };
+    auto stash = [&](int buf, const float (&st)[VPT]) {
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const int e = tid + u * kThreads;
+            if (e < 4 * DK) (&vec[buf][0][0])[e] = st[u];
+        }
+    };
+
+    float stage[VPT];
+    if (a.T > 0) {
+        fetch(0, stage);
+        stash(0, stage);
+    }
+    __syncthreads();
+
+    for (int64_t t = 0; t < a.T; ++t) {
+        const int buf = (int)(t & 1);
+        if (t + 1 < a.T) fetch(t + 1, stage);
+        const int64_t rowv = ((bb * a.T + t) * a.H + hh) * dv + jc;
+
+        f32x4 u = {0.f, 0.f, 0.f, 0.f};
+        f32x4 r = u, m = u;
+        float qk = 0.f;
+        float kreg[RPT];   // k of this thread's rows; vec[buf] is refilled for token t+2
+                           // while slower waves may still be finishing token t
+        if (holder) {
+            u = *reinterpret_cast<const f32x4*>(a.w + rowv) * ld_vec4(v + rowv);
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const int c = rg + NR * i;
+                const float al = vec[buf][0][c], e = vec[buf][1][c];
+                const float kk = vec[buf][2][c], qq = vec[buf][3][c];
+                kreg[i] = kk;
+                S[i] *= al;
+                r += e * S[i];
+                m += qq * S[i];
+                qk += qq * kk;
+            }
+        }
+        // reduce over the row groups of this wave (lanes sharing jg)
+#pragma unroll
+        for (int off = NJ; off < 64; off <<= 1) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                r[jj] += __shfl_xor(r[jj], off, 64);
+                m[jj] += __shfl_xor(m[jj], off, 64);
+            }
+            qk += __shfl_xor(qk, off, 64);
+        }
+        if (holder && lane < NJ) {
+            float* dst = red[buf][wave][jg];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                dst[jj] = r[jj];
+                dst[4 + jj] = m[jj];
+            }
+            dst[8] = qk;
+        }
+        if (t + 1 < a.T) stash(buf ^ 1, stage);
+        __syncthreads();
+
+        if (holder) {
+            f32x4 R = {0.f, 0.f, 0.f, 0.f};
+            f32x4 M = R;
+            float QK = 0.f;
+#pragma unroll
+            for (int wv = 0; wv < NW; ++wv) {
+                const float* src = red[buf][wv][jg];
+                R += f32x4{src[0], src[1], src[2], src[3]};
+                M += f32x4{src[4], src[5], src[6], src[7]};
+                QK += src[8];
+            }
+            const f32x4 delta = u - R;
+            if (rg == 0) st_vec4(o + rowv, M + QK * delta);
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) S[i] += kreg[i] * delta;
+        }
+    }
+
+    if (holder && a.S_out != nullptr) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+            *reinterpret_cast<f32x4*>(a.S_out + (chain * DK + rg + NR * i) * dv + jc) = S[i];
+    }
+}
+
+int recurrent_slice(int64_t nchains, int64_t T, int dv)
+{
+    // a decode step streams whole rows (widest slice); longer runs trade row
+    // width for more independent workgroups
+    static const int widths[4] = {128, 64, 32, 16};
+    for (int i = 0; i < 4; ++i) {
+        const int w = widths[i];
+        if (dv % w) continue;
+        if (T <= 1 || nchains * (dv / w) >= 1024 || w == 16) return w;
+    }
+    return 16;
+}
+
+template <typename Tio, int DK, int VS>
+static hipError_t rec_v(const RecArgs& a, hipStream_t s)
+{
+    const int64_t nblk = a.B * a.H * (int64_t)a.nslices;
+    hipLaunchKernelGGL((k_recurrent<Tio, DK, VS>), dim3((unsigned)nblk), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+template <typename Tio, int DK>
+static hipError_t rec_dk(const RecArgs& a, int vs, hipStream_t s)
+{
+    switch (vs) {
+        case 16: return rec_v<Tio, DK, 16>(a, s);
+        case 32: return rec_v<Tio, DK, 32>(a, s);
+        case 64: return rec_v<Tio, DK, 64>(a, s);
+        case 128: return rec_v<Tio, DK, 128>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename Tio>
+static hipError_t rec_t(const RecArgs& a, int dk, int vs, hipStream_t s)
+{
+    switch (dk) {
+        case 16: return rec_dk<Tio, 16>(a, vs, s);
+        case 32: return rec_dk<Tio, 32>(a, vs, s);
+        case 64: return rec_dk<Tio, 64>(a, vs, s);
+        case 128: return rec_dk<Tio, 128>(a, vs, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_recurrent(const RecArgs& a, int dk, int vs, bool bf16, hipStream_t s)
+{
+    return bf16 ? rec_t<__bf16>(a, dk, vs, s) : rec_t<float>(a, dk, vs, s);
+}
+
+}  // namespace gdn2

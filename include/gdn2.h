@@ -1,0 +1,157 @@
+/*
+ * gdn2.h -- C ABI of the Gated DeltaNet-2 token-mixer core for AMD MI355X (gfx950).
+ *
+ * The core computes, per (batch, head), the recurrence on a fp32 matrix state
+ * S of shape (dk, dv) given in the burn-gdn2 0.1.9 README (docs.rs), section
+ * "Architecture":
+ *
+ *     S_t = (I - k_t (b_t * k_t)^T) diag(alpha_t) S_{t-1} + k_t (w_t * v_t)^T
+ *     o_t = q_t^T S_t
+ *
+ * alpha (decay) and b (erase gate) are per key channel, w (write gate) per
+ * value channel.  The output reads the state after the token's update; there
+ * is no query scale and no normalisation inside the core (the layer
+ * L2-normalises q and k before it, README "Architecture" diagram).
+ *
+ * Two forward modes (README intro and "Architecture"): a chunked WY form used
+ * for training-length sequences (chunk size 64, README "Configuration") and a
+ * fused token-by-token recurrent form used for inference with a persistent
+ * state (README "Quick start").  Both compute the same function; only the
+ * rounding differs.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.  Every pointer is device memory owned by the caller.  The library
+ *   never allocates, frees or synchronises, keeps no mutable global state, and
+ *   launches all work on `stream` (a hipStream_t; NULL = the default stream).
+ *   Calls on different streams are independent if their outputs and
+ *   workspaces are disjoint.
+ * Layouts (all C-contiguous, element strides implied by the sizes):
+ *   q, k, alpha, b : [B, T, H, dk]
+ *   v, w, o        : [B, T, H, dv]
+ *   S0/S_in, S_out : [B, H, dk, dv]   fp32, dv fastest
+ * Dtypes.  io_dtype covers q, k, v and o; gate_dtype covers alpha, b, w.
+ *   Supported pairs: (GDN2_F32, GDN2_F32) and (GDN2_BF16, GDN2_F32).  The
+ *   state is always fp32.  bf16 outputs are rounded to nearest even.
+ * Sizes.  B, T, H >= 0 (any zero makes the call a no-op apart from the
+ *   state copy described below); dk in {16, 32, 64, 128}; dv a multiple of
+ *   16 in [16, 256]; chunk == 64 for the chunked mode.
+ * Domain.  alpha in (0, 1].  The chunked mode rescales keys by partial decay
+ *   products inside 16-token blocks, so within any 16 consecutive tokens of
+ *   a chunk the product of alpha in one key channel must stay above ~1e-30
+ *   (fp32 range); the recurrent mode has no such limit.  b, w, q, k, v are
+ *   any finite values (b in (0, 2) is the README's negative-eigenvalue
+ *   option, "b x 2").
+ * Alignment.  Every tensor pointer is 16-byte aligned (the kernels use
+ *   16-byte vector accesses); the workspace is 256-byte aligned.
+ * Aliasing.  Inputs are never written.  Outputs (o, S_out, workspace) must
+ *   not overlap any input or each other, except that S_out may equal S0 /
+ *   S_in exactly (in-place state update).  Any other overlap is an error.
+ * Errors.  Every argument is checked on the host before anything is
+ *   launched; the first failing check returns its code and nothing runs.
+ *   A failed launch returns GDN2_ERR_DEVICE (also when no GPU is present).
+ *   Faults inside a kernel surface on the stream, as for any HIP launch.
+ *   Nothing is printed and no C++ exception crosses this interface.
+ */
+#ifndef GDN2_H_
+#define GDN2_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN2_ABI_VERSION 1
+
+typedef enum {
+    GDN2_OK = 0,
+    GDN2_ERR_NULL = 1,       /* a required pointer is NULL                      */
+    GDN2_ERR_SHAPE = 2,      /* unsupported or inconsistent sizes               */
+    GDN2_ERR_DTYPE = 3,      /* unsupported dtype pair                          */
+    GDN2_ERR_ALIAS = 4,      /* an output overlaps an input or another output   */
+    GDN2_ERR_WORKSPACE = 5,  /* workspace missing or smaller than required      */
+    GDN2_ERR_DEVICE = 6,     /* no usable GPU, or a launch failed               */
+    GDN2_ERR_ALIGN = 7       /* a tensor pointer is not 16-byte aligned         */
+} gdn2_status;
+
+typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1 } gdn2_dtype;
+
+/* Problem description (plain old data; 56 bytes). */
+typedef struct {
+    int64_t B, T, H;         /* batch, tokens per sequence, heads             */
+    int64_t dk, dv;          /* key/query width and value width of a head     */
+    int32_t chunk;           /* chunk length of the chunked mode; must be 64  */
+    int32_t io_dtype;        /* gdn2_dtype of q, k, v, o                      */
+    int32_t gate_dtype;      /* gdn2_dtype of alpha, b, w (GDN2_F32 only)     */
+    int32_t reserved;        /* must be 0                                     */
+} gdn2_problem;
+
+/* ABI version of the loaded library (GDN2_ABI_VERSION). */
+int gdn2_abi_version(void);
+
+/* Static English text for a status code (never NULL). */
+const char* gdn2_status_str(int status);
+
+/*
+ * Bytes of device workspace gdn2_chunk_fwd needs for problem *p (0 if *p is
+ * invalid).  The workspace holds, per (batch, head, chunk), the chunk's WY
+ * factors and decay-scaled operands; it is scratch, its contents are
+ * undefined between calls, and it must be 256-byte aligned.
+ */
+size_t gdn2_chunk_fwd_workspace_size(const gdn2_problem* p);
+
+/*
+ * Chunked forward (README: "chunked WY decomposition", chunk_size 64).
+ * Computes o for all T tokens and, if S_out != NULL, the state after token
+ * T-1.  S0 == NULL means the zero initial state (README "Quick start": the
+ * state starts empty).  T need not be a multiple of 64.
+ *
+ * Runs as two launches on `stream`: gdn2_chunk_prep followed by
+ * gdn2_chunk_state (declared below), which callers may also issue
+ * themselves, e.g. to time them apart.
+ */
+int gdn2_chunk_fwd(const gdn2_problem* p,
+                   const void* q, const void* k, const void* v,
+                   const void* alpha, const void* b, const void* w,
+                   const float* S0, void* o, float* S_out,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * First stage of gdn2_chunk_fwd, fully parallel over (batch, head, chunk):
+ * forms each chunk's cumulative key-axis decay, its erase-interaction matrix
+ * and the WY factors (unit-lower-triangular solve), and writes them with the
+ * decay-scaled q/k operands into `workspace`.  Reads q, k, v, alpha, b, w.
+ */
+int gdn2_chunk_prep(const gdn2_problem* p,
+                    const void* q, const void* k, const void* v,
+                    const void* alpha, const void* b, const void* w,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Second stage of gdn2_chunk_fwd: the sequential pass over chunks that
+ * carries the fp32 state of every (batch, head) and writes o and S_out.
+ * Reads only the workspace written by gdn2_chunk_prep for the same problem,
+ * and S0.
+ */
+int gdn2_chunk_state(const gdn2_problem* p, const float* S0, void* o, float* S_out,
+                     const void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Fused recurrent forward (README: "Fused Recurrent", token-by-token
+ * inference with a persistent state).  Processes the T tokens one after the
+ * other from S_in (NULL = zero state), writes o for each token and, if
+ * S_out != NULL, the final state.  T == 1 is the decode step; passing
+ * S_out == S_in updates the state in place.  p->chunk is ignored.
+ */
+int gdn2_recurrent_step(const gdn2_problem* p,
+                        const void* q, const void* k, const void* v,
+                        const void* alpha, const void* b, const void* w,
+                        const float* S_in, void* o, float* S_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN2_H_ */

@@ -1,0 +1,200 @@
+"""C-ABI contract checks that need no GPU (include/gdn2.h).
+
+The library loads on a host without a GPU (it only links the HIP runtime);
+every argument check runs on the host before any HIP call, so each error path
+is exercised here with fake device addresses that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gated_delta_rule_19_amd as g
+from gated_delta_rule_19_amd import _binding as bnd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn2.h")
+
+OK, NULL, SHAPE, DTYPE, ALIAS, WS, DEVICE, ALIGN = range(8)
+BASE = 0x7f0000000000          # fake, 256-aligned, never dereferenced
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(gdn2_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == sorted(bnd.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", bnd.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT\s+(gdn2_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(g.lib(), name)
+
+
+def test_version_and_status_strings():
+    assert g.abi_version() == 1
+    for code in range(8):
+        assert g.status_str(code).startswith(bnd._STATUS[code])
+    assert "unknown" in g.status_str(99)
+
+
+def test_problem_struct_layout():
+    assert ctypes.sizeof(bnd.Problem) == 56
+
+
+class Call:
+    """Lay out fake, disjoint device buffers for one problem."""
+
+    def __init__(self, B=2, T=100, H=3, dk=64, dv=32, io=1, gate=0, chunk=64):
+        self.p = bnd.Problem(B, T, H, dk, dv, chunk, io, gate, 0)
+        es = 2 if io == 1 else 4
+        rows = B * T * H
+        sizes = dict(q=rows * dk * es, k=rows * dk * es, v=rows * dv * es, alpha=rows * dk * 4,
+                     b=rows * dk * 4, w=rows * dv * 4, S0=B * H * dk * dv * 4, o=rows * dv * es,
+                     S_out=B * H * dk * dv * 4)
+        sizes["ws"] = g.lib().gdn2_chunk_fwd_workspace_size(ctypes.byref(self.p)) or 256
+        self.size = sizes
+        addr = BASE
+        self.ptr = {}
+        for name, n in sizes.items():
+            self.ptr[name] = addr
+            addr += (n + 4095) // 4096 * 4096 + 4096
+
+    def fwd(self, **over):
+        a = dict(self.ptr)
+        a.update(over)
+        P = lambda x: None if x is None else ctypes.c_void_p(x)
+        wsb = over.pop("ws_bytes", None) if "ws_bytes" in over else self.size["ws"]
+        return g.lib().gdn2_chunk_fwd(ctypes.byref(self.p), *(P(a[n]) for n in
+                                      ("q", "k", "v", "alpha", "b", "w", "S0", "o", "S_out")),
+                                      P(a["ws"]), wsb, None)
+
+    def rec(self, **over):
+        a = dict(self.ptr)
+        a.update(over)
+        P = lambda x: None if x is None else ctypes.c_void_p(x)
+        return g.lib().gdn2_recurrent_step(ctypes.byref(self.p), *(P(a[n]) for n in
+                                           ("q", "k", "v", "alpha", "b", "w", "S0", "o", "S_out")), None)
+
+
+def test_valid_call_reaches_the_device_check():
+    # on a host with no GPU the first HIP call fails -> GDN2_ERR_DEVICE
+    c = Call()
+    assert c.fwd() == DEVICE
+    assert c.rec() == DEVICE
+
+
+def test_workspace_size():
+    p = bnd.problem(4, 2048, 16, 128, 128, __import__("torch").bfloat16)
+    n = g.lib().gdn2_chunk_fwd_workspace_size(ctypes.byref(p))
+    # one 256-aligned block per (batch, head, chunk); bf16 block = 74,240 bytes at dk = dv = 128
+    assert n == 4 * 16 * 32 * 74240
+    assert g.lib().gdn2_chunk_fwd_workspace_size(None) == 0
+    bad = bnd.Problem(1, 1, 1, 100, 16, 64, 1, 0, 0)
+    assert g.lib().gdn2_chunk_fwd_workspace_size(ctypes.byref(bad)) == 0
+
+
+@pytest.mark.parametrize("field,value", [("dk", 48), ("dk", 256), ("dv", 8), ("dv", 24), ("dv", 272),
+                                         ("B", -1), ("T", -1), ("chunk", 32), ("reserved", 1)])
+def test_shape_errors(field, value):
+    c = Call()
+    setattr(c.p, field, value)
+    if field == "chunk":
+        assert c.fwd() == SHAPE and c.rec() == DEVICE   # the recurrent mode ignores chunk
+    else:
+        assert c.fwd() == SHAPE and c.rec() == SHAPE
+
+
+@pytest.mark.parametrize("io,gate", [(0, 1), (1, 1), (2, 0), (1, 5)])
+def test_dtype_errors(io, gate):
+    c = Call(io=io, gate=gate)
+    assert c.fwd() == DTYPE and c.rec() == DTYPE
+
+
+def test_null_errors():
+    c = Call()
+    assert g.lib().gdn2_chunk_fwd(None, *([None] * 10), 0, None) == NULL
+    for name in ("q", "k", "v", "alpha", "b", "w", "o"):
+        assert c.fwd(**{name: None}) == NULL, name
+        assert c.rec(**{name: None}) == NULL, name
+    # S0 and S_out are optional
+    assert c.fwd(S0=None, S_out=None) == DEVICE
+    assert c.rec(S0=None) == DEVICE
+
+
+def test_empty_problems_need_no_pointers_and_no_device():
+    for B, T, H in ((0, 10, 2), (2, 10, 0)):
+        c = Call(B=B, T=T, H=H)
+        none = {n: None for n in ("q", "k", "v", "alpha", "b", "w", "S0", "o", "S_out", "ws")}
+        assert c.fwd(**none, ws_bytes=0) == OK
+        assert c.rec(**none) == OK
+    # T == 0 with the state updated in place is a no-op
+    c = Call(T=0)
+    assert c.rec(q=None, k=None, v=None, alpha=None, b=None, w=None, o=None, S_out=c.ptr["S0"]) == OK
+    assert c.fwd(q=None, k=None, v=None, alpha=None, b=None, w=None, o=None, ws=None, ws_bytes=0,
+                 S_out=c.ptr["S0"]) == OK
+
+
+def test_workspace_errors():
+    c = Call()
+    assert c.fwd(ws=None) == WS
+    assert c.fwd(ws_bytes=c.size["ws"] - 1) == WS
+    assert c.fwd(ws=c.ptr["ws"] + 16) == WS        # not 256-byte aligned
+
+
+def test_alias_errors():
+    c = Call()
+    # an output overlapping an input
+    assert c.fwd(o=c.ptr["q"] + 64) == ALIAS
+    assert c.rec(o=c.ptr["v"]) == ALIAS
+    assert c.fwd(S_out=c.ptr["alpha"]) == ALIAS
+    assert c.fwd(ws=c.ptr["w"]) == ALIAS
+    # outputs overlapping each other
+    assert c.fwd(S_out=c.ptr["o"]) == ALIAS
+    assert c.fwd(ws=c.ptr["o"]) == ALIAS
+    # the state may be updated in place only with identical pointers
+    assert c.fwd(S_out=c.ptr["S0"]) == DEVICE
+    assert c.rec(S_out=c.ptr["S0"]) == DEVICE
+    assert c.fwd(S_out=c.ptr["S0"] + 256) == ALIAS
+    assert c.rec(S_out=c.ptr["S0"] + 4) == ALIAS
+
+
+def test_alignment_errors():
+    c = Call()
+    for name in ("q", "k", "v", "alpha", "b", "w", "o", "S_out", "S0"):
+        assert c.fwd(**{name: c.ptr[name] + 8}) == ALIGN, name
+        assert c.rec(**{name: c.ptr[name] + 4}) == ALIGN, name
+
+
+def test_stage_entry_points_validate():
+    c = Call()
+    P = ctypes.c_void_p
+    L = g.lib()
+    args = [P(c.ptr[n]) for n in ("q", "k", "v", "alpha", "b", "w")]
+    assert L.gdn2_chunk_prep(ctypes.byref(c.p), *args, P(c.ptr["ws"]), c.size["ws"], None) == DEVICE
+    assert L.gdn2_chunk_prep(ctypes.byref(c.p), *args, None, c.size["ws"], None) == WS
+    assert L.gdn2_chunk_prep(ctypes.byref(c.p), *args, P(c.ptr["q"]), c.size["ws"], None) == ALIAS
+    assert L.gdn2_chunk_state(ctypes.byref(c.p), P(c.ptr["S0"]), P(c.ptr["o"]), P(c.ptr["S_out"]),
+                              P(c.ptr["ws"]), c.size["ws"], None) == DEVICE
+    assert L.gdn2_chunk_state(ctypes.byref(c.p), None, None, None, P(c.ptr["ws"]), c.size["ws"], None) == NULL
+    assert L.gdn2_chunk_state(ctypes.byref(c.p), None, P(c.ptr["ws"]), None, P(c.ptr["ws"]),
+                              c.size["ws"], None) == ALIAS
+
+
+def test_binding_rejects_cpu_tensors_and_bad_shapes():
+    import torch
+    q = torch.zeros(1, 4, 1, 16)
+    with pytest.raises(ValueError):
+        g.recurrent_step(q, q, torch.zeros(1, 4, 1, 16), q, q, torch.zeros(1, 4, 1, 16))
+    with pytest.raises(ValueError):
+        g.chunk_fwd(q, q, torch.zeros(1, 4, 2, 16), q, q, torch.zeros(1, 4, 2, 16))
+    with pytest.raises(TypeError):
+        g.chunk_fwd(q.double(), q.double(), torch.zeros(1, 4, 1, 16).double(), q, q, torch.zeros(1, 4, 1, 16))
