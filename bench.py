@@ -1,0 +1,329 @@
+"""Benchmark of the GDN-2 token-mixer hot path on one MI355X.
+
+One step = one chunked forward of the B4 H16 T2048 d128 workload (bf16 q/k/v,
+fp32 gates and state; returns o and the final state) followed by one decode
+step of the B256 H16 d128 workload (fp32 state updated in place).  Inputs are
+seeded synthetic tensors resident in HBM before timing; three input sets (and
+three decode states) are rotated so that consecutive steps never find their
+data in the 256 MB Infinity Cache.
+
+Prints ONE JSON line.  `value` is the chunked forward's throughput in tokens/s
+(8192 tokens per call divided by the call's GPU time, from HIP events on the
+launch stream); the decode step's HBM rate is reported beside it.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --copy-calibration      # plain 1 GiB copies, for counter scaling
+    python bench.py --pmc-summary DIR ...   # fold rocprofv3 counter CSVs into profiles/
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0            # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0         # MI355X dense bf16 matrix, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+KERNEL_SOURCES = ["gated_delta_rule_19_amd/csrc/gdn2_chunk.hip", "gated_delta_rule_19_amd/csrc/gdn2_recurrent.hip",
+                  "gated_delta_rule_19_amd/csrc/gdn2_device.hpp", "gated_delta_rule_19_amd/csrc/gdn2_layout.hpp"]
+KERNEL_NAMES = {"prep": "k_chunk_prep", "state": "k_chunk_state", "decode": "k_recurrent"}
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work (what the method must move / compute; workspace excluded)
+# ---------------------------------------------------------------------------
+def chunk_bytes_per_ht(dk, dv, io=2, gate=4):
+    """q, k, v read + alpha, b, w read + o written, per head-token."""
+    return io * (2 * dk + dv) + gate * (2 * dk + dv) + io * dv
+
+
+def chunk_flops_per_ht(dk, dv, C=64):
+    """A, P, W (3 * 2C dk) + U, P.Delta (2 * 2C dv) + W S, Qh S, Ktil^T Delta (3 * 2 dk dv) + solve."""
+    return 3 * 2 * C * dk + 2 * 2 * C * dv + 3 * 2 * dk * dv + 2 * C * C / 3
+
+
+def decode_bytes(B, H, dk, dv, io=2, gate=4):
+    """state read + written (fp32) + q, k, v, alpha, b, w read + o written."""
+    return B * H * (2 * 4 * dk * dv + io * (2 * dk + dv) + gate * (2 * dk + dv) + io * dv)
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sets", type=int, default=3, help="rotated input sets (>= 3 defeats the 256 MB MALL)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-chains", type=int, default=0,
+                    help="(batch, head) chains in the oracle sample; 0 = the whole workload")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--pmc-summary", metavar="DIR", default=None)
+    ap.add_argument("--copy-pmc", metavar="DIR", default=None)
+    return ap.parse_args(argv)
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": ms,
+                      "GBps": 2 * n / ms / 1e6}))
+
+
+def _read_counter_csvs(d):
+    """Sum counter values per (dispatch, kernel, counter) from rocprofv3 CSV output under d."""
+    import csv
+    rows = []
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection*.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                rows.append(r)
+    per = {}
+    for r in rows:
+        name = r.get("Kernel_Name") or r.get("Kernel-Name") or ""
+        ctr = r.get("Counter_Name") or r.get("Counter-Name")
+        val = float(r.get("Counter_Value") or r.get("Counter-Value") or 0.0)
+        disp = r.get("Dispatch_Id") or r.get("Dispatch-Id") or r.get("Correlation_Id")
+        per.setdefault((disp, name, ctr), 0.0)
+        per[(disp, name, ctr)] += val
+    return per
+
+
+def pmc_summary(dirs, copy_dirs):
+    """Fold FETCH_SIZE / WRITE_SIZE runs into profiles/pmc_traffic.json (KiB per dispatch, averaged)."""
+    out = {"kernel_sha": kernel_sha(), "kernels": {}, "copy": {}}
+
+    def avg_for(per, match, ctr):
+        vals = [v for (disp, name, c), v in per.items() if c == ctr and match(name)]
+        return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+
+    for d in dirs:
+        per = _read_counter_csvs(d)
+        for key, kname in KERNEL_NAMES.items():
+            for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+                v, n = avg_for(per, lambda s, kname=kname: kname in s, ctr)
+                if v is not None:
+                    out["kernels"].setdefault(key, {})[ctr + "_KiB"] = v
+                    out["kernels"][key][ctr + "_dispatches"] = n
+    for d in copy_dirs:
+        per = _read_counter_csvs(d)
+        for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+            # torch's same-dtype device copy is the runtime's blit kernel; median over its dispatches
+            vals = sorted(v for (disp, name, c), v in per.items() if c == ctr and "copyBuffer" in name)
+            if vals:
+                out["copy"][ctr + "_KiB"] = vals[len(vals) // 2]
+    n_kib = (1 << 30) / 1024.0
+    f = out["copy"].get("FETCH_SIZE_KiB")
+    w = out["copy"].get("WRITE_SIZE_KiB")
+    out["copy"]["fetch_factor"] = None if not f else f / n_kib
+    out["copy"]["write_factor"] = None if not w else w / n_kib
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1, sort_keys=True)
+    print(json.dumps(out))
+
+
+def load_traffic(key):
+    """HBM bytes per launch of kernel `key` from the committed counter summary, or None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha") != kernel_sha():
+        return None
+    k = t.get("kernels", {}).get(key, {})
+    c = t.get("copy", {})
+    if k.get("FETCH_SIZE_KiB") is None or k.get("WRITE_SIZE_KiB") is None:
+        return None
+    ff, wf = c.get("fetch_factor"), c.get("write_factor")
+    if not ff or not wf:
+        return None
+    return 1024.0 * (k["FETCH_SIZE_KiB"] / ff + k["WRITE_SIZE_KiB"] / wf)
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "every (batch, head) chain is independent, so more GPUs would each run their own share "
+              "without communication -- see the sharding notes in the design document.", file=sys.stderr)
+        return 2
+    if args.copy_calibration:
+        return copy_calibration()
+    if args.pmc_summary:
+        dirs = args.pmc_summary.split(",")
+        copy_dirs = args.copy_pmc.split(",") if args.copy_pmc else []
+        return pmc_summary(dirs, copy_dirs)
+
+    import torch
+
+    import gated_delta_rule_19_amd as g
+    from gated_delta_rule_19_amd import inputs
+
+    dev = torch.device("cuda:0")
+    wl_c = inputs.WORKLOADS[1]
+    wl_d = inputs.WORKLOADS[2]
+    B, T, H, dk, dv = wl_c.B, wl_c.T, wl_c.H, wl_c.dk, wl_c.dv
+    sets = [inputs.make(wl_c, seed=100 + i, device=dev) for i in range(args.sets)]
+    dsets = [inputs.make(wl_d, seed=200 + i, device=dev) for i in range(args.sets)]
+    prob = g.problem(B, T, H, dk, dv, wl_c.io_dtype)
+    ws = g.alloc_workspace(g.chunk_fwd_workspace_size(B, T, H, dk, dv, wl_c.io_dtype), dev)
+    outs = [torch.empty_like(s["v"]) for s in sets]
+    states = [torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev) for _ in sets]
+    douts = [torch.empty_like(s["v"]) for s in dsets]
+    A = lambda s: (s["q"], s["k"], s["v"], s["alpha"], s["b"], s["w"])
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        s, d = i % len(sets), i % len(dsets)
+        if ev is not None:
+            ev[0].record()
+        g.chunk_prep(*A(sets[s]), ws)
+        if ev is not None:
+            ev[1].record()
+        g.chunk_state(prob, ws, outs[s], sets[s]["S0"], states[s])
+        if ev is not None:
+            ev[2].record()
+        g.recurrent_step(*A(dsets[d]), dsets[d]["S0"], o=douts[d], inplace=True)
+        if ev is not None:
+            ev[3].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / max(args.steps, 1)
+    prep_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    state_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    dec_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    chunk_ms = prep_ms + state_ms
+
+    ht = B * T * H
+    tokens = B * T
+    bpht = chunk_bytes_per_ht(dk, dv)
+    alg_chunk = bpht * ht + B * H * dk * dv * 4                   # + final state written
+    alg_prep = (bpht - 2 * dv) * ht                               # inputs read
+    alg_state = 2 * dv * ht + B * H * dk * dv * 4                 # o + final state written
+    alg_dec = decode_bytes(wl_d.B, wl_d.H, wl_d.dk, wl_d.dv)
+    flops = chunk_flops_per_ht(dk, dv) * ht
+    gbps = lambda byts, ms: byts / (ms * 1e-3) / 1e9
+
+    kern = {
+        "prep": dict(ms=prep_ms, alg=alg_prep),
+        "state": dict(ms=state_ms, alg=alg_state),
+        "decode": dict(ms=dec_ms, alg=alg_dec),
+    }
+    dom = max(kern, key=lambda k_: kern[k_]["ms"])
+
+    def roof(key):
+        k_ = kern[key]
+        ach = gbps(k_["alg"], k_["ms"])
+        tr = load_traffic(key)
+        return {"kernel": KERNEL_NAMES[key], "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4),
+                "traffic": None if tr is None else round(tr), "alg_bytes": int(k_["alg"]),
+                "us_per_launch": round(k_["ms"] * 1e3, 2)}
+
+    chunk_gbps = gbps(alg_chunk, chunk_ms)
+    result = {
+        "metric": "chunk-fwd tokens/s (B4 H16 T2048 d128) + decode-step HBM GB/s; % roofline",
+        "value": round(tokens / (chunk_ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "chunk fwd B4 H16 T2048 dk=dv=128 (bf16 q/k/v, fp32 gates+state) "
+                               "+ decode step B256 H16 d128 (fp32 state in place)",
+                   "global_batch": B, "seq_len": T, "heads": H, "dk": dk, "dv": dv, "chunk": 64,
+                   "parallelism": "single GPU", "rotated_input_sets": args.sets},
+        "roofline": roof(dom),
+        "chunk_fwd": {"us": round(chunk_ms * 1e3, 2), "prep_us": round(prep_ms * 1e3, 2),
+                      "state_us": round(state_ms * 1e3, 2), "alg_GBps": round(chunk_gbps, 1),
+                      "frac_hbm_roofline": round(chunk_gbps / PEAK_HBM_GBPS, 4),
+                      "useful_TFLOPs": round(flops / (chunk_ms * 1e-3) / 1e12, 2),
+                      "frac_bf16_mfma_peak": round(flops / (chunk_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                      "roofline_prep": roof("prep"), "roofline_state": roof("state")},
+        "decode": {"us": round(dec_ms * 1e3, 2), "GBps": round(gbps(alg_dec, dec_ms), 1),
+                   "frac_hbm_peak": round(gbps(alg_dec, dec_ms) / PEAK_HBM_GBPS, 4),
+                   "roofline": roof("decode")},
+    }
+    ok = bool(torch.isfinite(outs[0].float()).all() and torch.isfinite(states[0]).all()
+              and torch.isfinite(douts[0].float()).all())
+    result["outputs_finite"] = ok
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(sets[0], args.cpu_chains, B, T, H, dk, dv)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def cpu_baseline(inp, chains, B, T, H, dk, dv):
+    """The fp64 C oracle on the first `chains` (batch, head) chains (0 = all), all T tokens,
+    timed on the host cores; tokens/s scaled by the share of chains run."""
+    import torch
+
+    from oracle import c_oracle
+    nch = B * H if chains <= 0 else max(1, min(chains, B * H))
+    nb = (nch + H - 1) // H
+    f = lambda x: x[0:nb].detach().to("cpu", torch.float32).contiguous().numpy()
+    arrs = [f(inp[k_]) for k_ in ("q", "k", "v", "alpha", "b", "w")]
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = min(cores, 16)
+    t0 = time.perf_counter()
+    c_oracle.recurrent(*arrs, None, nthreads=cores, col_block=16)
+    dt = time.perf_counter() - t0
+    frac = nb * H / float(B * H)
+    tok_s = B * T / (dt / frac)
+    return {"value": round(tok_s, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 C oracle (OpenMP over head x 16-column blocks) on {nb * H} of {B * H} "
+                      f"(batch, head) chains x {T} tokens of the same inputs: {dt:.2f} s",
+            "seconds": round(dt, 3)}
+
+
+if __name__ == "__main__":
+    sys.exit(main())
