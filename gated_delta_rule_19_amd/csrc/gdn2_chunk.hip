@@ -78,13 +78,13 @@ constexpr unsigned kPairI = pack2(kPairIv, 10), kPairJ = pack2(kPairJv, 10);
 constexpr unsigned kUpperI = pack2(kUpperIv, 6), kUpperJ = pack2(kUpperJv, 6);
 __device__ inline int unpack2(unsigned p, int i) { return (int)((p >> (2 * i)) & 3u); }
 
-template <typename Tio, int DK>
+// NUI = (token, 4-column) value items per thread: 64 * dv / 4 <= 256 * NUI
+template <typename Tio, int DK, int NUI>
 __global__ __launch_bounds__(kThreads, 2) void k_chunk_prep(PrepArgs a)
 {
     using IO = Io<Tio>;
     using SM = PrepSmem<Tio, DK>;
     constexpr int EPL = SM::EPL, KB = SM::KB, KPAD = SM::KPAD, RS = SM::RS, TS = SM::TS, FS = SM::FS;
-    constexpr int ITEMS = (DK * 4 + kThreads - 1) / kThreads;
     constexpr WsLayout LY = ws_layout(DK, 0, sizeof(Tio), KB);
 
     __shared__ __attribute__((aligned(16))) char smem[SM::BYTES];
@@ -120,23 +120,81 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_prep(PrepArgs a)
     float* gaml_out = reinterpret_cast<float*>(blk + LY.gaml);
     Tio* uwyt_out = reinterpret_cast<Tio*>(blk + LY.uwyt);
 
-    // ---- 1a. running decay products inside each 16-token block -------------
-    float gpre[ITEMS][16];
+    typedef typename IO::frag frag;
+    typedef typename IO::pair pair2;
+
+    // ---- 0. every global load of the kernel, before any global store --------
+    // One vector-memory counter tracks loads and stores alike, so a load
+    // issued after a store would also wait for that store to complete.  Loads
+    // are unconditional (rows past the sequence end are clamped to its last
+    // row and replaced by identity tokens afterwards): a load under a branch
+    // would be waited for at the join.  16-byte accesses keep the count of
+    // loads per lane under the 63 the counter can track.
+    // Key-axis item = (4 channels c0..c0+3, 8-token group rg); block p = rg/2.
+    constexpr int NQ = DK / 4;
+    const bool kact = tid < 2 * DK;
+    const int cq = tid % NQ, rg = (tid / NQ) & 7, p = rg >> 1, half = rg & 1, c0 = 4 * cq;
+    f32x4 al[8], bt[8];
+    typename IO::vec4 kk[8], qq[8];
 #pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-        const int item = tid + it * kThreads;
-        if (item < DK * 4) {
-            const int c = item % DK, p = item / DK;
-            float run = 1.f;
+    for (int i = 0; i < 8; ++i) {
+        const int r = 8 * rg + i;
+        const int64_t off = (row0 + (r < L ? r : L - 1) * H) * DK + c0;
+        al[i] = *reinterpret_cast<const f32x4*>(a.alpha + off);
+        bt[i] = *reinterpret_cast<const f32x4*>(a.b + off);
+        kk[i] = *reinterpret_cast<const typename IO::vec4*>(k + off);
+        qq[i] = *reinterpret_cast<const typename IO::vec4*>(q + off);
+    }
+    // value-axis item = (token s, 4 columns): u = w * v
+    constexpr int NVQ_MAX = NUI;
+    f32x4 wr[NVQ_MAX];
+    typename IO::vec4 vr[NVQ_MAX];
+    const int nvq = a.dv / 4;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int r = 16 * p + i;
-                const float al = (r < L) ? a.alpha[(row0 + r * H) * DK + c] : 1.f;
-                run *= al;
-                gpre[it][i] = run;
-            }
-            Zs[p * DK + c] = run;
+    for (int m = 0; m < NVQ_MAX; ++m) {
+        const int u = tid + m * kThreads;
+        const int jq = u % nvq, s = u / nvq;
+        const int64_t off = (row0 + (s < L ? s : L - 1) * H) * a.dv + 4 * jq;
+        wr[m] = *reinterpret_cast<const f32x4*>(a.w + off);
+        vr[m] = *reinterpret_cast<const typename IO::vec4*>(v + off);
+    }
+    f32x4 uu[NVQ_MAX];
+#pragma unroll
+    for (int m = 0; m < NVQ_MAX; ++m) {
+        const int s = (tid + m * kThreads) / nvq;
+        uu[m] = (s < L && s < 64) ? wr[m] * IO::unpack4(vr[m]) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if (!(kact && 8 * rg + i < L)) {
+            al[i] = f32x4{1.f, 1.f, 1.f, 1.f};
+            bt[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            kk[i] = IO::pack4(f32x4{0.f, 0.f, 0.f, 0.f});
+            qq[i] = kk[i];
         }
+    }
+
+    // ---- 1a. running decay products inside each 16-token block -------------
+    // g[i] = prod of alpha from the start of the 16-token block to row i; the
+    // second 8-token half multiplies in the first half's total (lane +- NQ).
+    f32x4 g[8];
+    f32x4 zblk;
+    {
+        f32x4 run = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            run *= al[i];
+            g[i] = run;
+        }
+        f32x4 other;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) other[e] = __shfl_xor(run[e], NQ, 64);
+        if (half) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) g[i] *= other;
+        }
+        zblk = run * other;
+        if (kact && half == 0) *reinterpret_cast<f32x4*>(Zs + p * DK + c0) = zblk;
     }
     if constexpr (KPAD > DK) {   // zero the K padding of the operand arrays
         for (int e = tid; e < 64 * (KPAD - DK); e += kThreads) {
@@ -154,55 +212,55 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_prep(PrepArgs a)
     __syncthreads();
 
     // ---- 1b. block factors, decay-scaled operands ---------------------------
-    for (int c = tid; c < DK; c += kThreads) {
-        const float z0 = Zs[c], z1 = Zs[DK + c], z2 = Zs[2 * DK + c], z3 = Zs[3 * DK + c];
-        Fs[0 * KPAD + c] = z0;            // pair (1,0)
-        Fs[1 * KPAD + c] = z1;            // pair (2,1)
-        Fs[2 * KPAD + c] = z2;            // pair (3,2)
-        Fs[3 * KPAD + c] = z0 * z1;       // pair (2,0)
-        Fs[4 * KPAD + c] = z1 * z2;       // pair (3,1)
-        Fs[5 * KPAD + c] = z0 * z1 * z2;  // pair (3,0)
-        gaml_out[c] = z0 * z1 * z2 * z3;
-    }
+    if (kact) {
+        f32x4 z[4];
 #pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-        const int item = tid + it * kThreads;
-        if (item < DK * 4) {
-            const int c = item % DK, p = item / DK;
-            float pre = 1.f, post = 1.f;
+        for (int K = 0; K < 4; ++K) z[K] = *reinterpret_cast<const f32x4*>(Zs + K * DK + c0);
+        if (rg == 0) {
+            *reinterpret_cast<f32x4*>(Fs + 0 * KPAD + c0) = z[0];                 // pair (1,0)
+            *reinterpret_cast<f32x4*>(Fs + 1 * KPAD + c0) = z[1];                 // pair (2,1)
+            *reinterpret_cast<f32x4*>(Fs + 2 * KPAD + c0) = z[2];                 // pair (3,2)
+            *reinterpret_cast<f32x4*>(Fs + 3 * KPAD + c0) = z[0] * z[1];          // pair (2,0)
+            *reinterpret_cast<f32x4*>(Fs + 4 * KPAD + c0) = z[1] * z[2];          // pair (3,1)
+            *reinterpret_cast<f32x4*>(Fs + 5 * KPAD + c0) = z[0] * z[1] * z[2];   // pair (3,0)
+            *reinterpret_cast<f32x4*>(gaml_out + c0) = z[0] * z[1] * z[2] * z[3];
+        }
+        f32x4 pre = {1.f, 1.f, 1.f, 1.f}, post = pre;
 #pragma unroll
-            for (int K = 0; K < 4; ++K) {
-                const float z = Zs[K * DK + c];
-                if (K < p) pre *= z;
-                if (K > p) post *= z;
+        for (int K = 0; K < 4; ++K) {
+            if (K < p) pre *= z[K];
+            if (K > p) post *= z[K];
+        }
+        Tio eh[4][8], kt[4][8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 8 * rg + i;
+            const f32x4 kv = IO::unpack4(kk[i]), qv = IO::unpack4(qq[i]);
+            const f32x4 ig = {fast_rcp(g[i][0]), fast_rcp(g[i][1]), fast_rcp(g[i][2]), fast_rcp(g[i][3])};
+            const f32x4 xe = bt[i] * kv * g[i], xq = qv * g[i];
+            st_vec4(Xe + r * RS + c0, xe);
+            st_vec4(Xq + r * RS + c0, xq);
+            st_vec4(Yd + r * RS + c0, kv * ig);
+            st_vec4(qh_out + r * KPAD + c0, xq * pre);
+            const f32x4 ehv = xe * pre, ktv = kv * (zblk * ig) * post;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                eh[e][i] = IO::from_f(ehv[e]);
+                kt[e][i] = IO::from_f(ktv[e]);
             }
-            const float zend = gpre[it][15];
-            Tio kt[16];
+        }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int r = 16 * p + i;
-                const bool valid = r < L;
-                const int64_t off = (row0 + r * H) * DK + c;
-                const float kv = valid ? IO::to_f(k[off]) : 0.f;
-                const float qv = valid ? IO::to_f(q[off]) : 0.f;
-                const float bv = valid ? a.b[off] : 0.f;
-                const float g = gpre[it][i];
-                const float ig = fast_rcp(g);
-                const float e = bv * kv;
-                Xe[r * RS + c] = IO::from_f(e * g);
-                Xq[r * RS + c] = IO::from_f(qv * g);
-                Yd[r * RS + c] = IO::from_f(kv * ig);
-                EhT[c * TS + r] = IO::from_f(e * g * pre);
-                qh_out[r * KPAD + c] = IO::from_f(qv * g * pre);
-                kt[i] = IO::from_f(kv * (zend * ig) * post);
-            }
-            typedef typename IO::frag frag;
+        for (int e = 0; e < 4; ++e) {
 #pragma unroll
-            for (int i = 0; i < 16; i += EPL) {
-                frag f;
+            for (int i = 0; i < 8; i += EPL) {
+                frag f0, f1;
 #pragma unroll
-                for (int e2 = 0; e2 < EPL; ++e2) f[e2] = kt[i + e2];
-                *reinterpret_cast<frag*>(ktt_out + c * 64 + 16 * p + i) = f;
+                for (int e2 = 0; e2 < EPL; ++e2) {
+                    f0[e2] = eh[e][i + e2];
+                    f1[e2] = kt[e][i + e2];
+                }
+                *reinterpret_cast<frag*>(EhT + (c0 + e) * TS + 8 * rg + i) = f0;
+                *reinterpret_cast<frag*>(ktt_out + (c0 + e) * 64 + 8 * rg + i) = f1;
             }
         }
     }
@@ -331,14 +389,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_prep(PrepArgs a)
     // ---- 5. U = T (w * v), stored transposed, in column blocks of 64 --------
     for (int j0 = 0; j0 < a.dv; j0 += 64) {
         const int nj = (a.dv - j0) < 64 ? (a.dv - j0) : 64;
-        for (int e = tid; e < 64 * nj; e += kThreads) {
-            const int s = e / nj, jj = e - s * nj;
-            float u = 0.f;
-            if (s < L) {
-                const int64_t off = (row0 + s * H) * a.dv + j0 + jj;
-                u = a.w[off] * IO::to_f(v[off]);
+#pragma unroll
+        for (int m = 0; m < NVQ_MAX; ++m) {
+            const int u = tid + m * kThreads;
+            const int j = 4 * (u % nvq), s = u / nvq;
+            if (s < 64 && j >= j0 && j < j0 + nj) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) UT[(j - j0 + e) * TS + s] = IO::from_f(uu[m][e]);
             }
-            UT[jj * TS + s] = IO::from_f(u);
         }
         __syncthreads();
         for (int jt = 0; jt < nj / 16; ++jt) {
@@ -346,7 +404,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_prep(PrepArgs a)
 #pragma unroll
             for (int kb = 0; kb < 64 / KB; ++kb) {
                 if (kb * KB <= 16 * wave + 15) {
-                    const typename IO::frag fu = ld_frag(UT + (16 * jt + l16) * TS + kb * KB + grp * EPL);
+                    const frag fu = ld_frag(UT + (16 * jt + l16) * TS + kb * KB + grp * EPL);
                     acc = IO::mma(acc, tf[kb], fu);
                 }
             }
@@ -436,7 +494,14 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(StateArgs a)
     }
     __syncthreads();
 
-    for (int n = 0; n < a.nt; ++n) {
+    // operands of one chunk, loaded one chunk ahead (registers)
+    typedef typename IO::frag frag;
+    struct Ops {
+        frag w[NKX], q[NKX], p[NKT], k[SPW][NKT];
+        typename IO::vec4 u[NCT];
+        f32x4 gl[SPW];
+    };
+    auto load_ops = [&](int n, Ops& op) {
         const char* blk = static_cast<const char*>(a.ws) + (chain * a.nt + n) * a.ws_block;
         const Tio* Qh = reinterpret_cast<const Tio*>(blk + LY.qh);
         const Tio* Ww = reinterpret_cast<const Tio*>(blk + LY.wwy);
@@ -444,6 +509,37 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(StateArgs a)
         const Tio* Pm = reinterpret_cast<const Tio*>(blk + LY.p);
         const float* Gl = reinterpret_cast<const float*>(blk + LY.gaml);
         const Tio* Ut = reinterpret_cast<const Tio*>(blk + LY.uwyt);
+#pragma unroll
+        for (int kb = 0; kb < NKX; ++kb) {
+            op.w[kb] = ld_frag(Ww + (16 * wave + l16) * KPAD + kb * KB + grp * EPL);
+            op.q[kb] = ld_frag(Qh + (16 * wave + l16) * KPAD + kb * KB + grp * EPL);
+        }
+        // unconditional loads (rows of idle tiles clamped into range) keep the
+        // compiler from waiting at branch joins
+#pragma unroll
+        for (int kb = 0; kb < NKT; ++kb) {
+            op.p[kb] = ld_frag(Pm + (16 * wave + l16) * 64 + kb * KB + grp * EPL);
+#pragma unroll
+            for (int i = 0; i < SPW; ++i) {
+                const int rt = (wave * SPW + i) < SRT ? (wave * SPW + i) : SRT - 1;
+                op.k[i][kb] = ld_frag(Kt + (16 * rt + l16) * 64 + kb * KB + grp * EPL);
+            }
+        }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+            op.u[ct] = *reinterpret_cast<const typename IO::vec4*>(Ut + (int64_t)(j0 + 16 * ct + l16) * 64 + 16 * wave + 4 * grp);
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const int rt = (wave * SPW + i) < SRT ? (wave * SPW + i) : SRT - 1;
+            op.gl[i] = *reinterpret_cast<const f32x4*>(Gl + 16 * rt + 4 * grp);
+        }
+    };
+
+    // one chunk: prefetch chunk n+1 into `nx`, compute chunk n from `cu`
+    auto step = [&](int n, const Ops& cu, Ops& nx) {
+        // unconditional (the last chunk reloads itself): a prefetch under a
+        // branch makes the compiler drain every outstanding access first
+        load_ops(n + 1 < a.nt ? n + 1 : n, nx);
         const Tio* Sb = SbT[n & 1];
         Tio* Dt = DT[n & 1];
 
@@ -457,21 +553,17 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(StateArgs a)
 #pragma unroll
         for (int kb = 0; kb < NKX; ++kb) {
             const int ko = kb * KB + grp * EPL;
-            const typename IO::frag fw = ld_frag(Ww + (16 * wave + l16) * KPAD + ko);
-            const typename IO::frag fq = ld_frag(Qh + (16 * wave + l16) * KPAD + ko);
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
-                const typename IO::frag fs = ld_frag(Sb + (16 * ct + l16) * SRS + ko);
-                accW[ct] = IO::mma(accW[ct], fw, fs);
-                accQ[ct] = IO::mma(accQ[ct], fq, fs);
+                const frag fs = ld_frag(Sb + (16 * ct + l16) * SRS + ko);
+                accW[ct] = IO::mma(accW[ct], cu.w[kb], fs);
+                accQ[ct] = IO::mma(accQ[ct], cu.q[kb], fs);
             }
         }
         // Delta = U - X_W (rows 16*wave + 4*grp + i, column 16*ct + l16)
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            const f32x4 u = ld_vec4(Ut + (int64_t)(j0 + 16 * ct + l16) * 64 + 16 * wave + 4 * grp);
-            st_vec4(Dt + (16 * ct + l16) * DTS + 16 * wave + 4 * grp, u - accW[ct]);
-        }
+        for (int ct = 0; ct < NCT; ++ct)
+            st_vec4(Dt + (16 * ct + l16) * DTS + 16 * wave + 4 * grp, IO::unpack4(cu.u[ct]) - accW[ct]);
         __syncthreads();
 
         // O = X_Q + P Delta
@@ -479,14 +571,36 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(StateArgs a)
         for (int kb = 0; kb < NKT; ++kb) {
             if (kb * KB <= 16 * wave + 15) {
                 const int ko = kb * KB + grp * EPL;
-                const typename IO::frag fp = ld_frag(Pm + (16 * wave + l16) * 64 + ko);
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) {
-                    const typename IO::frag fd = ld_frag(Dt + (16 * ct + l16) * DTS + ko);
-                    accQ[ct] = IO::mma(accQ[ct], fp, fd);
+                    const frag fd = ld_frag(Dt + (16 * ct + l16) * DTS + ko);
+                    accQ[ct] = IO::mma(accQ[ct], cu.p[kb], fd);
                 }
             }
         }
+
+        // S = diag(Gamma_L) S + Ktil^T Delta
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const int rt = wave * SPW + i;
+            if (rt < SRT) {
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) accS[i][ct] *= cu.gl[i];
+#pragma unroll
+                for (int kb = 0; kb < NKT; ++kb) {
+                    const int ko = kb * KB + grp * EPL;
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) {
+                        const frag fd = ld_frag(Dt + (16 * ct + l16) * DTS + ko);
+                        accS[i][ct] = IO::mma(accS[i][ct], cu.k[i][kb], fd);
+                    }
+                }
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct)
+                    st_vec4(&SbT[(n + 1) & 1][(16 * ct + l16) * SRS + 16 * rt + 4 * grp], accS[i][ct]);
+            }
+        }
+        // o rows of token block `wave` (after the next chunk's loads were issued)
         {
             const int64_t tb = (int64_t)n * kChunk + 16 * wave + 4 * grp;
 #pragma unroll
@@ -499,31 +613,15 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(StateArgs a)
                 }
             }
         }
-
-        // S = diag(Gamma_L) S + Ktil^T Delta
-#pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int rt = wave * SPW + i;
-            if (rt < SRT) {
-                const f32x4 gl = *reinterpret_cast<const f32x4*>(Gl + 16 * rt + 4 * grp);
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) accS[i][ct] *= gl;
-#pragma unroll
-                for (int kb = 0; kb < NKT; ++kb) {
-                    const int ko = kb * KB + grp * EPL;
-                    const typename IO::frag fk = ld_frag(Kt + (16 * rt + l16) * 64 + ko);
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) {
-                        const typename IO::frag fd = ld_frag(Dt + (16 * ct + l16) * DTS + ko);
-                        accS[i][ct] = IO::mma(accS[i][ct], fk, fd);
-                    }
-                }
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-                    st_vec4(&SbT[(n + 1) & 1][(16 * ct + l16) * SRS + 16 * rt + 4 * grp], accS[i][ct]);
-            }
-        }
         __syncthreads();
+    };
+    // unrolled by two so that the operand sets swap roles without copies
+    // (a register copy of a prefetched value would wait for its load)
+    Ops opa, opb;
+    if (a.nt > 0) load_ops(0, opa);
+    for (int n = 0; n < a.nt; n += 2) {
+        step(n, opa, opb);
+        if (n + 1 < a.nt) step(n + 1, opb, opa);
     }
 
     if (a.S_out != nullptr) {
@@ -557,7 +655,12 @@ template <typename Tio, int DK>
 static hipError_t prep_dk(const PrepArgs& a, hipStream_t s)
 {
     const int64_t nblk = a.B * a.H * (int64_t)a.nt;
-    hipLaunchKernelGGL((k_chunk_prep<Tio, DK>), dim3((unsigned)nblk), dim3(kThreads), 0, s, a);
+    if (a.dv <= 64)
+        hipLaunchKernelGGL((k_chunk_prep<Tio, DK, 4>), dim3((unsigned)nblk), dim3(kThreads), 0, s, a);
+    else if (a.dv <= 128)
+        hipLaunchKernelGGL((k_chunk_prep<Tio, DK, 8>), dim3((unsigned)nblk), dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((k_chunk_prep<Tio, DK, 16>), dim3((unsigned)nblk), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -24,6 +24,8 @@ namespace gdn2 {
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 
 constexpr int kThreads = 256;   // every kernel runs 4 waves of 64 lanes
 constexpr int kChunk = 64;      // chunk length of the chunked form
@@ -40,7 +42,10 @@ template <> struct Io<float> {
     static constexpr int KB = 16;        // K per K-block
     typedef f32x4 frag;                  // 16 bytes
     typedef f32x4 vec4;                  // 4 elements
+    typedef f32x2 pair;                  // 2 elements
     __device__ static inline float to_f(float x) { return x; }
+    __device__ static inline f32x2 pair_f(pair p) { return p; }
+    __device__ static inline pair pack2(float x, float y) { return f32x2{x, y}; }
     __device__ static inline float from_f(float x) { return x; }
     __device__ static inline vec4 pack4(f32x4 v) { return v; }
     __device__ static inline f32x4 unpack4(vec4 v) { return v; }
@@ -63,7 +68,14 @@ template <> struct Io<__bf16> {
     static constexpr int KB = 32;
     typedef bf16x8 frag;
     typedef bf16x4 vec4;
+    typedef bf16x2 pair;
     __device__ static inline float to_f(__bf16 x) { return (float)x; }
+    __device__ static inline f32x2 pair_f(pair p) { return f32x2{(float)p[0], (float)p[1]}; }
+    __device__ static inline pair pack2(float x, float y) {
+        pair r;
+        r[0] = (__bf16)x; r[1] = (__bf16)y;
+        return r;
+    }
     __device__ static inline __bf16 from_f(float x) { return (__bf16)x; }   // RNE (v_cvt_pk_bf16_f32)
     __device__ static inline vec4 pack4(f32x4 v) {
         vec4 r;
