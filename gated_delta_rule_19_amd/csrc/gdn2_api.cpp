@@ -136,7 +136,7 @@ int do_state(const gdn2_problem* p, const float* S0, void* o, float* S_out, cons
     const int64_t nch = p->B * p->H;
     if (nch == 0) return GDN2_OK;
     if (nchunks(p) == 0 && S_out == S0) return GDN2_OK;   // nothing to compute or copy
-    const int vs = gdn2::chunk_state_slice(nch, (int)p->dv);
+    const int vs = gdn2::chunk_state_slice(nch, (int)p->dv, (int)p->dk, (int)io_size(p));
     gdn2::StateArgs a{ws, ws_block_bytes(p), S0, o, S_out, p->B, p->T, p->H, (int)p->dv,
                       (int)nchunks(p), (int)(p->dv / vs)};
     return launch_status(gdn2::launch_chunk_state(a, (int)p->dk, vs, is_bf16(p), s));

@@ -100,7 +100,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_prep(PrepArgs a)
     float* Zs = reinterpret_cast<float*>(smem + SM::OZ);
     float* Fs = reinterpret_cast<float*>(smem + SM::OF);
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
     const int64_t chi = blockIdx.x;
     const int64_t chain = chi / a.nt;
     const int n = (int)(chi - chain * a.nt);
@@ -418,34 +419,98 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_prep(PrepArgs a)
 // ---------------------------------------------------------------------------
 // k_chunk_state
 // ---------------------------------------------------------------------------
-// Workgroup = (batch, head, value slice of VS columns).  The slice of S
-// (DK x VS, fp32) lives in accumulators: wave w owns row tiles
-// [w*SPW, (w+1)*SPW).  Per chunk:
-//   X_W = W S, X_Q = Qh S        (wave w: rows of token block w)
-//   Delta = U - X_W   -> LDS (transposed, I/O dtype)
-//   O = X_Q + P Delta -> o
-//   S = diag(Gamma_L) S + Ktil^T Delta -> LDS copy of S (I/O dtype) for the next chunk
-// The slices of one head are mapped to one XCD (block id = xcd + 8*k) so that
-// the shared workspace blocks are read through a single L2.
+// Workgroup = (batch, head, slice of VS value columns), 8 waves: 4 compute
+// waves and 4 loader waves.
+//
+// Compute waves: the slice of S (DK x VS, fp32) lives in matrix-core
+// accumulators; compute wave w owns state row tiles [w*SPW, (w+1)*SPW) and
+// token block w of every chunk.  Per chunk:
+//   X_W = W S          (rows: token block w; B operand: S^T copy in LDS)
+//   Delta = U - X_W    -> LDS (transposed)                      | barrier 1
+//   O^T = S^T Qh^T + Delta^T P^T   (lanes hold 4 adjacent columns of one
+//                                   token, so o is written 4 columns at a time)
+//   S = diag(Gamma_L) S + Ktil^T Delta  -> LDS copy of S for the next chunk
+//                                                               | barrier 2
+// Loader waves keep the next three chunks' factors (W, Qh, P, Ktil^T,
+// Gamma_L and this slice's U^T) in flight in their own registers and copy
+// chunk n+1 into the second LDS buffer while chunk n is computed, so the
+// memory latency of a chunk is hidden behind three chunks of compute.  In
+// LDS every factor row is stored with its 16-byte granules XOR-permuted by
+// the row index so that the 16 rows a fragment read touches fall into
+// distinct banks.  LDS operands of a stage are read before its products.
+// The slices of one head get block ids congruent mod 8 so that they run on
+// one XCD and fetch the head's workspace blocks through a single L2.
+__device__ inline int swz(int row, int g)
+{
+    // granule permutation for rows of g 16-byte granules
+    const int rpb = g >= 8 ? 1 : 8 / g;            // rows per 128-byte bank cycle
+    const int m = g >= 16 ? 16 : (g >= 8 ? g : g);
+    return (row / rpb) % m;
+}
+
 template <typename Tio, int DK, int VS>
-__global__ __launch_bounds__(kThreads) void k_chunk_state(StateArgs a)
+struct StateLds {
+    static constexpr int ES = (int)sizeof(Tio), KB = Io<Tio>::KB, EPL = Io<Tio>::EPL;
+    static constexpr int KPAD = round_up(DK, KB);
+    static constexpr int GW = KPAD * ES / 16;       // granules per row of W / Qh
+    static constexpr int GT = 64 * ES / 16;         // granules per row of P / Ktil^T / U^T
+    // granule offsets of the sections of one operand buffer
+    static constexpr int O_W = 0, O_Q = O_W + 64 * GW, O_P = O_Q + 64 * GW, O_K = O_P + 64 * GT;
+    static constexpr int O_U = O_K + DK * GT, O_G = O_U + VS * GT, GBUF = O_G + DK / 4;
+    static constexpr int SRS = KPAD + EPL, DTS = 64 + EPL;
+    static constexpr int PRIV = VS * SRS * ES + VS * DTS * ES;
+    static constexpr int LIMIT = 160 * 1024;
+    // two operand buffers when they fit (loads of chunk n+1 overlap chunk n),
+    // else one (the copy waits for the chunk to finish: one more barrier)
+    static constexpr int NB = (2 * GBUF * 16 + PRIV <= LIMIT) ? 2 : 1;
+    static constexpr bool FITS = GBUF * 16 + PRIV <= LIMIT;
+    static constexpr int BYTES = NB * GBUF * 16 + PRIV;
+    static constexpr int NLD = 256;                 // loader lanes
+    static constexpr int LPL = (GBUF + NLD - 1) / NLD;   // granules per loader lane per chunk
+};
+
+// bytes of LDS the state kernel needs for (dk, slice width, element size),
+// or 0 when it does not fit (mirrors StateLds for the host)
+inline int state_lds_bytes(int dk, int vs, int es)
+{
+    const int kb = es == 2 ? 32 : 16;
+    const int kpad = (dk + kb - 1) / kb * kb;
+    const int gw = kpad * es / 16, gt = 64 * es / 16;
+    const int gbuf = 64 * gw * 2 + 64 * gt + dk * gt + vs * gt + dk / 4;
+    const int priv = vs * (kpad + 16 / es) * es + vs * (64 + 16 / es) * es;
+    if (2 * gbuf * 16 + priv <= 160 * 1024) return 2 * gbuf * 16 + priv;
+    if (gbuf * 16 + priv <= 160 * 1024) return gbuf * 16 + priv;
+    return 0;
+}
+
+template <typename Tio, int DK, int VS>
+__global__ __launch_bounds__(2 * kThreads, 1) void k_chunk_state(StateArgs a)
 {
     using IO = Io<Tio>;
-    constexpr int EPL = IO::EPL, KB = IO::KB;
-    constexpr int KPAD = round_up(DK, KB);
+    using L = StateLds<Tio, DK, VS>;
+    typedef typename IO::frag frag;
+    typedef typename IO::vec4 vec4;
+    constexpr int EPL = IO::EPL, KB = IO::KB, ES = L::ES;
+    constexpr int KPAD = L::KPAD, GW = L::GW, GT = L::GT;
     constexpr int NCT = VS / 16;
     constexpr int SRT = DK / 16;
     constexpr int SPW = (SRT + 3) / 4;
-    constexpr int SRS = KPAD + EPL;
-    constexpr int DTS = 64 + EPL;
+    constexpr int SRS = L::SRS, DTS = L::DTS;
     constexpr int NKX = KPAD / KB;
     constexpr int NKT = 64 / KB;
+    constexpr int GB = KB * ES / 16;                // granules per K-block
+    constexpr int LPL = L::LPL;
     constexpr WsLayout LY = ws_layout(DK, 0, sizeof(Tio), KB);
+    constexpr int NB = L::NB;
+    static_assert(L::FITS && L::BYTES <= L::LIMIT, "LDS budget");
 
-    __shared__ __attribute__((aligned(16))) Tio SbT[2][VS * SRS];
-    __shared__ __attribute__((aligned(16))) Tio DT[2][VS * DTS];
+    __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
+    Tio* SbT = reinterpret_cast<Tio*>(smem + NB * L::GBUF * 16);            // S^T      [j][c]
+    Tio* DT = reinterpret_cast<Tio*>(smem + NB * L::GBUF * 16 + VS * SRS * ES);  // Delta^T  [j][s]
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool loader = wave >= 4;
     const int64_t nch = a.B * a.H;
     const int ns = a.nslices;
     const int64_t x = blockIdx.x;
@@ -461,167 +526,216 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(StateArgs a)
     const int j0 = slice * VS;
     const int64_t bb = chain / a.H, hh = chain - bb * a.H;
     const int dv = a.dv;
-    Tio* o = static_cast<Tio*>(a.o);
+    const int nt = a.nt;
+    const char* wsbase = static_cast<const char*>(a.ws) + chain * (int64_t)nt * a.ws_block;
 
+    if (loader) {
+        // ---------------- loader waves ------------------------------------
+        // granule g = (wave-4)*64 + lane + 256*m of a buffer: source offset in
+        // the workspace block and destination in the buffer (constant per chunk)
+        int src[LPL], dst[LPL];
+#pragma unroll
+        for (int m = 0; m < LPL; ++m) {
+            int g = (wave - 4) * 64 + lane + 256 * m;
+            if (g >= L::GBUF) g = L::GBUF - 1;           // idle lanes repeat the last granule
+            int so, row, gr, gpr, rb;
+            if (g < L::O_Q)      { row = (g - L::O_W) / GW; gr = (g - L::O_W) % GW; gpr = GW; rb = KPAD * ES; so = (int)LY.wwy; }
+            else if (g < L::O_P) { row = (g - L::O_Q) / GW; gr = (g - L::O_Q) % GW; gpr = GW; rb = KPAD * ES; so = (int)LY.qh; }
+            else if (g < L::O_K) { row = (g - L::O_P) / GT; gr = (g - L::O_P) % GT; gpr = GT; rb = 64 * ES; so = (int)LY.p; }
+            else if (g < L::O_U) { row = (g - L::O_K) / GT; gr = (g - L::O_K) % GT; gpr = GT; rb = 64 * ES; so = (int)LY.ktt; }
+            else if (g < L::O_G) { row = (g - L::O_U) / GT; gr = (g - L::O_U) % GT; gpr = GT; rb = 64 * ES;
+                                   so = (int)LY.uwyt + j0 * 64 * ES; }
+            else                 { row = 0; gr = g - L::O_G; gpr = 1 << 30; rb = 0; so = (int)LY.gaml; }
+            const int base = g < L::O_Q ? L::O_W : g < L::O_P ? L::O_Q : g < L::O_K ? L::O_P
+                           : g < L::O_U ? L::O_K : g < L::O_G ? L::O_U : L::O_G;
+            src[m] = so + row * rb + gr * 16;
+            // stored granule = (row, gr ^ swz(row))
+            dst[m] = g < L::O_G ? (base + row * gpr + (gr ^ swz(row, gpr))) * 16 : g * 16;
+        }
+        frag r0[LPL], r1[LPL], r2[LPL];
+        auto fetch = [&](int n, frag (&r)[LPL]) {
+            const char* blk = wsbase + (int64_t)(n < nt ? n : nt - 1) * a.ws_block;
+#pragma unroll
+            for (int m = 0; m < LPL; ++m) r[m] = *reinterpret_cast<const frag*>(blk + src[m]);
+        };
+        auto store = [&](int buf, const frag (&r)[LPL]) {
+            char* b0 = smem + buf * L::GBUF * 16;
+#pragma unroll
+            for (int m = 0; m < LPL; ++m) *reinterpret_cast<frag*>(b0 + dst[m]) = r[m];
+        };
+        if (nt > 0) {
+            fetch(0, r0);
+            fetch(1, r1);
+            fetch(2, r2);
+            store(0, r0);
+            fetch(3, r0);
+        }
+        __syncthreads();                                  // prologue barrier
+        // iteration n: chunk n+1 goes to LDS, chunk n+4 is requested
+        auto iter = [&](int n, frag (&rn1)[LPL]) {
+            if (NB == 2 && n + 1 < nt) {
+                store((n + 1) & 1, rn1);
+                fetch(n + 4, rn1);
+            }
+            __syncthreads();                              // barrier 1
+            __syncthreads();                              // barrier 2
+            if (NB == 1) {
+                if (n + 1 < nt) {
+                    store(0, rn1);
+                    fetch(n + 4, rn1);
+                }
+                __syncthreads();                          // barrier 3: buffer refilled
+            }
+        };
+        for (int n = 0; n < nt; n += 3) {
+            iter(n, r1);
+            if (n + 1 < nt) iter(n + 1, r2);
+            if (n + 2 < nt) iter(n + 2, r0);
+        }
+        return;
+    }
+
+    // ---------------- compute waves -------------------------------------------
+    Tio* o = static_cast<Tio*>(a.o);
     f32x4 accS[SPW][NCT];
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
-        const int rt = wave * SPW + i;
+        const int rt = wave * SPW + i < SRT ? wave * SPW + i : SRT - 1;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-            f32x4 s = {0.f, 0.f, 0.f, 0.f};
-            if (a.S0 != nullptr && rt < SRT) {
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (a.S0 != nullptr) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    s[e] = a.S0[(chain * DK + 16 * rt + 4 * grp + e) * dv + j0 + 16 * ct + l16];
+                for (int e = 0; e < 4; ++e) v[e] = a.S0[(chain * DK + 16 * rt + 4 * grp + e) * dv + j0 + 16 * ct + l16];
             }
-            accS[i][ct] = s;
+            accS[i][ct] = v;
         }
     }
     if constexpr (KPAD > DK) {
-        for (int e = tid; e < 2 * VS * (KPAD - DK); e += kThreads) {
-            const int bf = e / (VS * (KPAD - DK)), rem = e % (VS * (KPAD - DK));
-            SbT[bf][(rem / (KPAD - DK)) * SRS + DK + rem % (KPAD - DK)] = IO::from_f(0.f);
-        }
+        for (int e = tid; e < VS * (KPAD - DK); e += kThreads)
+            SbT[(e / (KPAD - DK)) * SRS + DK + e % (KPAD - DK)] = IO::from_f(0.f);
     }
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
         const int rt = wave * SPW + i;
         if (rt < SRT) {
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) st_vec4(&SbT[0][(16 * ct + l16) * SRS + 16 * rt + 4 * grp], accS[i][ct]);
+            for (int ct = 0; ct < NCT; ++ct) st_vec4(&SbT[(16 * ct + l16) * SRS + 16 * rt + 4 * grp], accS[i][ct]);
         }
     }
-    __syncthreads();
+    __syncthreads();                                      // prologue barrier
 
-    // operands of one chunk, loaded one chunk ahead (registers)
-    typedef typename IO::frag frag;
-    struct Ops {
-        frag w[NKX], q[NKX], p[NKT], k[SPW][NKT];
-        typename IO::vec4 u[NCT];
-        f32x4 gl[SPW];
+    // fragment (16 bytes) of row r, K-block kb of a swizzled section
+    auto lfrag = [&](const char* sec, int r, int gpr, int kb) -> frag {
+        const int g = (kb * GB + grp) ^ swz(r, gpr);
+        return *reinterpret_cast<const frag*>(sec + (r * gpr + g) * 16);
     };
-    auto load_ops = [&](int n, Ops& op) {
-        const char* blk = static_cast<const char*>(a.ws) + (chain * a.nt + n) * a.ws_block;
-        const Tio* Qh = reinterpret_cast<const Tio*>(blk + LY.qh);
-        const Tio* Ww = reinterpret_cast<const Tio*>(blk + LY.wwy);
-        const Tio* Kt = reinterpret_cast<const Tio*>(blk + LY.ktt);
-        const Tio* Pm = reinterpret_cast<const Tio*>(blk + LY.p);
-        const float* Gl = reinterpret_cast<const float*>(blk + LY.gaml);
-        const Tio* Ut = reinterpret_cast<const Tio*>(blk + LY.uwyt);
+
+    for (int n = 0; n < nt; ++n) {
+        const char* B0 = smem + (NB == 2 ? (n & 1) : 0) * L::GBUF * 16;
+        const char* Wl = B0 + L::O_W * 16;
+        const char* Ql = B0 + L::O_Q * 16;
+        const char* Pl = B0 + L::O_P * 16;
+        const char* Kl = B0 + L::O_K * 16;
+        const char* Ul = B0 + L::O_U * 16;
+        const float* Gl = reinterpret_cast<const float*>(B0 + L::O_G * 16);
+
+        // X_W = W S and O^T = S^T Qh^T
+        frag fw[NKX], fq[NKX];
 #pragma unroll
         for (int kb = 0; kb < NKX; ++kb) {
-            op.w[kb] = ld_frag(Ww + (16 * wave + l16) * KPAD + kb * KB + grp * EPL);
-            op.q[kb] = ld_frag(Qh + (16 * wave + l16) * KPAD + kb * KB + grp * EPL);
+            fw[kb] = lfrag(Wl, 16 * wave + l16, GW, kb);
+            fq[kb] = lfrag(Ql, 16 * wave + l16, GW, kb);
         }
-        // unconditional loads (rows of idle tiles clamped into range) keep the
-        // compiler from waiting at branch joins
+        f32x4 accW[NCT], accO[NCT];
+        frag fsb[2][NKX];
 #pragma unroll
-        for (int kb = 0; kb < NKT; ++kb) {
-            op.p[kb] = ld_frag(Pm + (16 * wave + l16) * 64 + kb * KB + grp * EPL);
-#pragma unroll
-            for (int i = 0; i < SPW; ++i) {
-                const int rt = (wave * SPW + i) < SRT ? (wave * SPW + i) : SRT - 1;
-                op.k[i][kb] = ld_frag(Kt + (16 * rt + l16) * 64 + kb * KB + grp * EPL);
-            }
-        }
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-            op.u[ct] = *reinterpret_cast<const typename IO::vec4*>(Ut + (int64_t)(j0 + 16 * ct + l16) * 64 + 16 * wave + 4 * grp);
-#pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int rt = (wave * SPW + i) < SRT ? (wave * SPW + i) : SRT - 1;
-            op.gl[i] = *reinterpret_cast<const f32x4*>(Gl + 16 * rt + 4 * grp);
-        }
-    };
-
-    // one chunk: prefetch chunk n+1 into `nx`, compute chunk n from `cu`
-    auto step = [&](int n, const Ops& cu, Ops& nx) {
-        // unconditional (the last chunk reloads itself): a prefetch under a
-        // branch makes the compiler drain every outstanding access first
-        load_ops(n + 1 < a.nt ? n + 1 : n, nx);
-        const Tio* Sb = SbT[n & 1];
-        Tio* Dt = DT[n & 1];
-
-        // X_W, X_Q for token block `wave`
-        f32x4 accW[NCT], accQ[NCT];
+        for (int kb = 0; kb < NKX; ++kb) fsb[0][kb] = ld_frag(&SbT[l16 * SRS + kb * KB + grp * EPL]);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-            accW[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-            accQ[ct] = accW[ct];
-        }
+            if (ct + 1 < NCT) {
 #pragma unroll
-        for (int kb = 0; kb < NKX; ++kb) {
-            const int ko = kb * KB + grp * EPL;
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                const frag fs = ld_frag(Sb + (16 * ct + l16) * SRS + ko);
-                accW[ct] = IO::mma(accW[ct], cu.w[kb], fs);
-                accQ[ct] = IO::mma(accQ[ct], cu.q[kb], fs);
+                for (int kb = 0; kb < NKX; ++kb)
+                    fsb[(ct + 1) & 1][kb] = ld_frag(&SbT[(16 * (ct + 1) + l16) * SRS + kb * KB + grp * EPL]);
             }
-        }
-        // Delta = U - X_W (rows 16*wave + 4*grp + i, column 16*ct + l16)
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4 w4 = {0.f, 0.f, 0.f, 0.f}, o4 = w4;
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-            st_vec4(Dt + (16 * ct + l16) * DTS + 16 * wave + 4 * grp, IO::unpack4(cu.u[ct]) - accW[ct]);
-        __syncthreads();
+            for (int kb = 0; kb < NKX; ++kb) {
+                w4 = IO::mma(w4, fw[kb], fsb[ct & 1][kb]);     // D[token][col]
+                o4 = IO::mma(o4, fsb[ct & 1][kb], fq[kb]);     // D[col][token]
+            }
+            accW[ct] = w4;
+            accO[ct] = o4;
+        }
+        // Delta = U - X_W  (rows 16*wave + 4*grp + e, column 16*ct + l16) -> DT[col][token]
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int row = 16 * ct + l16, r = 16 * wave + 4 * grp;
+            const int g = (r * ES / 16) ^ swz(row, GT);
+            const vec4 u4 = *reinterpret_cast<const vec4*>(Ul + (row * GT + g) * 16 + (r * ES) % 16);
+            st_vec4(&DT[row * DTS + r], IO::unpack4(u4) - accW[ct]);
+        }
+        __syncthreads();                                  // barrier 1
 
-        // O = X_Q + P Delta
+        // O^T += Delta^T P^T;  S = diag(Gamma_L) S + Ktil^T Delta
+        frag fp[NKT], fk[SPW][NKT];
+        f32x4 gl[SPW];
 #pragma unroll
         for (int kb = 0; kb < NKT; ++kb) {
-            if (kb * KB <= 16 * wave + 15) {
-                const int ko = kb * KB + grp * EPL;
+            fp[kb] = lfrag(Pl, 16 * wave + l16, GT, kb);
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) {
-                    const frag fd = ld_frag(Dt + (16 * ct + l16) * DTS + ko);
-                    accQ[ct] = IO::mma(accQ[ct], cu.p[kb], fd);
-                }
+            for (int i = 0; i < SPW; ++i) {
+                const int rt = wave * SPW + i < SRT ? wave * SPW + i : SRT - 1;
+                fk[i][kb] = lfrag(Kl, 16 * rt + l16, GT, kb);
             }
         }
-
-        // S = diag(Gamma_L) S + Ktil^T Delta
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const int rt = wave * SPW + i < SRT ? wave * SPW + i : SRT - 1;
+            gl[i] = *reinterpret_cast<const f32x4*>(Gl + 16 * rt + 4 * grp);
+        }
+#pragma unroll
+        for (int i = 0; i < SPW; ++i)
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) accS[i][ct] *= gl[i];
+        frag fdb[2][NKT];
+#pragma unroll
+        for (int kb = 0; kb < NKT; ++kb) fdb[0][kb] = ld_frag(&DT[l16 * DTS + kb * KB + grp * EPL]);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            if (ct + 1 < NCT) {
+#pragma unroll
+                for (int kb = 0; kb < NKT; ++kb)
+                    fdb[(ct + 1) & 1][kb] = ld_frag(&DT[(16 * (ct + 1) + l16) * DTS + kb * KB + grp * EPL]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kb = 0; kb < NKT; ++kb) {
+                if (kb * KB <= 16 * wave + 15) accO[ct] = IO::mma(accO[ct], fdb[ct & 1][kb], fp[kb]);
+#pragma unroll
+                for (int i = 0; i < SPW; ++i) accS[i][ct] = IO::mma(accS[i][ct], fk[i][kb], fdb[ct & 1][kb]);
+            }
+        }
+        // o: token 16*wave + l16, columns 16*ct + 4*grp .. +3
+        {
+            const int64_t t = (int64_t)n * kChunk + 16 * wave + l16;
+            if (t < a.T) {
+                Tio* orow = o + ((bb * a.T + t) * a.H + hh) * dv + j0 + 4 * grp;
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) st_vec4(orow + 16 * ct, accO[ct]);
+            }
+        }
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
             const int rt = wave * SPW + i;
             if (rt < SRT) {
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) accS[i][ct] *= cu.gl[i];
-#pragma unroll
-                for (int kb = 0; kb < NKT; ++kb) {
-                    const int ko = kb * KB + grp * EPL;
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) {
-                        const frag fd = ld_frag(Dt + (16 * ct + l16) * DTS + ko);
-                        accS[i][ct] = IO::mma(accS[i][ct], cu.k[i][kb], fd);
-                    }
-                }
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-                    st_vec4(&SbT[(n + 1) & 1][(16 * ct + l16) * SRS + 16 * rt + 4 * grp], accS[i][ct]);
+                for (int ct = 0; ct < NCT; ++ct) st_vec4(&SbT[(16 * ct + l16) * SRS + 16 * rt + 4 * grp], accS[i][ct]);
             }
         }
-        // o rows of token block `wave` (after the next chunk's loads were issued)
-        {
-            const int64_t tb = (int64_t)n * kChunk + 16 * wave + 4 * grp;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t t = tb + e;
-                if (t < a.T) {
-                    Tio* orow = o + ((bb * a.T + t) * a.H + hh) * dv + j0 + l16;
-#pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct) orow[16 * ct] = IO::from_f(accQ[ct][e]);
-                }
-            }
-        }
-        __syncthreads();
-    };
-    // unrolled by two so that the operand sets swap roles without copies
-    // (a register copy of a prefetched value would wait for its load)
-    Ops opa, opb;
-    if (a.nt > 0) load_ops(0, opa);
-    for (int n = 0; n < a.nt; n += 2) {
-        step(n, opa, opb);
-        if (n + 1 < a.nt) step(n + 1, opb, opa);
+        __syncthreads();                                  // barrier 2
+        if (NB == 1) __syncthreads();                     // barrier 3: buffer refilled
     }
 
     if (a.S_out != nullptr) {
@@ -642,12 +756,17 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(StateArgs a)
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-int chunk_state_slice(int64_t nchains, int dv)
+int chunk_state_slice(int64_t nchains, int dv, int dk, int esize)
 {
-    // enough workgroups to cover 256 CUs while keeping the per-slice operand
-    // reuse (every slice re-reads the chunk's W/Qh/P/Ktil blocks) bounded
-    if (dv % 64 == 0 && nchains * (dv / 64) >= 1024) return 64;
-    if (dv % 32 == 0) return 32;
+    // widest slice that still gives every CU a workgroup and fits in LDS:
+    // wider slices copy each chunk's factors into fewer workgroups
+    static const int widths[3] = {64, 32, 16};
+    for (int i = 0; i < 3; ++i) {
+        const int w = widths[i];
+        if (dv % w == 0 && nchains * (dv / w) >= 256 && state_lds_bytes(dk, w, esize) > 0) return w;
+    }
+    for (int i = 1; i < 3; ++i)
+        if (dv % widths[i] == 0 && state_lds_bytes(dk, widths[i], esize) > 0) return widths[i];
     return 16;
 }
 
@@ -684,9 +803,13 @@ hipError_t launch_chunk_prep(const PrepArgs& a, int dk, bool bf16, hipStream_t s
 template <typename Tio, int DK, int VS>
 static hipError_t state_v(const StateArgs& a, hipStream_t s)
 {
-    const int64_t nblk = a.B * a.H * (int64_t)a.nslices;
-    hipLaunchKernelGGL((k_chunk_state<Tio, DK, VS>), dim3((unsigned)nblk), dim3(kThreads), 0, s, a);
-    return hipGetLastError();
+    if constexpr (!StateLds<Tio, DK, VS>::FITS) {
+        return hipErrorInvalidValue;
+    } else {
+        const int64_t nblk = a.B * a.H * (int64_t)a.nslices;
+        hipLaunchKernelGGL((k_chunk_state<Tio, DK, VS>), dim3((unsigned)nblk), dim3(2 * kThreads), 0, s, a);
+        return hipGetLastError();
+    }
 }
 
 template <typename Tio, int DK>

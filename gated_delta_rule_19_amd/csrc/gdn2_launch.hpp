@@ -32,7 +32,7 @@ hipError_t launch_chunk_state(const StateArgs& a, int dk, int vs, bool bf16, hip
 hipError_t launch_recurrent(const RecArgs& a, int dk, int vs, bool bf16, hipStream_t s);
 
 // Value-slice width the state pass uses for a problem (16, 32 or 64).
-int chunk_state_slice(int64_t nchains, int dv);
+int chunk_state_slice(int64_t nchains, int dv, int dk, int esize);
 // Value-slice width the recurrent kernel uses (16, 32, 64 or 128).
 int recurrent_slice(int64_t nchains, int64_t T, int dv);
 
