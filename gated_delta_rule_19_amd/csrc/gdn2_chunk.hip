@@ -484,7 +484,7 @@ inline int state_lds_bytes(int dk, int vs, int es)
 }
 
 template <typename Tio, int DK, int VS>
-__global__ __launch_bounds__(2 * kThreads, 1) void k_chunk_state(StateArgs a)
+__global__ __launch_bounds__(64 * (4 * (VS > 32 ? VS / 32 : 1) + 4), 1) void k_chunk_state(StateArgs a)
 {
     using IO = Io<Tio>;
     using L = StateLds<Tio, DK, VS>;
@@ -492,7 +492,10 @@ __global__ __launch_bounds__(2 * kThreads, 1) void k_chunk_state(StateArgs a)
     typedef typename IO::vec4 vec4;
     constexpr int EPL = IO::EPL, KB = IO::KB, ES = L::ES;
     constexpr int KPAD = L::KPAD, GW = L::GW, GT = L::GT;
-    constexpr int NCT = VS / 16;
+    constexpr int CW = VS < 32 ? VS : 32;          // columns per compute wave
+    constexpr int NCH = VS / CW;                   // column groups: compute waves = 4 * NCH
+    constexpr int NCW = 4 * NCH;
+    constexpr int NCT = CW / 16;                   // column tiles per compute wave
     constexpr int SRT = DK / 16;
     constexpr int SPW = (SRT + 3) / 4;
     constexpr int SRS = L::SRS, DTS = L::DTS;
@@ -510,7 +513,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void k_chunk_state(StateArgs a)
 
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool loader = wave >= 4;
+    const bool loader = wave >= NCW;
     const int64_t nch = a.B * a.H;
     const int ns = a.nslices;
     const int64_t x = blockIdx.x;
@@ -536,7 +539,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void k_chunk_state(StateArgs a)
         int src[LPL], dst[LPL];
 #pragma unroll
         for (int m = 0; m < LPL; ++m) {
-            int g = (wave - 4) * 64 + lane + 256 * m;
+            int g = (wave - NCW) * 64 + lane + 256 * m;
             if (g >= L::GBUF) g = L::GBUF - 1;           // idle lanes repeat the last granule
             int so, row, gr, gpr, rb;
             if (g < L::O_Q)      { row = (g - L::O_W) / GW; gr = (g - L::O_W) % GW; gpr = GW; rb = KPAD * ES; so = (int)LY.wwy; }
@@ -552,75 +555,94 @@ __global__ __launch_bounds__(2 * kThreads, 1) void k_chunk_state(StateArgs a)
             // stored granule = (row, gr ^ swz(row))
             dst[m] = g < L::O_G ? (base + row * gpr + (gr ^ swz(row, gpr))) * 16 : g * 16;
         }
-        frag r0[LPL], r1[LPL], r2[LPL];
-        auto fetch = [&](int n, frag (&r)[LPL]) {
+        // register slots of chunks in flight: three, or two when the compute
+        // waves' register budget (more waves per SIMD) leaves less room
+        constexpr int DEPTH = NCH > 1 ? 2 : 3;
+        frag r0[LPL], r1[LPL], r2[DEPTH == 3 ? LPL : 1];
+        auto fetch = [&](int n, auto& r) {
             const char* blk = wsbase + (int64_t)(n < nt ? n : nt - 1) * a.ws_block;
 #pragma unroll
             for (int m = 0; m < LPL; ++m) r[m] = *reinterpret_cast<const frag*>(blk + src[m]);
         };
-        auto store = [&](int buf, const frag (&r)[LPL]) {
+        auto store = [&](int buf, const auto& r) {
             char* b0 = smem + buf * L::GBUF * 16;
 #pragma unroll
             for (int m = 0; m < LPL; ++m) *reinterpret_cast<frag*>(b0 + dst[m]) = r[m];
         };
-        if (nt > 0) {
-            fetch(0, r0);
-            fetch(1, r1);
-            fetch(2, r2);
-            store(0, r0);
-            fetch(3, r0);
-        }
-        __syncthreads();                                  // prologue barrier
-        // iteration n: chunk n+1 goes to LDS, chunk n+4 is requested
-        auto iter = [&](int n, frag (&rn1)[LPL]) {
+        // iteration n: chunk n+1 goes to LDS, chunk n+1+DEPTH is requested
+        auto iter = [&](int n, auto& rn1) {
             if (NB == 2 && n + 1 < nt) {
                 store((n + 1) & 1, rn1);
-                fetch(n + 4, rn1);
+                fetch(n + 1 + DEPTH, rn1);
             }
             __syncthreads();                              // barrier 1
             __syncthreads();                              // barrier 2
             if (NB == 1) {
                 if (n + 1 < nt) {
                     store(0, rn1);
-                    fetch(n + 4, rn1);
+                    fetch(n + 1 + DEPTH, rn1);
                 }
                 __syncthreads();                          // barrier 3: buffer refilled
             }
         };
-        for (int n = 0; n < nt; n += 3) {
-            iter(n, r1);
-            if (n + 1 < nt) iter(n + 1, r2);
-            if (n + 2 < nt) iter(n + 2, r0);
+        if constexpr (DEPTH == 3) {
+            if (nt > 0) {
+                fetch(0, r0);
+                fetch(1, r1);
+                fetch(2, r2);
+                store(0, r0);
+                fetch(3, r0);
+            }
+            __syncthreads();                              // prologue barrier
+            for (int n = 0; n < nt; n += 3) {
+                iter(n, r1);
+                if (n + 1 < nt) iter(n + 1, r2);
+                if (n + 2 < nt) iter(n + 2, r0);
+            }
+        } else {
+            if (nt > 0) {
+                fetch(0, r0);
+                fetch(1, r1);
+                store(0, r0);
+                fetch(2, r0);
+            }
+            __syncthreads();                              // prologue barrier
+            for (int n = 0; n < nt; n += 2) {
+                iter(n, r1);
+                if (n + 1 < nt) iter(n + 1, r0);
+            }
         }
         return;
     }
 
     // ---------------- compute waves -------------------------------------------
+    // compute wave = (token block tb, column group ch of CW columns)
+    const int tb = wave & 3, ch = wave >> 2, jc = ch * CW;
     Tio* o = static_cast<Tio*>(a.o);
     f32x4 accS[SPW][NCT];
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
-        const int rt = wave * SPW + i < SRT ? wave * SPW + i : SRT - 1;
+        const int rt = tb * SPW + i < SRT ? tb * SPW + i : SRT - 1;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
             f32x4 v = {0.f, 0.f, 0.f, 0.f};
             if (a.S0 != nullptr) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = a.S0[(chain * DK + 16 * rt + 4 * grp + e) * dv + j0 + 16 * ct + l16];
+                for (int e = 0; e < 4; ++e) v[e] = a.S0[(chain * DK + 16 * rt + 4 * grp + e) * dv + j0 + jc + 16 * ct + l16];
             }
             accS[i][ct] = v;
         }
     }
     if constexpr (KPAD > DK) {
-        for (int e = tid; e < VS * (KPAD - DK); e += kThreads)
+        for (int e = tid; e < VS * (KPAD - DK); e += 64 * NCW)
             SbT[(e / (KPAD - DK)) * SRS + DK + e % (KPAD - DK)] = IO::from_f(0.f);
     }
 #pragma unroll
     for (int i = 0; i < SPW; ++i) {
-        const int rt = wave * SPW + i;
+        const int rt = tb * SPW + i;
         if (rt < SRT) {
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) st_vec4(&SbT[(16 * ct + l16) * SRS + 16 * rt + 4 * grp], accS[i][ct]);
+            for (int ct = 0; ct < NCT; ++ct) st_vec4(&SbT[(jc + 16 * ct + l16) * SRS + 16 * rt + 4 * grp], accS[i][ct]);
         }
     }
     __syncthreads();                                      // prologue barrier
@@ -644,19 +666,19 @@ __global__ __launch_bounds__(2 * kThreads, 1) void k_chunk_state(StateArgs a)
         frag fw[NKX], fq[NKX];
 #pragma unroll
         for (int kb = 0; kb < NKX; ++kb) {
-            fw[kb] = lfrag(Wl, 16 * wave + l16, GW, kb);
-            fq[kb] = lfrag(Ql, 16 * wave + l16, GW, kb);
+            fw[kb] = lfrag(Wl, 16 * tb + l16, GW, kb);
+            fq[kb] = lfrag(Ql, 16 * tb + l16, GW, kb);
         }
         f32x4 accW[NCT], accO[NCT];
         frag fsb[2][NKX];
 #pragma unroll
-        for (int kb = 0; kb < NKX; ++kb) fsb[0][kb] = ld_frag(&SbT[l16 * SRS + kb * KB + grp * EPL]);
+        for (int kb = 0; kb < NKX; ++kb) fsb[0][kb] = ld_frag(&SbT[(jc + l16) * SRS + kb * KB + grp * EPL]);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
             if (ct + 1 < NCT) {
 #pragma unroll
                 for (int kb = 0; kb < NKX; ++kb)
-                    fsb[(ct + 1) & 1][kb] = ld_frag(&SbT[(16 * (ct + 1) + l16) * SRS + kb * KB + grp * EPL]);
+                    fsb[(ct + 1) & 1][kb] = ld_frag(&SbT[(jc + 16 * (ct + 1) + l16) * SRS + kb * KB + grp * EPL]);
             }
             __builtin_amdgcn_sched_barrier(0);
             f32x4 w4 = {0.f, 0.f, 0.f, 0.f}, o4 = w4;
@@ -671,7 +693,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void k_chunk_state(StateArgs a)
         // Delta = U - X_W  (rows 16*wave + 4*grp + e, column 16*ct + l16) -> DT[col][token]
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-            const int row = 16 * ct + l16, r = 16 * wave + 4 * grp;
+            const int row = jc + 16 * ct + l16, r = 16 * tb + 4 * grp;
             const int g = (r * ES / 16) ^ swz(row, GT);
             const vec4 u4 = *reinterpret_cast<const vec4*>(Ul + (row * GT + g) * 16 + (r * ES) % 16);
             st_vec4(&DT[row * DTS + r], IO::unpack4(u4) - accW[ct]);
@@ -683,16 +705,16 @@ __global__ __launch_bounds__(2 * kThreads, 1) void k_chunk_state(StateArgs a)
         f32x4 gl[SPW];
 #pragma unroll
         for (int kb = 0; kb < NKT; ++kb) {
-            fp[kb] = lfrag(Pl, 16 * wave + l16, GT, kb);
+            fp[kb] = lfrag(Pl, 16 * tb + l16, GT, kb);
 #pragma unroll
             for (int i = 0; i < SPW; ++i) {
-                const int rt = wave * SPW + i < SRT ? wave * SPW + i : SRT - 1;
+                const int rt = tb * SPW + i < SRT ? tb * SPW + i : SRT - 1;
                 fk[i][kb] = lfrag(Kl, 16 * rt + l16, GT, kb);
             }
         }
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
-            const int rt = wave * SPW + i < SRT ? wave * SPW + i : SRT - 1;
+            const int rt = tb * SPW + i < SRT ? tb * SPW + i : SRT - 1;
             gl[i] = *reinterpret_cast<const f32x4*>(Gl + 16 * rt + 4 * grp);
         }
 #pragma unroll
@@ -701,37 +723,37 @@ __global__ __launch_bounds__(2 * kThreads, 1) void k_chunk_state(StateArgs a)
             for (int ct = 0; ct < NCT; ++ct) accS[i][ct] *= gl[i];
         frag fdb[2][NKT];
 #pragma unroll
-        for (int kb = 0; kb < NKT; ++kb) fdb[0][kb] = ld_frag(&DT[l16 * DTS + kb * KB + grp * EPL]);
+        for (int kb = 0; kb < NKT; ++kb) fdb[0][kb] = ld_frag(&DT[(jc + l16) * DTS + kb * KB + grp * EPL]);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
             if (ct + 1 < NCT) {
 #pragma unroll
                 for (int kb = 0; kb < NKT; ++kb)
-                    fdb[(ct + 1) & 1][kb] = ld_frag(&DT[(16 * (ct + 1) + l16) * DTS + kb * KB + grp * EPL]);
+                    fdb[(ct + 1) & 1][kb] = ld_frag(&DT[(jc + 16 * (ct + 1) + l16) * DTS + kb * KB + grp * EPL]);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kb = 0; kb < NKT; ++kb) {
-                if (kb * KB <= 16 * wave + 15) accO[ct] = IO::mma(accO[ct], fdb[ct & 1][kb], fp[kb]);
+                if (kb * KB <= 16 * tb + 15) accO[ct] = IO::mma(accO[ct], fdb[ct & 1][kb], fp[kb]);
 #pragma unroll
                 for (int i = 0; i < SPW; ++i) accS[i][ct] = IO::mma(accS[i][ct], fk[i][kb], fdb[ct & 1][kb]);
             }
         }
         // o: token 16*wave + l16, columns 16*ct + 4*grp .. +3
         {
-            const int64_t t = (int64_t)n * kChunk + 16 * wave + l16;
+            const int64_t t = (int64_t)n * kChunk + 16 * tb + l16;
             if (t < a.T) {
-                Tio* orow = o + ((bb * a.T + t) * a.H + hh) * dv + j0 + 4 * grp;
+                Tio* orow = o + ((bb * a.T + t) * a.H + hh) * dv + j0 + jc + 4 * grp;
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) st_vec4(orow + 16 * ct, accO[ct]);
             }
         }
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
-            const int rt = wave * SPW + i;
+            const int rt = tb * SPW + i;
             if (rt < SRT) {
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) st_vec4(&SbT[(16 * ct + l16) * SRS + 16 * rt + 4 * grp], accS[i][ct]);
+                for (int ct = 0; ct < NCT; ++ct) st_vec4(&SbT[(jc + 16 * ct + l16) * SRS + 16 * rt + 4 * grp], accS[i][ct]);
             }
         }
         __syncthreads();                                  // barrier 2
@@ -741,13 +763,13 @@ __global__ __launch_bounds__(2 * kThreads, 1) void k_chunk_state(StateArgs a)
     if (a.S_out != nullptr) {
 #pragma unroll
         for (int i = 0; i < SPW; ++i) {
-            const int rt = wave * SPW + i;
+            const int rt = tb * SPW + i;
             if (rt < SRT) {
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        a.S_out[(chain * DK + 16 * rt + 4 * grp + e) * dv + j0 + 16 * ct + l16] = accS[i][ct][e];
+                        a.S_out[(chain * DK + 16 * rt + 4 * grp + e) * dv + j0 + jc + 16 * ct + l16] = accS[i][ct][e];
             }
         }
     }
@@ -807,7 +829,8 @@ static hipError_t state_v(const StateArgs& a, hipStream_t s)
         return hipErrorInvalidValue;
     } else {
         const int64_t nblk = a.B * a.H * (int64_t)a.nslices;
-        hipLaunchKernelGGL((k_chunk_state<Tio, DK, VS>), dim3((unsigned)nblk), dim3(2 * kThreads), 0, s, a);
+        constexpr int nthreads = 64 * (4 * (VS > 32 ? VS / 32 : 1) + 4);
+        hipLaunchKernelGGL((k_chunk_state<Tio, DK, VS>), dim3((unsigned)nblk), dim3(nthreads), 0, s, a);
         return hipGetLastError();
     }
 }
