@@ -51,8 +51,8 @@ struct PrepSmem {
     static constexpr int SZ_X = 64 * RS * ES;
     static constexpr int SZ_F64 = 64 * FS * 4;
     static constexpr int SZ_T = 64 * TS * ES;
-    static constexpr int SZ_BSC = 16 * 48 * 4;
-    // R0: Xe -> A32 -> UT;  R1: Xq -> T32;  R2: Yd -> (Tm, Bsc);  R3: EhT
+    static constexpr int SZ_BSC = 4 * 16 * 20 * 4;   // TD: diagonal blocks of T, row-major
+    // R0: Xe -> A32 -> UT;  R1: Xq -> T32T;  R2: Yd -> (Tm, TD);  R3: EhT
     static constexpr int R0 = align16(imax(imax(SZ_X, SZ_F64), SZ_T));
     static constexpr int R1 = align16(imax(SZ_X, SZ_F64));
     static constexpr int R2 = align16(imax(SZ_X, SZ_T + SZ_BSC));
@@ -92,10 +92,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_prep(PrepArgs a)
     float* A32 = reinterpret_cast<float*>(smem);
     Tio* UT = reinterpret_cast<Tio*>(smem);
     Tio* Xq = reinterpret_cast<Tio*>(smem + SM::O1);
-    float* T32 = reinterpret_cast<float*>(smem + SM::O1);
+    float* T32T = reinterpret_cast<float*>(smem + SM::O1);
     Tio* Yd = reinterpret_cast<Tio*>(smem + SM::O2);
     Tio* Tm = reinterpret_cast<Tio*>(smem + SM::O2);
-    float* Bsc = reinterpret_cast<float*>(smem + SM::O2 + SM::SZ_T);
+    float* TD = reinterpret_cast<float*>(smem + SM::O2 + SM::SZ_T);
     Tio* EhT = reinterpret_cast<Tio*>(smem + SM::O3);
     float* Zs = reinterpret_cast<float*>(smem + SM::OZ);
     float* Fs = reinterpret_cast<float*>(smem + SM::OF);
@@ -316,58 +316,62 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_prep(PrepArgs a)
     }
     __syncthreads();
 
-    // ---- 3. T = (I + A)^{-1}, fp32, blocked forward substitution -------------
+    // ---- 3. T = (I + A)^{-1}, fp32 -------------------------------------------
+    // Diagonal 16x16 blocks by forward substitution (one lane per column);
+    // then, block row by block row, T[I][J] = -T_II (A[I][0:I] T[0:I][J]) on
+    // fp32 matrix cores: the first product's accumulator is already laid out
+    // as the second product's B operand.  T is kept transposed (T32T[n][s],
+    // K index contiguous) for the B operands, the diagonal blocks row-major
+    // (TD) for the A operands, and in the I/O dtype (Tm) for phases 4 and 5.
+    using F32 = Io<float>;
     if (wave == 0) {
-        // diagonal 16x16 blocks: lane = (block I, column j)
         const int I = lane >> 4, j = lane & 15;
         const float* Ab = A32 + (16 * I) * FS + 16 * I;
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            float s = (r == j) ? 1.f : 0.f;
+            float acc = (r == j) ? 1.f : 0.f;
 #pragma unroll
-            for (int sp = 0; sp < r; ++sp) s -= Ab[r * FS + sp] * x[sp];
-            x[r] = s;
+            for (int sp = 0; sp < r; ++sp) acc -= Ab[r * FS + sp] * x[sp];
+            x[r] = acc;
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) T32[(16 * I + r) * FS + 16 * I + j] = x[r];
+        for (int r = 0; r < 16; ++r) {
+            TD[(I * 16 + r) * 20 + j] = x[r];
+            Tm[(16 * I + r) * TS + 16 * I + j] = IO::from_f(x[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; r += 4)
+            *reinterpret_cast<f32x4*>(T32T + (16 * I + j) * FS + 16 * I + r) = f32x4{x[r], x[r + 1], x[r + 2], x[r + 3]};
     } else {
-        // blocks above the diagonal are zero
+        // blocks of T above the diagonal are zero (T32T only ever reads the
+        // blocks on or below it)
         for (int e = tid - 64; e < 6 * 256; e += kThreads - 64) {
             const int u = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
-            T32[(16 * unpack2(kUpperI, u) + rr) * FS + 16 * unpack2(kUpperJ, u) + cc] = 0.f;
+            const int bi = unpack2(kUpperI, u), bj = unpack2(kUpperJ, u);
+            Tm[(16 * bi + rr) * TS + 16 * bj + cc] = IO::from_f(0.f);
         }
     }
     __syncthreads();
 #pragma unroll
     for (int I = 1; I < 4; ++I) {
-        const int ncol = 16 * I;
-        // Bsc = A[block I rows][0:16I] * T[0:16I][0:16I]
-        for (int e = tid; e < 16 * ncol; e += kThreads) {
-            const int rr = e / ncol, cc = e - rr * ncol;
-            const float* arow = A32 + (16 * I + rr) * FS;
-            float s = 0.f;
+        if (wave < I) {
+            const int J = wave;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int kb = J; kb < I; ++kb) {
+                const f32x4 fa = *reinterpret_cast<const f32x4*>(A32 + (16 * I + l16) * FS + 16 * kb + 4 * grp);
+                const f32x4 fb = *reinterpret_cast<const f32x4*>(T32T + (16 * J + l16) * FS + 16 * kb + 4 * grp);
+                acc = F32::mma(acc, fa, fb);
+            }
+            const f32x4 ft = *reinterpret_cast<const f32x4*>(TD + (I * 16 + l16) * 20 + 4 * grp);
+            const f32x4 t4 = -F32::mma(f32x4{0.f, 0.f, 0.f, 0.f}, ft, acc);
+            // t4[e] = T[16I + 4grp + e][16J + l16]
+            *reinterpret_cast<f32x4*>(T32T + (16 * J + l16) * FS + 16 * I + 4 * grp) = t4;
 #pragma unroll
-            for (int sp = 0; sp < ncol; ++sp) s += arow[sp] * T32[sp * FS + cc];
-            Bsc[rr * 48 + cc] = s;
-        }
-        __syncthreads();
-        // T[block I rows][0:16I] = -T_II * Bsc
-        for (int e = tid; e < 16 * ncol; e += kThreads) {
-            const int rr = e / ncol, cc = e - rr * ncol;
-            const float* trow = T32 + (16 * I + rr) * FS + 16 * I;
-            float s = 0.f;
-#pragma unroll
-            for (int sp = 0; sp < 16; ++sp) s += trow[sp] * Bsc[sp * 48 + cc];
-            T32[(16 * I + rr) * FS + cc] = -s;
+            for (int e = 0; e < 4; ++e) Tm[(16 * I + 4 * grp + e) * TS + 16 * J + l16] = IO::from_f(t4[e]);
         }
         __syncthreads();
     }
-    for (int e = tid; e < 64 * 64; e += kThreads) {
-        const int r = e >> 6, s = e & 63;
-        Tm[r * TS + s] = IO::from_f(s <= r ? T32[r * FS + s] : 0.f);
-    }
-    __syncthreads();
 
     // ---- 4. W^T = (Gamma e)^T T^T : tile (c-block, r-block = wave) ----------
     typename IO::frag tf[64 / KB];
