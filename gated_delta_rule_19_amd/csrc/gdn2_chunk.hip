@@ -41,25 +41,37 @@ __host__ __device__ constexpr int align16(int x) { return (x + 15) & ~15; }
 // ---------------------------------------------------------------------------
 // k_chunk_prep
 // ---------------------------------------------------------------------------
+// Granule permutation of LDS rows: in a row of g 16-byte granules, granule x
+// is stored at x ^ swz(row, g), so that the 16 rows one fragment read touches
+// (same granule, consecutive rows) fall into distinct banks.
+__host__ __device__ constexpr int swz(int row, int g)
+{
+    return (row / (g >= 8 ? 1 : 8 / g)) % (g >= 16 ? 16 : g);
+}
+
 template <typename Tio, int DK>
 struct PrepSmem {
     static constexpr int EPL = Io<Tio>::EPL, KB = Io<Tio>::KB, ES = (int)sizeof(Tio);
     static constexpr int KPAD = round_up(DK, KB);
-    static constexpr int RS = KPAD + EPL;   // row stride of [64][KPAD] operand arrays (elements)
-    static constexpr int TS = 64 + EPL;     // row stride of [*][64] operand arrays (elements)
-    static constexpr int FS = 68;           // row stride of fp32 64x64 matrices
-    static constexpr int SZ_X = 64 * RS * ES;
-    static constexpr int SZ_F64 = 64 * FS * 4;
+    static constexpr int GX = KPAD * ES / 16;   // granules per row of Xe / Xq / Yd
+    static constexpr int GE = 64 * ES / 16;     // granules per row of EhT
+    static constexpr int TS = 64 + EPL;         // row stride of Tm / UT (elements)
+    static constexpr int SZ_X = 64 * KPAD * ES;
+    static constexpr int SZ_F = 64 * 64 * 4;    // fp32 64x64, swizzled rows
+    static constexpr int SZ_E = DK * 64 * ES;
     static constexpr int SZ_T = 64 * TS * ES;
-    static constexpr int SZ_BSC = 4 * 16 * 20 * 4;   // TD: diagonal blocks of T, row-major
-    // R0: Xe -> A32 -> UT;  R1: Xq -> T32T;  R2: Yd -> (Tm, TD);  R3: EhT
-    static constexpr int R0 = align16(imax(imax(SZ_X, SZ_F64), SZ_T));
-    static constexpr int R1 = align16(imax(SZ_X, SZ_F64));
-    static constexpr int R2 = align16(imax(SZ_X, SZ_T + SZ_BSC));
-    static constexpr int R3 = align16(KPAD * TS * ES);
-    static constexpr int O1 = R0, O2 = O1 + R1, O3 = O2 + R2, OZ = O3 + R3;
-    static constexpr int OF = OZ + 4 * DK * 4;          // Zs [4][DK]
-    static constexpr int BYTES = OF + 6 * KPAD * 4;     // Fs [6][KPAD]
+    static constexpr int SZ_TD = 4 * 16 * 20 * 4;   // TD: diagonal blocks of T, row-major
+    // R0: Xe -> A32 -> EhT;  R1: Xq -> T32T -> UT;  R2: Yd -> (Tm, TD)
+    static constexpr int R0 = align16(imax(imax(SZ_X, SZ_F), SZ_E));
+    static constexpr int R1 = align16(imax(imax(SZ_X, SZ_F), SZ_T));
+    static constexpr int R2 = align16(imax(SZ_X, SZ_T + SZ_TD));
+    static constexpr int O1 = R0, O2 = O1 + R1, OF = O2 + R2;
+    // Fs [7][KPAD]: rows 0..5 the per-channel decay factors of the block pairs
+    // (1,0) (2,1) (3,2) (2,0) (3,1) (3,0); rows 0..2 double as the block
+    // totals Z_0..Z_2 and row 6 holds Z_3
+    static constexpr int BYTES = OF + 7 * KPAD * 4;
+    // workgroups per CU the LDS and register budgets are sized for
+    static constexpr int MINB = BYTES * 3 <= 160 * 1024 ? 3 : (BYTES * 2 <= 160 * 1024 ? 2 : 1);
 };
 
 // block pairs (I >= J) of the 64x64 lower triangle, diagonal first; the
@@ -80,25 +92,29 @@ __device__ inline int unpack2(unsigned p, int i) { return (int)((p >> (2 * i)) &
 
 // NUI = (token, 4-column) value items per thread: 64 * dv / 4 <= 256 * NUI
 template <typename Tio, int DK, int NUI>
-__global__ __launch_bounds__(kThreads, 2) void k_chunk_prep(PrepArgs a)
+__global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2)) void k_chunk_prep(PrepArgs a)
 {
     using IO = Io<Tio>;
     using SM = PrepSmem<Tio, DK>;
-    constexpr int EPL = SM::EPL, KB = SM::KB, KPAD = SM::KPAD, RS = SM::RS, TS = SM::TS, FS = SM::FS;
+    constexpr int EPL = SM::EPL, KB = SM::KB, KPAD = SM::KPAD, TS = SM::TS, ES = SM::ES;
+    constexpr int GX = SM::GX, GE = SM::GE, EPG = 16 / ES;   // EPG: elements per granule
     constexpr WsLayout LY = ws_layout(DK, 0, sizeof(Tio), KB);
 
     __shared__ __attribute__((aligned(16))) char smem[SM::BYTES];
     Tio* Xe = reinterpret_cast<Tio*>(smem);
     float* A32 = reinterpret_cast<float*>(smem);
-    Tio* UT = reinterpret_cast<Tio*>(smem);
+    Tio* EhT = reinterpret_cast<Tio*>(smem);
     Tio* Xq = reinterpret_cast<Tio*>(smem + SM::O1);
     float* T32T = reinterpret_cast<float*>(smem + SM::O1);
+    Tio* UT = reinterpret_cast<Tio*>(smem + SM::O1);
     Tio* Yd = reinterpret_cast<Tio*>(smem + SM::O2);
     Tio* Tm = reinterpret_cast<Tio*>(smem + SM::O2);
     float* TD = reinterpret_cast<float*>(smem + SM::O2 + SM::SZ_T);
-    Tio* EhT = reinterpret_cast<Tio*>(smem + SM::O3);
-    float* Zs = reinterpret_cast<float*>(smem + SM::OZ);
     float* Fs = reinterpret_cast<float*>(smem + SM::OF);
+    // element offsets in the swizzled arrays
+    auto xo = [](int r, int c) { return r * KPAD + (((c / EPG) ^ swz(r, GX)) * EPG) + c % EPG; };   // [64][KPAD]
+    auto fo = [](int r, int c) { return r * 64 + (((c / 4) ^ swz(r, 16)) * 4) + c % 4; };          // fp32 [64][64]
+    auto eo = [](int r, int c) { return r * 64 + (((c / EPG) ^ swz(r, GE)) * EPG) + c % EPG; };      // [DK][64]
 
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
@@ -122,15 +138,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_prep(PrepArgs a)
     Tio* uwyt_out = reinterpret_cast<Tio*>(blk + LY.uwyt);
 
     typedef typename IO::frag frag;
-    typedef typename IO::pair pair2;
 
-    // ---- 0. every global load of the kernel, before any global store --------
+    // ---- 0. key-axis loads ----------------------------------------------------
     // One vector-memory counter tracks loads and stores alike, so a load
-    // issued after a store would also wait for that store to complete.  Loads
-    // are unconditional (rows past the sequence end are clamped to its last
-    // row and replaced by identity tokens afterwards): a load under a branch
-    // would be waited for at the join.  16-byte accesses keep the count of
-    // loads per lane under the 63 the counter can track.
+    // issued after a store would also wait for that store to complete: every
+    // load needed before the first global store is issued here.  Loads are
+    // unconditional (rows past the sequence end are clamped to its last row
+    // and replaced by identity tokens afterwards): a load under a branch would
+    // be waited for at the join.  16-byte accesses keep the count of loads per
+    // lane under the 63 the counter can track.
     // Key-axis item = (4 channels c0..c0+3, 8-token group rg); block p = rg/2.
     constexpr int NQ = DK / 4;
     const bool kact = tid < 2 * DK;
@@ -145,25 +161,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_prep(PrepArgs a)
         bt[i] = *reinterpret_cast<const f32x4*>(a.b + off);
         kk[i] = *reinterpret_cast<const typename IO::vec4*>(k + off);
         qq[i] = *reinterpret_cast<const typename IO::vec4*>(q + off);
-    }
-    // value-axis item = (token s, 4 columns): u = w * v
-    constexpr int NVQ_MAX = NUI;
-    f32x4 wr[NVQ_MAX];
-    typename IO::vec4 vr[NVQ_MAX];
-    const int nvq = a.dv / 4;
-#pragma unroll
-    for (int m = 0; m < NVQ_MAX; ++m) {
-        const int u = tid + m * kThreads;
-        const int jq = u % nvq, s = u / nvq;
-        const int64_t off = (row0 + (s < L ? s : L - 1) * H) * a.dv + 4 * jq;
-        wr[m] = *reinterpret_cast<const f32x4*>(a.w + off);
-        vr[m] = *reinterpret_cast<const typename IO::vec4*>(v + off);
-    }
-    f32x4 uu[NVQ_MAX];
-#pragma unroll
-    for (int m = 0; m < NVQ_MAX; ++m) {
-        const int s = (tid + m * kThreads) / nvq;
-        uu[m] = (s < L && s < 64) ? wr[m] * IO::unpack4(vr[m]) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -195,15 +192,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_prep(PrepArgs a)
             for (int i = 0; i < 8; ++i) g[i] *= other;
         }
         zblk = run * other;
-        if (kact && half == 0) *reinterpret_cast<f32x4*>(Zs + p * DK + c0) = zblk;
+        if (kact && half == 0) *reinterpret_cast<f32x4*>(Fs + (p < 3 ? p : 6) * KPAD + c0) = zblk;
     }
     if constexpr (KPAD > DK) {   // zero the K padding of the operand arrays
         for (int e = tid; e < 64 * (KPAD - DK); e += kThreads) {
             const int r = e / (KPAD - DK), c = DK + e % (KPAD - DK);
-            Xe[r * RS + c] = IO::from_f(0.f);
-            Xq[r * RS + c] = IO::from_f(0.f);
-            Yd[r * RS + c] = IO::from_f(0.f);
-            EhT[c * TS + r] = IO::from_f(0.f);
+            Xe[xo(r, c)] = IO::from_f(0.f);
+            Xq[xo(r, c)] = IO::from_f(0.f);
+            Yd[xo(r, c)] = IO::from_f(0.f);
             qh_out[r * KPAD + c] = IO::from_f(0.f);
             wwy_out[r * KPAD + c] = IO::from_f(0.f);
         }
@@ -213,14 +209,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_prep(PrepArgs a)
     __syncthreads();
 
     // ---- 1b. block factors, decay-scaled operands ---------------------------
+    // The (Gamma e)^T fragments are kept in registers and written to LDS after
+    // the solve, when the space of A is free.
+    constexpr int NEF = 8 / EPL;
+    frag ehf[4][NEF];
     if (kact) {
         f32x4 z[4];
 #pragma unroll
-        for (int K = 0; K < 4; ++K) z[K] = *reinterpret_cast<const f32x4*>(Zs + K * DK + c0);
-        if (rg == 0) {
-            *reinterpret_cast<f32x4*>(Fs + 0 * KPAD + c0) = z[0];                 // pair (1,0)
-            *reinterpret_cast<f32x4*>(Fs + 1 * KPAD + c0) = z[1];                 // pair (2,1)
-            *reinterpret_cast<f32x4*>(Fs + 2 * KPAD + c0) = z[2];                 // pair (3,2)
+        for (int K = 0; K < 4; ++K) z[K] = *reinterpret_cast<const f32x4*>(Fs + (K < 3 ? K : 6) * KPAD + c0);
+        if (rg == 0) {   // rows 0..2 (pairs (1,0) (2,1) (3,2)) already hold Z_0..Z_2
             *reinterpret_cast<f32x4*>(Fs + 3 * KPAD + c0) = z[0] * z[1];          // pair (2,0)
             *reinterpret_cast<f32x4*>(Fs + 4 * KPAD + c0) = z[1] * z[2];          // pair (3,1)
             *reinterpret_cast<f32x4*>(Fs + 5 * KPAD + c0) = z[0] * z[1] * z[2];   // pair (3,0)
@@ -232,21 +229,21 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_prep(PrepArgs a)
             if (K < p) pre *= z[K];
             if (K > p) post *= z[K];
         }
-        Tio eh[4][8], kt[4][8];
+        Tio kt[4][8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int r = 8 * rg + i;
             const f32x4 kv = IO::unpack4(kk[i]), qv = IO::unpack4(qq[i]);
             const f32x4 ig = {fast_rcp(g[i][0]), fast_rcp(g[i][1]), fast_rcp(g[i][2]), fast_rcp(g[i][3])};
             const f32x4 xe = bt[i] * kv * g[i], xq = qv * g[i];
-            st_vec4(Xe + r * RS + c0, xe);
-            st_vec4(Xq + r * RS + c0, xq);
-            st_vec4(Yd + r * RS + c0, kv * ig);
+            st_vec4(Xe + xo(r, c0), xe);
+            st_vec4(Xq + xo(r, c0), xq);
+            st_vec4(Yd + xo(r, c0), kv * ig);
             st_vec4(qh_out + r * KPAD + c0, xq * pre);
             const f32x4 ehv = xe * pre, ktv = kv * (zblk * ig) * post;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                eh[e][i] = IO::from_f(ehv[e]);
+                ehf[e][i / EPL][i % EPL] = IO::from_f(ehv[e]);
                 kt[e][i] = IO::from_f(ktv[e]);
             }
         }
@@ -254,16 +251,27 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_prep(PrepArgs a)
         for (int e = 0; e < 4; ++e) {
 #pragma unroll
             for (int i = 0; i < 8; i += EPL) {
-                frag f0, f1;
+                frag f1;
 #pragma unroll
-                for (int e2 = 0; e2 < EPL; ++e2) {
-                    f0[e2] = eh[e][i + e2];
-                    f1[e2] = kt[e][i + e2];
-                }
-                *reinterpret_cast<frag*>(EhT + (c0 + e) * TS + 8 * rg + i) = f0;
+                for (int e2 = 0; e2 < EPL; ++e2) f1[e2] = kt[e][i + e2];
                 *reinterpret_cast<frag*>(ktt_out + (c0 + e) * 64 + 8 * rg + i) = f1;
             }
         }
+    }
+
+    // ---- value-axis loads: u = w * v, needed from phase 5 on ----------------
+    // value-axis item = (token s, 4 columns)
+    constexpr int NVQ_MAX = NUI;
+    f32x4 wr[NVQ_MAX];
+    typename IO::vec4 vr[NVQ_MAX];
+    const int nvq = a.dv / 4;
+#pragma unroll
+    for (int m = 0; m < NVQ_MAX; ++m) {
+        const int u = tid + m * kThreads;
+        const int jq = u % nvq, s = u / nvq;
+        const int64_t off = (row0 + (s < L ? s : L - 1) * H) * a.dv + 4 * jq;
+        wr[m] = *reinterpret_cast<const f32x4*>(a.w + off);
+        vr[m] = *reinterpret_cast<const typename IO::vec4*>(v + off);
     }
     __syncthreads();
 
@@ -281,10 +289,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_prep(PrepArgs a)
 #pragma unroll
             for (int kb = 0; kb < KPAD / KB; ++kb) {
                 const int ko = kb * KB + grp * EPL;
-                typename IO::frag y = ld_frag(Yd + (16 * J + l16) * RS + ko);
+                typename IO::frag y = ld_frag(Yd + xo(16 * J + l16, ko));
                 if (pr >= 4) y = IO::scale(y, Fs + (pr - 4) * KPAD + ko);
-                const typename IO::frag xe = ld_frag(Xe + (16 * I + l16) * RS + ko);
-                const typename IO::frag xq = ld_frag(Xq + (16 * I + l16) * RS + ko);
+                const typename IO::frag xe = ld_frag(Xe + xo(16 * I + l16, ko));
+                const typename IO::frag xq = ld_frag(Xq + xo(16 * I + l16, ko));
                 accA[pi] = IO::mma(accA[pi], y, xe);
                 accP[pi] = IO::mma(accP[pi], y, xq);
             }
@@ -306,7 +314,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_prep(PrepArgs a)
                     if (s > l16) pv[i] = 0.f;
                 }
             }
-            *reinterpret_cast<f32x4*>(A32 + r * FS + 16 * J + 4 * grp) = av;
+            *reinterpret_cast<f32x4*>(A32 + fo(r, 16 * J + 4 * grp)) = av;
             st_vec4(p_out + r * 64 + 16 * J + 4 * grp, pv);
         }
     }
@@ -326,13 +334,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_prep(PrepArgs a)
     using F32 = Io<float>;
     if (wave == 0) {
         const int I = lane >> 4, j = lane & 15;
-        const float* Ab = A32 + (16 * I) * FS + 16 * I;
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float acc = (r == j) ? 1.f : 0.f;
 #pragma unroll
-            for (int sp = 0; sp < r; ++sp) acc -= Ab[r * FS + sp] * x[sp];
+            for (int sp = 0; sp < r; ++sp) acc -= A32[fo(16 * I + r, 16 * I + sp)] * x[sp];
             x[r] = acc;
         }
 #pragma unroll
@@ -342,7 +349,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_prep(PrepArgs a)
         }
 #pragma unroll
         for (int r = 0; r < 16; r += 4)
-            *reinterpret_cast<f32x4*>(T32T + (16 * I + j) * FS + 16 * I + r) = f32x4{x[r], x[r + 1], x[r + 2], x[r + 3]};
+            *reinterpret_cast<f32x4*>(T32T + fo(16 * I + j, 16 * I + r)) = f32x4{x[r], x[r + 1], x[r + 2], x[r + 3]};
     } else {
         // blocks of T above the diagonal are zero (T32T only ever reads the
         // blocks on or below it)
@@ -359,19 +366,28 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_prep(PrepArgs a)
             const int J = wave;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             for (int kb = J; kb < I; ++kb) {
-                const f32x4 fa = *reinterpret_cast<const f32x4*>(A32 + (16 * I + l16) * FS + 16 * kb + 4 * grp);
-                const f32x4 fb = *reinterpret_cast<const f32x4*>(T32T + (16 * J + l16) * FS + 16 * kb + 4 * grp);
+                const f32x4 fa = *reinterpret_cast<const f32x4*>(A32 + fo(16 * I + l16, 16 * kb + 4 * grp));
+                const f32x4 fb = *reinterpret_cast<const f32x4*>(T32T + fo(16 * J + l16, 16 * kb + 4 * grp));
                 acc = F32::mma(acc, fa, fb);
             }
             const f32x4 ft = *reinterpret_cast<const f32x4*>(TD + (I * 16 + l16) * 20 + 4 * grp);
             const f32x4 t4 = -F32::mma(f32x4{0.f, 0.f, 0.f, 0.f}, ft, acc);
             // t4[e] = T[16I + 4grp + e][16J + l16]
-            *reinterpret_cast<f32x4*>(T32T + (16 * J + l16) * FS + 16 * I + 4 * grp) = t4;
+            *reinterpret_cast<f32x4*>(T32T + fo(16 * J + l16, 16 * I + 4 * grp)) = t4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) Tm[(16 * I + 4 * grp + e) * TS + 16 * J + l16] = IO::from_f(t4[e]);
         }
         __syncthreads();
     }
+    // (Gamma e)^T into the space of A
+    if (kact) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int i = 0; i < NEF; ++i)
+                *reinterpret_cast<frag*>(EhT + eo(c0 + e, 8 * rg + EPL * i)) = ehf[e][i];
+    }
+    __syncthreads();
 
     // ---- 4. W^T = (Gamma e)^T T^T : tile (c-block, r-block = wave) ----------
     typename IO::frag tf[64 / KB];
@@ -383,7 +399,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_prep(PrepArgs a)
 #pragma unroll
         for (int kb = 0; kb < 64 / KB; ++kb) {
             if (kb * KB <= 16 * wave + 15) {
-                const typename IO::frag fe = ld_frag(EhT + (16 * ct + l16) * TS + kb * KB + grp * EPL);
+                const typename IO::frag fe = ld_frag(EhT + eo(16 * ct + l16, kb * KB + grp * EPL));
                 acc = IO::mma(acc, fe, tf[kb]);
             }
         }
@@ -392,6 +408,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_prep(PrepArgs a)
     }
 
     // ---- 5. U = T (w * v), stored transposed, in column blocks of 64 --------
+    f32x4 uu[NVQ_MAX];
+#pragma unroll
+    for (int m = 0; m < NVQ_MAX; ++m) {
+        const int s = (tid + m * kThreads) / nvq;
+        uu[m] = (s < L && s < 64) ? wr[m] * IO::unpack4(vr[m]) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     for (int j0 = 0; j0 < a.dv; j0 += 64) {
         const int nj = (a.dv - j0) < 64 ? (a.dv - j0) : 64;
 #pragma unroll
@@ -444,13 +466,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_prep(PrepArgs a)
 // distinct banks.  LDS operands of a stage are read before its products.
 // The slices of one head get block ids congruent mod 8 so that they run on
 // one XCD and fetch the head's workspace blocks through a single L2.
-__device__ inline int swz(int row, int g)
-{
-    // granule permutation for rows of g 16-byte granules
-    const int rpb = g >= 8 ? 1 : 8 / g;            // rows per 128-byte bank cycle
-    const int m = g >= 16 ? 16 : (g >= 8 ? g : g);
-    return (row / rpb) % m;
-}
 
 template <typename Tio, int DK, int VS>
 struct StateLds {
@@ -487,8 +502,15 @@ inline int state_lds_bytes(int dk, int vs, int es)
     return 0;
 }
 
+#ifndef GDN2_STATE_CW
+#define GDN2_STATE_CW 32
+#endif
+// value columns per compute wave and threads per workgroup of the state pass
+__host__ __device__ constexpr int state_cw(int vs) { return vs < GDN2_STATE_CW ? vs : GDN2_STATE_CW; }
+__host__ __device__ constexpr int state_threads(int vs) { return 64 * (4 * (vs / state_cw(vs)) + 4); }
+
 template <typename Tio, int DK, int VS>
-__global__ __launch_bounds__(64 * (4 * (VS > 32 ? VS / 32 : 1) + 4), 1) void k_chunk_state(StateArgs a)
+__global__ __launch_bounds__(state_threads(VS), 1) void k_chunk_state(StateArgs a)
 {
     using IO = Io<Tio>;
     using L = StateLds<Tio, DK, VS>;
@@ -496,7 +518,7 @@ __global__ __launch_bounds__(64 * (4 * (VS > 32 ? VS / 32 : 1) + 4), 1) void k_c
     typedef typename IO::vec4 vec4;
     constexpr int EPL = IO::EPL, KB = IO::KB, ES = L::ES;
     constexpr int KPAD = L::KPAD, GW = L::GW, GT = L::GT;
-    constexpr int CW = VS < 32 ? VS : 32;          // columns per compute wave
+    constexpr int CW = state_cw(VS);               // columns per compute wave
     constexpr int NCH = VS / CW;                   // column groups: compute waves = 4 * NCH
     constexpr int NCW = 4 * NCH;
     constexpr int NCT = CW / 16;                   // column tiles per compute wave
@@ -559,62 +581,64 @@ __global__ __launch_bounds__(64 * (4 * (VS > 32 ? VS / 32 : 1) + 4), 1) void k_c
             // stored granule = (row, gr ^ swz(row))
             dst[m] = g < L::O_G ? (base + row * gpr + (gr ^ swz(row, gpr))) * 16 : g * 16;
         }
-        // register slots of chunks in flight: three, or two when the compute
-        // waves' register budget (more waves per SIMD) leaves less room
-        constexpr int DEPTH = NCH > 1 ? 2 : 3;
-        frag r0[LPL], r1[LPL], r2[DEPTH == 3 ? LPL : 1];
-        auto fetch = [&](int n, auto& r) {
+        // register slots of chunks in flight: as many (up to three) as fit in
+        // the registers a lane has next to the compute waves' budget
+        constexpr int NW = NCW + 4;
+        constexpr int VBUDGET = (NW <= 8 ? 256 : (NW <= 12 ? 168 : 128)) - 56;
+        constexpr int DEPTH = LPL * 4 * 3 <= VBUDGET ? 3 : (LPL * 4 * 2 <= VBUDGET ? 2 : 1);
+        frag r[DEPTH][LPL];
+        // granules [m0, m1) of chunk n into / out of a register slot
+        auto fetch = [&](int n, frag* rs, int m0, int m1) {
             const char* blk = wsbase + (int64_t)(n < nt ? n : nt - 1) * a.ws_block;
 #pragma unroll
-            for (int m = 0; m < LPL; ++m) r[m] = *reinterpret_cast<const frag*>(blk + src[m]);
+            for (int m = 0; m < LPL; ++m)
+                if (m >= m0 && m < m1) rs[m] = *reinterpret_cast<const frag*>(blk + src[m]);
         };
-        auto store = [&](int buf, const auto& r) {
+        auto store = [&](int buf, const frag* rs, int m0, int m1) {
             char* b0 = smem + buf * L::GBUF * 16;
 #pragma unroll
-            for (int m = 0; m < LPL; ++m) *reinterpret_cast<frag*>(b0 + dst[m]) = r[m];
+            for (int m = 0; m < LPL; ++m)
+                if (m >= m0 && m < m1) *reinterpret_cast<frag*>(b0 + dst[m]) = rs[m];
         };
-        // iteration n: chunk n+1 goes to LDS, chunk n+1+DEPTH is requested
-        auto iter = [&](int n, auto& rn1) {
-            if (NB == 2 && n + 1 < nt) {
-                store((n + 1) & 1, rn1);
-                fetch(n + 1 + DEPTH, rn1);
+        // Chunk c travels in slot c % DEPTH.  Iteration n: chunk n+1 goes to
+        // LDS and chunk n+1+DEPTH is requested into the slot it leaves, half
+        // before barrier 1 and half after it, so that the copy overlaps both
+        // compute phases and barrier 1 (which orders the compute waves' Delta
+        // exchange) does not wait for the whole copy.
+        constexpr int HALF = LPL / 2;
+        auto iter = [&](int n, frag* rs) {
+            const bool go = NB == 2 && n + 1 < nt;
+            if (go) {
+                store((n + 1) & 1, rs, 0, HALF);
+                fetch(n + 1 + DEPTH, rs, 0, HALF);
             }
             __syncthreads();                              // barrier 1
+            if (go) {
+                store((n + 1) & 1, rs, HALF, LPL);
+                fetch(n + 1 + DEPTH, rs, HALF, LPL);
+            }
             __syncthreads();                              // barrier 2
             if (NB == 1) {
                 if (n + 1 < nt) {
-                    store(0, rn1);
-                    fetch(n + 1 + DEPTH, rn1);
+                    store(0, rs, 0, LPL);
+                    fetch(n + 1 + DEPTH, rs, 0, LPL);
                 }
                 __syncthreads();                          // barrier 3: buffer refilled
             }
         };
-        if constexpr (DEPTH == 3) {
-            if (nt > 0) {
-                fetch(0, r0);
-                fetch(1, r1);
-                fetch(2, r2);
-                store(0, r0);
-                fetch(3, r0);
-            }
-            __syncthreads();                              // prologue barrier
-            for (int n = 0; n < nt; n += 3) {
-                iter(n, r1);
-                if (n + 1 < nt) iter(n + 1, r2);
-                if (n + 2 < nt) iter(n + 2, r0);
-            }
-        } else {
-            if (nt > 0) {
-                fetch(0, r0);
-                fetch(1, r1);
-                store(0, r0);
-                fetch(2, r0);
-            }
-            __syncthreads();                              // prologue barrier
-            for (int n = 0; n < nt; n += 2) {
-                iter(n, r1);
-                if (n + 1 < nt) iter(n + 1, r0);
-            }
+        if (nt > 0) {
+            // chunk 0 first: the compute waves start as soon as it is in LDS
+            fetch(0, r[0], 0, LPL);
+            store(0, r[0], 0, LPL);
+#pragma unroll
+            for (int d = 1; d < DEPTH; ++d) fetch(d, r[d], 0, LPL);
+            fetch(DEPTH, r[0], 0, LPL);
+        }
+        __syncthreads();                                  // prologue barrier
+        for (int n = 0; n < nt; n += DEPTH) {
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d)
+                if (n + d < nt) iter(n + d, r[(d + 1) % DEPTH]);
         }
         return;
     }
@@ -833,7 +857,7 @@ static hipError_t state_v(const StateArgs& a, hipStream_t s)
         return hipErrorInvalidValue;
     } else {
         const int64_t nblk = a.B * a.H * (int64_t)a.nslices;
-        constexpr int nthreads = 64 * (4 * (VS > 32 ? VS / 32 : 1) + 4);
+        constexpr int nthreads = state_threads(VS);
         hipLaunchKernelGGL((k_chunk_state<Tio, DK, VS>), dim3((unsigned)nblk), dim3(nthreads), 0, s, a);
         return hipGetLastError();
     }
