@@ -29,6 +29,8 @@
 // column operand on load.  Only 1/g_s can exceed 1, by at most the inverse
 // decay of 16 tokens.  No exp/log is evaluated: all factors are running
 // products of alpha.
+#include <type_traits>
+
 #include "gdn2_device.hpp"
 #include "gdn2_launch.hpp"
 #include "gdn2_layout.hpp"
@@ -567,19 +569,23 @@ __global__ __launch_bounds__(state_threads(VS), 1) void k_chunk_state(StateArgs 
         for (int m = 0; m < LPL; ++m) {
             int g = (wave - NCW) * 64 + lane + 256 * m;
             if (g >= L::GBUF) g = L::GBUF - 1;           // idle lanes repeat the last granule
-            int so, row, gr, gpr, rb;
-            if (g < L::O_Q)      { row = (g - L::O_W) / GW; gr = (g - L::O_W) % GW; gpr = GW; rb = KPAD * ES; so = (int)LY.wwy; }
-            else if (g < L::O_P) { row = (g - L::O_Q) / GW; gr = (g - L::O_Q) % GW; gpr = GW; rb = KPAD * ES; so = (int)LY.qh; }
-            else if (g < L::O_K) { row = (g - L::O_P) / GT; gr = (g - L::O_P) % GT; gpr = GT; rb = 64 * ES; so = (int)LY.p; }
-            else if (g < L::O_U) { row = (g - L::O_K) / GT; gr = (g - L::O_K) % GT; gpr = GT; rb = 64 * ES; so = (int)LY.ktt; }
-            else if (g < L::O_G) { row = (g - L::O_U) / GT; gr = (g - L::O_U) % GT; gpr = GT; rb = 64 * ES;
-                                   so = (int)LY.uwyt + j0 * 64 * ES; }
-            else                 { row = 0; gr = g - L::O_G; gpr = 1 << 30; rb = 0; so = (int)LY.gaml; }
-            const int base = g < L::O_Q ? L::O_W : g < L::O_P ? L::O_Q : g < L::O_K ? L::O_P
-                           : g < L::O_U ? L::O_K : g < L::O_G ? L::O_U : L::O_G;
-            src[m] = so + row * rb + gr * 16;
-            // stored granule = (row, gr ^ swz(row))
-            dst[m] = g < L::O_G ? (base + row * gpr + (gr ^ swz(row, gpr))) * 16 : g * 16;
+            // granule x of a section whose rows hold GPR granules (compile-time
+            // widths keep the index arithmetic to shifts and masks); stored
+            // granule = (row, column ^ swz(row))
+            auto map = [&](int x, auto gpr_c, int sec_src, int sec_base) {
+                constexpr int GPR = decltype(gpr_c)::value;
+                const int row = x / GPR, gr = x % GPR;
+                src[m] = sec_src + row * (GPR * 16) + gr * 16;
+                dst[m] = (sec_base + row * GPR + (gr ^ swz(row, GPR))) * 16;
+            };
+            using cGW = std::integral_constant<int, GW>;
+            using cGT = std::integral_constant<int, GT>;
+            if (g < L::O_Q)      map(g - L::O_W, cGW{}, (int)LY.wwy, L::O_W);
+            else if (g < L::O_P) map(g - L::O_Q, cGW{}, (int)LY.qh, L::O_Q);
+            else if (g < L::O_K) map(g - L::O_P, cGT{}, (int)LY.p, L::O_P);
+            else if (g < L::O_U) map(g - L::O_K, cGT{}, (int)LY.ktt, L::O_K);
+            else if (g < L::O_G) map(g - L::O_U, cGT{}, (int)LY.uwyt + j0 * 64 * ES, L::O_U);
+            else { src[m] = (int)LY.gaml + (g - L::O_G) * 16; dst[m] = g * 16; }
         }
         // register slots of chunks in flight: as many (up to three) as fit in
         // the registers a lane has next to the compute waves' budget
@@ -626,15 +632,18 @@ __global__ __launch_bounds__(state_threads(VS), 1) void k_chunk_state(StateArgs 
                 __syncthreads();                          // barrier 3: buffer refilled
             }
         };
+        // chunk 0 first: the compute waves start as soon as it is in LDS
         if (nt > 0) {
-            // chunk 0 first: the compute waves start as soon as it is in LDS
             fetch(0, r[0], 0, LPL);
+            if (DEPTH > 1) fetch(1, r[DEPTH > 1 ? 1 : 0], 0, LPL);
             store(0, r[0], 0, LPL);
-#pragma unroll
-            for (int d = 1; d < DEPTH; ++d) fetch(d, r[d], 0, LPL);
-            fetch(DEPTH, r[0], 0, LPL);
         }
         __syncthreads();                                  // prologue barrier
+        if (nt > 0) {
+#pragma unroll
+            for (int d = 2; d < DEPTH; ++d) fetch(d, r[d], 0, LPL);
+            fetch(DEPTH, r[0], 0, LPL);
+        }
         for (int n = 0; n < nt; n += DEPTH) {
 #pragma unroll
             for (int d = 0; d < DEPTH; ++d)
