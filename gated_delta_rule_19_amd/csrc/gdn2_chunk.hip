@@ -469,6 +469,14 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
 // The slices of one head get block ids congruent mod 8 so that they run on
 // one XCD and fetch the head's workspace blocks through a single L2.
 
+// value columns per compute wave, loader waves per workgroup
+#ifndef GDN2_STATE_CW
+#define GDN2_STATE_CW 32
+#endif
+#ifndef GDN2_STATE_NLW
+#define GDN2_STATE_NLW 8
+#endif
+
 template <typename Tio, int DK, int VS>
 struct StateLds {
     static constexpr int ES = (int)sizeof(Tio), KB = Io<Tio>::KB, EPL = Io<Tio>::EPL;
@@ -486,7 +494,7 @@ struct StateLds {
     static constexpr int NB = (2 * GBUF * 16 + PRIV <= LIMIT) ? 2 : 1;
     static constexpr bool FITS = GBUF * 16 + PRIV <= LIMIT;
     static constexpr int BYTES = NB * GBUF * 16 + PRIV;
-    static constexpr int NLD = 256;                 // loader lanes
+    static constexpr int NLD = 64 * GDN2_STATE_NLW; // loader lanes
     static constexpr int LPL = (GBUF + NLD - 1) / NLD;   // granules per loader lane per chunk
 };
 
@@ -504,12 +512,9 @@ inline int state_lds_bytes(int dk, int vs, int es)
     return 0;
 }
 
-#ifndef GDN2_STATE_CW
-#define GDN2_STATE_CW 32
-#endif
 // value columns per compute wave and threads per workgroup of the state pass
 __host__ __device__ constexpr int state_cw(int vs) { return vs < GDN2_STATE_CW ? vs : GDN2_STATE_CW; }
-__host__ __device__ constexpr int state_threads(int vs) { return 64 * (4 * (vs / state_cw(vs)) + 4); }
+__host__ __device__ constexpr int state_threads(int vs) { return 64 * (4 * (vs / state_cw(vs)) + GDN2_STATE_NLW); }
 
 template <typename Tio, int DK, int VS>
 __global__ __launch_bounds__(state_threads(VS), 1) void k_chunk_state(StateArgs a)
@@ -562,12 +567,12 @@ __global__ __launch_bounds__(state_threads(VS), 1) void k_chunk_state(StateArgs 
 
     if (loader) {
         // ---------------- loader waves ------------------------------------
-        // granule g = (wave-4)*64 + lane + 256*m of a buffer: source offset in
-        // the workspace block and destination in the buffer (constant per chunk)
+        // granule g = (wave - NCW)*64 + lane + NLD*m of a buffer: source offset
+        // in the workspace block and destination in the buffer (constant per chunk)
         int src[LPL], dst[LPL];
 #pragma unroll
         for (int m = 0; m < LPL; ++m) {
-            int g = (wave - NCW) * 64 + lane + 256 * m;
+            int g = (wave - NCW) * 64 + lane + L::NLD * m;
             if (g >= L::GBUF) g = L::GBUF - 1;           // idle lanes repeat the last granule
             // granule x of a section whose rows hold GPR granules (compile-time
             // widths keep the index arithmetic to shifts and masks); stored
@@ -589,9 +594,11 @@ __global__ __launch_bounds__(state_threads(VS), 1) void k_chunk_state(StateArgs 
         }
         // register slots of chunks in flight: as many (up to three) as fit in
         // the registers a lane has next to the compute waves' budget
-        constexpr int NW = NCW + 4;
-        constexpr int VBUDGET = (NW <= 8 ? 256 : (NW <= 12 ? 168 : 128)) - 56;
-        constexpr int DEPTH = LPL * 4 * 3 <= VBUDGET ? 3 : (LPL * 4 * 2 <= VBUDGET ? 2 : 1);
+        constexpr int NW = NCW + GDN2_STATE_NLW;
+        constexpr int WAVES_PER_SIMD = (NW + 3) / 4;
+        constexpr int VBUDGET = (WAVES_PER_SIMD <= 2 ? 256 : (WAVES_PER_SIMD == 3 ? 168 : 128)) - 2 * LPL - 16;
+        constexpr int DEPTH0 = VBUDGET / (4 * LPL);
+        constexpr int DEPTH = DEPTH0 > 5 ? 5 : (DEPTH0 < 1 ? 1 : DEPTH0);
         frag r[DEPTH][LPL];
         // granules [m0, m1) of chunk n into / out of a register slot
         auto fetch = [&](int n, frag* rs, int m0, int m1) {
@@ -610,45 +617,49 @@ __global__ __launch_bounds__(state_threads(VS), 1) void k_chunk_state(StateArgs 
         // LDS and chunk n+1+DEPTH is requested into the slot it leaves, half
         // before barrier 1 and half after it, so that the copy overlaps both
         // compute phases and barrier 1 (which orders the compute waves' Delta
-        // exchange) does not wait for the whole copy.
+        // exchange) does not wait for the whole copy.  Every iteration issues
+        // the same loads and stores (chunk numbers past the end are clamped,
+        // and a copy past the end lands in the buffer no one reads any more):
+        // with no conditional fetch the compiler can count exactly how many
+        // loads are still in flight behind the ones a store needs, so the
+        // stores wait only for their own chunk, DEPTH iterations old.
         constexpr int HALF = LPL / 2;
         auto iter = [&](int n, frag* rs) {
-            const bool go = NB == 2 && n + 1 < nt;
-            if (go) {
+            if (NB == 2) {
                 store((n + 1) & 1, rs, 0, HALF);
                 fetch(n + 1 + DEPTH, rs, 0, HALF);
-            }
-            __syncthreads();                              // barrier 1
-            if (go) {
+                __syncthreads();                          // barrier 1
                 store((n + 1) & 1, rs, HALF, LPL);
                 fetch(n + 1 + DEPTH, rs, HALF, LPL);
-            }
-            __syncthreads();                              // barrier 2
-            if (NB == 1) {
-                if (n + 1 < nt) {
-                    store(0, rs, 0, LPL);
-                    fetch(n + 1 + DEPTH, rs, 0, LPL);
-                }
+                __syncthreads();                          // barrier 2
+            } else {
+                __syncthreads();                          // barrier 1
+                __syncthreads();                          // barrier 2: chunk n done
+                store(0, rs, 0, LPL);
+                fetch(n + 1 + DEPTH, rs, 0, LPL);
                 __syncthreads();                          // barrier 3: buffer refilled
             }
         };
+        if (nt == 0) {                                    // state copy only
+            __syncthreads();                              // prologue barrier
+            return;
+        }
         // chunk 0 first: the compute waves start as soon as it is in LDS
-        if (nt > 0) {
-            fetch(0, r[0], 0, LPL);
-            if (DEPTH > 1) fetch(1, r[DEPTH > 1 ? 1 : 0], 0, LPL);
-            store(0, r[0], 0, LPL);
-        }
+        fetch(0, r[0], 0, LPL);
+        if (DEPTH > 1) fetch(1, r[DEPTH > 1 ? 1 : 0], 0, LPL);
+        store(0, r[0], 0, LPL);
         __syncthreads();                                  // prologue barrier
-        if (nt > 0) {
 #pragma unroll
-            for (int d = 2; d < DEPTH; ++d) fetch(d, r[d], 0, LPL);
-            fetch(DEPTH, r[0], 0, LPL);
-        }
-        for (int n = 0; n < nt; n += DEPTH) {
+        for (int d = 2; d < DEPTH; ++d) fetch(d, r[d], 0, LPL);
+        fetch(DEPTH, r[0], 0, LPL);
+        int n = 0;
+        for (; n + DEPTH <= nt; n += DEPTH) {
 #pragma unroll
-            for (int d = 0; d < DEPTH; ++d)
-                if (n + d < nt) iter(n + d, r[(d + 1) % DEPTH]);
+            for (int d = 0; d < DEPTH; ++d) iter(n + d, r[(d + 1) % DEPTH]);
         }
+#pragma unroll
+        for (int d = 0; d < DEPTH - 1; ++d)
+            if (n + d < nt) iter(n + d, r[(d + 1) % DEPTH]);
         return;
     }
 
