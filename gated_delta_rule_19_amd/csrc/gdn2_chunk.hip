@@ -473,9 +473,11 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
 #ifndef GDN2_STATE_CW
 #define GDN2_STATE_CW 32
 #endif
-#ifndef GDN2_STATE_NLW
-#define GDN2_STATE_NLW 8
-#endif
+// loader waves: 8, or 4 where the workgroup already has 8 compute waves or
+// fp32 operands (their registers would not fit beside eight loaders)
+__host__ __device__ constexpr int state_cw(int vs) { return vs < GDN2_STATE_CW ? vs : GDN2_STATE_CW; }
+__host__ __device__ constexpr int state_nlw(int vs, int es) { return (vs / state_cw(vs) > 1 || es == 4) ? 4 : 8; }
+__host__ __device__ constexpr int state_threads(int vs, int es) { return 64 * (4 * (vs / state_cw(vs)) + state_nlw(vs, es)); }
 
 template <typename Tio, int DK, int VS>
 struct StateLds {
@@ -494,7 +496,7 @@ struct StateLds {
     static constexpr int NB = (2 * GBUF * 16 + PRIV <= LIMIT) ? 2 : 1;
     static constexpr bool FITS = GBUF * 16 + PRIV <= LIMIT;
     static constexpr int BYTES = NB * GBUF * 16 + PRIV;
-    static constexpr int NLD = 64 * GDN2_STATE_NLW; // loader lanes
+    static constexpr int NLD = 64 * state_nlw(VS, ES);   // loader lanes
     static constexpr int LPL = (GBUF + NLD - 1) / NLD;   // granules per loader lane per chunk
 };
 
@@ -513,11 +515,9 @@ inline int state_lds_bytes(int dk, int vs, int es)
 }
 
 // value columns per compute wave and threads per workgroup of the state pass
-__host__ __device__ constexpr int state_cw(int vs) { return vs < GDN2_STATE_CW ? vs : GDN2_STATE_CW; }
-__host__ __device__ constexpr int state_threads(int vs) { return 64 * (4 * (vs / state_cw(vs)) + GDN2_STATE_NLW); }
 
 template <typename Tio, int DK, int VS>
-__global__ __launch_bounds__(state_threads(VS), 1) void k_chunk_state(StateArgs a)
+__global__ __launch_bounds__(state_threads(VS, (int)sizeof(Tio)), 1) void k_chunk_state(StateArgs a)
 {
     using IO = Io<Tio>;
     using L = StateLds<Tio, DK, VS>;
@@ -573,7 +573,10 @@ __global__ __launch_bounds__(state_threads(VS), 1) void k_chunk_state(StateArgs 
 #pragma unroll
         for (int m = 0; m < LPL; ++m) {
             int g = (wave - NCW) * 64 + lane + L::NLD * m;
-            if (g >= L::GBUF) g = L::GBUF - 1;           // idle lanes repeat the last granule
+            // idle slots copy a granule some other lane copies too (the same
+            // bytes to the same place); distinct addresses keep their loads
+            // and LDS writes spread over banks instead of piling onto one
+            g %= L::GBUF;
             // granule x of a section whose rows hold GPR granules (compile-time
             // widths keep the index arithmetic to shifts and masks); stored
             // granule = (row, column ^ swz(row))
@@ -594,7 +597,7 @@ __global__ __launch_bounds__(state_threads(VS), 1) void k_chunk_state(StateArgs 
         }
         // register slots of chunks in flight: as many (up to three) as fit in
         // the registers a lane has next to the compute waves' budget
-        constexpr int NW = NCW + GDN2_STATE_NLW;
+        constexpr int NW = NCW + state_nlw(VS, ES);
         constexpr int WAVES_PER_SIMD = (NW + 3) / 4;
         constexpr int VBUDGET = (WAVES_PER_SIMD <= 2 ? 256 : (WAVES_PER_SIMD == 3 ? 168 : 128)) - 2 * LPL - 16;
         constexpr int DEPTH0 = VBUDGET / (4 * LPL);
@@ -721,6 +724,31 @@ __global__ __launch_bounds__(state_threads(VS), 1) void k_chunk_state(StateArgs 
         frag fsb[2][NKX];
 #pragma unroll
         for (int kb = 0; kb < NKX; ++kb) fsb[0][kb] = ld_frag(&SbT[(jc + l16) * SRS + kb * KB + grp * EPL]);
+        // operands that do not depend on this chunk's products are read now,
+        // so that only the Delta reads remain behind barrier 1
+        vec4 u4[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int row = jc + 16 * ct + l16, r = 16 * tb + 4 * grp;
+            const int g = (r * ES / 16) ^ swz(row, GT);
+            u4[ct] = *reinterpret_cast<const vec4*>(Ul + (row * GT + g) * 16 + (r * ES) % 16);
+        }
+        frag fp[NKT], fk[SPW][NKT];
+        f32x4 gl[SPW];
+#pragma unroll
+        for (int kb = 0; kb < NKT; ++kb) {
+            fp[kb] = lfrag(Pl, 16 * tb + l16, GT, kb);
+#pragma unroll
+            for (int i = 0; i < SPW; ++i) {
+                const int rt = tb * SPW + i < SRT ? tb * SPW + i : SRT - 1;
+                fk[i][kb] = lfrag(Kl, 16 * rt + l16, GT, kb);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const int rt = tb * SPW + i < SRT ? tb * SPW + i : SRT - 1;
+            gl[i] = *reinterpret_cast<const f32x4*>(Gl + 16 * rt + 4 * grp);
+        }
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
             if (ct + 1 < NCT) {
@@ -742,29 +770,11 @@ __global__ __launch_bounds__(state_threads(VS), 1) void k_chunk_state(StateArgs 
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
             const int row = jc + 16 * ct + l16, r = 16 * tb + 4 * grp;
-            const int g = (r * ES / 16) ^ swz(row, GT);
-            const vec4 u4 = *reinterpret_cast<const vec4*>(Ul + (row * GT + g) * 16 + (r * ES) % 16);
-            st_vec4(&DT[row * DTS + r], IO::unpack4(u4) - accW[ct]);
+            st_vec4(&DT[row * DTS + r], IO::unpack4(u4[ct]) - accW[ct]);
         }
         __syncthreads();                                  // barrier 1
 
         // O^T += Delta^T P^T;  S = diag(Gamma_L) S + Ktil^T Delta
-        frag fp[NKT], fk[SPW][NKT];
-        f32x4 gl[SPW];
-#pragma unroll
-        for (int kb = 0; kb < NKT; ++kb) {
-            fp[kb] = lfrag(Pl, 16 * tb + l16, GT, kb);
-#pragma unroll
-            for (int i = 0; i < SPW; ++i) {
-                const int rt = tb * SPW + i < SRT ? tb * SPW + i : SRT - 1;
-                fk[i][kb] = lfrag(Kl, 16 * rt + l16, GT, kb);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < SPW; ++i) {
-            const int rt = tb * SPW + i < SRT ? tb * SPW + i : SRT - 1;
-            gl[i] = *reinterpret_cast<const f32x4*>(Gl + 16 * rt + 4 * grp);
-        }
 #pragma unroll
         for (int i = 0; i < SPW; ++i)
 #pragma unroll
@@ -877,7 +887,7 @@ static hipError_t state_v(const StateArgs& a, hipStream_t s)
         return hipErrorInvalidValue;
     } else {
         const int64_t nblk = a.B * a.H * (int64_t)a.nslices;
-        constexpr int nthreads = state_threads(VS);
+        constexpr int nthreads = state_threads(VS, (int)sizeof(Tio));
         hipLaunchKernelGGL((k_chunk_state<Tio, DK, VS>), dim3((unsigned)nblk), dim3(nthreads), 0, s, a);
         return hipGetLastError();
     }
