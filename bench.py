@@ -14,6 +14,7 @@ launch stream); the decode step's HBM rate is reported beside it.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --copy-calibration      # plain 1 GiB copies, for counter scaling
     python bench.py --pmc-summary DIR ...   # fold rocprofv3 counter CSVs into profiles/
+    python bench.py --util-summary DIR,...  # fold MFMA / LDS counter runs into profiles/
 """
 from __future__ import annotations
 
@@ -32,6 +33,7 @@ if ROOT not in sys.path:
 PEAK_HBM_GBPS = 8000.0            # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2500.0         # MI355X dense bf16 matrix, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+UTIL_FILE = os.path.join(ROOT, "profiles", "pmc_util.json")
 KERNEL_SOURCES = ["gated_delta_rule_19_amd/csrc/gdn2_chunk.hip", "gated_delta_rule_19_amd/csrc/gdn2_recurrent.hip",
                   "gated_delta_rule_19_amd/csrc/gdn2_device.hpp", "gated_delta_rule_19_amd/csrc/gdn2_layout.hpp"]
 KERNEL_NAMES = {"prep": "k_chunk_prep", "state": "k_chunk_state", "decode": "k_recurrent"}
@@ -75,6 +77,7 @@ def parse_args(argv=None):
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--pmc-summary", metavar="DIR", default=None)
     ap.add_argument("--copy-pmc", metavar="DIR", default=None)
+    ap.add_argument("--util-summary", metavar="DIRS", default=None)
     return ap.parse_args(argv)
 
 
@@ -151,6 +154,36 @@ def pmc_summary(dirs, copy_dirs):
     print(json.dumps(out))
 
 
+def util_summary(dirs):
+    """Fold counter runs (MfmaUtil, MfmaFlopsBF16, LDS counters, ...) into profiles/pmc_util.json:
+    per kernel, each counter averaged over its dispatches."""
+    out = {"kernel_sha": kernel_sha(), "kernels": {}}
+    for d in dirs:
+        per = _read_counter_csvs(d)
+        for key, kname in KERNEL_NAMES.items():
+            ctrs = sorted({c for (disp, name, c) in per if kname in name})
+            for ctr in ctrs:
+                vals = [v for (disp, name, c), v in per.items() if c == ctr and kname in name]
+                out["kernels"].setdefault(key, {})[ctr] = sum(vals) / len(vals)
+                out["kernels"][key][ctr + "_dispatches"] = len(vals)
+    os.makedirs(os.path.dirname(UTIL_FILE), exist_ok=True)
+    with open(UTIL_FILE, "w") as fh:
+        json.dump(out, fh, indent=1, sort_keys=True)
+    print(json.dumps(out))
+
+
+def load_util(key):
+    """Counter averages for kernel `key` from the committed summary, or None when stale."""
+    try:
+        with open(UTIL_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha") != kernel_sha():
+        return None
+    return t.get("kernels", {}).get(key)
+
+
 def load_traffic(key):
     """HBM bytes per launch of kernel `key` from the committed counter summary, or None."""
     try:
@@ -180,6 +213,8 @@ def main(argv=None):
         return 2
     if args.copy_calibration:
         return copy_calibration()
+    if args.util_summary:
+        return util_summary(args.util_summary.split(","))
     if args.pmc_summary:
         dirs = args.pmc_summary.split(",")
         copy_dirs = args.copy_pmc.split(",") if args.copy_pmc else []
@@ -229,9 +264,16 @@ def main(argv=None):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / max(args.steps, 1)
-    prep_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    state_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    dec_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    per_step = {"prep": sorted(e[0].elapsed_time(e[1]) for e in evs),
+                "state": sorted(e[1].elapsed_time(e[2]) for e in evs),
+                "decode": sorted(e[2].elapsed_time(e[3]) for e in evs),
+                "chunk": sorted(e[0].elapsed_time(e[2]) for e in evs)}
+    prep_ms = sum(per_step["prep"]) / args.steps
+    state_ms = sum(per_step["state"]) / args.steps
+    dec_ms = sum(per_step["decode"]) / args.steps
+    spread = {k_: {"median_us": round(v_[len(v_) // 2] * 1e3, 2), "min_us": round(v_[0] * 1e3, 2)}
+              for k_, v_ in per_step.items()}
+    copy_gbps = device_copy_gbps(dev)
     chunk_ms = prep_ms + state_ms
 
     ht = B * T * H
@@ -255,10 +297,15 @@ def main(argv=None):
         k_ = kern[key]
         ach = gbps(k_["alg"], k_["ms"])
         tr = load_traffic(key)
-        return {"kernel": KERNEL_NAMES[key], "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS,
-                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4),
-                "traffic": None if tr is None else round(tr), "alg_bytes": int(k_["alg"]),
-                "us_per_launch": round(k_["ms"] * 1e3, 2)}
+        r = {"kernel": KERNEL_NAMES[key], "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS,
+             "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4),
+             "traffic": None if tr is None else round(tr), "alg_bytes": int(k_["alg"]),
+             "us_per_launch": round(k_["ms"] * 1e3, 2)}
+        r.update(spread[key])
+        u = load_util(key)
+        if u is not None and "MfmaUtil" in u:
+            r["mfma_busy_pct"] = round(u["MfmaUtil"], 2)
+        return r
 
     chunk_gbps = gbps(alg_chunk, chunk_ms)
     result = {
@@ -284,9 +331,12 @@ def main(argv=None):
                       "frac_hbm_roofline": round(chunk_gbps / PEAK_HBM_GBPS, 4),
                       "useful_TFLOPs": round(flops / (chunk_ms * 1e-3) / 1e12, 2),
                       "frac_bf16_mfma_peak": round(flops / (chunk_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                      "median_us": spread["chunk"]["median_us"], "min_us": spread["chunk"]["min_us"],
                       "roofline_prep": roof("prep"), "roofline_state": roof("state")},
         "decode": {"us": round(dec_ms * 1e3, 2), "GBps": round(gbps(alg_dec, dec_ms), 1),
                    "frac_hbm_peak": round(gbps(alg_dec, dec_ms) / PEAK_HBM_GBPS, 4),
+                   "device_copy_GBps": round(copy_gbps, 1),
+                   "frac_of_device_copy": round(gbps(alg_dec, dec_ms) / copy_gbps, 4),
                    "roofline": roof("decode")},
     }
     ok = bool(torch.isfinite(outs[0].float()).all() and torch.isfinite(states[0]).all()
@@ -297,6 +347,36 @@ def main(argv=None):
         result["cpu_baseline"] = cpu_baseline(sets[0], args.cpu_chains, B, T, H, dk, dv)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def device_copy_gbps(dev, nbytes=1 << 30, reps=5):
+    """Read + write rate of a plain 1 GiB device-to-device copy (the runtime's blit kernel):
+    the HBM rate a streaming kernel can reach on this machine."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(inp, chains, B, T, H, dk, dv):
@@ -319,7 +399,7 @@ def cpu_baseline(inp, chains, B, T, H, dk, dv):
     dt = time.perf_counter() - t0
     frac = nb * H / float(B * H)
     tok_s = B * T / (dt / frac)
-    return {"value": round(tok_s, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": round(tok_s, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu": cpu_model(),
             "sample": f"fp64 C oracle (OpenMP over head x 16-column blocks) on {nb * H} of {B * H} "
                       f"(batch, head) chains x {T} tokens of the same inputs: {dt:.2f} s",
             "seconds": round(dt, 3)}
