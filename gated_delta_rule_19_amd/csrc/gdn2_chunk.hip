@@ -50,6 +50,12 @@ __host__ __device__ constexpr int swz(int row, int g)
 {
     return (row / (g >= 8 ? 1 : 8 / g)) % (g >= 16 ? 16 : g);
 }
+// variant for rows of >= 8 granules that are also written by lanes striding 4
+// rows apart (rows 4c + e): row + row/4 keeps both patterns spread
+__host__ __device__ constexpr int swzu(int row, int g)
+{
+    return (row + row / 4) % (g >= 16 ? 16 : g);
+}
 
 template <typename Tio, int DK>
 struct PrepSmem {
@@ -65,7 +71,8 @@ struct PrepSmem {
     static constexpr int SZ_TD = 4 * 16 * 20 * 4;   // TD: diagonal blocks of T, row-major
     // R0: Xe -> A32 -> EhT;  R1: Xq -> T32T -> UT;  R2: Yd -> (Tm, TD)
     static constexpr int R0 = align16(imax(imax(SZ_X, SZ_F), SZ_E));
-    static constexpr int R1 = align16(imax(imax(SZ_X, SZ_F), SZ_T));
+    static constexpr int SZ_U = 64 * 64 * ES;     // UT [64 columns][64 tokens], swizzled rows
+    static constexpr int R1 = align16(imax(imax(SZ_X, SZ_F), SZ_U));
     static constexpr int R2 = align16(imax(SZ_X, SZ_T + SZ_TD));
     static constexpr int O1 = R0, O2 = O1 + R1, OF = O2 + R2;
     // Fs [7][KPAD]: rows 0..5 the per-channel decay factors of the block pairs
@@ -116,7 +123,9 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
     // element offsets in the swizzled arrays
     auto xo = [](int r, int c) { return r * KPAD + (((c / EPG) ^ swz(r, GX)) * EPG) + c % EPG; };   // [64][KPAD]
     auto fo = [](int r, int c) { return r * 64 + (((c / 4) ^ swz(r, 16)) * 4) + c % 4; };          // fp32 [64][64]
-    auto eo = [](int r, int c) { return r * 64 + (((c / EPG) ^ swz(r, GE)) * EPG) + c % EPG; };      // [DK][64]
+    // [DK][64] and [64][64] arrays written by rows 4c+e and read by rows 16t+l
+    auto eo = [](int r, int c) { return r * 64 + (((c / EPG) ^ swzu(r, GE)) * EPG) + c % EPG; };     // EhT
+    auto uo = [](int r, int c) { return r * 64 + (((c / EPG) ^ swzu(r, GE)) * EPG) + c % EPG; };     // UT
 
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
@@ -262,18 +271,24 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
     }
 
     // ---- value-axis loads: u = w * v, needed from phase 5 on ----------------
-    // value-axis item = (token s, 4 columns)
-    constexpr int NVQ_MAX = NUI;
-    f32x4 wr[NVQ_MAX];
-    typename IO::vec4 vr[NVQ_MAX];
+    // value-axis item = (8-token group sg, 4 columns 4jq..4jq+3): a lane holds
+    // 8 tokens of each of its columns, so that (w*v)^T goes to LDS as whole
+    // 8-token fragments
+    constexpr int NIT = NUI <= 8 ? 1 : 2;     // items per thread: 8 * dv/4 <= 256 * NIT
+    f32x4 wr[NIT][8];
+    typename IO::vec4 vr[NIT][8];
     const int nvq = a.dv / 4;
 #pragma unroll
-    for (int m = 0; m < NVQ_MAX; ++m) {
-        const int u = tid + m * kThreads;
-        const int jq = u % nvq, s = u / nvq;
-        const int64_t off = (row0 + (s < L ? s : L - 1) * H) * a.dv + 4 * jq;
-        wr[m] = *reinterpret_cast<const f32x4*>(a.w + off);
-        vr[m] = *reinterpret_cast<const typename IO::vec4*>(v + off);
+    for (int it = 0; it < NIT; ++it) {
+        const int q = tid + it * kThreads;
+        const int jq = q % nvq, sg = (q / nvq) & 7;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int s = 8 * sg + i;
+            const int64_t off = (row0 + (s < L ? s : L - 1) * H) * a.dv + 4 * jq;
+            wr[it][i] = *reinterpret_cast<const f32x4*>(a.w + off);
+            vr[it][i] = *reinterpret_cast<const typename IO::vec4*>(v + off);
+        }
     }
     __syncthreads();
 
@@ -410,21 +425,30 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
     }
 
     // ---- 5. U = T (w * v), stored transposed, in column blocks of 64 --------
-    f32x4 uu[NVQ_MAX];
+    // (w*v) of tokens past the sequence end is zero
+    frag uf[NIT][4][8 / EPL];      // per item and column: the 8 tokens as fragments
 #pragma unroll
-    for (int m = 0; m < NVQ_MAX; ++m) {
-        const int s = (tid + m * kThreads) / nvq;
-        uu[m] = (s < L && s < 64) ? wr[m] * IO::unpack4(vr[m]) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < NIT; ++it) {
+        const int sg = ((tid + it * kThreads) / nvq) & 7;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const f32x4 u4 = (8 * sg + i < L) ? wr[it][i] * IO::unpack4(vr[it][i]) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) uf[it][e][i / EPL][i % EPL] = IO::from_f(u4[e]);
+        }
     }
     for (int j0 = 0; j0 < a.dv; j0 += 64) {
         const int nj = (a.dv - j0) < 64 ? (a.dv - j0) : 64;
 #pragma unroll
-        for (int m = 0; m < NVQ_MAX; ++m) {
-            const int u = tid + m * kThreads;
-            const int j = 4 * (u % nvq), s = u / nvq;
-            if (s < 64 && j >= j0 && j < j0 + nj) {
+        for (int it = 0; it < NIT; ++it) {
+            const int q = tid + it * kThreads;
+            const int c = 4 * (q % nvq) - j0, sg = q / nvq;
+            if (sg < 8 && c >= 0 && c < nj) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) UT[(j - j0 + e) * TS + s] = IO::from_f(uu[m][e]);
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int f = 0; f < 8 / EPL; ++f)
+                        *reinterpret_cast<frag*>(UT + uo(c + e, 8 * sg + EPL * f)) = uf[it][e][f];
             }
         }
         __syncthreads();
@@ -433,7 +457,7 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
 #pragma unroll
             for (int kb = 0; kb < 64 / KB; ++kb) {
                 if (kb * KB <= 16 * wave + 15) {
-                    const frag fu = ld_frag(UT + (16 * jt + l16) * TS + kb * KB + grp * EPL);
+                    const frag fu = ld_frag(UT + uo(16 * jt + l16, kb * KB + grp * EPL));
                     acc = IO::mma(acc, tf[kb], fu);
                 }
             }
