@@ -15,6 +15,12 @@ Recipe (per workload; draw order q, k, v, alpha-logits, b-logits, w-logits, S0):
           README's negative-eigenvalue option, "b x 2");
   w     = sigmoid(N(0, 1)) per value channel, fp32;
   S0    = N(0, s0_std) fp32 when s0_std is given, else no initial state.
+
+Prologue variants (for the kernels' in-kernel prologue options):
+  gate_logits=True returns the gates' pre-activation draws instead of their
+  sigmoids (alpha-logit ~ N(alpha_mu, 1), b-logit ~ N(0, 1), w-logit ~ N(0, 1);
+  b_scale is then the kernels' job), unit_qk=False leaves q and k unnormalised
+  (N(0, 1) rows), and gate_dtype sets the gates' dtype (rounded RNE).
 """
 from __future__ import annotations
 
@@ -74,7 +80,7 @@ def make(wl: Workload, seed: int, device="cpu", B=None, T=None, H=None):
 
 
 def make_raw(B, T, H, dk, dv, io_dtype, seed, device="cpu", alpha_mu=3.0,
-             b_scale=1.0, s0_std=None):
+             b_scale=1.0, s0_std=None, gate_logits=False, unit_qk=True, gate_dtype=torch.float32):
     dev = torch.device(device)
     g = torch.Generator(device=dev)
     g.manual_seed(int(seed))
@@ -87,12 +93,16 @@ def make_raw(B, T, H, dk, dv, io_dtype, seed, device="cpu", alpha_mu=3.0,
         n = torch.linalg.vector_norm(x, dim=-1, keepdim=True)
         return x / torch.clamp(n, min=1e-30)
 
-    q = unit_rows(randn(B, T, H, dk)).to(io_dtype)
-    k = unit_rows(randn(B, T, H, dk)).to(io_dtype)
+    rows = unit_rows if unit_qk else (lambda x: x)
+    q = rows(randn(B, T, H, dk)).to(io_dtype)
+    k = rows(randn(B, T, H, dk)).to(io_dtype)
     v = randn(B, T, H, dv).to(io_dtype)
-    alpha = torch.sigmoid(randn(B, T, H, dk) + alpha_mu)
-    b = b_scale * torch.sigmoid(randn(B, T, H, dk))
-    w = torch.sigmoid(randn(B, T, H, dv))
+    la, lb, lw = randn(B, T, H, dk) + alpha_mu, randn(B, T, H, dk), randn(B, T, H, dv)
+    if gate_logits:
+        alpha, b, w = la, lb, lw
+    else:
+        alpha, b, w = torch.sigmoid(la), b_scale * torch.sigmoid(lb), torch.sigmoid(lw)
+    alpha, b, w = alpha.to(gate_dtype), b.to(gate_dtype), w.to(gate_dtype)
     S0 = None
     if s0_std is not None:
         S0 = randn(B, H, dk, dv) * s0_std

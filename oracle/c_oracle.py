@@ -26,7 +26,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(LIB_PATH):
         tmp = LIB_PATH + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared",
-                               "-o", tmp, SRC_PATH])
+                               "-o", tmp, SRC_PATH, "-lm"])
         os.replace(tmp, LIB_PATH)
     return LIB_PATH
 
@@ -40,7 +40,7 @@ def _load():
         f = lib.gdn2_oracle_f64
         f.restype = ctypes.c_int
         i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
-        f.argtypes = [i64] * 5 + [vp] * 9 + [ci, i64]
+        f.argtypes = [i64] * 5 + [vp] * 9 + [ci, i64, ci]
         lib.gdn2_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -54,8 +54,10 @@ def _f32(x):
     return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
 
 
-def recurrent(q, k, v, alpha, b, w, S0=None, nthreads: int = 0, col_block: int = 16):
-    """fp64 recurrence; returns (o, S_T) as float64 arrays."""
+def recurrent(q, k, v, alpha, b, w, S0=None, nthreads: int = 0, col_block: int = 16, flags: int = 0):
+    """fp64 recurrence; returns (o, S_T) as float64 arrays.  ``flags``: the prologue options
+    (1 gate logits -> sigmoid, 2 with 1: b = 2 sigmoid(b), 4 q/k L2 norm), as in
+    ``oracle.reference.prologue``."""
     q, k, v, alpha, b, w = map(_f32, (q, k, v, alpha, b, w))
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -69,7 +71,7 @@ def recurrent(q, k, v, alpha, b, w, S0=None, nthreads: int = 0, col_block: int =
     S = np.zeros((B, H, dk, dv), dtype=np.float64)
     p = lambda a: None if a is None else a.ctypes.data
     rc = _load().gdn2_oracle_f64(B, T, H, dk, dv, p(q), p(k), p(v), p(alpha), p(b), p(w),
-                                 p(S0a), p(o), p(S), int(nthreads), int(col_block))
+                                 p(S0a), p(o), p(S), int(nthreads), int(col_block), int(flags))
     if rc != 0:
         raise RuntimeError("oracle: bad sizes")
     return o, S

@@ -42,11 +42,50 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["recurrent", "chunked_wy", "rel_l2"]
+__all__ = ["recurrent", "chunked_wy", "rel_l2", "prologue", "sigmoid",
+           "FLAG_GATE_LOGITS", "FLAG_NEG_EIGVAL", "FLAG_QK_L2NORM"]
+
+# prologue options (the library's GDN2_FLAG_* values)
+FLAG_GATE_LOGITS, FLAG_NEG_EIGVAL, FLAG_QK_L2NORM = 1, 2, 4
+L2NORM_EPS = 1e-6
 
 
 def _f64(x):
     return None if x is None else np.asarray(x, dtype=np.float64)
+
+
+def sigmoid(x):
+    """Logistic function 1 / (1 + exp(-x)), fp64."""
+    x = _f64(x)
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def prologue(q, k, alpha, b, w, flags=0):
+    """The steps the layer runs right before the core, as optional flags.
+
+    burn-gdn2 README, "Architecture" diagram: the Q/K/V/B/W/G projections are
+    followed by L2-Norm before the recurrence, and "Configuration" lists
+    allow_neg_eigval ("b x 2").  The README does not name the gate activation;
+    the logistic sigmoid is the reading taken here (the synthetic workloads
+    draw their gates as sigmoids of normal logits).
+
+      FLAG_GATE_LOGITS: alpha, b, w are pre-activations -> sigmoid(.)
+      FLAG_NEG_EIGVAL (with GATE_LOGITS): b -> 2 * sigmoid(b)
+      FLAG_QK_L2NORM: q, k -> x / sqrt(sum over d_k of x^2 + 1e-6), per row
+
+    Returns fp64 (q, k, alpha, b, w), ready for ``recurrent``/``chunked_wy``.
+    """
+    q, k, alpha, b, w = map(_f64, (q, k, alpha, b, w))
+    if flags & FLAG_NEG_EIGVAL and not flags & FLAG_GATE_LOGITS:
+        raise ValueError("NEG_EIGVAL needs GATE_LOGITS")
+    if flags & FLAG_GATE_LOGITS:
+        alpha = sigmoid(alpha)
+        b = sigmoid(b) * (2.0 if flags & FLAG_NEG_EIGVAL else 1.0)
+        w = sigmoid(w)
+    if flags & FLAG_QK_L2NORM:
+        q = q / np.sqrt(np.sum(q * q, axis=-1, keepdims=True) + L2NORM_EPS)
+        k = k / np.sqrt(np.sum(k * k, axis=-1, keepdims=True) + L2NORM_EPS)
+    return q, k, alpha, b, w
 
 
 def recurrent(q, k, v, alpha, b, w, S0=None):
