@@ -6,6 +6,9 @@ GDN-2 recurrence, with hand-written HIP kernels doing all the arithmetic.
 The library is loaded on first use; a missing library raises.
 """
 from ._binding import (  # noqa: F401
+    FLAG_GATE_LOGITS,
+    FLAG_NEG_EIGVAL,
+    FLAG_QK_L2NORM,
     Gdn2Error,
     Problem,
     abi_version,

@@ -17,6 +17,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn2.so")
 
 GDN2_F32, GDN2_BF16 = 0, 1
+FLAG_GATE_LOGITS, FLAG_NEG_EIGVAL, FLAG_QK_L2NORM = 1, 2, 4
 _STATUS = {0: "GDN2_OK", 1: "GDN2_ERR_NULL", 2: "GDN2_ERR_SHAPE", 3: "GDN2_ERR_DTYPE",
            4: "GDN2_ERR_ALIAS", 5: "GDN2_ERR_WORKSPACE", 6: "GDN2_ERR_DEVICE", 7: "GDN2_ERR_ALIGN"}
 EXPORTED = ("gdn2_abi_version", "gdn2_status_str", "gdn2_chunk_fwd_workspace_size",
@@ -28,7 +29,7 @@ class Problem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
                 ("dk", ctypes.c_int64), ("dv", ctypes.c_int64), ("chunk", ctypes.c_int32),
                 ("io_dtype", ctypes.c_int32), ("gate_dtype", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("flags", ctypes.c_int32)]
 
 
 class Gdn2Error(RuntimeError):
@@ -88,12 +89,13 @@ def _stream(dev: torch.device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
-def problem(B, T, H, dk, dv, io_dtype: torch.dtype, chunk: int = 64) -> Problem:
-    io = {torch.float32: GDN2_F32, torch.bfloat16: GDN2_BF16}.get(io_dtype, -1)
-    return Problem(B, T, H, dk, dv, chunk, io, GDN2_F32, 0)
+def problem(B, T, H, dk, dv, io_dtype: torch.dtype, chunk: int = 64, gate_dtype: torch.dtype = torch.float32,
+            flags: int = 0) -> Problem:
+    code = {torch.float32: GDN2_F32, torch.bfloat16: GDN2_BF16}
+    return Problem(B, T, H, dk, dv, chunk, code.get(io_dtype, -1), code.get(gate_dtype, -1), int(flags))
 
 
-def _problem_from(q, k, v, alpha, b, w) -> Tuple[Problem, torch.device]:
+def _problem_from(q, k, v, alpha, b, w, flags: int = 0) -> Tuple[Problem, torch.device]:
     if q.dim() != 4 or v.dim() != 4:
         raise ValueError("q/k/alpha/b must be [B,T,H,dk] and v/w [B,T,H,dv]")
     B, T, H, dk = q.shape
@@ -103,16 +105,15 @@ def _problem_from(q, k, v, alpha, b, w) -> Tuple[Problem, torch.device]:
             raise ValueError(f"{name} has shape {tuple(x.shape)}, expected {(B, T, H, last)}")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("q, k, v must share one dtype: float32 or bfloat16")
-    for name, x in (("alpha", alpha), ("b", b), ("w", w)):
-        if x.dtype != torch.float32:
-            raise TypeError(f"{name} must be float32")
+    if not (alpha.dtype == b.dtype == w.dtype) or alpha.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("alpha, b, w must share one dtype: float32 or bfloat16")
     dev = q.device
     for name, x in (("q", q), ("k", k), ("v", v), ("alpha", alpha), ("b", b), ("w", w)):
         if x.device != dev or dev.type != "cuda":
             raise ValueError(f"{name} must be a GPU tensor on {dev}")
         if not x.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    return problem(B, T, H, dk, dv, q.dtype), dev
+    return problem(B, T, H, dk, dv, q.dtype, gate_dtype=alpha.dtype, flags=flags), dev
 
 
 def _check_state(S, p: Problem, dev, name):
@@ -125,6 +126,7 @@ def _check_state(S, p: Problem, dev, name):
 
 
 def chunk_fwd_workspace_size(B, T, H, dk, dv, io_dtype: torch.dtype) -> int:
+    # the workspace size does not depend on the gate dtype or the flags
     return int(lib().gdn2_chunk_fwd_workspace_size(ctypes.byref(problem(B, T, H, dk, dv, io_dtype))))
 
 
@@ -134,9 +136,10 @@ def alloc_workspace(nbytes: int, device) -> torch.Tensor:
 
 
 def chunk_fwd(q, k, v, alpha, b, w, S0=None, *, out_state: bool = True, o=None, S_out=None,
-              workspace=None):
-    """Chunked forward (``gdn2_chunk_fwd``).  Returns (o, S_final or None)."""
-    p, dev = _problem_from(q, k, v, alpha, b, w)
+              workspace=None, flags: int = 0):
+    """Chunked forward (``gdn2_chunk_fwd``).  Returns (o, S_final or None).
+    ``flags``: FLAG_* prologue options (gate logits, negative-eigenvalue b, q/k L2 norm)."""
+    p, dev = _problem_from(q, k, v, alpha, b, w, flags)
     _check_state(S0, p, dev, "S0")
     if o is None:
         o = torch.empty(v.shape, dtype=v.dtype, device=dev)
@@ -152,9 +155,9 @@ def chunk_fwd(q, k, v, alpha, b, w, S0=None, *, out_state: bool = True, o=None, 
     return o, S_out
 
 
-def chunk_prep(q, k, v, alpha, b, w, workspace):
+def chunk_prep(q, k, v, alpha, b, w, workspace, flags: int = 0):
     """First stage of the chunked forward (``gdn2_chunk_prep``): fills ``workspace``."""
-    p, dev = _problem_from(q, k, v, alpha, b, w)
+    p, dev = _problem_from(q, k, v, alpha, b, w, flags)
     _check(lib().gdn2_chunk_prep(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w),
                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
                                  _stream(dev)))
@@ -170,13 +173,13 @@ def chunk_state(p: Problem, workspace, o, S0=None, S_out=None):
 
 
 def recurrent_step(q, k, v, alpha, b, w, S_in=None, *, o=None, S_out=None, out_state: bool = True,
-                   inplace: bool = False):
+                   inplace: bool = False, flags: int = 0):
     """Fused recurrent forward (``gdn2_recurrent_step``); T == 1 is one decode step.
 
     ``inplace=True`` writes the final state back into ``S_in``.
     Returns (o, S_final or None).
     """
-    p, dev = _problem_from(q, k, v, alpha, b, w)
+    p, dev = _problem_from(q, k, v, alpha, b, w, flags)
     _check_state(S_in, p, dev, "S_in")
     if o is None:
         o = torch.empty(v.shape, dtype=v.dtype, device=dev)

@@ -44,18 +44,22 @@ int check_problem(const gdn2_problem* p, bool chunked)
     if (!(p->dk == 16 || p->dk == 32 || p->dk == 64 || p->dk == 128)) return GDN2_ERR_SHAPE;
     if (p->dv < 16 || p->dv > 256 || p->dv % 16 != 0) return GDN2_ERR_SHAPE;
     if (chunked && p->chunk != 64) return GDN2_ERR_SHAPE;
-    if (p->reserved != 0) return GDN2_ERR_SHAPE;
+    if ((p->flags & ~(GDN2_FLAG_GATE_LOGITS | GDN2_FLAG_NEG_EIGVAL | GDN2_FLAG_QK_L2NORM)) != 0)
+        return GDN2_ERR_SHAPE;
+    if ((p->flags & GDN2_FLAG_NEG_EIGVAL) && !(p->flags & GDN2_FLAG_GATE_LOGITS)) return GDN2_ERR_SHAPE;
     // element counts stay far inside int64 and every grid inside 2^31 workgroups
     const double rows = double(p->B) * double(p->T) * double(p->H);
     if (rows * 256.0 > 9.0e15) return GDN2_ERR_SHAPE;
     if (double(p->B) * double(p->H) * (double((p->T + 63) / 64) + 16.0) > 2.0e9) return GDN2_ERR_SHAPE;
     const bool f32 = p->io_dtype == GDN2_F32 && p->gate_dtype == GDN2_F32;
-    const bool bf = p->io_dtype == GDN2_BF16 && p->gate_dtype == GDN2_F32;
+    const bool bf = p->io_dtype == GDN2_BF16 && (p->gate_dtype == GDN2_F32 || p->gate_dtype == GDN2_BF16);
     if (!f32 && !bf) return GDN2_ERR_DTYPE;
     return GDN2_OK;
 }
 
 bool is_bf16(const gdn2_problem* p) { return p->io_dtype == GDN2_BF16; }
+bool gates_bf16(const gdn2_problem* p) { return p->gate_dtype == GDN2_BF16; }
+int64_t gate_size(const gdn2_problem* p) { return gates_bf16(p) ? 2 : 4; }
 int64_t io_size(const gdn2_problem* p) { return is_bf16(p) ? 2 : 4; }
 int64_t nchunks(const gdn2_problem* p) { return (p->T + 63) / 64; }
 
@@ -68,14 +72,14 @@ int64_t ws_bytes(const gdn2_problem* p) { return p->B * p->H * nchunks(p) * ws_b
 
 struct Sizes {
     int64_t key, val, state;   // bytes of a [B,T,H,dk] io tensor, a [B,T,H,dv] io tensor, a state
-    int64_t gk, gv;            // bytes of the fp32 gates on the key / value axis
+    int64_t gk, gv;            // bytes of the gates on the key / value axis
 };
 
 Sizes sizes_of(const gdn2_problem* p)
 {
     const int64_t rows = p->B * p->T * p->H;
     return Sizes{rows * p->dk * io_size(p), rows * p->dv * io_size(p), p->B * p->H * p->dk * p->dv * 4,
-                 rows * p->dk * 4, rows * p->dv * 4};
+                 rows * p->dk * gate_size(p), rows * p->dv * gate_size(p)};
 }
 
 bool rows_nonempty(const gdn2_problem* p) { return p->B * p->T * p->H > 0; }
@@ -125,10 +129,9 @@ int do_prep(const gdn2_problem* p, const void* q, const void* k, const void* v, 
             const void* b, const void* w, void* ws, hipStream_t s)
 {
     if (p->B * p->H * nchunks(p) == 0) return GDN2_OK;
-    gdn2::PrepArgs a{q, k, v, static_cast<const float*>(alpha), static_cast<const float*>(b),
-                     static_cast<const float*>(w), ws, ws_block_bytes(p), p->B, p->T, p->H,
-                     (int)p->dv, (int)nchunks(p)};
-    return launch_status(gdn2::launch_chunk_prep(a, (int)p->dk, is_bf16(p), s));
+    gdn2::PrepArgs a{q, k, v, alpha, b, w, ws, ws_block_bytes(p), p->B, p->T, p->H,
+                     (int)p->dv, (int)nchunks(p), (int)p->flags};
+    return launch_status(gdn2::launch_chunk_prep(a, (int)p->dk, is_bf16(p), gates_bf16(p), s));
 }
 
 int do_state(const gdn2_problem* p, const float* S0, void* o, float* S_out, const void* ws, hipStream_t s)
@@ -272,10 +275,10 @@ int gdn2_recurrent_step(const gdn2_problem* p, const void* q, const void* k, con
     st = device_ready();
     if (st) return st;
     const int vs = gdn2::recurrent_slice(nch, p->T, (int)p->dv);
-    gdn2::RecArgs a{q, k, v, static_cast<const float*>(alpha), static_cast<const float*>(b),
-                    static_cast<const float*>(w), S_in, o, S_out, p->B, p->T, p->H, (int)p->dv,
-                    (int)(p->dv / vs)};
-    return launch_status(gdn2::launch_recurrent(a, (int)p->dk, vs, is_bf16(p), static_cast<hipStream_t>(stream)));
+    gdn2::RecArgs a{q, k, v, alpha, b, w, S_in, o, S_out, p->B, p->T, p->H, (int)p->dv,
+                    (int)(p->dv / vs), (int)p->flags};
+    return launch_status(gdn2::launch_recurrent(a, (int)p->dk, vs, is_bf16(p), gates_bf16(p),
+                                                static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

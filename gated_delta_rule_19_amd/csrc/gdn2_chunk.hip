@@ -100,7 +100,8 @@ constexpr unsigned kUpperI = pack2(kUpperIv, 6), kUpperJ = pack2(kUpperJv, 6);
 __device__ inline int unpack2(unsigned p, int i) { return (int)((p >> (2 * i)) & 3u); }
 
 // NUI = (token, 4-column) value items per thread: 64 * dv / 4 <= 256 * NUI
-template <typename Tio, int DK, int NUI>
+// Tg = gate dtype (alpha, b, w): float, or __bf16 with bf16 I/O
+template <typename Tio, int DK, int NUI, typename Tg>
 __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2)) void k_chunk_prep(PrepArgs a)
 {
     using IO = Io<Tio>;
@@ -162,16 +163,51 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
     constexpr int NQ = DK / 4;
     const bool kact = tid < 2 * DK;
     const int cq = tid % NQ, rg = (tid / NQ) & 7, p = rg >> 1, half = rg & 1, c0 = 4 * cq;
-    f32x4 al[8], bt[8];
+    typedef typename GateVec<Tg>::type gvec;
+    const Tg* galpha = static_cast<const Tg*>(a.alpha);
+    const Tg* gb = static_cast<const Tg*>(a.b);
+    gvec alr[8], btr[8];
     typename IO::vec4 kk[8], qq[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int r = 8 * rg + i;
         const int64_t off = (row0 + (r < L ? r : L - 1) * H) * DK + c0;
-        al[i] = *reinterpret_cast<const f32x4*>(a.alpha + off);
-        bt[i] = *reinterpret_cast<const f32x4*>(a.b + off);
+        alr[i] = *reinterpret_cast<const gvec*>(galpha + off);
+        btr[i] = *reinterpret_cast<const gvec*>(gb + off);
         kk[i] = *reinterpret_cast<const typename IO::vec4*>(k + off);
         qq[i] = *reinterpret_cast<const typename IO::vec4*>(q + off);
+    }
+    // prologue: gate activations, q/k L2 norms (sum of squares over the NQ
+    // lanes that hold one token's channels)
+    f32x4 al[8], bt[8];
+    const bool logits = (a.flags & kFlagGateLogits) != 0;
+    const float bscale = (a.flags & kFlagNegEigval) ? 2.f : 1.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        al[i] = widen4(alr[i]);
+        bt[i] = widen4(btr[i]);
+        if (logits) {
+            al[i] = sigmoid4(al[i]);
+            bt[i] = sigmoid4(bt[i]) * bscale;
+        }
+    }
+    float sk[8], sq[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sk[i] = sq[i] = 1.f;
+    if (a.flags & kFlagQkL2norm) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const f32x4 kv = IO::unpack4(kk[i]), qv = IO::unpack4(qq[i]);
+            float k2 = kv[0] * kv[0] + kv[1] * kv[1] + kv[2] * kv[2] + kv[3] * kv[3];
+            float q2 = qv[0] * qv[0] + qv[1] * qv[1] + qv[2] * qv[2] + qv[3] * qv[3];
+#pragma unroll
+            for (int off = 1; off < NQ; off <<= 1) {
+                k2 += __shfl_xor(k2, off, 64);
+                q2 += __shfl_xor(q2, off, 64);
+            }
+            sk[i] = __builtin_amdgcn_rsqf(k2 + kL2normEps);
+            sq[i] = __builtin_amdgcn_rsqf(q2 + kL2normEps);
+        }
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -244,7 +280,7 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int r = 8 * rg + i;
-            const f32x4 kv = IO::unpack4(kk[i]), qv = IO::unpack4(qq[i]);
+            const f32x4 kv = IO::unpack4(kk[i]) * sk[i], qv = IO::unpack4(qq[i]) * sq[i];
             const f32x4 ig = {fast_rcp(g[i][0]), fast_rcp(g[i][1]), fast_rcp(g[i][2]), fast_rcp(g[i][3])};
             const f32x4 xe = bt[i] * kv * g[i], xq = qv * g[i];
             st_vec4(Xe + xo(r, c0), xe);
@@ -275,8 +311,9 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
     // 8 tokens of each of its columns, so that (w*v)^T goes to LDS as whole
     // 8-token fragments
     constexpr int NIT = NUI <= 8 ? 1 : 2;     // items per thread: 8 * dv/4 <= 256 * NIT
-    f32x4 wr[NIT][8];
+    gvec wr[NIT][8];
     typename IO::vec4 vr[NIT][8];
+    const Tg* gw = static_cast<const Tg*>(a.w);
     const int nvq = a.dv / 4;
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
@@ -286,7 +323,7 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
         for (int i = 0; i < 8; ++i) {
             const int s = 8 * sg + i;
             const int64_t off = (row0 + (s < L ? s : L - 1) * H) * a.dv + 4 * jq;
-            wr[it][i] = *reinterpret_cast<const f32x4*>(a.w + off);
+            wr[it][i] = *reinterpret_cast<const gvec*>(gw + off);
             vr[it][i] = *reinterpret_cast<const typename IO::vec4*>(v + off);
         }
     }
@@ -432,7 +469,8 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
         const int sg = ((tid + it * kThreads) / nvq) & 7;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const f32x4 u4 = (8 * sg + i < L) ? wr[it][i] * IO::unpack4(vr[it][i]) : f32x4{0.f, 0.f, 0.f, 0.f};
+            const f32x4 w4 = logits ? sigmoid4(widen4(wr[it][i])) : widen4(wr[it][i]);
+            const f32x4 u4 = (8 * sg + i < L) ? w4 * IO::unpack4(vr[it][i]) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int e = 0; e < 4; ++e) uf[it][e][i / EPL][i % EPL] = IO::from_f(u4[e]);
         }
@@ -874,34 +912,35 @@ int chunk_state_slice(int64_t nchains, int dv, int dk, int esize)
     return 16;
 }
 
-template <typename Tio, int DK>
+template <typename Tio, int DK, typename Tg>
 static hipError_t prep_dk(const PrepArgs& a, hipStream_t s)
 {
     const int64_t nblk = a.B * a.H * (int64_t)a.nt;
     if (a.dv <= 64)
-        hipLaunchKernelGGL((k_chunk_prep<Tio, DK, 4>), dim3((unsigned)nblk), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((k_chunk_prep<Tio, DK, 4, Tg>), dim3((unsigned)nblk), dim3(kThreads), 0, s, a);
     else if (a.dv <= 128)
-        hipLaunchKernelGGL((k_chunk_prep<Tio, DK, 8>), dim3((unsigned)nblk), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((k_chunk_prep<Tio, DK, 8, Tg>), dim3((unsigned)nblk), dim3(kThreads), 0, s, a);
     else
-        hipLaunchKernelGGL((k_chunk_prep<Tio, DK, 16>), dim3((unsigned)nblk), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((k_chunk_prep<Tio, DK, 16, Tg>), dim3((unsigned)nblk), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
-template <typename Tio>
+template <typename Tio, typename Tg>
 static hipError_t prep_t(const PrepArgs& a, int dk, hipStream_t s)
 {
     switch (dk) {
-        case 16: return prep_dk<Tio, 16>(a, s);
-        case 32: return prep_dk<Tio, 32>(a, s);
-        case 64: return prep_dk<Tio, 64>(a, s);
-        case 128: return prep_dk<Tio, 128>(a, s);
+        case 16: return prep_dk<Tio, 16, Tg>(a, s);
+        case 32: return prep_dk<Tio, 32, Tg>(a, s);
+        case 64: return prep_dk<Tio, 64, Tg>(a, s);
+        case 128: return prep_dk<Tio, 128, Tg>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_chunk_prep(const PrepArgs& a, int dk, bool bf16, hipStream_t s)
+hipError_t launch_chunk_prep(const PrepArgs& a, int dk, bool bf16, bool gbf16, hipStream_t s)
 {
-    return bf16 ? prep_t<__bf16>(a, dk, s) : prep_t<float>(a, dk, s);
+    if (!bf16) return gbf16 ? hipErrorInvalidValue : prep_t<float, float>(a, dk, s);
+    return gbf16 ? prep_t<__bf16, __bf16>(a, dk, s) : prep_t<__bf16, float>(a, dk, s);
 }
 
 template <typename Tio, int DK, int VS>

@@ -119,4 +119,36 @@ __device__ inline f32x4 ld_vec4(const T* p) {
 
 __device__ inline float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
+// ---------------------------------------------------------------------------
+// Gates: fp32 or bf16 in memory, fp32 in registers.  Prologue flags
+// (GDN2_FLAG_* of gdn2.h) are passed to the kernels as plain ints.
+// ---------------------------------------------------------------------------
+constexpr int kFlagGateLogits = 1, kFlagNegEigval = 2, kFlagQkL2norm = 4;
+constexpr float kL2normEps = 1e-6f;
+
+__device__ inline float gate_f(float x) { return x; }
+__device__ inline float gate_f(__bf16 x) { return (float)x; }
+
+template <typename Tg> struct GateVec;
+template <> struct GateVec<float> { typedef f32x4 type; };
+template <> struct GateVec<__bf16> { typedef bf16x4 type; };
+
+// four consecutive gates, widened to fp32
+__device__ inline f32x4 ld_gate4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ inline f32x4 ld_gate4(const __bf16* p)
+{
+    const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+
+__device__ inline f32x4 widen4(f32x4 v) { return v; }
+__device__ inline f32x4 widen4(bf16x4 v) { return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]}; }
+
+// logistic function 1 / (1 + exp(-x)); saturates to 0 / 1 for large |x|
+__device__ inline float sigmoid_f(float x) { return fast_rcp(1.f + __expf(-x)); }
+__device__ inline f32x4 sigmoid4(f32x4 x)
+{
+    return f32x4{sigmoid_f(x[0]), sigmoid_f(x[1]), sigmoid_f(x[2]), sigmoid_f(x[3])};
+}
+
 }  // namespace gdn2

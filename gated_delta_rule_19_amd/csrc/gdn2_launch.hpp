@@ -6,11 +6,13 @@
 
 namespace gdn2 {
 
+// Gates (alpha, b, w) are fp32 or bf16 as the launch's gate type says;
+// flags are the GDN2_FLAG_* prologue options.
 struct PrepArgs {
     const void* q; const void* k; const void* v;
-    const float* alpha; const float* b; const float* w;
+    const void* alpha; const void* b; const void* w;
     void* ws; int64_t ws_block;
-    int64_t B, T, H; int dv; int nt;
+    int64_t B, T, H; int dv; int nt; int flags;
 };
 
 struct StateArgs {
@@ -21,15 +23,16 @@ struct StateArgs {
 
 struct RecArgs {
     const void* q; const void* k; const void* v;
-    const float* alpha; const float* b; const float* w;
+    const void* alpha; const void* b; const void* w;
     const float* S_in; void* o; float* S_out;
-    int64_t B, T, H; int dv; int nslices;
+    int64_t B, T, H; int dv; int nslices; int flags;
 };
 
-// Each returns hipSuccess or the launch error.  bf16 selects the I/O dtype.
-hipError_t launch_chunk_prep(const PrepArgs& a, int dk, bool bf16, hipStream_t s);
+// Each returns hipSuccess or the launch error.  bf16 selects the I/O dtype,
+// gbf16 the gate dtype (bf16 gates only with bf16 I/O).
+hipError_t launch_chunk_prep(const PrepArgs& a, int dk, bool bf16, bool gbf16, hipStream_t s);
 hipError_t launch_chunk_state(const StateArgs& a, int dk, int vs, bool bf16, hipStream_t s);
-hipError_t launch_recurrent(const RecArgs& a, int dk, int vs, bool bf16, hipStream_t s);
+hipError_t launch_recurrent(const RecArgs& a, int dk, int vs, bool bf16, bool gbf16, hipStream_t s);
 
 // Value-slice width the state pass uses for a problem (16, 32 or 64).
 int chunk_state_slice(int64_t nchains, int dv, int dk, int esize);

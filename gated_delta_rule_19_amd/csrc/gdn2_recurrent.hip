@@ -16,12 +16,19 @@
 // covers 64/NJ whole rows of the slice, contiguous in memory when VS == dv.
 // The key-axis vectors of token t+1 are fetched into LDS while token t is
 // reduced; one barrier per token.
+//
+// Prologue flags: gate logits go through the sigmoid as they are fetched.
+// With q/k L2 normalisation the reductions run on the raw q and k and also
+// sum k^2 and q^2; r, m and q.k are then scaled by 1/|k|, 1/|q| and
+// 1/(|q||k|) and the state update uses k/|k| -- the same values, with no
+// extra pass over the key axis.
 #include "gdn2_device.hpp"
 #include "gdn2_launch.hpp"
 
 namespace gdn2 {
 
-template <typename Tio, int DK, int VS>
+// Tg = gate dtype (alpha, b, w): float, or __bf16 with bf16 I/O
+template <typename Tio, int DK, int VS, typename Tg>
 __global__ __launch_bounds__(kThreads) void k_recurrent(RecArgs a)
 {
     using IO = Io<Tio>;
@@ -33,7 +40,7 @@ __global__ __launch_bounds__(kThreads) void k_recurrent(RecArgs a)
     static_assert(NTH % 64 == 0 && NTH <= kThreads && DK % NR == 0, "thread layout");
 
     __shared__ __attribute__((aligned(16))) float vec[2][4][DK];   // alpha, b*k, k, q of a token
-    __shared__ float red[2][NW][NJ][9];
+    __shared__ float red[2][NW][NJ][11];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const bool holder = tid < NTH;
@@ -47,6 +54,12 @@ __global__ __launch_bounds__(kThreads) void k_recurrent(RecArgs a)
     const Tio* k = static_cast<const Tio*>(a.k);
     const Tio* v = static_cast<const Tio*>(a.v);
     Tio* o = static_cast<Tio*>(a.o);
+    const Tg* galpha = static_cast<const Tg*>(a.alpha);
+    const Tg* gb = static_cast<const Tg*>(a.b);
+    const Tg* gw = static_cast<const Tg*>(a.w);
+    const bool logits = (a.flags & kFlagGateLogits) != 0;
+    const bool l2norm = (a.flags & kFlagQkL2norm) != 0;
+    const float bscale = (a.flags & kFlagNegEigval) ? 2.f : 1.f;
 
     f32x4 S[RPT];
 #pragma unroll
@@ -66,8 +79,14 @@ __global__ __launch_bounds__(kThreads) void k_recurrent(RecArgs a)
             float x = 0.f;
             if (e < 4 * DK) {
                 const int which = e / DK, c = e - which * DK;
-                if (which == 0) x = a.alpha[rowk + c];
-                else if (which == 1) x = a.b[rowk + c] * IO::to_f(k[rowk + c]);
+                if (which == 0) {
+                    x = gate_f(galpha[rowk + c]);
+                    if (logits) x = sigmoid_f(x);
+                } else if (which == 1) {
+                    float g = gate_f(gb[rowk + c]);
+                    if (logits) g = sigmoid_f(g) * bscale;
+                    x = g * IO::to_f(k[rowk + c]);
+                }
                 else if (which == 2) x = IO::to_f(k[rowk + c]);
                 else x = IO::to_f(q[rowk + c]);
             }
@@ -96,11 +115,13 @@ __global__ __launch_bounds__(kThreads) void k_recurrent(RecArgs a)
 
         f32x4 u = {0.f, 0.f, 0.f, 0.f};
         f32x4 r = u, m = u;
-        float qk = 0.f;
+        float qk = 0.f, k2 = 0.f, q2 = 0.f;
         float kreg[RPT];   // k of this thread's rows; vec[buf] is refilled for token t+2
                            // while slower waves may still be finishing token t
         if (holder) {
-            u = *reinterpret_cast<const f32x4*>(a.w + rowv) * ld_vec4(v + rowv);
+            f32x4 w4 = ld_gate4(gw + rowv);
+            if (logits) w4 = sigmoid4(w4);
+            u = w4 * ld_vec4(v + rowv);
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
                 const int c = rg + NR * i;
@@ -111,6 +132,8 @@ __global__ __launch_bounds__(kThreads) void k_recurrent(RecArgs a)
                 r += e * S[i];
                 m += qq * S[i];
                 qk += qq * kk;
+                k2 += kk * kk;
+                q2 += qq * qq;
             }
         }
         // reduce over the row groups of this wave (lanes sharing jg)
@@ -122,6 +145,10 @@ __global__ __launch_bounds__(kThreads) void k_recurrent(RecArgs a)
                 m[jj] += __shfl_xor(m[jj], off, 64);
             }
             qk += __shfl_xor(qk, off, 64);
+            if (l2norm) {
+                k2 += __shfl_xor(k2, off, 64);
+                q2 += __shfl_xor(q2, off, 64);
+            }
         }
         if (holder && lane < NJ) {
             float* dst = red[buf][wave][jg];
@@ -131,6 +158,8 @@ __global__ __launch_bounds__(kThreads) void k_recurrent(RecArgs a)
                 dst[4 + jj] = m[jj];
             }
             dst[8] = qk;
+            dst[9] = k2;
+            dst[10] = q2;
         }
         if (t + 1 < a.T) stash(buf ^ 1, stage);
         __syncthreads();
@@ -138,18 +167,29 @@ __global__ __launch_bounds__(kThreads) void k_recurrent(RecArgs a)
         if (holder) {
             f32x4 R = {0.f, 0.f, 0.f, 0.f};
             f32x4 M = R;
-            float QK = 0.f;
+            float QK = 0.f, K2 = 0.f, Q2 = 0.f;
 #pragma unroll
             for (int wv = 0; wv < NW; ++wv) {
                 const float* src = red[buf][wv][jg];
                 R += f32x4{src[0], src[1], src[2], src[3]};
                 M += f32x4{src[4], src[5], src[6], src[7]};
                 QK += src[8];
+                K2 += src[9];
+                Q2 += src[10];
+            }
+            float rk = 1.f;
+            if (l2norm) {
+                rk = __builtin_amdgcn_rsqf(K2 + kL2normEps);
+                const float rq = __builtin_amdgcn_rsqf(Q2 + kL2normEps);
+                R *= rk;
+                M *= rq;
+                QK *= rq * rk;
             }
             const f32x4 delta = u - R;
             if (rg == 0) st_vec4(o + rowv, M + QK * delta);
+            const f32x4 kd = rk * delta;
 #pragma unroll
-            for (int i = 0; i < RPT; ++i) S[i] += kreg[i] * delta;
+            for (int i = 0; i < RPT; ++i) S[i] += kreg[i] * kd;
         }
     }
 
@@ -173,41 +213,42 @@ int recurrent_slice(int64_t nchains, int64_t T, int dv)
     return 16;
 }
 
-template <typename Tio, int DK, int VS>
+template <typename Tio, int DK, int VS, typename Tg>
 static hipError_t rec_v(const RecArgs& a, hipStream_t s)
 {
     const int64_t nblk = a.B * a.H * (int64_t)a.nslices;
-    hipLaunchKernelGGL((k_recurrent<Tio, DK, VS>), dim3((unsigned)nblk), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k_recurrent<Tio, DK, VS, Tg>), dim3((unsigned)nblk), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
-template <typename Tio, int DK>
+template <typename Tio, int DK, typename Tg>
 static hipError_t rec_dk(const RecArgs& a, int vs, hipStream_t s)
 {
     switch (vs) {
-        case 16: return rec_v<Tio, DK, 16>(a, s);
-        case 32: return rec_v<Tio, DK, 32>(a, s);
-        case 64: return rec_v<Tio, DK, 64>(a, s);
-        case 128: return rec_v<Tio, DK, 128>(a, s);
+        case 16: return rec_v<Tio, DK, 16, Tg>(a, s);
+        case 32: return rec_v<Tio, DK, 32, Tg>(a, s);
+        case 64: return rec_v<Tio, DK, 64, Tg>(a, s);
+        case 128: return rec_v<Tio, DK, 128, Tg>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <typename Tio>
+template <typename Tio, typename Tg>
 static hipError_t rec_t(const RecArgs& a, int dk, int vs, hipStream_t s)
 {
     switch (dk) {
-        case 16: return rec_dk<Tio, 16>(a, vs, s);
-        case 32: return rec_dk<Tio, 32>(a, vs, s);
-        case 64: return rec_dk<Tio, 64>(a, vs, s);
-        case 128: return rec_dk<Tio, 128>(a, vs, s);
+        case 16: return rec_dk<Tio, 16, Tg>(a, vs, s);
+        case 32: return rec_dk<Tio, 32, Tg>(a, vs, s);
+        case 64: return rec_dk<Tio, 64, Tg>(a, vs, s);
+        case 128: return rec_dk<Tio, 128, Tg>(a, vs, s);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_recurrent(const RecArgs& a, int dk, int vs, bool bf16, hipStream_t s)
+hipError_t launch_recurrent(const RecArgs& a, int dk, int vs, bool bf16, bool gbf16, hipStream_t s)
 {
-    return bf16 ? rec_t<__bf16>(a, dk, vs, s) : rec_t<float>(a, dk, vs, s);
+    if (!bf16) return gbf16 ? hipErrorInvalidValue : rec_t<float, float>(a, dk, vs, s);
+    return gbf16 ? rec_t<__bf16, __bf16>(a, dk, vs, s) : rec_t<__bf16, float>(a, dk, vs, s);
 }
 
 }  // namespace gdn2

@@ -10,8 +10,10 @@
  *
  * alpha (decay) and b (erase gate) are per key channel, w (write gate) per
  * value channel.  The output reads the state after the token's update; there
- * is no query scale and no normalisation inside the core (the layer
- * L2-normalises q and k before it, README "Architecture" diagram).
+ * is no query scale.  By default q, k and the gates enter the core as given
+ * (the layer L2-normalises q and k and activates the gates before it, README
+ * "Architecture" diagram); the flags below move those prologue steps into
+ * the kernels.
  *
  * Two forward modes (README intro and "Architecture"): a chunked WY form used
  * for training-length sequences (chunk size 64, README "Configuration") and a
@@ -31,17 +33,30 @@
  *   v, w, o        : [B, T, H, dv]
  *   S0/S_in, S_out : [B, H, dk, dv]   fp32, dv fastest
  * Dtypes.  io_dtype covers q, k, v and o; gate_dtype covers alpha, b, w.
- *   Supported pairs: (GDN2_F32, GDN2_F32) and (GDN2_BF16, GDN2_F32).  The
- *   state is always fp32.  bf16 outputs are rounded to nearest even.
+ *   Supported pairs: (GDN2_F32, GDN2_F32), (GDN2_BF16, GDN2_F32) and
+ *   (GDN2_BF16, GDN2_BF16).  The state is always fp32; all arithmetic is
+ *   fp32 (bf16 only as matrix-core operands).  bf16 outputs are rounded to
+ *   nearest even.
+ * Prologue flags (gdn2_problem.flags, any combination of):
+ *   GDN2_FLAG_GATE_LOGITS  alpha, b, w hold pre-activation values; the
+ *       kernels use sigmoid(alpha), sigmoid(b), sigmoid(w), sigmoid(x) =
+ *       1 / (1 + exp(-x)).  (The README names the gate projections but not
+ *       their activation; the sigmoid is this library's reading.)
+ *   GDN2_FLAG_NEG_EIGVAL   with GATE_LOGITS only: b = 2 * sigmoid(b), the
+ *       README's allow_neg_eigval option ("b x 2", "Configuration").
+ *   GDN2_FLAG_QK_L2NORM    q and k are L2-normalised per (token, head) over
+ *       dk inside the kernels, x / sqrt(sum(x^2) + 1e-6) (README
+ *       "Architecture": L2-Norm before the recurrence).
+ *   Any other bit, or NEG_EIGVAL without GATE_LOGITS, is GDN2_ERR_SHAPE.
  * Sizes.  B, T, H >= 0 (any zero makes the call a no-op apart from the
  *   state copy described below); dk in {16, 32, 64, 128}; dv a multiple of
  *   16 in [16, 256]; chunk == 64 for the chunked mode.
- * Domain.  alpha in (0, 1].  The chunked mode rescales keys by partial decay
- *   products inside 16-token blocks, so within any 16 consecutive tokens of
- *   a chunk the product of alpha in one key channel must stay above ~1e-30
- *   (fp32 range); the recurrent mode has no such limit.  b, w, q, k, v are
- *   any finite values (b in (0, 2) is the README's negative-eigenvalue
- *   option, "b x 2").
+ * Domain.  alpha in (0, 1] (after the sigmoid with GATE_LOGITS).  The
+ *   chunked mode rescales keys by partial decay products inside 16-token
+ *   blocks, so within any 16 consecutive tokens of a chunk the product of
+ *   alpha in one key channel must stay above ~1e-30 (fp32 range); the
+ *   recurrent mode has no such limit.  b, w, q, k, v are any finite values
+ *   (b in (0, 2) is the README's negative-eigenvalue option, "b x 2").
  * Alignment.  Every tensor pointer is 16-byte aligned (the kernels use
  *   16-byte vector accesses); the workspace is 256-byte aligned.
  * Aliasing.  Inputs are never written.  Outputs (o, S_out, workspace) must
@@ -63,7 +78,7 @@
 extern "C" {
 #endif
 
-#define GDN2_ABI_VERSION 1
+#define GDN2_ABI_VERSION 2
 
 typedef enum {
     GDN2_OK = 0,
@@ -78,14 +93,20 @@ typedef enum {
 
 typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1 } gdn2_dtype;
 
+enum {
+    GDN2_FLAG_GATE_LOGITS = 1,   /* gates are pre-activations: sigmoid in-kernel */
+    GDN2_FLAG_NEG_EIGVAL = 2,    /* b = 2 * sigmoid(b) (requires GATE_LOGITS)     */
+    GDN2_FLAG_QK_L2NORM = 4      /* L2-normalise q and k over dk in-kernel        */
+};
+
 /* Problem description (plain old data; 56 bytes). */
 typedef struct {
     int64_t B, T, H;         /* batch, tokens per sequence, heads             */
     int64_t dk, dv;          /* key/query width and value width of a head     */
     int32_t chunk;           /* chunk length of the chunked mode; must be 64  */
     int32_t io_dtype;        /* gdn2_dtype of q, k, v, o                      */
-    int32_t gate_dtype;      /* gdn2_dtype of alpha, b, w (GDN2_F32 only)     */
-    int32_t reserved;        /* must be 0                                     */
+    int32_t gate_dtype;      /* gdn2_dtype of alpha, b, w                     */
+    int32_t flags;           /* GDN2_FLAG_* prologue options (0 = none)       */
 } gdn2_problem;
 
 /* ABI version of the loaded library (GDN2_ABI_VERSION). */

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert g.abi_version() == 1
+    assert g.abi_version() == 2
     for code in range(8):
         assert g.status_str(code).startswith(bnd._STATUS[code])
     assert "unknown" in g.status_str(99)
@@ -53,12 +53,13 @@ def test_problem_struct_layout():
 class Call:
     """Lay out fake, disjoint device buffers for one problem."""
 
-    def __init__(self, B=2, T=100, H=3, dk=64, dv=32, io=1, gate=0, chunk=64):
-        self.p = bnd.Problem(B, T, H, dk, dv, chunk, io, gate, 0)
+    def __init__(self, B=2, T=100, H=3, dk=64, dv=32, io=1, gate=0, chunk=64, flags=0):
+        self.p = bnd.Problem(B, T, H, dk, dv, chunk, io, gate, flags)
         es = 2 if io == 1 else 4
+        gs = 2 if gate == 1 else 4
         rows = B * T * H
-        sizes = dict(q=rows * dk * es, k=rows * dk * es, v=rows * dv * es, alpha=rows * dk * 4,
-                     b=rows * dk * 4, w=rows * dv * 4, S0=B * H * dk * dv * 4, o=rows * dv * es,
+        sizes = dict(q=rows * dk * es, k=rows * dk * es, v=rows * dv * es, alpha=rows * dk * gs,
+                     b=rows * dk * gs, w=rows * dv * gs, S0=B * H * dk * dv * 4, o=rows * dv * es,
                      S_out=B * H * dk * dv * 4)
         sizes["ws"] = g.lib().gdn2_chunk_fwd_workspace_size(ctypes.byref(self.p)) or 256
         self.size = sizes
@@ -103,7 +104,8 @@ def test_workspace_size():
 
 
 @pytest.mark.parametrize("field,value", [("dk", 48), ("dk", 256), ("dv", 8), ("dv", 24), ("dv", 272),
-                                         ("B", -1), ("T", -1), ("chunk", 32), ("reserved", 1)])
+                                         ("B", -1), ("T", -1), ("chunk", 32), ("flags", 8), ("flags", 2),
+                                         ("flags", 6), ("flags", -1)])
 def test_shape_errors(field, value):
     c = Call()
     setattr(c.p, field, value)
@@ -113,10 +115,27 @@ def test_shape_errors(field, value):
         assert c.fwd() == SHAPE and c.rec() == SHAPE
 
 
-@pytest.mark.parametrize("io,gate", [(0, 1), (1, 1), (2, 0), (1, 5)])
+@pytest.mark.parametrize("io,gate", [(0, 1), (2, 0), (1, 5), (1, 2)])
 def test_dtype_errors(io, gate):
     c = Call(io=io, gate=gate)
     assert c.fwd() == DTYPE and c.rec() == DTYPE
+
+
+@pytest.mark.parametrize("io,gate,flags", [(0, 0, 0), (1, 0, 0), (1, 1, 0), (1, 1, 1), (1, 1, 3), (1, 0, 4),
+                                           (0, 0, 7), (1, 1, 5)])
+def test_supported_dtypes_and_flags_reach_the_device_check(io, gate, flags):
+    c = Call(io=io, gate=gate, flags=flags)
+    assert c.fwd() == DEVICE and c.rec() == DEVICE
+
+
+def test_bf16_gates_are_sized_as_bf16():
+    # one token, dk = 64: alpha holds 128 bytes in bf16 (256 in fp32); a state
+    # placed right after those 128 bytes overlaps nothing
+    c = Call(B=1, T=1, H=1, dk=64, dv=16, io=1, gate=1)
+    assert c.fwd(S_out=c.ptr["alpha"] + 128) == DEVICE
+    assert c.fwd(S_out=c.ptr["alpha"] + 112) == ALIAS
+    f = Call(B=1, T=1, H=1, dk=64, dv=16, io=1, gate=0)
+    assert f.fwd(S_out=f.ptr["alpha"] + 128) == ALIAS
 
 
 def test_null_errors():
