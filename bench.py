@@ -78,6 +78,7 @@ def parse_args(argv=None):
     ap.add_argument("--pmc-summary", metavar="DIR", default=None)
     ap.add_argument("--copy-pmc", metavar="DIR", default=None)
     ap.add_argument("--util-summary", metavar="DIRS", default=None)
+    ap.add_argument("--no-prologue", action="store_true", help="skip the in-kernel prologue leg")
     return ap.parse_args(argv)
 
 
@@ -339,6 +340,9 @@ def main(argv=None):
                    "frac_of_device_copy": round(gbps(alg_dec, dec_ms) / copy_gbps, 4),
                    "roofline": roof("decode")},
     }
+    if not args.no_prologue:
+        result["chunk_fwd_prologue"] = prologue_leg(g, inputs, wl_c, dev, args)
+
     ok = bool(torch.isfinite(outs[0].float()).all() and torch.isfinite(states[0]).all()
               and torch.isfinite(douts[0].float()).all())
     result["outputs_finite"] = ok
@@ -347,6 +351,54 @@ def main(argv=None):
         result["cpu_baseline"] = cpu_baseline(sets[0], args.cpu_chains, B, T, H, dk, dv)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def prologue_leg(g, inputs, wl, dev, args):
+    """The same chunked forward with the layer's prologue moved into the kernels: bf16 gate
+    logits (sigmoid in-kernel, b x 2) and unnormalised q/k (L2 norm in-kernel).  Algorithmic
+    bytes: q, k, v and the gates in bf16 + o = 1,792 B per head-token at d = 128."""
+    import torch
+    B, T, H, dk, dv = wl.B, wl.T, wl.H, wl.dk, wl.dv
+    flags = g.FLAG_GATE_LOGITS | g.FLAG_NEG_EIGVAL | g.FLAG_QK_L2NORM
+    sets = [inputs.make_raw(B, T, H, dk, dv, wl.io_dtype, 300 + i, dev, gate_logits=True, unit_qk=False,
+                            gate_dtype=torch.bfloat16) for i in range(args.sets)]
+    prob = g.problem(B, T, H, dk, dv, wl.io_dtype, gate_dtype=torch.bfloat16, flags=flags)
+    ws = g.alloc_workspace(g.chunk_fwd_workspace_size(B, T, H, dk, dv, wl.io_dtype), dev)
+    outs = [torch.empty_like(x["v"]) for x in sets]
+    st = torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev)
+    A = lambda x: (x["q"], x["k"], x["v"], x["alpha"], x["b"], x["w"])
+    steps = max(args.steps // 2, 5)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(args.warmup + steps):
+        x = sets[i % len(sets)]
+        ev = evs[i - args.warmup] if i >= args.warmup else None
+        if ev:
+            ev[0].record()
+        g.chunk_prep(*A(x), ws, flags=flags)
+        if ev:
+            ev[1].record()
+        g.chunk_state(prob, ws, outs[i % len(sets)], None, st)
+        if ev:
+            ev[2].record()
+    torch.cuda.synchronize()
+    prep = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    state = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    tot = sorted(e[0].elapsed_time(e[2]) for e in evs)
+    ms = sum(tot) / steps
+    ht = B * T * H
+    alg = (2 * (2 * dk + dv) + 2 * (2 * dk + dv) + 2 * dv) * ht + B * H * dk * dv * 4
+    alg_prep = (2 * (2 * dk + dv) + 2 * (2 * dk + dv)) * ht
+    gbps = alg / (ms * 1e-3) / 1e9
+    prep_ms = sum(prep) / steps
+    return {"workload": "chunk fwd B4 H16 T2048 d128, bf16 q/k/v and bf16 gate logits, flags gate-logits | "
+                        "b x 2 | q/k L2 norm (prologue in-kernel), zero initial state",
+            "tokens_per_s": round(B * T / (ms * 1e-3), 1), "us": round(ms * 1e3, 2),
+            "median_us": round(tot[len(tot) // 2] * 1e3, 2), "min_us": round(tot[0] * 1e3, 2),
+            "prep_us": round(prep_ms * 1e3, 2), "state_us": round(sum(state) / steps * 1e3, 2),
+            "alg_bytes_per_head_token": 2 * (2 * dk + dv) + 2 * (2 * dk + dv) + 2 * dv,
+            "alg_GBps": round(gbps, 1), "frac_hbm_roofline": round(gbps / PEAK_HBM_GBPS, 4),
+            "prep_alg_GBps": round(alg_prep / (prep_ms * 1e-3) / 1e9, 1),
+            "outputs_finite": bool(torch.isfinite(outs[0].float()).all() and torch.isfinite(st).all())}
 
 
 def device_copy_gbps(dev, nbytes=1 << 30, reps=5):
