@@ -42,7 +42,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["recurrent", "chunked_wy", "rel_l2", "prologue", "sigmoid",
+__all__ = ["recurrent", "chunked_wy", "rel_l2", "prologue", "sigmoid", "gated_rmsnorm", "NORM_EPS",
            "FLAG_GATE_LOGITS", "FLAG_NEG_EIGVAL", "FLAG_QK_L2NORM"]
 
 # prologue options (the library's GDN2_FLAG_* values)
@@ -86,6 +86,28 @@ def prologue(q, k, alpha, b, w, flags=0):
         q = q / np.sqrt(np.sum(q * q, axis=-1, keepdims=True) + L2NORM_EPS)
         k = k / np.sqrt(np.sum(k * k, axis=-1, keepdims=True) + L2NORM_EPS)
     return q, k, alpha, b, w
+
+
+NORM_EPS = 1e-5   # burn-gdn2 README, "Configuration": norm_eps
+
+
+def gated_rmsnorm(o, g, weight, eps=NORM_EPS):
+    """The layer's output step after the core, fp64.
+
+    burn-gdn2 README, "Architecture" diagram: the core's output goes through a
+    gated RMS norm fed by a SiLU gate (the G projection), then the output
+    projection; "Configuration" gives norm_eps = 1e-5.  Reading taken: per
+    (token, head) over the d_v channels,
+
+        y = o / sqrt(mean(o^2) + eps) * weight * silu(g),   silu(x) = x * sigmoid(x),
+
+    with one weight vector of length d_v shared by all heads.
+
+    o, g: [..., d_v]; weight: [d_v].  Returns fp64 y of o's shape.
+    """
+    o, g, weight = _f64(o), _f64(g), _f64(weight)
+    rms = np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+    return o / rms * weight * (g * sigmoid(g))
 
 
 def recurrent(q, k, v, alpha, b, w, S0=None):
