@@ -342,6 +342,7 @@ def main(argv=None):
     }
     if not args.no_prologue:
         result["chunk_fwd_prologue"] = prologue_leg(g, inputs, wl_c, dev, args)
+        result["epilogue"] = epilogue_leg(g, outs, dev, args)
 
     ok = bool(torch.isfinite(outs[0].float()).all() and torch.isfinite(states[0]).all()
               and torch.isfinite(douts[0].float()).all())
@@ -399,6 +400,37 @@ def prologue_leg(g, inputs, wl, dev, args):
             "alg_GBps": round(gbps, 1), "frac_hbm_roofline": round(gbps / PEAK_HBM_GBPS, 4),
             "prep_alg_GBps": round(alg_prep / (prep_ms * 1e-3) / 1e9, 1),
             "outputs_finite": bool(torch.isfinite(outs[0].float()).all() and torch.isfinite(st).all())}
+
+
+def epilogue_leg(g, outs, dev, args):
+    """The output step (gated RMS norm with a SiLU gate) on the chunked forward's o
+    (B4 H16 T2048 dv128, bf16): reads o and g, writes y -- 6 B per element."""
+    import torch
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    gates = [torch.randn(o.shape, generator=gen, device=dev).to(o.dtype) for o in outs]
+    wt = torch.ones(outs[0].shape[-1], device=dev)
+    ys = [torch.empty_like(o) for o in outs]
+    steps = max(args.steps // 2, 5)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(args.warmup + steps):
+        j = i % len(outs)
+        ev = evs[i - args.warmup] if i >= args.warmup else None
+        if ev:
+            ev[0].record()
+        g.gated_rmsnorm(outs[j], gates[j], wt, out=ys[j])
+        if ev:
+            ev[1].record()
+    torch.cuda.synchronize()
+    t = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    ms = sum(t) / steps
+    nbytes = 3 * outs[0].numel() * outs[0].element_size() + wt.numel() * 4
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": "gated RMS norm + SiLU gate on o of the chunked workload, B4 T2048 H16 dv128 bf16",
+            "us": round(ms * 1e3, 2), "median_us": round(t[len(t) // 2] * 1e3, 2), "min_us": round(t[0] * 1e3, 2),
+            "alg_bytes": int(nbytes),
+            "roofline": {"kernel": "k_gated_rmsnorm", "bound": "hbm", "achieved": round(gbps, 1),
+                         "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4)}}
 
 
 def device_copy_gbps(dev, nbytes=1 << 30, reps=5):

@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     chunk_fwd_workspace_size,
     chunk_prep,
     chunk_state,
+    gated_rmsnorm,
     lib,
     problem,
     recurrent_step,

@@ -21,7 +21,8 @@ FLAG_GATE_LOGITS, FLAG_NEG_EIGVAL, FLAG_QK_L2NORM = 1, 2, 4
 _STATUS = {0: "GDN2_OK", 1: "GDN2_ERR_NULL", 2: "GDN2_ERR_SHAPE", 3: "GDN2_ERR_DTYPE",
            4: "GDN2_ERR_ALIAS", 5: "GDN2_ERR_WORKSPACE", 6: "GDN2_ERR_DEVICE", 7: "GDN2_ERR_ALIGN"}
 EXPORTED = ("gdn2_abi_version", "gdn2_status_str", "gdn2_chunk_fwd_workspace_size",
-            "gdn2_chunk_fwd", "gdn2_chunk_prep", "gdn2_chunk_state", "gdn2_recurrent_step")
+            "gdn2_chunk_fwd", "gdn2_chunk_prep", "gdn2_chunk_state", "gdn2_recurrent_step",
+            "gdn2_gated_rmsnorm")
 
 
 class Problem(ctypes.Structure):
@@ -64,6 +65,8 @@ def lib():
         L.gdn2_chunk_state.argtypes = [P, vp, vp, vp, vp, sz, vp]
         L.gdn2_recurrent_step.restype = ctypes.c_int
         L.gdn2_recurrent_step.argtypes = [P] + [vp] * 9 + [vp]
+        L.gdn2_gated_rmsnorm.restype = ctypes.c_int
+        L.gdn2_gated_rmsnorm.argtypes = [P, vp, vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -193,3 +196,25 @@ def recurrent_step(q, k, v, alpha, b, w, S_in=None, *, o=None, S_out=None, out_s
     _check(lib().gdn2_recurrent_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w),
                                      _ptr(S_in), _ptr(o), _ptr(S_out), _stream(dev)))
     return o, S_out
+
+
+def gated_rmsnorm(o, g, weight, *, out=None, inplace: bool = False):
+    """Output step (``gdn2_gated_rmsnorm``): y = o / sqrt(mean(o^2) + 1e-5) * weight * silu(g)
+    per (token, head) row.  o, g: [B,T,H,dv] (float32 or bfloat16); weight: [dv] float32.
+    ``inplace=True`` writes y over o.  Returns y."""
+    if o.dim() != 4 or tuple(g.shape) != tuple(o.shape) or g.dtype != o.dtype:
+        raise ValueError("o and g must be [B,T,H,dv] tensors of one dtype")
+    if o.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("o must be float32 or bfloat16")
+    B, T, H, dv = o.shape
+    if tuple(weight.shape) != (dv,) or weight.dtype != torch.float32:
+        raise ValueError(f"weight must be float32 [{dv}]")
+    dev = o.device
+    for name, x in (("o", o), ("g", g), ("weight", weight)):
+        if x.device != dev or dev.type != "cuda" or not x.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor on {dev}")
+    y = o if inplace else (torch.empty_like(o) if out is None else out)
+    # dk is not used by this call; 16 is any supported value
+    p = problem(B, T, H, 16, dv, o.dtype)
+    _check(lib().gdn2_gated_rmsnorm(ctypes.byref(p), _ptr(o), _ptr(g), _ptr(weight), _ptr(y), _stream(dev)))
+    return y

@@ -281,4 +281,25 @@ int gdn2_recurrent_step(const gdn2_problem* p, const void* q, const void* k, con
                                                 static_cast<hipStream_t>(stream)));
 }
 
+int gdn2_gated_rmsnorm(const gdn2_problem* p, const void* o, const void* g, const float* weight, void* y,
+                       void* stream)
+{
+    int st = check_problem(p, false);
+    if (st) return st;
+    const int64_t rows = p->B * p->T * p->H;
+    if (rows == 0) return GDN2_OK;
+    if (!o || !g || !weight || !y) return GDN2_ERR_NULL;
+    const Sizes z = sizes_of(p);
+    const Range ins[3] = {range_of(o, z.val), range_of(g, z.val), range_of(weight, p->dv * 4)};
+    const Range outs[1] = {range_of(y, z.val)};
+    st = check_alias(outs, 1, ins, 3, o, y, 0, 0);
+    if (st) return st;
+    st = check_align({o, g, weight, y});
+    if (st) return st;
+    st = device_ready();
+    if (st) return st;
+    gdn2::NormArgs a{o, g, weight, y, rows, (int)p->dv, 1.0f / (float)p->dv, 1e-5f};
+    return launch_status(gdn2::launch_gated_rmsnorm(a, is_bf16(p), static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

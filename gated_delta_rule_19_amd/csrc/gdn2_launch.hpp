@@ -28,11 +28,17 @@ struct RecArgs {
     int64_t B, T, H; int dv; int nslices; int flags;
 };
 
+struct NormArgs {
+    const void* o; const void* g; const float* weight; void* y;
+    int64_t rows; int dv; float inv_dv; float eps;
+};
+
 // Each returns hipSuccess or the launch error.  bf16 selects the I/O dtype,
 // gbf16 the gate dtype (bf16 gates only with bf16 I/O).
 hipError_t launch_chunk_prep(const PrepArgs& a, int dk, bool bf16, bool gbf16, hipStream_t s);
 hipError_t launch_chunk_state(const StateArgs& a, int dk, int vs, bool bf16, hipStream_t s);
 hipError_t launch_recurrent(const RecArgs& a, int dk, int vs, bool bf16, bool gbf16, hipStream_t s);
+hipError_t launch_gated_rmsnorm(const NormArgs& a, bool bf16, hipStream_t s);
 
 // Value-slice width the state pass uses for a problem (16, 32 or 64).
 int chunk_state_slice(int64_t nchains, int dv, int dk, int esize);

@@ -171,6 +171,26 @@ int gdn2_recurrent_step(const gdn2_problem* p,
                         const void* alpha, const void* b, const void* w,
                         const float* S_in, void* o, float* S_out, void* stream);
 
+/*
+ * Output step of the layer (README "Architecture": "Gated RMS Norm <- SiLU
+ * Gate"; "Configuration": norm_eps = 1e-5).  For every (token, head) row of
+ * dv channels
+ *
+ *     y = o / sqrt(mean(o^2) + 1e-5) * weight * g * sigmoid(g)
+ *
+ * with one fp32 weight vector [dv] shared by all heads (the SiLU-gate form
+ * and the shared weight are this library's reading of the diagram).
+ * o, g, y: [B, T, H, dv] in io_dtype; weight: [dv] fp32.  dk, chunk,
+ * gate_dtype and flags are checked as for the other calls but unused.
+ * y may equal o exactly (normalise in place); any other overlap is
+ * GDN2_ERR_ALIAS.  Usable after either forward mode.  (The chunked state pass
+ * splits a head's value columns over several workgroups, so the row
+ * statistic cannot be taken inside its output write; this call streams o, g
+ * and y once.)
+ */
+int gdn2_gated_rmsnorm(const gdn2_problem* p, const void* o, const void* g, const float* weight,
+                       void* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -217,3 +217,25 @@ def test_binding_rejects_cpu_tensors_and_bad_shapes():
         g.chunk_fwd(q, q, torch.zeros(1, 4, 2, 16), q, q, torch.zeros(1, 4, 2, 16))
     with pytest.raises(TypeError):
         g.chunk_fwd(q.double(), q.double(), torch.zeros(1, 4, 1, 16).double(), q, q, torch.zeros(1, 4, 1, 16))
+
+
+def test_gated_rmsnorm_validates():
+    c = Call(B=2, T=10, H=3, dk=64, dv=48)
+    L = g.lib()
+    P = ctypes.c_void_p
+    o, gt, y = c.ptr["o"], c.ptr["v"], c.ptr["S_out"]
+    wt = c.ptr["w"]
+    call = lambda **kw: L.gdn2_gated_rmsnorm(ctypes.byref(c.p), *(P(kw.get(n, d)) if kw.get(n, d) is not None
+                                                                  else None for n, d in
+                                                                  (("o", o), ("g", gt), ("wt", wt), ("y", y))),
+                                             None)
+    assert call() == DEVICE
+    assert call(y=o) == DEVICE                  # in place
+    assert call(y=o + 16) == ALIAS
+    assert call(y=gt) == ALIAS
+    assert call(g=None) == NULL and call(wt=None) == NULL and call(y=None) == NULL
+    assert call(o=o + 8) == ALIGN
+    empty = Call(B=0)
+    assert L.gdn2_gated_rmsnorm(ctypes.byref(empty.p), None, None, None, None, None) == OK
+    bad = Call(dv=40)
+    assert L.gdn2_gated_rmsnorm(ctypes.byref(bad.p), P(o), P(gt), P(wt), P(y), None) == SHAPE
