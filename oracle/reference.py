@@ -32,6 +32,8 @@ Layouts (all row-major / C-contiguous):
   v, w           : [B, T, H, d_v]
   S0, S          : [B, H, d_k, d_v]
   o              : [B, T, H, d_v]
+(with grouped value heads, H here is the value-head count: ``share_qk_heads``
+widens q and k to it first).
 
 Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
 hand-worked examples (``tests/golden``), the special cases the pages name
@@ -42,7 +44,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["recurrent", "chunked_wy", "rel_l2", "prologue", "sigmoid", "gated_rmsnorm", "NORM_EPS",
+__all__ = ["recurrent", "chunked_wy", "rel_l2", "prologue", "sigmoid", "gated_rmsnorm", "NORM_EPS", "share_qk_heads",
            "FLAG_GATE_LOGITS", "FLAG_NEG_EIGVAL", "FLAG_QK_L2NORM"]
 
 # prologue options (the library's GDN2_FLAG_* values)
@@ -86,6 +88,25 @@ def prologue(q, k, alpha, b, w, flags=0):
         q = q / np.sqrt(np.sum(q * q, axis=-1, keepdims=True) + L2NORM_EPS)
         k = k / np.sqrt(np.sum(k * k, axis=-1, keepdims=True) + L2NORM_EPS)
     return q, k, alpha, b, w
+
+
+def share_qk_heads(q, k, Hv):
+    """Grouped value heads (burn-gdn2 README, "Configuration": num_v_heads, whose
+    default is the number of query/key heads).
+
+    With Hv value heads over H query/key heads (Hv a multiple of H, G = Hv / H),
+    each value head keeps its own state, gates and values and reads the q and
+    k of one query/key head.  The README does not say which; the reading taken
+    is that consecutive groups of G value heads share a head: value head hv
+    reads head hv // G.  Returns q and k widened to [B, T, Hv, d_k] so that
+    ``recurrent`` / ``chunked_wy`` apply per value head unchanged.
+    """
+    q, k = _f64(q), _f64(k)
+    H = q.shape[2]
+    if k.shape != q.shape or Hv <= 0 or H <= 0 or Hv % H:
+        raise ValueError(f"value heads {Hv} must be a positive multiple of query/key heads {H}")
+    src = np.arange(Hv) // (Hv // H)          # the query/key head of each value head
+    return q[:, :, src], k[:, :, src]
 
 
 NORM_EPS = 1e-5   # burn-gdn2 README, "Configuration": norm_eps
