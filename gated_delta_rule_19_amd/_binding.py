@@ -16,6 +16,7 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn2.so")
 
+ABI_VERSION = 3
 GDN2_F32, GDN2_BF16 = 0, 1
 FLAG_GATE_LOGITS, FLAG_NEG_EIGVAL, FLAG_QK_L2NORM = 1, 2, 4
 _STATUS = {0: "GDN2_OK", 1: "GDN2_ERR_NULL", 2: "GDN2_ERR_SHAPE", 3: "GDN2_ERR_DTYPE",
@@ -30,7 +31,11 @@ class Problem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
                 ("dk", ctypes.c_int64), ("dv", ctypes.c_int64), ("chunk", ctypes.c_int32),
                 ("io_dtype", ctypes.c_int32), ("gate_dtype", ctypes.c_int32),
-                ("flags", ctypes.c_int32)]
+                ("flags", ctypes.c_int32), ("Hv", ctypes.c_int64)]
+
+    @property
+    def value_heads(self) -> int:
+        return self.Hv if self.Hv else self.H
 
 
 class Gdn2Error(RuntimeError):
@@ -67,6 +72,9 @@ def lib():
         L.gdn2_recurrent_step.argtypes = [P] + [vp] * 9 + [vp]
         L.gdn2_gated_rmsnorm.restype = ctypes.c_int
         L.gdn2_gated_rmsnorm.argtypes = [P, vp, vp, vp, vp, vp]
+        if L.gdn2_abi_version() != ABI_VERSION:   # the Problem mirror must match the library's struct
+            raise ImportError(f"{LIB_PATH} has ABI {L.gdn2_abi_version()}, this binding expects {ABI_VERSION}: "
+                              "rebuild it")
         _lib = L
     return _lib
 
@@ -93,19 +101,23 @@ def _stream(dev: torch.device) -> ctypes.c_void_p:
 
 
 def problem(B, T, H, dk, dv, io_dtype: torch.dtype, chunk: int = 64, gate_dtype: torch.dtype = torch.float32,
-            flags: int = 0) -> Problem:
+            flags: int = 0, Hv: int = 0) -> Problem:
+    """H query/key heads; Hv value heads (0 = H), a multiple of H."""
     code = {torch.float32: GDN2_F32, torch.bfloat16: GDN2_BF16}
-    return Problem(B, T, H, dk, dv, chunk, code.get(io_dtype, -1), code.get(gate_dtype, -1), int(flags))
+    return Problem(B, T, H, dk, dv, chunk, code.get(io_dtype, -1), code.get(gate_dtype, -1), int(flags), int(Hv))
 
 
 def _problem_from(q, k, v, alpha, b, w, flags: int = 0) -> Tuple[Problem, torch.device]:
     if q.dim() != 4 or v.dim() != 4:
-        raise ValueError("q/k/alpha/b must be [B,T,H,dk] and v/w [B,T,H,dv]")
+        raise ValueError("q/k must be [B,T,H,dk], alpha/b [B,T,Hv,dk] and v/w [B,T,Hv,dv]")
     B, T, H, dk = q.shape
-    dv = v.shape[-1]
-    for name, x, last in (("k", k, dk), ("alpha", alpha, dk), ("b", b, dk), ("v", v, dv), ("w", w, dv)):
-        if tuple(x.shape) != (B, T, H, last):
-            raise ValueError(f"{name} has shape {tuple(x.shape)}, expected {(B, T, H, last)}")
+    Hv, dv = v.shape[2], v.shape[3]
+    if H == 0 and Hv != 0 or H != 0 and Hv % H != 0:
+        raise ValueError(f"value heads ({Hv}) must be a multiple of query/key heads ({H})")
+    for name, x, heads, last in (("k", k, H, dk), ("alpha", alpha, Hv, dk), ("b", b, Hv, dk), ("v", v, Hv, dv),
+                                 ("w", w, Hv, dv)):
+        if tuple(x.shape) != (B, T, heads, last):
+            raise ValueError(f"{name} has shape {tuple(x.shape)}, expected {(B, T, heads, last)}")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("q, k, v must share one dtype: float32 or bfloat16")
     if not (alpha.dtype == b.dtype == w.dtype) or alpha.dtype not in (torch.float32, torch.bfloat16):
@@ -116,21 +128,21 @@ def _problem_from(q, k, v, alpha, b, w, flags: int = 0) -> Tuple[Problem, torch.
             raise ValueError(f"{name} must be a GPU tensor on {dev}")
         if not x.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    return problem(B, T, H, dk, dv, q.dtype, gate_dtype=alpha.dtype, flags=flags), dev
+    return problem(B, T, H, dk, dv, q.dtype, gate_dtype=alpha.dtype, flags=flags, Hv=Hv), dev
 
 
 def _check_state(S, p: Problem, dev, name):
     if S is None:
         return
-    if tuple(S.shape) != (p.B, p.H, p.dk, p.dv) or S.dtype != torch.float32:
-        raise ValueError(f"{name} must be float32 [{p.B},{p.H},{p.dk},{p.dv}]")
+    if tuple(S.shape) != (p.B, p.value_heads, p.dk, p.dv) or S.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32 [{p.B},{p.value_heads},{p.dk},{p.dv}]")
     if S.device != dev or not S.is_contiguous():
         raise ValueError(f"{name} must be a contiguous tensor on {dev}")
 
 
-def chunk_fwd_workspace_size(B, T, H, dk, dv, io_dtype: torch.dtype) -> int:
+def chunk_fwd_workspace_size(B, T, H, dk, dv, io_dtype: torch.dtype, Hv: int = 0) -> int:
     # the workspace size does not depend on the gate dtype or the flags
-    return int(lib().gdn2_chunk_fwd_workspace_size(ctypes.byref(problem(B, T, H, dk, dv, io_dtype))))
+    return int(lib().gdn2_chunk_fwd_workspace_size(ctypes.byref(problem(B, T, H, dk, dv, io_dtype, Hv=Hv))))
 
 
 def alloc_workspace(nbytes: int, device) -> torch.Tensor:
@@ -147,7 +159,7 @@ def chunk_fwd(q, k, v, alpha, b, w, S0=None, *, out_state: bool = True, o=None, 
     if o is None:
         o = torch.empty(v.shape, dtype=v.dtype, device=dev)
     if S_out is None and out_state:
-        S_out = torch.empty((p.B, p.H, p.dk, p.dv), dtype=torch.float32, device=dev)
+        S_out = torch.empty((p.B, p.value_heads, p.dk, p.dv), dtype=torch.float32, device=dev)
     _check_state(S_out, p, dev, "S_out")
     need = int(lib().gdn2_chunk_fwd_workspace_size(ctypes.byref(p)))
     if workspace is None:
@@ -191,7 +203,7 @@ def recurrent_step(q, k, v, alpha, b, w, S_in=None, *, o=None, S_out=None, out_s
             raise ValueError("inplace needs S_in")
         S_out = S_in
     elif S_out is None and out_state:
-        S_out = torch.empty((p.B, p.H, p.dk, p.dv), dtype=torch.float32, device=dev)
+        S_out = torch.empty((p.B, p.value_heads, p.dk, p.dv), dtype=torch.float32, device=dev)
     _check_state(S_out, p, dev, "S_out")
     _check(lib().gdn2_recurrent_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w),
                                      _ptr(S_in), _ptr(o), _ptr(S_out), _stream(dev)))

@@ -41,6 +41,8 @@ int check_problem(const gdn2_problem* p, bool chunked)
     if (p == nullptr) return GDN2_ERR_NULL;
     if (p->B < 0 || p->T < 0 || p->H < 0 || p->B > kMaxDim || p->T > kMaxDim || p->H > kMaxDim)
         return GDN2_ERR_SHAPE;
+    if (p->Hv < 0 || p->Hv > kMaxDim) return GDN2_ERR_SHAPE;
+    if (p->Hv != 0 && (p->H == 0 || p->Hv % p->H != 0)) return GDN2_ERR_SHAPE;
     if (!(p->dk == 16 || p->dk == 32 || p->dk == 64 || p->dk == 128)) return GDN2_ERR_SHAPE;
     if (p->dv < 16 || p->dv > 256 || p->dv % 16 != 0) return GDN2_ERR_SHAPE;
     if (chunked && p->chunk != 64) return GDN2_ERR_SHAPE;
@@ -48,9 +50,10 @@ int check_problem(const gdn2_problem* p, bool chunked)
         return GDN2_ERR_SHAPE;
     if ((p->flags & GDN2_FLAG_NEG_EIGVAL) && !(p->flags & GDN2_FLAG_GATE_LOGITS)) return GDN2_ERR_SHAPE;
     // element counts stay far inside int64 and every grid inside 2^31 workgroups
-    const double rows = double(p->B) * double(p->T) * double(p->H);
+    const double hv = double(p->Hv != 0 ? p->Hv : p->H);
+    const double rows = double(p->B) * double(p->T) * hv;
     if (rows * 256.0 > 9.0e15) return GDN2_ERR_SHAPE;
-    if (double(p->B) * double(p->H) * (double((p->T + 63) / 64) + 16.0) > 2.0e9) return GDN2_ERR_SHAPE;
+    if (double(p->B) * hv * (double((p->T + 63) / 64) + 16.0) > 2.0e9) return GDN2_ERR_SHAPE;
     const bool f32 = p->io_dtype == GDN2_F32 && p->gate_dtype == GDN2_F32;
     const bool bf = p->io_dtype == GDN2_BF16 && (p->gate_dtype == GDN2_F32 || p->gate_dtype == GDN2_BF16);
     if (!f32 && !bf) return GDN2_ERR_DTYPE;
@@ -58,6 +61,8 @@ int check_problem(const gdn2_problem* p, bool chunked)
 }
 
 bool is_bf16(const gdn2_problem* p) { return p->io_dtype == GDN2_BF16; }
+// value heads: each has its own state, gates and values (q and k are per query/key head)
+int64_t nvh(const gdn2_problem* p) { return p->Hv != 0 ? p->Hv : p->H; }
 bool gates_bf16(const gdn2_problem* p) { return p->gate_dtype == GDN2_BF16; }
 int64_t gate_size(const gdn2_problem* p) { return gates_bf16(p) ? 2 : 4; }
 int64_t io_size(const gdn2_problem* p) { return is_bf16(p) ? 2 : 4; }
@@ -68,18 +73,18 @@ int64_t ws_block_bytes(const gdn2_problem* p)
     return gdn2::ws_layout(p->dk, p->dv, io_size(p), is_bf16(p) ? 32 : 16).block;
 }
 
-int64_t ws_bytes(const gdn2_problem* p) { return p->B * p->H * nchunks(p) * ws_block_bytes(p); }
+int64_t ws_bytes(const gdn2_problem* p) { return p->B * nvh(p) * nchunks(p) * ws_block_bytes(p); }
 
 struct Sizes {
-    int64_t key, val, state;   // bytes of a [B,T,H,dk] io tensor, a [B,T,H,dv] io tensor, a state
-    int64_t gk, gv;            // bytes of the gates on the key / value axis
+    int64_t key, val, state;   // bytes of q or k [B,T,H,dk], of v or o [B,T,Hv,dv], of a state
+    int64_t gk, gv;            // bytes of alpha or b [B,T,Hv,dk], of w [B,T,Hv,dv]
 };
 
 Sizes sizes_of(const gdn2_problem* p)
 {
-    const int64_t rows = p->B * p->T * p->H;
-    return Sizes{rows * p->dk * io_size(p), rows * p->dv * io_size(p), p->B * p->H * p->dk * p->dv * 4,
-                 rows * p->dk * gate_size(p), rows * p->dv * gate_size(p)};
+    const int64_t rows = p->B * p->T * p->H, vrows = p->B * p->T * nvh(p);
+    return Sizes{rows * p->dk * io_size(p), vrows * p->dv * io_size(p), p->B * nvh(p) * p->dk * p->dv * 4,
+                 vrows * p->dk * gate_size(p), vrows * p->dv * gate_size(p)};
 }
 
 bool rows_nonempty(const gdn2_problem* p) { return p->B * p->T * p->H > 0; }
@@ -128,19 +133,19 @@ int launch_status(hipError_t e) { return e == hipSuccess ? GDN2_OK : GDN2_ERR_DE
 int do_prep(const gdn2_problem* p, const void* q, const void* k, const void* v, const void* alpha,
             const void* b, const void* w, void* ws, hipStream_t s)
 {
-    if (p->B * p->H * nchunks(p) == 0) return GDN2_OK;
-    gdn2::PrepArgs a{q, k, v, alpha, b, w, ws, ws_block_bytes(p), p->B, p->T, p->H,
+    if (p->B * nvh(p) * nchunks(p) == 0) return GDN2_OK;
+    gdn2::PrepArgs a{q, k, v, alpha, b, w, ws, ws_block_bytes(p), p->B, p->T, nvh(p), p->H,
                      (int)p->dv, (int)nchunks(p), (int)p->flags};
     return launch_status(gdn2::launch_chunk_prep(a, (int)p->dk, is_bf16(p), gates_bf16(p), s));
 }
 
 int do_state(const gdn2_problem* p, const float* S0, void* o, float* S_out, const void* ws, hipStream_t s)
 {
-    const int64_t nch = p->B * p->H;
+    const int64_t nch = p->B * nvh(p);
     if (nch == 0) return GDN2_OK;
     if (nchunks(p) == 0 && S_out == S0) return GDN2_OK;   // nothing to compute or copy
     const int vs = gdn2::chunk_state_slice(nch, (int)p->dv, (int)p->dk, (int)io_size(p));
-    gdn2::StateArgs a{ws, ws_block_bytes(p), S0, o, S_out, p->B, p->T, p->H, (int)p->dv,
+    gdn2::StateArgs a{ws, ws_block_bytes(p), S0, o, S_out, p->B, p->T, nvh(p), (int)p->dv,
                       (int)nchunks(p), (int)(p->dv / vs)};
     return launch_status(gdn2::launch_chunk_state(a, (int)p->dk, vs, is_bf16(p), s));
 }
@@ -269,13 +274,13 @@ int gdn2_recurrent_step(const gdn2_problem* p, const void* q, const void* k, con
     if (st) return st;
     st = check_align({q, k, v, alpha, b, w, S_in, o, S_out});
     if (st) return st;
-    const int64_t nch = p->B * p->H;
+    const int64_t nch = p->B * nvh(p);
     if (nch == 0) return GDN2_OK;
     if (p->T == 0 && S_out == S_in) return GDN2_OK;
     st = device_ready();
     if (st) return st;
     const int vs = gdn2::recurrent_slice(nch, p->T, (int)p->dv);
-    gdn2::RecArgs a{q, k, v, alpha, b, w, S_in, o, S_out, p->B, p->T, p->H, (int)p->dv,
+    gdn2::RecArgs a{q, k, v, alpha, b, w, S_in, o, S_out, p->B, p->T, nvh(p), p->H, (int)p->dv,
                     (int)(p->dv / vs), (int)p->flags};
     return launch_status(gdn2::launch_recurrent(a, (int)p->dk, vs, is_bf16(p), gates_bf16(p),
                                                 static_cast<hipStream_t>(stream)));
@@ -286,7 +291,7 @@ int gdn2_gated_rmsnorm(const gdn2_problem* p, const void* o, const void* g, cons
 {
     int st = check_problem(p, false);
     if (st) return st;
-    const int64_t rows = p->B * p->T * p->H;
+    const int64_t rows = p->B * p->T * nvh(p);
     if (rows == 0) return GDN2_OK;
     if (!o || !g || !weight || !y) return GDN2_ERR_NULL;
     const Sizes z = sizes_of(p);

@@ -136,8 +136,9 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
     const int64_t bb = chain / a.H, hh = chain - bb * a.H;
     const int64_t t0 = (int64_t)n * kChunk;
     const int L = (int)((a.T - t0) < kChunk ? (a.T - t0) : kChunk);
-    const int64_t row0 = (bb * a.T + t0) * a.H + hh;    // row of token t0 in [B,T,H,*]
-    const int64_t H = a.H;
+    const int64_t row0 = (bb * a.T + t0) * a.H + hh;    // row of token t0 in [B,T,Hv,*]
+    const int64_t H = a.H, Hk = a.Hk;
+    const int64_t row0k = (bb * a.T + t0) * Hk + hh / (H / Hk);   // its q/k row in [B,T,H,dk]
     const Tio* q = static_cast<const Tio*>(a.q);
     const Tio* k = static_cast<const Tio*>(a.k);
     const Tio* v = static_cast<const Tio*>(a.v);
@@ -171,11 +172,12 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int r = 8 * rg + i;
-        const int64_t off = (row0 + (r < L ? r : L - 1) * H) * DK + c0;
+        const int rc = r < L ? r : L - 1;
+        const int64_t off = (row0 + rc * H) * DK + c0, offk = (row0k + rc * Hk) * DK + c0;
         alr[i] = *reinterpret_cast<const gvec*>(galpha + off);
         btr[i] = *reinterpret_cast<const gvec*>(gb + off);
-        kk[i] = *reinterpret_cast<const typename IO::vec4*>(k + off);
-        qq[i] = *reinterpret_cast<const typename IO::vec4*>(q + off);
+        kk[i] = *reinterpret_cast<const typename IO::vec4*>(k + offk);
+        qq[i] = *reinterpret_cast<const typename IO::vec4*>(q + offk);
     }
     // prologue: gate activations, q/k L2 norms (sum of squares over the NQ
     // lanes that hold one token's channels)

@@ -7,12 +7,14 @@
 namespace gdn2 {
 
 // Gates (alpha, b, w) are fp32 or bf16 as the launch's gate type says;
-// flags are the GDN2_FLAG_* prologue options.
+// flags are the GDN2_FLAG_* prologue options.  H counts value heads (one
+// state each); Hk the query/key heads, H a multiple of Hk, value head h
+// reading q/k head h / (H / Hk).
 struct PrepArgs {
     const void* q; const void* k; const void* v;
     const void* alpha; const void* b; const void* w;
     void* ws; int64_t ws_block;
-    int64_t B, T, H; int dv; int nt; int flags;
+    int64_t B, T, H, Hk; int dv; int nt; int flags;
 };
 
 struct StateArgs {
@@ -25,7 +27,7 @@ struct RecArgs {
     const void* q; const void* k; const void* v;
     const void* alpha; const void* b; const void* w;
     const float* S_in; void* o; float* S_out;
-    int64_t B, T, H; int dv; int nslices; int flags;
+    int64_t B, T, H, Hk; int dv; int nslices; int flags;
 };
 
 struct NormArgs {

@@ -48,6 +48,7 @@ __global__ __launch_bounds__(kThreads) void k_recurrent(RecArgs a)
     const int64_t chain = blockIdx.x / a.nslices;
     const int slice = (int)(blockIdx.x - chain * a.nslices);
     const int64_t bb = chain / a.H, hh = chain - bb * a.H;
+    const int64_t hk = hh / (a.H / a.Hk);   // the query/key head this value head reads
     const int dv = a.dv;
     const int jc = slice * VS + 4 * jg;                 // first column of this thread
     const Tio* q = static_cast<const Tio*>(a.q);
@@ -72,7 +73,8 @@ __global__ __launch_bounds__(kThreads) void k_recurrent(RecArgs a)
     // key-axis vectors of a token -> registers (cooperative, coalesced)
     constexpr int VPT = (4 * DK + kThreads - 1) / kThreads;
     auto fetch = [&](int64_t t, float (&st)[VPT]) {
-        const int64_t rowk = ((bb * a.T + t) * a.H + hh) * DK;
+        const int64_t rowk = ((bb * a.T + t) * a.H + hh) * DK;                // gates: value head
+        const int64_t rowq = ((bb * a.T + t) * a.Hk + hk) * DK;               // q, k: its key head
 #pragma unroll
         for (int u = 0; u < VPT; ++u) {
             const int e = tid + u * kThreads;
@@ -85,10 +87,10 @@ __global__ __launch_bounds__(kThreads) void k_recurrent(RecArgs a)
                 } else if (which == 1) {
                     float g = gate_f(gb[rowk + c]);
                     if (logits) g = sigmoid_f(g) * bscale;
-                    x = g * IO::to_f(k[rowk + c]);
+                    x = g * IO::to_f(k[rowq + c]);
                 }
-                else if (which == 2) x = IO::to_f(k[rowk + c]);
-                else x = IO::to_f(q[rowk + c]);
+                else if (which == 2) x = IO::to_f(k[rowq + c]);
+                else x = IO::to_f(q[rowq + c]);
             }
             st[u] = x;
         }

@@ -21,6 +21,9 @@ Prologue variants (for the kernels' in-kernel prologue options):
   sigmoids (alpha-logit ~ N(alpha_mu, 1), b-logit ~ N(0, 1), w-logit ~ N(0, 1);
   b_scale is then the kernels' job), unit_qk=False leaves q and k unnormalised
   (N(0, 1) rows), and gate_dtype sets the gates' dtype (rounded RNE).
+
+Grouped value heads: Hv (default H) value heads, a multiple of H; q and k are
+drawn for the H query/key heads, v, the gates and S0 for the Hv value heads.
 """
 from __future__ import annotations
 
@@ -80,7 +83,7 @@ def make(wl: Workload, seed: int, device="cpu", B=None, T=None, H=None):
 
 
 def make_raw(B, T, H, dk, dv, io_dtype, seed, device="cpu", alpha_mu=3.0,
-             b_scale=1.0, s0_std=None, gate_logits=False, unit_qk=True, gate_dtype=torch.float32):
+             b_scale=1.0, s0_std=None, gate_logits=False, unit_qk=True, gate_dtype=torch.float32, Hv=None):
     dev = torch.device(device)
     g = torch.Generator(device=dev)
     g.manual_seed(int(seed))
@@ -94,10 +97,11 @@ def make_raw(B, T, H, dk, dv, io_dtype, seed, device="cpu", alpha_mu=3.0,
         return x / torch.clamp(n, min=1e-30)
 
     rows = unit_rows if unit_qk else (lambda x: x)
+    Hv = H if Hv is None else Hv
     q = rows(randn(B, T, H, dk)).to(io_dtype)
     k = rows(randn(B, T, H, dk)).to(io_dtype)
-    v = randn(B, T, H, dv).to(io_dtype)
-    la, lb, lw = randn(B, T, H, dk) + alpha_mu, randn(B, T, H, dk), randn(B, T, H, dv)
+    v = randn(B, T, Hv, dv).to(io_dtype)
+    la, lb, lw = randn(B, T, Hv, dk) + alpha_mu, randn(B, T, Hv, dk), randn(B, T, Hv, dv)
     if gate_logits:
         alpha, b, w = la, lb, lw
     else:
@@ -105,7 +109,7 @@ def make_raw(B, T, H, dk, dv, io_dtype, seed, device="cpu", alpha_mu=3.0,
     alpha, b, w = alpha.to(gate_dtype), b.to(gate_dtype), w.to(gate_dtype)
     S0 = None
     if s0_std is not None:
-        S0 = randn(B, H, dk, dv) * s0_std
+        S0 = randn(B, Hv, dk, dv) * s0_std
     return dict(q=q, k=k, v=v, alpha=alpha, b=b, w=w, S0=S0)
 
 

@@ -29,9 +29,14 @@
  *   Calls on different streams are independent if their outputs and
  *   workspaces are disjoint.
  * Layouts (all C-contiguous, element strides implied by the sizes):
- *   q, k, alpha, b : [B, T, H, dk]
- *   v, w, o        : [B, T, H, dv]
- *   S0/S_in, S_out : [B, H, dk, dv]   fp32, dv fastest
+ *   q, k           : [B, T, H,  dk]
+ *   alpha, b       : [B, T, Hv, dk]
+ *   v, w, o        : [B, T, Hv, dv]
+ *   S0/S_in, S_out : [B, Hv, dk, dv]   fp32, dv fastest
+ *   with Hv = p->Hv value heads (0 = H).  Grouped value heads (README
+ *   "Configuration": num_v_heads, "None = same as num_heads"): Hv a multiple
+ *   of H, and value head hv reads query/key head hv / (Hv / H).  Each value
+ *   head has its own state, gates and values; only q and k are shared.
  * Dtypes.  io_dtype covers q, k, v and o; gate_dtype covers alpha, b, w.
  *   Supported pairs: (GDN2_F32, GDN2_F32), (GDN2_BF16, GDN2_F32) and
  *   (GDN2_BF16, GDN2_BF16).  The state is always fp32; all arithmetic is
@@ -49,8 +54,9 @@
  *       "Architecture": L2-Norm before the recurrence).
  *   Any other bit, or NEG_EIGVAL without GATE_LOGITS, is GDN2_ERR_SHAPE.
  * Sizes.  B, T, H >= 0 (any zero makes the call a no-op apart from the
- *   state copy described below); dk in {16, 32, 64, 128}; dv a multiple of
- *   16 in [16, 256]; chunk == 64 for the chunked mode.
+ *   state copy described below); Hv = 0 or a positive multiple of H; dk in
+ *   {16, 32, 64, 128}; dv a multiple of 16 in [16, 256]; chunk == 64 for the
+ *   chunked mode.
  * Domain.  alpha in (0, 1] (after the sigmoid with GATE_LOGITS).  The
  *   chunked mode rescales keys by partial decay products inside 16-token
  *   blocks, so within any 16 consecutive tokens of a chunk the product of
@@ -78,7 +84,7 @@
 extern "C" {
 #endif
 
-#define GDN2_ABI_VERSION 2
+#define GDN2_ABI_VERSION 3
 
 typedef enum {
     GDN2_OK = 0,
@@ -99,14 +105,15 @@ enum {
     GDN2_FLAG_QK_L2NORM = 4      /* L2-normalise q and k over dk in-kernel        */
 };
 
-/* Problem description (plain old data; 56 bytes). */
+/* Problem description (plain old data; 64 bytes). */
 typedef struct {
-    int64_t B, T, H;         /* batch, tokens per sequence, heads             */
+    int64_t B, T, H;         /* batch, tokens per sequence, query/key heads   */
     int64_t dk, dv;          /* key/query width and value width of a head     */
     int32_t chunk;           /* chunk length of the chunked mode; must be 64  */
     int32_t io_dtype;        /* gdn2_dtype of q, k, v, o                      */
     int32_t gate_dtype;      /* gdn2_dtype of alpha, b, w                     */
     int32_t flags;           /* GDN2_FLAG_* prologue options (0 = none)       */
+    int64_t Hv;              /* value heads: 0 (= H) or a multiple of H       */
 } gdn2_problem;
 
 /* ABI version of the loaded library (GDN2_ABI_VERSION). */
@@ -180,7 +187,7 @@ int gdn2_recurrent_step(const gdn2_problem* p,
  *
  * with one fp32 weight vector [dv] shared by all heads (the SiLU-gate form
  * and the shared weight are this library's reading of the diagram).
- * o, g, y: [B, T, H, dv] in io_dtype; weight: [dv] fp32.  dk, chunk,
+ * o, g, y: [B, T, Hv, dv] in io_dtype; weight: [dv] fp32.  dk, chunk,
  * gate_dtype and flags are checked as for the other calls but unused.
  * y may equal o exactly (normalise in place); any other overlap is
  * GDN2_ERR_ALIAS.  Usable after either forward mode.  (The chunked state pass

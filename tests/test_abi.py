@@ -40,27 +40,28 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert g.abi_version() == 2
+    assert g.abi_version() == 3
     for code in range(8):
         assert g.status_str(code).startswith(bnd._STATUS[code])
     assert "unknown" in g.status_str(99)
 
 
 def test_problem_struct_layout():
-    assert ctypes.sizeof(bnd.Problem) == 56
+    assert ctypes.sizeof(bnd.Problem) == 64
+    assert bnd.Problem.Hv.offset == 56
 
 
 class Call:
     """Lay out fake, disjoint device buffers for one problem."""
 
-    def __init__(self, B=2, T=100, H=3, dk=64, dv=32, io=1, gate=0, chunk=64, flags=0):
-        self.p = bnd.Problem(B, T, H, dk, dv, chunk, io, gate, flags)
+    def __init__(self, B=2, T=100, H=3, dk=64, dv=32, io=1, gate=0, chunk=64, flags=0, Hv=0):
+        self.p = bnd.Problem(B, T, H, dk, dv, chunk, io, gate, flags, Hv)
         es = 2 if io == 1 else 4
         gs = 2 if gate == 1 else 4
-        rows = B * T * H
-        sizes = dict(q=rows * dk * es, k=rows * dk * es, v=rows * dv * es, alpha=rows * dk * gs,
-                     b=rows * dk * gs, w=rows * dv * gs, S0=B * H * dk * dv * 4, o=rows * dv * es,
-                     S_out=B * H * dk * dv * 4)
+        rows, vrows, nv = B * T * H, B * T * (Hv or H), B * (Hv or H)
+        sizes = dict(q=rows * dk * es, k=rows * dk * es, v=vrows * dv * es, alpha=vrows * dk * gs,
+                     b=vrows * dk * gs, w=vrows * dv * gs, S0=nv * dk * dv * 4, o=vrows * dv * es,
+                     S_out=nv * dk * dv * 4)
         sizes["ws"] = g.lib().gdn2_chunk_fwd_workspace_size(ctypes.byref(self.p)) or 256
         self.size = sizes
         addr = BASE
@@ -136,6 +137,28 @@ def test_bf16_gates_are_sized_as_bf16():
     assert c.fwd(S_out=c.ptr["alpha"] + 112) == ALIAS
     f = Call(B=1, T=1, H=1, dk=64, dv=16, io=1, gate=0)
     assert f.fwd(S_out=f.ptr["alpha"] + 128) == ALIAS
+
+
+@pytest.mark.parametrize("H,Hv,want", [(3, 0, DEVICE), (3, 3, DEVICE), (3, 6, DEVICE), (2, 8, DEVICE),
+                                       (1, 16, DEVICE), (3, 4, SHAPE), (4, 2, SHAPE), (3, -3, SHAPE),
+                                       (0, 2, SHAPE)])
+def test_value_head_counts(H, Hv, want):
+    c = Call(H=H, Hv=Hv)
+    assert c.fwd() == want and c.rec() == want
+
+
+def test_grouped_heads_are_sized_per_tensor():
+    # B = T = 1, H = 1 query/key head of dk = 64 (128 bytes bf16), Hv = 4 value
+    # heads: v is 4 x 16 bf16 = 128 bytes, the state 4 x 64 x 16 fp32
+    c = Call(B=1, T=1, H=1, Hv=4, dk=64, dv=16, io=1, gate=1)
+    assert c.fwd(o=c.ptr["q"] + 128) == DEVICE          # q holds one head only
+    assert c.fwd(o=c.ptr["v"] + 112) == ALIAS           # v holds all four
+    assert c.fwd(o=c.ptr["alpha"] + 496) == ALIAS       # alpha: 4 x 64 bf16 = 512 bytes
+    assert c.fwd(o=c.ptr["alpha"] + 512) == DEVICE
+    one = bnd.problem(2, 300, 4, 128, 128, __import__("torch").bfloat16)
+    four = bnd.problem(2, 300, 4, 128, 128, __import__("torch").bfloat16, Hv=16)
+    ws = lambda p: g.lib().gdn2_chunk_fwd_workspace_size(ctypes.byref(p))
+    assert ws(four) == 4 * ws(one) > 0                  # one workspace block per value head and chunk
 
 
 def test_null_errors():
