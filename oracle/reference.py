@@ -44,7 +44,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["recurrent", "chunked_wy", "rel_l2", "prologue", "sigmoid", "gated_rmsnorm", "NORM_EPS", "share_qk_heads",
+__all__ = ["recurrent", "chunked_wy", "rel_l2", "prologue", "sigmoid", "gated_rmsnorm", "NORM_EPS", "share_qk_heads", "varlen",
            "FLAG_GATE_LOGITS", "FLAG_NEG_EIGVAL", "FLAG_QK_L2NORM"]
 
 # prologue options (the library's GDN2_FLAG_* values)
@@ -107,6 +107,47 @@ def share_qk_heads(q, k, Hv):
         raise ValueError(f"value heads {Hv} must be a positive multiple of query/key heads {H}")
     src = np.arange(Hv) // (Hv // H)          # the query/key head of each value head
     return q[:, :, src], k[:, :, src]
+
+
+def varlen(cu_seqlens, q, k, v, alpha, b, w, S0=None, form=None):
+    """Packed batch of variable-length sequences, fp64.
+
+    The recurrence of the burn-gdn2 README ("Architecture") runs per sequence,
+    and each sequence starts from its own state (an empty one when none is
+    given, README "Quick start").  A packed batch lays N sequences back to
+    back along the token axis: sequence i holds tokens
+    cu_seqlens[i] .. cu_seqlens[i+1]-1 of the [1, T, H, *] tensors and
+    starts from S0[i].  No state crosses a sequence boundary.
+
+    cu_seqlens: N+1 nondecreasing offsets with cu_seqlens[0] = 0 and
+    cu_seqlens[N] = T.  q, k: [1, T, H, d_k]; v, w: [1, T, H, d_v] (widen q, k
+    with ``share_qk_heads`` first for grouped value heads); alpha, b:
+    [1, T, H, d_k]; S0: [N, H, d_k, d_v] or None.  ``form`` is the per-batch
+    function applied to each sequence (default ``recurrent``).
+    Returns o [1, T, H, d_v] and S [N, H, d_k, d_v], fp64.
+    """
+    form = recurrent if form is None else form
+    cu = [int(x) for x in np.asarray(cu_seqlens).ravel()]
+    T = np.asarray(v).shape[1]
+    if len(cu) < 1 or cu[0] != 0 or cu[-1] != T or any(b_ < a_ for a_, b_ in zip(cu, cu[1:])):
+        raise ValueError("cu_seqlens must rise from 0 to T")
+    if np.asarray(v).shape[0] != 1:
+        raise ValueError("a packed batch has batch dimension 1")
+    N = len(cu) - 1
+    H, dk, dv = np.asarray(v).shape[2], np.asarray(alpha).shape[3], np.asarray(v).shape[3]
+    o = np.zeros((1, T, H, dv))
+    S = np.zeros((N, H, dk, dv))
+    for i in range(N):
+        s, e = cu[i], cu[i + 1]
+        sl = lambda x: np.ascontiguousarray(np.asarray(x)[:, s:e])
+        s0 = None if S0 is None else np.ascontiguousarray(np.asarray(S0)[i:i + 1])
+        if e == s:          # an empty sequence leaves its state as it was
+            S[i] = 0.0 if s0 is None else s0[0]
+            continue
+        oi, Si = form(sl(q), sl(k), sl(v), sl(alpha), sl(b), sl(w), s0)
+        o[:, s:e] = oi
+        S[i] = Si[0]
+    return o, S
 
 
 NORM_EPS = 1e-5   # burn-gdn2 README, "Configuration": norm_eps
