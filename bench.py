@@ -78,7 +78,7 @@ def parse_args(argv=None):
     ap.add_argument("--pmc-summary", metavar="DIR", default=None)
     ap.add_argument("--copy-pmc", metavar="DIR", default=None)
     ap.add_argument("--util-summary", metavar="DIRS", default=None)
-    ap.add_argument("--no-prologue", action="store_true", help="skip the in-kernel prologue leg")
+    ap.add_argument("--no-prologue", action="store_true", help="skip the side legs (in-kernel prologue, grouped heads, packed batch, output step)")
     return ap.parse_args(argv)
 
 
@@ -342,6 +342,8 @@ def main(argv=None):
     }
     if not args.no_prologue:
         result["chunk_fwd_prologue"] = prologue_leg(g, inputs, wl_c, dev, args)
+        result["chunk_fwd_grouped"] = grouped_leg(g, inputs, wl_c, dev, args)
+        result["chunk_fwd_varlen"] = varlen_leg(g, inputs, wl_c, dev, args)
         result["epilogue"] = epilogue_leg(g, outs, dev, args)
 
     ok = bool(torch.isfinite(outs[0].float()).all() and torch.isfinite(states[0]).all()
@@ -352,6 +354,35 @@ def main(argv=None):
         result["cpu_baseline"] = cpu_baseline(sets[0], args.cpu_chains, B, T, H, dk, dv)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def _time_chunk(g, sets, prob, ws, outs, st, flags, steps, warmup):
+    """Time prep and state launches of the chunked forward over rotating input sets;
+    returns (prep, state, total) lists of milliseconds, sorted."""
+    import torch
+    A = lambda x: (x["q"], x["k"], x["v"], x["alpha"], x["b"], x["w"])
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(warmup + steps):
+        x = sets[i % len(sets)]
+        ev = evs[i - warmup] if i >= warmup else None
+        if ev:
+            ev[0].record()
+        g.chunk_prep(*A(x), ws, flags=flags)
+        if ev:
+            ev[1].record()
+        g.chunk_state(prob, ws, outs[i % len(sets)], None, st)
+        if ev:
+            ev[2].record()
+    torch.cuda.synchronize()
+    return (sorted(e[0].elapsed_time(e[1]) for e in evs), sorted(e[1].elapsed_time(e[2]) for e in evs),
+            sorted(e[0].elapsed_time(e[2]) for e in evs))
+
+
+def _leg_times(prep, state, tot):
+    n = len(tot)
+    return {"us": round(sum(tot) / n * 1e3, 2), "median_us": round(tot[n // 2] * 1e3, 2),
+            "min_us": round(tot[0] * 1e3, 2), "prep_us": round(sum(prep) / n * 1e3, 2),
+            "state_us": round(sum(state) / n * 1e3, 2)}
 
 
 def prologue_leg(g, inputs, wl, dev, args):
@@ -367,38 +398,86 @@ def prologue_leg(g, inputs, wl, dev, args):
     ws = g.alloc_workspace(g.chunk_fwd_workspace_size(B, T, H, dk, dv, wl.io_dtype), dev)
     outs = [torch.empty_like(x["v"]) for x in sets]
     st = torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev)
-    A = lambda x: (x["q"], x["k"], x["v"], x["alpha"], x["b"], x["w"])
     steps = max(args.steps // 2, 5)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    prep, state, tot = _time_chunk(g, sets, prob, ws, outs, st, flags, steps, args.warmup)
+    t = _leg_times(prep, state, tot)
+    ms, prep_ms = t["us"] * 1e-3, t["prep_us"] * 1e-3
+    ht = B * T * H
+    per_ht = 2 * (2 * dk + dv) + 2 * (2 * dk + dv) + 2 * dv
+    alg = per_ht * ht + B * H * dk * dv * 4
+    alg_prep = (2 * (2 * dk + dv) + 2 * (2 * dk + dv)) * ht
+    gbps = alg / (ms * 1e-3) / 1e9
+    return {"workload": "chunk fwd B4 H16 T2048 d128, bf16 q/k/v and bf16 gate logits, flags gate-logits | "
+                        "b x 2 | q/k L2 norm (prologue in-kernel), zero initial state",
+            "tokens_per_s": round(B * T / (ms * 1e-3), 1), **t,
+            "alg_bytes_per_head_token": per_ht,
+            "alg_GBps": round(gbps, 1), "frac_hbm_roofline": round(gbps / PEAK_HBM_GBPS, 4),
+            "prep_alg_GBps": round(alg_prep / (prep_ms * 1e-3) / 1e9, 1),
+            "outputs_finite": bool(torch.isfinite(outs[0].float()).all() and torch.isfinite(st).all())}
+
+
+def grouped_leg(g, inputs, wl, dev, args, H=4):
+    """The chunked workload with grouped value heads: 16 value heads (own state, gates,
+    values) over 4 query/key heads, bf16 q/k/v, fp32 gates.  Algorithmic bytes per value
+    head-token: q and k of its key head shared by 4 (2 x 256 / 4), v and o 256 each, fp32
+    gates 1,536 -> 2,176 B at d = 128."""
+    import torch
+    B, T, Hv, dk, dv = wl.B, wl.T, wl.H, wl.dk, wl.dv
+    sets = [inputs.make_raw(B, T, H, dk, dv, wl.io_dtype, 500 + i, dev, Hv=Hv) for i in range(args.sets)]
+    prob = g.problem(B, T, H, dk, dv, wl.io_dtype, Hv=Hv)
+    ws = g.alloc_workspace(g.chunk_fwd_workspace_size(B, T, H, dk, dv, wl.io_dtype, Hv=Hv), dev)
+    outs = [torch.empty_like(x["v"]) for x in sets]
+    st = torch.empty(B, Hv, dk, dv, dtype=torch.float32, device=dev)
+    steps = max(args.steps // 2, 5)
+    prep, state, tot = _time_chunk(g, sets, prob, ws, outs, st, 0, steps, args.warmup)
+    t = _leg_times(prep, state, tot)
+    ms = t["us"] * 1e-3
+    vht = B * T * Hv
+    per_vht = 2 * 2 * dk * H // Hv + 2 * dv + 4 * (2 * dk + dv) + 2 * dv
+    alg = per_vht * vht + B * Hv * dk * dv * 4
+    gbps = alg / (ms * 1e-3) / 1e9
+    return {"workload": f"chunk fwd B{B} T{T} H{H} query/key heads, Hv{Hv} value heads, d{dk}, bf16 q/k/v, "
+                        "fp32 gates, zero initial state",
+            "tokens_per_s": round(B * T / (ms * 1e-3), 1), **t,
+            "alg_bytes_per_value_head_token": per_vht,
+            "alg_GBps": round(gbps, 1), "frac_hbm_roofline": round(gbps / PEAK_HBM_GBPS, 4),
+            "outputs_finite": bool(torch.isfinite(outs[0].float()).all() and torch.isfinite(st).all())}
+
+
+def varlen_leg(g, inputs, wl, dev, args):
+    """The chunked workload's 8,192 tokens per head as a packed batch of sequences of mixed
+    length (seeded log-uniform in [16, 4096]), each from a zero state: the whole call (chunk
+    plan, prep, state pass) timed.  Algorithmic bytes as for the equal-length workload:
+    2,560 B per head-token + the final states."""
+    import torch
+    H, dk, dv = wl.H, wl.dk, wl.dv
+    lens = inputs.length_mix(wl.B * wl.T, seed=1)
+    N, T = len(lens), sum(lens)
+    sets = [inputs.make_packed(lens, H, dk, dv, wl.io_dtype, 700 + i, dev) for i in range(args.sets)]
+    ws = g.alloc_workspace(g.chunk_fwd_varlen_workspace_size(N, T, H, dk, dv, wl.io_dtype), dev)
+    outs = [torch.empty_like(x["v"]) for x in sets]
+    st = torch.empty(N, H, dk, dv, dtype=torch.float32, device=dev)
+    A = lambda x: (x["q"], x["k"], x["v"], x["alpha"], x["b"], x["w"], x["cu"])
+    steps = max(args.steps // 2, 5)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     for i in range(args.warmup + steps):
-        x = sets[i % len(sets)]
+        j = i % len(sets)
         ev = evs[i - args.warmup] if i >= args.warmup else None
         if ev:
             ev[0].record()
-        g.chunk_prep(*A(x), ws, flags=flags)
+        g.chunk_fwd_varlen(*A(sets[j]), None, o=outs[j], S_out=st, workspace=ws)
         if ev:
             ev[1].record()
-        g.chunk_state(prob, ws, outs[i % len(sets)], None, st)
-        if ev:
-            ev[2].record()
     torch.cuda.synchronize()
-    prep = sorted(e[0].elapsed_time(e[1]) for e in evs)
-    state = sorted(e[1].elapsed_time(e[2]) for e in evs)
-    tot = sorted(e[0].elapsed_time(e[2]) for e in evs)
-    ms = sum(tot) / steps
-    ht = B * T * H
-    alg = (2 * (2 * dk + dv) + 2 * (2 * dk + dv) + 2 * dv) * ht + B * H * dk * dv * 4
-    alg_prep = (2 * (2 * dk + dv) + 2 * (2 * dk + dv)) * ht
+    t = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    ms = sum(t) / steps
+    alg = chunk_bytes_per_ht(dk, dv) * T * H + N * H * dk * dv * 4
     gbps = alg / (ms * 1e-3) / 1e9
-    prep_ms = sum(prep) / steps
-    return {"workload": "chunk fwd B4 H16 T2048 d128, bf16 q/k/v and bf16 gate logits, flags gate-logits | "
-                        "b x 2 | q/k L2 norm (prologue in-kernel), zero initial state",
-            "tokens_per_s": round(B * T / (ms * 1e-3), 1), "us": round(ms * 1e3, 2),
-            "median_us": round(tot[len(tot) // 2] * 1e3, 2), "min_us": round(tot[0] * 1e3, 2),
-            "prep_us": round(prep_ms * 1e3, 2), "state_us": round(sum(state) / steps * 1e3, 2),
-            "alg_bytes_per_head_token": 2 * (2 * dk + dv) + 2 * (2 * dk + dv) + 2 * dv,
+    return {"workload": f"packed batch of {N} sequences, {T} tokens (lengths log-uniform in [16, 4096], seed 1), "
+                        f"H{H} d{dk}, bf16 q/k/v, fp32 gates, zero initial states",
+            "lengths": lens, "tokens_per_s": round(T / (ms * 1e-3), 1), "us": round(ms * 1e3, 2),
+            "median_us": round(t[len(t) // 2] * 1e3, 2), "min_us": round(t[0] * 1e3, 2),
             "alg_GBps": round(gbps, 1), "frac_hbm_roofline": round(gbps / PEAK_HBM_GBPS, 4),
-            "prep_alg_GBps": round(alg_prep / (prep_ms * 1e-3) / 1e9, 1),
             "outputs_finite": bool(torch.isfinite(outs[0].float()).all() and torch.isfinite(st).all())}
 
 

@@ -2,7 +2,9 @@
 
 Python face of the C ABI in ``include/gdn2.h`` (``libgdn2.so`` in this
 directory): the chunked forward and the fused recurrent / decode step of the
-GDN-2 recurrence, with hand-written HIP kernels doing all the arithmetic.
+GDN-2 recurrence (also over packed variable-length batches and with grouped
+value heads), the output step, with hand-written HIP kernels doing all the
+arithmetic.
 The library is loaded on first use; a missing library raises.
 """
 from ._binding import (  # noqa: F401
@@ -14,6 +16,8 @@ from ._binding import (  # noqa: F401
     abi_version,
     alloc_workspace,
     chunk_fwd,
+    chunk_fwd_varlen,
+    chunk_fwd_varlen_workspace_size,
     chunk_fwd_workspace_size,
     chunk_prep,
     chunk_state,
@@ -21,5 +25,6 @@ from ._binding import (  # noqa: F401
     lib,
     problem,
     recurrent_step,
+    recurrent_varlen,
     status_str,
 )

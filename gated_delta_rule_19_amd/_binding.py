@@ -23,7 +23,8 @@ _STATUS = {0: "GDN2_OK", 1: "GDN2_ERR_NULL", 2: "GDN2_ERR_SHAPE", 3: "GDN2_ERR_D
            4: "GDN2_ERR_ALIAS", 5: "GDN2_ERR_WORKSPACE", 6: "GDN2_ERR_DEVICE", 7: "GDN2_ERR_ALIGN"}
 EXPORTED = ("gdn2_abi_version", "gdn2_status_str", "gdn2_chunk_fwd_workspace_size",
             "gdn2_chunk_fwd", "gdn2_chunk_prep", "gdn2_chunk_state", "gdn2_recurrent_step",
-            "gdn2_gated_rmsnorm")
+            "gdn2_gated_rmsnorm", "gdn2_chunk_fwd_varlen_workspace_size", "gdn2_chunk_fwd_varlen",
+            "gdn2_recurrent_varlen")
 
 
 class Problem(ctypes.Structure):
@@ -72,6 +73,12 @@ def lib():
         L.gdn2_recurrent_step.argtypes = [P] + [vp] * 9 + [vp]
         L.gdn2_gated_rmsnorm.restype = ctypes.c_int
         L.gdn2_gated_rmsnorm.argtypes = [P, vp, vp, vp, vp, vp]
+        L.gdn2_chunk_fwd_varlen_workspace_size.restype = sz
+        L.gdn2_chunk_fwd_varlen_workspace_size.argtypes = [P]
+        L.gdn2_chunk_fwd_varlen.restype = ctypes.c_int
+        L.gdn2_chunk_fwd_varlen.argtypes = [P, vp] + [vp] * 9 + [vp, sz, vp]
+        L.gdn2_recurrent_varlen.restype = ctypes.c_int
+        L.gdn2_recurrent_varlen.argtypes = [P, vp] + [vp] * 9 + [vp]
         if L.gdn2_abi_version() != ABI_VERSION:   # the Problem mirror must match the library's struct
             raise ImportError(f"{LIB_PATH} has ABI {L.gdn2_abi_version()}, this binding expects {ABI_VERSION}: "
                               "rebuild it")
@@ -207,6 +214,65 @@ def recurrent_step(q, k, v, alpha, b, w, S_in=None, *, o=None, S_out=None, out_s
     _check_state(S_out, p, dev, "S_out")
     _check(lib().gdn2_recurrent_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w),
                                      _ptr(S_in), _ptr(o), _ptr(S_out), _stream(dev)))
+    return o, S_out
+
+
+def _varlen_problem(q, k, v, alpha, b, w, cu_seqlens, flags):
+    p, dev = _problem_from(q, k, v, alpha, b, w, flags)
+    if p.B != 1:
+        raise ValueError("a packed batch is passed as [1, T, heads, d] tensors")
+    if (not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1
+            or cu_seqlens.numel() < 1 or cu_seqlens.device != dev or not cu_seqlens.is_contiguous()):
+        raise ValueError(f"cu_seqlens must be a contiguous int32 [N+1] tensor on {dev}")
+    p.B = cu_seqlens.numel() - 1
+    return p, dev
+
+
+def chunk_fwd_varlen_workspace_size(N, T, H, dk, dv, io_dtype: torch.dtype, Hv: int = 0) -> int:
+    """Workspace bytes of ``chunk_fwd_varlen`` for N sequences of T packed tokens in all."""
+    return int(lib().gdn2_chunk_fwd_varlen_workspace_size(ctypes.byref(problem(N, T, H, dk, dv, io_dtype, Hv=Hv))))
+
+
+def chunk_fwd_varlen(q, k, v, alpha, b, w, cu_seqlens, S0=None, *, out_state: bool = True, o=None, S_out=None,
+                     workspace=None, flags: int = 0):
+    """Chunked forward over a packed batch (``gdn2_chunk_fwd_varlen``).
+
+    q, k: [1, T, H, dk]; alpha, b: [1, T, Hv, dk]; v, w: [1, T, Hv, dv]; cu_seqlens: int32 [N+1]
+    token offsets on the GPU (sequence i = tokens cu_seqlens[i] .. cu_seqlens[i+1]-1); S0:
+    [N, Hv, dk, dv] or None.  Returns (o [1, T, Hv, dv], S_final [N, Hv, dk, dv] or None)."""
+    p, dev = _varlen_problem(q, k, v, alpha, b, w, cu_seqlens, flags)
+    _check_state(S0, p, dev, "S0")
+    if o is None:
+        o = torch.empty(v.shape, dtype=v.dtype, device=dev)
+    if S_out is None and out_state:
+        S_out = torch.empty((p.B, p.value_heads, p.dk, p.dv), dtype=torch.float32, device=dev)
+    _check_state(S_out, p, dev, "S_out")
+    need = int(lib().gdn2_chunk_fwd_varlen_workspace_size(ctypes.byref(p)))
+    if workspace is None:
+        workspace = alloc_workspace(need, dev)
+    _check(lib().gdn2_chunk_fwd_varlen(ctypes.byref(p), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                       _ptr(b), _ptr(w), _ptr(S0), _ptr(o), _ptr(S_out), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(dev)))
+    return o, S_out
+
+
+def recurrent_varlen(q, k, v, alpha, b, w, cu_seqlens, S_in=None, *, o=None, S_out=None, out_state: bool = True,
+                     inplace: bool = False, flags: int = 0):
+    """Fused recurrent forward over a packed batch (``gdn2_recurrent_varlen``); layouts as for
+    ``chunk_fwd_varlen``.  ``inplace=True`` writes the final states back into ``S_in``."""
+    p, dev = _varlen_problem(q, k, v, alpha, b, w, cu_seqlens, flags)
+    _check_state(S_in, p, dev, "S_in")
+    if o is None:
+        o = torch.empty(v.shape, dtype=v.dtype, device=dev)
+    if inplace:
+        if S_in is None:
+            raise ValueError("inplace needs S_in")
+        S_out = S_in
+    elif S_out is None and out_state:
+        S_out = torch.empty((p.B, p.value_heads, p.dk, p.dv), dtype=torch.float32, device=dev)
+    _check_state(S_out, p, dev, "S_out")
+    _check(lib().gdn2_recurrent_varlen(ctypes.byref(p), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                       _ptr(b), _ptr(w), _ptr(S_in), _ptr(o), _ptr(S_out), _stream(dev)))
     return o, S_out
 
 

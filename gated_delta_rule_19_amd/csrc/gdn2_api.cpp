@@ -35,8 +35,9 @@ bool overlap(Range a, Range b)
     return a.lo < b.hi && b.lo < a.hi;
 }
 
-// checks shared by every entry point; `chunked` adds the chunk-length rule
-int check_problem(const gdn2_problem* p, bool chunked)
+// checks shared by every entry point; `chunked` adds the chunk-length rule,
+// `varlen` reads B as the sequence count and T as the packed token count
+int check_problem(const gdn2_problem* p, bool chunked, bool varlen = false)
 {
     if (p == nullptr) return GDN2_ERR_NULL;
     if (p->B < 0 || p->T < 0 || p->H < 0 || p->B > kMaxDim || p->T > kMaxDim || p->H > kMaxDim)
@@ -51,9 +52,17 @@ int check_problem(const gdn2_problem* p, bool chunked)
     if ((p->flags & GDN2_FLAG_NEG_EIGVAL) && !(p->flags & GDN2_FLAG_GATE_LOGITS)) return GDN2_ERR_SHAPE;
     // element counts stay far inside int64 and every grid inside 2^31 workgroups
     const double hv = double(p->Hv != 0 ? p->Hv : p->H);
-    const double rows = double(p->B) * double(p->T) * hv;
-    if (rows * 256.0 > 9.0e15) return GDN2_ERR_SHAPE;
-    if (double(p->B) * hv * (double((p->T + 63) / 64) + 16.0) > 2.0e9) return GDN2_ERR_SHAPE;
+    if (!varlen) {
+        const double rows = double(p->B) * double(p->T) * hv;
+        if (rows * 256.0 > 9.0e15) return GDN2_ERR_SHAPE;
+        if (double(p->B) * hv * (double((p->T + 63) / 64) + 16.0) > 2.0e9) return GDN2_ERR_SHAPE;
+    } else {
+        // int32 token offsets; prep grid hv * (ceil(T/64) + N), state grid N * hv * slices
+        if (p->T > INT32_MAX - 64 || p->B > INT32_MAX / 4) return GDN2_ERR_SHAPE;
+        if (double(p->T) * hv * 256.0 > 9.0e15) return GDN2_ERR_SHAPE;
+        if (hv * (double((p->T + 63) / 64) + double(p->B)) > 2.0e9) return GDN2_ERR_SHAPE;
+        if (double(p->B) * hv * 16.0 > 2.0e9) return GDN2_ERR_SHAPE;
+    }
     const bool f32 = p->io_dtype == GDN2_F32 && p->gate_dtype == GDN2_F32;
     const bool bf = p->io_dtype == GDN2_BF16 && (p->gate_dtype == GDN2_F32 || p->gate_dtype == GDN2_BF16);
     if (!f32 && !bf) return GDN2_ERR_DTYPE;
@@ -75,21 +84,35 @@ int64_t ws_block_bytes(const gdn2_problem* p)
 
 int64_t ws_bytes(const gdn2_problem* p) { return p->B * nvh(p) * nchunks(p) * ws_block_bytes(p); }
 
+// packed batches: the chunk plan, then one block per (value head, chunk slot)
+int64_t varlen_ncmax(const gdn2_problem* p) { return nchunks(p) + p->B; }
+int64_t varlen_plan_bytes(const gdn2_problem* p)
+{
+    return (4 * gdn2::plan_head_words(p->B) + 8 * varlen_ncmax(p) + 255) / 256 * 256;
+}
+int64_t varlen_ws_bytes(const gdn2_problem* p)
+{
+    return varlen_plan_bytes(p) + nvh(p) * varlen_ncmax(p) * ws_block_bytes(p);
+}
+
 struct Sizes {
     int64_t key, val, state;   // bytes of q or k [B,T,H,dk], of v or o [B,T,Hv,dv], of a state
     int64_t gk, gv;            // bytes of alpha or b [B,T,Hv,dk], of w [B,T,Hv,dv]
 };
 
-Sizes sizes_of(const gdn2_problem* p)
+// token tensors span B sequences of T tokens, or (varlen) T packed tokens
+Sizes sizes_of(const gdn2_problem* p, bool varlen = false)
 {
-    const int64_t rows = p->B * p->T * p->H, vrows = p->B * p->T * nvh(p);
+    const int64_t tok = varlen ? p->T : p->B * p->T;
+    const int64_t rows = tok * p->H, vrows = tok * nvh(p);
     return Sizes{rows * p->dk * io_size(p), vrows * p->dv * io_size(p), p->B * nvh(p) * p->dk * p->dv * 4,
                  vrows * p->dk * gate_size(p), vrows * p->dv * gate_size(p)};
 }
 
 bool rows_nonempty(const gdn2_problem* p) { return p->B * p->T * p->H > 0; }
 
-// inputs must be non-null whenever they hold any element
+// inputs must be non-null whenever they hold any element (a packed batch of
+// B > 0 sequences holds T tokens)
 int check_inputs(const gdn2_problem* p, const void* q, const void* k, const void* v,
                  const void* alpha, const void* b, const void* w, const void* o)
 {
@@ -114,6 +137,15 @@ int check_alias(const Range* outs, int nout, const Range* ins, int nin, const vo
     return GDN2_OK;
 }
 
+// the offsets of a packed batch: present, int32-aligned
+int check_cu(const gdn2_problem* p, const int32_t* cu)
+{
+    if (p->B * nvh(p) == 0) return GDN2_OK;
+    if (cu == nullptr) return GDN2_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(cu) & 3u) != 0) return GDN2_ERR_ALIGN;
+    return GDN2_OK;
+}
+
 int check_align(std::initializer_list<const void*> ptrs)
 {
     for (const void* p : ptrs)
@@ -135,7 +167,7 @@ int do_prep(const gdn2_problem* p, const void* q, const void* k, const void* v, 
 {
     if (p->B * nvh(p) * nchunks(p) == 0) return GDN2_OK;
     gdn2::PrepArgs a{q, k, v, alpha, b, w, ws, ws_block_bytes(p), p->B, p->T, nvh(p), p->H,
-                     (int)p->dv, (int)nchunks(p), (int)p->flags};
+                     (int)p->dv, (int)nchunks(p), (int)p->flags, nullptr, 0};
     return launch_status(gdn2::launch_chunk_prep(a, (int)p->dk, is_bf16(p), gates_bf16(p), s));
 }
 
@@ -146,7 +178,7 @@ int do_state(const gdn2_problem* p, const float* S0, void* o, float* S_out, cons
     if (nchunks(p) == 0 && S_out == S0) return GDN2_OK;   // nothing to compute or copy
     const int vs = gdn2::chunk_state_slice(nch, (int)p->dv, (int)p->dk, (int)io_size(p));
     gdn2::StateArgs a{ws, ws_block_bytes(p), S0, o, S_out, p->B, p->T, nvh(p), (int)p->dv,
-                      (int)nchunks(p), (int)(p->dv / vs)};
+                      (int)nchunks(p), (int)(p->dv / vs), nullptr, 0};
     return launch_status(gdn2::launch_chunk_state(a, (int)p->dk, vs, is_bf16(p), s));
 }
 
@@ -281,7 +313,94 @@ int gdn2_recurrent_step(const gdn2_problem* p, const void* q, const void* k, con
     if (st) return st;
     const int vs = gdn2::recurrent_slice(nch, p->T, (int)p->dv);
     gdn2::RecArgs a{q, k, v, alpha, b, w, S_in, o, S_out, p->B, p->T, nvh(p), p->H, (int)p->dv,
-                    (int)(p->dv / vs), (int)p->flags};
+                    (int)(p->dv / vs), (int)p->flags, nullptr};
+    return launch_status(gdn2::launch_recurrent(a, (int)p->dk, vs, is_bf16(p), gates_bf16(p),
+                                                static_cast<hipStream_t>(stream)));
+}
+
+size_t gdn2_chunk_fwd_varlen_workspace_size(const gdn2_problem* p)
+{
+    if (check_problem(p, true, true) != GDN2_OK) return 0;
+    return static_cast<size_t>(varlen_ws_bytes(p));
+}
+
+int gdn2_chunk_fwd_varlen(const gdn2_problem* p, const int32_t* cu_seqlens, const void* q, const void* k,
+                          const void* v, const void* alpha, const void* b, const void* w, const float* S0,
+                          void* o, float* S_out, void* workspace, size_t workspace_bytes, void* stream)
+{
+    int st = check_problem(p, true, true);
+    if (st) return st;
+    st = check_cu(p, cu_seqlens);
+    if (st) return st;
+    const bool any = p->B * nvh(p) > 0;
+    if (any) {
+        st = check_inputs(p, q, k, v, alpha, b, w, o);
+        if (st) return st;
+    }
+    const int64_t need = any ? varlen_ws_bytes(p) : 0;
+    if (need > 0 && (workspace == nullptr || static_cast<int64_t>(workspace_bytes) < need))
+        return GDN2_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_WORKSPACE;
+    const Sizes z = sizes_of(p, true);
+    const Range ins[8] = {range_of(q, z.key),  range_of(k, z.key),  range_of(v, z.val),
+                          range_of(alpha, z.gk), range_of(b, z.gk), range_of(w, z.gv),
+                          range_of(S0, z.state), range_of(cu_seqlens, any ? 4 * (p->B + 1) : 0)};
+    const Range outs[3] = {range_of(o, z.val), range_of(S_out, z.state), range_of(workspace, need)};
+    st = check_alias(outs, 3, ins, 8, S0, S_out, 6, 1);
+    if (st) return st;
+    st = check_align({q, k, v, alpha, b, w, S0, o, S_out});
+    if (st) return st;
+    if (!any || (p->T == 0 && (S_out == S0 || S_out == nullptr))) return GDN2_OK;
+    st = device_ready();
+    if (st) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    int* plan = static_cast<int*>(workspace);
+    char* blocks = static_cast<char*>(workspace) + varlen_plan_bytes(p);
+    const int64_t ncmax = varlen_ncmax(p);
+    st = launch_status(gdn2::launch_varlen_plan(gdn2::PlanArgs{cu_seqlens, plan, p->B, p->T, ncmax}, s));
+    if (st) return st;
+    if (p->T > 0) {
+        gdn2::PrepArgs a{q, k, v, alpha, b, w, blocks, ws_block_bytes(p), p->B, p->T, nvh(p), p->H,
+                         (int)p->dv, 0, (int)p->flags, plan, ncmax};
+        st = launch_status(gdn2::launch_chunk_prep(a, (int)p->dk, is_bf16(p), gates_bf16(p), s));
+        if (st) return st;
+    }
+    const int64_t nch = p->B * nvh(p);
+    const int vs = gdn2::chunk_state_slice(nch, (int)p->dv, (int)p->dk, (int)io_size(p));
+    gdn2::StateArgs a{blocks, ws_block_bytes(p), S0, o, S_out, p->B, p->T, nvh(p), (int)p->dv, 0,
+                      (int)(p->dv / vs), plan, ncmax};
+    return launch_status(gdn2::launch_chunk_state(a, (int)p->dk, vs, is_bf16(p), s));
+}
+
+int gdn2_recurrent_varlen(const gdn2_problem* p, const int32_t* cu_seqlens, const void* q, const void* k,
+                          const void* v, const void* alpha, const void* b, const void* w, const float* S_in,
+                          void* o, float* S_out, void* stream)
+{
+    int st = check_problem(p, false, true);
+    if (st) return st;
+    st = check_cu(p, cu_seqlens);
+    if (st) return st;
+    const int64_t nch = p->B * nvh(p);
+    if (nch > 0) {
+        st = check_inputs(p, q, k, v, alpha, b, w, o);
+        if (st) return st;
+    }
+    const Sizes z = sizes_of(p, true);
+    const Range ins[8] = {range_of(q, z.key),  range_of(k, z.key),  range_of(v, z.val),
+                          range_of(alpha, z.gk), range_of(b, z.gk), range_of(w, z.gv),
+                          range_of(S_in, z.state), range_of(cu_seqlens, nch > 0 ? 4 * (p->B + 1) : 0)};
+    const Range outs[2] = {range_of(o, z.val), range_of(S_out, z.state)};
+    st = check_alias(outs, 2, ins, 8, S_in, S_out, 6, 1);
+    if (st) return st;
+    st = check_align({q, k, v, alpha, b, w, S_in, o, S_out});
+    if (st) return st;
+    if (nch == 0 || (p->T == 0 && (S_out == S_in || S_out == nullptr))) return GDN2_OK;
+    st = device_ready();
+    if (st) return st;
+    // slice width from the mean sequence length
+    const int vs = gdn2::recurrent_slice(nch, p->T / p->B, (int)p->dv);
+    gdn2::RecArgs a{q, k, v, alpha, b, w, S_in, o, S_out, p->B, p->T, nvh(p), p->H, (int)p->dv,
+                    (int)(p->dv / vs), (int)p->flags, cu_seqlens};
     return launch_status(gdn2::launch_recurrent(a, (int)p->dk, vs, is_bf16(p), gates_bf16(p),
                                                 static_cast<hipStream_t>(stream)));
 }

@@ -130,15 +130,30 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
 
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
+    // this workgroup's chunk: value head hh, packed token index tok0 of its
+    // first token, length L, workspace block chi
     const int64_t chi = blockIdx.x;
-    const int64_t chain = chi / a.nt;
-    const int n = (int)(chi - chain * a.nt);
-    const int64_t bb = chain / a.H, hh = chain - bb * a.H;
-    const int64_t t0 = (int64_t)n * kChunk;
-    const int L = (int)((a.T - t0) < kChunk ? (a.T - t0) : kChunk);
-    const int64_t row0 = (bb * a.T + t0) * a.H + hh;    // row of token t0 in [B,T,Hv,*]
+    int64_t hh, tok0;
+    int L;
+    if (a.plan == nullptr) {
+        const int64_t chain = chi / a.nt;
+        const int n = (int)(chi - chain * a.nt);
+        const int64_t bb = chain / a.H;
+        hh = chain - bb * a.H;
+        const int64_t t0 = (int64_t)n * kChunk;
+        L = (int)((a.T - t0) < kChunk ? (a.T - t0) : kChunk);
+        tok0 = bb * a.T + t0;
+    } else {
+        hh = chi / a.ncmax;
+        const int64_t gc = chi - hh * a.ncmax;
+        if (gc >= a.plan[2 * a.B + 1]) return;         // past the batch's last chunk (first[N])
+        const int2 e = reinterpret_cast<const int2*>(a.plan + 2 * (a.B + 1))[gc];
+        tok0 = e.x;
+        L = e.y;
+    }
     const int64_t H = a.H, Hk = a.Hk;
-    const int64_t row0k = (bb * a.T + t0) * Hk + hh / (H / Hk);   // its q/k row in [B,T,H,dk]
+    const int64_t row0 = tok0 * H + hh;                  // row of the chunk's first token in [.,Hv,*]
+    const int64_t row0k = tok0 * Hk + hh / (H / Hk);     // its q/k row in [.,H,dk]
     const Tio* q = static_cast<const Tio*>(a.q);
     const Tio* k = static_cast<const Tio*>(a.k);
     const Tio* v = static_cast<const Tio*>(a.v);
@@ -624,10 +639,25 @@ __global__ __launch_bounds__(state_threads(VS, (int)sizeof(Tio)), 1) void k_chun
         slice = (int)(x - chain * ns);
     }
     const int j0 = slice * VS;
-    const int64_t bb = chain / a.H, hh = chain - bb * a.H;
+    const int64_t bb = chain / a.H, hh = chain - bb * a.H;   // sequence, value head
     const int dv = a.dv;
-    const int nt = a.nt;
-    const char* wsbase = static_cast<const char*>(a.ws) + chain * (int64_t)nt * a.ws_block;
+    // the sequence's first packed token, its length, chunk count and first
+    // workspace block
+    int64_t tok0, tlen;
+    int nt;
+    const char* wsbase;
+    if (a.plan == nullptr) {
+        tok0 = bb * a.T;
+        tlen = a.T;
+        nt = a.nt;
+        wsbase = static_cast<const char*>(a.ws) + chain * (int64_t)nt * a.ws_block;
+    } else {
+        const int* first = a.plan + (a.B + 1);
+        tok0 = a.plan[bb];
+        tlen = a.plan[bb + 1] - tok0;
+        nt = first[bb + 1] - first[bb];
+        wsbase = static_cast<const char*>(a.ws) + (hh * a.ncmax + first[bb]) * a.ws_block;
+    }
 
     if (loader) {
         // ---------------- loader waves ------------------------------------
@@ -864,8 +894,8 @@ __global__ __launch_bounds__(state_threads(VS, (int)sizeof(Tio)), 1) void k_chun
         // o: token 16*wave + l16, columns 16*ct + 4*grp .. +3
         {
             const int64_t t = (int64_t)n * kChunk + 16 * tb + l16;
-            if (t < a.T) {
-                Tio* orow = o + ((bb * a.T + t) * a.H + hh) * dv + j0 + jc + 4 * grp;
+            if (t < tlen) {
+                Tio* orow = o + ((tok0 + t) * a.H + hh) * dv + j0 + jc + 4 * grp;
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) st_vec4(orow + 16 * ct, accO[ct]);
             }
@@ -917,7 +947,7 @@ int chunk_state_slice(int64_t nchains, int dv, int dk, int esize)
 template <typename Tio, int DK, typename Tg>
 static hipError_t prep_dk(const PrepArgs& a, hipStream_t s)
 {
-    const int64_t nblk = a.B * a.H * (int64_t)a.nt;
+    const int64_t nblk = a.plan == nullptr ? a.B * a.H * (int64_t)a.nt : a.H * a.ncmax;
     if (a.dv <= 64)
         hipLaunchKernelGGL((k_chunk_prep<Tio, DK, 4, Tg>), dim3((unsigned)nblk), dim3(kThreads), 0, s, a);
     else if (a.dv <= 128)

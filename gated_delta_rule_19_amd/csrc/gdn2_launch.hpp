@@ -10,24 +10,41 @@ namespace gdn2 {
 // flags are the GDN2_FLAG_* prologue options.  H counts value heads (one
 // state each); Hk the query/key heads, H a multiple of Hk, value head h
 // reading q/k head h / (H / Hk).
+//
+// Packed variable-length batches: B is the number of sequences, T the
+// packed token count, and `plan` (null for equal-length batches) points at
+// the table k_varlen_plan writes: clamped offsets cu[B+1], each sequence's
+// first chunk first[B+1] (first[B] = chunk count), then per chunk its
+// {first token, length}.  Chunk c of value head h owns workspace block
+// h * ncmax + c; ncmax bounds the chunk count.
 struct PrepArgs {
     const void* q; const void* k; const void* v;
     const void* alpha; const void* b; const void* w;
     void* ws; int64_t ws_block;
     int64_t B, T, H, Hk; int dv; int nt; int flags;
+    const int* plan; int64_t ncmax;
 };
 
 struct StateArgs {
     const void* ws; int64_t ws_block;
     const float* S0; void* o; float* S_out;
     int64_t B, T, H; int dv; int nt; int nslices;
+    const int* plan; int64_t ncmax;
 };
 
+// cu (null for equal-length batches): the N+1 caller offsets of a packed
+// batch, each clamped into [0, T] before use
 struct RecArgs {
     const void* q; const void* k; const void* v;
     const void* alpha; const void* b; const void* w;
     const float* S_in; void* o; float* S_out;
     int64_t B, T, H, Hk; int dv; int nslices; int flags;
+    const int* cu;
+};
+
+struct PlanArgs {
+    const int* cu; int* plan;
+    int64_t N, T, ncmax;
 };
 
 struct NormArgs {
@@ -41,6 +58,11 @@ hipError_t launch_chunk_prep(const PrepArgs& a, int dk, bool bf16, bool gbf16, h
 hipError_t launch_chunk_state(const StateArgs& a, int dk, int vs, bool bf16, hipStream_t s);
 hipError_t launch_recurrent(const RecArgs& a, int dk, int vs, bool bf16, bool gbf16, hipStream_t s);
 hipError_t launch_gated_rmsnorm(const NormArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_varlen_plan(const PlanArgs& a, hipStream_t s);
+
+// int32 words of the varlen plan ahead of its chunk table (kept even so the
+// 8-byte table entries stay aligned)
+__host__ __device__ inline int64_t plan_head_words(int64_t N) { return 2 * (N + 1); }
 
 // Value-slice width the state pass uses for a problem (16, 32 or 64).
 int chunk_state_slice(int64_t nchains, int dv, int dk, int esize);

@@ -47,8 +47,17 @@ __global__ __launch_bounds__(kThreads) void k_recurrent(RecArgs a)
     const int jg = tid % NJ, rg = tid / NJ;
     const int64_t chain = blockIdx.x / a.nslices;
     const int slice = (int)(blockIdx.x - chain * a.nslices);
-    const int64_t bb = chain / a.H, hh = chain - bb * a.H;
+    const int64_t bb = chain / a.H, hh = chain - bb * a.H;   // sequence, value head
     const int64_t hk = hh / (a.H / a.Hk);   // the query/key head this value head reads
+    // the sequence's first packed token and its length (offsets of a packed
+    // batch clamped into [0, T])
+    int64_t tok0 = bb * a.T, tlen = a.T;
+    if (a.cu != nullptr) {
+        const int c0 = a.cu[bb], c1 = a.cu[bb + 1];
+        tok0 = c0 < 0 ? 0 : (c0 > a.T ? a.T : c0);
+        const int64_t e = c1 < tok0 ? tok0 : (c1 > a.T ? a.T : c1);
+        tlen = e - tok0;
+    }
     const int dv = a.dv;
     const int jc = slice * VS + 4 * jg;                 // first column of this thread
     const Tio* q = static_cast<const Tio*>(a.q);
@@ -73,8 +82,8 @@ __global__ __launch_bounds__(kThreads) void k_recurrent(RecArgs a)
     // key-axis vectors of a token -> registers (cooperative, coalesced)
     constexpr int VPT = (4 * DK + kThreads - 1) / kThreads;
     auto fetch = [&](int64_t t, float (&st)[VPT]) {
-        const int64_t rowk = ((bb * a.T + t) * a.H + hh) * DK;                // gates: value head
-        const int64_t rowq = ((bb * a.T + t) * a.Hk + hk) * DK;               // q, k: its key head
+        const int64_t rowk = ((tok0 + t) * a.H + hh) * DK;                    // gates: value head
+        const int64_t rowq = ((tok0 + t) * a.Hk + hk) * DK;                   // q, k: its key head
 #pragma unroll
         for (int u = 0; u < VPT; ++u) {
             const int e = tid + u * kThreads;
@@ -104,16 +113,16 @@ __global__ __launch_bounds__(kThreads) void k_recurrent(RecArgs a)
     };
 
     float stage[VPT];
-    if (a.T > 0) {
+    if (tlen > 0) {
         fetch(0, stage);
         stash(0, stage);
     }
     __syncthreads();
 
-    for (int64_t t = 0; t < a.T; ++t) {
+    for (int64_t t = 0; t < tlen; ++t) {
         const int buf = (int)(t & 1);
-        if (t + 1 < a.T) fetch(t + 1, stage);
-        const int64_t rowv = ((bb * a.T + t) * a.H + hh) * dv + jc;
+        if (t + 1 < tlen) fetch(t + 1, stage);
+        const int64_t rowv = ((tok0 + t) * a.H + hh) * dv + jc;
 
         f32x4 u = {0.f, 0.f, 0.f, 0.f};
         f32x4 r = u, m = u;
@@ -163,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void k_recurrent(RecArgs a)
             dst[9] = k2;
             dst[10] = q2;
         }
-        if (t + 1 < a.T) stash(buf ^ 1, stage);
+        if (t + 1 < tlen) stash(buf ^ 1, stage);
         __syncthreads();
 
         if (holder) {

@@ -24,6 +24,12 @@ Prologue variants (for the kernels' in-kernel prologue options):
 
 Grouped value heads: Hv (default H) value heads, a multiple of H; q and k are
 drawn for the H query/key heads, v, the gates and S0 for the Hv value heads.
+
+Packed variable-length batches (``make_packed``): the token tensors of one
+[1, T, *, *] batch with T = sum of the lengths, drawn as above, plus one
+initial state per sequence and the int32 offsets cu_seqlens.  The length mix
+(``length_mix``) draws log-uniform lengths in [lo, hi] until the total is
+reached (the last one cut to fit).
 """
 from __future__ import annotations
 
@@ -83,7 +89,9 @@ def make(wl: Workload, seed: int, device="cpu", B=None, T=None, H=None):
 
 
 def make_raw(B, T, H, dk, dv, io_dtype, seed, device="cpu", alpha_mu=3.0,
-             b_scale=1.0, s0_std=None, gate_logits=False, unit_qk=True, gate_dtype=torch.float32, Hv=None):
+             b_scale=1.0, s0_std=None, gate_logits=False, unit_qk=True, gate_dtype=torch.float32, Hv=None,
+             n_states=None):
+    """One input set; ``n_states`` initial states (default B) when ``s0_std`` is given."""
     dev = torch.device(device)
     g = torch.Generator(device=dev)
     g.manual_seed(int(seed))
@@ -109,8 +117,34 @@ def make_raw(B, T, H, dk, dv, io_dtype, seed, device="cpu", alpha_mu=3.0,
     alpha, b, w = alpha.to(gate_dtype), b.to(gate_dtype), w.to(gate_dtype)
     S0 = None
     if s0_std is not None:
-        S0 = randn(B, Hv, dk, dv) * s0_std
+        S0 = randn(B if n_states is None else n_states, Hv, dk, dv) * s0_std
     return dict(q=q, k=k, v=v, alpha=alpha, b=b, w=w, S0=S0)
+
+
+def length_mix(total, seed, lo=16, hi=4096):
+    """Seeded sequence lengths summing to ``total``: log-uniform in [lo, hi], last one cut."""
+    g = torch.Generator()
+    g.manual_seed(int(seed))
+    out, left = [], int(total)
+    while left > 0:
+        u = torch.rand((), generator=g).item()
+        n = int(round(lo * (hi / lo) ** u))
+        n = max(1, min(n, left))
+        out.append(n)
+        left -= n
+    return out
+
+
+def make_packed(lengths, H, dk, dv, io_dtype, seed, device="cpu", **kw):
+    """A packed batch of len(lengths) sequences: make_raw's tensors for [1, sum(lengths)],
+    S0 per sequence (with ``s0_std``), and ``cu`` = int32 offsets [N+1] on ``device``."""
+    T = int(sum(lengths))
+    inp = make_raw(1, T, H, dk, dv, io_dtype, seed, device, n_states=len(lengths), **kw)
+    cu = [0]
+    for n in lengths:
+        cu.append(cu[-1] + int(n))
+    inp["cu"] = torch.tensor(cu, dtype=torch.int32, device=torch.device(device))
+    return inp
 
 
 def to_numpy_f32(inp):

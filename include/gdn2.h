@@ -94,7 +94,7 @@ typedef enum {
     GDN2_ERR_ALIAS = 4,      /* an output overlaps an input or another output   */
     GDN2_ERR_WORKSPACE = 5,  /* workspace missing or smaller than required      */
     GDN2_ERR_DEVICE = 6,     /* no usable GPU, or a launch failed               */
-    GDN2_ERR_ALIGN = 7       /* a tensor pointer is not 16-byte aligned         */
+    GDN2_ERR_ALIGN = 7       /* a pointer is misaligned (16 B; cu_seqlens 4 B)  */
 } gdn2_status;
 
 typedef enum { GDN2_F32 = 0, GDN2_BF16 = 1 } gdn2_dtype;
@@ -177,6 +177,46 @@ int gdn2_recurrent_step(const gdn2_problem* p,
                         const void* q, const void* k, const void* v,
                         const void* alpha, const void* b, const void* w,
                         const float* S_in, void* o, float* S_out, void* stream);
+
+/*
+ * Packed variable-length batches.  The recurrence runs per sequence and each
+ * sequence starts from its own state (README "Architecture" and "Quick
+ * start"); a packed batch lays N sequences back to back on the token axis
+ * so that sequences of different lengths share one call without padding.
+ *   p->B      = N, the number of sequences;
+ *   p->T      = the total number of packed tokens (< 2^31);
+ *   cu_seqlens: N+1 int32 token offsets in device memory (4-byte aligned,
+ *               read by the kernels, never written): sequence i holds tokens
+ *               cu_seqlens[i] .. cu_seqlens[i+1]-1; the offsets must rise
+ *               from cu_seqlens[0] = 0 to cu_seqlens[N] = T (equal
+ *               neighbours are empty sequences, whose state passes through).
+ * Layouts: q, k [T, H, dk]; alpha, b [T, Hv, dk]; v, w, o [T, Hv, dv];
+ * S0/S_in, S_out [N, Hv, dk, dv].  Everything else (dtypes, flags, grouped
+ * value heads, alignment, aliasing, in-place state) is as for the calls
+ * above; cu_seqlens counts as an input for the aliasing rule.
+ * The offsets live on the device, so the host cannot check them: offsets
+ * that break the rule give undefined o and S_out, but every offset is
+ * clamped into [0, T] (and, in the chunked mode, to at least its
+ * predecessor) before use, so no access leaves the tensors.
+ *
+ * Chunked mode: each sequence's chunks start at its first token (no chunk
+ * spans two sequences).  Three launches on `stream`: a one-workgroup plan
+ * (per-chunk token ranges, written into the workspace), the prep stage and
+ * the state pass.
+ */
+size_t gdn2_chunk_fwd_varlen_workspace_size(const gdn2_problem* p);
+
+int gdn2_chunk_fwd_varlen(const gdn2_problem* p, const int32_t* cu_seqlens,
+                          const void* q, const void* k, const void* v,
+                          const void* alpha, const void* b, const void* w,
+                          const float* S0, void* o, float* S_out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Fused recurrent mode over a packed batch: one pass per sequence. */
+int gdn2_recurrent_varlen(const gdn2_problem* p, const int32_t* cu_seqlens,
+                          const void* q, const void* k, const void* v,
+                          const void* alpha, const void* b, const void* w,
+                          const float* S_in, void* o, float* S_out, void* stream);
 
 /*
  * Output step of the layer (README "Architecture": "Gated RMS Norm <- SiLU

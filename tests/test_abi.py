@@ -262,3 +262,101 @@ def test_gated_rmsnorm_validates():
     assert L.gdn2_gated_rmsnorm(ctypes.byref(empty.p), None, None, None, None, None) == OK
     bad = Call(dv=40)
     assert L.gdn2_gated_rmsnorm(ctypes.byref(bad.p), P(o), P(gt), P(wt), P(y), None) == SHAPE
+
+
+class VCall(Call):
+    """Fake buffers of a packed batch: N sequences, T packed tokens."""
+
+    def __init__(self, N=3, T=100, H=2, dk=64, dv=32, io=1, gate=0, flags=0, Hv=0):
+        super().__init__(B=1, T=T, H=H, dk=dk, dv=dv, io=io, gate=gate, flags=flags, Hv=Hv)
+        self.p.B = N
+        nv = N * (Hv or H)
+        self.size["S0"] = self.size["S_out"] = nv * dk * dv * 4
+        self.size["cu"] = 4 * (N + 1)
+        self.size["ws"] = g.lib().gdn2_chunk_fwd_varlen_workspace_size(ctypes.byref(self.p)) or 256
+        addr = BASE
+        for name, n in self.size.items():
+            self.ptr[name] = addr
+            addr += (n + 4095) // 4096 * 4096 + 4096
+
+    def fwd(self, **over):
+        a = dict(self.ptr)
+        a.update(over)
+        P = lambda x: None if x is None else ctypes.c_void_p(x)
+        wsb = over.pop("ws_bytes", None) if "ws_bytes" in over else self.size["ws"]
+        return g.lib().gdn2_chunk_fwd_varlen(ctypes.byref(self.p), P(a["cu"]), *(P(a[n]) for n in
+                                             ("q", "k", "v", "alpha", "b", "w", "S0", "o", "S_out")),
+                                             P(a["ws"]), wsb, None)
+
+    def rec(self, **over):
+        a = dict(self.ptr)
+        a.update(over)
+        P = lambda x: None if x is None else ctypes.c_void_p(x)
+        return g.lib().gdn2_recurrent_varlen(ctypes.byref(self.p), P(a["cu"]), *(P(a[n]) for n in
+                                             ("q", "k", "v", "alpha", "b", "w", "S0", "o", "S_out")), None)
+
+
+def test_varlen_valid_calls_reach_the_device_check():
+    for kw in ({}, {"Hv": 4}, {"io": 0}, {"gate": 1, "flags": 7}, {"N": 1}, {"T": 0}):
+        c = VCall(**kw)
+        assert c.fwd() == DEVICE and c.rec() == DEVICE, kw
+
+
+def test_varlen_workspace_size():
+    # plan (2 (N+1) int32 offsets + 8 bytes per chunk slot, 256-aligned), then one
+    # block per (value head, chunk slot); slots = ceil(T / 64) + N
+    import torch
+    N, T, H, Hv = 5, 1000, 4, 8
+    p = bnd.problem(N, T, H, 128, 128, torch.bfloat16, Hv=Hv)
+    slots = (T + 63) // 64 + N
+    plan = (4 * 2 * (N + 1) + 8 * slots + 255) // 256 * 256
+    assert g.lib().gdn2_chunk_fwd_varlen_workspace_size(ctypes.byref(p)) == plan + Hv * slots * 74240
+    bad = bnd.problem(N, T, H, 100, 128, torch.bfloat16)
+    assert g.lib().gdn2_chunk_fwd_varlen_workspace_size(ctypes.byref(bad)) == 0
+
+
+def test_varlen_errors():
+    c = VCall()
+    assert c.fwd(cu=None) == NULL and c.rec(cu=None) == NULL
+    assert c.fwd(cu=c.ptr["cu"] + 2) == ALIGN and c.rec(cu=c.ptr["cu"] + 2) == ALIGN
+    assert c.fwd(cu=c.ptr["cu"] + 4) == DEVICE                  # int32 alignment is enough
+    assert c.fwd(o=c.ptr["cu"]) == ALIAS and c.rec(S_out=c.ptr["cu"]) == ALIAS
+    assert c.fwd(ws=c.ptr["cu"]) == ALIAS
+    assert c.fwd(ws_bytes=c.size["ws"] - 1) == WS and c.fwd(ws=None) == WS
+    assert c.fwd(q=None) == NULL and c.rec(w=None) == NULL
+    assert c.fwd(S_out=c.ptr["S0"]) == DEVICE and c.rec(S_out=c.ptr["S0"]) == DEVICE   # in place
+    assert c.fwd(S_out=c.ptr["S0"] + 256) == ALIAS
+    big = VCall(T=2 ** 31 - 60)
+    assert big.fwd() == SHAPE and big.rec() == SHAPE
+    chunk = VCall()
+    chunk.p.chunk = 32
+    assert chunk.fwd() == SHAPE and chunk.rec() == DEVICE
+
+
+def test_varlen_states_are_per_sequence():
+    # N = 3 sequences, Hv = 4, dk = 64, dv = 32: a state tensor holds 3 x 4 x 64 x 32 fp32
+    c = VCall(N=3, Hv=4)
+    n = 3 * 4 * 64 * 32 * 4
+    assert c.fwd(o=c.ptr["S0"] + n) == DEVICE
+    assert c.fwd(o=c.ptr["S0"] + n - 256) == ALIAS
+
+
+def test_varlen_empty_calls_need_no_pointers():
+    none = {n: None for n in ("cu", "q", "k", "v", "alpha", "b", "w", "S0", "o", "S_out", "ws")}
+    c = VCall(N=0)
+    assert c.fwd(**none, ws_bytes=0) == OK and c.rec(**none) == OK
+    # no tokens and the state left in place: nothing to do
+    t0 = VCall(T=0)
+    assert t0.fwd(q=None, k=None, v=None, alpha=None, b=None, w=None, o=None, S_out=t0.ptr["S0"]) == OK
+    assert t0.rec(q=None, k=None, v=None, alpha=None, b=None, w=None, o=None, S_out=t0.ptr["S0"]) == OK
+
+
+def test_varlen_binding_validates():
+    import torch
+    q = torch.zeros(1, 8, 2, 16)
+    v = torch.zeros(1, 8, 2, 16)
+    cu = torch.tensor([0, 3, 8], dtype=torch.int32)
+    with pytest.raises(ValueError):          # CPU tensors
+        g.chunk_fwd_varlen(q, q, v, q, q, v, cu)
+    with pytest.raises(ValueError):
+        g.recurrent_varlen(q, q, v, q, q, v, cu.long())
