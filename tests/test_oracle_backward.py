@@ -1,0 +1,133 @@
+"""Pins of the backward oracle (CPU only).
+
+The gradient of the forward recurrence (burn-gdn2 README, "Architecture") is
+fixed by the forward alone.  Both backward routines are checked against
+central finite differences of the pinned forward (``oracle.reference.recurrent``)
+for every input element, on shapes that span several chunks with a ragged
+tail, then against each other on larger shapes; a reverse loop with planted
+slips shows that the finite-difference pin rejects each of them.
+"""
+import numpy as np
+import pytest
+
+from oracle.backward import chunked_bwd, loss, recurrent_bwd
+from oracle.reference import recurrent, rel_l2
+
+NAMES = ("q", "k", "v", "alpha", "b", "w", "S0")
+
+
+def _draw(rng, B=1, T=6, H=1, dk=3, dv=2):
+    k = rng.standard_normal((B, T, H, dk))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    return dict(q=rng.standard_normal((B, T, H, dk)), k=k, v=rng.standard_normal((B, T, H, dv)),
+                alpha=rng.uniform(0.5, 1.0, (B, T, H, dk)), b=rng.uniform(0.0, 2.0, (B, T, H, dk)),
+                w=rng.uniform(0.0, 1.0, (B, T, H, dv)), S0=rng.standard_normal((B, H, dk, dv)) * 0.5), \
+        rng.standard_normal((B, T, H, dv)), rng.standard_normal((B, H, dk, dv))
+
+
+def _fd(x, dO, dS, h=1e-6):
+    """Central differences of loss(recurrent(x)) for every element of every input."""
+    out = {}
+    for n in NAMES:
+        g = np.zeros_like(x[n])
+        for idx in np.ndindex(*x[n].shape):
+            vals = []
+            for s in (h, -h):
+                y = {m: a.copy() for m, a in x.items()}
+                y[n][idx] += s
+                o, S = recurrent(*(y[m] for m in NAMES[:6]), y["S0"])
+                vals.append(loss(o, S, dO, dS))
+            g[idx] = (vals[0] - vals[1]) / (2 * h)
+        out["d" + n] = g
+    return out
+
+
+def _check_fd(bwd, x, dO, dS, tol=1e-7):
+    fd = _fd(x, dO, dS)
+    g = bwd(*(x[m] for m in NAMES), dO, dS)
+    for n in fd:
+        err = np.max(np.abs(g[n] - fd[n])) / max(1.0, np.max(np.abs(fd[n])))
+        assert err < tol, f"{n}: max error {err:.2e} against finite differences"
+
+
+@pytest.mark.parametrize("T", [1, 6])
+def test_recurrent_bwd_matches_finite_differences(T):
+    x, dO, dS = _draw(np.random.default_rng(T), T=T)
+    _check_fd(recurrent_bwd, x, dO, dS)
+
+
+@pytest.mark.parametrize("T,chunk", [(6, 4), (9, 4), (8, 4), (3, 16)])
+def test_chunked_bwd_matches_finite_differences(T, chunk):
+    x, dO, dS = _draw(np.random.default_rng(10 + T), B=1, T=T, H=2, dk=3, dv=2)
+    _check_fd(lambda *a: chunked_bwd(*a, chunk=chunk), x, dO, dS)
+
+
+@pytest.mark.parametrize("T,chunk", [(1, 16), (16, 16), (17, 16), (40, 16), (130, 64)])
+def test_chunked_equals_recurrent(T, chunk):
+    x, dO, dS = _draw(np.random.default_rng(20 + T), B=2, T=T, H=2, dk=8, dv=5)
+    g1 = recurrent_bwd(*(x[m] for m in NAMES), dO, dS)
+    g2 = chunked_bwd(*(x[m] for m in NAMES), dO, dS, chunk=chunk)
+    for n in g1:
+        assert rel_l2(g2[n], g1[n]) < 1e-11, n
+
+
+def test_missing_state_and_state_gradient():
+    """S0 = None is the zero state, dS_T = None no gradient on the final state."""
+    x, dO, _ = _draw(np.random.default_rng(3), T=5, dk=4, dv=3)
+    g1 = recurrent_bwd(*(x[m] for m in NAMES[:6]), None, dO, None)
+    g2 = recurrent_bwd(*(x[m] for m in NAMES[:6]), np.zeros_like(x["S0"]), dO, np.zeros_like(x["S0"]))
+    for n in g1:
+        np.testing.assert_array_equal(g1[n], g2[n])
+    g3 = chunked_bwd(*(x[m] for m in NAMES[:6]), None, dO, None, chunk=2)
+    for n in g1:
+        assert rel_l2(g3[n], g1[n]) < 1e-12
+
+
+# ---- planted slips: each must fail the finite-difference pin ------------------
+def _reverse_with_slip(slip):
+    def bwd(q, k, v, alpha, b, w, S0, dO, dS_T=None):
+        B, T, H, dk = q.shape
+        dv = v.shape[-1]
+        S = [S0.copy()]
+        for t in range(T):
+            z = alpha[:, t] * b[:, t] * k[:, t]
+            delta = w[:, t] * v[:, t] - np.einsum("bhcj,bhc->bhj", S[-1], z)
+            S.append(alpha[:, t][..., None] * S[-1] + k[:, t][..., :, None] * delta[..., None, :])
+        G = dS_T.copy()
+        g = {n: np.zeros_like(a) for n, a in (("dq", q), ("dk", k), ("dv", v), ("dalpha", alpha), ("db", b),
+                                              ("dw", w))}
+        for t in range(T - 1, -1, -1):
+            St, Sp = S[t + 1], S[t]
+            if slip != "no_output_grad":
+                G = G + q[:, t][..., :, None] * dO[:, t][..., None, :]
+            g["dq"][:, t] = np.einsum("bhcj,bhj->bhc", Sp if slip == "dq_old_state" else St, dO[:, t])
+            z = alpha[:, t] * b[:, t] * k[:, t]
+            delta = w[:, t] * v[:, t] - np.einsum("bhcj,bhc->bhj", Sp, z)
+            dd = np.einsum("bhcj,bhc->bhj", G, k[:, t])
+            dz = -np.einsum("bhcj,bhj->bhc", Sp, dd)
+            g["dk"][:, t] = np.einsum("bhcj,bhj->bhc", G, delta) + (0 if slip == "no_dz_in_dk" else
+                                                                    dz * alpha[:, t] * b[:, t])
+            g["dw"][:, t] = dd * v[:, t]
+            g["dv"][:, t] = dd * w[:, t]
+            g["db"][:, t] = dz * alpha[:, t] * k[:, t]
+            g["dalpha"][:, t] = (0 if slip == "no_decay_grad" else np.sum(G * Sp, axis=-1)) + dz * b[:, t] * k[:, t]
+            sign = 1.0 if slip == "erase_sign" else -1.0
+            G = alpha[:, t][..., None] * G + sign * z[..., :, None] * dd[..., None, :]
+        g["dS0"] = G
+        return g
+    return bwd
+
+
+SLIPS = ["no_output_grad", "dq_old_state", "no_dz_in_dk", "no_decay_grad", "erase_sign"]
+
+
+@pytest.mark.parametrize("slip", SLIPS)
+def test_backward_slip_is_rejected(slip):
+    x, dO, dS = _draw(np.random.default_rng(5), T=4)
+    with pytest.raises(AssertionError):
+        _check_fd(_reverse_with_slip(slip), x, dO, dS)
+
+
+def test_correct_reverse_passes_the_slip_harness():
+    x, dO, dS = _draw(np.random.default_rng(5), T=4)
+    _check_fd(_reverse_with_slip(None), x, dO, dS)
