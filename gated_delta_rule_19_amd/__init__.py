@@ -15,6 +15,8 @@ from ._binding import (  # noqa: F401
     Problem,
     abi_version,
     alloc_workspace,
+    chunk_bwd,
+    chunk_bwd_workspace_size,
     chunk_fwd,
     chunk_fwd_varlen,
     chunk_fwd_varlen_workspace_size,

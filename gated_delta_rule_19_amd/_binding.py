@@ -24,7 +24,7 @@ _STATUS = {0: "GDN2_OK", 1: "GDN2_ERR_NULL", 2: "GDN2_ERR_SHAPE", 3: "GDN2_ERR_D
 EXPORTED = ("gdn2_abi_version", "gdn2_status_str", "gdn2_chunk_fwd_workspace_size",
             "gdn2_chunk_fwd", "gdn2_chunk_prep", "gdn2_chunk_state", "gdn2_recurrent_step",
             "gdn2_gated_rmsnorm", "gdn2_chunk_fwd_varlen_workspace_size", "gdn2_chunk_fwd_varlen",
-            "gdn2_recurrent_varlen")
+            "gdn2_recurrent_varlen", "gdn2_chunk_bwd_workspace_size", "gdn2_chunk_bwd")
 
 
 class Problem(ctypes.Structure):
@@ -79,6 +79,10 @@ def lib():
         L.gdn2_chunk_fwd_varlen.argtypes = [P, vp] + [vp] * 9 + [vp, sz, vp]
         L.gdn2_recurrent_varlen.restype = ctypes.c_int
         L.gdn2_recurrent_varlen.argtypes = [P, vp] + [vp] * 9 + [vp]
+        L.gdn2_chunk_bwd_workspace_size.restype = sz
+        L.gdn2_chunk_bwd_workspace_size.argtypes = [P]
+        L.gdn2_chunk_bwd.restype = ctypes.c_int
+        L.gdn2_chunk_bwd.argtypes = [P] + [vp] * 16 + [vp, sz, vp]
         if L.gdn2_abi_version() != ABI_VERSION:   # the Problem mirror must match the library's struct
             raise ImportError(f"{LIB_PATH} has ABI {L.gdn2_abi_version()}, this binding expects {ABI_VERSION}: "
                               "rebuild it")
@@ -274,6 +278,36 @@ def recurrent_varlen(q, k, v, alpha, b, w, cu_seqlens, S_in=None, *, o=None, S_o
     _check(lib().gdn2_recurrent_varlen(ctypes.byref(p), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                                        _ptr(b), _ptr(w), _ptr(S_in), _ptr(o), _ptr(S_out), _stream(dev)))
     return o, S_out
+
+
+def chunk_bwd_workspace_size(B, T, H, dk, dv, io_dtype: torch.dtype, gate_dtype: torch.dtype = torch.float32) -> int:
+    p = problem(B, T, H, dk, dv, io_dtype, gate_dtype=gate_dtype)
+    return int(lib().gdn2_chunk_bwd_workspace_size(ctypes.byref(p)))
+
+
+def chunk_bwd(q, k, v, alpha, b, w, dO, S0=None, dS_T=None, *, want_dS0: bool = True, workspace=None,
+              flags: int = 0):
+    """Backward of the chunked forward (``gdn2_chunk_bwd``): gradients of
+    sum(dO * o) + sum(dS_T * S_T) w.r.t. q, k, v, alpha, b, w (same shapes and dtypes as
+    the inputs) and S0 (float32, when ``want_dS0``).  Returns a dict dq, dk, dv, dalpha,
+    db, dw, dS0."""
+    p, dev = _problem_from(q, k, v, alpha, b, w, flags)
+    _check_state(S0, p, dev, "S0")
+    _check_state(dS_T, p, dev, "dS_T")
+    if tuple(dO.shape) != tuple(v.shape) or dO.dtype != v.dtype or dO.device != dev or not dO.is_contiguous():
+        raise ValueError("dO must be a contiguous tensor like v")
+    g = {n: torch.empty_like(x) for n, x in (("dq", q), ("dk", k), ("dv", v), ("dalpha", alpha), ("db", b),
+                                            ("dw", w))}
+    g["dS0"] = (torch.empty((p.B, p.value_heads, p.dk, p.dv), dtype=torch.float32, device=dev)
+                if want_dS0 else None)
+    need = int(lib().gdn2_chunk_bwd_workspace_size(ctypes.byref(p)))
+    if workspace is None:
+        workspace = alloc_workspace(need, dev)
+    _check(lib().gdn2_chunk_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w), _ptr(S0),
+                                _ptr(dO), _ptr(dS_T), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dalpha"]),
+                                _ptr(g["db"]), _ptr(g["dw"]), _ptr(g["dS0"]), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(dev)))
+    return g
 
 
 def gated_rmsnorm(o, g, weight, *, out=None, inplace: bool = False):

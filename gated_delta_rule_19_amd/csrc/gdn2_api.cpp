@@ -182,6 +182,32 @@ int do_state(const gdn2_problem* p, const float* S0, void* o, float* S_out, cons
     return launch_status(gdn2::launch_chunk_state(a, (int)p->dk, vs, is_bf16(p), s));
 }
 
+// backward workspace: forward factors | chunk entry states | chunk exit
+// state gradients | gradient scratch, each 256-byte aligned
+struct BwdLayout {
+    int64_t chk, dsl, scratch, total;
+};
+
+BwdLayout bwd_layout(const gdn2_problem* p)
+{
+    const int64_t states = p->B * p->H * nchunks(p) * p->dk * p->dv * 4;
+    const int64_t align = 255;
+    BwdLayout l;
+    l.chk = (ws_bytes(p) + align) & ~align;
+    l.dsl = (l.chk + states + align) & ~align;
+    l.scratch = (l.dsl + states + align) & ~align;
+    l.total = l.scratch + gdn2::chunk_grad_scratch_bytes((int)p->dk, (int)p->dv, p->B * p->H * nchunks(p));
+    return l;
+}
+
+int check_bwd_problem(const gdn2_problem* p)
+{
+    const int st = check_problem(p, true);
+    if (st) return st;
+    if (p->flags != 0 || (p->Hv != 0 && p->Hv != p->H)) return GDN2_ERR_SHAPE;
+    return GDN2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -403,6 +429,68 @@ int gdn2_recurrent_varlen(const gdn2_problem* p, const int32_t* cu_seqlens, cons
                     (int)(p->dv / vs), (int)p->flags, cu_seqlens};
     return launch_status(gdn2::launch_recurrent(a, (int)p->dk, vs, is_bf16(p), gates_bf16(p),
                                                 static_cast<hipStream_t>(stream)));
+}
+
+size_t gdn2_chunk_bwd_workspace_size(const gdn2_problem* p)
+{
+    if (check_bwd_problem(p) != GDN2_OK) return 0;
+    return static_cast<size_t>(bwd_layout(p).total);
+}
+
+int gdn2_chunk_bwd(const gdn2_problem* p, const void* q, const void* k, const void* v, const void* alpha,
+                   const void* b, const void* w, const float* S0, const void* dO, const float* dS_T, void* dq,
+                   void* dk, void* dv, void* dalpha, void* db, void* dw, float* dS0, void* workspace,
+                   size_t workspace_bytes, void* stream)
+{
+    int st = check_bwd_problem(p);
+    if (st) return st;
+    st = check_inputs(p, q, k, v, alpha, b, w, dO);
+    if (st) return st;
+    if (rows_nonempty(p) && (!dq || !dk || !dv || !dalpha || !db || !dw)) return GDN2_ERR_NULL;
+    const BwdLayout l = bwd_layout(p);
+    const int64_t need = p->B * p->H > 0 ? l.total : 0;
+    if (need > 0 && (workspace == nullptr || static_cast<int64_t>(workspace_bytes) < need))
+        return GDN2_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_WORKSPACE;
+    const Sizes z = sizes_of(p);
+    const Range ins[9] = {range_of(q, z.key),  range_of(k, z.key),  range_of(v, z.val),
+                          range_of(alpha, z.gk), range_of(b, z.gk), range_of(w, z.gv),
+                          range_of(S0, z.state), range_of(dO, z.val), range_of(dS_T, z.state)};
+    const Range outs[8] = {range_of(dq, z.key),  range_of(dk, z.key), range_of(dv, z.val),
+                           range_of(dalpha, z.gk), range_of(db, z.gk), range_of(dw, z.gv),
+                           range_of(dS0, z.state), range_of(workspace, need)};
+    st = check_alias(outs, 8, ins, 9, nullptr, nullptr, -1, -1);
+    if (st) return st;
+    st = check_align({q, k, v, alpha, b, w, S0, dO, dS_T, dq, dk, dv, dalpha, db, dw, dS0});
+    if (st) return st;
+    if (p->B * p->H == 0) return GDN2_OK;
+    if (nchunks(p) == 0 && dS0 == nullptr) return GDN2_OK;
+    st = device_ready();
+    if (st) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    float* chk = reinterpret_cast<float*>(ws + l.chk);
+    float* dsl = reinterpret_cast<float*>(ws + l.dsl);
+    const int64_t nch = p->B * p->H;
+    if (nchunks(p) > 0) {
+        st = do_prep(p, q, k, v, alpha, b, w, ws, s);
+        if (st) return st;
+        const int vs = gdn2::chunk_state_slice(nch, (int)p->dv, (int)p->dk, (int)io_size(p));
+        gdn2::StateArgs fa{ws, ws_block_bytes(p), S0, nullptr, nullptr, p->B, p->T, p->H, (int)p->dv,
+                           (int)nchunks(p), (int)(p->dv / vs), nullptr, 0, chk};
+        st = launch_status(gdn2::launch_chunk_state(fa, (int)p->dk, vs, is_bf16(p), s));
+        if (st) return st;
+    }
+    const int bvs = p->dv <= 64 ? (int)p->dv : (p->dv % 64 == 0 ? 64 : (p->dv % 32 == 0 ? 32 : 16));
+    gdn2::BwdStateArgs ba{ws, ws_block_bytes(p), dO, dS_T, dsl, dS0, p->B, p->T, p->H, (int)p->dk, (int)p->dv,
+                          (int)nchunks(p), (int)(p->dv / bvs), bvs};
+    st = launch_status(gdn2::launch_chunk_state_bwd(ba, is_bf16(p), s));
+    if (st) return st;
+    if (nchunks(p) == 0) return GDN2_OK;
+    gdn2::GradArgs ga{q, k, v, alpha, b, w, dO, chk, dsl, dq, dk, dv, dalpha, db, dw,
+                      reinterpret_cast<float*>(ws + l.scratch), p->B, p->T, p->H, (int)p->dk, (int)p->dv,
+                      (int)nchunks(p), nch * nchunks(p)};
+    return launch_status(gdn2::launch_chunk_grad(ga, is_bf16(p), gates_bf16(p), s));
 }
 
 int gdn2_gated_rmsnorm(const gdn2_problem* p, const void* o, const void* g, const float* weight, void* y,

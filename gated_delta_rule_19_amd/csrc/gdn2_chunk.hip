@@ -595,7 +595,8 @@ inline int state_lds_bytes(int dk, int vs, int es)
 
 // value columns per compute wave and threads per workgroup of the state pass
 
-template <typename Tio, int DK, int VS>
+// CHK: also write the state entering every chunk to a.S_chk
+template <typename Tio, int DK, int VS, bool CHK>
 __global__ __launch_bounds__(state_threads(VS, (int)sizeof(Tio)), 1) void k_chunk_state(StateArgs a)
 {
     using IO = Io<Tio>;
@@ -799,6 +800,20 @@ __global__ __launch_bounds__(state_threads(VS, (int)sizeof(Tio)), 1) void k_chun
     };
 
     for (int n = 0; n < nt; ++n) {
+        if constexpr (CHK) {
+            // checkpoint: the state entering chunk n (kept for the backward pass)
+            float* dst = a.S_chk + (chain * (int64_t)nt + n) * DK * dv + j0 + jc + l16;
+#pragma unroll
+            for (int i = 0; i < SPW; ++i) {
+                const int rt = tb * SPW + i;
+                if (rt < SRT) {
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) dst[(16 * rt + 4 * grp + e) * dv + 16 * ct] = accS[i][ct][e];
+                }
+            }
+        }
         const char* B0 = smem + (NB == 2 ? (n & 1) : 0) * L::GBUF * 16;
         const char* Wl = B0 + L::O_W * 16;
         const char* Ql = B0 + L::O_Q * 16;
@@ -894,7 +909,7 @@ __global__ __launch_bounds__(state_threads(VS, (int)sizeof(Tio)), 1) void k_chun
         // o: token 16*wave + l16, columns 16*ct + 4*grp .. +3
         {
             const int64_t t = (int64_t)n * kChunk + 16 * tb + l16;
-            if (t < tlen) {
+            if (t < tlen && o != nullptr) {
                 Tio* orow = o + ((tok0 + t) * a.H + hh) * dv + j0 + jc + 4 * grp;
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) st_vec4(orow + 16 * ct, accO[ct]);
@@ -983,7 +998,10 @@ static hipError_t state_v(const StateArgs& a, hipStream_t s)
     } else {
         const int64_t nblk = a.B * a.H * (int64_t)a.nslices;
         constexpr int nthreads = state_threads(VS, (int)sizeof(Tio));
-        hipLaunchKernelGGL((k_chunk_state<Tio, DK, VS>), dim3((unsigned)nblk), dim3(nthreads), 0, s, a);
+        if (a.S_chk != nullptr)
+            hipLaunchKernelGGL((k_chunk_state<Tio, DK, VS, true>), dim3((unsigned)nblk), dim3(nthreads), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_chunk_state<Tio, DK, VS, false>), dim3((unsigned)nblk), dim3(nthreads), 0, s, a);
         return hipGetLastError();
     }
 }

@@ -25,11 +25,14 @@ struct PrepArgs {
     const int* plan; int64_t ncmax;
 };
 
+// S_chk (optional, equal-length batches only): the fp32 state entering every
+// chunk, [B*H][nt][dk][dv]; o may be null when only states are wanted
 struct StateArgs {
     const void* ws; int64_t ws_block;
     const float* S0; void* o; float* S_out;
     int64_t B, T, H; int dv; int nt; int nslices;
     const int* plan; int64_t ncmax;
+    float* S_chk;
 };
 
 // cu (null for equal-length batches): the N+1 caller offsets of a packed
@@ -40,6 +43,29 @@ struct RecArgs {
     const float* S_in; void* o; float* S_out;
     int64_t B, T, H, Hk; int dv; int nslices; int flags;
     const int* cu;
+};
+
+// Backward (equal-length batches, H value heads = query/key heads, no
+// prologue flags).  Reverse state pass: per (batch, head, slice of vs value
+// columns), reads the forward workspace, dO and dS_T (nullable), writes the
+// gradient each chunk's exit state receives, dSL [B*H][nt][dk][dv], and dS0
+// (nullable).
+struct BwdStateArgs {
+    const void* ws; int64_t ws_block;
+    const void* dO; const float* dS_T; float* dSL; float* dS0;
+    int64_t B, T, H; int dk, dv, nt, nslices, vs;
+};
+
+// Per-chunk gradients: inputs, dO, the chunk entry states S_chk and exit
+// gradients dSL ([B*H][nt][dk][dv] fp32); writes dq, dk, dv (I/O dtype) and
+// dalpha, db, dw (gate dtype).  scratch: fp32 per workgroup.
+struct GradArgs {
+    const void* q; const void* k; const void* v;
+    const void* alpha; const void* b; const void* w; const void* dO;
+    const float* S_chk; const float* dSL;
+    void* dq; void* dk_out; void* dv_out; void* dalpha; void* db; void* dw;
+    float* scratch;
+    int64_t B, T, H; int dk, dv, nt; int64_t total;
 };
 
 struct PlanArgs {
@@ -59,6 +85,11 @@ hipError_t launch_chunk_state(const StateArgs& a, int dk, int vs, bool bf16, hip
 hipError_t launch_recurrent(const RecArgs& a, int dk, int vs, bool bf16, bool gbf16, hipStream_t s);
 hipError_t launch_gated_rmsnorm(const NormArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_varlen_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_chunk_state_bwd(const BwdStateArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_chunk_grad(const GradArgs& a, bool bf16, bool gbf16, hipStream_t s);
+// workgroups of the gradient launch and the bytes of its scratch
+int64_t grad_blocks(int64_t total);
+int64_t chunk_grad_scratch_bytes(int dk, int dv, int64_t total);
 
 // int32 words of the varlen plan ahead of its chunk table (kept even so the
 // 8-byte table entries stay aligned)

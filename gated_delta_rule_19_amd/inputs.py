@@ -121,6 +121,17 @@ def make_raw(B, T, H, dk, dv, io_dtype, seed, device="cpu", alpha_mu=3.0,
     return dict(q=q, k=k, v=v, alpha=alpha, b=b, w=w, S0=S0)
 
 
+def make_out_grads(B, T, H, dk, dv, io_dtype, seed, device="cpu", state_grad=True):
+    """Seeded output gradients for the backward: dO ~ N(0, 1) [B,T,H,dv] in the I/O dtype,
+    dS_T ~ N(0, 1) [B,H,dk,dv] fp32 (None without ``state_grad``)."""
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(int(seed))
+    dO = torch.randn(B, T, H, dv, generator=g, device=dev).to(io_dtype)
+    dS = torch.randn(B, H, dk, dv, generator=g, device=dev) if state_grad else None
+    return dO, dS
+
+
 def length_mix(total, seed, lo=16, hi=4096):
     """Seeded sequence lengths summing to ``total``: log-uniform in [lo, hi], last one cut."""
     g = torch.Generator()

@@ -219,6 +219,36 @@ int gdn2_recurrent_varlen(const gdn2_problem* p, const int32_t* cu_seqlens,
                           const float* S_in, void* o, float* S_out, void* stream);
 
 /*
+ * Backward pass of the chunked forward (README: chunk mode is the training
+ * mode).  For the loss  sum(dO * o) + sum(dS_T * S_T)  of the forward
+ * gdn2_chunk_fwd(p, q, k, v, alpha, b, w, S0) computes its gradients with
+ * respect to every input:
+ *   dq, dk, dv        [B, T, H, dk|dv]   io_dtype
+ *   dalpha, db, dw    [B, T, H, dk|dv]   gate_dtype
+ *   dS0               [B, H, dk, dv]     fp32 (NULL: not wanted)
+ * dO [B, T, H, dv] (io_dtype) is the gradient of o; dS_T (fp32, NULL = 0) that
+ * of the final state; S0 NULL = the zero initial state, as in the forward.
+ * The forward is recomputed inside (no forward workspace is kept between
+ * the calls); the backward is exact up to rounding, with fp32 arithmetic
+ * throughout and the forward's operands in io_dtype.
+ * This version requires flags == 0 and Hv == 0 or H (GDN2_ERR_SHAPE
+ * otherwise).  Every gradient output must be distinct from every input and
+ * from each other (GDN2_ERR_ALIAS); all tensors 16-byte aligned; the
+ * workspace 256-byte aligned and at least gdn2_chunk_bwd_workspace_size(p)
+ * bytes (it holds the forward factors, the state entering every chunk, the
+ * state gradient leaving every chunk and per-workgroup scratch).
+ * Launches five kernels on `stream`.
+ */
+size_t gdn2_chunk_bwd_workspace_size(const gdn2_problem* p);
+
+int gdn2_chunk_bwd(const gdn2_problem* p,
+                   const void* q, const void* k, const void* v,
+                   const void* alpha, const void* b, const void* w,
+                   const float* S0, const void* dO, const float* dS_T,
+                   void* dq, void* dk, void* dv, void* dalpha, void* db, void* dw, float* dS0,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Output step of the layer (README "Architecture": "Gated RMS Norm <- SiLU
  * Gate"; "Configuration": norm_eps = 1e-5).  For every (token, head) row of
  * dv channels

@@ -1,0 +1,114 @@
+"""GPU parity of the chunked backward against the fp64 oracle (needs an MI355X).
+
+``gdn2_chunk_bwd`` returns the gradients of sum(dO * o) + sum(dS_T * S_T)
+with respect to q, k, v, alpha, b, w and S0; the oracle
+(``oracle.backward.recurrent_bwd``, pinned by finite differences of the
+forward) computes them in fp64 from the same inputs (bf16 widened exactly).
+Relative L2 error per gradient tensor: <= 1e-4 with fp32 I/O, <= 2e-2 with
+bf16 I/O (the forward's operands are bf16 there).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_19_amd as g
+from gated_delta_rule_19_amd import inputs
+from oracle.backward import recurrent_bwd
+from oracle.reference import rel_l2
+
+pytestmark = pytest.mark.gpu
+
+F32, BF16 = torch.float32, torch.bfloat16
+TOL = {F32: 1e-4, BF16: 2e-2}
+NAMES = ("dq", "dk", "dv", "dalpha", "db", "dw", "dS0")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    g.lib()
+    return torch.device("cuda:0")
+
+
+def _np(x):
+    return None if x is None else x.detach().to("cpu", torch.float64).numpy()
+
+
+def run(dev, B, T, H, dk, dv, io, gate, s0, dS, seed, b_scale=1.0):
+    inp = inputs.make_raw(B, T, H, dk, dv, io, seed, dev, s0_std=s0, gate_dtype=gate, b_scale=b_scale)
+    dO, dS_T = inputs.make_out_grads(B, T, H, dk, dv, io, seed + 1, dev, state_grad=dS)
+    got = g.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["b"], inp["w"], dO, inp["S0"], dS_T)
+    torch.cuda.synchronize()
+    return inp, dO, dS_T, got
+
+
+def ref(inp, dO, dS_T, chains=None):
+    h = {n: _np(x) for n, x in inp.items()}
+    dOn, dSn = _np(dO), _np(dS_T)
+    if chains is None:
+        return recurrent_bwd(h["q"], h["k"], h["v"], h["alpha"], h["b"], h["w"], h["S0"], dOn, dSn)
+    out = {n: [] for n in NAMES}
+    for bi, hi in chains:
+        sl = lambda x: None if x is None else x[bi:bi + 1, :, hi:hi + 1]
+        st = lambda x: None if x is None else x[bi:bi + 1, hi:hi + 1]
+        r = recurrent_bwd(sl(h["q"]), sl(h["k"]), sl(h["v"]), sl(h["alpha"]), sl(h["b"]), sl(h["w"]), st(h["S0"]),
+                          sl(dOn), st(dSn))
+        for n in NAMES:
+            out[n].append(r[n][0, :, 0] if n != "dS0" else r[n][0, 0])
+    return {n: np.stack(v) for n, v in out.items()}
+
+
+def check(what, got, want, tol):
+    errs = {n: rel_l2(got[n], want[n]) for n in NAMES}
+    print(f"[parity] {what}: " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()) + f" (tol {tol:g})", flush=True)
+    bad = {n: e for n, e in errs.items() if not e <= tol}
+    assert not bad, f"{what}: {bad}"
+
+
+CASES = [
+    # B, T, H, dk, dv, io, gate dtype, S0 std, dS_T, b_scale
+    (1, 64, 1, 16, 16, F32, F32, None, False, 1.0),
+    (2, 100, 2, 64, 32, F32, F32, 0.05, True, 1.0),
+    (2, 65, 3, 64, 64, F32, F32, 0.05, True, 2.0),
+    (1, 130, 2, 128, 128, BF16, F32, 0.05, True, 1.0),
+    (1, 47, 2, 32, 48, BF16, BF16, None, True, 1.0),
+    (1, 200, 1, 128, 256, BF16, F32, 0.05, False, 2.0),
+    (1, 1, 2, 128, 128, BF16, F32, 0.05, True, 1.0),
+]
+
+
+def _id(c):
+    B, T, H, dk, dv, io, gt, s0, ds, bs = c
+    n = lambda d: "bf16" if d == BF16 else "f32"
+    return f"B{B}T{T}H{H}dk{dk}dv{dv}io{n(io)}g{n(gt)}{'S0' if s0 else ''}{'dS' if ds else ''}b{bs:g}"
+
+
+@pytest.mark.parametrize("case", CASES, ids=_id)
+def test_backward_small(dev, case):
+    B, T, H, dk, dv, io, gt, s0, ds, bs = case
+    inp, dO, dS_T, got = run(dev, B, T, H, dk, dv, io, gt, s0, ds, seed=T + dk + dv, b_scale=bs)
+    want = ref(inp, dO, dS_T)
+    gn = {n: _np(got[n]) for n in NAMES}
+    if inp["S0"] is None:                       # dS0 is still returned: the zero state's gradient
+        pass
+    check(_id(case), gn, want, TOL[io])
+
+
+def test_backward_full_size_sampled(dev):
+    """B4 H16 T2048 d128 bf16 (the chunked workload), sampled (batch, head) chains."""
+    B, T, H, dk, dv = 4, 2048, 16, 128, 128
+    inp, dO, dS_T, got = run(dev, B, T, H, dk, dv, BF16, F32, None, True, seed=77)
+    chains = [(0, 0), (3, 15)]
+    want = ref(inp, dO, dS_T, chains)
+    gn = {n: _np(got[n]) for n in NAMES}
+    gs = {n: np.stack([gn[n][bi, :, hi] if n != "dS0" else gn[n][bi, hi] for bi, hi in chains]) for n in NAMES}
+    check("B4H16T2048 sampled", gs, want, 2e-2)
+
+
+def test_backward_deterministic(dev):
+    inp, dO, dS_T, g1 = run(dev, 1, 150, 2, 64, 64, BF16, F32, 0.05, True, seed=5)
+    g2 = g.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["b"], inp["w"], dO, inp["S0"], dS_T)
+    torch.cuda.synchronize()
+    for n in NAMES:
+        assert torch.equal(g1[n], g2[n]), n
