@@ -78,7 +78,7 @@ def parse_args(argv=None):
     ap.add_argument("--pmc-summary", metavar="DIR", default=None)
     ap.add_argument("--copy-pmc", metavar="DIR", default=None)
     ap.add_argument("--util-summary", metavar="DIRS", default=None)
-    ap.add_argument("--no-prologue", action="store_true", help="skip the side legs (in-kernel prologue, grouped heads, packed batch, output step)")
+    ap.add_argument("--no-prologue", action="store_true", help="skip the side legs (in-kernel prologue, grouped heads, packed batch, backward, output step)")
     return ap.parse_args(argv)
 
 
@@ -344,6 +344,7 @@ def main(argv=None):
         result["chunk_fwd_prologue"] = prologue_leg(g, inputs, wl_c, dev, args)
         result["chunk_fwd_grouped"] = grouped_leg(g, inputs, wl_c, dev, args)
         result["chunk_fwd_varlen"] = varlen_leg(g, inputs, wl_c, dev, args)
+        result["chunk_bwd"] = backward_leg(g, inputs, wl_c, dev, args)
         result["epilogue"] = epilogue_leg(g, outs, dev, args)
 
     ok = bool(torch.isfinite(outs[0].float()).all() and torch.isfinite(states[0]).all()
@@ -479,6 +480,50 @@ def varlen_leg(g, inputs, wl, dev, args):
             "median_us": round(t[len(t) // 2] * 1e3, 2), "min_us": round(t[0] * 1e3, 2),
             "alg_GBps": round(gbps, 1), "frac_hbm_roofline": round(gbps / PEAK_HBM_GBPS, 4),
             "outputs_finite": bool(torch.isfinite(outs[0].float()).all() and torch.isfinite(st).all())}
+
+
+def grad_flops_per_chunk(dk, dv, C=64):
+    """Useful flops of one chunk's gradient step (k_chunk_grad): the decayed key products
+    A, P and their four transposed uses (per 16-column block), U, W, Delta, dDelta, dQh, dP,
+    dKtil, dW, du, dT, dEh and the two products of dA."""
+    blocks = sum(C - 16 * j for j in range(C // 16)) * 16          # rows x columns over the blocks
+    decayed = 6 * blocks * dk * 2
+    dense = 2 * (C * dv * C + C * dk * C + C * dv * dk + C * dv * (C + dk) + C * dk * dv + C * C * dv
+                 + C * dk * dv + C * dk * dv + C * dv * C + C * C * (dv + dk) + C * dk * C + 2 * C * C * C)
+    return decayed + dense
+
+
+def backward_leg(g, inputs, wl, dev, args):
+    """Backward of the chunked workload (B4 H16 T2048 d128, bf16 q/k/v, fp32 gates, zero
+    initial state, gradients of o and of the final state): the whole call, which recomputes
+    the forward (prep + state pass with checkpoints) before the reverse state pass and the
+    per-chunk gradients."""
+    import torch
+    B, T, H, dk, dv = wl.B, wl.T, wl.H, wl.dk, wl.dv
+    sets = [inputs.make_raw(B, T, H, dk, dv, wl.io_dtype, 900 + i, dev) for i in range(2)]
+    grads = [inputs.make_out_grads(B, T, H, dk, dv, wl.io_dtype, 950 + i, dev) for i in range(2)]
+    ws = g.alloc_workspace(g.chunk_bwd_workspace_size(B, T, H, dk, dv, wl.io_dtype), dev)
+    steps = max(args.steps // 5, 3)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    out = None
+    for i in range(args.warmup + steps):
+        x, (dO, dS) = sets[i % 2], grads[i % 2]
+        ev = evs[i - args.warmup] if i >= args.warmup else None
+        if ev:
+            ev[0].record()
+        out = g.chunk_bwd(x["q"], x["k"], x["v"], x["alpha"], x["b"], x["w"], dO, None, dS, workspace=ws)
+        if ev:
+            ev[1].record()
+    torch.cuda.synchronize()
+    t = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    ms = sum(t) / steps
+    nchunks = B * H * ((T + 63) // 64)
+    flops = grad_flops_per_chunk(dk, dv) * nchunks
+    return {"workload": f"chunked backward B{B} H{H} T{T} d{dk}, bf16 q/k/v/dO, fp32 gates, dS_T given",
+            "tokens_per_s": round(B * T / (ms * 1e-3), 1), "us": round(ms * 1e3, 2),
+            "median_us": round(t[len(t) // 2] * 1e3, 2), "min_us": round(t[0] * 1e3, 2),
+            "grad_kernel_useful_GFLOP": round(flops / 1e9, 2),
+            "outputs_finite": bool(all(torch.isfinite(v.float()).all() for v in out.values() if v is not None))}
 
 
 def epilogue_leg(g, outs, dev, args):

@@ -481,7 +481,7 @@ int gdn2_chunk_bwd(const gdn2_problem* p, const void* q, const void* k, const vo
         st = launch_status(gdn2::launch_chunk_state(fa, (int)p->dk, vs, is_bf16(p), s));
         if (st) return st;
     }
-    const int bvs = p->dv <= 64 ? (int)p->dv : (p->dv % 64 == 0 ? 64 : (p->dv % 32 == 0 ? 32 : 16));
+    const int bvs = gdn2::state_bwd_slice((int)p->dv);
     gdn2::BwdStateArgs ba{ws, ws_block_bytes(p), dO, dS_T, dsl, dS0, p->B, p->T, p->H, (int)p->dk, (int)p->dv,
                           (int)nchunks(p), (int)(p->dv / bvs), bvs};
     st = launch_status(gdn2::launch_chunk_state_bwd(ba, is_bf16(p), s));

@@ -46,25 +46,37 @@ namespace gdn2 {
 
 // ---------------------------------------------------------------------------
 // C[M][N] = sum_k A(m, k) B(k, n) on the 256 threads of a workgroup.
-// M, N multiples of 4 with M <= 128, N <= 256, M * N <= 16384; any K.
-// fa(m, k) and fb(k, n) return operand elements (fp32); fe(m, n, v) consumes
-// each result.  Ends with a barrier, so the next product may read what fe
+// M <= 64 and N multiples of 4, any K.  fa(m, k) and fb(k, n) return operand
+// elements (fp32); fe(m, n, v) consumes each result.  AK: A's memory is
+// contiguous along k (else along m); BN: B's memory is contiguous along n
+// (else along k) -- consecutive threads then load consecutive addresses.
+// The columns are taken 128 at a time; each thread owns two 4x4 output
+// tiles.  K-slices of both operands are staged in LDS (rows padded against
+// bank conflicts), the next slice loaded into registers while the current
+// one is used.  Ends with a barrier, so the next product may read what fe
 // wrote.
 // ---------------------------------------------------------------------------
 constexpr int kGK = 16;
 struct __attribute__((aligned(16))) GemmLds {
-    float a[kGK][128];
-    float b[kGK][256];
+    float a[kGK][64 + 4];
+    float b[kGK][128 + 4];
 };
 
-template <typename FA, typename FB, typename FE>
-__device__ void gemm(GemmLds& sm, int M, int N, int K, FA fa, FB fb, FE fe)
+template <bool AK, bool BN, typename FA, typename FB, typename FE>
+__device__ __attribute__((always_inline)) inline void gemm(GemmLds& sm, int M, int N, int K, FA fa, FB fb, FE fe)
 {
     const int tid = threadIdx.x;
-    const int tnc = N / 4, nsl = (M / 4) * tnc;
-    // passes of up to 512 4x4 tiles (two per thread); larger products
-    // stage their operands once per pass
-    for (int p0 = 0; p0 < nsl; p0 += 2 * kThreads) {
+    for (int nb = 0; nb < N; nb += 128) {
+        const int NB = N - nb < 128 ? N - nb : 128;
+        const int tnc = NB / 4, nsl = (M / 4) * tnc;      // <= 512 tiles
+        // staging element u of this thread: A (m, kk), B (kk, n)
+        auto a_of = [&](int i, int& m, int& kk) {
+            if (AK) { m = i / kGK; kk = i % kGK; } else { kk = i / M; m = i - kk * M; }
+        };
+        auto b_of = [&](int i, int& kk, int& n) {
+            if (BN) { kk = i / NB; n = i - kk * NB; } else { n = i / kGK; kk = i % kGK; }
+        };
+        float ra[4], rb[8];
         float acc[2][4][4];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -72,43 +84,70 @@ __device__ void gemm(GemmLds& sm, int M, int N, int K, FA fa, FB fb, FE fe)
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[t][i][j] = 0.f;
-        for (int k0 = 0; k0 < K; k0 += kGK) {
-            for (int i = tid; i < M * kGK; i += kThreads) {
-                const int m = i / kGK, kk = i - m * kGK;
-                sm.a[kk][m] = k0 + kk < K ? fa(m, k0 + kk) : 0.f;
+        for (int k0 = -kGK; k0 < K; k0 += kGK) {
+            if (k0 >= 0) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int i = tid + u * kThreads;
+                    int m, kk;
+                    a_of(i, m, kk);
+                    if (i < M * kGK) sm.a[kk][m] = ra[u];
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int i = tid + u * kThreads;
+                    int kk, n;
+                    b_of(i, kk, n);
+                    if (i < kGK * NB) sm.b[kk][n] = rb[u];
+                }
+                __syncthreads();
             }
-            for (int i = tid; i < kGK * N; i += kThreads) {
-                const int kk = i / N, n = i - kk * N;
-                sm.b[kk][n] = k0 + kk < K ? fb(k0 + kk, n) : 0.f;
-            }
-            __syncthreads();
+            const int kn = k0 + kGK;                      // slice to fetch now
+            if (kn < K) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int slot = p0 + tid + t * kThreads;
-                if (slot < nsl) {
-                    const int m0 = 4 * (slot / tnc), n0 = 4 * (slot - (slot / tnc) * tnc);
-#pragma unroll 4
-                    for (int kk = 0; kk < kGK; ++kk) {
-                        const f32x4 av = *reinterpret_cast<const f32x4*>(&sm.a[kk][m0]);
-                        const f32x4 bv = *reinterpret_cast<const f32x4*>(&sm.b[kk][n0]);
+                for (int u = 0; u < 4; ++u) {
+                    const int i = tid + u * kThreads;
+                    int m, kk;
+                    a_of(i, m, kk);
+                    ra[u] = (i < M * kGK && kn + kk < K) ? fa(m, kn + kk) : 0.f;
+                }
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) acc[t][i][j] += av[i] * bv[j];
-                    }
+                for (int u = 0; u < 8; ++u) {
+                    const int i = tid + u * kThreads;
+                    int kk, n;
+                    b_of(i, kk, n);
+                    rb[u] = (i < kGK * NB && kn + kk < K) ? fb(kn + kk, nb + n) : 0.f;
                 }
             }
-            __syncthreads();
+            if (k0 >= 0) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int slot = tid + t * kThreads;
+                    if (slot < nsl) {
+                        const int m0 = 4 * (slot / tnc), n0 = 4 * (slot - (slot / tnc) * tnc);
+#pragma unroll 4
+                        for (int kk = 0; kk < kGK; ++kk) {
+                            const f32x4 av = *reinterpret_cast<const f32x4*>(&sm.a[kk][m0]);
+                            const f32x4 bv = *reinterpret_cast<const f32x4*>(&sm.b[kk][n0]);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                                for (int j = 0; j < 4; ++j) acc[t][i][j] += av[i] * bv[j];
+                        }
+                    }
+                }
+                __syncthreads();
+            }
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const int slot = p0 + tid + t * kThreads;
+            const int slot = tid + t * kThreads;
             if (slot < nsl) {
                 const int m0 = 4 * (slot / tnc), n0 = 4 * (slot - (slot / tnc) * tnc);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) fe(m0 + i, n0 + j, acc[t][i][j]);
+                    for (int j = 0; j < 4; ++j) fe(m0 + i, nb + n0 + j, acc[t][i][j]);
             }
         }
     }
@@ -120,61 +159,177 @@ template <typename T> __device__ inline void stf(T* p, int64_t i, float x) { p[i
 
 // ---------------------------------------------------------------------------
 // launch 3: reverse pass over chunks
+//
+// One workgroup per (batch, head, slice of VS value columns).  The chunk's
+// factors are copied byte for byte from the front of its workspace block
+// (Qh, W, Ktil^T, P, Gamma_L: everything before U^T) into an LDS image,
+// with the chunk's dO columns behind it; the copy of chunk n-1 is loaded
+// into registers (16-byte granules) while chunk n is computed.  The state
+// gradient dS [DK][VS] and dDelta [64][VS] stay in LDS in fp32; each thread
+// accumulates a small output tile with fp32 FMAs.
 // ---------------------------------------------------------------------------
-template <typename Tio>
-__global__ __launch_bounds__(kThreads) void k_chunk_state_bwd(BwdStateArgs a)
+template <typename Tio, int DK>
+struct BwdStateLds {
+    static constexpr int ES = (int)sizeof(Tio), KB = Io<Tio>::KB;
+    static constexpr WsLayout LY = ws_layout(DK, 0, sizeof(Tio), KB);
+    static constexpr int IMG = (int)LY.uwyt;                 // bytes of the factor image
+};
+
+template <typename Tio, int DK, int VS>
+__global__ __launch_bounds__(kThreads, 1) void k_chunk_state_bwd(BwdStateArgs a)
 {
-    __shared__ GemmLds gl;
-    __shared__ float dS[128 * 64];     // [dk][vs]
-    __shared__ float dD[64 * 64];      // [64][vs]
+    using SL = BwdStateLds<Tio, DK>;
+    constexpr int ES = SL::ES, IMG = SL::IMG;
+    constexpr int KPAD = round_up(DK, SL::KB);
+    constexpr int GROW = VS * ES / 16;                     // granules of one dO row slice
+    constexpr int NG = IMG / 16 + 64 * GROW;                // granules per chunk
+    constexpr int NPT = (NG + kThreads - 1) / kThreads;
+    constexpr int TR = VS / 16;                             // dDelta rows per thread (x 4 columns)
+    constexpr int TC = DK * VS / 1024 > 0 ? DK * VS / 1024 : 1;   // dS rows per thread (x 4 columns)
+    constexpr int NCG = VS / 4;                             // column groups
+    static_assert(IMG % 16 == 0 && TR >= 1, "layout");
+
+    __shared__ __attribute__((aligned(16))) char img[IMG + 64 * VS * ES];
+    __shared__ __attribute__((aligned(16))) float dS[DK * VS];
+    __shared__ __attribute__((aligned(16))) float dD[64 * VS];
+    const Tio* P = reinterpret_cast<const Tio*>(img + SL::LY.p);       // [64][64]
+    const Tio* Kt = reinterpret_cast<const Tio*>(img + SL::LY.ktt);    // [DK][64]
+    const Tio* Qh = reinterpret_cast<const Tio*>(img + SL::LY.qh);     // [64][KPAD]
+    const Tio* Wf = reinterpret_cast<const Tio*>(img + SL::LY.wwy);    // [64][KPAD]
+    const float* gam = reinterpret_cast<const float*>(img + SL::LY.gaml);
+    const Tio* dOs = reinterpret_cast<const Tio*>(img + IMG);          // [64][VS]
+
     const int tid = threadIdx.x;
-    const int dk = a.dk, dv = a.dv, vs = a.vs, nt = a.nt;
-    const int64_t chain = blockIdx.x / a.nslices;
-    const int j0 = (int)(blockIdx.x - chain * a.nslices) * vs;
+    const int dv = a.dv, nt = a.nt;
+    // the slices of one head get block ids congruent mod 8 (one XCD, one L2
+    // for the head's factors)
+    const int64_t nch = a.B * a.H, x = blockIdx.x;
+    const int ns = a.nslices;
+    int64_t chain;
+    int slice;
+    if ((nch & 7) == 0) {
+        chain = (x / (8 * ns)) * 8 + (x & 7);
+        slice = (int)((x >> 3) % ns);
+    } else {
+        chain = x / ns;
+        slice = (int)(x - chain * ns);
+    }
+    const int j0 = slice * VS;
     const int64_t bb = chain / a.H, hh = chain - bb * a.H;
-    const int kb = sizeof(Tio) == 2 ? 32 : 16;
-    const WsLayout LY = ws_layout(dk, dv, sizeof(Tio), kb);
-    const int kpad = (dk + kb - 1) / kb * kb;
     const Tio* dO = static_cast<const Tio*>(a.dO);
 
-    for (int i = tid; i < dk * vs; i += kThreads) {
-        const int c = i / vs, j = i - c * vs;
-        dS[i] = a.dS_T ? a.dS_T[(chain * dk + c) * dv + j0 + j] : 0.f;
-    }
-    __syncthreads();
-    for (int n = nt - 1; n >= 0; --n) {
+    f32x4 pre[NPT];
+    auto fetch = [&](int n) {
         const char* blk = static_cast<const char*>(a.ws) + (chain * nt + n) * a.ws_block;
-        const Tio* Qh = reinterpret_cast<const Tio*>(blk + LY.qh);
-        const Tio* Wf = reinterpret_cast<const Tio*>(blk + LY.wwy);
-        const Tio* Ktt = reinterpret_cast<const Tio*>(blk + LY.ktt);
-        const Tio* Pf = reinterpret_cast<const Tio*>(blk + LY.p);
-        const float* gam = reinterpret_cast<const float*>(blk + LY.gaml);
         const int64_t t0 = (int64_t)n * kChunk;
         const int L = (int)(a.T - t0 < kChunk ? a.T - t0 : kChunk);
-        auto dOf = [&](int r, int j) -> float {
-            return r < L ? ldf(dO, ((bb * a.T + t0 + r) * a.H + hh) * dv + j0 + j) : 0.f;
-        };
-        // the gradient this chunk's exit state receives
-        float* dsl = a.dSL + (chain * nt + n) * (int64_t)dk * dv + j0;
-        for (int i = tid; i < dk * vs; i += kThreads) {
-            const int c = i / vs, j = i - c * vs;
-            dsl[(int64_t)c * dv + j] = dS[i];
+#pragma unroll
+        for (int i = 0; i < NPT; ++i) {
+            const int gi = tid + i * kThreads;
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+            if (gi < IMG / 16) {
+                x = *reinterpret_cast<const f32x4*>(blk + 16 * gi);
+            } else if (gi < NG) {
+                const int r = (gi - IMG / 16) / GROW, g = (gi - IMG / 16) % GROW;
+                if (r < L)
+                    x = *reinterpret_cast<const f32x4*>(
+                        dO + ((bb * a.T + t0 + r) * a.H + hh) * dv + j0 + g * (16 / ES));
+            }
+            pre[i] = x;
         }
-        // dDelta = P^T dO + Ktil dS
-        gemm(gl, 64, vs, 64 + dk,
-             [&](int m, int k) { return k < 64 ? ldf(Pf, k * 64 + m) : ldf(Ktt, (k - 64) * 64 + m); },
-             [&](int k, int j) { return k < 64 ? dOf(k, j) : dS[(k - 64) * vs + j]; },
-             [&](int m, int j, float v) { dD[m * vs + j] = v; });
-        // dS = Qh^T dO - W^T dDelta + Gamma_L dS
-        gemm(gl, dk, vs, 128,
-             [&](int m, int k) { return k < 64 ? ldf(Qh, k * kpad + m) : -ldf(Wf, (k - 64) * kpad + m); },
-             [&](int k, int j) { return k < 64 ? dOf(k, j) : dD[(k - 64) * vs + j]; },
-             [&](int m, int j, float v) { dS[m * vs + j] = v + gam[m] * dS[m * vs + j]; });
+    };
+    auto stash = [&]() {
+#pragma unroll
+        for (int i = 0; i < NPT; ++i) {
+            const int gi = tid + i * kThreads;
+            if (gi < NG) *reinterpret_cast<f32x4*>(img + 16 * gi) = pre[i];
+        }
+    };
+
+    for (int i = tid; i < DK * VS; i += kThreads) {
+        const int c = i / VS, j = i - c * VS;
+        dS[i] = a.dS_T ? a.dS_T[(chain * DK + c) * dv + j0 + j] : 0.f;
     }
+    if (nt > 0) fetch(nt - 1);
+    for (int n = nt - 1; n >= 0; --n) {
+        __syncthreads();                                   // the previous chunk is done with LDS
+        stash();
+        // the gradient this chunk's exit state receives
+        float* dsl = a.dSL + (chain * nt + n) * (int64_t)DK * dv + j0;
+        for (int i = tid; i < DK * VS / 4; i += kThreads) {
+            const int c = i / NCG, g = i - c * NCG;
+            *reinterpret_cast<f32x4*>(dsl + (int64_t)c * dv + 4 * g) = *reinterpret_cast<const f32x4*>(&dS[c * VS + 4 * g]);
+        }
+        if (n > 0) fetch(n - 1);
+        __syncthreads();
+        // dDelta = P^T dO + Ktil dS: rows r0 .. r0+TR-1, columns 4cg .. 4cg+3
+        {
+            const int cg = tid % NCG, r0 = (tid / NCG) * TR;
+            float acc[TR][4];
+#pragma unroll
+            for (int i = 0; i < TR; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+#pragma unroll 8
+            for (int s = 0; s < 64; ++s) {
+                const f32x4 o = ld_vec4(dOs + s * VS + 4 * cg);
+#pragma unroll
+                for (int i = 0; i < TR; ++i) {
+                    const float p = Io<Tio>::to_f(P[s * 64 + r0 + i]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[i][j] += p * o[j];
+                }
+            }
+#pragma unroll 8
+            for (int c = 0; c < DK; ++c) {
+                const f32x4 d = *reinterpret_cast<const f32x4*>(&dS[c * VS + 4 * cg]);
+#pragma unroll
+                for (int i = 0; i < TR; ++i) {
+                    const float k = Io<Tio>::to_f(Kt[c * 64 + r0 + i]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[i][j] += k * d[j];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < TR; ++i)
+                *reinterpret_cast<f32x4*>(&dD[(r0 + i) * VS + 4 * cg]) = f32x4{acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
+        }
+        __syncthreads();
+        // dS = Gamma_L dS + Qh^T dO - W^T dDelta: rows c0 .. c0+TC-1, columns 4cg ..
+        if (tid < DK / TC * NCG) {
+            const int cg = tid % NCG, c0 = (tid / NCG) * TC;
+            float acc[TC][4];
+#pragma unroll
+            for (int i = 0; i < TC; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+#pragma unroll 8
+            for (int r = 0; r < 64; ++r) {
+                const f32x4 o = ld_vec4(dOs + r * VS + 4 * cg);
+                const f32x4 d = *reinterpret_cast<const f32x4*>(&dD[r * VS + 4 * cg]);
+#pragma unroll
+                for (int i = 0; i < TC; ++i) {
+                    const float qv = Io<Tio>::to_f(Qh[r * KPAD + c0 + i]);
+                    const float wv = Io<Tio>::to_f(Wf[r * KPAD + c0 + i]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[i][j] += qv * o[j] - wv * d[j];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < TC; ++i) {
+                f32x4 x = *reinterpret_cast<const f32x4*>(&dS[(c0 + i) * VS + 4 * cg]);
+                const float gm = gam[c0 + i];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) x[j] = gm * x[j] + acc[i][j];
+                *reinterpret_cast<f32x4*>(&dS[(c0 + i) * VS + 4 * cg]) = x;
+            }
+        }
+    }
+    __syncthreads();
     if (a.dS0 != nullptr) {
-        for (int i = tid; i < dk * vs; i += kThreads) {
-            const int c = i / vs, j = i - c * vs;
-            a.dS0[(chain * dk + c) * dv + j0 + j] = dS[i];
+        for (int i = tid; i < DK * VS; i += kThreads) {
+            const int c = i / VS, j = i - c * VS;
+            a.dS0[(chain * DK + c) * dv + j0 + j] = dS[i];
         }
     }
 }
@@ -269,11 +424,11 @@ __global__ __launch_bounds__(kThreads) void k_chunk_grad(GradArgs a)
         // ---- A (s < r) and P (s <= r), one 16-column block at a time
         for (int J = 0; J < 4; ++J) {
             const int j0 = 16 * J;
-            gemm(gl, 64 - j0, 16, dk,
+            gemm<true, false>(gl, 64 - j0, 16, dk,
                  [&](int m, int c) { return ef[(j0 + m) * dk + c] * __expf(G[(j0 + m) * dk + c] - G[j0 * dk + c]); },
                  [&](int c, int s) { return KY[(j0 + s) * dk + c]; },
                  [&](int m, int s, float x) { if (s < m) A[(j0 + m) * 64 + j0 + s] = x; });
-            gemm(gl, 64 - j0, 16, dk,
+            gemm<true, false>(gl, 64 - j0, 16, dk,
                  [&](int m, int c) { return qf[(j0 + m) * dk + c] * __expf(G[(j0 + m) * dk + c] - G[j0 * dk + c]); },
                  [&](int c, int s) { return KY[(j0 + s) * dk + c]; },
                  [&](int m, int s, float x) { if (s <= m) P[(j0 + m) * 64 + j0 + s] = x; });
@@ -318,28 +473,29 @@ __global__ __launch_bounds__(kThreads) void k_chunk_grad(GradArgs a)
         }
 
         // ---- U = T u, W = T Eh
-        gemm(gl, 64, dv, 64, [&](int m, int s) { return Tm[m * 64 + s]; }, [&](int s, int j) { return u[s * dv + j]; },
+        gemm<true, true>(gl, 64, dv, 64, [&](int m, int s) { return Tm[m * 64 + s]; }, [&](int s, int j) { return u[s * dv + j]; },
              [&](int m, int j, float x) { U[m * dv + j] = x; });
-        gemm(gl, 64, dk, 64, [&](int m, int s) { return Tm[m * 64 + s]; }, [&](int s, int c) { return Eh[s * dk + c]; },
+        gemm<true, true>(gl, 64, dk, 64, [&](int m, int s) { return Tm[m * 64 + s]; }, [&](int s, int c) { return Eh[s * dk + c]; },
              [&](int m, int c, float x) { W[m * dk + c] = x; });
         // ---- Delta = U - W S0;  dDelta = P^T dO + Ktil dSL
-        gemm(gl, 64, dv, dk, [&](int m, int c) { return W[m * dk + c]; },
+        gemm<true, true>(gl, 64, dv, dk, [&](int m, int c) { return W[m * dk + c]; },
              [&](int c, int j) { return S0[(int64_t)c * dv + j]; },
              [&](int m, int j, float x) { Dl[m * dv + j] = U[m * dv + j] - x; });
-        gemm(gl, 64, dv, 64 + dk,
-             [&](int m, int kk) { return kk < 64 ? P[kk * 64 + m] : Kt[m * dk + kk - 64]; },
-             [&](int kk, int j) { return kk < 64 ? dOf[kk * dv + j] : dSL[(int64_t)(kk - 64) * dv + j]; },
-             [&](int m, int j, float x) { dDl[m * dv + j] = x; });
+        gemm<false, true>(gl, 64, dv, 64, [&](int m, int s) { return P[s * 64 + m]; },
+                          [&](int s, int j) { return dOf[s * dv + j]; }, [&](int m, int j, float x) { dDl[m * dv + j] = x; });
+        gemm<true, true>(gl, 64, dv, dk, [&](int m, int c) { return Kt[m * dk + c]; },
+                         [&](int c, int j) { return dSL[(int64_t)c * dv + j]; },
+                         [&](int m, int j, float x) { dDl[m * dv + j] += x; });
         // ---- dQh, dP, dKtil, dW, du (-> dw, dv), dGamma_L
-        gemm(gl, 64, dk, dv, [&](int m, int j) { return dOf[m * dv + j]; },
+        gemm<true, false>(gl, 64, dk, dv, [&](int m, int j) { return dOf[m * dv + j]; },
              [&](int j, int c) { return S0[(int64_t)c * dv + j]; }, [&](int m, int c, float x) { dQh[m * dk + c] = x; });
-        gemm(gl, 64, 64, dv, [&](int m, int j) { return dOf[m * dv + j]; }, [&](int j, int s) { return Dl[s * dv + j]; },
+        gemm<true, false>(gl, 64, 64, dv, [&](int m, int j) { return dOf[m * dv + j]; }, [&](int j, int s) { return Dl[s * dv + j]; },
              [&](int m, int s, float x) { dP[m * 64 + s] = s <= m ? x : 0.f; });
-        gemm(gl, 64, dk, dv, [&](int m, int j) { return Dl[m * dv + j]; },
+        gemm<true, false>(gl, 64, dk, dv, [&](int m, int j) { return Dl[m * dv + j]; },
              [&](int j, int c) { return dSL[(int64_t)c * dv + j]; }, [&](int m, int c, float x) { dKt[m * dk + c] = x; });
-        gemm(gl, 64, dk, dv, [&](int m, int j) { return dDl[m * dv + j]; },
+        gemm<true, false>(gl, 64, dk, dv, [&](int m, int j) { return dDl[m * dv + j]; },
              [&](int j, int c) { return S0[(int64_t)c * dv + j]; }, [&](int m, int c, float x) { dW[m * dk + c] = -x; });
-        gemm(gl, 64, dv, 64, [&](int m, int s) { return Tm[s * 64 + m]; }, [&](int s, int j) { return dDl[s * dv + j]; },
+        gemm<false, true>(gl, 64, dv, 64, [&](int m, int s) { return Tm[s * 64 + m]; }, [&](int s, int j) { return dDl[s * dv + j]; },
              [&](int r, int j, float x) {
                  if (r < L) {
                      const int64_t o = (row0 + r * H) * dv + j;
@@ -353,34 +509,34 @@ __global__ __launch_bounds__(kThreads) void k_chunk_grad(GradArgs a)
             dGamL[c] = x;
         }
         // ---- dT = dDelta u^T + dW Eh^T, dEh = T^T dW, dA = mask(-T^T dT T^T)
-        gemm(gl, 64, 64, dv + dk,
+        gemm<true, false>(gl, 64, 64, dv + dk,
              [&](int m, int kk) { return kk < dv ? dDl[m * dv + kk] : dW[m * dk + kk - dv]; },
              [&](int kk, int s) { return kk < dv ? u[s * dv + kk] : Eh[s * dk + kk - dv]; },
              [&](int m, int s, float x) { dT[m * 64 + s] = x; });
-        gemm(gl, 64, dk, 64, [&](int m, int s) { return Tm[s * 64 + m]; }, [&](int s, int c) { return dW[s * dk + c]; },
+        gemm<false, true>(gl, 64, dk, 64, [&](int m, int s) { return Tm[s * 64 + m]; }, [&](int s, int c) { return dW[s * dk + c]; },
              [&](int m, int c, float x) { dEh[m * dk + c] = x; });
-        gemm(gl, 64, 64, 64, [&](int m, int s) { return Tm[s * 64 + m]; }, [&](int s, int j) { return dT[s * 64 + j]; },
+        gemm<false, true>(gl, 64, 64, 64, [&](int m, int s) { return Tm[s * 64 + m]; }, [&](int s, int j) { return dT[s * 64 + j]; },
              [&](int m, int j, float x) { tmp[m * 64 + j] = x; });
-        gemm(gl, 64, 64, 64, [&](int m, int j) { return tmp[m * 64 + j]; }, [&](int j, int s) { return Tm[s * 64 + j]; },
+        gemm<true, false>(gl, 64, 64, 64, [&](int m, int j) { return tmp[m * 64 + j]; }, [&](int j, int s) { return Tm[s * 64 + j]; },
              [&](int m, int s, float x) { dA[m * 64 + s] = s < m ? -x : 0.f; });
 
         // ---- through A and P: row side (rows r >= j0 of column block J) and
         // column side (columns s of block J)
         for (int J = 0; J < 4; ++J) {
             const int j0 = 16 * J;
-            gemm(gl, 64 - j0, dk, 16, [&](int m, int s) { return dA[(j0 + m) * 64 + j0 + s]; },
+            gemm<true, true>(gl, 64 - j0, dk, 16, [&](int m, int s) { return dA[(j0 + m) * 64 + j0 + s]; },
                  [&](int s, int c) { return KY[(j0 + s) * dk + c]; },
                  [&](int m, int c, float x) {
                      const int r = j0 + m;
                      deA[r * dk + c] += x * __expf(G[r * dk + c] - G[j0 * dk + c]);
                  });
-            gemm(gl, 64 - j0, dk, 16, [&](int m, int s) { return dP[(j0 + m) * 64 + j0 + s]; },
+            gemm<true, true>(gl, 64 - j0, dk, 16, [&](int m, int s) { return dP[(j0 + m) * 64 + j0 + s]; },
                  [&](int s, int c) { return KY[(j0 + s) * dk + c]; },
                  [&](int m, int c, float x) {
                      const int r = j0 + m;
                      dqP[r * dk + c] += x * __expf(G[r * dk + c] - G[j0 * dk + c]);
                  });
-            gemm(gl, 16, dk, 64 - j0, [&](int m, int rr) { return dA[(j0 + rr) * 64 + j0 + m]; },
+            gemm<false, true>(gl, 16, dk, 64 - j0, [&](int m, int rr) { return dA[(j0 + rr) * 64 + j0 + m]; },
                  [&](int rr, int c) {
                      const int r = j0 + rr;
                      return ef[r * dk + c] * __expf(G[r * dk + c] - G[j0 * dk + c]);
@@ -389,7 +545,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_grad(GradArgs a)
                      const int s = j0 + m;
                      dkA[s * dk + c] += x * __expf(G[j0 * dk + c] - G[s * dk + c]);
                  });
-            gemm(gl, 16, dk, 64 - j0, [&](int m, int rr) { return dP[(j0 + rr) * 64 + j0 + m]; },
+            gemm<false, true>(gl, 16, dk, 64 - j0, [&](int m, int rr) { return dP[(j0 + rr) * 64 + j0 + m]; },
                  [&](int rr, int c) {
                      const int r = j0 + rr;
                      return qf[r * dk + c] * __expf(G[r * dk + c] - G[j0 * dk + c]);
@@ -440,21 +596,48 @@ __global__ __launch_bounds__(kThreads) void k_chunk_grad(GradArgs a)
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-int64_t grad_blocks(int64_t total) { return total < 1024 ? total : 1024; }
+#ifndef GDN2_GRAD_BLOCKS
+#define GDN2_GRAD_BLOCKS 1024
+#endif
+int64_t grad_blocks(int64_t total) { return total < GDN2_GRAD_BLOCKS ? total : GDN2_GRAD_BLOCKS; }
 
 int64_t chunk_grad_scratch_bytes(int dk, int dv, int64_t total)
 {
     return grad_blocks(total) * grad_scratch_floats(dk, dv) * 4;
 }
 
+template <typename Tio, int DK>
+static hipError_t state_bwd_dk(const BwdStateArgs& a, hipStream_t s)
+{
+    const dim3 grid((unsigned)(a.B * a.H * (int64_t)a.nslices));
+    if (a.vs == 32)
+        hipLaunchKernelGGL((k_chunk_state_bwd<Tio, DK, 32>), grid, dim3(kThreads), 0, s, a);
+    else if (a.vs == 16)
+        hipLaunchKernelGGL((k_chunk_state_bwd<Tio, DK, 16>), grid, dim3(kThreads), 0, s, a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+template <typename Tio>
+static hipError_t state_bwd_t(const BwdStateArgs& a, hipStream_t s)
+{
+    switch (a.dk) {
+        case 16: return state_bwd_dk<Tio, 16>(a, s);
+        case 32: return state_bwd_dk<Tio, 32>(a, s);
+        case 64: return state_bwd_dk<Tio, 64>(a, s);
+        case 128: return state_bwd_dk<Tio, 128>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// value-slice width of the reverse state pass
+// (16 columns: twice the workgroups of 32 and half the serial work per chunk)
+int state_bwd_slice(int dv) { return dv % 16 == 0 ? 16 : 0; }
+
 hipError_t launch_chunk_state_bwd(const BwdStateArgs& a, bool bf16, hipStream_t s)
 {
-    const int64_t nblk = a.B * a.H * (int64_t)a.nslices;
-    if (bf16)
-        hipLaunchKernelGGL(k_chunk_state_bwd<__bf16>, dim3((unsigned)nblk), dim3(kThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL(k_chunk_state_bwd<float>, dim3((unsigned)nblk), dim3(kThreads), 0, s, a);
-    return hipGetLastError();
+    return bf16 ? state_bwd_t<__bf16>(a, s) : state_bwd_t<float>(a, s);
 }
 
 hipError_t launch_chunk_grad(const GradArgs& a, bool bf16, bool gbf16, hipStream_t s)

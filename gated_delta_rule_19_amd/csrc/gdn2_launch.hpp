@@ -86,6 +86,7 @@ hipError_t launch_recurrent(const RecArgs& a, int dk, int vs, bool bf16, bool gb
 hipError_t launch_gated_rmsnorm(const NormArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_varlen_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_chunk_state_bwd(const BwdStateArgs& a, bool bf16, hipStream_t s);
+int state_bwd_slice(int dv);
 hipError_t launch_chunk_grad(const GradArgs& a, bool bf16, bool gbf16, hipStream_t s);
 // workgroups of the gradient launch and the bytes of its scratch
 int64_t grad_blocks(int64_t total);
