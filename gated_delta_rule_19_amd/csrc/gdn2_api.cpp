@@ -183,20 +183,34 @@ int do_state(const gdn2_problem* p, const float* S0, void* o, float* S_out, cons
 }
 
 // backward workspace: forward factors | chunk entry states | chunk exit
-// state gradients | gradient scratch, each 256-byte aligned
+// state gradients | gradient scratch, each 256-byte aligned.  The matrix-core
+// path (bf16 I/O, dk 32/64/128, dv a multiple of 32 up to 128) also keeps T in
+// each factor block and transposed bf16 copies of both checkpoints.
 struct BwdLayout {
-    int64_t chk, dsl, scratch, total;
+    bool mf;
+    int64_t block, t_off;                 // factor block stride, offset of T in it
+    int64_t chk, chkT, dsl, dslT, scratch, total;
 };
 
 BwdLayout bwd_layout(const gdn2_problem* p)
 {
-    const int64_t states = p->B * p->H * nchunks(p) * p->dk * p->dv * 4;
-    const int64_t align = 255;
-    BwdLayout l;
-    l.chk = (ws_bytes(p) + align) & ~align;
-    l.dsl = (l.chk + states + align) & ~align;
-    l.scratch = (l.dsl + states + align) & ~align;
-    l.total = l.scratch + gdn2::chunk_grad_scratch_bytes((int)p->dk, (int)p->dv, p->B * p->H * nchunks(p));
+    const int64_t nblk = p->B * p->H * nchunks(p);
+    const int64_t states = nblk * p->dk * p->dv * 4;
+    auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
+    BwdLayout l{};
+    l.mf = gdn2::gradmf_supported((int)p->dk, (int)p->dv, is_bf16(p));
+    l.block = ws_block_bytes(p);
+    if (l.mf) {
+        l.t_off = l.block;
+        l.block = up(l.block + 64 * 64 * 2);
+    }
+    l.chk = up(nblk * l.block);
+    l.chkT = up(l.chk + states);
+    l.dsl = l.mf ? up(l.chkT + states / 2) : l.chkT;
+    l.dslT = up(l.dsl + states);
+    l.scratch = l.mf ? up(l.dslT + states / 2) : l.dslT;
+    l.total = l.scratch + (l.mf ? gdn2::gradmf_scratch_bytes((int)p->dk, nblk)
+                                : gdn2::chunk_grad_scratch_bytes((int)p->dk, (int)p->dv, nblk));
     return l;
 }
 
@@ -471,25 +485,37 @@ int gdn2_chunk_bwd(const gdn2_problem* p, const void* q, const void* k, const vo
     char* ws = static_cast<char*>(workspace);
     float* chk = reinterpret_cast<float*>(ws + l.chk);
     float* dsl = reinterpret_cast<float*>(ws + l.dsl);
+    void* chkT = l.mf ? ws + l.chkT : nullptr;
+    void* dslT = l.mf ? ws + l.dslT : nullptr;
     const int64_t nch = p->B * p->H;
+    const int64_t total = nch * nchunks(p);
     if (nchunks(p) > 0) {
-        st = do_prep(p, q, k, v, alpha, b, w, ws, s);
+        gdn2::PrepArgs pa{q, k, v, alpha, b, w, ws, l.block, p->B, p->T, p->H, p->H,
+                          (int)p->dv, (int)nchunks(p), (int)p->flags, nullptr, 0, l.t_off};
+        st = launch_status(gdn2::launch_chunk_prep(pa, (int)p->dk, is_bf16(p), gates_bf16(p), s));
         if (st) return st;
         const int vs = gdn2::chunk_state_slice(nch, (int)p->dv, (int)p->dk, (int)io_size(p));
-        gdn2::StateArgs fa{ws, ws_block_bytes(p), S0, nullptr, nullptr, p->B, p->T, p->H, (int)p->dv,
-                           (int)nchunks(p), (int)(p->dv / vs), nullptr, 0, chk};
+        gdn2::StateArgs fa{ws, l.block, S0, nullptr, nullptr, p->B, p->T, p->H, (int)p->dv,
+                           (int)nchunks(p), (int)(p->dv / vs), nullptr, 0, chk, chkT};
         st = launch_status(gdn2::launch_chunk_state(fa, (int)p->dk, vs, is_bf16(p), s));
         if (st) return st;
     }
     const int bvs = gdn2::state_bwd_slice((int)p->dv);
-    gdn2::BwdStateArgs ba{ws, ws_block_bytes(p), dO, dS_T, dsl, dS0, p->B, p->T, p->H, (int)p->dk, (int)p->dv,
-                          (int)nchunks(p), (int)(p->dv / bvs), bvs};
+    gdn2::BwdStateArgs ba{ws, l.block, dO, dS_T, dsl, dS0, p->B, p->T, p->H, (int)p->dk, (int)p->dv,
+                          (int)nchunks(p), (int)(p->dv / bvs), bvs, dslT};
     st = launch_status(gdn2::launch_chunk_state_bwd(ba, is_bf16(p), s));
     if (st) return st;
     if (nchunks(p) == 0) return GDN2_OK;
-    gdn2::GradArgs ga{q, k, v, alpha, b, w, dO, chk, dsl, dq, dk, dv, dalpha, db, dw,
-                      reinterpret_cast<float*>(ws + l.scratch), p->B, p->T, p->H, (int)p->dk, (int)p->dv,
-                      (int)nchunks(p), nch * nchunks(p)};
+    float* gsc = reinterpret_cast<float*>(ws + l.scratch);
+    if (l.mf) {
+        gdn2::GradVArgs va{ws, l.block, l.t_off, k, v, alpha, b, w, dO, chk, chkT, dsl, dslT, dw, dv, gsc,
+                           p->B, p->T, p->H, (int)p->dk, (int)p->dv, (int)nchunks(p), total};
+        gdn2::GradKArgs ka{q, k, alpha, b, gsc, dq, dk, dalpha, db, p->B, p->T, p->H, (int)p->dk,
+                           (int)nchunks(p), total};
+        return launch_status(gdn2::launch_chunk_grad_mf(va, ka, gates_bf16(p), s));
+    }
+    gdn2::GradArgs ga{q, k, v, alpha, b, w, dO, chk, dsl, dq, dk, dv, dalpha, db, dw, gsc, p->B, p->T, p->H,
+                      (int)p->dk, (int)p->dv, (int)nchunks(p), total};
     return launch_status(gdn2::launch_chunk_grad(ga, is_bf16(p), gates_bf16(p), s));
 }
 

@@ -260,6 +260,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_state_bwd(BwdStateArgs a)
             const int c = i / NCG, g = i - c * NCG;
             *reinterpret_cast<f32x4*>(dsl + (int64_t)c * dv + 4 * g) = *reinterpret_cast<const f32x4*>(&dS[c * VS + 4 * g]);
         }
+        if (a.dSLT != nullptr) {
+            // and transposed, [dv][dk] in the I/O dtype
+            Tio* dslT = static_cast<Tio*>(a.dSLT) + (chain * nt + n) * (int64_t)DK * dv;
+            for (int i = tid; i < DK * VS / 4; i += kThreads) {
+                const int j = i / (DK / 4), c4 = 4 * (i - j * (DK / 4));
+                const f32x4 x = {dS[c4 * VS + j], dS[(c4 + 1) * VS + j], dS[(c4 + 2) * VS + j], dS[(c4 + 3) * VS + j]};
+                st_vec4(dslT + (int64_t)(j0 + j) * DK + c4, x);
+            }
+        }
         if (n > 0) fetch(n - 1);
         __syncthreads();
         // dDelta = P^T dO + Ktil dS: rows r0 .. r0+TR-1, columns 4cg .. 4cg+3

@@ -1,0 +1,717 @@
+// Per-chunk gradients of the chunked GDN-2 forward on the matrix cores
+// (bf16 I/O, dk in {32, 64, 128}, dv a multiple of 32 up to 128).
+//
+// Same gradient as k_chunk_grad (the formulas are in gdn2_backward.hip's
+// header), split in two launches of one workgroup per chunk:
+//
+// k_chunk_grad_val  the value-side products on bf16 matrix cores, fp32
+//   accumulation.  Operands come from the forward workspace (W, P, Ktil^T,
+//   U^T, and T written by the prep kernel for the backward), from the chunk
+//   checkpoints (S0 and the exit gradient dSL, each in fp32 [dk][dv] and
+//   transposed in bf16 [dv][dk]) and from dO, v, w, b, k, alpha.  Every
+//   operand is laid out with its contraction index contiguous (transposed
+//   copies are made in LDS where needed; LDS rows are padded by 16 bytes), so
+//   a fragment is one 16-byte read.  In order:
+//     Delta = U - W S0,  dDelta = P^T dO + Ktil dSL,
+//     dQh = dO S0^T, dP = mask(dO Delta^T), dKtil = Delta dSL^T,
+//     dW = -dDelta S0^T, du = T^T dDelta (-> dw = du v, dv = du w),
+//     dT = dDelta u^T + dW Eh^T, dEh = T^T dW, dA = mask(-(T^T dT) T^T),
+//     dGamma_L = rowsum(dSL * S0);
+//   dQh, dKtil, dEh, dP, dA and dGamma_L go to an fp32 scratch block per chunk.
+// k_chunk_grad_key  the key side on vector ALUs from LDS: the cumulative log
+//   decay G, the contractions of dA and dP with the block-split decay ratios
+//   (row side: sum_s dA[r,s] k_s R[r,s]; column side: sum_r dA[r,s] e_r R[r,s],
+//   and the same with dP and q), the gradients of q, k, b, and dalpha from
+//   the reverse cumulative sum of dG.
+#include "gdn2_device.hpp"
+#include "gdn2_launch.hpp"
+#include "gdn2_layout.hpp"
+
+namespace gdn2 {
+
+namespace {
+
+typedef __bf16 bf;
+using IOB = Io<__bf16>;
+typedef IOB::frag bfrag;
+
+constexpr int kMaxD = 128;
+constexpr int LT = 64 + 8;                // padded row of a [.][64] bf16 array
+constexpr int LD = kMaxD + 8;             // padded row of a [.][dk|dv] bf16 array (maximum)
+
+// fragment (8 consecutive k) of row `row`, K-block kb, from a bf16 array with row stride ld
+__device__ inline bfrag fr(const bf* base, int row, int64_t ld, int kb, int grp)
+{
+    return *reinterpret_cast<const bfrag*>(base + row * ld + kb * 32 + grp * 8);
+}
+
+// the same from an fp32 array, rounded to bf16
+__device__ inline bfrag fr32(const float* base, int row, int64_t ld, int kb, int grp)
+{
+    const float* p = base + row * ld + kb * 32 + grp * 8;
+    const f32x4 x = *reinterpret_cast<const f32x4*>(p), y = *reinterpret_cast<const f32x4*>(p + 4);
+    bfrag r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[i] = (bf)x[i];
+        r[4 + i] = (bf)y[i];
+    }
+    return r;
+}
+
+template <typename T> __device__ inline float gf(const T* p, int64_t i) { return Io<T>::to_f(p[i]); }
+template <typename T> __device__ inline void gs(T* p, int64_t i, float x) { p[i] = Io<T>::from_f(x); }
+
+}  // namespace
+
+// fp32 scratch per chunk between the two launches, in floats:
+// dQh, dKtil, dEh [64][dk], dP, dA [64][64], dGamma_L [dk]
+__host__ __device__ inline int64_t gradmf_scratch_floats(int dk) { return 3 * 64 * (int64_t)dk + 2 * 4096 + dk; }
+
+// G[r][c] = sum of log alpha over tokens 0..r of the chunk (alpha = 1 past its
+// end), for 256 threads: logs in parallel, then a scan of 256/dk segments per
+// channel with the segment totals carried through `tot`
+template <typename Tg>
+__device__ __attribute__((always_inline)) inline void cum_log_decay(float* G, float* tot, const Tg* alpha,
+                                                                    int64_t row0, int64_t H, int dk, int Ln)
+{
+    const int tid = threadIdx.x;
+    for (int i = tid; i < 64 * dk; i += kThreads) {
+        const int r = i / dk, c = i - r * dk;
+        G[i] = r < Ln ? __logf(gf(alpha, (row0 + r * H) * dk + c)) : 0.f;
+    }
+    __syncthreads();
+    const int nseg = kThreads / dk, sl = 64 / nseg;
+    const int c = tid % dk, g = tid / dk;
+    float run = 0.f;
+    for (int r = g * sl; r < (g + 1) * sl; ++r) {
+        run += G[r * dk + c];
+        G[r * dk + c] = run;
+    }
+    tot[g * dk + c] = run;
+    __syncthreads();
+    float carry = 0.f;
+    for (int h = 0; h < g; ++h) carry += tot[h * dk + c];
+    if (g > 0)
+        for (int r = g * sl; r < (g + 1) * sl; ++r) G[r * dk + c] += carry;
+    __syncthreads();
+}
+
+// LDS regions of k_chunk_grad_val (bytes), sized for dk = dv = 128
+struct GvLds {
+    static constexpr int R0 = 0;                                  // T [64][LT], T^T [64][LT]
+    static constexpr int R1 = R0 + 2 * 64 * LT * 2;               // dO [64][LD] | u [64][LD] | tmp [64][LT]
+    static constexpr int R2 = R1 + 64 * LD * 2;                   // dO^T [dv][LT] | dW [64][LD]
+    static constexpr int R3 = R2 + kMaxD * LT * 2;                // P^T [64][LT] + Ktil [64][LD] | dW^T [dk][LT] + dT^T [64][LT]
+    static constexpr int R3SZ = (64 * LT + 64 * LD) * 2 > (kMaxD * LT + 64 * LT) * 2 ? (64 * LT + 64 * LD) * 2
+                                                                                       : (kMaxD * LT + 64 * LT) * 2;
+    static constexpr int R4 = R3 + R3SZ;                          // U, then Delta [64][LD]
+    static constexpr int R5 = R4 + 64 * LD * 2;                   // dDelta [64][LD] + dDelta^T [dv][LT] | G fp32 [64][dk]
+    static constexpr int R5SZ = (64 * LD + kMaxD * LT) * 2 > 64 * kMaxD * 4 ? (64 * LD + kMaxD * LT) * 2 : 64 * kMaxD * 4;
+    static constexpr int R7 = R5 + R5SZ;                          // Eh [64][LD]
+    static constexpr int RT = R7 + 64 * LD * 2;                   // scan totals [256]
+    static constexpr int BYTES = RT + kThreads * 4;
+};
+
+// Tiles t = wave, wave + 4, ... < NT of one product: fetch(t, a, b) loads the
+// NKB K-blocks of a tile's A and B fragments, epi(t, acc) consumes its
+// result.  The next tile's fragments are requested before the current
+// tile's products, so global-memory operands arrive while the matrix cores work.
+template <int NKB, typename FF, typename FE>
+__device__ __attribute__((always_inline)) inline void tiles(int wave, int NT, FF fetch, FE epi)
+{
+    bfrag ca[NKB], cb[NKB], na[NKB], nb[NKB];
+    int t = wave;
+    if (t < NT) fetch(t, na, nb);
+    for (; t < NT; t += 4) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            ca[kb] = na[kb];
+            cb[kb] = nb[kb];
+        }
+        if (t + 4 < NT) fetch(t + 4, na, nb);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) acc = IOB::mma(acc, ca[kb], cb[kb]);
+        epi(t, acc);
+    }
+}
+
+template <int DK, int DV, typename Tg>
+__global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
+{
+    using L = GvLds;
+    static_assert(L::BYTES <= 160 * 1024, "LDS budget");
+    constexpr int NKK = DK / 32, NKV = DV / 32, NTK = DK / 16, NTV = DV / 16;
+    constexpr int ldv = DV + 8, ldk = DK + 8;
+    __shared__ __attribute__((aligned(16))) char sm[L::BYTES];
+    bf* Tl = reinterpret_cast<bf*>(sm + L::R0);
+    bf* Ttl = Tl + 64 * LT;
+    bf* dOl = reinterpret_cast<bf*>(sm + L::R1);
+    bf* ul = dOl;
+    bf* tmpl = dOl;
+    bf* dOtl = reinterpret_cast<bf*>(sm + L::R2);
+    bf* dWl = dOtl;
+    bf* Ptl = reinterpret_cast<bf*>(sm + L::R3);
+    bf* Ktl = Ptl + 64 * LT;
+    bf* dWtl = Ptl;
+    bf* dTtl = Ptl + kMaxD * LT;
+    bf* Dll = reinterpret_cast<bf*>(sm + L::R4);
+    bf* dDl = reinterpret_cast<bf*>(sm + L::R5);
+    bf* dDtl = dDl + 64 * ldv;
+    float* Gl = reinterpret_cast<float*>(sm + L::R5);
+    bf* Ehl = reinterpret_cast<bf*>(sm + L::R7);
+    float* tot = reinterpret_cast<float*>(sm + L::RT);
+
+    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+    const int wave = tid >> 6;
+    const int nt = a.nt;
+    const int64_t ci = blockIdx.x;
+    const int64_t chain = ci / nt;
+    const int n = (int)(ci - chain * nt);
+    const int64_t bb = chain / a.H, hh = chain - bb * a.H;
+    const int64_t t0 = (int64_t)n * kChunk;
+    const int Ln = (int)(a.T - t0 < kChunk ? a.T - t0 : kChunk);
+    const int64_t H = a.H;
+    const int64_t row0 = (bb * a.T + t0) * H + hh;
+    constexpr WsLayout LY = ws_layout(DK, DV, 2, 32);
+    const char* blk = static_cast<const char*>(a.ws) + ci * a.ws_block;
+    const bf* Tg_ = reinterpret_cast<const bf*>(blk + a.t_off);         // T [64][64]
+    const bf* Pg = reinterpret_cast<const bf*>(blk + LY.p);              // P [64][64]
+    const bf* Kttg = reinterpret_cast<const bf*>(blk + LY.ktt);          // Ktil^T [dk][64]
+    const bf* Wg = reinterpret_cast<const bf*>(blk + LY.wwy);            // W [64][dk]
+    const bf* Utg = reinterpret_cast<const bf*>(blk + LY.uwyt);          // U^T [dv][64]
+    const float* S0 = a.S_chk + ci * (int64_t)DK * DV;                    // [dk][dv]
+    const bf* S0t = static_cast<const bf*>(a.S_chkT) + ci * (int64_t)DK * DV;   // [dv][dk]
+    const float* dSL = a.dSL + ci * (int64_t)DK * DV;
+    const bf* dSLt = static_cast<const bf*>(a.dSLT) + ci * (int64_t)DK * DV;
+    const bf* dO = static_cast<const bf*>(a.dO);
+    const bf* vg = static_cast<const bf*>(a.v);
+    const bf* kg = static_cast<const bf*>(a.k);
+    const Tg* wgt = static_cast<const Tg*>(a.w);
+    const Tg* bgt = static_cast<const Tg*>(a.b);
+    const Tg* agt = static_cast<const Tg*>(a.alpha);
+    Tg* dwg = static_cast<Tg*>(a.dw);
+    bf* dvg = static_cast<bf*>(a.dv_out);
+    float* sc = a.gsc + ci * gradmf_scratch_floats(DK);
+    float* s_dQh = sc;
+    float* s_dKt = sc + 64 * DK;
+    float* s_dEh = sc + 2 * 64 * DK;
+    float* s_dP = sc + 3 * 64 * DK;
+    float* s_dA = s_dP + 4096;
+    float* s_dGL = s_dA + 4096;
+
+    // ---- phase 0: operands into LDS ----------------------------------------
+    for (int g = tid; g < 64 * 8; g += kThreads) {                 // T, T^T; P^T
+        const int r = g >> 3, c0 = (g & 7) * 8;
+        const bfrag t = *reinterpret_cast<const bfrag*>(Tg_ + r * 64 + c0);
+        const bfrag p = *reinterpret_cast<const bfrag*>(Pg + r * 64 + c0);
+        *reinterpret_cast<bfrag*>(Tl + r * LT + c0) = t;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            Ttl[(c0 + e) * LT + r] = t[e];
+            Ptl[(c0 + e) * LT + r] = p[e];
+        }
+    }
+    for (int g = tid; g < DK * 8; g += kThreads) {                 // Ktil [r][c] from Ktil^T [c][r]
+        const int c = g >> 3, r0 = (g & 7) * 8;
+        const bfrag x = *reinterpret_cast<const bfrag*>(Kttg + c * 64 + r0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Ktl[(r0 + e) * ldk + c] = x[e];
+    }
+    for (int g = tid; g < DV * 8; g += kThreads) {                 // U [r][j] from U^T [j][r]
+        const int j = g >> 3, r0 = (g & 7) * 8;
+        const bfrag x = *reinterpret_cast<const bfrag*>(Utg + j * 64 + r0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Dll[(r0 + e) * ldv + j] = x[e];
+    }
+    for (int g = tid; g < 64 * (DV / 8); g += kThreads) {          // dO, dO^T (zero past the end)
+        const int r = g / (DV / 8), j0 = (g - r * (DV / 8)) * 8;
+        bfrag x;
+        if (r < Ln) {
+            x = *reinterpret_cast<const bfrag*>(dO + (row0 + r * H) * DV + j0);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = (bf)0.f;
+        }
+        *reinterpret_cast<bfrag*>(dOl + r * ldv + j0) = x;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dOtl[(j0 + e) * LT + r] = x[e];
+    }
+    cum_log_decay(Gl, tot, agt, row0, H, DK, Ln);
+    for (int i = tid; i < 64 * DK; i += kThreads) {                // Eh = Gamma b k
+        const int r = i / DK, c = i - r * DK;
+        float x = 0.f;
+        if (r < Ln) {
+            const int64_t o = (row0 + r * H) * DK + c;
+            x = __expf(Gl[i]) * gf(bgt, o) * gf(kg, o);
+        }
+        Ehl[r * ldk + c] = (bf)x;
+    }
+    __syncthreads();
+
+    // ---- Delta = U - W S0 (in place over U) ----------------------------------------
+    tiles<NKK>(wave, 4 * NTV,
+               [&](int t, bfrag (&fa)[NKK], bfrag (&fb)[NKK]) {
+                   const int tr = t / NTV, tn = t - tr * NTV;
+#pragma unroll
+                   for (int kb = 0; kb < NKK; ++kb) {
+                       fa[kb] = fr(Wg, 16 * tr + l16, DK, kb, grp);
+                       fb[kb] = fr(S0t, 16 * tn + l16, DK, kb, grp);
+                   }
+               },
+               [&](int t, f32x4 acc) {
+                   const int tr = t / NTV, tn = t - tr * NTV;
+                   const int r = 16 * tr + 4 * grp, j = 16 * tn + l16;
+#pragma unroll
+                   for (int i = 0; i < 4; ++i) {
+                       bf* d = &Dll[(r + i) * ldv + j];
+                       *d = (bf)((float)*d - acc[i]);
+                   }
+               });
+    // ---- dDelta = P^T dO + Ktil dSL ----------------------------------------------
+    tiles<2 + NKK>(wave, 4 * NTV,
+                   [&](int t, bfrag (&fa)[2 + NKK], bfrag (&fb)[2 + NKK]) {
+                       const int tr = t / NTV, tn = t - tr * NTV;
+#pragma unroll
+                       for (int kb = 0; kb < 2; ++kb) {
+                           fa[kb] = fr(Ptl, 16 * tr + l16, LT, kb, grp);
+                           fb[kb] = fr(dOtl, 16 * tn + l16, LT, kb, grp);
+                       }
+#pragma unroll
+                       for (int kb = 0; kb < NKK; ++kb) {
+                           fa[2 + kb] = fr(Ktl, 16 * tr + l16, ldk, kb, grp);
+                           fb[2 + kb] = fr(dSLt, 16 * tn + l16, DK, kb, grp);
+                       }
+                   },
+                   [&](int t, f32x4 acc) {
+                       const int tr = t / NTV, tn = t - tr * NTV;
+                       const int r = 16 * tr + 4 * grp, j = 16 * tn + l16;
+#pragma unroll
+                       for (int i = 0; i < 4; ++i) dDl[(r + i) * ldv + j] = (bf)acc[i];
+                       st_vec4(dDtl + j * LT + r, acc);
+                   });
+    __syncthreads();
+    // ---- dQh = dO S0^T, dKtil = Delta dSL^T, dW = -dDelta S0^T ---------------------
+    tiles<NKV>(wave, 3 * 4 * NTK,
+               [&](int t, bfrag (&fa)[NKV], bfrag (&fb)[NKV]) {
+                   const int which = t / (4 * NTK), u = t - which * 4 * NTK, tr = u / NTK, tn = u - tr * NTK;
+                   const bf* A = which == 0 ? dOl : (which == 1 ? Dll : dDl);
+                   const float* B = which == 1 ? dSL : S0;
+#pragma unroll
+                   for (int kb = 0; kb < NKV; ++kb) {
+                       fa[kb] = fr(A, 16 * tr + l16, ldv, kb, grp);
+                       fb[kb] = fr32(B, 16 * tn + l16, DV, kb, grp);
+                   }
+               },
+               [&](int t, f32x4 acc) {
+                   const int which = t / (4 * NTK), u = t - which * 4 * NTK, tr = u / NTK, tn = u - tr * NTK;
+                   const int r = 16 * tr + 4 * grp, c = 16 * tn + l16;
+                   if (which == 0) {
+#pragma unroll
+                       for (int i = 0; i < 4; ++i) s_dQh[(r + i) * DK + c] = acc[i];
+                   } else if (which == 1) {
+#pragma unroll
+                       for (int i = 0; i < 4; ++i) s_dKt[(r + i) * DK + c] = acc[i];
+                   } else {
+                       acc = -acc;
+#pragma unroll
+                       for (int i = 0; i < 4; ++i) dWl[(r + i) * ldk + c] = (bf)acc[i];
+                       st_vec4(dWtl + c * LT + r, acc);
+                   }
+               });
+    // ---- dP = mask(dO Delta^T) -------------------------------------------------------
+    tiles<NKV>(wave, 16,
+               [&](int t, bfrag (&fa)[NKV], bfrag (&fb)[NKV]) {
+                   const int tr = t >> 2, tn = t & 3;
+#pragma unroll
+                   for (int kb = 0; kb < NKV; ++kb) {
+                       fa[kb] = fr(dOl, 16 * tr + l16, ldv, kb, grp);
+                       fb[kb] = fr(Dll, 16 * tn + l16, ldv, kb, grp);
+                   }
+               },
+               [&](int t, f32x4 acc) {
+                   const int r = 16 * (t >> 2) + 4 * grp, s = 16 * (t & 3) + l16;
+#pragma unroll
+                   for (int i = 0; i < 4; ++i) s_dP[(r + i) * 64 + s] = s <= r + i ? acc[i] : 0.f;
+               });
+    // ---- du = T^T dDelta -> dw = du v, dv = du w ---------------------------------
+    tiles<2>(wave, 4 * NTV,
+             [&](int t, bfrag (&fa)[2], bfrag (&fb)[2]) {
+                 const int tr = t / NTV, tn = t - tr * NTV;
+#pragma unroll
+                 for (int kb = 0; kb < 2; ++kb) {
+                     fa[kb] = fr(Ttl, 16 * tr + l16, LT, kb, grp);
+                     fb[kb] = fr(dDtl, 16 * tn + l16, LT, kb, grp);
+                 }
+             },
+             [&](int t, f32x4 acc) {
+                 const int tr = t / NTV, tn = t - tr * NTV;
+                 const int r = 16 * tr + 4 * grp, j = 16 * tn + l16;
+#pragma unroll
+                 for (int i = 0; i < 4; ++i) {
+                     if (r + i < Ln) {
+                         const int64_t o = (row0 + (r + i) * H) * DV + j;
+                         gs(dwg, o, acc[i] * gf(vg, o));
+                         gs(dvg, o, acc[i] * gf(wgt, o));
+                     }
+                 }
+             });
+    for (int c = tid; c < DK; c += kThreads) {                      // dGamma_L
+        float x = 0.f;
+#pragma unroll 4
+        for (int j = 0; j < DV; j += 4) {
+            const f32x4 p = *reinterpret_cast<const f32x4*>(dSL + (int64_t)c * DV + j);
+            const f32x4 q = *reinterpret_cast<const f32x4*>(S0 + (int64_t)c * DV + j);
+            x += p[0] * q[0] + p[1] * q[1] + p[2] * q[2] + p[3] * q[3];
+        }
+        s_dGL[c] = x;
+    }
+    __syncthreads();
+    // ---- u = w v (padding tokens 0) ----------------------------------------------
+    for (int i = tid; i < 64 * DV; i += kThreads) {
+        const int r = i / DV, j = i - r * DV;
+        float x = 0.f;
+        if (r < Ln) {
+            const int64_t o = (row0 + r * H) * DV + j;
+            x = gf(wgt, o) * gf(vg, o);
+        }
+        ul[r * ldv + j] = (bf)x;
+    }
+    __syncthreads();
+    // ---- dT = dDelta u^T + dW Eh^T (stored transposed);  dEh = T^T dW ------------
+    tiles<NKV + NKK>(wave, 16,
+                     [&](int t, bfrag (&fa)[NKV + NKK], bfrag (&fb)[NKV + NKK]) {
+                         const int tr = t >> 2, tn = t & 3;
+#pragma unroll
+                         for (int kb = 0; kb < NKV; ++kb) {
+                             fa[kb] = fr(dDl, 16 * tr + l16, ldv, kb, grp);
+                             fb[kb] = fr(ul, 16 * tn + l16, ldv, kb, grp);
+                         }
+#pragma unroll
+                         for (int kb = 0; kb < NKK; ++kb) {
+                             fa[NKV + kb] = fr(dWl, 16 * tr + l16, ldk, kb, grp);
+                             fb[NKV + kb] = fr(Ehl, 16 * tn + l16, ldk, kb, grp);
+                         }
+                     },
+                     [&](int t, f32x4 acc) {
+                         st_vec4(dTtl + (16 * (t & 3) + l16) * LT + 16 * (t >> 2) + 4 * grp, acc);
+                     });
+    tiles<2>(wave, 4 * NTK,
+             [&](int t, bfrag (&fa)[2], bfrag (&fb)[2]) {
+                 const int tr = t / NTK, tn = t - tr * NTK;
+#pragma unroll
+                 for (int kb = 0; kb < 2; ++kb) {
+                     fa[kb] = fr(Ttl, 16 * tr + l16, LT, kb, grp);
+                     fb[kb] = fr(dWtl, 16 * tn + l16, LT, kb, grp);
+                 }
+             },
+             [&](int t, f32x4 acc) {
+                 const int tr = t / NTK, tn = t - tr * NTK;
+                 const int r = 16 * tr + 4 * grp, c = 16 * tn + l16;
+#pragma unroll
+                 for (int i = 0; i < 4; ++i) s_dEh[(r + i) * DK + c] = acc[i];
+             });
+    __syncthreads();
+    // ---- tmp = T^T dT -------------------------------------------------------------
+    tiles<2>(wave, 16,
+             [&](int t, bfrag (&fa)[2], bfrag (&fb)[2]) {
+#pragma unroll
+                 for (int kb = 0; kb < 2; ++kb) {
+                     fa[kb] = fr(Ttl, 16 * (t >> 2) + l16, LT, kb, grp);
+                     fb[kb] = fr(dTtl, 16 * (t & 3) + l16, LT, kb, grp);
+                 }
+             },
+             [&](int t, f32x4 acc) {
+                 const int r = 16 * (t >> 2) + 4 * grp, j = 16 * (t & 3) + l16;
+#pragma unroll
+                 for (int i = 0; i < 4; ++i) tmpl[(r + i) * LT + j] = (bf)acc[i];
+             });
+    __syncthreads();
+    // ---- dA = mask(-tmp T^T) --------------------------------------------------------
+    tiles<2>(wave, 16,
+             [&](int t, bfrag (&fa)[2], bfrag (&fb)[2]) {
+#pragma unroll
+                 for (int kb = 0; kb < 2; ++kb) {
+                     fa[kb] = fr(tmpl, 16 * (t >> 2) + l16, LT, kb, grp);
+                     fb[kb] = fr(Tl, 16 * (t & 3) + l16, LT, kb, grp);
+                 }
+             },
+             [&](int t, f32x4 acc) {
+                 const int r = 16 * (t >> 2) + 4 * grp, s = 16 * (t & 3) + l16;
+#pragma unroll
+                 for (int i = 0; i < 4; ++i) s_dA[(r + i) * 64 + s] = s < r + i ? -acc[i] : 0.f;
+             });
+}
+
+// ---------------------------------------------------------------------------
+// key side: one workgroup per chunk; thread = R = DK/16 rows (inside one
+// 16-token block) x 4 key channels
+// ---------------------------------------------------------------------------
+template <int DK, typename Tg>
+__global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
+{
+    constexpr int CG = DK / 4, R = DK / 16;
+    __shared__ __attribute__((aligned(16))) float G[64 * DK];
+    __shared__ __attribute__((aligned(16))) bf KYE[2 * 64 * DK];
+    __shared__ __attribute__((aligned(16))) bf Q[64 * DK];
+    __shared__ __attribute__((aligned(16))) float dA[64 * 64];
+    __shared__ __attribute__((aligned(16))) float dP[64 * 64];
+    __shared__ float ext[(kThreads / CG) * DK];                // per row group: sum of dKtil * Ktil
+    __shared__ float tot[kThreads];
+    bf* KY = KYE;                                               // k_s exp(G_j0(s) - G_s)
+    bf* E = KYE + 64 * DK;                                      // e = b k
+    float* dG = reinterpret_cast<float*>(KYE);                  // [64][DK] over KY and E once they are used
+
+    const int tid = threadIdx.x;
+    const int nt = a.nt;
+    const int64_t ci = blockIdx.x;
+    const int64_t chain = ci / nt;
+    const int n = (int)(ci - chain * nt);
+    const int64_t bb = chain / a.H, hh = chain - bb * a.H;
+    const int64_t t0 = (int64_t)n * kChunk;
+    const int Ln = (int)(a.T - t0 < kChunk ? a.T - t0 : kChunk);
+    const int64_t H = a.H;
+    const int64_t row0 = (bb * a.T + t0) * H + hh;
+    const bf* qg = static_cast<const bf*>(a.q);
+    const bf* kg = static_cast<const bf*>(a.k);
+    const Tg* agt = static_cast<const Tg*>(a.alpha);
+    const Tg* bgt = static_cast<const Tg*>(a.b);
+    const float* sc = a.gsc + ci * gradmf_scratch_floats(DK);
+    const float* s_dQh = sc;
+    const float* s_dKt = sc + 64 * DK;
+    const float* s_dEh = sc + 2 * 64 * DK;
+    const float* s_dP = sc + 3 * 64 * DK;
+    const float* s_dA = s_dP + 4096;
+    const float* s_dGL = s_dA + 4096;
+
+    for (int i = tid; i < 4096 / 4; i += kThreads) {
+        *reinterpret_cast<f32x4*>(&dA[4 * i]) = *reinterpret_cast<const f32x4*>(s_dA + 4 * i);
+        *reinterpret_cast<f32x4*>(&dP[4 * i]) = *reinterpret_cast<const f32x4*>(s_dP + 4 * i);
+    }
+    cum_log_decay(G, tot, agt, row0, H, DK, Ln);
+    for (int i = tid; i < 64 * DK; i += kThreads) {
+        const int r = i / DK, c = i - r * DK;
+        float kv = 0.f, qv = 0.f, bv = 0.f;
+        if (r < Ln) {
+            const int64_t o = (row0 + r * H) * DK + c;
+            kv = gf(kg, o);
+            qv = gf(qg, o);
+            bv = gf(bgt, o);
+        }
+        KY[i] = (bf)(kv * __expf(G[(r & ~15) * DK + c] - G[i]));
+        E[i] = (bf)(bv * kv);
+        Q[i] = (bf)qv;
+    }
+    __syncthreads();
+
+    const int c0 = 4 * (tid % CG), r0 = (tid / CG) * R, J0 = r0 >> 4;
+    // row side: sum over earlier columns s of dA[r,s] k_s R[r,s] (and dP with k)
+    float deA[R][4], dqP[R][4];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) deA[rr][cc] = dqP[rr][cc] = 0.f;
+    for (int J = 0; J <= J0; ++J) {
+        const int j0 = 16 * J;
+        float pa[R][4], pp[R][4];
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) pa[rr][cc] = pp[rr][cc] = 0.f;
+        for (int s0 = j0; s0 < j0 + 16; s0 += 4) {
+            f32x4 ky[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ky[e] = IOB::unpack4(*reinterpret_cast<const bf16x4*>(&KY[(s0 + e) * DK + c0]));
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(&dA[(r0 + rr) * 64 + s0]);
+                const f32x4 y = *reinterpret_cast<const f32x4*>(&dP[(r0 + rr) * 64 + s0]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int cc = 0; cc < 4; ++cc) {
+                        pa[rr][cc] += x[e] * ky[e][cc];
+                        pp[rr][cc] += y[e] * ky[e][cc];
+                    }
+            }
+        }
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                const float xr = __expf(G[(r0 + rr) * DK + c0 + cc] - G[j0 * DK + c0 + cc]);
+                deA[rr][cc] += pa[rr][cc] * xr;
+                dqP[rr][cc] += pp[rr][cc] * xr;
+            }
+    }
+    // gradients that need only the row side; partial dk and dG
+    float dkp[R][4], dGp[R][4];
+    {
+        float ex[4] = {0.f, 0.f, 0.f, 0.f};
+        bf* dq = static_cast<bf*>(a.dq);
+        Tg* db = static_cast<Tg*>(a.db);
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
+            const int r = r0 + rr;
+            const bool ok = r < Ln;
+            const int64_t o = (row0 + r * H) * DK + c0;
+            const f32x4 dQh = *reinterpret_cast<const f32x4*>(s_dQh + r * DK + c0);
+            const f32x4 dEh = *reinterpret_cast<const f32x4*>(s_dEh + r * DK + c0);
+            const f32x4 dKt = *reinterpret_cast<const f32x4*>(s_dKt + r * DK + c0);
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                const int c = c0 + cc;
+                float qv = 0.f, kv = 0.f, bv = 0.f;
+                if (ok) {
+                    qv = gf(qg, o + cc);
+                    kv = gf(kg, o + cc);
+                    bv = gf(bgt, o + cc);
+                }
+                const float g = G[r * DK + c], gam = __expf(g), kt = __expf(G[63 * DK + c] - g);
+                const float ev = bv * kv;
+                const float de = gam * dEh[cc] + deA[rr][cc];
+                if (ok) {
+                    gs(dq, o + cc, gam * dQh[cc] + dqP[rr][cc]);
+                    gs(db, o + cc, de * kv);
+                }
+                dkp[rr][cc] = kt * dKt[cc] + de * bv;
+                dGp[rr][cc] = dQh[cc] * gam * qv + dEh[cc] * gam * ev - dKt[cc] * kv * kt + ev * deA[rr][cc] +
+                              qv * dqP[rr][cc];
+                ex[cc] += dKt[cc] * kv * kt;
+            }
+        }
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) ext[(tid / CG) * DK + c0 + cc] = ex[cc];
+    }
+    // column side: sum over later rows r of dA[r,s] e_r R[r,s] (and dP with q)
+    float dkA[R][4], dkP[R][4];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) dkA[rr][cc] = dkP[rr][cc] = 0.f;
+    {
+        const int j0 = 16 * J0;
+        for (int r = j0; r < 64; ++r) {
+            const f32x4 e4 = IOB::unpack4(*reinterpret_cast<const bf16x4*>(&E[r * DK + c0]));
+            const f32x4 q4 = IOB::unpack4(*reinterpret_cast<const bf16x4*>(&Q[r * DK + c0]));
+            const f32x4 g4 = *reinterpret_cast<const f32x4*>(&G[r * DK + c0]);
+            const f32x4 gj = *reinterpret_cast<const f32x4*>(&G[j0 * DK + c0]);
+            f32x4 ea, qa;
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                const float x = __expf(g4[cc] - gj[cc]);
+                ea[cc] = e4[cc] * x;
+                qa[cc] = q4[cc] * x;
+            }
+            if constexpr (R % 4 == 0) {
+#pragma unroll
+                for (int r4 = 0; r4 < R; r4 += 4) {
+                    const f32x4 x = *reinterpret_cast<const f32x4*>(&dA[r * 64 + r0 + r4]);
+                    const f32x4 y = *reinterpret_cast<const f32x4*>(&dP[r * 64 + r0 + r4]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int cc = 0; cc < 4; ++cc) {
+                            dkA[r4 + e][cc] += x[e] * ea[cc];
+                            dkP[r4 + e][cc] += y[e] * qa[cc];
+                        }
+                }
+            } else {
+#pragma unroll
+                for (int rr = 0; rr < R; ++rr) {
+                    const float x = dA[r * 64 + r0 + rr], y = dP[r * 64 + r0 + rr];
+#pragma unroll
+                    for (int cc = 0; cc < 4; ++cc) {
+                        dkA[rr][cc] += x * ea[cc];
+                        dkP[rr][cc] += y * qa[cc];
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();                                       // KY and E are read for the last time
+    {
+        bf* dk_out = static_cast<bf*>(a.dk_out);
+        const int j0 = 16 * J0;
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
+            const int s = r0 + rr;
+            const int64_t o = (row0 + s * H) * DK + c0;
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                const int c = c0 + cc;
+                const float y = __expf(G[j0 * DK + c] - G[s * DK + c]);
+                const float ka = dkA[rr][cc] * y, kp = dkP[rr][cc] * y;
+                const float kv = s < Ln ? gf(kg, o + cc) : 0.f;
+                if (s < Ln) gs(dk_out, o + cc, dkp[rr][cc] + ka + kp);
+                dG[s * DK + c] = dGp[rr][cc] - kv * (ka + kp);
+            }
+        }
+    }
+    __syncthreads();
+    // dlog(alpha): reverse cumulative sum of dG; the last token also carries the
+    // uses of Gamma_L (the state decay over the chunk and Ktil)
+    {
+        Tg* dalpha = static_cast<Tg*>(a.dalpha);
+        for (int c = tid; c < DK; c += kThreads) {
+            float acc = s_dGL[c] * __expf(G[63 * DK + c]);
+            for (int g = 0; g < kThreads / CG; ++g) acc += ext[g * DK + c];
+            for (int r = 63; r >= 0; --r) {
+                acc += dG[r * DK + c];
+                if (r < Ln) {
+                    const int64_t o = (row0 + r * H) * DK + c;
+                    gs(dalpha, o, acc / gf(agt, o));
+                }
+            }
+        }
+    }
+}
+
+int64_t gradmf_scratch_bytes(int dk, int64_t total) { return total * gradmf_scratch_floats(dk) * 4; }
+
+bool gradmf_supported(int dk, int dv, bool bf16)
+{
+    return bf16 && (dk == 32 || dk == 64 || dk == 128) && (dv == 32 || dv == 64 || dv == 128);
+}
+
+template <int DK, int DV>
+static void val_launch(const GradVArgs& v, bool gbf16, dim3 grid, hipStream_t s)
+{
+    if (gbf16)
+        hipLaunchKernelGGL((k_chunk_grad_val<DK, DV, __bf16>), grid, dim3(kThreads), 0, s, v);
+    else
+        hipLaunchKernelGGL((k_chunk_grad_val<DK, DV, float>), grid, dim3(kThreads), 0, s, v);
+}
+
+template <int DK>
+static hipError_t grad_mf_dk(const GradVArgs& v, const GradKArgs& k, bool gbf16, hipStream_t s)
+{
+    const dim3 grid((unsigned)v.total);
+    switch (v.dv) {
+        case 32: val_launch<DK, 32>(v, gbf16, grid, s); break;
+        case 64: val_launch<DK, 64>(v, gbf16, grid, s); break;
+        case 128: val_launch<DK, 128>(v, gbf16, grid, s); break;
+        default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (gbf16)
+        hipLaunchKernelGGL((k_chunk_grad_key<DK, __bf16>), grid, dim3(kThreads), 0, s, k);
+    else
+        hipLaunchKernelGGL((k_chunk_grad_key<DK, float>), grid, dim3(kThreads), 0, s, k);
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_grad_mf(const GradVArgs& v, const GradKArgs& k, bool gbf16, hipStream_t s)
+{
+    if (!gradmf_supported(v.dk, v.dv, true)) return hipErrorInvalidValue;
+    switch (v.dk) {
+        case 32: return grad_mf_dk<32>(v, k, gbf16, s);
+        case 64: return grad_mf_dk<64>(v, k, gbf16, s);
+        case 128: return grad_mf_dk<128>(v, k, gbf16, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace gdn2

@@ -101,7 +101,9 @@ __device__ inline int unpack2(unsigned p, int i) { return (int)((p >> (2 * i)) &
 
 // NUI = (token, 4-column) value items per thread: 64 * dv / 4 <= 256 * NUI
 // Tg = gate dtype (alpha, b, w): float, or __bf16 with bf16 I/O
-template <typename Tio, int DK, int NUI, typename Tg>
+// TOUT: also write T = (I + A)^{-1} (row-major [64][64], I/O dtype) at a.t_off
+// of the chunk's workspace block (kept for the backward pass)
+template <typename Tio, int DK, int NUI, typename Tg, bool TOUT = false>
 __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2)) void k_chunk_prep(PrepArgs a)
 {
     using IO = Io<Tio>;
@@ -464,6 +466,12 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
     typename IO::frag tf[64 / KB];
 #pragma unroll
     for (int kb = 0; kb < 64 / KB; ++kb) tf[kb] = ld_frag(Tm + (16 * wave + l16) * TS + kb * KB + grp * EPL);
+    if constexpr (TOUT) {
+        Tio* t_out = reinterpret_cast<Tio*>(blk + a.t_off);
+#pragma unroll
+        for (int kb = 0; kb < 64 / KB; ++kb)
+            *reinterpret_cast<frag*>(t_out + (16 * wave + l16) * 64 + kb * KB + grp * EPL) = tf[kb];
+    }
 #pragma unroll
     for (int ct = 0; ct < DK / 16; ++ct) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -813,6 +821,19 @@ __global__ __launch_bounds__(state_threads(VS, (int)sizeof(Tio)), 1) void k_chun
                         for (int e = 0; e < 4; ++e) dst[(16 * rt + 4 * grp + e) * dv + 16 * ct] = accS[i][ct][e];
                 }
             }
+            if (a.S_chkT != nullptr) {
+                // the same state transposed, [dv][dk] in the I/O dtype
+                Tio* dstT = static_cast<Tio*>(a.S_chkT) + (chain * (int64_t)nt + n) * DK * dv;
+#pragma unroll
+                for (int i = 0; i < SPW; ++i) {
+                    const int rt = tb * SPW + i;
+                    if (rt < SRT) {
+#pragma unroll
+                        for (int ct = 0; ct < NCT; ++ct)
+                            st_vec4(dstT + (int64_t)(j0 + jc + 16 * ct + l16) * DK + 16 * rt + 4 * grp, accS[i][ct]);
+                    }
+                }
+            }
         }
         const char* B0 = smem + (NB == 2 ? (n & 1) : 0) * L::GBUF * 16;
         const char* Wl = B0 + L::O_W * 16;
@@ -963,6 +984,15 @@ template <typename Tio, int DK, typename Tg>
 static hipError_t prep_dk(const PrepArgs& a, hipStream_t s)
 {
     const int64_t nblk = a.plan == nullptr ? a.B * a.H * (int64_t)a.nt : a.H * a.ncmax;
+    if (a.t_off != 0) {                          // backward: T kept (bf16 I/O, dv <= 128)
+        if constexpr (sizeof(Tio) == 2) {
+            if (a.dv > 128) return hipErrorInvalidValue;
+            hipLaunchKernelGGL((k_chunk_prep<Tio, DK, 8, Tg, true>), dim3((unsigned)nblk), dim3(kThreads), 0, s, a);
+            return hipGetLastError();
+        } else {
+            return hipErrorInvalidValue;
+        }
+    }
     if (a.dv <= 64)
         hipLaunchKernelGGL((k_chunk_prep<Tio, DK, 4, Tg>), dim3((unsigned)nblk), dim3(kThreads), 0, s, a);
     else if (a.dv <= 128)

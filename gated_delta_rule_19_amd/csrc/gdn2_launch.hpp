@@ -23,16 +23,18 @@ struct PrepArgs {
     void* ws; int64_t ws_block;
     int64_t B, T, H, Hk; int dv; int nt; int flags;
     const int* plan; int64_t ncmax;
+    int64_t t_off;          // backward: byte offset of T in each block (0 = not written)
 };
 
 // S_chk (optional, equal-length batches only): the fp32 state entering every
-// chunk, [B*H][nt][dk][dv]; o may be null when only states are wanted
+// chunk, [B*H][nt][dk][dv], and (optional with it) its transpose in the I/O
+// dtype, S_chkT [B*H][nt][dv][dk]; o may be null when only states are wanted
 struct StateArgs {
     const void* ws; int64_t ws_block;
     const float* S0; void* o; float* S_out;
     int64_t B, T, H; int dv; int nt; int nslices;
     const int* plan; int64_t ncmax;
-    float* S_chk;
+    float* S_chk; void* S_chkT;
 };
 
 // cu (null for equal-length batches): the N+1 caller offsets of a packed
@@ -54,6 +56,7 @@ struct BwdStateArgs {
     const void* ws; int64_t ws_block;
     const void* dO; const float* dS_T; float* dSL; float* dS0;
     int64_t B, T, H; int dk, dv, nt, nslices, vs;
+    void* dSLT;             // optional: dSL transposed, [B*H][nt][dv][dk], I/O dtype
 };
 
 // Per-chunk gradients: inputs, dO, the chunk entry states S_chk and exit
@@ -66,6 +69,26 @@ struct GradArgs {
     void* dq; void* dk_out; void* dv_out; void* dalpha; void* db; void* dw;
     float* scratch;
     int64_t B, T, H; int dk, dv, nt; int64_t total;
+};
+
+// Matrix-core per-chunk gradients (bf16 I/O): the value-side launch reads the
+// forward workspace (blocks of ws_block bytes with T at t_off), the
+// checkpoints S_chk/S_chkT and dSL/dSLT, dO, v, w, b, k, alpha; writes dw, dv
+// and an fp32 scratch block per chunk that the key-side launch reads with q,
+// k, b, alpha to write dq, dk, db, dalpha.
+struct GradVArgs {
+    const void* ws; int64_t ws_block, t_off;
+    const void* k; const void* v; const void* alpha; const void* b; const void* w; const void* dO;
+    const float* S_chk; const void* S_chkT; const float* dSL; const void* dSLT;
+    void* dw; void* dv_out; float* gsc;
+    int64_t B, T, H; int dk, dv, nt; int64_t total;
+};
+
+struct GradKArgs {
+    const void* q; const void* k; const void* alpha; const void* b;
+    const float* gsc;
+    void* dq; void* dk_out; void* dalpha; void* db;
+    int64_t B, T, H; int dk, nt; int64_t total;
 };
 
 struct PlanArgs {
@@ -88,6 +111,9 @@ hipError_t launch_varlen_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_chunk_state_bwd(const BwdStateArgs& a, bool bf16, hipStream_t s);
 int state_bwd_slice(int dv);
 hipError_t launch_chunk_grad(const GradArgs& a, bool bf16, bool gbf16, hipStream_t s);
+hipError_t launch_chunk_grad_mf(const GradVArgs& v, const GradKArgs& k, bool gbf16, hipStream_t s);
+bool gradmf_supported(int dk, int dv, bool bf16);
+int64_t gradmf_scratch_bytes(int dk, int64_t total);
 // workgroups of the gradient launch and the bytes of its scratch
 int64_t grad_blocks(int64_t total);
 int64_t chunk_grad_scratch_bytes(int dk, int dv, int64_t total);

@@ -5,7 +5,9 @@ with respect to q, k, v, alpha, b, w and S0; the oracle
 (``oracle.backward.recurrent_bwd``, pinned by finite differences of the
 forward) computes them in fp64 from the same inputs (bf16 widened exactly).
 Relative L2 error per gradient tensor: <= 1e-4 with fp32 I/O, <= 2e-2 with
-bf16 I/O (the forward's operands are bf16 there).
+bf16 I/O (the forward's operands are bf16 there).  The bf16 cases with dk in
+{32, 64, 128} and dv in {32, 64, 128} run the matrix-core gradient kernels,
+the others the vector-ALU ones.
 """
 import numpy as np
 import pytest
@@ -75,6 +77,10 @@ CASES = [
     (1, 47, 2, 32, 48, BF16, BF16, None, True, 1.0),
     (1, 200, 1, 128, 256, BF16, F32, 0.05, False, 2.0),
     (1, 1, 2, 128, 128, BF16, F32, 0.05, True, 1.0),
+    (2, 150, 2, 64, 64, BF16, BF16, 0.05, True, 2.0),
+    (1, 97, 3, 32, 96, BF16, F32, None, True, 1.0),
+    (1, 64, 2, 128, 32, BF16, BF16, 0.05, False, 1.0),
+    (2, 80, 2, 32, 64, BF16, F32, 0.05, True, 2.0),
 ]
 
 
