@@ -69,31 +69,44 @@ template <typename T> __device__ inline void gs(T* p, int64_t i, float x) { p[i]
 __host__ __device__ inline int64_t gradmf_scratch_floats(int dk) { return 3 * 64 * (int64_t)dk + 2 * 4096 + dk; }
 
 // G[r][c] = sum of log alpha over tokens 0..r of the chunk (alpha = 1 past its
-// end), for 256 threads: logs in parallel, then a scan of 256/dk segments per
-// channel with the segment totals carried through `tot`
-template <typename Tg>
+// end), for 256 threads: logs in parallel (every load issued before the first
+// use), then a scan of 256/DK segments per channel with the segment totals
+// carried through `tot`
+template <int DK, typename Tg>
 __device__ __attribute__((always_inline)) inline void cum_log_decay(float* G, float* tot, const Tg* alpha,
-                                                                    int64_t row0, int64_t H, int dk, int Ln)
+                                                                    int64_t row0, int64_t H, int Ln)
 {
+    constexpr int NV = 64 * DK / 4 / kThreads;
     const int tid = threadIdx.x;
-    for (int i = tid; i < 64 * dk; i += kThreads) {
-        const int r = i / dk, c = i - r * dk;
-        G[i] = r < Ln ? __logf(gf(alpha, (row0 + r * H) * dk + c)) : 0.f;
+    f32x4 x[NV];
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+        const int i = tid + u * kThreads, r = i / (DK / 4), c4 = 4 * (i - r * (DK / 4));
+        x[u] = r < Ln ? ld_gate4(alpha + (row0 + r * H) * DK + c4) : f32x4{1.f, 1.f, 1.f, 1.f};
+    }
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+        const int i = tid + u * kThreads, r = i / (DK / 4), c4 = 4 * (i - r * (DK / 4));
+        f32x4 l;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) l[e] = __logf(x[u][e]);
+        *reinterpret_cast<f32x4*>(&G[r * DK + c4]) = l;
     }
     __syncthreads();
-    const int nseg = kThreads / dk, sl = 64 / nseg;
-    const int c = tid % dk, g = tid / dk;
+    constexpr int nseg = kThreads / DK, sl = 64 / nseg;
+    const int c = tid % DK, g = tid / DK;
     float run = 0.f;
+#pragma unroll 8
     for (int r = g * sl; r < (g + 1) * sl; ++r) {
-        run += G[r * dk + c];
-        G[r * dk + c] = run;
+        run += G[r * DK + c];
+        G[r * DK + c] = run;
     }
-    tot[g * dk + c] = run;
+    tot[g * DK + c] = run;
     __syncthreads();
     float carry = 0.f;
-    for (int h = 0; h < g; ++h) carry += tot[h * dk + c];
+    for (int h = 0; h < g; ++h) carry += tot[h * DK + c];
     if (g > 0)
-        for (int r = g * sl; r < (g + 1) * sl; ++r) G[r * dk + c] += carry;
+        for (int r = g * sl; r < (g + 1) * sl; ++r) G[r * DK + c] += carry;
     __syncthreads();
 }
 
@@ -238,15 +251,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
 #pragma unroll
         for (int e = 0; e < 8; ++e) dOtl[(j0 + e) * LT + r] = x[e];
     }
-    cum_log_decay(Gl, tot, agt, row0, H, DK, Ln);
-    for (int i = tid; i < 64 * DK; i += kThreads) {                // Eh = Gamma b k
-        const int r = i / DK, c = i - r * DK;
-        float x = 0.f;
-        if (r < Ln) {
-            const int64_t o = (row0 + r * H) * DK + c;
-            x = __expf(Gl[i]) * gf(bgt, o) * gf(kg, o);
+    cum_log_decay<DK>(Gl, tot, agt, row0, H, Ln);
+    {                                                              // Eh = Gamma b k
+        constexpr int NV = 64 * DK / 4 / kThreads;
+        f32x4 bx[NV], kx[NV];
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int i = tid + u * kThreads, r = i / (DK / 4), c4 = 4 * (i - r * (DK / 4));
+            const int64_t o = (row0 + r * H) * DK + c4;
+            bx[u] = r < Ln ? ld_gate4(bgt + o) : f32x4{0.f, 0.f, 0.f, 0.f};
+            kx[u] = r < Ln ? ld_vec4(kg + o) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        Ehl[r * ldk + c] = (bf)x;
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int i = tid + u * kThreads, r = i / (DK / 4), c4 = 4 * (i - r * (DK / 4));
+            const f32x4 g4 = *reinterpret_cast<const f32x4*>(&Gl[r * DK + c4]);
+            f32x4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = __expf(g4[e]) * bx[u][e] * kx[u][e];
+            st_vec4(Ehl + r * ldk + c4, x);
+        }
     }
     __syncthreads();
 
@@ -369,14 +393,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
     }
     __syncthreads();
     // ---- u = w v (padding tokens 0) ----------------------------------------------
-    for (int i = tid; i < 64 * DV; i += kThreads) {
-        const int r = i / DV, j = i - r * DV;
-        float x = 0.f;
-        if (r < Ln) {
-            const int64_t o = (row0 + r * H) * DV + j;
-            x = gf(wgt, o) * gf(vg, o);
+    {
+        constexpr int NV = 64 * DV / 4 / kThreads;
+        f32x4 wx[NV], vx[NV];
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int i = tid + u * kThreads, r = i / (DV / 4), j4 = 4 * (i - r * (DV / 4));
+            const int64_t o = (row0 + r * H) * DV + j4;
+            wx[u] = r < Ln ? ld_gate4(wgt + o) : f32x4{0.f, 0.f, 0.f, 0.f};
+            vx[u] = r < Ln ? ld_vec4(vg + o) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        ul[r * ldv + j] = (bf)x;
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int i = tid + u * kThreads, r = i / (DV / 4), j4 = 4 * (i - r * (DV / 4));
+            st_vec4(ul + r * ldv + j4, wx[u] * vx[u]);
+        }
     }
     __syncthreads();
     // ---- dT = dDelta u^T + dW Eh^T (stored transposed);  dEh = T^T dW ------------
@@ -485,23 +516,46 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
     const float* s_dA = s_dP + 4096;
     const float* s_dGL = s_dA + 4096;
 
-    for (int i = tid; i < 4096 / 4; i += kThreads) {
-        *reinterpret_cast<f32x4*>(&dA[4 * i]) = *reinterpret_cast<const f32x4*>(s_dA + 4 * i);
-        *reinterpret_cast<f32x4*>(&dP[4 * i]) = *reinterpret_cast<const f32x4*>(s_dP + 4 * i);
-    }
-    cum_log_decay(G, tot, agt, row0, H, DK, Ln);
-    for (int i = tid; i < 64 * DK; i += kThreads) {
-        const int r = i / DK, c = i - r * DK;
-        float kv = 0.f, qv = 0.f, bv = 0.f;
-        if (r < Ln) {
-            const int64_t o = (row0 + r * H) * DK + c;
-            kv = gf(kg, o);
-            qv = gf(qg, o);
-            bv = gf(bgt, o);
+    {
+        f32x4 xa[4], xp[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = tid + u * kThreads;
+            xa[u] = *reinterpret_cast<const f32x4*>(s_dA + 4 * i);
+            xp[u] = *reinterpret_cast<const f32x4*>(s_dP + 4 * i);
         }
-        KY[i] = (bf)(kv * __expf(G[(r & ~15) * DK + c] - G[i]));
-        E[i] = (bf)(bv * kv);
-        Q[i] = (bf)qv;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = tid + u * kThreads;
+            *reinterpret_cast<f32x4*>(&dA[4 * i]) = xa[u];
+            *reinterpret_cast<f32x4*>(&dP[4 * i]) = xp[u];
+        }
+    }
+    cum_log_decay<DK>(G, tot, agt, row0, H, Ln);
+    {
+        constexpr int NV = 64 * DK / 4 / kThreads;
+        f32x4 kx[NV], qx[NV], bx[NV];
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int i = tid + u * kThreads, r = i / (DK / 4), c4 = 4 * (i - r * (DK / 4));
+            const int64_t o = (row0 + r * H) * DK + c4;
+            const bool ok = r < Ln;
+            kx[u] = ok ? ld_vec4(kg + o) : f32x4{0.f, 0.f, 0.f, 0.f};
+            qx[u] = ok ? ld_vec4(qg + o) : f32x4{0.f, 0.f, 0.f, 0.f};
+            bx[u] = ok ? ld_gate4(bgt + o) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int i = tid + u * kThreads, r = i / (DK / 4), c4 = 4 * (i - r * (DK / 4));
+            const f32x4 g4 = *reinterpret_cast<const f32x4*>(&G[r * DK + c4]);
+            const f32x4 gj = *reinterpret_cast<const f32x4*>(&G[(r & ~15) * DK + c4]);
+            f32x4 ky;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ky[e] = kx[u][e] * __expf(gj[e] - g4[e]);
+            st_vec4(KY + r * DK + c4, ky);
+            st_vec4(E + r * DK + c4, bx[u] * kx[u]);
+            st_vec4(Q + r * DK + c4, qx[u]);
+        }
     }
     __syncthreads();
 
@@ -545,45 +599,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
                 dqP[rr][cc] += pp[rr][cc] * xr;
             }
     }
-    // gradients that need only the row side; partial dk and dG
-    float dkp[R][4], dGp[R][4];
-    {
-        float ex[4] = {0.f, 0.f, 0.f, 0.f};
-        bf* dq = static_cast<bf*>(a.dq);
-        Tg* db = static_cast<Tg*>(a.db);
-#pragma unroll
-        for (int rr = 0; rr < R; ++rr) {
-            const int r = r0 + rr;
-            const bool ok = r < Ln;
-            const int64_t o = (row0 + r * H) * DK + c0;
-            const f32x4 dQh = *reinterpret_cast<const f32x4*>(s_dQh + r * DK + c0);
-            const f32x4 dEh = *reinterpret_cast<const f32x4*>(s_dEh + r * DK + c0);
-            const f32x4 dKt = *reinterpret_cast<const f32x4*>(s_dKt + r * DK + c0);
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-                const int c = c0 + cc;
-                float qv = 0.f, kv = 0.f, bv = 0.f;
-                if (ok) {
-                    qv = gf(qg, o + cc);
-                    kv = gf(kg, o + cc);
-                    bv = gf(bgt, o + cc);
-                }
-                const float g = G[r * DK + c], gam = __expf(g), kt = __expf(G[63 * DK + c] - g);
-                const float ev = bv * kv;
-                const float de = gam * dEh[cc] + deA[rr][cc];
-                if (ok) {
-                    gs(dq, o + cc, gam * dQh[cc] + dqP[rr][cc]);
-                    gs(db, o + cc, de * kv);
-                }
-                dkp[rr][cc] = kt * dKt[cc] + de * bv;
-                dGp[rr][cc] = dQh[cc] * gam * qv + dEh[cc] * gam * ev - dKt[cc] * kv * kt + ev * deA[rr][cc] +
-                              qv * dqP[rr][cc];
-                ex[cc] += dKt[cc] * kv * kt;
-            }
-        }
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) ext[(tid / CG) * DK + c0 + cc] = ex[cc];
-    }
     // column side: sum over later rows r of dA[r,s] e_r R[r,s] (and dP with q)
     float dkA[R][4], dkP[R][4];
 #pragma unroll
@@ -592,11 +607,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
         for (int cc = 0; cc < 4; ++cc) dkA[rr][cc] = dkP[rr][cc] = 0.f;
     {
         const int j0 = 16 * J0;
+        const f32x4 gj = *reinterpret_cast<const f32x4*>(&G[j0 * DK + c0]);
         for (int r = j0; r < 64; ++r) {
             const f32x4 e4 = IOB::unpack4(*reinterpret_cast<const bf16x4*>(&E[r * DK + c0]));
             const f32x4 q4 = IOB::unpack4(*reinterpret_cast<const bf16x4*>(&Q[r * DK + c0]));
             const f32x4 g4 = *reinterpret_cast<const f32x4*>(&G[r * DK + c0]);
-            const f32x4 gj = *reinterpret_cast<const f32x4*>(&G[j0 * DK + c0]);
             f32x4 ea, qa;
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) {
@@ -631,39 +646,99 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
         }
     }
     __syncthreads();                                       // KY and E are read for the last time
+    // per row: the gradients of q, k, b and dG; the next row's inputs are
+    // requested before this row's results are stored
     {
+        bf* dq = static_cast<bf*>(a.dq);
         bf* dk_out = static_cast<bf*>(a.dk_out);
+        Tg* db = static_cast<Tg*>(a.db);
         const int j0 = 16 * J0;
+        float ex[4] = {0.f, 0.f, 0.f, 0.f};
+        struct RowIn {
+            f32x4 q, k, b, dQh, dEh, dKt;
+        };
+        auto load = [&](int rr) {
+            RowIn x;
+            const int r = r0 + rr;
+            x.dQh = *reinterpret_cast<const f32x4*>(s_dQh + r * DK + c0);
+            x.dEh = *reinterpret_cast<const f32x4*>(s_dEh + r * DK + c0);
+            x.dKt = *reinterpret_cast<const f32x4*>(s_dKt + r * DK + c0);
+            if (r < Ln) {
+                const int64_t o = (row0 + r * H) * DK + c0;
+                x.q = ld_vec4(qg + o);
+                x.k = ld_vec4(kg + o);
+                x.b = ld_gate4(bgt + o);
+            } else {
+                x.q = x.k = x.b = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            return x;
+        };
+        RowIn nx = load(0);
 #pragma unroll
         for (int rr = 0; rr < R; ++rr) {
-            const int s = r0 + rr;
-            const int64_t o = (row0 + s * H) * DK + c0;
+            const RowIn cx = nx;
+            if (rr + 1 < R) nx = load(rr + 1);
+            const int r = r0 + rr;
+            f32x4 oq, ok, ob;
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) {
                 const int c = c0 + cc;
-                const float y = __expf(G[j0 * DK + c] - G[s * DK + c]);
-                const float ka = dkA[rr][cc] * y, kp = dkP[rr][cc] * y;
-                const float kv = s < Ln ? gf(kg, o + cc) : 0.f;
-                if (s < Ln) gs(dk_out, o + cc, dkp[rr][cc] + ka + kp);
-                dG[s * DK + c] = dGp[rr][cc] - kv * (ka + kp);
+                const float g = G[r * DK + c], gam = __expf(g), kt = __expf(G[63 * DK + c] - g);
+                const float y = __expf(G[j0 * DK + c] - g);
+                const float qv = cx.q[cc], kv = cx.k[cc], bv = cx.b[cc], ev = bv * kv;
+                const float de = gam * cx.dEh[cc] + deA[rr][cc];
+                const float kak = (dkA[rr][cc] + dkP[rr][cc]) * y;
+                oq[cc] = gam * cx.dQh[cc] + dqP[rr][cc];
+                ok[cc] = kt * cx.dKt[cc] + de * bv + kak;
+                ob[cc] = de * kv;
+                dG[r * DK + c] = cx.dQh[cc] * gam * qv + cx.dEh[cc] * gam * ev - cx.dKt[cc] * kv * kt +
+                                 ev * deA[rr][cc] + qv * dqP[rr][cc] - kv * kak;
+                ex[cc] += cx.dKt[cc] * kv * kt;
+            }
+            if (r < Ln) {
+                const int64_t o = (row0 + r * H) * DK + c0;
+                st_vec4(dq + o, oq);
+                st_vec4(dk_out + o, ok);
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) gs(db, o + cc, ob[cc]);
             }
         }
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) ext[(tid / CG) * DK + c0 + cc] = ex[cc];
     }
     __syncthreads();
-    // dlog(alpha): reverse cumulative sum of dG; the last token also carries the
-    // uses of Gamma_L (the state decay over the chunk and Ktil)
+    // dlog(alpha) = reverse cumulative sum of dG; the last token also carries
+    // the uses of Gamma_L (the state decay over the chunk and Ktil)
+    if (tid < DK) {
+        float x = s_dGL[tid] * __expf(G[63 * DK + tid]);
+        for (int g = 0; g < kThreads / CG; ++g) x += ext[g * DK + tid];
+        dG[63 * DK + tid] += x;
+    }
+    __syncthreads();
+    {
+        const int nseg = kThreads / DK, sl = 64 / nseg;
+        const int c = tid % DK, g = tid / DK;
+        float run = 0.f;
+        for (int r = (g + 1) * sl - 1; r >= g * sl; --r) {
+            run += dG[r * DK + c];
+            dG[r * DK + c] = run;
+        }
+        tot[g * DK + c] = run;
+        __syncthreads();
+        float carry = 0.f;
+        for (int h = g + 1; h < nseg; ++h) carry += tot[h * DK + c];
+        if (g + 1 < nseg)
+            for (int r = g * sl; r < (g + 1) * sl; ++r) dG[r * DK + c] += carry;
+    }
+    __syncthreads();
     {
         Tg* dalpha = static_cast<Tg*>(a.dalpha);
-        for (int c = tid; c < DK; c += kThreads) {
-            float acc = s_dGL[c] * __expf(G[63 * DK + c]);
-            for (int g = 0; g < kThreads / CG; ++g) acc += ext[g * DK + c];
-            for (int r = 63; r >= 0; --r) {
-                acc += dG[r * DK + c];
-                if (r < Ln) {
-                    const int64_t o = (row0 + r * H) * DK + c;
-                    gs(dalpha, o, acc / gf(agt, o));
-                }
-            }
+        for (int i = tid; i < Ln * (DK / 4); i += kThreads) {
+            const int r = i / (DK / 4), c4 = 4 * (i - r * (DK / 4));
+            const int64_t o = (row0 + r * H) * DK + c4;
+            const f32x4 al = ld_gate4(agt + o);
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) gs(dalpha, o + cc, dG[r * DK + c4 + cc] / al[cc]);
         }
     }
 }
