@@ -150,6 +150,24 @@ __device__ __attribute__((always_inline)) inline void tiles(int wave, int NT, FF
     }
 }
 
+// Column panels p = wave, wave + 4, ... < NP of products whose B operand
+// (NKB K-blocks of one 16-column panel) comes from global memory: fetch(p, b)
+// loads it once, body(p, b) runs the panel's row tiles with A from LDS.  The
+// next panel's B is requested before the current panel's products.
+template <int NKB, typename FF, typename FB>
+__device__ __attribute__((always_inline)) inline void panels(int wave, int NP, FF fetch, FB body)
+{
+    bfrag cb[NKB], nb[NKB];
+    int p = wave;
+    if (p < NP) fetch(p, nb);
+    for (; p < NP; p += 4) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) cb[kb] = nb[kb];
+        if (p + 4 < NP) fetch(p + 4, nb);
+        body(p, cb);
+    }
+}
+
 template <int DK, int DV, typename Tg>
 __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
 {
@@ -274,76 +292,94 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
     }
     __syncthreads();
 
-    // ---- Delta = U - W S0 (in place over U) ----------------------------------------
-    tiles<NKK>(wave, 4 * NTV,
-               [&](int t, bfrag (&fa)[NKK], bfrag (&fb)[NKK]) {
-                   const int tr = t / NTV, tn = t - tr * NTV;
+    // ---- Delta = U - W S0 (in place over U): W for all row tiles in registers,
+    // S0^T one 16-column panel at a time ------------------------------------------
+    {
+        bfrag wa[4][NKK];
 #pragma unroll
-                   for (int kb = 0; kb < NKK; ++kb) {
-                       fa[kb] = fr(Wg, 16 * tr + l16, DK, kb, grp);
-                       fb[kb] = fr(S0t, 16 * tn + l16, DK, kb, grp);
-                   }
-               },
-               [&](int t, f32x4 acc) {
-                   const int tr = t / NTV, tn = t - tr * NTV;
-                   const int r = 16 * tr + 4 * grp, j = 16 * tn + l16;
+        for (int tr = 0; tr < 4; ++tr)
 #pragma unroll
-                   for (int i = 0; i < 4; ++i) {
-                       bf* d = &Dll[(r + i) * ldv + j];
-                       *d = (bf)((float)*d - acc[i]);
-                   }
-               });
+            for (int kb = 0; kb < NKK; ++kb) wa[tr][kb] = fr(Wg, 16 * tr + l16, DK, kb, grp);
+        panels<NKK>(wave, NTV,
+                    [&](int tn, bfrag (&fb)[NKK]) {
+#pragma unroll
+                        for (int kb = 0; kb < NKK; ++kb) fb[kb] = fr(S0t, 16 * tn + l16, DK, kb, grp);
+                    },
+                    [&](int tn, bfrag (&fb)[NKK]) {
+                        const int j = 16 * tn + l16;
+#pragma unroll
+                        for (int tr = 0; tr < 4; ++tr) {
+                            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int kb = 0; kb < NKK; ++kb) acc = IOB::mma(acc, wa[tr][kb], fb[kb]);
+                            const int r = 16 * tr + 4 * grp;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                bf* d = &Dll[(r + i) * ldv + j];
+                                *d = (bf)((float)*d - acc[i]);
+                            }
+                        }
+                    });
+    }
     // ---- dDelta = P^T dO + Ktil dSL ----------------------------------------------
-    tiles<2 + NKK>(wave, 4 * NTV,
-                   [&](int t, bfrag (&fa)[2 + NKK], bfrag (&fb)[2 + NKK]) {
-                       const int tr = t / NTV, tn = t - tr * NTV;
+    panels<NKK>(wave, NTV,
+                [&](int tn, bfrag (&fb)[NKK]) {
 #pragma unroll
-                       for (int kb = 0; kb < 2; ++kb) {
-                           fa[kb] = fr(Ptl, 16 * tr + l16, LT, kb, grp);
-                           fb[kb] = fr(dOtl, 16 * tn + l16, LT, kb, grp);
-                       }
+                    for (int kb = 0; kb < NKK; ++kb) fb[kb] = fr(dSLt, 16 * tn + l16, DK, kb, grp);
+                },
+                [&](int tn, bfrag (&fb)[NKK]) {
+                    const int j = 16 * tn + l16;
+                    const bfrag o0 = fr(dOtl, j, LT, 0, grp), o1 = fr(dOtl, j, LT, 1, grp);
 #pragma unroll
-                       for (int kb = 0; kb < NKK; ++kb) {
-                           fa[2 + kb] = fr(Ktl, 16 * tr + l16, ldk, kb, grp);
-                           fb[2 + kb] = fr(dSLt, 16 * tn + l16, DK, kb, grp);
-                       }
-                   },
-                   [&](int t, f32x4 acc) {
-                       const int tr = t / NTV, tn = t - tr * NTV;
-                       const int r = 16 * tr + 4 * grp, j = 16 * tn + l16;
+                    for (int tr = 0; tr < 4; ++tr) {
+                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                        acc = IOB::mma(acc, fr(Ptl, 16 * tr + l16, LT, 0, grp), o0);
+                        acc = IOB::mma(acc, fr(Ptl, 16 * tr + l16, LT, 1, grp), o1);
 #pragma unroll
-                       for (int i = 0; i < 4; ++i) dDl[(r + i) * ldv + j] = (bf)acc[i];
-                       st_vec4(dDtl + j * LT + r, acc);
-                   });
+                        for (int kb = 0; kb < NKK; ++kb) acc = IOB::mma(acc, fr(Ktl, 16 * tr + l16, ldk, kb, grp), fb[kb]);
+                        const int r = 16 * tr + 4 * grp;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) dDl[(r + i) * ldv + j] = (bf)acc[i];
+                        st_vec4(dDtl + j * LT + r, acc);
+                    }
+                });
     __syncthreads();
-    // ---- dQh = dO S0^T, dKtil = Delta dSL^T, dW = -dDelta S0^T ---------------------
-    tiles<NKV>(wave, 3 * 4 * NTK,
-               [&](int t, bfrag (&fa)[NKV], bfrag (&fb)[NKV]) {
-                   const int which = t / (4 * NTK), u = t - which * 4 * NTK, tr = u / NTK, tn = u - tr * NTK;
-                   const bf* A = which == 0 ? dOl : (which == 1 ? Dll : dDl);
-                   const float* B = which == 1 ? dSL : S0;
+    // ---- dQh = dO S0^T and dW = -dDelta S0^T (one pass over S0), dKtil = Delta dSL^T
+    panels<NKV>(wave, 2 * NTK,
+                [&](int p, bfrag (&fb)[NKV]) {
+                    const float* B = p < NTK ? S0 : dSL;
+                    const int tn = p < NTK ? p : p - NTK;
 #pragma unroll
-                   for (int kb = 0; kb < NKV; ++kb) {
-                       fa[kb] = fr(A, 16 * tr + l16, ldv, kb, grp);
-                       fb[kb] = fr32(B, 16 * tn + l16, DV, kb, grp);
-                   }
-               },
-               [&](int t, f32x4 acc) {
-                   const int which = t / (4 * NTK), u = t - which * 4 * NTK, tr = u / NTK, tn = u - tr * NTK;
-                   const int r = 16 * tr + 4 * grp, c = 16 * tn + l16;
-                   if (which == 0) {
+                    for (int kb = 0; kb < NKV; ++kb) fb[kb] = fr32(B, 16 * tn + l16, DV, kb, grp);
+                },
+                [&](int p, bfrag (&fb)[NKV]) {
+                    const int tn = p < NTK ? p : p - NTK, c = 16 * tn + l16;
 #pragma unroll
-                       for (int i = 0; i < 4; ++i) s_dQh[(r + i) * DK + c] = acc[i];
-                   } else if (which == 1) {
+                    for (int tr = 0; tr < 4; ++tr) {
+                        const int r = 16 * tr + 4 * grp;
+                        if (p < NTK) {
+                            f32x4 aq = {0.f, 0.f, 0.f, 0.f}, aw = aq;
 #pragma unroll
-                       for (int i = 0; i < 4; ++i) s_dKt[(r + i) * DK + c] = acc[i];
-                   } else {
-                       acc = -acc;
+                            for (int kb = 0; kb < NKV; ++kb) {
+                                aq = IOB::mma(aq, fr(dOl, 16 * tr + l16, ldv, kb, grp), fb[kb]);
+                                aw = IOB::mma(aw, fr(dDl, 16 * tr + l16, ldv, kb, grp), fb[kb]);
+                            }
+                            aw = -aw;
 #pragma unroll
-                       for (int i = 0; i < 4; ++i) dWl[(r + i) * ldk + c] = (bf)acc[i];
-                       st_vec4(dWtl + c * LT + r, acc);
-                   }
-               });
+                            for (int i = 0; i < 4; ++i) {
+                                s_dQh[(r + i) * DK + c] = aq[i];
+                                dWl[(r + i) * ldk + c] = (bf)aw[i];
+                            }
+                            st_vec4(dWtl + c * LT + r, aw);
+                        } else {
+                            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int kb = 0; kb < NKV; ++kb) acc = IOB::mma(acc, fr(Dll, 16 * tr + l16, ldv, kb, grp), fb[kb]);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) s_dKt[(r + i) * DK + c] = acc[i];
+                        }
+                    }
+                });
     // ---- dP = mask(dO Delta^T) -------------------------------------------------------
     tiles<NKV>(wave, 16,
                [&](int t, bfrag (&fa)[NKV], bfrag (&fb)[NKV]) {
