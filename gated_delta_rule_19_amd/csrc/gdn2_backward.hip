@@ -165,8 +165,9 @@ template <typename T> __device__ inline void stf(T* p, int64_t i, float x) { p[i
 // (Qh, W, Ktil^T, P, Gamma_L: everything before U^T) into an LDS image,
 // with the chunk's dO columns behind it; the copy of chunk n-1 is loaded
 // into registers (16-byte granules) while chunk n is computed.  The state
-// gradient dS [DK][VS] and dDelta [64][VS] stay in LDS in fp32; each thread
-// accumulates a small output tile with fp32 FMAs.
+// gradient dS [DK][VS] and dDelta [64][VS] stay in LDS in fp32; the two
+// products per chunk run on the matrix cores (fp32 accumulation), their
+// fragments gathered element by element from the LDS image.
 // ---------------------------------------------------------------------------
 template <typename Tio, int DK>
 struct BwdStateLds {
@@ -184,10 +185,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_state_bwd(BwdStateArgs a)
     constexpr int GROW = VS * ES / 16;                     // granules of one dO row slice
     constexpr int NG = IMG / 16 + 64 * GROW;                // granules per chunk
     constexpr int NPT = (NG + kThreads - 1) / kThreads;
-    constexpr int TR = VS / 16;                             // dDelta rows per thread (x 4 columns)
-    constexpr int TC = DK * VS / 1024 > 0 ? DK * VS / 1024 : 1;   // dS rows per thread (x 4 columns)
     constexpr int NCG = VS / 4;                             // column groups
-    static_assert(IMG % 16 == 0 && TR >= 1, "layout");
+    using IO = Io<Tio>;
+    typedef typename IO::frag frag;
+    constexpr int EPL = IO::EPL, KB = IO::KB;
+    static_assert(IMG % 16 == 0 && VS == 16, "layout: the slice is one 16-column tile");
 
     __shared__ __attribute__((aligned(16))) char img[IMG + 64 * VS * ES];
     __shared__ __attribute__((aligned(16))) float dS[DK * VS];
@@ -199,8 +201,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_state_bwd(BwdStateArgs a)
     const float* gam = reinterpret_cast<const float*>(img + SL::LY.gaml);
     const Tio* dOs = reinterpret_cast<const Tio*>(img + IMG);          // [64][VS]
 
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4, wave = tid >> 6;
     const int dv = a.dv, nt = a.nt;
+    f32x4 accD = {0.f, 0.f, 0.f, 0.f};
     // the slices of one head get block ids congruent mod 8 (one XCD, one L2
     // for the head's factors)
     const int64_t nch = a.B * a.H, x = blockIdx.x;
@@ -271,66 +274,59 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_state_bwd(BwdStateArgs a)
         }
         if (n > 0) fetch(n - 1);
         __syncthreads();
-        // dDelta = P^T dO + Ktil dS: rows r0 .. r0+TR-1, columns 4cg .. 4cg+3
+        // dDelta = P^T dO + Ktil dS on the matrix cores: wave w owns rows
+        // 16w .. 16w+15 (the slice is one 16-column tile); operand fragments are
+        // gathered from the LDS image (P and Ktil^T are stored with the
+        // contraction index outermost)
         {
-            const int cg = tid % NCG, r0 = (tid / NCG) * TR;
-            float acc[TR][4];
 #pragma unroll
-            for (int i = 0; i < TR; ++i)
+            for (int kb = 0; kb < 64 / KB; ++kb) {
+                frag fa, fb;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-#pragma unroll 8
-            for (int s = 0; s < 64; ++s) {
-                const f32x4 o = ld_vec4(dOs + s * VS + 4 * cg);
-#pragma unroll
-                for (int i = 0; i < TR; ++i) {
-                    const float p = Io<Tio>::to_f(P[s * 64 + r0 + i]);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[i][j] += p * o[j];
+                for (int e = 0; e < EPL; ++e) {
+                    const int k = kb * KB + grp * EPL + e;
+                    fa[e] = P[k * 64 + 16 * wave + l16];
+                    fb[e] = dOs[k * VS + l16];
                 }
-            }
-#pragma unroll 8
-            for (int c = 0; c < DK; ++c) {
-                const f32x4 d = *reinterpret_cast<const f32x4*>(&dS[c * VS + 4 * cg]);
-#pragma unroll
-                for (int i = 0; i < TR; ++i) {
-                    const float k = Io<Tio>::to_f(Kt[c * 64 + r0 + i]);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[i][j] += k * d[j];
-                }
+                accD = IO::mma(accD, fa, fb);
             }
 #pragma unroll
-            for (int i = 0; i < TR; ++i)
-                *reinterpret_cast<f32x4*>(&dD[(r0 + i) * VS + 4 * cg]) = f32x4{acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
+            for (int kb = 0; kb < (DK + KB - 1) / KB; ++kb) {
+                frag fa, fb;
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) {
+                    const int k = kb * KB + grp * EPL + e;
+                    fa[e] = k < DK ? Kt[k * 64 + 16 * wave + l16] : IO::from_f(0.f);
+                    fb[e] = IO::from_f(k < DK ? dS[k * VS + l16] : 0.f);
+                }
+                accD = IO::mma(accD, fa, fb);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dD[(16 * wave + 4 * grp + i) * VS + l16] = accD[i];
+            accD = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         __syncthreads();
-        // dS = Gamma_L dS + Qh^T dO - W^T dDelta: rows c0 .. c0+TC-1, columns 4cg ..
-        if (tid < DK / TC * NCG) {
-            const int cg = tid % NCG, c0 = (tid / NCG) * TC;
-            float acc[TC][4];
+        // dS = Gamma_L dS + Qh^T dO - W^T dDelta: 16-row tiles of dS, one per wave in turn
+        for (int tc = wave; tc < DK / 16; tc += 4) {
+            f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1;
 #pragma unroll
-            for (int i = 0; i < TC; ++i)
+            for (int kb = 0; kb < 64 / KB; ++kb) {
+                frag fq, fw, fo, fd;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-#pragma unroll 8
-            for (int r = 0; r < 64; ++r) {
-                const f32x4 o = ld_vec4(dOs + r * VS + 4 * cg);
-                const f32x4 d = *reinterpret_cast<const f32x4*>(&dD[r * VS + 4 * cg]);
-#pragma unroll
-                for (int i = 0; i < TC; ++i) {
-                    const float qv = Io<Tio>::to_f(Qh[r * KPAD + c0 + i]);
-                    const float wv = Io<Tio>::to_f(Wf[r * KPAD + c0 + i]);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[i][j] += qv * o[j] - wv * d[j];
+                for (int e = 0; e < EPL; ++e) {
+                    const int k = kb * KB + grp * EPL + e;
+                    fq[e] = Qh[k * KPAD + 16 * tc + l16];
+                    fw[e] = Wf[k * KPAD + 16 * tc + l16];
+                    fo[e] = dOs[k * VS + l16];
+                    fd[e] = IO::from_f(dD[k * VS + l16]);
                 }
+                a1 = IO::mma(a1, fq, fo);
+                a2 = IO::mma(a2, fw, fd);
             }
 #pragma unroll
-            for (int i = 0; i < TC; ++i) {
-                f32x4 x = *reinterpret_cast<const f32x4*>(&dS[(c0 + i) * VS + 4 * cg]);
-                const float gm = gam[c0 + i];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) x[j] = gm * x[j] + acc[i][j];
-                *reinterpret_cast<f32x4*>(&dS[(c0 + i) * VS + 4 * cg]) = x;
+            for (int i = 0; i < 4; ++i) {
+                const int c = 16 * tc + 4 * grp + i;
+                dS[c * VS + l16] = gam[c] * dS[c * VS + l16] + a1[i] - a2[i];
             }
         }
     }
@@ -619,12 +615,8 @@ template <typename Tio, int DK>
 static hipError_t state_bwd_dk(const BwdStateArgs& a, hipStream_t s)
 {
     const dim3 grid((unsigned)(a.B * a.H * (int64_t)a.nslices));
-    if (a.vs == 32)
-        hipLaunchKernelGGL((k_chunk_state_bwd<Tio, DK, 32>), grid, dim3(kThreads), 0, s, a);
-    else if (a.vs == 16)
-        hipLaunchKernelGGL((k_chunk_state_bwd<Tio, DK, 16>), grid, dim3(kThreads), 0, s, a);
-    else
-        return hipErrorInvalidValue;
+    if (a.vs != 16) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_chunk_state_bwd<Tio, DK, 16>), grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
