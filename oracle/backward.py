@@ -60,7 +60,7 @@ import numpy as np
 
 from .reference import _f64
 
-__all__ = ["recurrent_bwd", "chunked_bwd", "loss"]
+__all__ = ["recurrent_bwd", "chunked_bwd", "full_bwd", "loss"]
 
 
 def loss(o, S, dO, dS_T=None):
@@ -206,3 +206,45 @@ def chunked_bwd(q, k, v, alpha, b, w, S0, dO, dS_T=None, chunk=64):
                 g["dw"][bi, sl, hi] = du * vc
                 g["dv"][bi, sl, hi] = du * wc
     return g
+
+
+def full_bwd(q, k, v, alpha, b, w, S0, dO, dS_T=None, flags=0):
+    """Gradients with the prologue options and grouped value heads, fp64.
+
+    The forward is: the prologue (``oracle.reference.prologue``: sigmoid of gate
+    logits, b x 2, q/k L2 norm), then, with more value heads than query/key
+    heads, the query/key heads shared by consecutive groups of value heads
+    (``oracle.reference.share_qk_heads``), then the recurrence.  The gradient
+    runs back through the three steps:
+      * ``recurrent_bwd`` on the activated, widened inputs;
+      * each query/key head gets the sum of its group's dq and dk;
+      * L2 norm: with n = sqrt(sum(x^2) + eps) and xh = x / n,
+        dx = (dxh - xh * sum(xh * dxh)) / n per (token, head);
+      * logits: dlogit = dgate * s (1 - s) with s = sigmoid(logit), times 2
+        for b in negative-eigenvalue mode.
+    q, k: [B, T, H, dk]; v, w: [B, T, Hv, dv]; alpha, b: [B, T, Hv, dk].
+    """
+    from .reference import FLAG_GATE_LOGITS, FLAG_NEG_EIGVAL, FLAG_QK_L2NORM, L2NORM_EPS, prologue, \
+        share_qk_heads, sigmoid
+    q, k, v, alpha, b, w, dO = map(_f64, (q, k, v, alpha, b, w, dO))
+    B, T, H, dk = q.shape
+    Hv = v.shape[2]
+    pq, pk, pa, pb, pw = prologue(q, k, alpha, b, w, flags)
+    qg, kg = share_qk_heads(pq, pk, Hv) if Hv != H else (pq, pk)
+    g = recurrent_bwd(qg, kg, v, pa, pb, pw, S0, dO, dS_T)
+    G = Hv // H
+    dq = g["dq"].reshape(B, T, H, G, dk).sum(axis=3)
+    dk_ = g["dk"].reshape(B, T, H, G, dk).sum(axis=3)
+    if flags & FLAG_QK_L2NORM:
+        def back(x, dxh):
+            n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + L2NORM_EPS)
+            xh = x / n
+            return (dxh - xh * np.sum(xh * dxh, axis=-1, keepdims=True)) / n
+        dq, dk_ = back(q, dq), back(k, dk_)
+    out = dict(dq=dq, dk=dk_, dv=g["dv"], dalpha=g["dalpha"], db=g["db"], dw=g["dw"], dS0=g["dS0"])
+    if flags & FLAG_GATE_LOGITS:
+        for name, x, scale in (("dalpha", alpha, 1.0), ("db", b, 2.0 if flags & FLAG_NEG_EIGVAL else 1.0),
+                               ("dw", w, 1.0)):
+            s = sigmoid(x)
+            out[name] = out[name] * s * (1.0 - s) * scale
+    return out

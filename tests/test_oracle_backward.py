@@ -131,3 +131,61 @@ def test_backward_slip_is_rejected(slip):
 def test_correct_reverse_passes_the_slip_harness():
     x, dO, dS = _draw(np.random.default_rng(5), T=4)
     _check_fd(_reverse_with_slip(None), x, dO, dS)
+
+
+# ---- prologue options and grouped value heads ------------------------------------
+def _fd_full(x, dO, dS, flags, h=1e-6):
+    """Central differences of loss(prologue -> shared heads -> recurrence) for every input."""
+    from oracle.reference import prologue, share_qk_heads
+    Hv = x["v"].shape[2]
+
+    def fwd(y):
+        pq, pk, pa, pb, pw = prologue(y["q"], y["k"], y["alpha"], y["b"], y["w"], flags)
+        if Hv != pq.shape[2]:
+            pq, pk = share_qk_heads(pq, pk, Hv)
+        o, S = recurrent(pq, pk, y["v"], pa, pb, pw, y["S0"])
+        return loss(o, S, dO, dS)
+    out = {}
+    for n in NAMES:
+        g = np.zeros_like(x[n])
+        for idx in np.ndindex(*x[n].shape):
+            vals = []
+            for s in (h, -h):
+                y = {m: a.copy() for m, a in x.items()}
+                y[n][idx] += s
+                vals.append(fwd(y))
+            g[idx] = (vals[0] - vals[1]) / (2 * h)
+        out["d" + n] = g
+    return out
+
+
+@pytest.mark.parametrize("flags,G", [(0, 2), (1, 1), (3, 1), (4, 1), (7, 2), (5, 3)])
+def test_full_bwd_matches_finite_differences(flags, G):
+    from oracle.backward import full_bwd
+    rng = np.random.default_rng(40 + flags + G)
+    B, T, H, dk, dv = 1, 5, 1, 3, 2
+    Hv = H * G
+    x = dict(q=rng.standard_normal((B, T, H, dk)) * 2, k=rng.standard_normal((B, T, H, dk)),
+             v=rng.standard_normal((B, T, Hv, dv)),
+             alpha=(rng.standard_normal((B, T, Hv, dk)) + 2) if flags & 1 else rng.uniform(0.5, 1, (B, T, Hv, dk)),
+             b=rng.standard_normal((B, T, Hv, dk)) if flags & 1 else rng.uniform(0, 2, (B, T, Hv, dk)),
+             w=rng.standard_normal((B, T, Hv, dv)) if flags & 1 else rng.uniform(0, 1, (B, T, Hv, dv)),
+             S0=rng.standard_normal((B, Hv, dk, dv)) * 0.5)
+    if not flags & 4:
+        x["k"] /= np.linalg.norm(x["k"], axis=-1, keepdims=True)
+    dO = rng.standard_normal((B, T, Hv, dv))
+    dS = rng.standard_normal((B, Hv, dk, dv))
+    fd = _fd_full(x, dO, dS, flags)
+    g = full_bwd(*(x[m] for m in NAMES), dO, dS, flags=flags)
+    for n in fd:
+        err = np.max(np.abs(g[n] - fd[n])) / max(1.0, np.max(np.abs(fd[n])))
+        assert err < 1e-7, f"{n}: {err:.2e}"
+
+
+def test_full_bwd_without_options_is_recurrent_bwd():
+    from oracle.backward import full_bwd
+    x, dO, dS = _draw(np.random.default_rng(9), T=7, dk=4, dv=3)
+    g1 = recurrent_bwd(*(x[m] for m in NAMES), dO, dS)
+    g2 = full_bwd(*(x[m] for m in NAMES), dO, dS, flags=0)
+    for n in g1:
+        np.testing.assert_array_equal(g1[n], g2[n])
