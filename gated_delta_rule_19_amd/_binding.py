@@ -280,17 +280,19 @@ def recurrent_varlen(q, k, v, alpha, b, w, cu_seqlens, S_in=None, *, o=None, S_o
     return o, S_out
 
 
-def chunk_bwd_workspace_size(B, T, H, dk, dv, io_dtype: torch.dtype, gate_dtype: torch.dtype = torch.float32) -> int:
-    p = problem(B, T, H, dk, dv, io_dtype, gate_dtype=gate_dtype)
+def chunk_bwd_workspace_size(B, T, H, dk, dv, io_dtype: torch.dtype, gate_dtype: torch.dtype = torch.float32,
+                             flags: int = 0, Hv: int = 0) -> int:
+    p = problem(B, T, H, dk, dv, io_dtype, gate_dtype=gate_dtype, flags=flags, Hv=Hv)
     return int(lib().gdn2_chunk_bwd_workspace_size(ctypes.byref(p)))
 
 
 def chunk_bwd(q, k, v, alpha, b, w, dO, S0=None, dS_T=None, *, want_dS0: bool = True, workspace=None,
               flags: int = 0):
-    """Backward of the chunked forward (``gdn2_chunk_bwd``): gradients of
-    sum(dO * o) + sum(dS_T * S_T) w.r.t. q, k, v, alpha, b, w (same shapes and dtypes as
-    the inputs) and S0 (float32, when ``want_dS0``).  Returns a dict dq, dk, dv, dalpha,
-    db, dw, dS0."""
+    """Backward of the chunked forward (``gdn2_chunk_bwd``) with the same ``flags`` and
+    head layout: gradients of sum(dO * o) + sum(dS_T * S_T) w.r.t. q, k, v, alpha, b, w
+    (same shapes and dtypes as the inputs; of the logits with FLAG_GATE_LOGITS, of the raw
+    q/k with FLAG_QK_L2NORM) and S0 (float32, when ``want_dS0``).  Returns a dict dq, dk,
+    dv, dalpha, db, dw, dS0."""
     p, dev = _problem_from(q, k, v, alpha, b, w, flags)
     _check_state(S0, p, dev, "S0")
     _check_state(dS_T, p, dev, "dS_T")

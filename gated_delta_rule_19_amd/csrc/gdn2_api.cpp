@@ -214,12 +214,88 @@ BwdLayout bwd_layout(const gdn2_problem* p)
     return l;
 }
 
-int check_bwd_problem(const gdn2_problem* p)
+// Prologue options and shared query/key heads in the backward: the core runs
+// with no flags and one query/key row per value head on inputs materialised in
+// workspace after its own (activated gates as fp32; q/k rows normalised and
+// widened to the value heads), and its gradients of those are mapped back.
+struct BwdWrap {
+    gdn2_problem core;     // the problem the core backward sees
+    BwdLayout l;           // its workspace layout
+    bool qk, gates;        // q/k rows materialised; gates activated
+    int64_t qh, kh, dqh, dkh, ga, gb, gw, dga, dgb, dgw, total;
+};
+
+BwdWrap bwd_wrap(const gdn2_problem* p)
 {
-    const int st = check_problem(p, true);
+    BwdWrap w{};
+    w.core = *p;
+    w.qk = (p->flags & GDN2_FLAG_QK_L2NORM) != 0 || nvh(p) != p->H;
+    w.gates = (p->flags & GDN2_FLAG_GATE_LOGITS) != 0;
+    w.core.flags = 0;
+    w.core.H = nvh(p);
+    w.core.Hv = 0;
+    if (w.gates) w.core.gate_dtype = GDN2_F32;
+    w.l = bwd_layout(&w.core);
+    int64_t off = w.l.total;
+    auto take = [&off](int64_t bytes) {
+        const int64_t o = (off + 255) & ~int64_t(255);
+        off = o + bytes;
+        return o;
+    };
+    const int64_t vrows = p->B * p->T * nvh(p);
+    if (w.qk) {
+        const int64_t bytes = vrows * p->dk * io_size(p);
+        w.qh = take(bytes); w.kh = take(bytes); w.dqh = take(bytes); w.dkh = take(bytes);
+    }
+    if (w.gates) {
+        const int64_t gk = vrows * p->dk * 4, gv = vrows * p->dv * 4;
+        w.ga = take(gk); w.gb = take(gk); w.gw = take(gv);
+        w.dga = take(gk); w.dgb = take(gk); w.dgw = take(gv);
+    }
+    w.total = off;
+    return w;
+}
+
+// the core backward: p has no flags and H value heads = query/key heads
+int bwd_core(const gdn2_problem* p, const BwdLayout& l, const void* q, const void* k, const void* v,
+             const void* alpha, const void* b, const void* w, const float* S0, const void* dO, const float* dS_T,
+             void* dq, void* dk, void* dv, void* dalpha, void* db, void* dw, float* dS0, char* ws, hipStream_t s)
+{
+    int st = GDN2_OK;
+    float* chk = reinterpret_cast<float*>(ws + l.chk);
+    float* dsl = reinterpret_cast<float*>(ws + l.dsl);
+    void* chkT = l.mf ? ws + l.chkT : nullptr;
+    void* dslT = l.mf ? ws + l.dslT : nullptr;
+    const int64_t nch = p->B * p->H;
+    const int64_t total = nch * nchunks(p);
+    if (nchunks(p) > 0) {
+        gdn2::PrepArgs pa{q, k, v, alpha, b, w, ws, l.block, p->B, p->T, p->H, p->H,
+                          (int)p->dv, (int)nchunks(p), 0, nullptr, 0, l.t_off};
+        st = launch_status(gdn2::launch_chunk_prep(pa, (int)p->dk, is_bf16(p), gates_bf16(p), s));
+        if (st) return st;
+        const int vs = gdn2::chunk_state_slice(nch, (int)p->dv, (int)p->dk, (int)io_size(p));
+        gdn2::StateArgs fa{ws, l.block, S0, nullptr, nullptr, p->B, p->T, p->H, (int)p->dv,
+                           (int)nchunks(p), (int)(p->dv / vs), nullptr, 0, chk, chkT};
+        st = launch_status(gdn2::launch_chunk_state(fa, (int)p->dk, vs, is_bf16(p), s));
+        if (st) return st;
+    }
+    const int bvs = gdn2::state_bwd_slice((int)p->dv);
+    gdn2::BwdStateArgs ba{ws, l.block, dO, dS_T, dsl, dS0, p->B, p->T, p->H, (int)p->dk, (int)p->dv,
+                          (int)nchunks(p), (int)(p->dv / bvs), bvs, dslT};
+    st = launch_status(gdn2::launch_chunk_state_bwd(ba, is_bf16(p), s));
     if (st) return st;
-    if (p->flags != 0 || (p->Hv != 0 && p->Hv != p->H)) return GDN2_ERR_SHAPE;
-    return GDN2_OK;
+    if (nchunks(p) == 0) return GDN2_OK;
+    float* gsc = reinterpret_cast<float*>(ws + l.scratch);
+    if (l.mf) {
+        gdn2::GradVArgs va{ws, l.block, l.t_off, k, v, alpha, b, w, dO, chk, chkT, dsl, dslT, dw, dv, gsc,
+                           p->B, p->T, p->H, (int)p->dk, (int)p->dv, (int)nchunks(p), total};
+        gdn2::GradKArgs ka{q, k, alpha, b, gsc, dq, dk, dalpha, db, p->B, p->T, p->H, (int)p->dk,
+                           (int)nchunks(p), total};
+        return launch_status(gdn2::launch_chunk_grad_mf(va, ka, gates_bf16(p), s));
+    }
+    gdn2::GradArgs ga{q, k, v, alpha, b, w, dO, chk, dsl, dq, dk, dv, dalpha, db, dw, gsc, p->B, p->T, p->H,
+                      (int)p->dk, (int)p->dv, (int)nchunks(p), total};
+    return launch_status(gdn2::launch_chunk_grad(ga, is_bf16(p), gates_bf16(p), s));
 }
 
 }  // namespace
@@ -447,8 +523,8 @@ int gdn2_recurrent_varlen(const gdn2_problem* p, const int32_t* cu_seqlens, cons
 
 size_t gdn2_chunk_bwd_workspace_size(const gdn2_problem* p)
 {
-    if (check_bwd_problem(p) != GDN2_OK) return 0;
-    return static_cast<size_t>(bwd_layout(p).total);
+    if (check_problem(p, true) != GDN2_OK) return 0;
+    return static_cast<size_t>(bwd_wrap(p).total);
 }
 
 int gdn2_chunk_bwd(const gdn2_problem* p, const void* q, const void* k, const void* v, const void* alpha,
@@ -456,13 +532,13 @@ int gdn2_chunk_bwd(const gdn2_problem* p, const void* q, const void* k, const vo
                    void* dk, void* dv, void* dalpha, void* db, void* dw, float* dS0, void* workspace,
                    size_t workspace_bytes, void* stream)
 {
-    int st = check_bwd_problem(p);
+    int st = check_problem(p, true);
     if (st) return st;
     st = check_inputs(p, q, k, v, alpha, b, w, dO);
     if (st) return st;
     if (rows_nonempty(p) && (!dq || !dk || !dv || !dalpha || !db || !dw)) return GDN2_ERR_NULL;
-    const BwdLayout l = bwd_layout(p);
-    const int64_t need = p->B * p->H > 0 ? l.total : 0;
+    const BwdWrap wr = bwd_wrap(p);
+    const int64_t need = p->B * p->H > 0 ? wr.total : 0;
     if (need > 0 && (workspace == nullptr || static_cast<int64_t>(workspace_bytes) < need))
         return GDN2_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_WORKSPACE;
@@ -483,40 +559,45 @@ int gdn2_chunk_bwd(const gdn2_problem* p, const void* q, const void* k, const vo
     if (st) return st;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     char* ws = static_cast<char*>(workspace);
-    float* chk = reinterpret_cast<float*>(ws + l.chk);
-    float* dsl = reinterpret_cast<float*>(ws + l.dsl);
-    void* chkT = l.mf ? ws + l.chkT : nullptr;
-    void* dslT = l.mf ? ws + l.dslT : nullptr;
-    const int64_t nch = p->B * p->H;
-    const int64_t total = nch * nchunks(p);
-    if (nchunks(p) > 0) {
-        gdn2::PrepArgs pa{q, k, v, alpha, b, w, ws, l.block, p->B, p->T, p->H, p->H,
-                          (int)p->dv, (int)nchunks(p), (int)p->flags, nullptr, 0, l.t_off};
-        st = launch_status(gdn2::launch_chunk_prep(pa, (int)p->dk, is_bf16(p), gates_bf16(p), s));
+    if (nchunks(p) == 0 || (!wr.qk && !wr.gates))   // no token to map: the core alone
+        return bwd_core(&wr.core, wr.l, q, k, v, alpha, b, w, S0, dO, dS_T, dq, dk, dv, dalpha, db, dw, dS0,
+                        ws, s);
+    const void *cq = q, *ck = k, *ca = alpha, *cb = b, *cw = w;
+    void *cdq = dq, *cdk = dk, *cda = dalpha, *cdb = db, *cdw = dw;
+    const int G = (int)(nvh(p) / p->H);
+    const gdn2::QkMapArgs qa{q, k, ws + wr.qh, ws + wr.kh, ws + wr.dqh, ws + wr.dkh, dq, dk,
+                             p->B * p->T * p->H, G, (int)p->dk, (p->flags & GDN2_FLAG_QK_L2NORM) != 0};
+    if (wr.qk) {
+        st = launch_status(gdn2::launch_bwd_qk_map(qa, false, is_bf16(p), s));
         if (st) return st;
-        const int vs = gdn2::chunk_state_slice(nch, (int)p->dv, (int)p->dk, (int)io_size(p));
-        gdn2::StateArgs fa{ws, l.block, S0, nullptr, nullptr, p->B, p->T, p->H, (int)p->dv,
-                           (int)nchunks(p), (int)(p->dv / vs), nullptr, 0, chk, chkT};
-        st = launch_status(gdn2::launch_chunk_state(fa, (int)p->dk, vs, is_bf16(p), s));
-        if (st) return st;
+        cq = ws + wr.qh; ck = ws + wr.kh; cdq = ws + wr.dqh; cdk = ws + wr.dkh;
     }
-    const int bvs = gdn2::state_bwd_slice((int)p->dv);
-    gdn2::BwdStateArgs ba{ws, l.block, dO, dS_T, dsl, dS0, p->B, p->T, p->H, (int)p->dk, (int)p->dv,
-                          (int)nchunks(p), (int)(p->dv / bvs), bvs, dslT};
-    st = launch_status(gdn2::launch_chunk_state_bwd(ba, is_bf16(p), s));
+    const int64_t vrows = p->B * p->T * nvh(p);
+    const float bscale = (p->flags & GDN2_FLAG_NEG_EIGVAL) ? 2.f : 1.f;
+    float* ga[3] = {reinterpret_cast<float*>(ws + wr.ga), reinterpret_cast<float*>(ws + wr.gb),
+                    reinterpret_cast<float*>(ws + wr.gw)};
+    float* dga[3] = {reinterpret_cast<float*>(ws + wr.dga), reinterpret_cast<float*>(ws + wr.dgb),
+                     reinterpret_cast<float*>(ws + wr.dgw)};
+    if (wr.gates) {
+        const gdn2::GateMapArgs pre{{alpha, b, w}, {nullptr, nullptr, nullptr}, {ga[0], ga[1], ga[2]},
+                                    {vrows * p->dk, vrows * p->dk, vrows * p->dv}, {1.f, bscale, 1.f}};
+        st = launch_status(gdn2::launch_bwd_gate_map(pre, false, gates_bf16(p), s));
+        if (st) return st;
+        ca = ga[0]; cb = ga[1]; cw = ga[2];
+        cda = dga[0]; cdb = dga[1]; cdw = dga[2];
+    }
+    st = bwd_core(&wr.core, wr.l, cq, ck, v, ca, cb, cw, S0, dO, dS_T, cdq, cdk, dv, cda, cdb, cdw, dS0, ws, s);
     if (st) return st;
-    if (nchunks(p) == 0) return GDN2_OK;
-    float* gsc = reinterpret_cast<float*>(ws + l.scratch);
-    if (l.mf) {
-        gdn2::GradVArgs va{ws, l.block, l.t_off, k, v, alpha, b, w, dO, chk, chkT, dsl, dslT, dw, dv, gsc,
-                           p->B, p->T, p->H, (int)p->dk, (int)p->dv, (int)nchunks(p), total};
-        gdn2::GradKArgs ka{q, k, alpha, b, gsc, dq, dk, dalpha, db, p->B, p->T, p->H, (int)p->dk,
-                           (int)nchunks(p), total};
-        return launch_status(gdn2::launch_chunk_grad_mf(va, ka, gates_bf16(p), s));
+    if (wr.qk) {
+        st = launch_status(gdn2::launch_bwd_qk_map(qa, true, is_bf16(p), s));
+        if (st) return st;
     }
-    gdn2::GradArgs ga{q, k, v, alpha, b, w, dO, chk, dsl, dq, dk, dv, dalpha, db, dw, gsc, p->B, p->T, p->H,
-                      (int)p->dk, (int)p->dv, (int)nchunks(p), total};
-    return launch_status(gdn2::launch_chunk_grad(ga, is_bf16(p), gates_bf16(p), s));
+    if (wr.gates) {
+        const gdn2::GateMapArgs post{{alpha, b, w}, {dga[0], dga[1], dga[2]}, {dalpha, db, dw},
+                                     {vrows * p->dk, vrows * p->dk, vrows * p->dv}, {1.f, bscale, 1.f}};
+        st = launch_status(gdn2::launch_bwd_gate_map(post, true, gates_bf16(p), s));
+    }
+    return st;
 }
 
 int gdn2_gated_rmsnorm(const gdn2_problem* p, const void* o, const void* g, const float* weight, void* y,

@@ -91,6 +91,25 @@ struct GradKArgs {
     int64_t B, T, H; int dk, nt; int64_t total;
 };
 
+// Prologue options in the backward.  Query/key rows (rows = B*T*Hk of dk
+// channels): the pre launch writes qh, kh = the rows, L2-normalised when l2,
+// each copied to the G value heads of its group ([B,T,Hk*G,dk]); the post
+// launch sums dqh, dkh over the G heads and takes the sum through the norm
+// (reading q, k) into dq, dk_out.  All in the I/O dtype.
+struct QkMapArgs {
+    const void* q; const void* k; void* qh; void* kh;
+    const void* dqh; const void* dkh; void* dq; void* dk_out;
+    int64_t rows; int G, dk; bool l2;
+};
+
+// Gate logits z[j] (gate dtype, n[j] elements each, a multiple of 4): the
+// pre launch writes dst[j] = scale[j] * sigmoid(z) as fp32, the post launch
+// dst[j] (gate dtype) = grad[j] * scale[j] * s (1 - s).
+struct GateMapArgs {
+    const void* z[3]; const float* grad[3]; void* dst[3];
+    int64_t n[3]; float scale[3];
+};
+
 struct PlanArgs {
     const int* cu; int* plan;
     int64_t N, T, ncmax;
@@ -110,6 +129,8 @@ hipError_t launch_gated_rmsnorm(const NormArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_varlen_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_chunk_state_bwd(const BwdStateArgs& a, bool bf16, hipStream_t s);
 int state_bwd_slice(int dv);
+hipError_t launch_bwd_qk_map(const QkMapArgs& a, bool post, bool bf16, hipStream_t s);
+hipError_t launch_bwd_gate_map(const GateMapArgs& a, bool post, bool gbf16, hipStream_t s);
 hipError_t launch_chunk_grad(const GradArgs& a, bool bf16, bool gbf16, hipStream_t s);
 hipError_t launch_chunk_grad_mf(const GradVArgs& v, const GradKArgs& k, bool gbf16, hipStream_t s);
 bool gradmf_supported(int dk, int dv, bool bf16);

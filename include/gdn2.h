@@ -222,22 +222,31 @@ int gdn2_recurrent_varlen(const gdn2_problem* p, const int32_t* cu_seqlens,
  * Backward pass of the chunked forward (README: chunk mode is the training
  * mode).  For the loss  sum(dO * o) + sum(dS_T * S_T)  of the forward
  * gdn2_chunk_fwd(p, q, k, v, alpha, b, w, S0) computes its gradients with
- * respect to every input:
- *   dq, dk, dv        [B, T, H, dk|dv]   io_dtype
- *   dalpha, db, dw    [B, T, H, dk|dv]   gate_dtype
- *   dS0               [B, H, dk, dv]     fp32 (NULL: not wanted)
- * dO [B, T, H, dv] (io_dtype) is the gradient of o; dS_T (fp32, NULL = 0) that
- * of the final state; S0 NULL = the zero initial state, as in the forward.
+ * respect to every input, in the forward's layout:
+ *   dq, dk            [B, T, H, dk]      io_dtype
+ *   dv                [B, T, Hv, dv]     io_dtype
+ *   dalpha, db, dw    [B, T, Hv, dk|dv]  gate_dtype
+ *   dS0               [B, Hv, dk, dv]    fp32 (NULL: not wanted)
+ * dO [B, T, Hv, dv] (io_dtype) is the gradient of o; dS_T (fp32, NULL = 0)
+ * that of the final state; S0 NULL = the zero initial state, as in the
+ * forward.  Every prologue flag and grouped value heads (README,
+ * "Architecture" and "Configuration") are supported: with gate logits the
+ * gradients are those of the logits, with the L2 norm those of the raw q
+ * and k, and a query/key head shared by G value heads gets the sum of their
+ * gradients.
  * The forward is recomputed inside (no forward workspace is kept between
  * the calls); the backward is exact up to rounding, with fp32 arithmetic
- * throughout and the forward's operands in io_dtype.
- * This version requires flags == 0 and Hv == 0 or H (GDN2_ERR_SHAPE
- * otherwise).  Every gradient output must be distinct from every input and
- * from each other (GDN2_ERR_ALIAS); all tensors 16-byte aligned; the
- * workspace 256-byte aligned and at least gdn2_chunk_bwd_workspace_size(p)
- * bytes (it holds the forward factors, the state entering every chunk, the
- * state gradient leaving every chunk and per-workgroup scratch).
- * Launches five kernels on `stream`.
+ * throughout and the forward's operands in io_dtype (normalised q/k rows
+ * rounded to io_dtype, activated gates kept in fp32).
+ * Every gradient output must be distinct from every input and from each
+ * other (GDN2_ERR_ALIAS); all tensors 16-byte aligned; the workspace
+ * 256-byte aligned and at least gdn2_chunk_bwd_workspace_size(p) bytes (it
+ * holds the forward factors, the state entering every chunk, the state
+ * gradient leaving every chunk, per-workgroup scratch and, with flags or
+ * grouped heads, the activated inputs and their gradients).
+ * Launches five kernels on `stream`, plus one before and one after the core
+ * for each of the two mappings (q/k rows: L2 norm or grouped heads; gates:
+ * logits).
  */
 size_t gdn2_chunk_bwd_workspace_size(const gdn2_problem* p);
 

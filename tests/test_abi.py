@@ -360,3 +360,83 @@ def test_varlen_binding_validates():
         g.chunk_fwd_varlen(q, q, v, q, q, v, cu)
     with pytest.raises(ValueError):
         g.recurrent_varlen(q, q, v, q, q, v, cu.long())
+
+
+# ---- backward ----------------------------------------------------------------------
+def _up(x):
+    return (x + 255) // 256 * 256
+
+
+def _bwd_ws(B, T, H, dk, dv, io, gate, flags, Hv):
+    return g.lib().gdn2_chunk_bwd_workspace_size(ctypes.byref(bnd.Problem(B, T, H, dk, dv, 64, io, gate, flags, Hv)))
+
+
+@pytest.mark.parametrize("flags,Hv,gate", [(0, 0, 0), (4, 0, 1), (1, 0, 1), (3, 6, 0), (0, 6, 1), (7, 6, 1)])
+def test_backward_workspace_with_options(flags, Hv, gate):
+    """With the prologue options or shared query/key heads the workspace is the
+    core's (no flags, one query/key head per value head, fp32 gates with logits)
+    followed by 256-aligned activated inputs and their gradients."""
+    B, T, H, dk, dv, io = 2, 100, 3, 64, 32, 1
+    hv = Hv or H
+    core = _bwd_ws(B, T, hv, dk, dv, io, 0 if flags & 1 else gate, 0, 0)
+    assert core > 0
+    off = core
+    parts = []
+    vrows = B * T * hv
+    if flags & 4 or hv != H:
+        parts += [vrows * dk * 2] * 4
+    if flags & 1:
+        parts += [vrows * dk * 4, vrows * dk * 4, vrows * dv * 4] * 2
+    for n in parts:
+        off = _up(off) + n
+    assert _bwd_ws(B, T, H, dk, dv, io, gate, flags, Hv) == off
+
+
+class BCall:
+    """Fake, disjoint device buffers for one backward call."""
+
+    def __init__(self, B=2, T=100, H=3, dk=64, dv=32, io=1, gate=0, flags=0, Hv=0):
+        self.p = bnd.Problem(B, T, H, dk, dv, 64, io, gate, flags, Hv)
+        es, gs = (2 if io == 1 else 4), (2 if gate == 1 else 4)
+        rows, vrows, nv = B * T * H, B * T * (Hv or H), B * (Hv or H)
+        st = nv * dk * dv * 4
+        self.names = ("q", "k", "v", "alpha", "b", "w", "S0", "dO", "dS_T", "dq", "dk", "dv", "dalpha", "db",
+                      "dw", "dS0", "ws")
+        sz = dict(q=rows * dk * es, k=rows * dk * es, v=vrows * dv * es, alpha=vrows * dk * gs, b=vrows * dk * gs,
+                  w=vrows * dv * gs, S0=st, dO=vrows * dv * es, dS_T=st)
+        for n in ("q", "k", "v", "alpha", "b", "w"):
+            sz["d" + n] = sz[n]
+        sz["dS0"] = st
+        sz["ws"] = g.lib().gdn2_chunk_bwd_workspace_size(ctypes.byref(self.p))
+        self.size, self.ptr, addr = sz, {}, BASE
+        for n in self.names:
+            self.ptr[n] = addr
+            addr += (sz[n] + 4095) // 4096 * 4096 + 4096
+
+    def __call__(self, **over):
+        wsb = over.pop("ws_bytes", self.size["ws"])
+        a = dict(self.ptr)
+        a.update(over)
+        P = lambda x: None if x is None else ctypes.c_void_p(x)
+        return g.lib().gdn2_chunk_bwd(ctypes.byref(self.p), *(P(a[n]) for n in self.names), wsb, None)
+
+
+@pytest.mark.parametrize("flags,Hv", [(0, 0), (7, 0), (4, 6), (1, 3)])
+def test_backward_checks(flags, Hv):
+    c = BCall(flags=flags, Hv=Hv)
+    assert c.size["ws"] > 0
+    assert c() == DEVICE
+    assert c(ws_bytes=c.size["ws"] - 1) == WS
+    assert c(ws=c.ptr["ws"] + 16) == WS
+    assert c(dq=None) == NULL
+    assert c(dq=c.ptr["q"]) == ALIAS
+    assert c(ws=c.ptr["dalpha"]) == ALIAS
+    assert c(dS0=c.ptr["S0"]) == ALIAS           # no in-place state gradient
+    assert c(dalpha=c.ptr["dalpha"] + 8) == ALIGN
+    assert c(S0=None, dS_T=None, dS0=None) == DEVICE
+
+
+def test_backward_rejects_what_the_forward_rejects():
+    assert BCall(flags=2).__call__() == SHAPE     # negative eigenvalues need gate logits
+    assert BCall(Hv=4).__call__() == SHAPE        # 4 value heads over 3 query/key heads
+    assert _bwd_ws(2, 100, 3, 64, 32, 1, 0, 2, 0) == 0

@@ -118,3 +118,85 @@ def test_backward_deterministic(dev):
     torch.cuda.synchronize()
     for n in NAMES:
         assert torch.equal(g1[n], g2[n]), n
+
+
+# ---- prologue options and grouped value heads -------------------------------------
+LOG, NEG, L2 = g.FLAG_GATE_LOGITS, g.FLAG_NEG_EIGVAL, g.FLAG_QK_L2NORM
+
+FULL_CASES = [
+    # B, T, H, Hv, dk, dv, io, gate dtype, flags, S0 std
+    (2, 100, 2, 4, 64, 64, F32, F32, 0, 0.05),
+    (2, 65, 1, 3, 16, 32, F32, F32, L2, None),
+    (1, 70, 2, 2, 64, 32, F32, F32, LOG | NEG, 0.05),
+    (1, 130, 1, 2, 128, 128, BF16, F32, LOG | NEG | L2, 0.05),
+    (1, 97, 2, 2, 32, 48, BF16, BF16, LOG, None),
+    (1, 150, 2, 4, 64, 64, BF16, BF16, LOG | NEG | L2, 0.05),
+    (1, 64, 1, 1, 128, 64, BF16, F32, L2, 0.05),
+    (2, 33, 2, 4, 128, 128, BF16, F32, 0, None),
+]
+
+
+def _fid(c):
+    B, T, H, Hv, dk, dv, io, gt, fl, s0 = c
+    n = lambda d: "bf16" if d == BF16 else "f32"
+    return f"B{B}T{T}H{H}Hv{Hv}dk{dk}dv{dv}io{n(io)}g{n(gt)}fl{fl}{'S0' if s0 else ''}"
+
+
+@pytest.mark.parametrize("case", FULL_CASES, ids=_fid)
+def test_backward_prologue_and_grouped_heads(dev, case):
+    """Gradients of the logits, of the raw q/k and of shared query/key heads against
+    ``oracle.backward.full_bwd`` (pinned by finite differences of the whole forward)."""
+    from oracle.backward import full_bwd
+    B, T, H, Hv, dk, dv, io, gt, fl, s0 = case
+    seed = 3 * T + dk + fl
+    inp = inputs.make_raw(B, T, H, dk, dv, io, seed, dev, s0_std=s0, gate_dtype=gt, Hv=Hv,
+                          gate_logits=bool(fl & LOG), unit_qk=not fl & L2)
+    dO, dS_T = inputs.make_out_grads(B, T, Hv, dk, dv, io, seed + 1, dev)
+    got = g.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["b"], inp["w"], dO, inp["S0"], dS_T,
+                      flags=fl)
+    torch.cuda.synchronize()
+    for n, x in (("dq", inp["q"]), ("dk", inp["k"]), ("dv", inp["v"]), ("dalpha", inp["alpha"]),
+                 ("db", inp["b"]), ("dw", inp["w"])):
+        assert got[n].shape == x.shape and got[n].dtype == x.dtype, n
+    h = {n: _np(x) for n, x in inp.items()}
+    want = full_bwd(h["q"], h["k"], h["v"], h["alpha"], h["b"], h["w"], h["S0"], _np(dO), _np(dS_T), flags=fl)
+    check(_fid(case), {n: _np(got[n]) for n in NAMES}, want, TOL[io])
+
+
+def test_backward_grouped_heads_equal_widened_call(dev):
+    """G value heads sharing a query/key head = the call on q/k copied to every value
+    head, with dq/dk summed over the group (same kernels: equal up to the sum's rounding)."""
+    B, T, H, Hv, dk, dv = 1, 140, 2, 4, 64, 64
+    inp = inputs.make_raw(B, T, H, dk, dv, BF16, 8, dev, s0_std=0.05, Hv=Hv)
+    dO, dS_T = inputs.make_out_grads(B, T, Hv, dk, dv, BF16, 9, dev)
+    a = (inp["v"], inp["alpha"], inp["b"], inp["w"], dO, inp["S0"], dS_T)
+    g1 = g.chunk_bwd(inp["q"], inp["k"], *a)
+    wide = lambda x: x.repeat_interleave(Hv // H, dim=2).contiguous()
+    g2 = g.chunk_bwd(wide(inp["q"]), wide(inp["k"]), *a)
+    torch.cuda.synchronize()
+    for n in ("dv", "dalpha", "db", "dw", "dS0"):
+        assert torch.equal(g1[n], g2[n]), n
+    for n in ("dq", "dk"):
+        s = g2[n].float().reshape(B, T, H, Hv // H, dk).sum(3)
+        assert rel_l2(_np(g1[n]), _np(s)) < 1e-2, n
+
+
+def test_backward_full_size_with_options_sampled(dev):
+    """B4 H16 T2048 d128 bf16 with gate logits in bf16, negative eigenvalues and the
+    q/k norm: sampled (batch, head) chains against full_bwd."""
+    from oracle.backward import full_bwd
+    B, T, H, dk, dv = 4, 2048, 16, 128, 128
+    fl = LOG | NEG | L2
+    inp = inputs.make_raw(B, T, H, dk, dv, BF16, 78, dev, gate_dtype=BF16, gate_logits=True, unit_qk=False)
+    dO, dS_T = inputs.make_out_grads(B, T, H, dk, dv, BF16, 79, dev)
+    got = g.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["b"], inp["w"], dO, None, dS_T, flags=fl)
+    torch.cuda.synchronize()
+    h = {n: _np(x) for n, x in inp.items()}
+    dOn, dSn = _np(dO), _np(dS_T)
+    for bi, hi in [(0, 0), (3, 15)]:
+        sl = lambda x: x[bi:bi + 1, :, hi:hi + 1]
+        want = full_bwd(sl(h["q"]), sl(h["k"]), sl(h["v"]), sl(h["alpha"]), sl(h["b"]), sl(h["w"]), None,
+                        sl(dOn), dSn[bi:bi + 1, hi:hi + 1], flags=fl)
+        gs = {n: (_np(got[n])[bi:bi + 1, :, hi:hi + 1] if n != "dS0" else _np(got[n])[bi:bi + 1, hi:hi + 1])
+              for n in NAMES}
+        check(f"B4H16T2048 flags {fl} chain ({bi},{hi})", gs, want, 2e-2)
