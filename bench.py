@@ -1,11 +1,13 @@
 """Benchmark of the GDN-2 token-mixer hot path on one MI355X.
 
 One step = one chunked forward of the B4 H16 T2048 d128 workload (bf16 q/k/v,
-fp32 gates and state; returns o and the final state) followed by one decode
-step of the B256 H16 d128 workload (fp32 state updated in place).  Inputs are
-seeded synthetic tensors resident in HBM before timing; three input sets (and
-three decode states) are rotated so that consecutive steps never find their
-data in the 256 MB Infinity Cache.
+fp32 gates and state; returns o and the final state).  The decode step of the
+B256 H16 d128 workload (fp32 state updated in place) is timed after the steps,
+in a loop of its own: run between two forwards, the write-back of its 268 MB
+of state would land in the next forward's time.  Inputs are seeded synthetic
+tensors resident in HBM before timing; three input sets (and three decode
+states) are rotated so that consecutive calls never find their data in the
+256 MB Infinity Cache.
 
 Prints ONE JSON line.  `value` is the chunked forward's throughput in tokens/s
 (8192 tokens per call divided by the call's GPU time, from HIP events on the
@@ -241,7 +243,7 @@ def main(argv=None):
     torch.cuda.synchronize()
 
     def step(i, ev=None):
-        s, d = i % len(sets), i % len(dsets)
+        s = i % len(sets)
         if ev is not None:
             ev[0].record()
         g.chunk_prep(*A(sets[s]), ws)
@@ -250,14 +252,20 @@ def main(argv=None):
         g.chunk_state(prob, ws, outs[s], sets[s]["S0"], states[s])
         if ev is not None:
             ev[2].record()
+
+    def decode(i, ev=None):
+        d = i % len(dsets)
+        if ev is not None:
+            ev[0].record()
         g.recurrent_step(*A(dsets[d]), dsets[d]["S0"], o=douts[d], inplace=True)
         if ev is not None:
-            ev[3].record()
+            ev[1].record()
 
+    # the timed steps: chunked forwards back to back over rotating input sets
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -265,9 +273,18 @@ def main(argv=None):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / max(args.steps, 1)
+    # the decode step in a loop of its own (its in-place state writes would
+    # otherwise be written back during the next chunked forward)
+    for i in range(args.warmup):
+        decode(i)
+    dev_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        decode(args.warmup + i, dev_evs[i])
+    torch.cuda.synchronize()
     per_step = {"prep": sorted(e[0].elapsed_time(e[1]) for e in evs),
                 "state": sorted(e[1].elapsed_time(e[2]) for e in evs),
-                "decode": sorted(e[2].elapsed_time(e[3]) for e in evs),
+                "decode": sorted(e[0].elapsed_time(e[1]) for e in dev_evs),
                 "chunk": sorted(e[0].elapsed_time(e[2]) for e in evs)}
     prep_ms = sum(per_step["prep"]) / args.steps
     state_ms = sum(per_step["state"]) / args.steps
@@ -322,8 +339,8 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "chunk fwd B4 H16 T2048 dk=dv=128 (bf16 q/k/v, fp32 gates+state) "
-                               "+ decode step B256 H16 d128 (fp32 state in place)",
+        "config": {"workload": "chunk fwd B4 H16 T2048 dk=dv=128 (bf16 q/k/v, fp32 gates+state); "
+                               "decode step B256 H16 d128 (fp32 state in place) timed in a loop of its own",
                    "global_batch": B, "seq_len": T, "heads": H, "dk": dk, "dv": dv, "chunk": 64,
                    "parallelism": "single GPU", "rotated_input_sets": args.sets},
         "roofline": roof(dom),
@@ -517,13 +534,34 @@ def backward_leg(g, inputs, wl, dev, args):
     torch.cuda.synchronize()
     t = sorted(e[0].elapsed_time(e[1]) for e in evs)
     ms = sum(t) / steps
+    finite = all(torch.isfinite(v.float()).all() for v in out.values() if v is not None)
+    # the same workload with bf16 gate logits, b x 2 and the q/k L2 norm
+    fl = g.FLAG_GATE_LOGITS | g.FLAG_NEG_EIGVAL | g.FLAG_QK_L2NORM
+    x = inputs.make_raw(B, T, H, dk, dv, wl.io_dtype, 990, dev, gate_dtype=torch.bfloat16, gate_logits=True,
+                        unit_qk=False)
+    del ws
+    ws = g.alloc_workspace(g.chunk_bwd_workspace_size(B, T, H, dk, dv, wl.io_dtype, torch.bfloat16, flags=fl), dev)
+    for i in range(args.warmup + steps):
+        dO, dS = grads[i % 2]
+        ev = evs[i - args.warmup] if i >= args.warmup else None
+        if ev:
+            ev[0].record()
+        out = g.chunk_bwd(x["q"], x["k"], x["v"], x["alpha"], x["b"], x["w"], dO, None, dS, workspace=ws, flags=fl)
+        if ev:
+            ev[1].record()
+    torch.cuda.synchronize()
+    tf = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    msf = sum(tf) / steps
+    finite = finite and all(torch.isfinite(v.float()).all() for v in out.values() if v is not None)
     nchunks = B * H * ((T + 63) // 64)
     flops = grad_flops_per_chunk(dk, dv) * nchunks
     return {"workload": f"chunked backward B{B} H{H} T{T} d{dk}, bf16 q/k/v/dO, fp32 gates, dS_T given",
             "tokens_per_s": round(B * T / (ms * 1e-3), 1), "us": round(ms * 1e3, 2),
             "median_us": round(t[len(t) // 2] * 1e3, 2), "min_us": round(t[0] * 1e3, 2),
             "grad_kernel_useful_GFLOP": round(flops / 1e9, 2),
-            "outputs_finite": bool(all(torch.isfinite(v.float()).all() for v in out.values() if v is not None))}
+            "with_prologue_flags": {"workload": "the same with bf16 gate logits, b x 2 and the q/k L2 norm",
+                                    "us": round(msf * 1e3, 2), "median_us": round(tf[len(tf) // 2] * 1e3, 2)},
+            "outputs_finite": bool(finite)}
 
 
 def epilogue_leg(g, outs, dev, args):

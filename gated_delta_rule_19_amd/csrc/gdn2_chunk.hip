@@ -170,6 +170,9 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
     typedef typename IO::frag frag;
 
     // ---- 0. key-axis loads ----------------------------------------------------
+    // Inputs are read once, with nontemporal (streaming) loads: they then do
+    // not displace the workspace blocks this launch writes from the last-level
+    // cache, and the state pass that follows finds most of them there.
     // One vector-memory counter tracks loads and stores alike, so a load
     // issued after a store would also wait for that store to complete: every
     // load needed before the first global store is issued here.  Loads are
@@ -191,10 +194,10 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
         const int r = 8 * rg + i;
         const int rc = r < L ? r : L - 1;
         const int64_t off = (row0 + rc * H) * DK + c0, offk = (row0k + rc * Hk) * DK + c0;
-        alr[i] = *reinterpret_cast<const gvec*>(galpha + off);
-        btr[i] = *reinterpret_cast<const gvec*>(gb + off);
-        kk[i] = *reinterpret_cast<const typename IO::vec4*>(k + offk);
-        qq[i] = *reinterpret_cast<const typename IO::vec4*>(q + offk);
+        alr[i] = __builtin_nontemporal_load(reinterpret_cast<const gvec*>(galpha + off));
+        btr[i] = __builtin_nontemporal_load(reinterpret_cast<const gvec*>(gb + off));
+        kk[i] = __builtin_nontemporal_load(reinterpret_cast<const typename IO::vec4*>(k + offk));
+        qq[i] = __builtin_nontemporal_load(reinterpret_cast<const typename IO::vec4*>(q + offk));
     }
     // prologue: gate activations, q/k L2 norms (sum of squares over the NQ
     // lanes that hold one token's channels)
@@ -342,8 +345,8 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
         for (int i = 0; i < 8; ++i) {
             const int s = 8 * sg + i;
             const int64_t off = (row0 + (s < L ? s : L - 1) * H) * a.dv + 4 * jq;
-            wr[it][i] = *reinterpret_cast<const gvec*>(gw + off);
-            vr[it][i] = *reinterpret_cast<const typename IO::vec4*>(v + off);
+            wr[it][i] = __builtin_nontemporal_load(reinterpret_cast<const gvec*>(gw + off));
+            vr[it][i] = __builtin_nontemporal_load(reinterpret_cast<const typename IO::vec4*>(v + off));
         }
     }
     __syncthreads();
