@@ -309,7 +309,7 @@ def main(argv=None):
         "state": dict(ms=state_ms, alg=alg_state),
         "decode": dict(ms=dec_ms, alg=alg_dec),
     }
-    dom = max(kern, key=lambda k_: kern[k_]["ms"])
+    dom = max(("prep", "state"), key=lambda k_: kern[k_]["ms"])   # the timed step: the chunked forward
 
     def roof(key):
         k_ = kern[key]
