@@ -370,6 +370,8 @@ def main(argv=None):
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(sets[0], args.cpu_chains, B, T, H, dk, dv)
+        if "chunk_bwd" in result:
+            result["chunk_bwd"]["cpu_baseline"] = cpu_baseline_backward(sets[0], B, T, H, dk, dv)
     print(json.dumps(result), flush=True)
     return 0
 
@@ -555,9 +557,18 @@ def backward_leg(g, inputs, wl, dev, args):
     finite = finite and all(torch.isfinite(v.float()).all() for v in out.values() if v is not None)
     nchunks = B * H * ((T + 63) // 64)
     flops = grad_flops_per_chunk(dk, dv) * nchunks
+    # algorithmic bytes: q, k, v, dO (bf16) and alpha, b, w (fp32) read, their
+    # gradients written in the same dtypes, plus dS_T read and dS0 written
+    per_ht = 2 * (2 * dk + 2 * dv) + 4 * (2 * dk + dv) + 2 * (2 * dk + dv) + 4 * (2 * dk + dv)
+    alg = per_ht * B * T * H + 2 * B * H * dk * dv * 4
+    ach = alg / (ms * 1e-3) / 1e9
     return {"workload": f"chunked backward B{B} H{H} T{T} d{dk}, bf16 q/k/v/dO, fp32 gates, dS_T given",
             "tokens_per_s": round(B * T / (ms * 1e-3), 1), "us": round(ms * 1e3, 2),
             "median_us": round(t[len(t) // 2] * 1e3, 2), "min_us": round(t[0] * 1e3, 2),
+            "alg_bytes_per_head_token": per_ht,
+            "roofline": {"kernel": "whole backward call (forward recompute + reverse pass + gradients)",
+                         "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                         "frac": round(ach / PEAK_HBM_GBPS, 4), "alg_bytes": int(alg)},
             "grad_kernel_useful_GFLOP": round(flops / 1e9, 2),
             "with_prologue_flags": {"workload": "the same with bf16 gate logits, b x 2 and the q/k L2 norm",
                                     "us": round(msf * 1e3, 2), "median_us": round(tf[len(tf) // 2] * 1e3, 2)},
@@ -648,6 +659,29 @@ def cpu_baseline(inp, chains, B, T, H, dk, dv):
     return {"value": round(tok_s, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu": cpu_model(),
             "sample": f"fp64 C oracle (OpenMP over head x 16-column blocks) on {nb * H} of {B * H} "
                       f"(batch, head) chains x {T} tokens of the same inputs: {dt:.2f} s",
+            "seconds": round(dt, 3)}
+
+
+def cpu_baseline_backward(inp, B, T, H, dk, dv, chains=2):
+    """The fp64 backward oracle (numpy, reverse loop over tokens) on `chains` (batch, head)
+    chains of the inputs, all T tokens, output gradients dO ~ N(0,1) and dS_T ~ N(0,1);
+    tokens/s scaled by the share of chains run."""
+    import numpy as np
+    import torch
+
+    from oracle.backward import recurrent_bwd
+    f = lambda x, h: x[0:1, :, h:h + 1].detach().to("cpu", torch.float64).numpy()
+    rng = np.random.default_rng(5)
+    t0 = time.perf_counter()
+    for h in range(chains):
+        dO = rng.standard_normal((1, T, 1, dv))
+        dS = rng.standard_normal((1, 1, dk, dv))
+        recurrent_bwd(*(f(inp[k_], h) for k_ in ("q", "k", "v", "alpha", "b", "w")), None, dO, dS)
+    dt = time.perf_counter() - t0
+    frac = chains / float(B * H)
+    return {"value": round(B * T / (dt / frac), 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"fp64 numpy backward oracle (reverse token loop) on {chains} of {B * H} (batch, head) "
+                      f"chains x {T} tokens of the forward's inputs: {dt:.2f} s",
             "seconds": round(dt, 3)}
 
 

@@ -71,25 +71,34 @@ __host__ __device__ inline int64_t gradmf_scratch_floats(int dk) { return 3 * 64
 // G[r][c] = sum of log alpha over tokens 0..r of the chunk (alpha = 1 past its
 // end), for 256 threads: logs in parallel (every load issued before the first
 // use), then a scan of 256/DK segments per channel with the segment totals
-// carried through `tot`
+// carried through `tot`.  cld_load issues the loads, cld_scan does the rest.
 template <int DK, typename Tg>
-__device__ __attribute__((always_inline)) inline void cum_log_decay(float* G, float* tot, const Tg* alpha,
-                                                                    int64_t row0, int64_t H, int Ln)
+__device__ __attribute__((always_inline)) inline void cld_load(typename GateVec<Tg>::type (&x)[64 * DK / 4 / kThreads],
+                                                               const Tg* alpha, int64_t row0, int64_t H, int Ln)
 {
     constexpr int NV = 64 * DK / 4 / kThreads;
     const int tid = threadIdx.x;
-    f32x4 x[NV];
 #pragma unroll
-    for (int u = 0; u < NV; ++u) {
+    for (int u = 0; u < NV; ++u) {       // raw and unconditional (rows past the end clamped)
         const int i = tid + u * kThreads, r = i / (DK / 4), c4 = 4 * (i - r * (DK / 4));
-        x[u] = r < Ln ? ld_gate4(alpha + (row0 + r * H) * DK + c4) : f32x4{1.f, 1.f, 1.f, 1.f};
+        x[u] = *reinterpret_cast<const typename GateVec<Tg>::type*>(alpha + (row0 + (r < Ln ? r : Ln - 1) * H) * DK + c4);
     }
+}
+
+template <int DK, typename Tg>
+__device__ __attribute__((always_inline)) inline void cld_scan(float* G, float* tot,
+                                                               const typename GateVec<Tg>::type (&x)[64 * DK / 4 / kThreads],
+                                                               int Ln)
+{
+    constexpr int NV = 64 * DK / 4 / kThreads;
+    const int tid = threadIdx.x;
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
         const int i = tid + u * kThreads, r = i / (DK / 4), c4 = 4 * (i - r * (DK / 4));
+        const f32x4 a = widen4(x[u]);
         f32x4 l;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) l[e] = __logf(x[u][e]);
+        for (int e = 0; e < 4; ++e) l[e] = r < Ln ? __logf(a[e]) : 0.f;   // alpha = 1 past the end
         *reinterpret_cast<f32x4*>(&G[r * DK + c4]) = l;
     }
     __syncthreads();
@@ -108,6 +117,15 @@ __device__ __attribute__((always_inline)) inline void cum_log_decay(float* G, fl
     if (g > 0)
         for (int r = g * sl; r < (g + 1) * sl; ++r) G[r * DK + c] += carry;
     __syncthreads();
+}
+
+template <int DK, typename Tg>
+__device__ __attribute__((always_inline)) inline void cum_log_decay(float* G, float* tot, const Tg* alpha,
+                                                                    int64_t row0, int64_t H, int Ln)
+{
+    typename GateVec<Tg>::type x[64 * DK / 4 / kThreads];
+    cld_load<DK>(x, alpha, row0, H, Ln);
+    cld_scan<DK, Tg>(G, tot, x, Ln);
 }
 
 // LDS regions of k_chunk_grad_val (bytes), sized for dk = dv = 128
@@ -233,62 +251,107 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
     float* s_dGL = s_dA + 4096;
 
     // ---- phase 0: operands into LDS ----------------------------------------
-    for (int g = tid; g < 64 * 8; g += kThreads) {                 // T, T^T; P^T
-        const int r = g >> 3, c0 = (g & 7) * 8;
-        const bfrag t = *reinterpret_cast<const bfrag*>(Tg_ + r * 64 + c0);
-        const bfrag p = *reinterpret_cast<const bfrag*>(Pg + r * 64 + c0);
-        *reinterpret_cast<bfrag*>(Tl + r * LT + c0) = t;
+    // Every global load of the phase is issued before the first LDS write (one
+    // round of memory latency instead of one per operand).
+    constexpr int NTP = 64 * 8 / kThreads, NKT = DK * 8 / kThreads, NUT = DV * 8 / kThreads;
+    constexpr int NDO = 64 * (DV / 8) / kThreads, NV = 64 * DK / 4 / kThreads;
+    bfrag tq[NTP], pq[NTP], kq[NKT], uq[NUT], oq[NDO];
+    typename GateVec<Tg>::type ax[NV], bx[NV];     // raw until used (see the du phase)
+    bf16x4 kx[NV];
+#pragma unroll
+    for (int m = 0; m < NTP; ++m) {                                 // T, P
+        const int g = tid + m * kThreads, r = g >> 3, c0 = (g & 7) * 8;
+        tq[m] = *reinterpret_cast<const bfrag*>(Tg_ + r * 64 + c0);
+        pq[m] = *reinterpret_cast<const bfrag*>(Pg + r * 64 + c0);
+    }
+#pragma unroll
+    for (int m = 0; m < NKT; ++m) {                                 // Ktil^T [c][r]
+        const int g = tid + m * kThreads, c = g >> 3, r0 = (g & 7) * 8;
+        kq[m] = *reinterpret_cast<const bfrag*>(Kttg + c * 64 + r0);
+    }
+#pragma unroll
+    for (int m = 0; m < NUT; ++m) {                                 // U^T [j][r]
+        const int g = tid + m * kThreads, j = g >> 3, r0 = (g & 7) * 8;
+        uq[m] = *reinterpret_cast<const bfrag*>(Utg + j * 64 + r0);
+    }
+#pragma unroll
+    for (int m = 0; m < NDO; ++m) {                                 // dO (zero past the end)
+        const int g = tid + m * kThreads, r = g / (DV / 8), j0 = (g - r * (DV / 8)) * 8;
+        oq[m] = *reinterpret_cast<const bfrag*>(dO + (row0 + (r < Ln ? r : Ln - 1) * H) * DV + j0);
+    }
+    cld_load<DK>(ax, agt, row0, H, Ln);
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {                                  // b, k for Eh
+        const int i = tid + u * kThreads, r = i / (DK / 4), c4 = 4 * (i - r * (DK / 4));
+        const int64_t o = (row0 + (r < Ln ? r : Ln - 1) * H) * DK + c4;
+        bx[u] = *reinterpret_cast<const typename GateVec<Tg>::type*>(bgt + o);
+        kx[u] = *reinterpret_cast<const bf16x4*>(kg + o);
+    }
+#pragma unroll
+    for (int m = 0; m < NTP; ++m) {                                 // T, T^T; P^T
+        const int g = tid + m * kThreads, r = g >> 3, c0 = (g & 7) * 8;
+        *reinterpret_cast<bfrag*>(Tl + r * LT + c0) = tq[m];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            Ttl[(c0 + e) * LT + r] = t[e];
-            Ptl[(c0 + e) * LT + r] = p[e];
+            Ttl[(c0 + e) * LT + r] = tq[m][e];
+            Ptl[(c0 + e) * LT + r] = pq[m][e];
         }
     }
-    for (int g = tid; g < DK * 8; g += kThreads) {                 // Ktil [r][c] from Ktil^T [c][r]
-        const int c = g >> 3, r0 = (g & 7) * 8;
-        const bfrag x = *reinterpret_cast<const bfrag*>(Kttg + c * 64 + r0);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) Ktl[(r0 + e) * ldk + c] = x[e];
+    for (int m = 0; m < NKT; ++m) {                                 // Ktil [r][c] from Ktil^T [c][r]
+        const int g = tid + m * kThreads, c = g >> 3, r0 = (g & 7) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Ktl[(r0 + e) * ldk + c] = kq[m][e];
     }
-    for (int g = tid; g < DV * 8; g += kThreads) {                 // U [r][j] from U^T [j][r]
-        const int j = g >> 3, r0 = (g & 7) * 8;
-        const bfrag x = *reinterpret_cast<const bfrag*>(Utg + j * 64 + r0);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) Dll[(r0 + e) * ldv + j] = x[e];
+    for (int m = 0; m < NUT; ++m) {                                 // U [r][j] from U^T [j][r]
+        const int g = tid + m * kThreads, j = g >> 3, r0 = (g & 7) * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Dll[(r0 + e) * ldv + j] = uq[m][e];
     }
-    for (int g = tid; g < 64 * (DV / 8); g += kThreads) {          // dO, dO^T (zero past the end)
-        const int r = g / (DV / 8), j0 = (g - r * (DV / 8)) * 8;
-        bfrag x;
-        if (r < Ln) {
-            x = *reinterpret_cast<const bfrag*>(dO + (row0 + r * H) * DV + j0);
-        } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = (bf)0.f;
+    for (int m = 0; m < NDO; ++m) {                                 // dO, dO^T (zero past the end)
+        const int g = tid + m * kThreads, r = g / (DV / 8), j0 = (g - r * (DV / 8)) * 8;
+        if (r >= Ln) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) oq[m][e] = (bf)0.f;
         }
-        *reinterpret_cast<bfrag*>(dOl + r * ldv + j0) = x;
+        *reinterpret_cast<bfrag*>(dOl + r * ldv + j0) = oq[m];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dOtl[(j0 + e) * LT + r] = x[e];
+        for (int e = 0; e < 8; ++e) dOtl[(j0 + e) * LT + r] = oq[m][e];
     }
-    cum_log_decay<DK>(Gl, tot, agt, row0, H, Ln);
-    {                                                              // Eh = Gamma b k
-        constexpr int NV = 64 * DK / 4 / kThreads;
-        f32x4 bx[NV], kx[NV];
+    cld_scan<DK, Tg>(Gl, tot, ax, Ln);
 #pragma unroll
-        for (int u = 0; u < NV; ++u) {
-            const int i = tid + u * kThreads, r = i / (DK / 4), c4 = 4 * (i - r * (DK / 4));
-            const int64_t o = (row0 + r * H) * DK + c4;
-            bx[u] = r < Ln ? ld_gate4(bgt + o) : f32x4{0.f, 0.f, 0.f, 0.f};
-            kx[u] = r < Ln ? ld_vec4(kg + o) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < NV; ++u) {                                  // Eh = Gamma b k (zero past the end)
+        const int i = tid + u * kThreads, r = i / (DK / 4), c4 = 4 * (i - r * (DK / 4));
+        const f32x4 g4 = *reinterpret_cast<const f32x4*>(&Gl[r * DK + c4]);
+        const f32x4 b4 = widen4(bx[u]), k4 = IOB::unpack4(kx[u]);
+        f32x4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = r < Ln ? __expf(g4[e]) * b4[e] * k4[e] : 0.f;
+        st_vec4(Ehl + r * ldk + c4, x);
+    }
+    // dGamma_L = rowsum(dSL * S0) in fp32 (dk = 32: with larger dk it comes
+    // from the panels below), before the first global store (a load behind a
+    // store would wait for it); stored at the end.  TPR threads per row, each
+    // with DV / TPR columns, all loads in flight at once.
+    constexpr int TPR = kThreads / DK, NCOL = DV / TPR;
+    float dgl = 0.f;
+    if constexpr (NTK % 4 != 0) {
+        const int c = tid / TPR, sub = tid % TPR;
+        f32x4 pa[NCOL / 4], pb[NCOL / 4];
+#pragma unroll
+        for (int m = 0; m < NCOL / 4; ++m) {
+            pa[m] = *reinterpret_cast<const f32x4*>(dSL + (int64_t)c * DV + sub * NCOL + 4 * m);
+            pb[m] = *reinterpret_cast<const f32x4*>(S0 + (int64_t)c * DV + sub * NCOL + 4 * m);
         }
+        float x = 0.f;
 #pragma unroll
-        for (int u = 0; u < NV; ++u) {
-            const int i = tid + u * kThreads, r = i / (DK / 4), c4 = 4 * (i - r * (DK / 4));
-            const f32x4 g4 = *reinterpret_cast<const f32x4*>(&Gl[r * DK + c4]);
-            f32x4 x;
+        for (int m = 0; m < NCOL / 4; ++m)
+            x += pa[m][0] * pb[m][0] + pa[m][1] * pb[m][1] + pa[m][2] * pb[m][2] + pa[m][3] * pb[m][3];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = __expf(g4[e]) * bx[u][e] * kx[u][e];
-            st_vec4(Ehl + r * ldk + c4, x);
-        }
+        for (int off = 1; off < TPR; off <<= 1) x += __shfl_xor(x, off, 64);
+        dgl = x;
     }
     __syncthreads();
 
@@ -345,41 +408,78 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
                 });
     __syncthreads();
     // ---- dQh = dO S0^T and dW = -dDelta S0^T (one pass over S0), dKtil = Delta dSL^T
-    panels<NKV>(wave, 2 * NTK,
-                [&](int p, bfrag (&fb)[NKV]) {
-                    const float* B = p < NTK ? S0 : dSL;
-                    const int tn = p < NTK ? p : p - NTK;
+    // Every B panel of this wave (fp32 rows of S0 and dSL) is requested at
+    // once, raw, before the kernel's first global store; with dk >= 64 one
+    // wave holds both the S0 and the dSL panel of a row block, and dGamma_L =
+    // rowsum(dSL * S0) comes from the same fp32 values.
+    constexpr int NPW = NTK / 2;                                    // panels per wave
+    constexpr bool FUSE_GL = NTK % 4 == 0;
+    f32x4 rb[NPW][NKV][2];
 #pragma unroll
-                    for (int kb = 0; kb < NKV; ++kb) fb[kb] = fr32(B, 16 * tn + l16, DV, kb, grp);
-                },
-                [&](int p, bfrag (&fb)[NKV]) {
-                    const int tn = p < NTK ? p : p - NTK, c = 16 * tn + l16;
+    for (int m = 0; m < NPW; ++m) {
+        const int p = wave + 4 * m;
+        const float* B = p < NTK ? S0 : dSL;
+        const int tn = p < NTK ? p : p - NTK;
 #pragma unroll
-                    for (int tr = 0; tr < 4; ++tr) {
-                        const int r = 16 * tr + 4 * grp;
-                        if (p < NTK) {
-                            f32x4 aq = {0.f, 0.f, 0.f, 0.f}, aw = aq;
+        for (int kb = 0; kb < NKV; ++kb) {
+            const float* q = B + (16 * tn + l16) * DV + kb * 32 + grp * 8;
+            rb[m][kb][0] = *reinterpret_cast<const f32x4*>(q);
+            rb[m][kb][1] = *reinterpret_cast<const f32x4*>(q + 4);
+        }
+    }
+    float glp[FUSE_GL ? NPW / 2 : 1];
 #pragma unroll
-                            for (int kb = 0; kb < NKV; ++kb) {
-                                aq = IOB::mma(aq, fr(dOl, 16 * tr + l16, ldv, kb, grp), fb[kb]);
-                                aw = IOB::mma(aw, fr(dDl, 16 * tr + l16, ldv, kb, grp), fb[kb]);
-                            }
-                            aw = -aw;
+    for (int m = 0; m < NPW; ++m) {
+        const int p = wave + 4 * m;
+        const int tn = p < NTK ? p : p - NTK, c = 16 * tn + l16;
+        bfrag fb[NKV];
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                s_dQh[(r + i) * DK + c] = aq[i];
-                                dWl[(r + i) * ldk + c] = (bf)aw[i];
-                            }
-                            st_vec4(dWtl + c * LT + r, aw);
-                        } else {
-                            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int kb = 0; kb < NKV; ++kb)
 #pragma unroll
-                            for (int kb = 0; kb < NKV; ++kb) acc = IOB::mma(acc, fr(Dll, 16 * tr + l16, ldv, kb, grp), fb[kb]);
+            for (int e = 0; e < 4; ++e) {
+                fb[kb][e] = (bf)rb[m][kb][0][e];
+                fb[kb][4 + e] = (bf)rb[m][kb][1][e];
+            }
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) s_dKt[(r + i) * DK + c] = acc[i];
-                        }
-                    }
-                });
+        for (int tr = 0; tr < 4; ++tr) {
+            const int r = 16 * tr + 4 * grp;
+            if (p < NTK) {
+                f32x4 aq = {0.f, 0.f, 0.f, 0.f}, aw = aq;
+#pragma unroll
+                for (int kb = 0; kb < NKV; ++kb) {
+                    aq = IOB::mma(aq, fr(dOl, 16 * tr + l16, ldv, kb, grp), fb[kb]);
+                    aw = IOB::mma(aw, fr(dDl, 16 * tr + l16, ldv, kb, grp), fb[kb]);
+                }
+                aw = -aw;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    s_dQh[(r + i) * DK + c] = aq[i];
+                    dWl[(r + i) * ldk + c] = (bf)aw[i];
+                }
+                st_vec4(dWtl + c * LT + r, aw);
+            } else {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < NKV; ++kb) acc = IOB::mma(acc, fr(Dll, 16 * tr + l16, ldv, kb, grp), fb[kb]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s_dKt[(r + i) * DK + c] = acc[i];
+            }
+        }
+        if constexpr (FUSE_GL) {
+            if (m >= NPW / 2) {
+                float x = 0.f;
+#pragma unroll
+                for (int kb = 0; kb < NKV; ++kb)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) x += rb[m][kb][h][e] * rb[m - NPW / 2][kb][h][e];
+                x += __shfl_xor(x, 16, 64);
+                x += __shfl_xor(x, 32, 64);
+                glp[m - NPW / 2] = x;
+            }
+        }
+    }
     // ---- dP = mask(dO Delta^T) -------------------------------------------------------
     tiles<NKV>(wave, 16,
                [&](int t, bfrag (&fa)[NKV], bfrag (&fb)[NKV]) {
@@ -396,54 +496,60 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
                    for (int i = 0; i < 4; ++i) s_dP[(r + i) * 64 + s] = s <= r + i ? acc[i] : 0.f;
                });
     // ---- du = T^T dDelta -> dw = du v, dv = du w ---------------------------------
-    tiles<2>(wave, 4 * NTV,
-             [&](int t, bfrag (&fa)[2], bfrag (&fb)[2]) {
-                 const int tr = t / NTV, tn = t - tr * NTV;
+    // v and w at this wave's tile positions, and w, v for u below, are all
+    // requested before the first product (one wait for the stores above
+    // instead of one per tile row)
+    constexpr int NTU = 4 * NTV / 4;                                // du tiles per wave
+    constexpr int NVV = 64 * DV / 4 / kThreads;
+    // (kept in their memory dtypes until used: a conversion right after the
+    // load would wait for it; rows past the end are clamped and never stored)
+    Tg wt[NTU][4];
+    bf vt[NTU][4];
+    typename GateVec<Tg>::type wx[NVV];
+    bf16x4 vx[NVV];
 #pragma unroll
-                 for (int kb = 0; kb < 2; ++kb) {
-                     fa[kb] = fr(Ttl, 16 * tr + l16, LT, kb, grp);
-                     fb[kb] = fr(dDtl, 16 * tn + l16, LT, kb, grp);
-                 }
-             },
-             [&](int t, f32x4 acc) {
-                 const int tr = t / NTV, tn = t - tr * NTV;
-                 const int r = 16 * tr + 4 * grp, j = 16 * tn + l16;
+    for (int m = 0; m < NTU; ++m) {
+        const int t = wave + 4 * m, tr = t / NTV, tn = t - tr * NTV;
+        const int r = 16 * tr + 4 * grp, j = 16 * tn + l16;
 #pragma unroll
-                 for (int i = 0; i < 4; ++i) {
-                     if (r + i < Ln) {
-                         const int64_t o = (row0 + (r + i) * H) * DV + j;
-                         gs(dwg, o, acc[i] * gf(vg, o));
-                         gs(dvg, o, acc[i] * gf(wgt, o));
-                     }
-                 }
-             });
-    for (int c = tid; c < DK; c += kThreads) {                      // dGamma_L
-        float x = 0.f;
-#pragma unroll 4
-        for (int j = 0; j < DV; j += 4) {
-            const f32x4 p = *reinterpret_cast<const f32x4*>(dSL + (int64_t)c * DV + j);
-            const f32x4 q = *reinterpret_cast<const f32x4*>(S0 + (int64_t)c * DV + j);
-            x += p[0] * q[0] + p[1] * q[1] + p[2] * q[2] + p[3] * q[3];
+        for (int i = 0; i < 4; ++i) {
+            const int rc = r + i < Ln ? r + i : Ln - 1;
+            const int64_t o = (row0 + rc * H) * DV + j;
+            wt[m][i] = wgt[o];
+            vt[m][i] = vg[o];
         }
-        s_dGL[c] = x;
+    }
+#pragma unroll
+    for (int u = 0; u < NVV; ++u) {
+        const int i = tid + u * kThreads, r = i / (DV / 4), j4 = 4 * (i - r * (DV / 4));
+        const int64_t o = (row0 + (r < Ln ? r : Ln - 1) * H) * DV + j4;
+        wx[u] = *reinterpret_cast<const typename GateVec<Tg>::type*>(wgt + o);
+        vx[u] = *reinterpret_cast<const bf16x4*>(vg + o);
+    }
+#pragma unroll
+    for (int m = 0; m < NTU; ++m) {
+        const int t = wave + 4 * m, tr = t / NTV, tn = t - tr * NTV;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            acc = IOB::mma(acc, fr(Ttl, 16 * tr + l16, LT, kb, grp), fr(dDtl, 16 * tn + l16, LT, kb, grp));
+        const int r = 16 * tr + 4 * grp, j = 16 * tn + l16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (r + i < Ln) {
+                const int64_t o = (row0 + (r + i) * H) * DV + j;
+                gs(dwg, o, acc[i] * Io<bf>::to_f(vt[m][i]));
+                gs(dvg, o, acc[i] * gate_f(wt[m][i]));
+            }
+        }
     }
     __syncthreads();
     // ---- u = w v (padding tokens 0) ----------------------------------------------
-    {
-        constexpr int NV = 64 * DV / 4 / kThreads;
-        f32x4 wx[NV], vx[NV];
 #pragma unroll
-        for (int u = 0; u < NV; ++u) {
-            const int i = tid + u * kThreads, r = i / (DV / 4), j4 = 4 * (i - r * (DV / 4));
-            const int64_t o = (row0 + r * H) * DV + j4;
-            wx[u] = r < Ln ? ld_gate4(wgt + o) : f32x4{0.f, 0.f, 0.f, 0.f};
-            vx[u] = r < Ln ? ld_vec4(vg + o) : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int u = 0; u < NV; ++u) {
-            const int i = tid + u * kThreads, r = i / (DV / 4), j4 = 4 * (i - r * (DV / 4));
-            st_vec4(ul + r * ldv + j4, wx[u] * vx[u]);
-        }
+    for (int u = 0; u < NVV; ++u) {
+        const int i = tid + u * kThreads, r = i / (DV / 4), j4 = 4 * (i - r * (DV / 4));
+        const f32x4 x = widen4(wx[u]) * IOB::unpack4(vx[u]);
+        st_vec4(ul + r * ldv + j4, r < Ln ? x : f32x4{0.f, 0.f, 0.f, 0.f});
     }
     __syncthreads();
     // ---- dT = dDelta u^T + dW Eh^T (stored transposed);  dEh = T^T dW ------------
@@ -509,6 +615,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
 #pragma unroll
                  for (int i = 0; i < 4; ++i) s_dA[(r + i) * 64 + s] = s < r + i ? -acc[i] : 0.f;
              });
+    if constexpr (FUSE_GL) {
+        if (grp == 0) {
+#pragma unroll
+            for (int i = 0; i < NPW / 2; ++i) s_dGL[16 * (wave + 4 * i) + l16] = glp[i];
+        }
+    } else {
+        if (tid % TPR == 0) s_dGL[tid / TPR] = dgl;
+    }
 }
 
 // ---------------------------------------------------------------------------
