@@ -626,25 +626,76 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// key side: one workgroup per chunk; thread = R = DK/16 rows (inside one
-// 16-token block) x 4 key channels
+// key side: one workgroup per chunk.  The contractions of dA and dP with the
+// decay ratios run on bf16 matrix cores, split at the chunk's 16-token blocks
+// as in the forward: for rows r in block I and columns s in block J,
+//   exp(G_r - G_s) = exp(G_r - G_16I) * exp(G_16I - G_16J) * exp(G_16J - G_s),
+// every factor bounded (the last two inverse decays stay inside one block);
+// the middle one, per (I, J, channel), scales a whole B fragment.
+//   row side    deA[r,c] = exp(G_r - G_16I) sum_s dA[r,s] F_IJ[c] KY[s,c]
+//               (and dqP with dP),   KY[s,c] = k_s exp(G_16J - G_s)
+//   column side kak[s,c] = exp(G_16J - G_s) sum_r dA[r,s] F_IJ[c] EA[r,c]
+//               + the same with dP and QA,  EA = e_r exp(G_r - G_16I),
+//               QA = q_r exp(G_r - G_16I)
+// The token-indexed operands stay row-major in LDS; fragments whose
+// contraction index runs over tokens are gathered with 2-byte reads.  Wave w
+// owns column tiles w, w+4, ... for all 64 rows.  Then a per-row pass forms
+// the gradients of q, k and b and dG, and dalpha is the reverse cumulative
+// sum of dG.  Every phase issues its global loads before using any of them.
 // ---------------------------------------------------------------------------
+
+// 8 consecutive rows k0..k0+7 of column c from a row-major bf16 array (stride ld)
+__device__ __forceinline__ bfrag gather8(const bf* base, int k0, int c, int ld)
+{
+    bfrag r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = base[(k0 + e) * ld + c];
+    return r;
+}
+
+__device__ __forceinline__ bfrag scale8(bfrag x, float f)
+{
+    bfrag r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (bf)((float)x[e] * f);
+    return r;
+}
+
+template <int DK>
+struct GkLds {
+    static constexpr int KS = DK + 4;              // row stride of KY, EA, QA (bf16)
+    static constexpr int RS = DK + 4;              // row stride of the fp32 results / dG
+    static constexpr int IN_A = 0;                 // dA, dP [64][LT] bf16
+    static constexpr int IN_K = IN_A + 2 * 64 * LT * 2;   // KY, EA, QA [64][KS] bf16
+    static constexpr int SZ_IN = IN_K + 3 * 64 * KS * 2;
+    static constexpr int SZ_RES = 3 * 64 * RS * 4;        // deA (then dG), dqP, kak fp32 [64][RS]
+    static constexpr int BIG = SZ_IN > SZ_RES ? SZ_IN : SZ_RES;
+};
+
 template <int DK, typename Tg>
 __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
 {
-    constexpr int CG = DK / 4, R = DK / 16;
+    using L = GkLds<DK>;
+    constexpr int CG = DK / 4, R = DK / 16, NCT = DK / 16, CPW = (NCT + 3) / 4;
+    constexpr int KS = L::KS, RS = L::RS;
+    constexpr int NV = 64 * DK / 4 / kThreads;
+    typedef typename GateVec<Tg>::type gvec;
     __shared__ __attribute__((aligned(16))) float G[64 * DK];
-    __shared__ __attribute__((aligned(16))) bf KYE[2 * 64 * DK];
-    __shared__ __attribute__((aligned(16))) bf Q[64 * DK];
-    __shared__ __attribute__((aligned(16))) float dA[64 * 64];
-    __shared__ __attribute__((aligned(16))) float dP[64 * 64];
+    __shared__ __attribute__((aligned(16))) char big[L::BIG];
     __shared__ float ext[(kThreads / CG) * DK];                // per row group: sum of dKtil * Ktil
     __shared__ float tot[kThreads];
-    bf* KY = KYE;                                               // k_s exp(G_j0(s) - G_s)
-    bf* E = KYE + 64 * DK;                                      // e = b k
-    float* dG = reinterpret_cast<float*>(KYE);                  // [64][DK] over KY and E once they are used
+    bf* dAl = reinterpret_cast<bf*>(big + L::IN_A);
+    bf* dPl = dAl + 64 * LT;
+    bf* KYl = reinterpret_cast<bf*>(big + L::IN_K);
+    bf* EAl = KYl + 64 * KS;
+    bf* QAl = EAl + 64 * KS;
+    float* deAl = reinterpret_cast<float*>(big);               // results, after the products
+    float* dqPl = deAl + 64 * RS;
+    float* kakl = dqPl + 64 * RS;
+    float* dG = deAl;                                          // over deA, element by element
 
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+    const int wave = tid >> 6;
     const int nt = a.nt;
     const int64_t ci = blockIdx.x;
     const int64_t chain = ci / nt;
@@ -666,189 +717,159 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
     const float* s_dA = s_dP + 4096;
     const float* s_dGL = s_dA + 4096;
 
+    // ---- phase A: loads (raw), then dA, dP, G, KY, EA, QA into LDS ----------
     {
         f32x4 xa[4], xp[4];
+        gvec ax[NV], bx[NV];
+        bf16x4 kx[NV], qx[NV];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int i = tid + u * kThreads;
             xa[u] = *reinterpret_cast<const f32x4*>(s_dA + 4 * i);
             xp[u] = *reinterpret_cast<const f32x4*>(s_dP + 4 * i);
         }
+        cld_load<DK>(ax, agt, row0, H, Ln);
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int i = tid + u * kThreads, r = i / CG, c4 = 4 * (i - r * CG);
+            const int64_t o = (row0 + (r < Ln ? r : Ln - 1) * H) * DK + c4;
+            kx[u] = *reinterpret_cast<const bf16x4*>(kg + o);
+            qx[u] = *reinterpret_cast<const bf16x4*>(qg + o);
+            bx[u] = *reinterpret_cast<const gvec*>(bgt + o);
+        }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int i = tid + u * kThreads;
-            *reinterpret_cast<f32x4*>(&dA[4 * i]) = xa[u];
-            *reinterpret_cast<f32x4*>(&dP[4 * i]) = xp[u];
+            const int i = tid + u * kThreads, r = i >> 4, s4 = 4 * (i & 15);
+            st_vec4(dAl + r * LT + s4, xa[u]);
+            st_vec4(dPl + r * LT + s4, xp[u]);
         }
-    }
-    cum_log_decay<DK>(G, tot, agt, row0, H, Ln);
-    {
-        constexpr int NV = 64 * DK / 4 / kThreads;
-        f32x4 kx[NV], qx[NV], bx[NV];
+        cld_scan<DK, Tg>(G, tot, ax, Ln);
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
-            const int i = tid + u * kThreads, r = i / (DK / 4), c4 = 4 * (i - r * (DK / 4));
-            const int64_t o = (row0 + r * H) * DK + c4;
-            const bool ok = r < Ln;
-            kx[u] = ok ? ld_vec4(kg + o) : f32x4{0.f, 0.f, 0.f, 0.f};
-            qx[u] = ok ? ld_vec4(qg + o) : f32x4{0.f, 0.f, 0.f, 0.f};
-            bx[u] = ok ? ld_gate4(bgt + o) : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int u = 0; u < NV; ++u) {
-            const int i = tid + u * kThreads, r = i / (DK / 4), c4 = 4 * (i - r * (DK / 4));
+            const int i = tid + u * kThreads, r = i / CG, c4 = 4 * (i - r * CG);
             const f32x4 g4 = *reinterpret_cast<const f32x4*>(&G[r * DK + c4]);
             const f32x4 gj = *reinterpret_cast<const f32x4*>(&G[(r & ~15) * DK + c4]);
-            f32x4 ky;
+            const bool ok = r < Ln;
+            const f32x4 k4 = IOB::unpack4(kx[u]), q4 = IOB::unpack4(qx[u]), b4 = widen4(bx[u]);
+            f32x4 ky, ea, qa;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ky[e] = kx[u][e] * __expf(gj[e] - g4[e]);
-            st_vec4(KY + r * DK + c4, ky);
-            st_vec4(E + r * DK + c4, bx[u] * kx[u]);
-            st_vec4(Q + r * DK + c4, qx[u]);
+            for (int e = 0; e < 4; ++e) {
+                const float up = __expf(g4[e] - gj[e]);        // <= 1
+                ky[e] = ok ? k4[e] * __expf(gj[e] - g4[e]) : 0.f;
+                ea[e] = ok ? b4[e] * k4[e] * up : 0.f;
+                qa[e] = ok ? q4[e] * up : 0.f;
+            }
+            st_vec4(KYl + r * KS + c4, ky);
+            st_vec4(EAl + r * KS + c4, ea);
+            st_vec4(QAl + r * KS + c4, qa);
         }
     }
     __syncthreads();
 
-    const int c0 = 4 * (tid % CG), r0 = (tid / CG) * R, J0 = r0 >> 4;
-    // row side: sum over earlier columns s of dA[r,s] k_s R[r,s] (and dP with k)
-    float deA[R][4], dqP[R][4];
+    // ---- products on the matrix cores: column tiles ct = wave + 4 m ----------
+    f32x4 acc[CPW][4][4];                                      // [tile][row block][rowA rowP colA colP]
 #pragma unroll
-    for (int rr = 0; rr < R; ++rr)
+    for (int m = 0; m < CPW; ++m) {
+        const int ct = wave + 4 * m;
+        const int c = 16 * (ct < NCT ? ct : 0) + l16;
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) deA[rr][cc] = dqP[rr][cc] = 0.f;
-    for (int J = 0; J <= J0; ++J) {
-        const int j0 = 16 * J;
-        float pa[R][4], pp[R][4];
+        for (int I = 0; I < 4; ++I) {
 #pragma unroll
-        for (int rr = 0; rr < R; ++rr)
+            for (int qd = 0; qd < 4; ++qd) acc[m][I][qd] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (ct >= NCT) continue;
+            const float gI = G[16 * I * DK + c];
+            // row side: s over blocks 0..I (dA, dP are zero for s >= r)
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc) pa[rr][cc] = pp[rr][cc] = 0.f;
-        for (int s0 = j0; s0 < j0 + 16; s0 += 4) {
-            f32x4 ky[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ky[e] = IOB::unpack4(*reinterpret_cast<const bf16x4*>(&KY[(s0 + e) * DK + c0]));
-#pragma unroll
-            for (int rr = 0; rr < R; ++rr) {
-                const f32x4 x = *reinterpret_cast<const f32x4*>(&dA[(r0 + rr) * 64 + s0]);
-                const f32x4 y = *reinterpret_cast<const f32x4*>(&dP[(r0 + rr) * 64 + s0]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-#pragma unroll
-                    for (int cc = 0; cc < 4; ++cc) {
-                        pa[rr][cc] += x[e] * ky[e][cc];
-                        pp[rr][cc] += y[e] * ky[e][cc];
-                    }
+            for (int kb = 0; kb < (I + 2) / 2; ++kb) {
+                const int s0 = kb * 32 + grp * 8, J = s0 >> 4;
+                const float f = J < I ? __expf(gI - G[16 * J * DK + c]) : 1.f;
+                const bfrag bk = scale8(gather8(KYl, s0, c, KS), f);
+                acc[m][I][0] = IOB::mma(acc[m][I][0], fr(dAl, 16 * I + l16, LT, kb, grp), bk);
+                acc[m][I][1] = IOB::mma(acc[m][I][1], fr(dPl, 16 * I + l16, LT, kb, grp), bk);
             }
-        }
+            // column side: r over blocks I..3 (dA[r][s] is zero for r <= s)
 #pragma unroll
-        for (int rr = 0; rr < R; ++rr)
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-                const float xr = __expf(G[(r0 + rr) * DK + c0 + cc] - G[j0 * DK + c0 + cc]);
-                deA[rr][cc] += pa[rr][cc] * xr;
-                dqP[rr][cc] += pp[rr][cc] * xr;
-            }
-    }
-    // column side: sum over later rows r of dA[r,s] e_r R[r,s] (and dP with q)
-    float dkA[R][4], dkP[R][4];
-#pragma unroll
-    for (int rr = 0; rr < R; ++rr)
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) dkA[rr][cc] = dkP[rr][cc] = 0.f;
-    {
-        const int j0 = 16 * J0;
-        const f32x4 gj = *reinterpret_cast<const f32x4*>(&G[j0 * DK + c0]);
-        for (int r = j0; r < 64; ++r) {
-            const f32x4 e4 = IOB::unpack4(*reinterpret_cast<const bf16x4*>(&E[r * DK + c0]));
-            const f32x4 q4 = IOB::unpack4(*reinterpret_cast<const bf16x4*>(&Q[r * DK + c0]));
-            const f32x4 g4 = *reinterpret_cast<const f32x4*>(&G[r * DK + c0]);
-            f32x4 ea, qa;
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-                const float x = __expf(g4[cc] - gj[cc]);
-                ea[cc] = e4[cc] * x;
-                qa[cc] = q4[cc] * x;
-            }
-            if constexpr (R % 4 == 0) {
-#pragma unroll
-                for (int r4 = 0; r4 < R; r4 += 4) {
-                    const f32x4 x = *reinterpret_cast<const f32x4*>(&dA[r * 64 + r0 + r4]);
-                    const f32x4 y = *reinterpret_cast<const f32x4*>(&dP[r * 64 + r0 + r4]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-#pragma unroll
-                        for (int cc = 0; cc < 4; ++cc) {
-                            dkA[r4 + e][cc] += x[e] * ea[cc];
-                            dkP[r4 + e][cc] += y[e] * qa[cc];
-                        }
-                }
-            } else {
-#pragma unroll
-                for (int rr = 0; rr < R; ++rr) {
-                    const float x = dA[r * 64 + r0 + rr], y = dP[r * 64 + r0 + rr];
-#pragma unroll
-                    for (int cc = 0; cc < 4; ++cc) {
-                        dkA[rr][cc] += x * ea[cc];
-                        dkP[rr][cc] += y * qa[cc];
-                    }
-                }
+            for (int kb = I / 2; kb < 2; ++kb) {
+                const int r0 = kb * 32 + grp * 8, Ir = r0 >> 4;
+                const float f = Ir > I ? __expf(G[16 * Ir * DK + c] - gI) : 1.f;
+                const int s = 16 * I + l16;
+                const bfrag be = scale8(gather8(EAl, r0, c, KS), f);
+                const bfrag bq = scale8(gather8(QAl, r0, c, KS), f);
+                acc[m][I][2] = IOB::mma(acc[m][I][2], gather8(dAl, r0, s, LT), be);
+                acc[m][I][3] = IOB::mma(acc[m][I][3], gather8(dPl, r0, s, LT), bq);
             }
         }
     }
-    __syncthreads();                                       // KY and E are read for the last time
-    // per row: the gradients of q, k, b and dG; the next row's inputs are
-    // requested before this row's results are stored
+    __syncthreads();                                           // inputs read; results overwrite them
+#pragma unroll
+    for (int m = 0; m < CPW; ++m) {
+        const int ct = wave + 4 * m;
+        if (ct >= NCT) continue;
+        const int c = 16 * ct + l16;
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            const float gI = G[16 * I * DK + c];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * I + 4 * grp + i;
+                const float d = G[r * DK + c] - gI;            // <= 0
+                const float xr = __expf(d), y = __expf(-d);
+                deAl[r * RS + c] = acc[m][I][0][i] * xr;
+                dqPl[r * RS + c] = acc[m][I][1][i] * xr;
+                kakl[r * RS + c] = (acc[m][I][2][i] + acc[m][I][3][i]) * y;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- per row: the gradients of q, k, b and dG (all loads first) ---------
     {
         bf* dq = static_cast<bf*>(a.dq);
         bf* dk_out = static_cast<bf*>(a.dk_out);
         Tg* db = static_cast<Tg*>(a.db);
-        const int j0 = 16 * J0;
-        float ex[4] = {0.f, 0.f, 0.f, 0.f};
-        struct RowIn {
-            f32x4 q, k, b, dQh, dEh, dKt;
-        };
-        auto load = [&](int rr) {
-            RowIn x;
-            const int r = r0 + rr;
-            x.dQh = *reinterpret_cast<const f32x4*>(s_dQh + r * DK + c0);
-            x.dEh = *reinterpret_cast<const f32x4*>(s_dEh + r * DK + c0);
-            x.dKt = *reinterpret_cast<const f32x4*>(s_dKt + r * DK + c0);
-            if (r < Ln) {
-                const int64_t o = (row0 + r * H) * DK + c0;
-                x.q = ld_vec4(qg + o);
-                x.k = ld_vec4(kg + o);
-                x.b = ld_gate4(bgt + o);
-            } else {
-                x.q = x.k = x.b = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-            return x;
-        };
-        RowIn nx = load(0);
+        const int c0 = 4 * (tid % CG), r0 = (tid / CG) * R;
+        bf16x4 qr[R], kr[R];
+        gvec br[R];
+        f32x4 dQh[R], dEh[R], dKt[R];
 #pragma unroll
         for (int rr = 0; rr < R; ++rr) {
-            const RowIn cx = nx;
-            if (rr + 1 < R) nx = load(rr + 1);
             const int r = r0 + rr;
-            f32x4 oq, ok, ob;
+            const int64_t o = (row0 + (r < Ln ? r : Ln - 1) * H) * DK + c0;
+            dQh[rr] = *reinterpret_cast<const f32x4*>(s_dQh + r * DK + c0);
+            dEh[rr] = *reinterpret_cast<const f32x4*>(s_dEh + r * DK + c0);
+            dKt[rr] = *reinterpret_cast<const f32x4*>(s_dKt + r * DK + c0);
+            qr[rr] = *reinterpret_cast<const bf16x4*>(qg + o);
+            kr[rr] = *reinterpret_cast<const bf16x4*>(kg + o);
+            br[rr] = *reinterpret_cast<const gvec*>(bgt + o);
+        }
+        float ex[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
+            const int r = r0 + rr;
+            const bool ok = r < Ln;
+            const f32x4 q4 = IOB::unpack4(qr[rr]), k4 = IOB::unpack4(kr[rr]), b4 = widen4(br[rr]);
+            const f32x4 deA = *reinterpret_cast<const f32x4*>(&deAl[r * RS + c0]);
+            const f32x4 dqP = *reinterpret_cast<const f32x4*>(&dqPl[r * RS + c0]);
+            const f32x4 kak = *reinterpret_cast<const f32x4*>(&kakl[r * RS + c0]);
+            f32x4 oq, okk, ob, dg;
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) {
                 const int c = c0 + cc;
                 const float g = G[r * DK + c], gam = __expf(g), kt = __expf(G[63 * DK + c] - g);
-                const float y = __expf(G[j0 * DK + c] - g);
-                const float qv = cx.q[cc], kv = cx.k[cc], bv = cx.b[cc], ev = bv * kv;
-                const float de = gam * cx.dEh[cc] + deA[rr][cc];
-                const float kak = (dkA[rr][cc] + dkP[rr][cc]) * y;
-                oq[cc] = gam * cx.dQh[cc] + dqP[rr][cc];
-                ok[cc] = kt * cx.dKt[cc] + de * bv + kak;
+                const float qv = ok ? q4[cc] : 0.f, kv = ok ? k4[cc] : 0.f, bv = ok ? b4[cc] : 0.f, ev = bv * kv;
+                const float de = gam * dEh[rr][cc] + deA[cc];
+                oq[cc] = gam * dQh[rr][cc] + dqP[cc];
+                okk[cc] = kt * dKt[rr][cc] + de * bv + kak[cc];
                 ob[cc] = de * kv;
-                dG[r * DK + c] = cx.dQh[cc] * gam * qv + cx.dEh[cc] * gam * ev - cx.dKt[cc] * kv * kt +
-                                 ev * deA[rr][cc] + qv * dqP[rr][cc] - kv * kak;
-                ex[cc] += cx.dKt[cc] * kv * kt;
+                dg[cc] = dQh[rr][cc] * gam * qv + dEh[rr][cc] * gam * ev - dKt[rr][cc] * kv * kt + ev * deA[cc] +
+                         qv * dqP[cc] - kv * kak[cc];
+                ex[cc] += dKt[rr][cc] * kv * kt;
             }
-            if (r < Ln) {
+            *reinterpret_cast<f32x4*>(&dG[r * RS + c0]) = dg;
+            if (ok) {
                 const int64_t o = (row0 + r * H) * DK + c0;
                 st_vec4(dq + o, oq);
-                st_vec4(dk_out + o, ok);
+                st_vec4(dk_out + o, okk);
 #pragma unroll
                 for (int cc = 0; cc < 4; ++cc) gs(db, o + cc, ob[cc]);
             }
@@ -862,7 +883,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
     if (tid < DK) {
         float x = s_dGL[tid] * __expf(G[63 * DK + tid]);
         for (int g = 0; g < kThreads / CG; ++g) x += ext[g * DK + tid];
-        dG[63 * DK + tid] += x;
+        dG[63 * RS + tid] += x;
     }
     __syncthreads();
     {
@@ -870,25 +891,34 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
         const int c = tid % DK, g = tid / DK;
         float run = 0.f;
         for (int r = (g + 1) * sl - 1; r >= g * sl; --r) {
-            run += dG[r * DK + c];
-            dG[r * DK + c] = run;
+            run += dG[r * RS + c];
+            dG[r * RS + c] = run;
         }
         tot[g * DK + c] = run;
         __syncthreads();
         float carry = 0.f;
         for (int h = g + 1; h < nseg; ++h) carry += tot[h * DK + c];
         if (g + 1 < nseg)
-            for (int r = g * sl; r < (g + 1) * sl; ++r) dG[r * DK + c] += carry;
+            for (int r = g * sl; r < (g + 1) * sl; ++r) dG[r * RS + c] += carry;
     }
     __syncthreads();
     {
         Tg* dalpha = static_cast<Tg*>(a.dalpha);
-        for (int i = tid; i < Ln * (DK / 4); i += kThreads) {
-            const int r = i / (DK / 4), c4 = 4 * (i - r * (DK / 4));
-            const int64_t o = (row0 + r * H) * DK + c4;
-            const f32x4 al = ld_gate4(agt + o);
+        gvec al[NV];
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc) gs(dalpha, o + cc, dG[r * DK + c4 + cc] / al[cc]);
+        for (int u = 0; u < NV; ++u) {
+            const int i = tid + u * kThreads, r = i / CG, c4 = 4 * (i - r * CG);
+            al[u] = *reinterpret_cast<const gvec*>(agt + (row0 + (r < Ln ? r : Ln - 1) * H) * DK + c4);
+        }
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int i = tid + u * kThreads, r = i / CG, c4 = 4 * (i - r * CG);
+            if (r < Ln) {
+                const int64_t o = (row0 + r * H) * DK + c4;
+                const f32x4 a4 = widen4(al[u]);
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) gs(dalpha, o + cc, dG[r * RS + c4 + cc] / a4[cc]);
+            }
         }
     }
 }
