@@ -229,6 +229,14 @@ BwdWrap bwd_wrap(const gdn2_problem* p)
 {
     BwdWrap w{};
     w.core = *p;
+    w.l = bwd_layout(p);
+    // the matrix-core kernels apply the prologue options themselves; only
+    // shared query/key heads (or the vector-ALU path) need the mappings
+    if (w.l.mf && nvh(p) == p->H) {
+        w.core.Hv = 0;
+        w.total = w.l.total;
+        return w;
+    }
     w.qk = (p->flags & GDN2_FLAG_QK_L2NORM) != 0 || nvh(p) != p->H;
     w.gates = (p->flags & GDN2_FLAG_GATE_LOGITS) != 0;
     w.core.flags = 0;
@@ -256,7 +264,8 @@ BwdWrap bwd_wrap(const gdn2_problem* p)
     return w;
 }
 
-// the core backward: p has no flags and H value heads = query/key heads
+// the core backward: H value heads = query/key heads; prologue flags only on
+// the matrix-core path
 int bwd_core(const gdn2_problem* p, const BwdLayout& l, const void* q, const void* k, const void* v,
              const void* alpha, const void* b, const void* w, const float* S0, const void* dO, const float* dS_T,
              void* dq, void* dk, void* dv, void* dalpha, void* db, void* dw, float* dS0, char* ws, hipStream_t s)
@@ -268,9 +277,10 @@ int bwd_core(const gdn2_problem* p, const BwdLayout& l, const void* q, const voi
     void* dslT = l.mf ? ws + l.dslT : nullptr;
     const int64_t nch = p->B * p->H;
     const int64_t total = nch * nchunks(p);
+    if (p->flags != 0 && !l.mf) return GDN2_ERR_SHAPE;   // never reached: the mappings clear the flags
     if (nchunks(p) > 0) {
         gdn2::PrepArgs pa{q, k, v, alpha, b, w, ws, l.block, p->B, p->T, p->H, p->H,
-                          (int)p->dv, (int)nchunks(p), 0, nullptr, 0, l.t_off};
+                          (int)p->dv, (int)nchunks(p), (int)p->flags, nullptr, 0, l.t_off};
         st = launch_status(gdn2::launch_chunk_prep(pa, (int)p->dk, is_bf16(p), gates_bf16(p), s));
         if (st) return st;
         const int vs = gdn2::chunk_state_slice(nch, (int)p->dv, (int)p->dk, (int)io_size(p));
@@ -288,9 +298,9 @@ int bwd_core(const gdn2_problem* p, const BwdLayout& l, const void* q, const voi
     float* gsc = reinterpret_cast<float*>(ws + l.scratch);
     if (l.mf) {
         gdn2::GradVArgs va{ws, l.block, l.t_off, k, v, alpha, b, w, dO, chk, chkT, dsl, dslT, dw, dv, gsc,
-                           p->B, p->T, p->H, (int)p->dk, (int)p->dv, (int)nchunks(p), total};
+                           p->B, p->T, p->H, (int)p->dk, (int)p->dv, (int)nchunks(p), total, (int)p->flags};
         gdn2::GradKArgs ka{q, k, alpha, b, gsc, dq, dk, dalpha, db, p->B, p->T, p->H, (int)p->dk,
-                           (int)nchunks(p), total};
+                           (int)nchunks(p), total, (int)p->flags};
         return launch_status(gdn2::launch_chunk_grad_mf(va, ka, gates_bf16(p), s));
     }
     gdn2::GradArgs ga{q, k, v, alpha, b, w, dO, chk, dsl, dq, dk, dv, dalpha, db, dw, gsc, p->B, p->T, p->H,

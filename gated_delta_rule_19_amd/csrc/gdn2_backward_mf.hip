@@ -60,6 +60,22 @@ __device__ inline bfrag fr32(const float* base, int row, int64_t ld, int kb, int
 }
 
 template <typename T> __device__ inline float gf(const T* p, int64_t i) { return Io<T>::to_f(p[i]); }
+
+// sum over the N consecutive lanes that hold one row (N a power of two <= 32)
+template <int N>
+__device__ __forceinline__ float lanes_sum(float x)
+{
+#pragma unroll
+    for (int off = 1; off < N; off <<= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+// 1 / sqrt(|x|^2 + eps) of a row spread over N lanes, 4 channels each
+template <int N>
+__device__ __forceinline__ float row_rnorm(f32x4 x)
+{
+    return __builtin_amdgcn_rsqf(lanes_sum<N>(x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3]) + kL2normEps);
+}
 template <typename T> __device__ inline void gs(T* p, int64_t i, float x) { p[i] = Io<T>::from_f(x); }
 
 }  // namespace
@@ -71,7 +87,8 @@ __host__ __device__ inline int64_t gradmf_scratch_floats(int dk) { return 3 * 64
 // G[r][c] = sum of log alpha over tokens 0..r of the chunk (alpha = 1 past its
 // end), for 256 threads: logs in parallel (every load issued before the first
 // use), then a scan of 256/DK segments per channel with the segment totals
-// carried through `tot`.  cld_load issues the loads, cld_scan does the rest.
+// carried through `tot`.  cld_load issues the loads, cld_scan does the rest
+// (alpha given as logits: alpha = sigmoid(logit)).
 template <int DK, typename Tg>
 __device__ __attribute__((always_inline)) inline void cld_load(typename GateVec<Tg>::type (&x)[64 * DK / 4 / kThreads],
                                                                const Tg* alpha, int64_t row0, int64_t H, int Ln)
@@ -88,14 +105,14 @@ __device__ __attribute__((always_inline)) inline void cld_load(typename GateVec<
 template <int DK, typename Tg>
 __device__ __attribute__((always_inline)) inline void cld_scan(float* G, float* tot,
                                                                const typename GateVec<Tg>::type (&x)[64 * DK / 4 / kThreads],
-                                                               int Ln)
+                                                               int Ln, bool logits)
 {
     constexpr int NV = 64 * DK / 4 / kThreads;
     const int tid = threadIdx.x;
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
         const int i = tid + u * kThreads, r = i / (DK / 4), c4 = 4 * (i - r * (DK / 4));
-        const f32x4 a = widen4(x[u]);
+        const f32x4 a = logits ? sigmoid4(widen4(x[u])) : widen4(x[u]);
         f32x4 l;
 #pragma unroll
         for (int e = 0; e < 4; ++e) l[e] = r < Ln ? __logf(a[e]) : 0.f;   // alpha = 1 past the end
@@ -117,15 +134,6 @@ __device__ __attribute__((always_inline)) inline void cld_scan(float* G, float* 
     if (g > 0)
         for (int r = g * sl; r < (g + 1) * sl; ++r) G[r * DK + c] += carry;
     __syncthreads();
-}
-
-template <int DK, typename Tg>
-__device__ __attribute__((always_inline)) inline void cum_log_decay(float* G, float* tot, const Tg* alpha,
-                                                                    int64_t row0, int64_t H, int Ln)
-{
-    typename GateVec<Tg>::type x[64 * DK / 4 / kThreads];
-    cld_load<DK>(x, alpha, row0, H, Ln);
-    cld_scan<DK, Tg>(G, tot, x, Ln);
 }
 
 // LDS regions of k_chunk_grad_val (bytes), sized for dk = dv = 128
@@ -249,6 +257,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
     float* s_dP = sc + 3 * 64 * DK;
     float* s_dA = s_dP + 4096;
     float* s_dGL = s_dA + 4096;
+    const bool logits = (a.flags & kFlagGateLogits) != 0, l2 = (a.flags & kFlagQkL2norm) != 0;
+    const float bscale = (a.flags & kFlagNegEigval) ? 2.f : 1.f;
 
     // ---- phase 0: operands into LDS ----------------------------------------
     // Every global load of the phase is issued before the first LDS write (one
@@ -320,12 +330,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
 #pragma unroll
         for (int e = 0; e < 8; ++e) dOtl[(j0 + e) * LT + r] = oq[m][e];
     }
-    cld_scan<DK, Tg>(Gl, tot, ax, Ln);
+    cld_scan<DK, Tg>(Gl, tot, ax, Ln, logits);
 #pragma unroll
     for (int u = 0; u < NV; ++u) {                                  // Eh = Gamma b k (zero past the end)
         const int i = tid + u * kThreads, r = i / (DK / 4), c4 = 4 * (i - r * (DK / 4));
         const f32x4 g4 = *reinterpret_cast<const f32x4*>(&Gl[r * DK + c4]);
-        const f32x4 b4 = widen4(bx[u]), k4 = IOB::unpack4(kx[u]);
+        const f32x4 b4 = logits ? sigmoid4(widen4(bx[u])) * bscale : widen4(bx[u]);
+        f32x4 k4 = IOB::unpack4(kx[u]);
+        if (l2) k4 = k4 * row_rnorm<DK / 4>(k4);
         f32x4 x;
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = r < Ln ? __expf(g4[e]) * b4[e] * k4[e] : 0.f;
@@ -538,8 +550,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
         for (int i = 0; i < 4; ++i) {
             if (r + i < Ln) {
                 const int64_t o = (row0 + (r + i) * H) * DV + j;
-                gs(dwg, o, acc[i] * Io<bf>::to_f(vt[m][i]));
-                gs(dvg, o, acc[i] * gate_f(wt[m][i]));
+                const float wr = gate_f(wt[m][i]), sw = logits ? sigmoid_f(wr) : wr;
+                const float dwa = acc[i] * Io<bf>::to_f(vt[m][i]);     // gradient of the activated gate
+                gs(dwg, o, logits ? dwa * sw * (1.f - sw) : dwa);
+                gs(dvg, o, acc[i] * sw);
             }
         }
     }
@@ -548,7 +562,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
 #pragma unroll
     for (int u = 0; u < NVV; ++u) {
         const int i = tid + u * kThreads, r = i / (DV / 4), j4 = 4 * (i - r * (DV / 4));
-        const f32x4 x = widen4(wx[u]) * IOB::unpack4(vx[u]);
+        const f32x4 x = (logits ? sigmoid4(widen4(wx[u])) : widen4(wx[u])) * IOB::unpack4(vx[u]);
         st_vec4(ul + r * ldv + j4, r < Ln ? x : f32x4{0.f, 0.f, 0.f, 0.f});
     }
     __syncthreads();
@@ -716,6 +730,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
     const float* s_dP = sc + 3 * 64 * DK;
     const float* s_dA = s_dP + 4096;
     const float* s_dGL = s_dA + 4096;
+    const bool logits = (a.flags & kFlagGateLogits) != 0, l2 = (a.flags & kFlagQkL2norm) != 0;
+    const float bscale = (a.flags & kFlagNegEigval) ? 2.f : 1.f;
 
     // ---- phase A: loads (raw), then dA, dP, G, KY, EA, QA into LDS ----------
     {
@@ -743,14 +759,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
             st_vec4(dAl + r * LT + s4, xa[u]);
             st_vec4(dPl + r * LT + s4, xp[u]);
         }
-        cld_scan<DK, Tg>(G, tot, ax, Ln);
+        cld_scan<DK, Tg>(G, tot, ax, Ln, logits);
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
             const int i = tid + u * kThreads, r = i / CG, c4 = 4 * (i - r * CG);
             const f32x4 g4 = *reinterpret_cast<const f32x4*>(&G[r * DK + c4]);
             const f32x4 gj = *reinterpret_cast<const f32x4*>(&G[(r & ~15) * DK + c4]);
             const bool ok = r < Ln;
-            const f32x4 k4 = IOB::unpack4(kx[u]), q4 = IOB::unpack4(qx[u]), b4 = widen4(bx[u]);
+            f32x4 k4 = IOB::unpack4(kx[u]), q4 = IOB::unpack4(qx[u]);
+            const f32x4 b4 = logits ? sigmoid4(widen4(bx[u])) * bscale : widen4(bx[u]);
+            if (l2) {
+                k4 = k4 * row_rnorm<CG>(k4);
+                q4 = q4 * row_rnorm<CG>(q4);
+            }
             f32x4 ky, ea, qa;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -847,7 +868,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
         for (int rr = 0; rr < R; ++rr) {
             const int r = r0 + rr;
             const bool ok = r < Ln;
-            const f32x4 q4 = IOB::unpack4(qr[rr]), k4 = IOB::unpack4(kr[rr]), b4 = widen4(br[rr]);
+            f32x4 q4 = IOB::unpack4(qr[rr]), k4 = IOB::unpack4(kr[rr]);
+            const f32x4 braw = widen4(br[rr]);
+            const f32x4 sb = logits ? sigmoid4(braw) : braw, b4 = logits ? sb * bscale : braw;
+            float nq = 1.f, nk = 1.f;                                 // 1 / norms with the L2 option
+            if (l2) {
+                nq = row_rnorm<CG>(q4);
+                nk = row_rnorm<CG>(k4);
+                q4 = q4 * nq;
+                k4 = k4 * nk;
+            }
             const f32x4 deA = *reinterpret_cast<const f32x4*>(&deAl[r * RS + c0]);
             const f32x4 dqP = *reinterpret_cast<const f32x4*>(&dqPl[r * RS + c0]);
             const f32x4 kak = *reinterpret_cast<const f32x4*>(&kakl[r * RS + c0]);
@@ -866,6 +896,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
                 ex[cc] += dKt[rr][cc] * kv * kt;
             }
             *reinterpret_cast<f32x4*>(&dG[r * RS + c0]) = dg;
+            if (l2) {   // through the norms: dx = (dxh - xh (xh . dxh)) / |x|
+                const f32x4 qh = ok ? q4 : f32x4{0.f, 0.f, 0.f, 0.f}, kh = ok ? k4 : f32x4{0.f, 0.f, 0.f, 0.f};
+                const float sq = lanes_sum<CG>(qh[0] * oq[0] + qh[1] * oq[1] + qh[2] * oq[2] + qh[3] * oq[3]);
+                const float sk = lanes_sum<CG>(kh[0] * okk[0] + kh[1] * okk[1] + kh[2] * okk[2] + kh[3] * okk[3]);
+                oq = (oq - qh * sq) * nq;
+                okk = (okk - kh * sk) * nk;
+            }
+            if (logits) ob = ob * (sb * (1.f - sb)) * bscale;            // gradient of the logit
             if (ok) {
                 const int64_t o = (row0 + r * H) * DK + c0;
                 st_vec4(dq + o, oq);
@@ -916,8 +954,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
             if (r < Ln) {
                 const int64_t o = (row0 + r * H) * DK + c4;
                 const f32x4 a4 = widen4(al[u]);
+                if (logits) {   // d logit = (dG / alpha) alpha (1 - alpha), alpha = sigmoid(logit)
+                    const f32x4 s4 = sigmoid4(a4);
 #pragma unroll
-                for (int cc = 0; cc < 4; ++cc) gs(dalpha, o + cc, dG[r * RS + c4 + cc] / a4[cc]);
+                    for (int cc = 0; cc < 4; ++cc) gs(dalpha, o + cc, dG[r * RS + c4 + cc] * (1.f - s4[cc]));
+                } else {
+#pragma unroll
+                    for (int cc = 0; cc < 4; ++cc) gs(dalpha, o + cc, dG[r * RS + c4 + cc] / a4[cc]);
+                }
             }
         }
     }

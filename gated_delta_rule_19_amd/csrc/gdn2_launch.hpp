@@ -71,7 +71,9 @@ struct GradArgs {
     int64_t B, T, H; int dk, dv, nt; int64_t total;
 };
 
-// Matrix-core per-chunk gradients (bf16 I/O): the value-side launch reads the
+// Matrix-core per-chunk gradients (bf16 I/O; with the prologue flags the
+// gates are logits and q/k unnormalised, and the gradients are those of the
+// raw inputs): the value-side launch reads the
 // forward workspace (blocks of ws_block bytes with T at t_off), the
 // checkpoints S_chk/S_chkT and dSL/dSLT, dO, v, w, b, k, alpha; writes dw, dv
 // and an fp32 scratch block per chunk that the key-side launch reads with q,
@@ -82,6 +84,7 @@ struct GradVArgs {
     const float* S_chk; const void* S_chkT; const float* dSL; const void* dSLT;
     void* dw; void* dv_out; float* gsc;
     int64_t B, T, H; int dk, dv, nt; int64_t total;
+    int flags;              // prologue options applied in-kernel (gradients of the logits, raw q/k)
 };
 
 struct GradKArgs {
@@ -89,6 +92,7 @@ struct GradKArgs {
     const float* gsc;
     void* dq; void* dk_out; void* dalpha; void* db;
     int64_t B, T, H; int dk, nt; int64_t total;
+    int flags;
 };
 
 // Prologue options in the backward.  Query/key rows (rows = B*T*Hk of dk

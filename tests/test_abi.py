@@ -371,13 +371,20 @@ def _bwd_ws(B, T, H, dk, dv, io, gate, flags, Hv):
     return g.lib().gdn2_chunk_bwd_workspace_size(ctypes.byref(bnd.Problem(B, T, H, dk, dv, 64, io, gate, flags, Hv)))
 
 
-@pytest.mark.parametrize("flags,Hv,gate", [(0, 0, 0), (4, 0, 1), (1, 0, 1), (3, 6, 0), (0, 6, 1), (7, 6, 1)])
-def test_backward_workspace_with_options(flags, Hv, gate):
-    """With the prologue options or shared query/key heads the workspace is the
-    core's (no flags, one query/key head per value head, fp32 gates with logits)
-    followed by 256-aligned activated inputs and their gradients."""
-    B, T, H, dk, dv, io = 2, 100, 3, 64, 32, 1
+@pytest.mark.parametrize("flags,Hv,gate,dv", [(0, 0, 0, 32), (4, 0, 1, 32), (1, 0, 1, 32), (3, 6, 0, 32),
+                                                (0, 6, 1, 32), (7, 6, 1, 32), (7, 0, 1, 48), (4, 0, 0, 48)])
+def test_backward_workspace_with_options(flags, Hv, gate, dv):
+    """The matrix-core path (bf16 I/O, dk and dv in {32, 64, 128}) applies the prologue
+    options in-kernel: with one value head per query/key head its workspace is the plain
+    one.  Otherwise (shared query/key heads, or the vector-ALU path) the workspace is the
+    core's (no flags, one query/key head per value head, fp32 gates with logits) followed
+    by 256-aligned activated inputs and their gradients."""
+    B, T, H, dk, io = 2, 100, 3, 64, 1
     hv = Hv or H
+    mf = dv in (32, 64, 128)
+    if mf and hv == H:
+        assert _bwd_ws(B, T, H, dk, dv, io, gate, flags, Hv) == _bwd_ws(B, T, H, dk, dv, io, gate, 0, 0)
+        return
     core = _bwd_ws(B, T, hv, dk, dv, io, 0 if flags & 1 else gate, 0, 0)
     assert core > 0
     off = core

@@ -133,6 +133,12 @@ FULL_CASES = [
     (1, 150, 2, 4, 64, 64, BF16, BF16, LOG | NEG | L2, 0.05),
     (1, 64, 1, 1, 128, 64, BF16, F32, L2, 0.05),
     (2, 33, 2, 4, 128, 128, BF16, F32, 0, None),
+    # matrix-core shapes with one value head per query/key head: options applied in-kernel
+    (2, 100, 2, 2, 64, 64, BF16, BF16, LOG | NEG, 0.05),
+    (1, 130, 2, 2, 128, 128, BF16, F32, LOG | L2, None),
+    (1, 65, 3, 3, 32, 32, BF16, BF16, LOG | NEG | L2, 0.05),
+    (1, 200, 1, 1, 128, 128, BF16, F32, L2, 0.05),
+    (1, 47, 2, 2, 64, 128, BF16, F32, LOG, None),
 ]
 
 
