@@ -230,16 +230,19 @@ BwdWrap bwd_wrap(const gdn2_problem* p)
     BwdWrap w{};
     w.core = *p;
     w.l = bwd_layout(p);
-    // the matrix-core kernels apply the prologue options themselves; only
-    // shared query/key heads (or the vector-ALU path) need the mappings
-    if (w.l.mf && nvh(p) == p->H) {
+    // the matrix-core kernels apply the prologue options themselves; shared
+    // query/key heads still need q/k widened to the value heads (and their
+    // gradients summed per group, through the norm when it is on), and the
+    // vector-ALU path needs every mapping
+    const bool mf = w.l.mf;
+    if (mf && nvh(p) == p->H) {
         w.core.Hv = 0;
         w.total = w.l.total;
         return w;
     }
     w.qk = (p->flags & GDN2_FLAG_QK_L2NORM) != 0 || nvh(p) != p->H;
-    w.gates = (p->flags & GDN2_FLAG_GATE_LOGITS) != 0;
-    w.core.flags = 0;
+    w.gates = !mf && (p->flags & GDN2_FLAG_GATE_LOGITS) != 0;
+    w.core.flags = mf ? (p->flags & ~GDN2_FLAG_QK_L2NORM) : 0;   // gate options stay in-kernel
     w.core.H = nvh(p);
     w.core.Hv = 0;
     if (w.gates) w.core.gate_dtype = GDN2_F32;

@@ -385,14 +385,15 @@ def test_backward_workspace_with_options(flags, Hv, gate, dv):
     if mf and hv == H:
         assert _bwd_ws(B, T, H, dk, dv, io, gate, flags, Hv) == _bwd_ws(B, T, H, dk, dv, io, gate, 0, 0)
         return
-    core = _bwd_ws(B, T, hv, dk, dv, io, 0 if flags & 1 else gate, 0, 0)
+    gates_mapped = flags & 1 and not mf         # the matrix-core kernels take gate logits themselves
+    core = _bwd_ws(B, T, hv, dk, dv, io, 0 if gates_mapped else gate, 0, 0)
     assert core > 0
     off = core
     parts = []
     vrows = B * T * hv
     if flags & 4 or hv != H:
         parts += [vrows * dk * 2] * 4
-    if flags & 1:
+    if gates_mapped:
         parts += [vrows * dk * 4, vrows * dk * 4, vrows * dv * 4] * 2
     for n in parts:
         off = _up(off) + n
