@@ -206,3 +206,25 @@ def test_backward_full_size_with_options_sampled(dev):
         gs = {n: (_np(got[n])[bi:bi + 1, :, hi:hi + 1] if n != "dS0" else _np(got[n])[bi:bi + 1, hi:hi + 1])
               for n in NAMES}
         check(f"B4H16T2048 flags {fl} chain ({bi},{hi})", gs, want, 2e-2)
+
+
+@pytest.mark.parametrize("flags", [0, LOG | NEG | L2])
+@pytest.mark.parametrize("io", [F32, BF16])
+def test_backward_without_tokens(dev, io, flags):
+    """T = 0: the state passes through unchanged, so dS0 = dS_T (and no token gradient);
+    B = 0: nothing at all."""
+    B, H, dk, dv = 2, 3, 64, 64
+    for T in (0,):
+        inp = inputs.make_raw(B, T, H, dk, dv, io, 5, dev, s0_std=0.05, gate_logits=bool(flags & LOG),
+                              unit_qk=not flags & L2)
+        dO, dS_T = inputs.make_out_grads(B, T, H, dk, dv, io, 6, dev)
+        got = g.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["b"], inp["w"], dO, inp["S0"], dS_T,
+                          flags=flags)
+        torch.cuda.synchronize()
+        assert torch.equal(got["dS0"], dS_T)
+        assert got["dq"].numel() == 0 and got["dw"].numel() == 0
+    inp = inputs.make_raw(0, 10, H, dk, dv, io, 5, dev)
+    dO, _ = inputs.make_out_grads(0, 10, H, dk, dv, io, 6, dev)
+    got = g.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["b"], inp["w"], dO, flags=flags)
+    torch.cuda.synchronize()
+    assert got["dS0"].numel() == 0
