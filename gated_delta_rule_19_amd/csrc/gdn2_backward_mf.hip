@@ -18,11 +18,16 @@
 //     dT = dDelta u^T + dW Eh^T, dEh = T^T dW, dA = mask(-(T^T dT) T^T),
 //     dGamma_L = rowsum(dSL * S0);
 //   dQh, dKtil, dEh, dP, dA and dGamma_L go to an fp32 scratch block per chunk.
-// k_chunk_grad_key  the key side on vector ALUs from LDS: the cumulative log
-//   decay G, the contractions of dA and dP with the block-split decay ratios
-//   (row side: sum_s dA[r,s] k_s R[r,s]; column side: sum_r dA[r,s] e_r R[r,s],
-//   and the same with dP and q), the gradients of q, k, b, and dalpha from
-//   the reverse cumulative sum of dG.
+// k_chunk_grad_key  the key side: the cumulative log decay G, the
+//   contractions of dA and dP with the block-split decay ratios on bf16
+//   matrix cores (row side: sum_s dA[r,s] k_s R[r,s]; column side:
+//   sum_r dA[r,s] e_r R[r,s], and the same with dP and q), then per row the
+//   gradients of q, k, b, and dalpha from the reverse cumulative sum of dG.
+// With the prologue options (burn-gdn2 0.1.9 README, "Architecture" and
+// "Configuration") both launches take the raw inputs: gates are activated
+// on load (sigmoid, b x 2 in negative-eigenvalue mode), q/k rows normalised
+// with lane-group reductions, and the gradients they write are those of
+// the logits and of the raw q/k.
 #include "gdn2_device.hpp"
 #include "gdn2_launch.hpp"
 #include "gdn2_layout.hpp"
