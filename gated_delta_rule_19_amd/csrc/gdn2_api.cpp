@@ -183,9 +183,11 @@ int do_state(const gdn2_problem* p, const float* S0, void* o, float* S_out, cons
 }
 
 // backward workspace: forward factors | chunk entry states | chunk exit
-// state gradients | gradient scratch, each 256-byte aligned.  The matrix-core
-// path (bf16 I/O, dk 32/64/128, dv a multiple of 32 up to 128) also keeps T in
-// each factor block and transposed bf16 copies of both checkpoints.
+// state gradients | gradient scratch, each 256-byte aligned.  The vector-ALU
+// path keeps both checkpoints in fp32 [dk][dv]; the matrix-core path (bf16
+// I/O, dk 32/64/128, dv a multiple of 32 up to 128) keeps T in each factor
+// block and both checkpoints in bf16, [dk][dv] and transposed [dv][dk] (its
+// products take bf16 operands, so an fp32 copy would only be rounded again).
 struct BwdLayout {
     bool mf;
     int64_t block, t_off;                 // factor block stride, offset of T in it
@@ -204,11 +206,12 @@ BwdLayout bwd_layout(const gdn2_problem* p)
         l.t_off = l.block;
         l.block = up(l.block + 64 * 64 * 2);
     }
+    const int64_t chk = l.mf ? states / 2 : states;        // one copy of one checkpoint set
     l.chk = up(nblk * l.block);
-    l.chkT = up(l.chk + states);
-    l.dsl = l.mf ? up(l.chkT + states / 2) : l.chkT;
-    l.dslT = up(l.dsl + states);
-    l.scratch = l.mf ? up(l.dslT + states / 2) : l.dslT;
+    l.chkT = up(l.chk + chk);
+    l.dsl = l.mf ? up(l.chkT + chk) : l.chkT;
+    l.dslT = up(l.dsl + chk);
+    l.scratch = l.mf ? up(l.dslT + chk) : l.dslT;
     l.total = l.scratch + (l.mf ? gdn2::gradmf_scratch_bytes((int)p->dk, nblk)
                                 : gdn2::chunk_grad_scratch_bytes((int)p->dk, (int)p->dv, nblk));
     return l;
@@ -274,8 +277,10 @@ int bwd_core(const gdn2_problem* p, const BwdLayout& l, const void* q, const voi
              void* dq, void* dk, void* dv, void* dalpha, void* db, void* dw, float* dS0, char* ws, hipStream_t s)
 {
     int st = GDN2_OK;
-    float* chk = reinterpret_cast<float*>(ws + l.chk);
-    float* dsl = reinterpret_cast<float*>(ws + l.dsl);
+    float* chk = l.mf ? nullptr : reinterpret_cast<float*>(ws + l.chk);     // fp32 checkpoints
+    float* dsl = l.mf ? nullptr : reinterpret_cast<float*>(ws + l.dsl);
+    void* chkIo = l.mf ? ws + l.chk : nullptr;                                // bf16, both layouts
+    void* dslIo = l.mf ? ws + l.dsl : nullptr;
     void* chkT = l.mf ? ws + l.chkT : nullptr;
     void* dslT = l.mf ? ws + l.dslT : nullptr;
     const int64_t nch = p->B * p->H;
@@ -288,19 +293,19 @@ int bwd_core(const gdn2_problem* p, const BwdLayout& l, const void* q, const voi
         if (st) return st;
         const int vs = gdn2::chunk_state_slice(nch, (int)p->dv, (int)p->dk, (int)io_size(p));
         gdn2::StateArgs fa{ws, l.block, S0, nullptr, nullptr, p->B, p->T, p->H, (int)p->dv,
-                           (int)nchunks(p), (int)(p->dv / vs), nullptr, 0, chk, chkT};
+                           (int)nchunks(p), (int)(p->dv / vs), nullptr, 0, chk, chkT, chkIo};
         st = launch_status(gdn2::launch_chunk_state(fa, (int)p->dk, vs, is_bf16(p), s));
         if (st) return st;
     }
     const int bvs = gdn2::state_bwd_slice((int)p->dv);
     gdn2::BwdStateArgs ba{ws, l.block, dO, dS_T, dsl, dS0, p->B, p->T, p->H, (int)p->dk, (int)p->dv,
-                          (int)nchunks(p), (int)(p->dv / bvs), bvs, dslT};
+                          (int)nchunks(p), (int)(p->dv / bvs), bvs, dslT, dslIo};
     st = launch_status(gdn2::launch_chunk_state_bwd(ba, is_bf16(p), s));
     if (st) return st;
     if (nchunks(p) == 0) return GDN2_OK;
     float* gsc = reinterpret_cast<float*>(ws + l.scratch);
     if (l.mf) {
-        gdn2::GradVArgs va{ws, l.block, l.t_off, k, v, alpha, b, w, dO, chk, chkT, dsl, dslT, dw, dv, gsc,
+        gdn2::GradVArgs va{ws, l.block, l.t_off, k, v, alpha, b, w, dO, chkIo, chkT, dslIo, dslT, dw, dv, gsc,
                            p->B, p->T, p->H, (int)p->dk, (int)p->dv, (int)nchunks(p), total, (int)p->flags};
         gdn2::GradKArgs ka{q, k, alpha, b, gsc, dq, dk, dalpha, db, p->B, p->T, p->H, (int)p->dk,
                            (int)nchunks(p), total, (int)p->flags};

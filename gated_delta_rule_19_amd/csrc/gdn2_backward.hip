@@ -258,10 +258,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_state_bwd(BwdStateArgs a)
         __syncthreads();                                   // the previous chunk is done with LDS
         stash();
         // the gradient this chunk's exit state receives
-        float* dsl = a.dSL + (chain * nt + n) * (int64_t)DK * dv + j0;
-        for (int i = tid; i < DK * VS / 4; i += kThreads) {
-            const int c = i / NCG, g = i - c * NCG;
-            *reinterpret_cast<f32x4*>(dsl + (int64_t)c * dv + 4 * g) = *reinterpret_cast<const f32x4*>(&dS[c * VS + 4 * g]);
+        if (a.dSL != nullptr) {
+            float* dsl = a.dSL + (chain * nt + n) * (int64_t)DK * dv + j0;
+            for (int i = tid; i < DK * VS / 4; i += kThreads) {
+                const int c = i / NCG, g = i - c * NCG;
+                *reinterpret_cast<f32x4*>(dsl + (int64_t)c * dv + 4 * g) = *reinterpret_cast<const f32x4*>(&dS[c * VS + 4 * g]);
+            }
+        }
+        if (a.dSLIo != nullptr) {
+            // the same in the I/O dtype
+            Tio* dsl = static_cast<Tio*>(a.dSLIo) + (chain * nt + n) * (int64_t)DK * dv + j0;
+            for (int i = tid; i < DK * VS / 4; i += kThreads) {
+                const int c = i / NCG, g = i - c * NCG;
+                st_vec4(dsl + (int64_t)c * dv + 4 * g, *reinterpret_cast<const f32x4*>(&dS[c * VS + 4 * g]));
+            }
         }
         if (a.dSLT != nullptr) {
             // and transposed, [dv][dk] in the I/O dtype

@@ -7,8 +7,8 @@
 // k_chunk_grad_val  the value-side products on bf16 matrix cores, fp32
 //   accumulation.  Operands come from the forward workspace (W, P, Ktil^T,
 //   U^T, and T written by the prep kernel for the backward), from the chunk
-//   checkpoints (S0 and the exit gradient dSL, each in fp32 [dk][dv] and
-//   transposed in bf16 [dv][dk]) and from dO, v, w, b, k, alpha.  Every
+//   checkpoints (S0 and the exit gradient dSL, each in bf16 [dk][dv] and
+//   transposed [dv][dk]) and from dO, v, w, b, k, alpha.  Every
 //   operand is laid out with its contraction index contiguous (transposed
 //   copies are made in LDS where needed; LDS rows are padded by 16 bytes), so
 //   a fragment is one 16-byte read.  In order:
@@ -17,7 +17,8 @@
 //     dW = -dDelta S0^T, du = T^T dDelta (-> dw = du v, dv = du w),
 //     dT = dDelta u^T + dW Eh^T, dEh = T^T dW, dA = mask(-(T^T dT) T^T),
 //     dGamma_L = rowsum(dSL * S0);
-//   dQh, dKtil, dEh, dP, dA and dGamma_L go to an fp32 scratch block per chunk.
+//   dQh, dKtil, dEh, dP, dA and dGamma_L go to a scratch block per chunk
+//   (fp32; dP and dA in bf16, the key side's operand dtype).
 // k_chunk_grad_key  the key side: the cumulative log decay G, the
 //   contractions of dA and dP with the block-split decay ratios on bf16
 //   matrix cores (row side: sum_s dA[r,s] k_s R[r,s]; column side:
@@ -85,9 +86,9 @@ template <typename T> __device__ inline void gs(T* p, int64_t i, float x) { p[i]
 
 }  // namespace
 
-// fp32 scratch per chunk between the two launches, in floats:
-// dQh, dKtil, dEh [64][dk], dP, dA [64][64], dGamma_L [dk]
-__host__ __device__ inline int64_t gradmf_scratch_floats(int dk) { return 3 * 64 * (int64_t)dk + 2 * 4096 + dk; }
+// scratch per chunk between the two launches, in 4-byte words: dQh, dKtil,
+// dEh fp32 [64][dk]; dP, dA bf16 [64][64]; dGamma_L fp32 [dk]
+__host__ __device__ inline int64_t gradmf_scratch_floats(int dk) { return 3 * 64 * (int64_t)dk + 4096 + dk; }
 
 // G[r][c] = sum of log alpha over tokens 0..r of the chunk (alpha = 1 past its
 // end), for 256 threads: logs in parallel (every load issued before the first
@@ -243,9 +244,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
     const bf* Kttg = reinterpret_cast<const bf*>(blk + LY.ktt);          // Ktil^T [dk][64]
     const bf* Wg = reinterpret_cast<const bf*>(blk + LY.wwy);            // W [64][dk]
     const bf* Utg = reinterpret_cast<const bf*>(blk + LY.uwyt);          // U^T [dv][64]
-    const float* S0 = a.S_chk + ci * (int64_t)DK * DV;                    // [dk][dv]
+    const bf* S0 = static_cast<const bf*>(a.S_chk) + ci * (int64_t)DK * DV;     // [dk][dv]
     const bf* S0t = static_cast<const bf*>(a.S_chkT) + ci * (int64_t)DK * DV;   // [dv][dk]
-    const float* dSL = a.dSL + ci * (int64_t)DK * DV;
+    const bf* dSL = static_cast<const bf*>(a.dSL) + ci * (int64_t)DK * DV;
     const bf* dSLt = static_cast<const bf*>(a.dSLT) + ci * (int64_t)DK * DV;
     const bf* dO = static_cast<const bf*>(a.dO);
     const bf* vg = static_cast<const bf*>(a.v);
@@ -259,9 +260,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
     float* s_dQh = sc;
     float* s_dKt = sc + 64 * DK;
     float* s_dEh = sc + 2 * 64 * DK;
-    float* s_dP = sc + 3 * 64 * DK;
-    float* s_dA = s_dP + 4096;
-    float* s_dGL = s_dA + 4096;
+    bf* s_dP = reinterpret_cast<bf*>(sc + 3 * 64 * DK);
+    bf* s_dA = s_dP + 4096;
+    float* s_dGL = sc + 3 * 64 * DK + 4096;
     const bool logits = (a.flags & kFlagGateLogits) != 0, l2 = (a.flags & kFlagQkL2norm) != 0;
     const float bscale = (a.flags & kFlagNegEigval) ? 2.f : 1.f;
 
@@ -348,24 +349,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
         for (int e = 0; e < 4; ++e) x[e] = r < Ln ? __expf(g4[e]) * b4[e] * k4[e] : 0.f;
         st_vec4(Ehl + r * ldk + c4, x);
     }
-    // dGamma_L = rowsum(dSL * S0) in fp32 (dk = 32: with larger dk it comes
-    // from the panels below), before the first global store (a load behind a
-    // store would wait for it); stored at the end.  TPR threads per row, each
-    // with DV / TPR columns, all loads in flight at once.
+    // dGamma_L = rowsum(dSL * S0), fp32 sums of the bf16 checkpoints (dk = 32:
+    // with larger dk it comes from the panels below), before the first global
+    // store (a load behind a store would wait for it); stored at the end.  TPR
+    // threads per row, each with DV / TPR columns, all loads in flight at once.
     constexpr int TPR = kThreads / DK, NCOL = DV / TPR;
     float dgl = 0.f;
     if constexpr (NTK % 4 != 0) {
         const int c = tid / TPR, sub = tid % TPR;
-        f32x4 pa[NCOL / 4], pb[NCOL / 4];
+        bf16x4 pa[NCOL / 4], pb[NCOL / 4];
 #pragma unroll
         for (int m = 0; m < NCOL / 4; ++m) {
-            pa[m] = *reinterpret_cast<const f32x4*>(dSL + (int64_t)c * DV + sub * NCOL + 4 * m);
-            pb[m] = *reinterpret_cast<const f32x4*>(S0 + (int64_t)c * DV + sub * NCOL + 4 * m);
+            pa[m] = *reinterpret_cast<const bf16x4*>(dSL + (int64_t)c * DV + sub * NCOL + 4 * m);
+            pb[m] = *reinterpret_cast<const bf16x4*>(S0 + (int64_t)c * DV + sub * NCOL + 4 * m);
         }
         float x = 0.f;
 #pragma unroll
-        for (int m = 0; m < NCOL / 4; ++m)
-            x += pa[m][0] * pb[m][0] + pa[m][1] * pb[m][1] + pa[m][2] * pb[m][2] + pa[m][3] * pb[m][3];
+        for (int m = 0; m < NCOL / 4; ++m) {
+            const f32x4 fa = IOB::unpack4(pa[m]), fb = IOB::unpack4(pb[m]);
+            x += fa[0] * fb[0] + fa[1] * fb[1] + fa[2] * fb[2] + fa[3] * fb[3];
+        }
 #pragma unroll
         for (int off = 1; off < TPR; off <<= 1) x += __shfl_xor(x, off, 64);
         dgl = x;
@@ -425,38 +428,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
                 });
     __syncthreads();
     // ---- dQh = dO S0^T and dW = -dDelta S0^T (one pass over S0), dKtil = Delta dSL^T
-    // Every B panel of this wave (fp32 rows of S0 and dSL) is requested at
-    // once, raw, before the kernel's first global store; with dk >= 64 one
-    // wave holds both the S0 and the dSL panel of a row block, and dGamma_L =
-    // rowsum(dSL * S0) comes from the same fp32 values.
+    // Every B panel of this wave (bf16 rows of S0 and dSL) is requested at
+    // once, before the kernel's first global store; with dk >= 64 one wave
+    // holds both the S0 and the dSL panel of a row block, and dGamma_L =
+    // rowsum(dSL * S0) comes from the same fragments.
     constexpr int NPW = NTK / 2;                                    // panels per wave
     constexpr bool FUSE_GL = NTK % 4 == 0;
-    f32x4 rb[NPW][NKV][2];
+    bfrag rb[NPW][NKV];
 #pragma unroll
     for (int m = 0; m < NPW; ++m) {
         const int p = wave + 4 * m;
-        const float* B = p < NTK ? S0 : dSL;
+        const bf* B = p < NTK ? S0 : dSL;
         const int tn = p < NTK ? p : p - NTK;
 #pragma unroll
-        for (int kb = 0; kb < NKV; ++kb) {
-            const float* q = B + (16 * tn + l16) * DV + kb * 32 + grp * 8;
-            rb[m][kb][0] = *reinterpret_cast<const f32x4*>(q);
-            rb[m][kb][1] = *reinterpret_cast<const f32x4*>(q + 4);
-        }
+        for (int kb = 0; kb < NKV; ++kb) rb[m][kb] = fr(B, 16 * tn + l16, DV, kb, grp);
     }
     float glp[FUSE_GL ? NPW / 2 : 1];
 #pragma unroll
     for (int m = 0; m < NPW; ++m) {
         const int p = wave + 4 * m;
         const int tn = p < NTK ? p : p - NTK, c = 16 * tn + l16;
-        bfrag fb[NKV];
-#pragma unroll
-        for (int kb = 0; kb < NKV; ++kb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                fb[kb][e] = (bf)rb[m][kb][0][e];
-                fb[kb][4 + e] = (bf)rb[m][kb][1][e];
-            }
+        const bfrag (&fb)[NKV] = rb[m];
 #pragma unroll
         for (int tr = 0; tr < 4; ++tr) {
             const int r = 16 * tr + 4 * grp;
@@ -488,9 +480,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
 #pragma unroll
                 for (int kb = 0; kb < NKV; ++kb)
 #pragma unroll
-                    for (int h = 0; h < 2; ++h)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) x += rb[m][kb][h][e] * rb[m - NPW / 2][kb][h][e];
+                    for (int e = 0; e < 8; ++e) x += (float)rb[m][kb][e] * (float)rb[m - NPW / 2][kb][e];
                 x += __shfl_xor(x, 16, 64);
                 x += __shfl_xor(x, 32, 64);
                 glp[m - NPW / 2] = x;
@@ -510,7 +500,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
                [&](int t, f32x4 acc) {
                    const int r = 16 * (t >> 2) + 4 * grp, s = 16 * (t & 3) + l16;
 #pragma unroll
-                   for (int i = 0; i < 4; ++i) s_dP[(r + i) * 64 + s] = s <= r + i ? acc[i] : 0.f;
+                   for (int i = 0; i < 4; ++i) s_dP[(r + i) * 64 + s] = (bf)(s <= r + i ? acc[i] : 0.f);
                });
     // ---- du = T^T dDelta -> dw = du v, dv = du w ---------------------------------
     // v and w at this wave's tile positions, and w, v for u below, are all
@@ -632,7 +622,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
              [&](int t, f32x4 acc) {
                  const int r = 16 * (t >> 2) + 4 * grp, s = 16 * (t & 3) + l16;
 #pragma unroll
-                 for (int i = 0; i < 4; ++i) s_dA[(r + i) * 64 + s] = s < r + i ? -acc[i] : 0.f;
+                 for (int i = 0; i < 4; ++i) s_dA[(r + i) * 64 + s] = (bf)(s < r + i ? -acc[i] : 0.f);
              });
     if constexpr (FUSE_GL) {
         if (grp == 0) {
@@ -732,22 +722,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
     const float* s_dQh = sc;
     const float* s_dKt = sc + 64 * DK;
     const float* s_dEh = sc + 2 * 64 * DK;
-    const float* s_dP = sc + 3 * 64 * DK;
-    const float* s_dA = s_dP + 4096;
-    const float* s_dGL = s_dA + 4096;
+    const bf* s_dP = reinterpret_cast<const bf*>(sc + 3 * 64 * DK);
+    const bf* s_dA = s_dP + 4096;
+    const float* s_dGL = sc + 3 * 64 * DK + 4096;
     const bool logits = (a.flags & kFlagGateLogits) != 0, l2 = (a.flags & kFlagQkL2norm) != 0;
     const float bscale = (a.flags & kFlagNegEigval) ? 2.f : 1.f;
 
     // ---- phase A: loads (raw), then dA, dP, G, KY, EA, QA into LDS ----------
     {
-        f32x4 xa[4], xp[4];
+        bfrag xa[2], xp[2];
         gvec ax[NV], bx[NV];
         bf16x4 kx[NV], qx[NV];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 2; ++u) {
             const int i = tid + u * kThreads;
-            xa[u] = *reinterpret_cast<const f32x4*>(s_dA + 4 * i);
-            xp[u] = *reinterpret_cast<const f32x4*>(s_dP + 4 * i);
+            xa[u] = *reinterpret_cast<const bfrag*>(s_dA + 8 * i);
+            xp[u] = *reinterpret_cast<const bfrag*>(s_dP + 8 * i);
         }
         cld_load<DK>(ax, agt, row0, H, Ln);
 #pragma unroll
@@ -759,10 +749,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
             bx[u] = *reinterpret_cast<const gvec*>(bgt + o);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = tid + u * kThreads, r = i >> 4, s4 = 4 * (i & 15);
-            st_vec4(dAl + r * LT + s4, xa[u]);
-            st_vec4(dPl + r * LT + s4, xp[u]);
+        for (int u = 0; u < 2; ++u) {
+            const int i = tid + u * kThreads, r = i >> 3, s8 = 8 * (i & 7);
+            *reinterpret_cast<bfrag*>(dAl + r * LT + s8) = xa[u];
+            *reinterpret_cast<bfrag*>(dPl + r * LT + s8) = xp[u];
         }
         cld_scan<DK, Tg>(G, tot, ax, Ln, logits);
 #pragma unroll

@@ -606,7 +606,7 @@ inline int state_lds_bytes(int dk, int vs, int es)
 
 // value columns per compute wave and threads per workgroup of the state pass
 
-// CHK: also write the state entering every chunk to a.S_chk
+// CHK: also write the state entering every chunk (the checkpoints of StateArgs)
 template <typename Tio, int DK, int VS, bool CHK>
 __global__ __launch_bounds__(state_threads(VS, (int)sizeof(Tio)), 1) void k_chunk_state(StateArgs a)
 {
@@ -812,16 +812,24 @@ __global__ __launch_bounds__(state_threads(VS, (int)sizeof(Tio)), 1) void k_chun
 
     for (int n = 0; n < nt; ++n) {
         if constexpr (CHK) {
-            // checkpoint: the state entering chunk n (kept for the backward pass)
-            float* dst = a.S_chk + (chain * (int64_t)nt + n) * DK * dv + j0 + jc + l16;
+            // checkpoint: the state entering chunk n (kept for the backward pass).
+            // Lanes 4m .. 4m+3 of a 16-lane row hold 4 columns of 4 state rows;
+            // a transpose inside each lane quad gives every lane 4 consecutive
+            // columns of one row, written as one vector.
+            if (a.S_chk != nullptr || a.S_chkIo != nullptr) {
+                const int64_t base = (chain * (int64_t)nt + n) * DK * dv + j0 + jc + (l16 & ~3);
 #pragma unroll
-            for (int i = 0; i < SPW; ++i) {
-                const int rt = tb * SPW + i;
-                if (rt < SRT) {
+                for (int i = 0; i < SPW; ++i) {
+                    const int rt = tb * SPW + i;
+                    if (rt < SRT) {
 #pragma unroll
-                    for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) dst[(16 * rt + 4 * grp + e) * dv + 16 * ct] = accS[i][ct][e];
+                        for (int ct = 0; ct < NCT; ++ct) {
+                            const f32x4 t = quad_transpose4(accS[i][ct]);
+                            const int64_t o = base + (int64_t)(16 * rt + 4 * grp + (l16 & 3)) * dv + 16 * ct;
+                            if (a.S_chk != nullptr) *reinterpret_cast<f32x4*>(a.S_chk + o) = t;
+                            if (a.S_chkIo != nullptr) st_vec4(static_cast<Tio*>(a.S_chkIo) + o, t);
+                        }
+                    }
                 }
             }
             if (a.S_chkT != nullptr) {
@@ -1031,7 +1039,7 @@ static hipError_t state_v(const StateArgs& a, hipStream_t s)
     } else {
         const int64_t nblk = a.B * a.H * (int64_t)a.nslices;
         constexpr int nthreads = state_threads(VS, (int)sizeof(Tio));
-        if (a.S_chk != nullptr)
+        if (a.S_chk != nullptr || a.S_chkT != nullptr || a.S_chkIo != nullptr)
             hipLaunchKernelGGL((k_chunk_state<Tio, DK, VS, true>), dim3((unsigned)nblk), dim3(nthreads), 0, s, a);
         else
             hipLaunchKernelGGL((k_chunk_state<Tio, DK, VS, false>), dim3((unsigned)nblk), dim3(nthreads), 0, s, a);

@@ -119,6 +119,32 @@ __device__ inline f32x4 ld_vec4(const T* p) {
 
 __device__ inline float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
+// Within every group of four consecutive lanes, transpose the 4 x 4 matrix
+// whose rows are the lanes and whose columns are the registers: lane q gets
+// register q of the four lanes, in lane order.  Two rounds of register swaps
+// between lane pairs (lane ^ 2, then lane ^ 1) through DPP quad permutations;
+// every lane of the wave must be active.
+__device__ inline f32x4 quad_transpose4(f32x4 v)
+{
+    const int q = threadIdx.x & 3;
+    const auto swap2 = [](float x) {     // quad_perm [2, 3, 0, 1]
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
+    };
+    const auto swap1 = [](float x) {     // quad_perm [1, 0, 3, 2]
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+    };
+    // lanes q, q ^ 2 exchange the registers whose bit 1 differs from q's
+    const bool hi = (q & 2) != 0;
+    float s0 = swap2(hi ? v[0] : v[2]), s1 = swap2(hi ? v[1] : v[3]);
+    if (hi) { v[0] = s0; v[1] = s1; } else { v[2] = s0; v[3] = s1; }
+    // lanes q, q ^ 1 exchange the registers whose bit 0 differs from q's
+    const bool odd = (q & 1) != 0;
+    s0 = swap1(odd ? v[0] : v[1]);
+    s1 = swap1(odd ? v[2] : v[3]);
+    if (odd) { v[0] = s0; v[2] = s1; } else { v[1] = s0; v[3] = s1; }
+    return v;
+}
+
 // ---------------------------------------------------------------------------
 // Gates: fp32 or bf16 in memory, fp32 in registers.  Prologue flags
 // (GDN2_FLAG_* of gdn2.h) are passed to the kernels as plain ints.

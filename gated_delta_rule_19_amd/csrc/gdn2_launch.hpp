@@ -26,15 +26,16 @@ struct PrepArgs {
     int64_t t_off;          // backward: byte offset of T in each block (0 = not written)
 };
 
-// S_chk (optional, equal-length batches only): the fp32 state entering every
-// chunk, [B*H][nt][dk][dv], and (optional with it) its transpose in the I/O
-// dtype, S_chkT [B*H][nt][dv][dk]; o may be null when only states are wanted
+// Checkpoints (optional, equal-length batches only): the state entering every
+// chunk, [B*H][nt][dk][dv] in fp32 (S_chk) or in the I/O dtype (S_chkIo), and
+// its transpose in the I/O dtype, S_chkT [B*H][nt][dv][dk]; each may be null.
+// o may be null when only states are wanted.
 struct StateArgs {
     const void* ws; int64_t ws_block;
     const float* S0; void* o; float* S_out;
     int64_t B, T, H; int dv; int nt; int nslices;
     const int* plan; int64_t ncmax;
-    float* S_chk; void* S_chkT;
+    float* S_chk; void* S_chkT; void* S_chkIo;
 };
 
 // cu (null for equal-length batches): the N+1 caller offsets of a packed
@@ -47,16 +48,17 @@ struct RecArgs {
     const int* cu;
 };
 
-// Backward (equal-length batches, H value heads = query/key heads, no
-// prologue flags).  Reverse state pass: per (batch, head, slice of vs value
-// columns), reads the forward workspace, dO and dS_T (nullable), writes the
-// gradient each chunk's exit state receives, dSL [B*H][nt][dk][dv], and dS0
-// (nullable).
+// Backward (equal-length batches, H value heads = query/key heads).  Reverse
+// state pass: per (batch, head, slice of vs value columns), reads the forward
+// workspace, dO and dS_T (nullable), writes the gradient each chunk's exit
+// state receives, [B*H][nt][dk][dv] in fp32 (dSL) and/or in the I/O dtype
+// (dSLIo), each nullable, and dS0 (nullable).
 struct BwdStateArgs {
     const void* ws; int64_t ws_block;
     const void* dO; const float* dS_T; float* dSL; float* dS0;
     int64_t B, T, H; int dk, dv, nt, nslices, vs;
-    void* dSLT;             // optional: dSL transposed, [B*H][nt][dv][dk], I/O dtype
+    void* dSLT;             // optional: the same transposed, [B*H][nt][dv][dk], I/O dtype
+    void* dSLIo;
 };
 
 // Per-chunk gradients: inputs, dO, the chunk entry states S_chk and exit
@@ -75,13 +77,14 @@ struct GradArgs {
 // gates are logits and q/k unnormalised, and the gradients are those of the
 // raw inputs): the value-side launch reads the
 // forward workspace (blocks of ws_block bytes with T at t_off), the
-// checkpoints S_chk/S_chkT and dSL/dSLT, dO, v, w, b, k, alpha; writes dw, dv
+// checkpoints S_chk/S_chkT and dSL/dSLT (bf16, [dk][dv] and [dv][dk] per
+// chunk), dO, v, w, b, k, alpha; writes dw, dv
 // and an fp32 scratch block per chunk that the key-side launch reads with q,
 // k, b, alpha to write dq, dk, db, dalpha.
 struct GradVArgs {
     const void* ws; int64_t ws_block, t_off;
     const void* k; const void* v; const void* alpha; const void* b; const void* w; const void* dO;
-    const float* S_chk; const void* S_chkT; const float* dSL; const void* dSLT;
+    const void* S_chk; const void* S_chkT; const void* dSL; const void* dSLT;
     void* dw; void* dv_out; float* gsc;
     int64_t B, T, H; int dk, dv, nt; int64_t total;
     int flags;              // prologue options applied in-kernel (gradients of the logits, raw q/k)
