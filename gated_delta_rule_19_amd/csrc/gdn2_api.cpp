@@ -202,9 +202,9 @@ BwdLayout bwd_layout(const gdn2_problem* p)
     BwdLayout l{};
     l.mf = gdn2::gradmf_supported((int)p->dk, (int)p->dv, is_bf16(p));
     l.block = ws_block_bytes(p);
-    if (l.mf) {
+    if (l.mf) {                           // the backward's layout of the blocks (BwdExt)
         l.t_off = l.block;
-        l.block = up(l.block + 64 * 64 * 2);
+        l.block = gdn2::bwd_ext(l.block, p->dk).block;
     }
     const int64_t chk = l.mf ? states / 2 : states;        // one copy of one checkpoint set
     l.chk = up(nblk * l.block);
@@ -297,10 +297,10 @@ int bwd_core(const gdn2_problem* p, const BwdLayout& l, const void* q, const voi
         st = launch_status(gdn2::launch_chunk_state(fa, (int)p->dk, vs, is_bf16(p), s));
         if (st) return st;
     }
-    const int bvs = gdn2::state_bwd_slice((int)p->dv);
+    const int bvs = l.mf ? 32 : gdn2::state_bwd_slice((int)p->dv);
     gdn2::BwdStateArgs ba{ws, l.block, dO, dS_T, dsl, dS0, p->B, p->T, p->H, (int)p->dk, (int)p->dv,
-                          (int)nchunks(p), (int)(p->dv / bvs), bvs, dslT, dslIo};
-    st = launch_status(gdn2::launch_chunk_state_bwd(ba, is_bf16(p), s));
+                          (int)nchunks(p), (int)(p->dv / bvs), bvs, dslT, dslIo, l.t_off};
+    st = launch_status(l.mf ? gdn2::launch_chunk_state_bwd_mf(ba, s) : gdn2::launch_chunk_state_bwd(ba, is_bf16(p), s));
     if (st) return st;
     if (nchunks(p) == 0) return GDN2_OK;
     float* gsc = reinterpret_cast<float*>(ws + l.scratch);

@@ -5,8 +5,8 @@
 // header), split in two launches of one workgroup per chunk:
 //
 // k_chunk_grad_val  the value-side products on bf16 matrix cores, fp32
-//   accumulation.  Operands come from the forward workspace (W, P, Ktil^T,
-//   U^T, and T written by the prep kernel for the backward), from the chunk
+//   accumulation.  Operands come from the workspace blocks the recomputed
+//   forward writes in the backward's layout (W, P^T, Ktil, U^T, T), from the chunk
 //   checkpoints (S0 and the exit gradient dSL, each in bf16 [dk][dv] and
 //   transposed [dv][dk]) and from dO, v, w, b, k, alpha.  Every
 //   operand is laid out with its contraction index contiguous (transposed
@@ -240,8 +240,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
     constexpr WsLayout LY = ws_layout(DK, DV, 2, 32);
     const char* blk = static_cast<const char*>(a.ws) + ci * a.ws_block;
     const bf* Tg_ = reinterpret_cast<const bf*>(blk + a.t_off);         // T [64][64]
-    const bf* Pg = reinterpret_cast<const bf*>(blk + LY.p);              // P [64][64]
-    const bf* Kttg = reinterpret_cast<const bf*>(blk + LY.ktt);          // Ktil^T [dk][64]
+    const bf* Ptg = reinterpret_cast<const bf*>(blk + LY.p);             // P^T [64][64]
+    const bf* Kng = reinterpret_cast<const bf*>(blk + bwd_ext(a.t_off, DK).kn);   // Ktil [64][dk]
     const bf* Wg = reinterpret_cast<const bf*>(blk + LY.wwy);            // W [64][dk]
     const bf* Utg = reinterpret_cast<const bf*>(blk + LY.uwyt);          // U^T [dv][64]
     const bf* S0 = static_cast<const bf*>(a.S_chk) + ci * (int64_t)DK * DV;     // [dk][dv]
@@ -278,12 +278,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
     for (int m = 0; m < NTP; ++m) {                                 // T, P
         const int g = tid + m * kThreads, r = g >> 3, c0 = (g & 7) * 8;
         tq[m] = *reinterpret_cast<const bfrag*>(Tg_ + r * 64 + c0);
-        pq[m] = *reinterpret_cast<const bfrag*>(Pg + r * 64 + c0);
+        pq[m] = *reinterpret_cast<const bfrag*>(Ptg + r * 64 + c0);
     }
 #pragma unroll
-    for (int m = 0; m < NKT; ++m) {                                 // Ktil^T [c][r]
-        const int g = tid + m * kThreads, c = g >> 3, r0 = (g & 7) * 8;
-        kq[m] = *reinterpret_cast<const bfrag*>(Kttg + c * 64 + r0);
+    for (int m = 0; m < NKT; ++m) {                                 // Ktil [r][c]
+        const int g = tid + m * kThreads, r = g / (DK / 8), c0 = (g - r * (DK / 8)) * 8;
+        kq[m] = *reinterpret_cast<const bfrag*>(Kng + r * DK + c0);
     }
 #pragma unroll
     for (int m = 0; m < NUT; ++m) {                                 // U^T [j][r]
@@ -307,17 +307,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
     for (int m = 0; m < NTP; ++m) {                                 // T, T^T; P^T
         const int g = tid + m * kThreads, r = g >> 3, c0 = (g & 7) * 8;
         *reinterpret_cast<bfrag*>(Tl + r * LT + c0) = tq[m];
+        *reinterpret_cast<bfrag*>(Ptl + r * LT + c0) = pq[m];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            Ttl[(c0 + e) * LT + r] = tq[m][e];
-            Ptl[(c0 + e) * LT + r] = pq[m][e];
-        }
+        for (int e = 0; e < 8; ++e) Ttl[(c0 + e) * LT + r] = tq[m][e];
     }
 #pragma unroll
-    for (int m = 0; m < NKT; ++m) {                                 // Ktil [r][c] from Ktil^T [c][r]
-        const int g = tid + m * kThreads, c = g >> 3, r0 = (g & 7) * 8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) Ktl[(r0 + e) * ldk + c] = kq[m][e];
+    for (int m = 0; m < NKT; ++m) {                                 // Ktil
+        const int g = tid + m * kThreads, r = g / (DK / 8), c0 = (g - r * (DK / 8)) * 8;
+        *reinterpret_cast<bfrag*>(Ktl + r * ldk + c0) = kq[m];
     }
 #pragma unroll
     for (int m = 0; m < NUT; ++m) {                                 // U [r][j] from U^T [j][r]
@@ -962,6 +959,299 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Reverse state pass of the matrix-core path: one workgroup per (batch, head,
+// 32-column slice), 4 compute waves and 8 loader waves, chunks in reverse.
+// The gradient dS [dk][32] of the chunk's exit state lives in the compute
+// waves' accumulators (wave w: row tiles w, w + 4, ...).  Per chunk:
+//   dDelta = P^T dO + Ktil dS                  (wave w: rows 16w .. 16w+15)
+//                                                            | barrier 1
+//   dS     = diag(Gamma_L) dS + Qh^T dO - W^T dDelta         | barrier 2
+// The factors come in the backward's layout of the workspace block (Qh^T,
+// P^T, Ktil, W^T: contraction index contiguous), so every A fragment is one
+// 16-byte LDS read; the B operands dO, dS (bf16) and dDelta are kept
+// transposed in LDS.  Loader waves keep the next chunks' factors and dO in
+// flight in their registers and copy chunk n-1 into the second LDS buffer
+// (half before barrier 1, half after) while chunk n is computed, dO
+// transposed on the way.  Before each chunk the compute waves write its exit
+// gradient in bf16, [dk][dv] and transposed [dv][dk].  The slices of one head
+// get block ids congruent mod 8 (one XCD, one L2 for the head's blocks).
+// ---------------------------------------------------------------------------
+template <int DK>
+struct RsLds {
+    static constexpr int VS = 32;                      // value columns per workgroup
+    static constexpr int RP = 64 + 8;                  // padded row of a [.][64] bf16 array
+    static constexpr int KR = DK + 8;                  // padded row of a [.][DK] bf16 array
+    // one operand buffer
+    static constexpr int QT = 0;                       // Qh^T [DK][RP]
+    static constexpr int PT = QT + DK * RP * 2;        // P^T [64][RP]
+    static constexpr int WT = PT + 64 * RP * 2;        // W^T [DK][RP]
+    static constexpr int KN = WT + DK * RP * 2;        // Ktil [64][KR]
+    static constexpr int GL = KN + 64 * KR * 2;        // Gamma_L fp32 [DK]
+    static constexpr int OT = GL + DK * 4;             // dO^T [VS][RP]
+    static constexpr int BUF = OT + VS * RP * 2;
+    static constexpr int DT = 2 * BUF;                 // dDelta^T [VS][RP]
+    static constexpr int ST = DT + VS * RP * 2;        // dS^T bf16 [VS][KR]
+    static constexpr int BYTES = ST + VS * KR * 2;
+    // 16-byte granules of one chunk: dO (64 rows of VS columns), then Qh^T,
+    // P^T, W^T, Ktil, Gamma_L
+    static constexpr int G_DO = 64 * VS / 8;
+    static constexpr int G_QT = DK * 8, G_PT = 64 * 8, G_WT = DK * 8, G_KN = 64 * DK / 8, G_GL = DK / 4;
+    static constexpr int NG = G_DO + G_QT + G_PT + G_WT + G_KN + G_GL;
+    static constexpr int NCW = 4, NLW = 8;             // compute and loader waves
+    static constexpr int NLD = 64 * NLW;
+    static constexpr int LPL = (NG + NLD - 1) / NLD;   // granules per loader lane per chunk
+    static constexpr int THREADS = 64 * (NCW + NLW);
+};
+
+template <int DK>
+__global__ __launch_bounds__(RsLds<DK>::THREADS, 1) void k_chunk_state_bwd_mf(BwdStateArgs a)
+{
+    using L = RsLds<DK>;
+    constexpr int RP = L::RP, KR = L::KR, VS = L::VS, LPL = L::LPL, NCW = L::NCW;
+    constexpr int NTC = DK / 16, TPW = (NTC + 3) / 4, NKK = DK / 32;
+    constexpr WsLayout LY = ws_layout(DK, 0, 2, 32);
+    static_assert(L::G_DO == 4 * 64 && L::BYTES <= 160 * 1024, "layout");
+    __shared__ __attribute__((aligned(16))) char sm[L::BYTES];
+    bf* DTl = reinterpret_cast<bf*>(sm + L::DT);
+    bf* STl = reinterpret_cast<bf*>(sm + L::ST);
+
+    const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int dv = a.dv, nt = a.nt;
+    const int64_t nch = a.B * a.H, x = blockIdx.x;
+    const int ns = a.nslices;
+    int64_t chain;
+    int slice;
+    if ((nch & 7) == 0) {
+        chain = (x / (8 * ns)) * 8 + (x & 7);
+        slice = (int)((x >> 3) % ns);
+    } else {
+        chain = x / ns;
+        slice = (int)(x - chain * ns);
+    }
+    const int j0 = slice * VS;
+    const int64_t bb = chain / a.H, hh = chain - bb * a.H;
+
+    if (wave >= NCW) {
+        // ---------------- loader waves ------------------------------------
+        // Step i of the pass works on chunk nt-1-i; its operands go to buffer
+        // i & 1.  Granule g = (wave - NCW)*64 + lane + NLD*m: slot 0 of loader
+        // waves 0..3 holds dO (row g/4, columns 8(g%4) .. +7 of the slice);
+        // every other slot a factor granule (source offset in the block,
+        // destination in the buffer); idle slots copy a factor granule some
+        // other lane copies too (the same bytes to the same place).
+        const int lw = wave - NCW;
+        const bool dol = lw < 4;
+        const bf* dO = static_cast<const bf*>(a.dO);
+        const int dr = (lw * 64 + lane) >> 2, dc = 8 * (lane & 3);
+        int src[LPL], dst[LPL];
+#pragma unroll
+        for (int m = 0; m < LPL; ++m) {
+            int g = lw * 64 + lane + L::NLD * m - L::G_DO;
+            if (g >= L::NG - L::G_DO) g %= (L::NG - L::G_DO);
+            if (g < 0) g = 0;                                // (dO slot: unused)
+            const BwdExt X = bwd_ext(a.t_off, DK);
+            int sr, ds;
+            if (g < L::G_QT) {
+                sr = (int)LY.qh + 16 * g;
+                ds = L::QT + (g >> 3) * RP * 2 + (g & 7) * 16;
+            } else if ((g -= L::G_QT) < L::G_PT) {
+                sr = (int)LY.p + 16 * g;
+                ds = L::PT + (g >> 3) * RP * 2 + (g & 7) * 16;
+            } else if ((g -= L::G_PT) < L::G_WT) {
+                sr = (int)X.wt + 16 * g;
+                ds = L::WT + (g >> 3) * RP * 2 + (g & 7) * 16;
+            } else if ((g -= L::G_WT) < L::G_KN) {
+                sr = (int)X.kn + 16 * g;
+                ds = L::KN + (g / (DK / 8)) * KR * 2 + (g % (DK / 8)) * 16;
+            } else {
+                g -= L::G_KN;
+                sr = (int)LY.gaml + 16 * g;
+                ds = L::GL + 16 * g;
+            }
+            src[m] = sr;
+            dst[m] = ds;
+        }
+        // register slots of chunks in flight: as many as fit, without spills,
+        // in the 168 registers of three waves per SIMD (dk = 128: two)
+        constexpr int DEPTH0 = (168 - 2 * LPL - 64) / (4 * LPL);
+        constexpr int DEPTH = DEPTH0 > 4 ? 4 : (DEPTH0 < 1 ? 1 : DEPTH0);
+        bfrag r[DEPTH][LPL];
+        // granules [m0, m1) of step i into / out of a register slot; steps past
+        // the end load chunk 0 again (every step issues the same loads)
+        auto fetch = [&](int i, bfrag* rs, int m0, int m1) {
+            const int n = nt - 1 - i < 0 ? 0 : nt - 1 - i;
+            const char* blk = static_cast<const char*>(a.ws) + (chain * nt + n) * a.ws_block;
+            const int64_t t0 = (int64_t)n * kChunk;
+            const int Ln = (int)(a.T - t0 < kChunk ? a.T - t0 : kChunk);
+            const int rc = dr < Ln ? dr : Ln - 1;
+            const char* pd = reinterpret_cast<const char*>(dO + ((bb * a.T + t0 + rc) * a.H + hh) * dv + j0 + dc);
+#pragma unroll
+            for (int m = 0; m < LPL; ++m)
+                if (m >= m0 && m < m1)
+                    rs[m] = *reinterpret_cast<const bfrag*>(m == 0 && dol ? pd : blk + src[m]);
+        };
+        auto store = [&](int i, const bfrag* rs, int m0, int m1) {
+            char* b0 = sm + (i & 1) * L::BUF;
+#pragma unroll
+            for (int m = 0; m < LPL; ++m) {
+                if (m >= m0 && m < m1) {
+                    if (m == 0 && dol) {                    // dO^T, zero past the end
+                        const int n = nt - 1 - i < 0 ? 0 : nt - 1 - i;
+                        const int64_t t0 = (int64_t)n * kChunk;
+                        const int Ln = (int)(a.T - t0 < kChunk ? a.T - t0 : kChunk);
+                        bf* ot = reinterpret_cast<bf*>(b0 + L::OT);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) ot[(dc + e) * RP + dr] = dr < Ln ? rs[0][e] : (bf)0.f;
+                    } else {
+                        *reinterpret_cast<bfrag*>(b0 + dst[m]) = rs[m];
+                    }
+                }
+            }
+        };
+        // Step i: step i+1 goes to LDS and step i+1+DEPTH is requested into the
+        // slot it leaves, half before barrier 1 and half after it.
+        constexpr int HALF = LPL / 2 > 0 ? LPL / 2 : 1;
+        auto iter = [&](int i, bfrag* rs) {
+            store(i + 1, rs, 0, HALF);
+            fetch(i + 1 + DEPTH, rs, 0, HALF);
+            __syncthreads();                                  // barrier 1
+            store(i + 1, rs, HALF, LPL);
+            fetch(i + 1 + DEPTH, rs, HALF, LPL);
+            __syncthreads();                                  // barrier 2
+        };
+        if (nt == 0) {
+            __syncthreads();                                  // prologue barrier
+            return;
+        }
+        fetch(0, r[0], 0, LPL);
+        if (DEPTH > 1) fetch(1, r[DEPTH > 1 ? 1 : 0], 0, LPL);
+        store(0, r[0], 0, LPL);
+        __syncthreads();                                      // prologue barrier
+#pragma unroll
+        for (int d = 2; d < DEPTH; ++d) fetch(d, r[d], 0, LPL);
+        fetch(DEPTH, r[0], 0, LPL);
+        int i = 0;
+        for (; i + DEPTH <= nt; i += DEPTH) {
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d) iter(i + d, r[(d + 1) % DEPTH]);
+        }
+#pragma unroll
+        for (int d = 0; d < DEPTH - 1; ++d)
+            if (i + d < nt) iter(i + d, r[(d + 1) % DEPTH]);
+        return;
+    }
+
+    // ---------------- compute waves -------------------------------------------
+    // dS: lane (l16, grp) of tile (t, ct) holds dS[16 tc + 4 grp + e][j0 + 16 ct + l16], tc = wave + 4t
+    f32x4 accS[TPW][2];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+        const int tc = wave + 4 * t;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (tc < NTC && a.dS_T != nullptr) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = a.dS_T[(chain * DK + 16 * tc + 4 * grp + e) * dv + j0 + 16 * ct + l16];
+            }
+            accS[t][ct] = v;
+            if (tc < NTC) st_vec4(STl + (16 * ct + l16) * KR + 16 * tc + 4 * grp, v);
+        }
+    }
+    __syncthreads();                                          // prologue barrier
+    for (int i = 0; i < nt; ++i) {
+        const int n = nt - 1 - i;
+        const char* B0 = sm + (i & 1) * L::BUF;
+        const bf* QTl = reinterpret_cast<const bf*>(B0 + L::QT);
+        const bf* PTl = reinterpret_cast<const bf*>(B0 + L::PT);
+        const bf* WTl = reinterpret_cast<const bf*>(B0 + L::WT);
+        const bf* KNl = reinterpret_cast<const bf*>(B0 + L::KN);
+        const float* GLl = reinterpret_cast<const float*>(B0 + L::GL);
+        const bf* OTl = reinterpret_cast<const bf*>(B0 + L::OT);
+        // the gradient this chunk's exit state receives: [dk][dv] rows after a
+        // transpose inside each lane quad (lane q: row 16 tc + 4 grp + q,
+        // columns (l16 & ~3) .. +3 of the tile), and [dv][dk] directly
+        {
+            const int64_t cb = (chain * nt + n) * (int64_t)DK * dv;
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                const int tc = wave + 4 * t;
+                if (tc < NTC) {
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct) {
+                        const int jc = j0 + 16 * ct;
+                        if (a.dSLIo != nullptr) {
+                            const f32x4 tr = quad_transpose4(accS[t][ct]);
+                            st_vec4(static_cast<bf*>(a.dSLIo) + cb + (int64_t)(16 * tc + 4 * grp + (l16 & 3)) * dv + jc + (l16 & ~3), tr);
+                        }
+                        if (a.dSLT != nullptr)
+                            st_vec4(static_cast<bf*>(a.dSLT) + cb + (int64_t)(jc + l16) * DK + 16 * tc + 4 * grp, accS[t][ct]);
+                    }
+                }
+            }
+        }
+        // dDelta rows 16 wave .. +15 -> dDelta^T
+        {
+            bfrag pa[2], ka[NKK];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) pa[kb] = fr(PTl, 16 * wave + l16, RP, kb, grp);
+#pragma unroll
+            for (int kb = 0; kb < NKK; ++kb) ka[kb] = fr(KNl, 16 * wave + l16, KR, kb, grp);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) acc = IOB::mma(acc, pa[kb], fr(OTl, 16 * ct + l16, RP, kb, grp));
+#pragma unroll
+                for (int kb = 0; kb < NKK; ++kb) acc = IOB::mma(acc, ka[kb], fr(STl, 16 * ct + l16, KR, kb, grp));
+                st_vec4(DTl + (16 * ct + l16) * RP + 16 * wave + 4 * grp, acc);
+            }
+        }
+        __syncthreads();                                      // barrier 1
+        // dS = diag(Gamma_L) dS + Qh^T dO - W^T dDelta -> dS^T for the next chunk
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int tc = wave + 4 * t;
+            if (tc < NTC) {
+                bfrag qa[2], wa[2];
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    qa[kb] = fr(QTl, 16 * tc + l16, RP, kb, grp);
+                    wa[kb] = fr(WTl, 16 * tc + l16, RP, kb, grp);
+                }
+                const f32x4 gl = *reinterpret_cast<const f32x4*>(GLl + 16 * tc + 4 * grp);
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1;
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) {
+                        a1 = IOB::mma(a1, qa[kb], fr(OTl, 16 * ct + l16, RP, kb, grp));
+                        a2 = IOB::mma(a2, wa[kb], fr(DTl, 16 * ct + l16, RP, kb, grp));
+                    }
+                    accS[t][ct] = gl * accS[t][ct] + a1 - a2;
+                    st_vec4(STl + (16 * ct + l16) * KR + 16 * tc + 4 * grp, accS[t][ct]);
+                }
+            }
+        }
+        __syncthreads();                                      // barrier 2
+    }
+    if (a.dS0 != nullptr) {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int tc = wave + 4 * t;
+            if (tc < NTC) {
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    const f32x4 tr = quad_transpose4(accS[t][ct]);
+                    *reinterpret_cast<f32x4*>(a.dS0 + (chain * DK + 16 * tc + 4 * grp + (l16 & 3)) * dv + j0 + 16 * ct + (l16 & ~3)) = tr;
+                }
+            }
+        }
+    }
+}
+
 int64_t gradmf_scratch_bytes(int dk, int64_t total) { return total * gradmf_scratch_floats(dk) * 4; }
 
 bool gradmf_supported(int dk, int dv, bool bf16)
@@ -994,6 +1284,21 @@ static hipError_t grad_mf_dk(const GradVArgs& v, const GradKArgs& k, bool gbf16,
         hipLaunchKernelGGL((k_chunk_grad_key<DK, __bf16>), grid, dim3(kThreads), 0, s, k);
     else
         hipLaunchKernelGGL((k_chunk_grad_key<DK, float>), grid, dim3(kThreads), 0, s, k);
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_state_bwd_mf(const BwdStateArgs& a, hipStream_t s)
+{
+    if (!gradmf_supported(a.dk, a.dv, true) || a.vs != 32 || a.nslices * 32 != a.dv || a.dSL != nullptr ||
+        a.t_off == 0)
+        return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(a.B * a.H * a.nslices));
+    switch (a.dk) {
+        case 32: hipLaunchKernelGGL(k_chunk_state_bwd_mf<32>, grid, dim3(RsLds<32>::THREADS), 0, s, a); break;
+        case 64: hipLaunchKernelGGL(k_chunk_state_bwd_mf<64>, grid, dim3(RsLds<64>::THREADS), 0, s, a); break;
+        case 128: hipLaunchKernelGGL(k_chunk_state_bwd_mf<128>, grid, dim3(RsLds<128>::THREADS), 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -101,8 +101,8 @@ __device__ inline int unpack2(unsigned p, int i) { return (int)((p >> (2 * i)) &
 
 // NUI = (token, 4-column) value items per thread: 64 * dv / 4 <= 256 * NUI
 // Tg = gate dtype (alpha, b, w): float, or __bf16 with bf16 I/O
-// TOUT: also write T = (I + A)^{-1} (row-major [64][64], I/O dtype) at a.t_off
-// of the chunk's workspace block (kept for the backward pass)
+// TOUT: the backward's layout of the block (bf16, KPAD = DK): Qh^T and P^T in
+// place of Qh and P, and T, Ktil and W^T appended from a.t_off on (BwdExt)
 template <typename Tio, int DK, int NUI, typename Tg, bool TOUT = false>
 __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2)) void k_chunk_prep(PrepArgs a)
 {
@@ -111,6 +111,7 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
     constexpr int EPL = SM::EPL, KB = SM::KB, KPAD = SM::KPAD, TS = SM::TS, ES = SM::ES;
     constexpr int GX = SM::GX, GE = SM::GE, EPG = 16 / ES;   // EPG: elements per granule
     constexpr WsLayout LY = ws_layout(DK, 0, sizeof(Tio), KB);
+    static_assert(!TOUT || (KPAD == DK && sizeof(Tio) == 2), "backward layout: bf16, no K padding");
 
     __shared__ __attribute__((aligned(16))) char smem[SM::BYTES];
     Tio* Xe = reinterpret_cast<Tio*>(smem);
@@ -166,6 +167,9 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
     Tio* p_out = reinterpret_cast<Tio*>(blk + LY.p);
     float* gaml_out = reinterpret_cast<float*>(blk + LY.gaml);
     Tio* uwyt_out = reinterpret_cast<Tio*>(blk + LY.uwyt);
+    const BwdExt BX = bwd_ext(a.t_off, DK);      // (TOUT only)
+    Tio* kn_out = reinterpret_cast<Tio*>(blk + BX.kn);
+    Tio* wt_out = reinterpret_cast<Tio*>(blk + BX.wt);
 
     typedef typename IO::frag frag;
 
@@ -298,7 +302,7 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
             if (K < p) pre *= z[K];
             if (K > p) post *= z[K];
         }
-        Tio kt[4][8];
+        Tio kt[4][8], qt[4][8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int r = 8 * rg + i;
@@ -308,22 +312,29 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
             st_vec4(Xe + xo(r, c0), xe);
             st_vec4(Xq + xo(r, c0), xq);
             st_vec4(Yd + xo(r, c0), kv * ig);
-            st_vec4(qh_out + r * KPAD + c0, xq * pre);
+            const f32x4 qhv = xq * pre;
+            if constexpr (!TOUT) st_vec4(qh_out + r * KPAD + c0, qhv);
             const f32x4 ehv = xe * pre, ktv = kv * (zblk * ig) * post;
+            if constexpr (TOUT) st_vec4(kn_out + r * DK + c0, ktv);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 ehf[e][i / EPL][i % EPL] = IO::from_f(ehv[e]);
                 kt[e][i] = IO::from_f(ktv[e]);
+                qt[e][i] = IO::from_f(qhv[e]);
             }
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
 #pragma unroll
             for (int i = 0; i < 8; i += EPL) {
-                frag f1;
+                frag f1, f2;
 #pragma unroll
-                for (int e2 = 0; e2 < EPL; ++e2) f1[e2] = kt[e][i + e2];
+                for (int e2 = 0; e2 < EPL; ++e2) {
+                    f1[e2] = kt[e][i + e2];
+                    f2[e2] = qt[e][i + e2];
+                }
                 *reinterpret_cast<frag*>(ktt_out + (c0 + e) * 64 + 8 * rg + i) = f1;
+                if constexpr (TOUT) *reinterpret_cast<frag*>(qh_out + (c0 + e) * 64 + 8 * rg + i) = f2;   // Qh^T
             }
         }
     }
@@ -370,7 +381,8 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
                 const typename IO::frag xe = ld_frag(Xe + xo(16 * I + l16, ko));
                 const typename IO::frag xq = ld_frag(Xq + xo(16 * I + l16, ko));
                 accA[pi] = IO::mma(accA[pi], y, xe);
-                accP[pi] = IO::mma(accP[pi], y, xq);
+                if constexpr (TOUT) accP[pi] = IO::mma(accP[pi], xq, y);   // D[r][s]
+                else accP[pi] = IO::mma(accP[pi], y, xq);
             }
         }
     }
@@ -387,16 +399,18 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
                 for (int i = 0; i < 4; ++i) {
                     const int s = 4 * grp + i;
                     if (s >= l16) av[i] = 0.f;
-                    if (s > l16) pv[i] = 0.f;
+                    if (TOUT ? l16 > s : s > l16) pv[i] = 0.f;    // TOUT: pv[i] = P[16I+4grp+i][16J+l16]
                 }
             }
             *reinterpret_cast<f32x4*>(A32 + fo(r, 16 * J + 4 * grp)) = av;
-            st_vec4(p_out + r * 64 + 16 * J + 4 * grp, pv);
+            if constexpr (TOUT) st_vec4(p_out + (16 * J + l16) * 64 + 16 * I + 4 * grp, pv);   // P^T
+            else st_vec4(p_out + r * 64 + 16 * J + 4 * grp, pv);
         }
     }
-    for (int u = wave; u < 6; u += 4) {   // P is zero above the block diagonal
-        const int r = 16 * unpack2(kUpperI, u) + l16;
-        st_vec4(p_out + r * 64 + 16 * unpack2(kUpperJ, u) + 4 * grp, f32x4{0.f, 0.f, 0.f, 0.f});
+    for (int u = wave; u < 6; u += 4) {   // P is zero above the block diagonal (P^T below it)
+        const int I = unpack2(kUpperI, u), J = unpack2(kUpperJ, u);
+        if constexpr (TOUT) st_vec4(p_out + (16 * J + l16) * 64 + 16 * I + 4 * grp, f32x4{0.f, 0.f, 0.f, 0.f});
+        else st_vec4(p_out + (16 * I + l16) * 64 + 16 * J + 4 * grp, f32x4{0.f, 0.f, 0.f, 0.f});
     }
     __syncthreads();
 
@@ -487,6 +501,12 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
         }
         // acc[i] = W[r = 16*wave + l16][c = 16*ct + 4*grp + i]
         st_vec4(wwy_out + (16 * wave + l16) * KPAD + 16 * ct + 4 * grp, acc);
+        if constexpr (TOUT) {
+            // W^T: after a transpose inside each lane quad, lane q holds
+            // W[16*wave + (l16 & ~3) + e][16*ct + 4*grp + q], e = 0..3
+            const f32x4 t = quad_transpose4(acc);
+            st_vec4(wt_out + (16 * ct + 4 * grp + (l16 & 3)) * 64 + 16 * wave + (l16 & ~3), t);
+        }
     }
 
     // ---- 5. U = T (w * v), stored transposed, in column blocks of 64 --------
@@ -569,14 +589,16 @@ __host__ __device__ constexpr int state_cw(int vs) { return vs < GDN2_STATE_CW ?
 __host__ __device__ constexpr int state_nlw(int vs, int es) { return (vs / state_cw(vs) > 1 || es == 4) ? 4 : 8; }
 __host__ __device__ constexpr int state_threads(int vs, int es) { return 64 * (4 * (vs / state_cw(vs)) + state_nlw(vs, es)); }
 
-template <typename Tio, int DK, int VS>
+// NOQ: the checkpointing pass, which writes no o and needs neither Qh nor P
+template <typename Tio, int DK, int VS, bool NOQ = false>
 struct StateLds {
     static constexpr int ES = (int)sizeof(Tio), KB = Io<Tio>::KB, EPL = Io<Tio>::EPL;
     static constexpr int KPAD = round_up(DK, KB);
     static constexpr int GW = KPAD * ES / 16;       // granules per row of W / Qh
     static constexpr int GT = 64 * ES / 16;         // granules per row of P / Ktil^T / U^T
-    // granule offsets of the sections of one operand buffer
-    static constexpr int O_W = 0, O_Q = O_W + 64 * GW, O_P = O_Q + 64 * GW, O_K = O_P + 64 * GT;
+    // granule offsets of the sections of one operand buffer (Qh and P empty with NOQ)
+    static constexpr int NQ = NOQ ? 0 : 1;
+    static constexpr int O_W = 0, O_Q = O_W + 64 * GW, O_P = O_Q + NQ * 64 * GW, O_K = O_P + NQ * 64 * GT;
     static constexpr int O_U = O_K + DK * GT, O_G = O_U + VS * GT, GBUF = O_G + DK / 4;
     static constexpr int SRS = KPAD + EPL, DTS = 64 + EPL;
     static constexpr int PRIV = VS * SRS * ES + VS * DTS * ES;
@@ -606,12 +628,13 @@ inline int state_lds_bytes(int dk, int vs, int es)
 
 // value columns per compute wave and threads per workgroup of the state pass
 
-// CHK: also write the state entering every chunk (the checkpoints of StateArgs)
+// CHK: write the state entering every chunk (the checkpoints of StateArgs)
+// instead of o: Qh and P are neither copied nor used
 template <typename Tio, int DK, int VS, bool CHK>
 __global__ __launch_bounds__(state_threads(VS, (int)sizeof(Tio)), 1) void k_chunk_state(StateArgs a)
 {
     using IO = Io<Tio>;
-    using L = StateLds<Tio, DK, VS>;
+    using L = StateLds<Tio, DK, VS, CHK>;
     typedef typename IO::frag frag;
     typedef typename IO::vec4 vec4;
     constexpr int EPL = IO::EPL, KB = IO::KB, ES = L::ES;
@@ -859,7 +882,7 @@ __global__ __launch_bounds__(state_threads(VS, (int)sizeof(Tio)), 1) void k_chun
 #pragma unroll
         for (int kb = 0; kb < NKX; ++kb) {
             fw[kb] = lfrag(Wl, 16 * tb + l16, GW, kb);
-            fq[kb] = lfrag(Ql, 16 * tb + l16, GW, kb);
+            if constexpr (!CHK) fq[kb] = lfrag(Ql, 16 * tb + l16, GW, kb);
         }
         f32x4 accW[NCT], accO[NCT];
         frag fsb[2][NKX];
@@ -878,7 +901,7 @@ __global__ __launch_bounds__(state_threads(VS, (int)sizeof(Tio)), 1) void k_chun
         f32x4 gl[SPW];
 #pragma unroll
         for (int kb = 0; kb < NKT; ++kb) {
-            fp[kb] = lfrag(Pl, 16 * tb + l16, GT, kb);
+            if constexpr (!CHK) fp[kb] = lfrag(Pl, 16 * tb + l16, GT, kb);
 #pragma unroll
             for (int i = 0; i < SPW; ++i) {
                 const int rt = tb * SPW + i < SRT ? tb * SPW + i : SRT - 1;
@@ -902,7 +925,7 @@ __global__ __launch_bounds__(state_threads(VS, (int)sizeof(Tio)), 1) void k_chun
 #pragma unroll
             for (int kb = 0; kb < NKX; ++kb) {
                 w4 = IO::mma(w4, fw[kb], fsb[ct & 1][kb]);     // D[token][col]
-                o4 = IO::mma(o4, fsb[ct & 1][kb], fq[kb]);     // D[col][token]
+                if constexpr (!CHK) o4 = IO::mma(o4, fsb[ct & 1][kb], fq[kb]);     // D[col][token]
             }
             accW[ct] = w4;
             accO[ct] = o4;
@@ -933,13 +956,13 @@ __global__ __launch_bounds__(state_threads(VS, (int)sizeof(Tio)), 1) void k_chun
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kb = 0; kb < NKT; ++kb) {
-                if (kb * KB <= 16 * tb + 15) accO[ct] = IO::mma(accO[ct], fdb[ct & 1][kb], fp[kb]);
+                if (!CHK && kb * KB <= 16 * tb + 15) accO[ct] = IO::mma(accO[ct], fdb[ct & 1][kb], fp[kb]);
 #pragma unroll
                 for (int i = 0; i < SPW; ++i) accS[i][ct] = IO::mma(accS[i][ct], fk[i][kb], fdb[ct & 1][kb]);
             }
         }
         // o: token 16*wave + l16, columns 16*ct + 4*grp .. +3
-        {
+        if constexpr (!CHK) {
             const int64_t t = (int64_t)n * kChunk + 16 * tb + l16;
             if (t < tlen && o != nullptr) {
                 Tio* orow = o + ((tok0 + t) * a.H + hh) * dv + j0 + jc + 4 * grp;
@@ -995,8 +1018,8 @@ template <typename Tio, int DK, typename Tg>
 static hipError_t prep_dk(const PrepArgs& a, hipStream_t s)
 {
     const int64_t nblk = a.plan == nullptr ? a.B * a.H * (int64_t)a.nt : a.H * a.ncmax;
-    if (a.t_off != 0) {                          // backward: T kept (bf16 I/O, dv <= 128)
-        if constexpr (sizeof(Tio) == 2) {
+    if (a.t_off != 0) {                          // backward layout (bf16 I/O, dk >= 32, dv <= 128)
+        if constexpr (sizeof(Tio) == 2 && DK % 32 == 0) {
             if (a.dv > 128) return hipErrorInvalidValue;
             hipLaunchKernelGGL((k_chunk_prep<Tio, DK, 8, Tg, true>), dim3((unsigned)nblk), dim3(kThreads), 0, s, a);
             return hipGetLastError();

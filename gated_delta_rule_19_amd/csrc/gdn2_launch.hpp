@@ -59,6 +59,7 @@ struct BwdStateArgs {
     int64_t B, T, H; int dk, dv, nt, nslices, vs;
     void* dSLT;             // optional: the same transposed, [B*H][nt][dv][dk], I/O dtype
     void* dSLIo;
+    int64_t t_off;          // matrix-core pass: the blocks' backward extension (BwdExt) starts here
 };
 
 // Per-chunk gradients: inputs, dO, the chunk entry states S_chk and exit
@@ -135,6 +136,9 @@ hipError_t launch_recurrent(const RecArgs& a, int dk, int vs, bool bf16, bool gb
 hipError_t launch_gated_rmsnorm(const NormArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_varlen_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_chunk_state_bwd(const BwdStateArgs& a, bool bf16, hipStream_t s);
+// the same on the matrix-core path (bf16, dk in {32, 64, 128}, dv in {32, 64,
+// 128}, slices of 32): blocks in the backward's layout, dSLIo and dSLT only
+hipError_t launch_chunk_state_bwd_mf(const BwdStateArgs& a, hipStream_t s);
 int state_bwd_slice(int dv);
 hipError_t launch_bwd_qk_map(const QkMapArgs& a, bool post, bool bf16, hipStream_t s);
 hipError_t launch_bwd_gate_map(const GateMapArgs& a, bool post, bool gbf16, hipStream_t s);

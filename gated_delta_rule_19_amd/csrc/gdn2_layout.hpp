@@ -15,6 +15,14 @@
 //
 // with T = (I + A)^{-1}, A[r][s] = sum_c b_r k_r k_s Gamma_r/Gamma_s for s < r.
 // Every section starts on a 256-byte boundary.
+//
+// The forward recomputed for the matrix-core backward (bf16, KPAD = dk)
+// writes blocks whose products contract over the token index instead: its
+// qh section holds Qh^T [dk][64] and its p section P^T [64][64] (qt[c][r] =
+// qh[r][c], pt[s][r] = p[r][s]), and the block continues after uwyt with
+//   t    [64][64]  T
+//   kn   [64][dk]  Ktil (row-major)
+//   wt   [dk][64]  W^T
 #pragma once
 
 #include <stdint.h>
@@ -38,6 +46,16 @@ __host__ __device__ constexpr WsLayout ws_layout(int64_t dk, int64_t dv, int64_t
     const int64_t uwyt = align256(gaml + dk * 4);
     const int64_t block = align256(uwyt + dv * 64 * esize);
     return WsLayout{qh, wwy, ktt, p, gaml, uwyt, block};
+}
+
+// the backward's extension of a block whose forward layout ends at fwd_block
+struct BwdExt {
+    int64_t t, kn, wt, block;
+};
+__host__ __device__ constexpr BwdExt bwd_ext(int64_t fwd_block, int64_t dk)
+{
+    return BwdExt{fwd_block, fwd_block + 64 * 64 * 2, fwd_block + 64 * 64 * 2 + 64 * dk * 2,
+                  fwd_block + 64 * 64 * 2 + 2 * (64 * dk * 2)};
 }
 
 }  // namespace gdn2
