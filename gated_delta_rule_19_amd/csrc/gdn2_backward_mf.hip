@@ -51,20 +51,6 @@ __device__ inline bfrag fr(const bf* base, int row, int64_t ld, int kb, int grp)
     return *reinterpret_cast<const bfrag*>(base + row * ld + kb * 32 + grp * 8);
 }
 
-// the same from an fp32 array, rounded to bf16
-__device__ inline bfrag fr32(const float* base, int row, int64_t ld, int kb, int grp)
-{
-    const float* p = base + row * ld + kb * 32 + grp * 8;
-    const f32x4 x = *reinterpret_cast<const f32x4*>(p), y = *reinterpret_cast<const f32x4*>(p + 4);
-    bfrag r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        r[i] = (bf)x[i];
-        r[4 + i] = (bf)y[i];
-    }
-    return r;
-}
-
 template <typename T> __device__ inline float gf(const T* p, int64_t i) { return Io<T>::to_f(p[i]); }
 
 // sum over the N consecutive lanes that hold one row (N a power of two <= 32)
@@ -973,9 +959,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
 // transposed in LDS.  Loader waves keep the next chunks' factors and dO in
 // flight in their registers and copy chunk n-1 into the second LDS buffer
 // (half before barrier 1, half after) while chunk n is computed, dO
-// transposed on the way.  Before each chunk the compute waves write its exit
-// gradient in bf16, [dk][dv] and transposed [dv][dk].  The slices of one head
-// get block ids congruent mod 8 (one XCD, one L2 for the head's blocks).
+// transposed on the way.  The exit gradient of each chunk is written in bf16,
+// [dk][dv] and transposed [dv][dk]: the compute waves keep both layouts in
+// LDS (dS^T is their operand anyway) and the loader waves copy them out
+// before barrier 1, so that no global store sits in the compute waves' path.
+// The slices of one head get block ids congruent mod 8 (one XCD, one L2 for
+// the head's blocks).
 // ---------------------------------------------------------------------------
 template <int DK>
 struct RsLds {
@@ -992,7 +981,10 @@ struct RsLds {
     static constexpr int BUF = OT + VS * RP * 2;
     static constexpr int DT = 2 * BUF;                 // dDelta^T [VS][RP]
     static constexpr int ST = DT + VS * RP * 2;        // dS^T bf16 [VS][KR]
-    static constexpr int BYTES = ST + VS * KR * 2;
+    static constexpr int SP = VS + 8;                  // padded row of dS
+    static constexpr int SN = ST + VS * KR * 2;        // dS bf16 [DK][SP]
+    static constexpr int BYTES = SN + DK * SP * 2;
+    static constexpr int G_CK = VS * DK / 8;           // granules of one layout of the exit gradient
     // 16-byte granules of one chunk: dO (64 rows of VS columns), then Qh^T,
     // P^T, W^T, Ktil, Gamma_L
     static constexpr int G_DO = 64 * VS / 8;
@@ -1015,6 +1007,7 @@ __global__ __launch_bounds__(RsLds<DK>::THREADS, 1) void k_chunk_state_bwd_mf(Bw
     __shared__ __attribute__((aligned(16))) char sm[L::BYTES];
     bf* DTl = reinterpret_cast<bf*>(sm + L::DT);
     bf* STl = reinterpret_cast<bf*>(sm + L::ST);
+    bf* SNl = reinterpret_cast<bf*>(sm + L::SN);
 
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1075,7 +1068,7 @@ __global__ __launch_bounds__(RsLds<DK>::THREADS, 1) void k_chunk_state_bwd_mf(Bw
         }
         // register slots of chunks in flight: as many as fit, without spills,
         // in the 168 registers of three waves per SIMD (dk = 128: two)
-        constexpr int DEPTH0 = (168 - 2 * LPL - 64) / (4 * LPL);
+        constexpr int DEPTH0 = (168 - 2 * LPL - 80) / (4 * LPL);
         constexpr int DEPTH = DEPTH0 > 4 ? 4 : (DEPTH0 < 1 ? 1 : DEPTH0);
         bfrag r[DEPTH][LPL];
         // granules [m0, m1) of step i into / out of a register slot; steps past
@@ -1110,10 +1103,31 @@ __global__ __launch_bounds__(RsLds<DK>::THREADS, 1) void k_chunk_state_bwd_mf(Bw
                 }
             }
         };
-        // Step i: step i+1 goes to LDS and step i+1+DEPTH is requested into the
-        // slot it leaves, half before barrier 1 and half after it.
+        // the exit gradient of step i's chunk from LDS to both global layouts
+        // (dS^T rows [dv][dk], dS rows [dk][dv]): granule q < G_CK of dS^T,
+        // then of dS
+        auto ckpt = [&](int i) {
+            const int64_t cb = (chain * nt + (nt - 1 - i)) * (int64_t)DK * dv;
+#pragma unroll
+            for (int q0 = 0; q0 < 2 * L::G_CK; q0 += L::NLD) {
+                const int q = q0 + lw * 64 + lane;
+                if (q < L::G_CK) {
+                    const int j = q / (DK / 8), c8 = 8 * (q % (DK / 8));
+                    const bfrag v = *reinterpret_cast<const bfrag*>(STl + j * KR + c8);
+                    if (a.dSLT != nullptr) *reinterpret_cast<bfrag*>(static_cast<bf*>(a.dSLT) + cb + (int64_t)(j0 + j) * DK + c8) = v;
+                } else if (q < 2 * L::G_CK) {
+                    const int c = (q - L::G_CK) / (VS / 8), j8 = 8 * ((q - L::G_CK) % (VS / 8));
+                    const bfrag v = *reinterpret_cast<const bfrag*>(SNl + c * L::SP + j8);
+                    if (a.dSLIo != nullptr) *reinterpret_cast<bfrag*>(static_cast<bf*>(a.dSLIo) + cb + (int64_t)c * dv + j0 + j8) = v;
+                }
+            }
+        };
+        // Step i: the exit gradient of step i's chunk goes out, step i+1 goes
+        // to LDS and step i+1+DEPTH is requested into the slot it leaves, half
+        // before barrier 1 and half after it.
         constexpr int HALF = LPL / 2 > 0 ? LPL / 2 : 1;
         auto iter = [&](int i, bfrag* rs) {
+            ckpt(i);
             store(i + 1, rs, 0, HALF);
             fetch(i + 1 + DEPTH, rs, 0, HALF);
             __syncthreads();                                  // barrier 1
@@ -1157,12 +1171,14 @@ __global__ __launch_bounds__(RsLds<DK>::THREADS, 1) void k_chunk_state_bwd_mf(Bw
                 for (int e = 0; e < 4; ++e) v[e] = a.dS_T[(chain * DK + 16 * tc + 4 * grp + e) * dv + j0 + 16 * ct + l16];
             }
             accS[t][ct] = v;
-            if (tc < NTC) st_vec4(STl + (16 * ct + l16) * KR + 16 * tc + 4 * grp, v);
+            if (tc < NTC) {
+                st_vec4(STl + (16 * ct + l16) * KR + 16 * tc + 4 * grp, v);
+                st_vec4(SNl + (16 * tc + 4 * grp + (l16 & 3)) * L::SP + 16 * ct + (l16 & ~3), quad_transpose4(v));
+            }
         }
     }
     __syncthreads();                                          // prologue barrier
     for (int i = 0; i < nt; ++i) {
-        const int n = nt - 1 - i;
         const char* B0 = sm + (i & 1) * L::BUF;
         const bf* QTl = reinterpret_cast<const bf*>(B0 + L::QT);
         const bf* PTl = reinterpret_cast<const bf*>(B0 + L::PT);
@@ -1170,28 +1186,6 @@ __global__ __launch_bounds__(RsLds<DK>::THREADS, 1) void k_chunk_state_bwd_mf(Bw
         const bf* KNl = reinterpret_cast<const bf*>(B0 + L::KN);
         const float* GLl = reinterpret_cast<const float*>(B0 + L::GL);
         const bf* OTl = reinterpret_cast<const bf*>(B0 + L::OT);
-        // the gradient this chunk's exit state receives: [dk][dv] rows after a
-        // transpose inside each lane quad (lane q: row 16 tc + 4 grp + q,
-        // columns (l16 & ~3) .. +3 of the tile), and [dv][dk] directly
-        {
-            const int64_t cb = (chain * nt + n) * (int64_t)DK * dv;
-#pragma unroll
-            for (int t = 0; t < TPW; ++t) {
-                const int tc = wave + 4 * t;
-                if (tc < NTC) {
-#pragma unroll
-                    for (int ct = 0; ct < 2; ++ct) {
-                        const int jc = j0 + 16 * ct;
-                        if (a.dSLIo != nullptr) {
-                            const f32x4 tr = quad_transpose4(accS[t][ct]);
-                            st_vec4(static_cast<bf*>(a.dSLIo) + cb + (int64_t)(16 * tc + 4 * grp + (l16 & 3)) * dv + jc + (l16 & ~3), tr);
-                        }
-                        if (a.dSLT != nullptr)
-                            st_vec4(static_cast<bf*>(a.dSLT) + cb + (int64_t)(jc + l16) * DK + 16 * tc + 4 * grp, accS[t][ct]);
-                    }
-                }
-            }
-        }
         // dDelta rows 16 wave .. +15 -> dDelta^T
         {
             bfrag pa[2], ka[NKK];
@@ -1231,7 +1225,9 @@ __global__ __launch_bounds__(RsLds<DK>::THREADS, 1) void k_chunk_state_bwd_mf(Bw
                         a2 = IOB::mma(a2, wa[kb], fr(DTl, 16 * ct + l16, RP, kb, grp));
                     }
                     accS[t][ct] = gl * accS[t][ct] + a1 - a2;
+                    // dS^T and dS (lane q of a quad: row 16 tc + 4 grp + q) for the next chunk
                     st_vec4(STl + (16 * ct + l16) * KR + 16 * tc + 4 * grp, accS[t][ct]);
+                    st_vec4(SNl + (16 * tc + 4 * grp + (l16 & 3)) * L::SP + 16 * ct + (l16 & ~3), quad_transpose4(accS[t][ct]));
                 }
             }
         }

@@ -601,7 +601,11 @@ struct StateLds {
     static constexpr int O_W = 0, O_Q = O_W + 64 * GW, O_P = O_Q + NQ * 64 * GW, O_K = O_P + NQ * 64 * GT;
     static constexpr int O_U = O_K + DK * GT, O_G = O_U + VS * GT, GBUF = O_G + DK / 4;
     static constexpr int SRS = KPAD + EPL, DTS = 64 + EPL;
-    static constexpr int PRIV = VS * SRS * ES + VS * DTS * ES;
+    // NOQ (bf16, dk a multiple of 32): the state also row-major, [DK][SP],
+    // for the checkpoint copy
+    static constexpr bool CKL = NOQ && ES == 2 && DK % 32 == 0;
+    static constexpr int SP = VS + 16 / ES;
+    static constexpr int PRIV = VS * SRS * ES + VS * DTS * ES + (CKL ? DK * SP * ES : 0);
     static constexpr int LIMIT = 160 * 1024;
     // two operand buffers when they fit (loads of chunk n+1 overlap chunk n),
     // else one (the copy waits for the chunk to finish: one more barrier)
@@ -657,6 +661,10 @@ __global__ __launch_bounds__(state_threads(VS, (int)sizeof(Tio)), 1) void k_chun
     __shared__ __attribute__((aligned(16))) char smem[L::BYTES];
     Tio* SbT = reinterpret_cast<Tio*>(smem + NB * L::GBUF * 16);            // S^T      [j][c]
     Tio* DT = reinterpret_cast<Tio*>(smem + NB * L::GBUF * 16 + VS * SRS * ES);  // Delta^T  [j][s]
+    Tio* SN = reinterpret_cast<Tio*>(smem + NB * L::GBUF * 16 + VS * (SRS + DTS) * ES);   // S [c][j] (CHK, bf16)
+    // the checkpoints in the I/O dtype are copied from LDS by the loader waves
+    constexpr bool CKL = L::CKL;
+    constexpr int SP = L::SP;
 
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -724,11 +732,14 @@ __global__ __launch_bounds__(state_threads(VS, (int)sizeof(Tio)), 1) void k_chun
             else if (g < L::O_G) map(g - L::O_U, cGT{}, (int)LY.uwyt + j0 * 64 * ES, L::O_U);
             else { src[m] = (int)LY.gaml + (g - L::O_G) * 16; dst[m] = g * 16; }
         }
-        // register slots of chunks in flight: as many (up to three) as fit in
-        // the registers a lane has next to the compute waves' budget
+        // register slots of chunks in flight: as many (up to five) as fit in
+        // the registers a lane has next to the compute waves' budget, less
+        // what the checkpoint copy holds (measured: no spills)
         constexpr int NW = NCW + state_nlw(VS, ES);
         constexpr int WAVES_PER_SIMD = (NW + 3) / 4;
-        constexpr int VBUDGET = (WAVES_PER_SIMD <= 2 ? 256 : (WAVES_PER_SIMD == 3 ? 168 : 128)) - 2 * LPL - 16;
+        constexpr int NCKI = (VS * DK * ES / 16 + DK * VS * ES / 16 + L::NLD - 1) / L::NLD;   // copy rounds
+        constexpr int CKREG = CKL ? (NCKI <= 2 ? 64 : 96) : 0;
+        constexpr int VBUDGET = (WAVES_PER_SIMD <= 2 ? 256 : (WAVES_PER_SIMD == 3 ? 168 : 128)) - 2 * LPL - 16 - CKREG;
         constexpr int DEPTH0 = VBUDGET / (4 * LPL);
         constexpr int DEPTH = DEPTH0 > 5 ? 5 : (DEPTH0 < 1 ? 1 : DEPTH0);
         frag r[DEPTH][LPL];
@@ -755,8 +766,34 @@ __global__ __launch_bounds__(state_threads(VS, (int)sizeof(Tio)), 1) void k_chun
         // with no conditional fetch the compiler can count exactly how many
         // loads are still in flight behind the ones a store needs, so the
         // stores wait only for their own chunk, DEPTH iterations old.
+        // the state entering chunk n, from LDS (S^T and S, bf16) to the
+        // checkpoints [dv][dk] and [dk][dv]; runs before barrier 1 of chunk n,
+        // while the compute waves only read both copies
+        auto ckpt = [&](int n) {
+            if constexpr (CKL) {
+                constexpr int GR = DK * ES / 16, GN = VS * ES / 16, EG = 16 / ES;
+                constexpr int G1 = VS * GR, G2 = DK * GN;
+                const int64_t cb = (chain * (int64_t)nt + n) * DK * dv;
+#pragma unroll
+                for (int q0 = 0; q0 < G1 + G2; q0 += L::NLD) {
+                    const int q = q0 + (wave - NCW) * 64 + lane;
+                    if (q < G1) {
+                        const int j = q / GR, c = (q % GR) * EG;
+                        const f32x4 v = *reinterpret_cast<const f32x4*>(SbT + j * SRS + c);
+                        if (a.S_chkT != nullptr)
+                            *reinterpret_cast<f32x4*>(static_cast<Tio*>(a.S_chkT) + cb + (int64_t)(j0 + j) * DK + c) = v;
+                    } else if (q < G1 + G2) {
+                        const int c = (q - G1) / GN, jj = ((q - G1) % GN) * EG;
+                        const f32x4 v = *reinterpret_cast<const f32x4*>(SN + c * SP + jj);
+                        if (a.S_chkIo != nullptr)
+                            *reinterpret_cast<f32x4*>(static_cast<Tio*>(a.S_chkIo) + cb + (int64_t)c * dv + j0 + jj) = v;
+                    }
+                }
+            }
+        };
         constexpr int HALF = LPL / 2;
         auto iter = [&](int n, frag* rs) {
+            ckpt(n);
             if (NB == 2) {
                 store((n + 1) & 1, rs, 0, HALF);
                 fetch(n + 1 + DEPTH, rs, 0, HALF);
@@ -822,7 +859,13 @@ __global__ __launch_bounds__(state_threads(VS, (int)sizeof(Tio)), 1) void k_chun
         const int rt = tb * SPW + i;
         if (rt < SRT) {
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) st_vec4(&SbT[(jc + 16 * ct + l16) * SRS + 16 * rt + 4 * grp], accS[i][ct]);
+            for (int ct = 0; ct < NCT; ++ct) {
+                st_vec4(&SbT[(jc + 16 * ct + l16) * SRS + 16 * rt + 4 * grp], accS[i][ct]);
+                // S row-major: after a transpose inside each lane quad, lane q
+                // holds row 16 rt + 4 grp + q, columns (l16 & ~3) .. +3 of the tile
+                if constexpr (CKL)
+                    st_vec4(&SN[(16 * rt + 4 * grp + (l16 & 3)) * SP + jc + 16 * ct + (l16 & ~3)], quad_transpose4(accS[i][ct]));
+            }
         }
     }
     __syncthreads();                                      // prologue barrier
@@ -836,10 +879,11 @@ __global__ __launch_bounds__(state_threads(VS, (int)sizeof(Tio)), 1) void k_chun
     for (int n = 0; n < nt; ++n) {
         if constexpr (CHK) {
             // checkpoint: the state entering chunk n (kept for the backward pass).
-            // Lanes 4m .. 4m+3 of a 16-lane row hold 4 columns of 4 state rows;
-            // a transpose inside each lane quad gives every lane 4 consecutive
+            // fp32 here; in bf16 the loader waves copy it from LDS.  Lanes
+            // 4m .. 4m+3 of a 16-lane row hold 4 columns of 4 state rows; a
+            // transpose inside each lane quad gives every lane 4 consecutive
             // columns of one row, written as one vector.
-            if (a.S_chk != nullptr || a.S_chkIo != nullptr) {
+            if (a.S_chk != nullptr) {
                 const int64_t base = (chain * (int64_t)nt + n) * DK * dv + j0 + jc + (l16 & ~3);
 #pragma unroll
                 for (int i = 0; i < SPW; ++i) {
@@ -849,22 +893,8 @@ __global__ __launch_bounds__(state_threads(VS, (int)sizeof(Tio)), 1) void k_chun
                         for (int ct = 0; ct < NCT; ++ct) {
                             const f32x4 t = quad_transpose4(accS[i][ct]);
                             const int64_t o = base + (int64_t)(16 * rt + 4 * grp + (l16 & 3)) * dv + 16 * ct;
-                            if (a.S_chk != nullptr) *reinterpret_cast<f32x4*>(a.S_chk + o) = t;
-                            if (a.S_chkIo != nullptr) st_vec4(static_cast<Tio*>(a.S_chkIo) + o, t);
+                            *reinterpret_cast<f32x4*>(a.S_chk + o) = t;
                         }
-                    }
-                }
-            }
-            if (a.S_chkT != nullptr) {
-                // the same state transposed, [dv][dk] in the I/O dtype
-                Tio* dstT = static_cast<Tio*>(a.S_chkT) + (chain * (int64_t)nt + n) * DK * dv;
-#pragma unroll
-                for (int i = 0; i < SPW; ++i) {
-                    const int rt = tb * SPW + i;
-                    if (rt < SRT) {
-#pragma unroll
-                        for (int ct = 0; ct < NCT; ++ct)
-                            st_vec4(dstT + (int64_t)(j0 + jc + 16 * ct + l16) * DK + 16 * rt + 4 * grp, accS[i][ct]);
                     }
                 }
             }
@@ -975,7 +1005,11 @@ __global__ __launch_bounds__(state_threads(VS, (int)sizeof(Tio)), 1) void k_chun
             const int rt = tb * SPW + i;
             if (rt < SRT) {
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) st_vec4(&SbT[(jc + 16 * ct + l16) * SRS + 16 * rt + 4 * grp], accS[i][ct]);
+                for (int ct = 0; ct < NCT; ++ct) {
+                    st_vec4(&SbT[(jc + 16 * ct + l16) * SRS + 16 * rt + 4 * grp], accS[i][ct]);
+                    if constexpr (CKL)
+                        st_vec4(&SN[(16 * rt + 4 * grp + (l16 & 3)) * SP + jc + 16 * ct + (l16 & ~3)], quad_transpose4(accS[i][ct]));
+                }
             }
         }
         __syncthreads();                                  // barrier 2
@@ -1062,6 +1096,7 @@ static hipError_t state_v(const StateArgs& a, hipStream_t s)
     } else {
         const int64_t nblk = a.B * a.H * (int64_t)a.nslices;
         constexpr int nthreads = state_threads(VS, (int)sizeof(Tio));
+        if ((a.S_chkT != nullptr || a.S_chkIo != nullptr) && !StateLds<Tio, DK, VS, true>::CKL) return hipErrorInvalidValue;
         if (a.S_chk != nullptr || a.S_chkT != nullptr || a.S_chkIo != nullptr)
             hipLaunchKernelGGL((k_chunk_state<Tio, DK, VS, true>), dim3((unsigned)nblk), dim3(nthreads), 0, s, a);
         else
