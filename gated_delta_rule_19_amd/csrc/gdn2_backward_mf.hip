@@ -6,9 +6,9 @@
 //
 // k_chunk_grad_val  the value-side products on bf16 matrix cores, fp32
 //   accumulation.  Operands come from the workspace blocks the recomputed
-//   forward writes in the backward's layout (W, P^T, Ktil, U^T, T), from the chunk
-//   checkpoints (S0 and the exit gradient dSL, each in bf16 [dk][dv] and
-//   transposed [dv][dk]) and from dO, v, w, b, k, alpha.  Every
+//   forward writes in the backward's layout (W, P^T, Ktil, U^T, T, Eh), from
+//   the chunk checkpoints (S0 and the exit gradient dSL, each in bf16
+//   [dk][dv] and transposed [dv][dk]) and from dO, v, w.  Every
 //   operand is laid out with its contraction index contiguous (transposed
 //   copies are made in LDS where needed; LDS rows are padded by 16 bytes), so
 //   a fragment is one 16-byte read.  In order:
@@ -137,11 +137,9 @@ struct GvLds {
     static constexpr int R3SZ = (64 * LT + 64 * LD) * 2 > (kMaxD * LT + 64 * LT) * 2 ? (64 * LT + 64 * LD) * 2
                                                                                        : (kMaxD * LT + 64 * LT) * 2;
     static constexpr int R4 = R3 + R3SZ;                          // U, then Delta [64][LD]
-    static constexpr int R5 = R4 + 64 * LD * 2;                   // dDelta [64][LD] + dDelta^T [dv][LT] | G fp32 [64][dk]
-    static constexpr int R5SZ = (64 * LD + kMaxD * LT) * 2 > 64 * kMaxD * 4 ? (64 * LD + kMaxD * LT) * 2 : 64 * kMaxD * 4;
-    static constexpr int R7 = R5 + R5SZ;                          // Eh [64][LD]
-    static constexpr int RT = R7 + 64 * LD * 2;                   // scan totals [256]
-    static constexpr int BYTES = RT + kThreads * 4;
+    static constexpr int R5 = R4 + 64 * LD * 2;                   // dDelta [64][LD] + dDelta^T [dv][LT]
+    static constexpr int R7 = R5 + (64 * LD + kMaxD * LT) * 2;    // Eh [64][LD]
+    static constexpr int BYTES = R7 + 64 * LD * 2;
 };
 
 // Tiles t = wave, wave + 4, ... < NT of one product: fetch(t, a, b) loads the
@@ -208,9 +206,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
     bf* Dll = reinterpret_cast<bf*>(sm + L::R4);
     bf* dDl = reinterpret_cast<bf*>(sm + L::R5);
     bf* dDtl = dDl + 64 * ldv;
-    float* Gl = reinterpret_cast<float*>(sm + L::R5);
     bf* Ehl = reinterpret_cast<bf*>(sm + L::R7);
-    float* tot = reinterpret_cast<float*>(sm + L::RT);
 
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
     const int wave = tid >> 6;
@@ -228,6 +224,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
     const bf* Tg_ = reinterpret_cast<const bf*>(blk + a.t_off);         // T [64][64]
     const bf* Ptg = reinterpret_cast<const bf*>(blk + LY.p);             // P^T [64][64]
     const bf* Kng = reinterpret_cast<const bf*>(blk + bwd_ext(a.t_off, DK).kn);   // Ktil [64][dk]
+    const bf* Ehg = reinterpret_cast<const bf*>(blk + bwd_ext(a.t_off, DK).eh);   // Eh [64][dk]
     const bf* Wg = reinterpret_cast<const bf*>(blk + LY.wwy);            // W [64][dk]
     const bf* Utg = reinterpret_cast<const bf*>(blk + LY.uwyt);          // U^T [dv][64]
     const bf* S0 = static_cast<const bf*>(a.S_chk) + ci * (int64_t)DK * DV;     // [dk][dv]
@@ -236,10 +233,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
     const bf* dSLt = static_cast<const bf*>(a.dSLT) + ci * (int64_t)DK * DV;
     const bf* dO = static_cast<const bf*>(a.dO);
     const bf* vg = static_cast<const bf*>(a.v);
-    const bf* kg = static_cast<const bf*>(a.k);
     const Tg* wgt = static_cast<const Tg*>(a.w);
-    const Tg* bgt = static_cast<const Tg*>(a.b);
-    const Tg* agt = static_cast<const Tg*>(a.alpha);
     Tg* dwg = static_cast<Tg*>(a.dw);
     bf* dvg = static_cast<bf*>(a.dv_out);
     float* sc = a.gsc + ci * gradmf_scratch_floats(DK);
@@ -249,17 +243,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
     bf* s_dP = reinterpret_cast<bf*>(sc + 3 * 64 * DK);
     bf* s_dA = s_dP + 4096;
     float* s_dGL = sc + 3 * 64 * DK + 4096;
-    const bool logits = (a.flags & kFlagGateLogits) != 0, l2 = (a.flags & kFlagQkL2norm) != 0;
-    const float bscale = (a.flags & kFlagNegEigval) ? 2.f : 1.f;
+    const bool logits = (a.flags & kFlagGateLogits) != 0;
 
     // ---- phase 0: operands into LDS ----------------------------------------
     // Every global load of the phase is issued before the first LDS write (one
     // round of memory latency instead of one per operand).
     constexpr int NTP = 64 * 8 / kThreads, NKT = DK * 8 / kThreads, NUT = DV * 8 / kThreads;
-    constexpr int NDO = 64 * (DV / 8) / kThreads, NV = 64 * DK / 4 / kThreads;
-    bfrag tq[NTP], pq[NTP], kq[NKT], uq[NUT], oq[NDO];
-    typename GateVec<Tg>::type ax[NV], bx[NV];     // raw until used (see the du phase)
-    bf16x4 kx[NV];
+    constexpr int NDO = 64 * (DV / 8) / kThreads;
+    bfrag tq[NTP], pq[NTP], kq[NKT], eq[NKT], uq[NUT], oq[NDO];
 #pragma unroll
     for (int m = 0; m < NTP; ++m) {                                 // T, P
         const int g = tid + m * kThreads, r = g >> 3, c0 = (g & 7) * 8;
@@ -270,6 +261,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
     for (int m = 0; m < NKT; ++m) {                                 // Ktil [r][c]
         const int g = tid + m * kThreads, r = g / (DK / 8), c0 = (g - r * (DK / 8)) * 8;
         kq[m] = *reinterpret_cast<const bfrag*>(Kng + r * DK + c0);
+        eq[m] = *reinterpret_cast<const bfrag*>(Ehg + r * DK + c0);
     }
 #pragma unroll
     for (int m = 0; m < NUT; ++m) {                                 // U^T [j][r]
@@ -281,14 +273,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
         const int g = tid + m * kThreads, r = g / (DV / 8), j0 = (g - r * (DV / 8)) * 8;
         oq[m] = *reinterpret_cast<const bfrag*>(dO + (row0 + (r < Ln ? r : Ln - 1) * H) * DV + j0);
     }
-    cld_load<DK>(ax, agt, row0, H, Ln);
-#pragma unroll
-    for (int u = 0; u < NV; ++u) {                                  // b, k for Eh
-        const int i = tid + u * kThreads, r = i / (DK / 4), c4 = 4 * (i - r * (DK / 4));
-        const int64_t o = (row0 + (r < Ln ? r : Ln - 1) * H) * DK + c4;
-        bx[u] = *reinterpret_cast<const typename GateVec<Tg>::type*>(bgt + o);
-        kx[u] = *reinterpret_cast<const bf16x4*>(kg + o);
-    }
 #pragma unroll
     for (int m = 0; m < NTP; ++m) {                                 // T, T^T; P^T
         const int g = tid + m * kThreads, r = g >> 3, c0 = (g & 7) * 8;
@@ -298,9 +282,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
         for (int e = 0; e < 8; ++e) Ttl[(c0 + e) * LT + r] = tq[m][e];
     }
 #pragma unroll
-    for (int m = 0; m < NKT; ++m) {                                 // Ktil
+    for (int m = 0; m < NKT; ++m) {                                 // Ktil, Eh
         const int g = tid + m * kThreads, r = g / (DK / 8), c0 = (g - r * (DK / 8)) * 8;
         *reinterpret_cast<bfrag*>(Ktl + r * ldk + c0) = kq[m];
+        *reinterpret_cast<bfrag*>(Ehl + r * ldk + c0) = eq[m];
     }
 #pragma unroll
     for (int m = 0; m < NUT; ++m) {                                 // U [r][j] from U^T [j][r]
@@ -318,19 +303,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
         *reinterpret_cast<bfrag*>(dOl + r * ldv + j0) = oq[m];
 #pragma unroll
         for (int e = 0; e < 8; ++e) dOtl[(j0 + e) * LT + r] = oq[m][e];
-    }
-    cld_scan<DK, Tg>(Gl, tot, ax, Ln, logits);
-#pragma unroll
-    for (int u = 0; u < NV; ++u) {                                  // Eh = Gamma b k (zero past the end)
-        const int i = tid + u * kThreads, r = i / (DK / 4), c4 = 4 * (i - r * (DK / 4));
-        const f32x4 g4 = *reinterpret_cast<const f32x4*>(&Gl[r * DK + c4]);
-        const f32x4 b4 = logits ? sigmoid4(widen4(bx[u])) * bscale : widen4(bx[u]);
-        f32x4 k4 = IOB::unpack4(kx[u]);
-        if (l2) k4 = k4 * row_rnorm<DK / 4>(k4);
-        f32x4 x;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = r < Ln ? __expf(g4[e]) * b4[e] * k4[e] : 0.f;
-        st_vec4(Ehl + r * ldk + c4, x);
     }
     // dGamma_L = rowsum(dSL * S0), fp32 sums of the bf16 checkpoints (dk = 32:
     // with larger dk it comes from the panels below), before the first global
@@ -485,36 +457,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
 #pragma unroll
                    for (int i = 0; i < 4; ++i) s_dP[(r + i) * 64 + s] = (bf)(s <= r + i ? acc[i] : 0.f);
                });
-    // ---- du = T^T dDelta -> dw = du v, dv = du w ---------------------------------
-    // v and w at this wave's tile positions, and w, v for u below, are all
-    // requested before the first product (one wait for the stores above
-    // instead of one per tile row)
-    constexpr int NTU = 4 * NTV / 4;                                // du tiles per wave
-    constexpr int NVV = 64 * DV / 4 / kThreads;
-    // (kept in their memory dtypes until used: a conversion right after the
-    // load would wait for it; rows past the end are clamped and never stored)
-    Tg wt[NTU][4];
-    bf vt[NTU][4];
-    typename GateVec<Tg>::type wx[NVV];
-    bf16x4 vx[NVV];
+    // ---- du = T^T dDelta -> dw = du v, dv = du w;  u = w v ----------------------
+    // A transpose inside each lane quad turns a du tile's accumulator into rows
+    // of 4 consecutive columns (lane q: row 16 tr + 4 grp + q), so w and v are
+    // read once, as vectors, for dw, dv and u alike.  They are requested before
+    // the first product and kept in their memory dtypes until used (a
+    // conversion right after the load would wait for it); rows past the end
+    // are clamped on load, never stored, and give u = 0.
+    constexpr int NTU = NTV;                                        // du tiles per wave
+    typedef typename GateVec<Tg>::type gvec;
+    gvec wx[NTU];
+    bf16x4 vx[NTU], ux[NTU];
 #pragma unroll
     for (int m = 0; m < NTU; ++m) {
         const int t = wave + 4 * m, tr = t / NTV, tn = t - tr * NTV;
-        const int r = 16 * tr + 4 * grp, j = 16 * tn + l16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rc = r + i < Ln ? r + i : Ln - 1;
-            const int64_t o = (row0 + rc * H) * DV + j;
-            wt[m][i] = wgt[o];
-            vt[m][i] = vg[o];
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < NVV; ++u) {
-        const int i = tid + u * kThreads, r = i / (DV / 4), j4 = 4 * (i - r * (DV / 4));
-        const int64_t o = (row0 + (r < Ln ? r : Ln - 1) * H) * DV + j4;
-        wx[u] = *reinterpret_cast<const typename GateVec<Tg>::type*>(wgt + o);
-        vx[u] = *reinterpret_cast<const bf16x4*>(vg + o);
+        const int r = 16 * tr + 4 * grp + (l16 & 3), j = 16 * tn + (l16 & ~3);
+        const int64_t o = (row0 + (r < Ln ? r : Ln - 1) * H) * DV + j;
+        wx[m] = *reinterpret_cast<const gvec*>(wgt + o);
+        vx[m] = *reinterpret_cast<const bf16x4*>(vg + o);
     }
 #pragma unroll
     for (int m = 0; m < NTU; ++m) {
@@ -523,25 +483,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
             acc = IOB::mma(acc, fr(Ttl, 16 * tr + l16, LT, kb, grp), fr(dDtl, 16 * tn + l16, LT, kb, grp));
-        const int r = 16 * tr + 4 * grp, j = 16 * tn + l16;
+        const f32x4 d4 = quad_transpose4(acc);                     // du[r][j .. j+3]
+        const int r = 16 * tr + 4 * grp + (l16 & 3), j = 16 * tn + (l16 & ~3);
+        const f32x4 w4 = widen4(wx[m]), sw = logits ? sigmoid4(w4) : w4, v4 = IOB::unpack4(vx[m]);
+        if (r < Ln) {
+            const int64_t o = (row0 + r * H) * DV + j;
+            const f32x4 dwa = d4 * v4;                              // gradient of the activated gate
+            f32x4 dw4 = dwa;
+            if (logits) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (r + i < Ln) {
-                const int64_t o = (row0 + (r + i) * H) * DV + j;
-                const float wr = gate_f(wt[m][i]), sw = logits ? sigmoid_f(wr) : wr;
-                const float dwa = acc[i] * Io<bf>::to_f(vt[m][i]);     // gradient of the activated gate
-                gs(dwg, o, logits ? dwa * sw * (1.f - sw) : dwa);
-                gs(dvg, o, acc[i] * sw);
+                for (int e = 0; e < 4; ++e) dw4[e] = dwa[e] * sw[e] * (1.f - sw[e]);
             }
+            st_vec4(dwg + o, dw4);
+            st_vec4(dvg + o, d4 * sw);
         }
+        ux[m] = IOB::pack4(r < Ln ? sw * v4 : f32x4{0.f, 0.f, 0.f, 0.f});
     }
     __syncthreads();
-    // ---- u = w v (padding tokens 0) ----------------------------------------------
 #pragma unroll
-    for (int u = 0; u < NVV; ++u) {
-        const int i = tid + u * kThreads, r = i / (DV / 4), j4 = 4 * (i - r * (DV / 4));
-        const f32x4 x = (logits ? sigmoid4(widen4(wx[u])) : widen4(wx[u])) * IOB::unpack4(vx[u]);
-        st_vec4(ul + r * ldv + j4, r < Ln ? x : f32x4{0.f, 0.f, 0.f, 0.f});
+    for (int m = 0; m < NTU; ++m) {                                 // u over dO (no longer read)
+        const int t = wave + 4 * m, tr = t / NTV, tn = t - tr * NTV;
+        *reinterpret_cast<bf16x4*>(ul + (16 * tr + 4 * grp + (l16 & 3)) * ldv + 16 * tn + (l16 & ~3)) = ux[m];
     }
     __syncthreads();
     // ---- dT = dDelta u^T + dW Eh^T (stored transposed);  dEh = T^T dW ------------

@@ -102,7 +102,7 @@ __device__ inline int unpack2(unsigned p, int i) { return (int)((p >> (2 * i)) &
 // NUI = (token, 4-column) value items per thread: 64 * dv / 4 <= 256 * NUI
 // Tg = gate dtype (alpha, b, w): float, or __bf16 with bf16 I/O
 // TOUT: the backward's layout of the block (bf16, KPAD = DK): Qh^T and P^T in
-// place of Qh and P, and T, Ktil and W^T appended from a.t_off on (BwdExt)
+// place of Qh and P, and T, Ktil, W^T and Eh appended from a.t_off on (BwdExt)
 template <typename Tio, int DK, int NUI, typename Tg, bool TOUT = false>
 __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2)) void k_chunk_prep(PrepArgs a)
 {
@@ -170,6 +170,7 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
     const BwdExt BX = bwd_ext(a.t_off, DK);      // (TOUT only)
     Tio* kn_out = reinterpret_cast<Tio*>(blk + BX.kn);
     Tio* wt_out = reinterpret_cast<Tio*>(blk + BX.wt);
+    Tio* eh_out = reinterpret_cast<Tio*>(blk + BX.eh);
 
     typedef typename IO::frag frag;
 
@@ -315,7 +316,10 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
             const f32x4 qhv = xq * pre;
             if constexpr (!TOUT) st_vec4(qh_out + r * KPAD + c0, qhv);
             const f32x4 ehv = xe * pre, ktv = kv * (zblk * ig) * post;
-            if constexpr (TOUT) st_vec4(kn_out + r * DK + c0, ktv);
+            if constexpr (TOUT) {
+                st_vec4(kn_out + r * DK + c0, ktv);
+                st_vec4(eh_out + r * DK + c0, ehv);
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 ehf[e][i / EPL][i % EPL] = IO::from_f(ehv[e]);

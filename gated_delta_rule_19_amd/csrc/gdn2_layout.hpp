@@ -23,6 +23,7 @@
 //   t    [64][64]  T
 //   kn   [64][dk]  Ktil (row-major)
 //   wt   [dk][64]  W^T
+//   eh   [64][dk]  Eh = Gamma (b k)
 #pragma once
 
 #include <stdint.h>
@@ -50,12 +51,12 @@ __host__ __device__ constexpr WsLayout ws_layout(int64_t dk, int64_t dv, int64_t
 
 // the backward's extension of a block whose forward layout ends at fwd_block
 struct BwdExt {
-    int64_t t, kn, wt, block;
+    int64_t t, kn, wt, eh, block;
 };
 __host__ __device__ constexpr BwdExt bwd_ext(int64_t fwd_block, int64_t dk)
 {
     return BwdExt{fwd_block, fwd_block + 64 * 64 * 2, fwd_block + 64 * 64 * 2 + 64 * dk * 2,
-                  fwd_block + 64 * 64 * 2 + 2 * (64 * dk * 2)};
+                  fwd_block + 64 * 64 * 2 + 2 * (64 * dk * 2), fwd_block + 64 * 64 * 2 + 3 * (64 * dk * 2)};
 }
 
 }  // namespace gdn2
