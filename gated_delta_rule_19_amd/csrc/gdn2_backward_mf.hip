@@ -76,6 +76,18 @@ template <typename T> __device__ inline void gs(T* p, int64_t i, float x) { p[i]
 // dEh fp32 [64][dk]; dP, dA bf16 [64][64]; dGamma_L fp32 [dk]
 __host__ __device__ inline int64_t gradmf_scratch_floats(int dk) { return 3 * 64 * (int64_t)dk + 4096 + dk; }
 
+// Key-axis items of a chunk on 256 threads: thread t holds channels
+// c4 .. c4+3, c4 = 4 (t mod DK/4), of the NV consecutive rows
+// (t div DK/4) NV + u, u < NV (the DK/4 lanes of a row are consecutive).
+template <int DK>
+__device__ __forceinline__ void key_item(int u, int& r, int& c4)
+{
+    constexpr int CG = DK / 4, NV = 64 * CG / kThreads;
+    const int tid = threadIdx.x;
+    r = (tid / CG) * NV + u;
+    c4 = 4 * (tid % CG);
+}
+
 // G[r][c] = sum of log alpha over tokens 0..r of the chunk (alpha = 1 past its
 // end), for 256 threads: logs in parallel (every load issued before the first
 // use), then a scan of 256/DK segments per channel with the segment totals
@@ -86,10 +98,10 @@ __device__ __attribute__((always_inline)) inline void cld_load(typename GateVec<
                                                                const Tg* alpha, int64_t row0, int64_t H, int Ln)
 {
     constexpr int NV = 64 * DK / 4 / kThreads;
-    const int tid = threadIdx.x;
 #pragma unroll
     for (int u = 0; u < NV; ++u) {       // raw and unconditional (rows past the end clamped)
-        const int i = tid + u * kThreads, r = i / (DK / 4), c4 = 4 * (i - r * (DK / 4));
+        int r, c4;
+        key_item<DK>(u, r, c4);
         x[u] = *reinterpret_cast<const typename GateVec<Tg>::type*>(alpha + (row0 + (r < Ln ? r : Ln - 1) * H) * DK + c4);
     }
 }
@@ -103,7 +115,8 @@ __device__ __attribute__((always_inline)) inline void cld_scan(float* G, float* 
     const int tid = threadIdx.x;
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
-        const int i = tid + u * kThreads, r = i / (DK / 4), c4 = 4 * (i - r * (DK / 4));
+        int r, c4;
+        key_item<DK>(u, r, c4);
         const f32x4 a = logits ? sigmoid4(widen4(x[u])) : widen4(x[u]);
         f32x4 l;
 #pragma unroll
@@ -591,21 +604,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
 //   column side kak[s,c] = exp(G_16J - G_s) sum_r dA[r,s] F_IJ[c] EA[r,c]
 //               + the same with dP and QA,  EA = e_r exp(G_r - G_16I),
 //               QA = q_r exp(G_r - G_16I)
-// The token-indexed operands stay row-major in LDS; fragments whose
-// contraction index runs over tokens are gathered with 2-byte reads.  Wave w
-// owns column tiles w, w+4, ... for all 64 rows.  Then a per-row pass forms
+// Every operand is stored in LDS with its contraction index contiguous:
+// dA and dP row-major and transposed, KY, EA and QA transposed ([channel]
+// [token]), written element by element from registers in phase A, so that
+// every fragment of the products is one 16-byte read.  Wave w owns column
+// tiles w, w+4, ... for all 64 rows.  Then a per-row pass forms
 // the gradients of q, k and b and dG, and dalpha is the reverse cumulative
 // sum of dG.  Every phase issues its global loads before using any of them.
 // ---------------------------------------------------------------------------
-
-// 8 consecutive rows k0..k0+7 of column c from a row-major bf16 array (stride ld)
-__device__ __forceinline__ bfrag gather8(const bf* base, int k0, int c, int ld)
-{
-    bfrag r;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = base[(k0 + e) * ld + c];
-    return r;
-}
 
 __device__ __forceinline__ bfrag scale8(bfrag x, float f)
 {
@@ -617,11 +623,11 @@ __device__ __forceinline__ bfrag scale8(bfrag x, float f)
 
 template <int DK>
 struct GkLds {
-    static constexpr int KS = DK + 4;              // row stride of KY, EA, QA (bf16)
     static constexpr int RS = DK + 4;              // row stride of the fp32 results / dG
     static constexpr int IN_A = 0;                 // dA, dP [64][LT] bf16
-    static constexpr int IN_K = IN_A + 2 * 64 * LT * 2;   // KY, EA, QA [64][KS] bf16
-    static constexpr int SZ_IN = IN_K + 3 * 64 * KS * 2;
+    static constexpr int IN_AT = IN_A + 2 * 64 * LT * 2;  // dA^T, dP^T [64][LT] bf16
+    static constexpr int IN_K = IN_AT + 2 * 64 * LT * 2;  // KY^T, EA^T, QA^T [DK][LT] bf16
+    static constexpr int SZ_IN = IN_K + 3 * DK * LT * 2;
     static constexpr int SZ_RES = 3 * 64 * RS * 4;        // deA (then dG), dqP, kak fp32 [64][RS]
     static constexpr int BIG = SZ_IN > SZ_RES ? SZ_IN : SZ_RES;
 };
@@ -631,7 +637,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
 {
     using L = GkLds<DK>;
     constexpr int CG = DK / 4, R = DK / 16, NCT = DK / 16, CPW = (NCT + 3) / 4;
-    constexpr int KS = L::KS, RS = L::RS;
+    constexpr int RS = L::RS;
     constexpr int NV = 64 * DK / 4 / kThreads;
     typedef typename GateVec<Tg>::type gvec;
     __shared__ __attribute__((aligned(16))) float G[64 * DK];
@@ -640,9 +646,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
     __shared__ float tot[kThreads];
     bf* dAl = reinterpret_cast<bf*>(big + L::IN_A);
     bf* dPl = dAl + 64 * LT;
-    bf* KYl = reinterpret_cast<bf*>(big + L::IN_K);
-    bf* EAl = KYl + 64 * KS;
-    bf* QAl = EAl + 64 * KS;
+    bf* dATl = reinterpret_cast<bf*>(big + L::IN_AT);
+    bf* dPTl = dATl + 64 * LT;
+    bf* KYTl = reinterpret_cast<bf*>(big + L::IN_K);
+    bf* EATl = KYTl + DK * LT;
+    bf* QATl = EATl + DK * LT;
     float* deAl = reinterpret_cast<float*>(big);               // results, after the products
     float* dqPl = deAl + 64 * RS;
     float* kakl = dqPl + 64 * RS;
@@ -675,34 +683,52 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
 
     // ---- phase A: loads (raw), then dA, dP, G, KY, EA, QA into LDS ----------
     {
-        bfrag xa[2], xp[2];
+        // dA and dP in 8 x 8 blocks: thread t < 128 takes block t mod 64 of dA
+        // (t < 64) or dP, rows 8 (b / 8) .., columns 8 (b mod 8) ..; it writes
+        // the block row-major and, transposed in registers, into the
+        // transposed copy (threads t >= 128 load the same blocks again and
+        // write nothing: every load is unconditional)
+        bfrag xb[8];
+        const int bk = tid & 63, bR = bk >> 3, bS = bk & 7;
+        const bf* bsrc = (tid & 64) ? s_dP : s_dA;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xb[e] = *reinterpret_cast<const bfrag*>(bsrc + (8 * bR + e) * 64 + 8 * bS);
         gvec ax[NV], bx[NV];
         bf16x4 kx[NV], qx[NV];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int i = tid + u * kThreads;
-            xa[u] = *reinterpret_cast<const bfrag*>(s_dA + 8 * i);
-            xp[u] = *reinterpret_cast<const bfrag*>(s_dP + 8 * i);
-        }
         cld_load<DK>(ax, agt, row0, H, Ln);
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
-            const int i = tid + u * kThreads, r = i / CG, c4 = 4 * (i - r * CG);
+            int r, c4;
+            key_item<DK>(u, r, c4);
             const int64_t o = (row0 + (r < Ln ? r : Ln - 1) * H) * DK + c4;
             kx[u] = *reinterpret_cast<const bf16x4*>(kg + o);
             qx[u] = *reinterpret_cast<const bf16x4*>(qg + o);
             bx[u] = *reinterpret_cast<const gvec*>(bgt + o);
         }
+        if (tid < 128) {
+            bf* dst = (tid & 64) ? dPl : dAl;
+            bf* dstT = (tid & 64) ? dPTl : dATl;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int i = tid + u * kThreads, r = i >> 3, s8 = 8 * (i & 7);
-            *reinterpret_cast<bfrag*>(dAl + r * LT + s8) = xa[u];
-            *reinterpret_cast<bfrag*>(dPl + r * LT + s8) = xp[u];
+            for (int e = 0; e < 8; ++e) *reinterpret_cast<bfrag*>(dst + (8 * bR + e) * LT + 8 * bS) = xb[e];
+#pragma unroll
+            for (int f = 0; f < 8; ++f) {
+                bfrag y;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] = xb[e][f];
+                *reinterpret_cast<bfrag*>(dstT + (8 * bS + f) * LT + 8 * bR) = y;
+            }
         }
         cld_scan<DK, Tg>(G, tot, ax, Ln, logits);
+        // KY, EA, QA transposed: a thread's NV consecutive rows of one channel
+        // are one vector store
+        typedef bf rowv __attribute__((ext_vector_type(NV)));
+        rowv ty[4], te[4], tq[4];
+        int rb = 0, cb = 0;
+        key_item<DK>(0, rb, cb);
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
-            const int i = tid + u * kThreads, r = i / CG, c4 = 4 * (i - r * CG);
+            int r, c4;
+            key_item<DK>(u, r, c4);
             const f32x4 g4 = *reinterpret_cast<const f32x4*>(&G[r * DK + c4]);
             const f32x4 gj = *reinterpret_cast<const f32x4*>(&G[(r & ~15) * DK + c4]);
             const bool ok = r < Ln;
@@ -720,9 +746,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
                 ea[e] = ok ? b4[e] * k4[e] * up : 0.f;
                 qa[e] = ok ? q4[e] * up : 0.f;
             }
-            st_vec4(KYl + r * KS + c4, ky);
-            st_vec4(EAl + r * KS + c4, ea);
-            st_vec4(QAl + r * KS + c4, qa);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                ty[e][u] = (bf)ky[e];
+                te[e][u] = (bf)ea[e];
+                tq[e][u] = (bf)qa[e];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            *reinterpret_cast<rowv*>(KYTl + (cb + e) * LT + rb) = ty[e];
+            *reinterpret_cast<rowv*>(EATl + (cb + e) * LT + rb) = te[e];
+            *reinterpret_cast<rowv*>(QATl + (cb + e) * LT + rb) = tq[e];
         }
     }
     __syncthreads();
@@ -744,7 +779,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
             for (int kb = 0; kb < (I + 2) / 2; ++kb) {
                 const int s0 = kb * 32 + grp * 8, J = s0 >> 4;
                 const float f = J < I ? __expf(gI - G[16 * J * DK + c]) : 1.f;
-                const bfrag bk = scale8(gather8(KYl, s0, c, KS), f);
+                const bfrag bk = scale8(fr(KYTl, c, LT, kb, grp), f);
                 acc[m][I][0] = IOB::mma(acc[m][I][0], fr(dAl, 16 * I + l16, LT, kb, grp), bk);
                 acc[m][I][1] = IOB::mma(acc[m][I][1], fr(dPl, 16 * I + l16, LT, kb, grp), bk);
             }
@@ -754,10 +789,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
                 const int r0 = kb * 32 + grp * 8, Ir = r0 >> 4;
                 const float f = Ir > I ? __expf(G[16 * Ir * DK + c] - gI) : 1.f;
                 const int s = 16 * I + l16;
-                const bfrag be = scale8(gather8(EAl, r0, c, KS), f);
-                const bfrag bq = scale8(gather8(QAl, r0, c, KS), f);
-                acc[m][I][2] = IOB::mma(acc[m][I][2], gather8(dAl, r0, s, LT), be);
-                acc[m][I][3] = IOB::mma(acc[m][I][3], gather8(dPl, r0, s, LT), bq);
+                const bfrag be = scale8(fr(EATl, c, LT, kb, grp), f);
+                const bfrag bq = scale8(fr(QATl, c, LT, kb, grp), f);
+                acc[m][I][2] = IOB::mma(acc[m][I][2], fr(dATl, s, LT, kb, grp), be);
+                acc[m][I][3] = IOB::mma(acc[m][I][3], fr(dPTl, s, LT, kb, grp), bq);
             }
         }
     }
@@ -848,8 +883,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
                 const int64_t o = (row0 + r * H) * DK + c0;
                 st_vec4(dq + o, oq);
                 st_vec4(dk_out + o, okk);
-#pragma unroll
-                for (int cc = 0; cc < 4; ++cc) gs(db, o + cc, ob[cc]);
+                st_vec4(db + o, ob);
             }
         }
 #pragma unroll
@@ -893,15 +927,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
             const int i = tid + u * kThreads, r = i / CG, c4 = 4 * (i - r * CG);
             if (r < Ln) {
                 const int64_t o = (row0 + r * H) * DK + c4;
-                const f32x4 a4 = widen4(al[u]);
+                const f32x4 a4 = widen4(al[u]), g4 = *reinterpret_cast<const f32x4*>(&dG[r * RS + c4]);
+                f32x4 d4;
                 if (logits) {   // d logit = (dG / alpha) alpha (1 - alpha), alpha = sigmoid(logit)
                     const f32x4 s4 = sigmoid4(a4);
 #pragma unroll
-                    for (int cc = 0; cc < 4; ++cc) gs(dalpha, o + cc, dG[r * RS + c4 + cc] * (1.f - s4[cc]));
+                    for (int cc = 0; cc < 4; ++cc) d4[cc] = g4[cc] * (1.f - s4[cc]);
                 } else {
 #pragma unroll
-                    for (int cc = 0; cc < 4; ++cc) gs(dalpha, o + cc, dG[r * RS + c4 + cc] / a4[cc]);
+                    for (int cc = 0; cc < 4; ++cc) d4[cc] = g4[cc] / a4[cc];
                 }
+                st_vec4(dalpha + o, d4);
             }
         }
     }
