@@ -17,8 +17,8 @@
 //     dW = -dDelta S0^T, du = T^T dDelta (-> dw = du v, dv = du w),
 //     dT = dDelta u^T + dW Eh^T, dEh = T^T dW, dA = mask(-(T^T dT) T^T),
 //     dGamma_L = rowsum(dSL * S0);
-//   dQh, dKtil, dEh, dP, dA and dGamma_L go to a scratch block per chunk
-//   (fp32; dP and dA in bf16, the key side's operand dtype).
+//   dQh, dKtil, dEh, dP, dA (bf16) and dGamma_L (fp32) go to a scratch block
+//   per chunk.
 // k_chunk_grad_key  the key side: the cumulative log decay G, the
 //   contractions of dA and dP with the block-split decay ratios on bf16
 //   matrix cores (row side: sum_s dA[r,s] k_s R[r,s]; column side:
@@ -73,8 +73,8 @@ template <typename T> __device__ inline void gs(T* p, int64_t i, float x) { p[i]
 }  // namespace
 
 // scratch per chunk between the two launches, in 4-byte words: dQh, dKtil,
-// dEh fp32 [64][dk]; dP, dA bf16 [64][64]; dGamma_L fp32 [dk]
-__host__ __device__ inline int64_t gradmf_scratch_floats(int dk) { return 3 * 64 * (int64_t)dk + 4096 + dk; }
+// dEh bf16 [64][dk]; dP, dA bf16 [64][64]; dGamma_L fp32 [dk]
+__host__ __device__ inline int64_t gradmf_scratch_floats(int dk) { return 96 * (int64_t)dk + 4096 + dk; }
 
 // Key-axis items of a chunk on 256 threads: thread t holds channels
 // c4 .. c4+3, c4 = 4 (t mod DK/4), of the NV consecutive rows
@@ -250,12 +250,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
     Tg* dwg = static_cast<Tg*>(a.dw);
     bf* dvg = static_cast<bf*>(a.dv_out);
     float* sc = a.gsc + ci * gradmf_scratch_floats(DK);
-    float* s_dQh = sc;
-    float* s_dKt = sc + 64 * DK;
-    float* s_dEh = sc + 2 * 64 * DK;
-    bf* s_dP = reinterpret_cast<bf*>(sc + 3 * 64 * DK);
+    bf* s_dQh = reinterpret_cast<bf*>(sc);
+    bf* s_dKt = s_dQh + 64 * DK;
+    bf* s_dEh = s_dKt + 64 * DK;
+    bf* s_dP = s_dEh + 64 * DK;
     bf* s_dA = s_dP + 4096;
-    float* s_dGL = sc + 3 * 64 * DK + 4096;
+    float* s_dGL = sc + 96 * DK + 4096;
     const bool logits = (a.flags & kFlagGateLogits) != 0;
 
     // ---- phase 0: operands into LDS ----------------------------------------
@@ -429,17 +429,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
                 }
                 aw = -aw;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    s_dQh[(r + i) * DK + c] = aq[i];
-                    dWl[(r + i) * ldk + c] = (bf)aw[i];
-                }
+                for (int i = 0; i < 4; ++i) dWl[(r + i) * ldk + c] = (bf)aw[i];
                 st_vec4(dWtl + c * LT + r, aw);
+                // rows of 4 columns after a transpose inside each lane quad
+                st_vec4(s_dQh + (r + (l16 & 3)) * DK + (c & ~3), quad_transpose4(aq));
             } else {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < NKV; ++kb) acc = IOB::mma(acc, fr(Dll, 16 * tr + l16, ldv, kb, grp), fb[kb]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) s_dKt[(r + i) * DK + c] = acc[i];
+                st_vec4(s_dKt + (r + (l16 & 3)) * DK + (c & ~3), quad_transpose4(acc));
             }
         }
         if constexpr (FUSE_GL) {
@@ -548,9 +546,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
              },
              [&](int t, f32x4 acc) {
                  const int tr = t / NTK, tn = t - tr * NTK;
-                 const int r = 16 * tr + 4 * grp, c = 16 * tn + l16;
-#pragma unroll
-                 for (int i = 0; i < 4; ++i) s_dEh[(r + i) * DK + c] = acc[i];
+                 const int r = 16 * tr + 4 * grp + (l16 & 3), c = 16 * tn + (l16 & ~3);
+                 st_vec4(s_dEh + r * DK + c, quad_transpose4(acc));
              });
     __syncthreads();
     // ---- tmp = T^T dT -------------------------------------------------------------
@@ -672,12 +669,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
     const Tg* agt = static_cast<const Tg*>(a.alpha);
     const Tg* bgt = static_cast<const Tg*>(a.b);
     const float* sc = a.gsc + ci * gradmf_scratch_floats(DK);
-    const float* s_dQh = sc;
-    const float* s_dKt = sc + 64 * DK;
-    const float* s_dEh = sc + 2 * 64 * DK;
-    const bf* s_dP = reinterpret_cast<const bf*>(sc + 3 * 64 * DK);
+    const bf* s_dQh = reinterpret_cast<const bf*>(sc);
+    const bf* s_dKt = s_dQh + 64 * DK;
+    const bf* s_dEh = s_dKt + 64 * DK;
+    const bf* s_dP = s_dEh + 64 * DK;
     const bf* s_dA = s_dP + 4096;
-    const float* s_dGL = sc + 3 * 64 * DK + 4096;
+    const float* s_dGL = sc + 96 * DK + 4096;
     const bool logits = (a.flags & kFlagGateLogits) != 0, l2 = (a.flags & kFlagQkL2norm) != 0;
     const float bscale = (a.flags & kFlagNegEigval) ? 2.f : 1.f;
 
@@ -826,14 +823,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
         const int c0 = 4 * (tid % CG), r0 = (tid / CG) * R;
         bf16x4 qr[R], kr[R];
         gvec br[R];
-        f32x4 dQh[R], dEh[R], dKt[R];
+        bf16x4 xqh[R], xeh[R], xkt[R];                             // raw until used
 #pragma unroll
         for (int rr = 0; rr < R; ++rr) {
             const int r = r0 + rr;
             const int64_t o = (row0 + (r < Ln ? r : Ln - 1) * H) * DK + c0;
-            dQh[rr] = *reinterpret_cast<const f32x4*>(s_dQh + r * DK + c0);
-            dEh[rr] = *reinterpret_cast<const f32x4*>(s_dEh + r * DK + c0);
-            dKt[rr] = *reinterpret_cast<const f32x4*>(s_dKt + r * DK + c0);
+            xqh[rr] = *reinterpret_cast<const bf16x4*>(s_dQh + r * DK + c0);
+            xeh[rr] = *reinterpret_cast<const bf16x4*>(s_dEh + r * DK + c0);
+            xkt[rr] = *reinterpret_cast<const bf16x4*>(s_dKt + r * DK + c0);
             qr[rr] = *reinterpret_cast<const bf16x4*>(qg + o);
             kr[rr] = *reinterpret_cast<const bf16x4*>(kg + o);
             br[rr] = *reinterpret_cast<const gvec*>(bgt + o);
@@ -843,6 +840,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
         for (int rr = 0; rr < R; ++rr) {
             const int r = r0 + rr;
             const bool ok = r < Ln;
+            const f32x4 dQh = IOB::unpack4(xqh[rr]), dEh = IOB::unpack4(xeh[rr]), dKt = IOB::unpack4(xkt[rr]);
             f32x4 q4 = IOB::unpack4(qr[rr]), k4 = IOB::unpack4(kr[rr]);
             const f32x4 braw = widen4(br[rr]);
             const f32x4 sb = logits ? sigmoid4(braw) : braw, b4 = logits ? sb * bscale : braw;
@@ -862,13 +860,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
                 const int c = c0 + cc;
                 const float g = G[r * DK + c], gam = __expf(g), kt = __expf(G[63 * DK + c] - g);
                 const float qv = ok ? q4[cc] : 0.f, kv = ok ? k4[cc] : 0.f, bv = ok ? b4[cc] : 0.f, ev = bv * kv;
-                const float de = gam * dEh[rr][cc] + deA[cc];
-                oq[cc] = gam * dQh[rr][cc] + dqP[cc];
-                okk[cc] = kt * dKt[rr][cc] + de * bv + kak[cc];
+                const float de = gam * dEh[cc] + deA[cc];
+                oq[cc] = gam * dQh[cc] + dqP[cc];
+                okk[cc] = kt * dKt[cc] + de * bv + kak[cc];
                 ob[cc] = de * kv;
-                dg[cc] = dQh[rr][cc] * gam * qv + dEh[rr][cc] * gam * ev - dKt[rr][cc] * kv * kt + ev * deA[cc] +
+                dg[cc] = dQh[cc] * gam * qv + dEh[cc] * gam * ev - dKt[cc] * kv * kt + ev * deA[cc] +
                          qv * dqP[cc] - kv * kak[cc];
-                ex[cc] += dKt[rr][cc] * kv * kt;
+                ex[cc] += dKt[cc] * kv * kt;
             }
             *reinterpret_cast<f32x4*>(&dG[r * RS + c0]) = dg;
             if (l2) {   // through the norms: dx = (dxh - xh (xh . dxh)) / |x|
