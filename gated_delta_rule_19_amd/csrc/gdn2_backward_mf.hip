@@ -184,6 +184,22 @@ __device__ __attribute__((always_inline)) inline void tiles(int wave, int NT, FF
 // loads it once, body(p, b) runs the panel's row tiles with A from LDS.  The
 // next panel's B is requested before the current panel's products.
 template <int NKB, typename FF, typename FB>
+__device__ __attribute__((always_inline)) inline void panels_from(int wave, int NP, const bfrag (&first)[NKB], FF fetch,
+                                                                  FB body)
+{
+    // the same, with panel p = wave already requested (into `first`)
+    bfrag cb[NKB], nb[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) nb[kb] = first[kb];
+    for (int p = wave; p < NP; p += 4) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) cb[kb] = nb[kb];
+        if (p + 4 < NP) fetch(p + 4, nb);
+        body(p, cb);
+    }
+}
+
+template <int NKB, typename FF, typename FB>
 __device__ __attribute__((always_inline)) inline void panels(int wave, int NP, FF fetch, FB body)
 {
     bfrag cb[NKB], nb[NKB];
@@ -286,6 +302,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
         const int g = tid + m * kThreads, r = g / (DV / 8), j0 = (g - r * (DV / 8)) * 8;
         oq[m] = *reinterpret_cast<const bfrag*>(dO + (row0 + (r < Ln ? r : Ln - 1) * H) * DV + j0);
     }
+    // the first products' operands (W for every row tile, this wave's first
+    // panels of S0^T and dSL^T) are requested now, behind the LDS copy below
+    bfrag wa[4][NKK], pan0[2 * NKK];
+#pragma unroll
+    for (int tr = 0; tr < 4; ++tr)
+#pragma unroll
+        for (int kb = 0; kb < NKK; ++kb) wa[tr][kb] = fr(Wg, 16 * tr + l16, DK, kb, grp);
+    auto fetch_pan = [&](int tn, bfrag (&fb)[2 * NKK]) {
+        const int tc = tn < NTV ? tn : 0;                           // (a wave without panels loads panel 0)
+#pragma unroll
+        for (int kb = 0; kb < NKK; ++kb) {
+            fb[kb] = fr(S0t, 16 * tc + l16, DK, kb, grp);
+            fb[NKK + kb] = fr(dSLt, 16 * tc + l16, DK, kb, grp);
+        }
+    };
+    fetch_pan(wave, pan0);
 #pragma unroll
     for (int m = 0; m < NTP; ++m) {                                 // T, T^T; P^T
         const int g = tid + m * kThreads, r = g >> 3, c0 = (g & 7) * 8;
@@ -343,57 +375,32 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
     }
     __syncthreads();
 
-    // ---- Delta = U - W S0 (in place over U): W for all row tiles in registers,
-    // S0^T one 16-column panel at a time ------------------------------------------
-    {
-        bfrag wa[4][NKK];
+    // ---- Delta = U - W S0 (in place over U) and dDelta = P^T dO + Ktil dSL, one
+    // 16-column panel of S0^T and dSL^T at a time (W for all row tiles in registers)
+    panels_from<2 * NKK>(wave, NTV, pan0, fetch_pan, [&](int tn, bfrag (&fb)[2 * NKK]) {
+        const int j = 16 * tn + l16;
+        const bfrag o0 = fr(dOtl, j, LT, 0, grp), o1 = fr(dOtl, j, LT, 1, grp);
 #pragma unroll
-        for (int tr = 0; tr < 4; ++tr)
+        for (int tr = 0; tr < 4; ++tr) {
+            const int r = 16 * tr + 4 * grp;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb < NKK; ++kb) wa[tr][kb] = fr(Wg, 16 * tr + l16, DK, kb, grp);
-        panels<NKK>(wave, NTV,
-                    [&](int tn, bfrag (&fb)[NKK]) {
+            for (int kb = 0; kb < NKK; ++kb) acc = IOB::mma(acc, wa[tr][kb], fb[kb]);
 #pragma unroll
-                        for (int kb = 0; kb < NKK; ++kb) fb[kb] = fr(S0t, 16 * tn + l16, DK, kb, grp);
-                    },
-                    [&](int tn, bfrag (&fb)[NKK]) {
-                        const int j = 16 * tn + l16;
+            for (int i = 0; i < 4; ++i) {
+                bf* d = &Dll[(r + i) * ldv + j];
+                *d = (bf)((float)*d - acc[i]);
+            }
+            f32x4 acd = {0.f, 0.f, 0.f, 0.f};
+            acd = IOB::mma(acd, fr(Ptl, 16 * tr + l16, LT, 0, grp), o0);
+            acd = IOB::mma(acd, fr(Ptl, 16 * tr + l16, LT, 1, grp), o1);
 #pragma unroll
-                        for (int tr = 0; tr < 4; ++tr) {
-                            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int kb = 0; kb < NKK; ++kb) acd = IOB::mma(acd, fr(Ktl, 16 * tr + l16, ldk, kb, grp), fb[NKK + kb]);
 #pragma unroll
-                            for (int kb = 0; kb < NKK; ++kb) acc = IOB::mma(acc, wa[tr][kb], fb[kb]);
-                            const int r = 16 * tr + 4 * grp;
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                bf* d = &Dll[(r + i) * ldv + j];
-                                *d = (bf)((float)*d - acc[i]);
-                            }
-                        }
-                    });
-    }
-    // ---- dDelta = P^T dO + Ktil dSL ----------------------------------------------
-    panels<NKK>(wave, NTV,
-                [&](int tn, bfrag (&fb)[NKK]) {
-#pragma unroll
-                    for (int kb = 0; kb < NKK; ++kb) fb[kb] = fr(dSLt, 16 * tn + l16, DK, kb, grp);
-                },
-                [&](int tn, bfrag (&fb)[NKK]) {
-                    const int j = 16 * tn + l16;
-                    const bfrag o0 = fr(dOtl, j, LT, 0, grp), o1 = fr(dOtl, j, LT, 1, grp);
-#pragma unroll
-                    for (int tr = 0; tr < 4; ++tr) {
-                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                        acc = IOB::mma(acc, fr(Ptl, 16 * tr + l16, LT, 0, grp), o0);
-                        acc = IOB::mma(acc, fr(Ptl, 16 * tr + l16, LT, 1, grp), o1);
-#pragma unroll
-                        for (int kb = 0; kb < NKK; ++kb) acc = IOB::mma(acc, fr(Ktl, 16 * tr + l16, ldk, kb, grp), fb[kb]);
-                        const int r = 16 * tr + 4 * grp;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) dDl[(r + i) * ldv + j] = (bf)acc[i];
-                        st_vec4(dDtl + j * LT + r, acc);
-                    }
-                });
+            for (int i = 0; i < 4; ++i) dDl[(r + i) * ldv + j] = (bf)acd[i];
+            st_vec4(dDtl + j * LT + r, acd);
+        }
+    });
     __syncthreads();
     // ---- dQh = dO S0^T and dW = -dDelta S0^T (one pass over S0), dKtil = Delta dSL^T
     // Every B panel of this wave (bf16 rows of S0 and dSL) is requested at
