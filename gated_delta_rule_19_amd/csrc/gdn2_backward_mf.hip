@@ -76,47 +76,47 @@ template <typename T> __device__ inline void gs(T* p, int64_t i, float x) { p[i]
 // dEh bf16 [64][dk]; dP, dA bf16 [64][64]; dGamma_L fp32 [dk]
 __host__ __device__ inline int64_t gradmf_scratch_floats(int dk) { return 96 * (int64_t)dk + 4096 + dk; }
 
-// Key-axis items of a chunk on 256 threads: thread t holds channels
-// c4 .. c4+3, c4 = 4 (t mod DK/4), of the NV consecutive rows
+// Key-axis items of a chunk on NTH threads: thread t holds channels
+// c4 .. c4+3, c4 = 4 (t mod DK/4), of the NV = 16 DK / NTH consecutive rows
 // (t div DK/4) NV + u, u < NV (the DK/4 lanes of a row are consecutive).
-template <int DK>
+template <int DK, int NTH>
 __device__ __forceinline__ void key_item(int u, int& r, int& c4)
 {
-    constexpr int CG = DK / 4, NV = 64 * CG / kThreads;
+    constexpr int CG = DK / 4, NV = 64 * CG / NTH;
     const int tid = threadIdx.x;
     r = (tid / CG) * NV + u;
     c4 = 4 * (tid % CG);
 }
 
 // G[r][c] = sum of log alpha over tokens 0..r of the chunk (alpha = 1 past its
-// end), for 256 threads: logs in parallel (every load issued before the first
-// use), then a scan of 256/DK segments per channel with the segment totals
-// carried through `tot`.  cld_load issues the loads, cld_scan does the rest
-// (alpha given as logits: alpha = sigmoid(logit)).
-template <int DK, typename Tg>
-__device__ __attribute__((always_inline)) inline void cld_load(typename GateVec<Tg>::type (&x)[64 * DK / 4 / kThreads],
+// end), for NTH threads: logs in parallel (every load issued before the first
+// use), then a scan of NTH/DK segments per channel with the segment totals
+// carried through `tot` [NTH].  cld_load issues the loads, cld_scan does the
+// rest (alpha given as logits: alpha = sigmoid(logit)).
+template <int DK, int NTH, typename Tg>
+__device__ __attribute__((always_inline)) inline void cld_load(typename GateVec<Tg>::type (&x)[64 * DK / 4 / NTH],
                                                                const Tg* alpha, int64_t row0, int64_t H, int Ln)
 {
-    constexpr int NV = 64 * DK / 4 / kThreads;
+    constexpr int NV = 64 * DK / 4 / NTH;
 #pragma unroll
     for (int u = 0; u < NV; ++u) {       // raw and unconditional (rows past the end clamped)
         int r, c4;
-        key_item<DK>(u, r, c4);
+        key_item<DK, NTH>(u, r, c4);
         x[u] = *reinterpret_cast<const typename GateVec<Tg>::type*>(alpha + (row0 + (r < Ln ? r : Ln - 1) * H) * DK + c4);
     }
 }
 
-template <int DK, typename Tg>
+template <int DK, int NTH, typename Tg>
 __device__ __attribute__((always_inline)) inline void cld_scan(float* G, float* tot,
-                                                               const typename GateVec<Tg>::type (&x)[64 * DK / 4 / kThreads],
+                                                               const typename GateVec<Tg>::type (&x)[64 * DK / 4 / NTH],
                                                                int Ln, bool logits)
 {
-    constexpr int NV = 64 * DK / 4 / kThreads;
+    constexpr int NV = 64 * DK / 4 / NTH;
     const int tid = threadIdx.x;
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
         int r, c4;
-        key_item<DK>(u, r, c4);
+        key_item<DK, NTH>(u, r, c4);
         const f32x4 a = logits ? sigmoid4(widen4(x[u])) : widen4(x[u]);
         f32x4 l;
 #pragma unroll
@@ -124,7 +124,7 @@ __device__ __attribute__((always_inline)) inline void cld_scan(float* G, float* 
         *reinterpret_cast<f32x4*>(&G[r * DK + c4]) = l;
     }
     __syncthreads();
-    constexpr int nseg = kThreads / DK, sl = 64 / nseg;
+    constexpr int nseg = NTH / DK, sl = 64 / nseg;
     const int c = tid % DK, g = tid / DK;
     float run = 0.f;
 #pragma unroll 8
@@ -625,6 +625,8 @@ __device__ __forceinline__ bfrag scale8(bfrag x, float f)
     return r;
 }
 
+constexpr int kGkThreads = 512;                    // 8 waves per key-side workgroup
+
 template <int DK>
 struct GkLds {
     static constexpr int RS = DK + 4;              // row stride of the fp32 results / dG
@@ -637,17 +639,18 @@ struct GkLds {
 };
 
 template <int DK, typename Tg>
-__global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
+__global__ __launch_bounds__(kGkThreads, 1) void k_chunk_grad_key(GradKArgs a)
 {
     using L = GkLds<DK>;
-    constexpr int CG = DK / 4, R = DK / 16, NCT = DK / 16, CPW = (NCT + 3) / 4;
+    constexpr int NTH = kGkThreads, NW = NTH / 64;
+    constexpr int CG = DK / 4, R = 64 * CG / NTH, NCT = DK / 16, CPW = (NCT + NW - 1) / NW;
     constexpr int RS = L::RS;
-    constexpr int NV = 64 * DK / 4 / kThreads;
+    constexpr int NV = 64 * DK / 4 / NTH;
     typedef typename GateVec<Tg>::type gvec;
     __shared__ __attribute__((aligned(16))) float G[64 * DK];
     __shared__ __attribute__((aligned(16))) char big[L::BIG];
-    __shared__ float ext[(kThreads / CG) * DK];                // per row group: sum of dKtil * Ktil
-    __shared__ float tot[kThreads];
+    __shared__ float ext[(NTH / CG) * DK];                // per row group: sum of dKtil * Ktil
+    __shared__ float tot[NTH];
     bf* dAl = reinterpret_cast<bf*>(big + L::IN_A);
     bf* dPl = dAl + 64 * LT;
     bf* dATl = reinterpret_cast<bf*>(big + L::IN_AT);
@@ -699,11 +702,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
         for (int e = 0; e < 8; ++e) xb[e] = *reinterpret_cast<const bfrag*>(bsrc + (8 * bR + e) * 64 + 8 * bS);
         gvec ax[NV], bx[NV];
         bf16x4 kx[NV], qx[NV];
-        cld_load<DK>(ax, agt, row0, H, Ln);
+        cld_load<DK, NTH>(ax, agt, row0, H, Ln);
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
             int r, c4;
-            key_item<DK>(u, r, c4);
+            key_item<DK, NTH>(u, r, c4);
             const int64_t o = (row0 + (r < Ln ? r : Ln - 1) * H) * DK + c4;
             kx[u] = *reinterpret_cast<const bf16x4*>(kg + o);
             qx[u] = *reinterpret_cast<const bf16x4*>(qg + o);
@@ -722,17 +725,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
                 *reinterpret_cast<bfrag*>(dstT + (8 * bS + f) * LT + 8 * bR) = y;
             }
         }
-        cld_scan<DK, Tg>(G, tot, ax, Ln, logits);
+        cld_scan<DK, NTH, Tg>(G, tot, ax, Ln, logits);
         // KY, EA, QA transposed: a thread's NV consecutive rows of one channel
         // are one vector store
         typedef bf rowv __attribute__((ext_vector_type(NV)));
         rowv ty[4], te[4], tq[4];
         int rb = 0, cb = 0;
-        key_item<DK>(0, rb, cb);
+        key_item<DK, NTH>(0, rb, cb);
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
             int r, c4;
-            key_item<DK>(u, r, c4);
+            key_item<DK, NTH>(u, r, c4);
             const f32x4 g4 = *reinterpret_cast<const f32x4*>(&G[r * DK + c4]);
             const f32x4 gj = *reinterpret_cast<const f32x4*>(&G[(r & ~15) * DK + c4]);
             const bool ok = r < Ln;
@@ -766,11 +769,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
     }
     __syncthreads();
 
-    // ---- products on the matrix cores: column tiles ct = wave + 4 m ----------
+    // ---- products on the matrix cores: column tiles ct = wave + NW m ---------
     f32x4 acc[CPW][4][4];                                      // [tile][row block][rowA rowP colA colP]
 #pragma unroll
     for (int m = 0; m < CPW; ++m) {
-        const int ct = wave + 4 * m;
+        const int ct = wave + NW * m;
         const int c = 16 * (ct < NCT ? ct : 0) + l16;
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
@@ -803,7 +806,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
     __syncthreads();                                           // inputs read; results overwrite them
 #pragma unroll
     for (int m = 0; m < CPW; ++m) {
-        const int ct = wave + 4 * m;
+        const int ct = wave + NW * m;
         if (ct >= NCT) continue;
         const int c = 16 * ct + l16;
 #pragma unroll
@@ -899,12 +902,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
     // the uses of Gamma_L (the state decay over the chunk and Ktil)
     if (tid < DK) {
         float x = s_dGL[tid] * __expf(G[63 * DK + tid]);
-        for (int g = 0; g < kThreads / CG; ++g) x += ext[g * DK + tid];
+        for (int g = 0; g < NTH / CG; ++g) x += ext[g * DK + tid];
         dG[63 * RS + tid] += x;
     }
     __syncthreads();
     {
-        const int nseg = kThreads / DK, sl = 64 / nseg;
+        const int nseg = NTH / DK, sl = 64 / nseg;
         const int c = tid % DK, g = tid / DK;
         float run = 0.f;
         for (int r = (g + 1) * sl - 1; r >= g * sl; --r) {
@@ -924,12 +927,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_key(GradKArgs a)
         gvec al[NV];
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
-            const int i = tid + u * kThreads, r = i / CG, c4 = 4 * (i - r * CG);
+            const int i = tid + u * NTH, r = i / CG, c4 = 4 * (i - r * CG);
             al[u] = *reinterpret_cast<const gvec*>(agt + (row0 + (r < Ln ? r : Ln - 1) * H) * DK + c4);
         }
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
-            const int i = tid + u * kThreads, r = i / CG, c4 = 4 * (i - r * CG);
+            const int i = tid + u * NTH, r = i / CG, c4 = 4 * (i - r * CG);
             if (r < Ln) {
                 const int64_t o = (row0 + r * H) * DK + c4;
                 const f32x4 a4 = widen4(al[u]), g4 = *reinterpret_cast<const f32x4*>(&dG[r * RS + c4]);
@@ -1280,9 +1283,9 @@ static hipError_t grad_mf_dk(const GradVArgs& v, const GradKArgs& k, bool gbf16,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (gbf16)
-        hipLaunchKernelGGL((k_chunk_grad_key<DK, __bf16>), grid, dim3(kThreads), 0, s, k);
+        hipLaunchKernelGGL((k_chunk_grad_key<DK, __bf16>), grid, dim3(kGkThreads), 0, s, k);
     else
-        hipLaunchKernelGGL((k_chunk_grad_key<DK, float>), grid, dim3(kThreads), 0, s, k);
+        hipLaunchKernelGGL((k_chunk_grad_key<DK, float>), grid, dim3(kGkThreads), 0, s, k);
     return hipGetLastError();
 }
 
