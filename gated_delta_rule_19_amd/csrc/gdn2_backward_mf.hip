@@ -155,7 +155,9 @@ struct GvLds {
     static constexpr int BYTES = R7 + 64 * LD * 2;
 };
 
-// Tiles t = wave, wave + 4, ... < NT of one product: fetch(t, a, b) loads the
+constexpr int kGvThreads = 512, kGvWaves = 8;      // value-side workgroup: 8 waves
+
+// Tiles t = wave, wave + 8, ... < NT of one product: fetch(t, a, b) loads the
 // NKB K-blocks of a tile's A and B fragments, epi(t, acc) consumes its
 // result.  The next tile's fragments are requested before the current
 // tile's products, so global-memory operands arrive while the matrix cores work.
@@ -165,13 +167,13 @@ __device__ __attribute__((always_inline)) inline void tiles(int wave, int NT, FF
     bfrag ca[NKB], cb[NKB], na[NKB], nb[NKB];
     int t = wave;
     if (t < NT) fetch(t, na, nb);
-    for (; t < NT; t += 4) {
+    for (; t < NT; t += kGvWaves) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             ca[kb] = na[kb];
             cb[kb] = nb[kb];
         }
-        if (t + 4 < NT) fetch(t + 4, na, nb);
+        if (t + kGvWaves < NT) fetch(t + kGvWaves, na, nb);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) acc = IOB::mma(acc, ca[kb], cb[kb]);
@@ -179,7 +181,7 @@ __device__ __attribute__((always_inline)) inline void tiles(int wave, int NT, FF
     }
 }
 
-// Column panels p = wave, wave + 4, ... < NP of products whose B operand
+// Column panels p = wave, wave + 8, ... < NP of products whose B operand
 // (NKB K-blocks of one 16-column panel) comes from global memory: fetch(p, b)
 // loads it once, body(p, b) runs the panel's row tiles with A from LDS.  The
 // next panel's B is requested before the current panel's products.
@@ -191,32 +193,19 @@ __device__ __attribute__((always_inline)) inline void panels_from(int wave, int 
     bfrag cb[NKB], nb[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) nb[kb] = first[kb];
-    for (int p = wave; p < NP; p += 4) {
+    for (int p = wave; p < NP; p += kGvWaves) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) cb[kb] = nb[kb];
-        if (p + 4 < NP) fetch(p + 4, nb);
-        body(p, cb);
-    }
-}
-
-template <int NKB, typename FF, typename FB>
-__device__ __attribute__((always_inline)) inline void panels(int wave, int NP, FF fetch, FB body)
-{
-    bfrag cb[NKB], nb[NKB];
-    int p = wave;
-    if (p < NP) fetch(p, nb);
-    for (; p < NP; p += 4) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) cb[kb] = nb[kb];
-        if (p + 4 < NP) fetch(p + 4, nb);
+        if (p + kGvWaves < NP) fetch(p + kGvWaves, nb);
         body(p, cb);
     }
 }
 
 template <int DK, int DV, typename Tg>
-__global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
+__global__ __launch_bounds__(kGvThreads, 1) void k_chunk_grad_val(GradVArgs a)
 {
     using L = GvLds;
+    constexpr int NTH = kGvThreads, NW = kGvWaves;
     static_assert(L::BYTES <= 160 * 1024, "LDS budget");
     constexpr int NKK = DK / 32, NKV = DV / 32, NTK = DK / 16, NTV = DV / 16;
     constexpr int ldv = DV + 8, ldk = DK + 8;
@@ -276,30 +265,34 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
 
     // ---- phase 0: operands into LDS ----------------------------------------
     // Every global load of the phase is issued before the first LDS write (one
-    // round of memory latency instead of one per operand).
-    constexpr int NTP = 64 * 8 / kThreads, NKT = DK * 8 / kThreads, NUT = DV * 8 / kThreads;
-    constexpr int NDO = 64 * (DV / 8) / kThreads;
+    // round of memory latency instead of one per operand).  Granule g = tid +
+    // NTH m of each operand; where an operand has fewer granules than threads
+    // the extra ones load a valid granule again and store nothing.
+    constexpr int GK = DK * 8, GU = DV * 8, GO = 8 * DV;           // granules of Ktil / Eh, U^T, dO
+    constexpr int NTP = 64 * 8 / NTH, NKT = (GK + NTH - 1) / NTH, NUT = (GU + NTH - 1) / NTH;
+    constexpr int NDO = (GO + NTH - 1) / NTH;
+    static_assert(64 * 8 % NTH == 0, "T and P granules");
     bfrag tq[NTP], pq[NTP], kq[NKT], eq[NKT], uq[NUT], oq[NDO];
 #pragma unroll
     for (int m = 0; m < NTP; ++m) {                                 // T, P
-        const int g = tid + m * kThreads, r = g >> 3, c0 = (g & 7) * 8;
+        const int g = tid + m * NTH, r = g >> 3, c0 = (g & 7) * 8;
         tq[m] = *reinterpret_cast<const bfrag*>(Tg_ + r * 64 + c0);
         pq[m] = *reinterpret_cast<const bfrag*>(Ptg + r * 64 + c0);
     }
 #pragma unroll
     for (int m = 0; m < NKT; ++m) {                                 // Ktil [r][c]
-        const int g = tid + m * kThreads, r = g / (DK / 8), c0 = (g - r * (DK / 8)) * 8;
+        const int g = (tid + m * NTH) % GK, r = g / (DK / 8), c0 = (g - r * (DK / 8)) * 8;
         kq[m] = *reinterpret_cast<const bfrag*>(Kng + r * DK + c0);
         eq[m] = *reinterpret_cast<const bfrag*>(Ehg + r * DK + c0);
     }
 #pragma unroll
     for (int m = 0; m < NUT; ++m) {                                 // U^T [j][r]
-        const int g = tid + m * kThreads, j = g >> 3, r0 = (g & 7) * 8;
+        const int g = (tid + m * NTH) % GU, j = g >> 3, r0 = (g & 7) * 8;
         uq[m] = *reinterpret_cast<const bfrag*>(Utg + j * 64 + r0);
     }
 #pragma unroll
     for (int m = 0; m < NDO; ++m) {                                 // dO (zero past the end)
-        const int g = tid + m * kThreads, r = g / (DV / 8), j0 = (g - r * (DV / 8)) * 8;
+        const int g = (tid + m * NTH) % GO, r = g / (DV / 8), j0 = (g - r * (DV / 8)) * 8;
         oq[m] = *reinterpret_cast<const bfrag*>(dO + (row0 + (r < Ln ? r : Ln - 1) * H) * DV + j0);
     }
     // the first products' operands (W for every row tile, this wave's first
@@ -320,7 +313,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
     fetch_pan(wave, pan0);
 #pragma unroll
     for (int m = 0; m < NTP; ++m) {                                 // T, T^T; P^T
-        const int g = tid + m * kThreads, r = g >> 3, c0 = (g & 7) * 8;
+        const int g = tid + m * NTH, r = g >> 3, c0 = (g & 7) * 8;
         *reinterpret_cast<bfrag*>(Tl + r * LT + c0) = tq[m];
         *reinterpret_cast<bfrag*>(Ptl + r * LT + c0) = pq[m];
 #pragma unroll
@@ -328,35 +321,43 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
     }
 #pragma unroll
     for (int m = 0; m < NKT; ++m) {                                 // Ktil, Eh
-        const int g = tid + m * kThreads, r = g / (DK / 8), c0 = (g - r * (DK / 8)) * 8;
-        *reinterpret_cast<bfrag*>(Ktl + r * ldk + c0) = kq[m];
-        *reinterpret_cast<bfrag*>(Ehl + r * ldk + c0) = eq[m];
+        if (GK % NTH == 0 || tid + m * NTH < GK) {
+            const int g = tid + m * NTH, r = g / (DK / 8), c0 = (g - r * (DK / 8)) * 8;
+            *reinterpret_cast<bfrag*>(Ktl + r * ldk + c0) = kq[m];
+            *reinterpret_cast<bfrag*>(Ehl + r * ldk + c0) = eq[m];
+        }
     }
 #pragma unroll
     for (int m = 0; m < NUT; ++m) {                                 // U [r][j] from U^T [j][r]
-        const int g = tid + m * kThreads, j = g >> 3, r0 = (g & 7) * 8;
+        if (GU % NTH == 0 || tid + m * NTH < GU) {
+            const int g = tid + m * NTH, j = g >> 3, r0 = (g & 7) * 8;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) Dll[(r0 + e) * ldv + j] = uq[m][e];
+            for (int e = 0; e < 8; ++e) Dll[(r0 + e) * ldv + j] = uq[m][e];
+        }
     }
 #pragma unroll
     for (int m = 0; m < NDO; ++m) {                                 // dO, dO^T (zero past the end)
-        const int g = tid + m * kThreads, r = g / (DV / 8), j0 = (g - r * (DV / 8)) * 8;
-        if (r >= Ln) {
+        if (GO % NTH == 0 || tid + m * NTH < GO) {
+            const int g = tid + m * NTH, r = g / (DV / 8), j0 = (g - r * (DV / 8)) * 8;
+            if (r >= Ln) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) oq[m][e] = (bf)0.f;
+                for (int e = 0; e < 8; ++e) oq[m][e] = (bf)0.f;
+            }
+            *reinterpret_cast<bfrag*>(dOl + r * ldv + j0) = oq[m];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dOtl[(j0 + e) * LT + r] = oq[m][e];
         }
-        *reinterpret_cast<bfrag*>(dOl + r * ldv + j0) = oq[m];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dOtl[(j0 + e) * LT + r] = oq[m][e];
     }
-    // dGamma_L = rowsum(dSL * S0), fp32 sums of the bf16 checkpoints (dk = 32:
-    // with larger dk it comes from the panels below), before the first global
+    // dGamma_L = rowsum(dSL * S0), fp32 sums of the bf16 checkpoints (dk < 128:
+    // with dk = 128 it comes from the panels below), before the first global
     // store (a load behind a store would wait for it); stored at the end.  TPR
-    // threads per row, each with DV / TPR columns, all loads in flight at once.
-    constexpr int TPR = kThreads / DK, NCOL = DV / TPR;
+    // threads per row, each with DV / TPR columns, all loads in flight at once
+    // (threads past DK * TPR repeat a row and store nothing).
+    constexpr bool FUSE_GL = NTK % NW == 0;
+    constexpr int TPR0 = NTH / DK < DV / 4 ? NTH / DK : DV / 4, TPR = TPR0 < 1 ? 1 : TPR0, NCOL = DV / TPR;
     float dgl = 0.f;
-    if constexpr (NTK % 4 != 0) {
-        const int c = tid / TPR, sub = tid % TPR;
+    if constexpr (!FUSE_GL) {
+        const int c = (tid / TPR) % DK, sub = tid % TPR;
         bf16x4 pa[NCOL / 4], pb[NCOL / 4];
 #pragma unroll
         for (int m = 0; m < NCOL / 4; ++m) {
@@ -407,12 +408,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
     // once, before the kernel's first global store; with dk >= 64 one wave
     // holds both the S0 and the dSL panel of a row block, and dGamma_L =
     // rowsum(dSL * S0) comes from the same fragments.
-    constexpr int NPW = NTK / 2;                                    // panels per wave
-    constexpr bool FUSE_GL = NTK % 4 == 0;
+    constexpr int NPW = (2 * NTK + NW - 1) / NW;                    // panels per wave
     bfrag rb[NPW][NKV];
 #pragma unroll
     for (int m = 0; m < NPW; ++m) {
-        const int p = wave + 4 * m;
+        const int p = (wave + NW * m) % (2 * NTK);                 // (a wave without panels loads one again)
         const bf* B = p < NTK ? S0 : dSL;
         const int tn = p < NTK ? p : p - NTK;
 #pragma unroll
@@ -421,7 +421,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
     float glp[FUSE_GL ? NPW / 2 : 1];
 #pragma unroll
     for (int m = 0; m < NPW; ++m) {
-        const int p = wave + 4 * m;
+        const int p = wave + NW * m;
+        if (p >= 2 * NTK) break;
         const int tn = p < NTK ? p : p - NTK, c = 16 * tn + l16;
         const bfrag (&fb)[NKV] = rb[m];
 #pragma unroll
@@ -482,13 +483,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
     // the first product and kept in their memory dtypes until used (a
     // conversion right after the load would wait for it); rows past the end
     // are clamped on load, never stored, and give u = 0.
-    constexpr int NTU = NTV;                                        // du tiles per wave
+    constexpr int NTU = 4 * NTV / NW;                               // du tiles per wave
+    static_assert(4 * NTV % NW == 0, "du tiles");
     typedef typename GateVec<Tg>::type gvec;
     gvec wx[NTU];
     bf16x4 vx[NTU], ux[NTU];
 #pragma unroll
     for (int m = 0; m < NTU; ++m) {
-        const int t = wave + 4 * m, tr = t / NTV, tn = t - tr * NTV;
+        const int t = wave + NW * m, tr = t / NTV, tn = t - tr * NTV;
         const int r = 16 * tr + 4 * grp + (l16 & 3), j = 16 * tn + (l16 & ~3);
         const int64_t o = (row0 + (r < Ln ? r : Ln - 1) * H) * DV + j;
         wx[m] = *reinterpret_cast<const gvec*>(wgt + o);
@@ -496,7 +498,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
     }
 #pragma unroll
     for (int m = 0; m < NTU; ++m) {
-        const int t = wave + 4 * m, tr = t / NTV, tn = t - tr * NTV;
+        const int t = wave + NW * m, tr = t / NTV, tn = t - tr * NTV;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -520,7 +522,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
     __syncthreads();
 #pragma unroll
     for (int m = 0; m < NTU; ++m) {                                 // u over dO (no longer read)
-        const int t = wave + 4 * m, tr = t / NTV, tn = t - tr * NTV;
+        const int t = wave + NW * m, tr = t / NTV, tn = t - tr * NTV;
         *reinterpret_cast<bf16x4*>(ul + (16 * tr + 4 * grp + (l16 & 3)) * ldv + 16 * tn + (l16 & ~3)) = ux[m];
     }
     __syncthreads();
@@ -589,10 +591,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_grad_val(GradVArgs a)
     if constexpr (FUSE_GL) {
         if (grp == 0) {
 #pragma unroll
-            for (int i = 0; i < NPW / 2; ++i) s_dGL[16 * (wave + 4 * i) + l16] = glp[i];
+            for (int i = 0; i < NPW / 2; ++i) s_dGL[16 * (wave + NW * i) + l16] = glp[i];
         }
     } else {
-        if (tid % TPR == 0) s_dGL[tid / TPR] = dgl;
+        if (tid % TPR == 0 && tid < DK * TPR) s_dGL[tid / TPR] = dgl;
     }
 }
 
@@ -1265,9 +1267,9 @@ template <int DK, int DV>
 static void val_launch(const GradVArgs& v, bool gbf16, dim3 grid, hipStream_t s)
 {
     if (gbf16)
-        hipLaunchKernelGGL((k_chunk_grad_val<DK, DV, __bf16>), grid, dim3(kThreads), 0, s, v);
+        hipLaunchKernelGGL((k_chunk_grad_val<DK, DV, __bf16>), grid, dim3(kGvThreads), 0, s, v);
     else
-        hipLaunchKernelGGL((k_chunk_grad_val<DK, DV, float>), grid, dim3(kThreads), 0, s, v);
+        hipLaunchKernelGGL((k_chunk_grad_val<DK, DV, float>), grid, dim3(kGvThreads), 0, s, v);
 }
 
 template <int DK>
