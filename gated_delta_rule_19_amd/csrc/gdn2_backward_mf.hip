@@ -1,8 +1,9 @@
 // Per-chunk gradients of the chunked GDN-2 forward on the matrix cores
-// (bf16 I/O, dk in {32, 64, 128}, dv a multiple of 32 up to 128).
+// (bf16 I/O, dk and dv in {32, 64, 128}), and the reverse state pass of the
+// same path (k_chunk_state_bwd_mf, described where it is defined).
 //
 // Same gradient as k_chunk_grad (the formulas are in gdn2_backward.hip's
-// header), split in two launches of one workgroup per chunk:
+// header), split in two launches of one workgroup (8 waves) per chunk:
 //
 // k_chunk_grad_val  the value-side products on bf16 matrix cores, fp32
 //   accumulation.  Operands come from the workspace blocks the recomputed
@@ -614,7 +615,7 @@ __global__ __launch_bounds__(kGvThreads, 1) void k_chunk_grad_val(GradVArgs a)
 // dA and dP row-major and transposed, KY, EA and QA transposed ([channel]
 // [token]), written element by element from registers in phase A, so that
 // every fragment of the products is one 16-byte read.  Wave w owns column
-// tiles w, w+4, ... for all 64 rows.  Then a per-row pass forms
+// tiles w, w+8, ... for all 64 rows.  Then a per-row pass forms
 // the gradients of q, k and b and dG, and dalpha is the reverse cumulative
 // sum of dG.  Every phase issues its global loads before using any of them.
 // ---------------------------------------------------------------------------
