@@ -692,6 +692,11 @@ __global__ __launch_bounds__(kGkThreads, 1) void k_chunk_grad_key(GradKArgs a)
     const float bscale = (a.flags & kFlagNegEigval) ? 2.f : 1.f;
 
     // ---- phase A: loads (raw), then dA, dP, G, KY, EA, QA into LDS ----------
+    // alpha, b, k, q stay in registers, raw, for the row pass and dalpha (the
+    // row pass's rows are this thread's key items)
+    static_assert(R == NV, "row pass on the key items");
+    gvec ax[NV], bx[NV];
+    bf16x4 kx[NV], qx[NV];
     {
         // dA and dP in 8 x 8 blocks: thread t < 128 takes block t mod 64 of dA
         // (t < 64) or dP, rows 8 (b / 8) .., columns 8 (b mod 8) ..; it writes
@@ -703,8 +708,6 @@ __global__ __launch_bounds__(kGkThreads, 1) void k_chunk_grad_key(GradKArgs a)
         const bf* bsrc = (tid & 64) ? s_dP : s_dA;
 #pragma unroll
         for (int e = 0; e < 8; ++e) xb[e] = *reinterpret_cast<const bfrag*>(bsrc + (8 * bR + e) * 64 + 8 * bS);
-        gvec ax[NV], bx[NV];
-        bf16x4 kx[NV], qx[NV];
         cld_load<DK, NTH>(ax, agt, row0, H, Ln);
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
@@ -772,6 +775,17 @@ __global__ __launch_bounds__(kGkThreads, 1) void k_chunk_grad_key(GradKArgs a)
     }
     __syncthreads();
 
+    // the row pass's scratch values, requested before the products
+    const int c0 = 4 * (tid % CG), r0 = (tid / CG) * R;
+    bf16x4 xqh[R], xeh[R], xkt[R];                                 // raw until used
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+        const int r = r0 + rr;
+        xqh[rr] = *reinterpret_cast<const bf16x4*>(s_dQh + r * DK + c0);
+        xeh[rr] = *reinterpret_cast<const bf16x4*>(s_dEh + r * DK + c0);
+        xkt[rr] = *reinterpret_cast<const bf16x4*>(s_dKt + r * DK + c0);
+    }
+
     // ---- products on the matrix cores: column tiles ct = wave + NW m ---------
     f32x4 acc[CPW][4][4];                                      // [tile][row block][rowA rowP colA colP]
 #pragma unroll
@@ -828,34 +842,19 @@ __global__ __launch_bounds__(kGkThreads, 1) void k_chunk_grad_key(GradKArgs a)
     }
     __syncthreads();
 
-    // ---- per row: the gradients of q, k, b and dG (all loads first) ---------
+    // ---- per row: the gradients of q, k, b and dG ------------------------------
     {
         bf* dq = static_cast<bf*>(a.dq);
         bf* dk_out = static_cast<bf*>(a.dk_out);
         Tg* db = static_cast<Tg*>(a.db);
-        const int c0 = 4 * (tid % CG), r0 = (tid / CG) * R;
-        bf16x4 qr[R], kr[R];
-        gvec br[R];
-        bf16x4 xqh[R], xeh[R], xkt[R];                             // raw until used
-#pragma unroll
-        for (int rr = 0; rr < R; ++rr) {
-            const int r = r0 + rr;
-            const int64_t o = (row0 + (r < Ln ? r : Ln - 1) * H) * DK + c0;
-            xqh[rr] = *reinterpret_cast<const bf16x4*>(s_dQh + r * DK + c0);
-            xeh[rr] = *reinterpret_cast<const bf16x4*>(s_dEh + r * DK + c0);
-            xkt[rr] = *reinterpret_cast<const bf16x4*>(s_dKt + r * DK + c0);
-            qr[rr] = *reinterpret_cast<const bf16x4*>(qg + o);
-            kr[rr] = *reinterpret_cast<const bf16x4*>(kg + o);
-            br[rr] = *reinterpret_cast<const gvec*>(bgt + o);
-        }
         float ex[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int rr = 0; rr < R; ++rr) {
             const int r = r0 + rr;
             const bool ok = r < Ln;
             const f32x4 dQh = IOB::unpack4(xqh[rr]), dEh = IOB::unpack4(xeh[rr]), dKt = IOB::unpack4(xkt[rr]);
-            f32x4 q4 = IOB::unpack4(qr[rr]), k4 = IOB::unpack4(kr[rr]);
-            const f32x4 braw = widen4(br[rr]);
+            f32x4 q4 = IOB::unpack4(qx[rr]), k4 = IOB::unpack4(kx[rr]);
+            const f32x4 braw = widen4(bx[rr]);
             const f32x4 sb = logits ? sigmoid4(braw) : braw, b4 = logits ? sb * bscale : braw;
             float nq = 1.f, nk = 1.f;                                 // 1 / norms with the L2 option
             if (l2) {
@@ -927,18 +926,13 @@ __global__ __launch_bounds__(kGkThreads, 1) void k_chunk_grad_key(GradKArgs a)
     __syncthreads();
     {
         Tg* dalpha = static_cast<Tg*>(a.dalpha);
-        gvec al[NV];
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
-            const int i = tid + u * NTH, r = i / CG, c4 = 4 * (i - r * CG);
-            al[u] = *reinterpret_cast<const gvec*>(agt + (row0 + (r < Ln ? r : Ln - 1) * H) * DK + c4);
-        }
-#pragma unroll
-        for (int u = 0; u < NV; ++u) {
-            const int i = tid + u * NTH, r = i / CG, c4 = 4 * (i - r * CG);
+            int r, c4;
+            key_item<DK, NTH>(u, r, c4);
             if (r < Ln) {
                 const int64_t o = (row0 + r * H) * DK + c4;
-                const f32x4 a4 = widen4(al[u]), g4 = *reinterpret_cast<const f32x4*>(&dG[r * RS + c4]);
+                const f32x4 a4 = widen4(ax[u]), g4 = *reinterpret_cast<const f32x4*>(&dG[r * RS + c4]);
                 f32x4 d4;
                 if (logits) {   // d logit = (dG / alpha) alpha (1 - alpha), alpha = sigmoid(logit)
                     const f32x4 s4 = sigmoid4(a4);
