@@ -203,14 +203,13 @@ __device__ __attribute__((always_inline)) inline void panels_from(int wave, int 
 }
 
 template <int DK, int DV, typename Tg>
-__global__ __launch_bounds__(kGvThreads, 1) void k_chunk_grad_val(GradVArgs a)
+__device__ __attribute__((always_inline)) inline void grad_val_chunk(const GradVArgs& a, char* sm)
 {
     using L = GvLds;
     constexpr int NTH = kGvThreads, NW = kGvWaves;
     static_assert(L::BYTES <= 160 * 1024, "LDS budget");
     constexpr int NKK = DK / 32, NKV = DV / 32, NTK = DK / 16, NTV = DV / 16;
     constexpr int ldv = DV + 8, ldk = DK + 8;
-    __shared__ __attribute__((aligned(16))) char sm[L::BYTES];
     bf* Tl = reinterpret_cast<bf*>(sm + L::R0);
     bf* Ttl = Tl + 64 * LT;
     bf* dOl = reinterpret_cast<bf*>(sm + L::R1);
@@ -639,10 +638,15 @@ struct GkLds {
     static constexpr int SZ_IN = IN_K + 3 * DK * LT * 2;
     static constexpr int SZ_RES = 3 * 64 * RS * 4;        // deA (then dG), dqP, kak fp32 [64][RS]
     static constexpr int BIG = SZ_IN > SZ_RES ? SZ_IN : SZ_RES;
+    // the workgroup's LDS: G fp32 [64][DK], the operands / results region, the
+    // per row group column sums and the scan totals
+    static constexpr int O_G = 0, O_BIG = 64 * DK * 4, O_EXT = O_BIG + BIG;
+    static constexpr int O_TOT = O_EXT + (kGkThreads / (DK / 4)) * DK * 4;
+    static constexpr int BYTES = O_TOT + kGkThreads * 4;
 };
 
 template <int DK, typename Tg>
-__global__ __launch_bounds__(kGkThreads, 1) void k_chunk_grad_key(GradKArgs a)
+__device__ __attribute__((always_inline)) inline void grad_key_chunk(const GradKArgs& a, char* sm)
 {
     using L = GkLds<DK>;
     constexpr int NTH = kGkThreads, NW = NTH / 64;
@@ -650,10 +654,10 @@ __global__ __launch_bounds__(kGkThreads, 1) void k_chunk_grad_key(GradKArgs a)
     constexpr int RS = L::RS;
     constexpr int NV = 64 * DK / 4 / NTH;
     typedef typename GateVec<Tg>::type gvec;
-    __shared__ __attribute__((aligned(16))) float G[64 * DK];
-    __shared__ __attribute__((aligned(16))) char big[L::BIG];
-    __shared__ float ext[(NTH / CG) * DK];                // per row group: sum of dKtil * Ktil
-    __shared__ float tot[NTH];
+    float* G = reinterpret_cast<float*>(sm + L::O_G);
+    char* big = sm + L::O_BIG;
+    float* ext = reinterpret_cast<float*>(sm + L::O_EXT);      // per row group: sum of dKtil * Ktil
+    float* tot = reinterpret_cast<float*>(sm + L::O_TOT);
     bf* dAl = reinterpret_cast<bf*>(big + L::IN_A);
     bf* dPl = dAl + 64 * LT;
     bf* dATl = reinterpret_cast<bf*>(big + L::IN_AT);
@@ -946,6 +950,21 @@ __global__ __launch_bounds__(kGkThreads, 1) void k_chunk_grad_key(GradKArgs a)
             }
         }
     }
+}
+
+// One workgroup per chunk runs the value side, then the key side of the same
+// chunk in the same LDS (the value side's results reach the key side through
+// the scratch block it has just written, from this XCD's L2).
+template <int DK, int DV, typename Tg>
+__global__ __launch_bounds__(kGvThreads, 1) void k_chunk_grad_mf(GradVArgs v, GradKArgs k)
+{
+    static_assert(kGvThreads == kGkThreads, "one workgroup shape for both sides");
+    constexpr int BYTES = GvLds::BYTES > GkLds<DK>::BYTES ? GvLds::BYTES : GkLds<DK>::BYTES;
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(16))) char sm[BYTES];
+    grad_val_chunk<DK, DV, Tg>(v, sm);
+    __syncthreads();                       // LDS reused; the scratch block written
+    grad_key_chunk<DK, Tg>(k, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -1259,12 +1278,12 @@ bool gradmf_supported(int dk, int dv, bool bf16)
 }
 
 template <int DK, int DV>
-static void val_launch(const GradVArgs& v, bool gbf16, dim3 grid, hipStream_t s)
+static void grad_launch(const GradVArgs& v, const GradKArgs& k, bool gbf16, dim3 grid, hipStream_t s)
 {
     if (gbf16)
-        hipLaunchKernelGGL((k_chunk_grad_val<DK, DV, __bf16>), grid, dim3(kGvThreads), 0, s, v);
+        hipLaunchKernelGGL((k_chunk_grad_mf<DK, DV, __bf16>), grid, dim3(kGvThreads), 0, s, v, k);
     else
-        hipLaunchKernelGGL((k_chunk_grad_val<DK, DV, float>), grid, dim3(kGvThreads), 0, s, v);
+        hipLaunchKernelGGL((k_chunk_grad_mf<DK, DV, float>), grid, dim3(kGvThreads), 0, s, v, k);
 }
 
 template <int DK>
@@ -1272,17 +1291,11 @@ static hipError_t grad_mf_dk(const GradVArgs& v, const GradKArgs& k, bool gbf16,
 {
     const dim3 grid((unsigned)v.total);
     switch (v.dv) {
-        case 32: val_launch<DK, 32>(v, gbf16, grid, s); break;
-        case 64: val_launch<DK, 64>(v, gbf16, grid, s); break;
-        case 128: val_launch<DK, 128>(v, gbf16, grid, s); break;
+        case 32: grad_launch<DK, 32>(v, k, gbf16, grid, s); break;
+        case 64: grad_launch<DK, 64>(v, k, gbf16, grid, s); break;
+        case 128: grad_launch<DK, 128>(v, k, gbf16, grid, s); break;
         default: return hipErrorInvalidValue;
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (gbf16)
-        hipLaunchKernelGGL((k_chunk_grad_key<DK, __bf16>), grid, dim3(kGkThreads), 0, s, k);
-    else
-        hipLaunchKernelGGL((k_chunk_grad_key<DK, float>), grid, dim3(kGkThreads), 0, s, k);
     return hipGetLastError();
 }
 
