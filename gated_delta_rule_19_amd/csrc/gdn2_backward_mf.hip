@@ -3,9 +3,10 @@
 // same path (k_chunk_state_bwd_mf, described where it is defined).
 //
 // Same gradient as k_chunk_grad (the formulas are in gdn2_backward.hip's
-// header), split in two launches of one workgroup (8 waves) per chunk:
+// header), in one launch of one workgroup (8 waves) per chunk, k_chunk_grad_mf,
+// which runs two stages in turn in the same LDS:
 //
-// k_chunk_grad_val  the value-side products on bf16 matrix cores, fp32
+// the value side (grad_val_chunk)  the value-side products on bf16 matrix cores, fp32
 //   accumulation.  Operands come from the workspace blocks the recomputed
 //   forward writes in the backward's layout (W, P^T, Ktil, U^T, T, Eh), from
 //   the chunk checkpoints (S0 and the exit gradient dSL, each in bf16
@@ -20,13 +21,13 @@
 //     dGamma_L = rowsum(dSL * S0);
 //   dQh, dKtil, dEh, dP, dA (bf16) and dGamma_L (fp32) go to a scratch block
 //   per chunk.
-// k_chunk_grad_key  the key side: the cumulative log decay G, the
+// the key side (grad_key_chunk)  the cumulative log decay G, the
 //   contractions of dA and dP with the block-split decay ratios on bf16
 //   matrix cores (row side: sum_s dA[r,s] k_s R[r,s]; column side:
 //   sum_r dA[r,s] e_r R[r,s], and the same with dP and q), then per row the
 //   gradients of q, k, b, and dalpha from the reverse cumulative sum of dG.
 // With the prologue options (burn-gdn2 0.1.9 README, "Architecture" and
-// "Configuration") both launches take the raw inputs: gates are activated
+// "Configuration") both stages take the raw inputs: gates are activated
 // on load (sigmoid, b x 2 in negative-eigenvalue mode), q/k rows normalised
 // with lane-group reductions, and the gradients they write are those of
 // the logits and of the raw q/k.
@@ -73,7 +74,7 @@ template <typename T> __device__ inline void gs(T* p, int64_t i, float x) { p[i]
 
 }  // namespace
 
-// scratch per chunk between the two launches, in 4-byte words: dQh, dKtil,
+// scratch per chunk between the two stages, in 4-byte words: dQh, dKtil,
 // dEh bf16 [64][dk]; dP, dA bf16 [64][64]; dGamma_L fp32 [dk]
 __host__ __device__ inline int64_t gradmf_scratch_floats(int dk) { return 96 * (int64_t)dk + 4096 + dk; }
 
@@ -142,7 +143,7 @@ __device__ __attribute__((always_inline)) inline void cld_scan(float* G, float* 
     __syncthreads();
 }
 
-// LDS regions of k_chunk_grad_val (bytes), sized for dk = dv = 128
+// LDS regions of the value side (bytes), sized for dk = dv = 128
 struct GvLds {
     static constexpr int R0 = 0;                                  // T [64][LT], T^T [64][LT]
     static constexpr int R1 = R0 + 2 * 64 * LT * 2;               // dO [64][LD] | u [64][LD] | tmp [64][LT]

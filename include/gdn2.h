@@ -236,15 +236,19 @@ int gdn2_recurrent_varlen(const gdn2_problem* p, const int32_t* cu_seqlens,
  * gradients.
  * The forward is recomputed inside (no forward workspace is kept between
  * the calls); the backward is exact up to rounding, with fp32 accumulation
- * throughout and the matrix-product operands in io_dtype.
+ * throughout and the matrix-product operands in io_dtype (with bf16 I/O the
+ * chunk checkpoints and the per-chunk values handed between the gradient
+ * stages are kept in bf16 too).
  * Every gradient output must be distinct from every input and from each
  * other (GDN2_ERR_ALIAS); all tensors 16-byte aligned; the workspace
  * 256-byte aligned and at least gdn2_chunk_bwd_workspace_size(p) bytes (it
  * holds the forward factors, the state entering every chunk, the state
  * gradient leaving every chunk, per-chunk scratch and, where the options
  * are mapped outside the kernels, the mapped inputs and their gradients).
- * Launches five kernels on `stream`.  With bf16 I/O and dk, dv in
- * {32, 64, 128} the kernels apply the prologue options themselves; grouped
+ * Launches four kernels on `stream` with bf16 I/O and dk, dv in
+ * {32, 64, 128} (forward recompute, checkpointing state pass, reverse pass,
+ * per-chunk gradients), five otherwise.  On that path the kernels apply
+ * the prologue options themselves; grouped
  * heads then add one kernel before and one after (q/k widened to the value
  * heads, their gradients summed per group).  Other shapes map every option
  * that way: one kernel before and one after for the q/k rows (L2 norm or
