@@ -81,6 +81,9 @@ CASES = [
     (1, 97, 3, 32, 96, BF16, F32, None, True, 1.0),
     (1, 64, 2, 128, 32, BF16, BF16, 0.05, False, 1.0),
     (2, 80, 2, 32, 64, BF16, F32, 0.05, True, 2.0),
+    # the remaining matrix-core shapes: dk 32 with dv 128, dk 64 with dv 32 (last chunk 1 token)
+    (1, 70, 2, 32, 128, BF16, F32, 0.05, True, 1.0),
+    (2, 129, 1, 64, 32, BF16, BF16, None, True, 2.0),
 ]
 
 
