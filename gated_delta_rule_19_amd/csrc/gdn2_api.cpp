@@ -185,9 +185,10 @@ int do_state(const gdn2_problem* p, const float* S0, void* o, float* S_out, cons
 // backward workspace: forward factors | chunk entry states | chunk exit
 // state gradients | gradient scratch, each 256-byte aligned.  The vector-ALU
 // path keeps both checkpoints in fp32 [dk][dv]; the matrix-core path (bf16
-// I/O, dk 32/64/128, dv a multiple of 32 up to 128) keeps T in each factor
-// block and both checkpoints in bf16, [dk][dv] and transposed [dv][dk] (its
-// products take bf16 operands, so an fp32 copy would only be rounded again).
+// I/O, dk and dv in {32, 64, 128}) keeps the backward's extension in each
+// factor block, both checkpoints in bf16, [dk][dv] and transposed [dv][dk]
+// (its products take bf16 operands, so an fp32 copy would only be rounded
+// again), and needs no gradient scratch (its two gradient stages share LDS).
 struct BwdLayout {
     bool mf;
     int64_t block, t_off;                 // factor block stride, offset of T in it
@@ -212,8 +213,7 @@ BwdLayout bwd_layout(const gdn2_problem* p)
     l.dsl = l.mf ? up(l.chkT + chk) : l.chkT;
     l.dslT = up(l.dsl + chk);
     l.scratch = l.mf ? up(l.dslT + chk) : l.dslT;
-    l.total = l.scratch + (l.mf ? gdn2::gradmf_scratch_bytes((int)p->dk, nblk)
-                                : gdn2::chunk_grad_scratch_bytes((int)p->dk, (int)p->dv, nblk));
+    l.total = l.scratch + (l.mf ? 0 : gdn2::chunk_grad_scratch_bytes((int)p->dk, (int)p->dv, nblk));
     return l;
 }
 
@@ -305,9 +305,9 @@ int bwd_core(const gdn2_problem* p, const BwdLayout& l, const void* q, const voi
     if (nchunks(p) == 0) return GDN2_OK;
     float* gsc = reinterpret_cast<float*>(ws + l.scratch);
     if (l.mf) {
-        gdn2::GradVArgs va{ws, l.block, l.t_off, k, v, alpha, b, w, dO, chkIo, chkT, dslIo, dslT, dw, dv, gsc,
+        gdn2::GradVArgs va{ws, l.block, l.t_off, k, v, alpha, b, w, dO, chkIo, chkT, dslIo, dslT, dw, dv,
                            p->B, p->T, p->H, (int)p->dk, (int)p->dv, (int)nchunks(p), total, (int)p->flags};
-        gdn2::GradKArgs ka{q, k, alpha, b, gsc, dq, dk, dalpha, db, p->B, p->T, p->H, (int)p->dk,
+        gdn2::GradKArgs ka{q, k, alpha, b, dq, dk, dalpha, db, p->B, p->T, p->H, (int)p->dk,
                            (int)nchunks(p), total, (int)p->flags};
         return launch_status(gdn2::launch_chunk_grad_mf(va, ka, gates_bf16(p), s));
     }

@@ -74,10 +74,6 @@ template <typename T> __device__ inline void gs(T* p, int64_t i, float x) { p[i]
 
 }  // namespace
 
-// scratch per chunk between the two stages, in 4-byte words: dQh, dKtil,
-// dEh bf16 [64][dk]; dP, dA bf16 [64][64]; dGamma_L fp32 [dk]
-__host__ __device__ inline int64_t gradmf_scratch_floats(int dk) { return 96 * (int64_t)dk + 4096 + dk; }
-
 // Key-axis items of a chunk on NTH threads: thread t holds channels
 // c4 .. c4+3, c4 = 4 (t mod DK/4), of the NV = 16 DK / NTH consecutive rows
 // (t div DK/4) NV + u, u < NV (the DK/4 lanes of a row are consecutive).
@@ -158,6 +154,16 @@ struct GvLds {
 };
 
 constexpr int kGvThreads = 512, kGvWaves = 8;      // value-side workgroup: 8 waves
+
+// The value side's results for the key side, handed over in LDS when both
+// stages' own regions are free (bytes): dQh, dKtil, dEh bf16 [64][DK + 8],
+// dP, dA bf16 [64][72], dGamma_L fp32 [DK]
+template <int DK>
+struct HandLds {
+    static constexpr int HS = DK + 8, PS = 64 + 8;
+    static constexpr int Q = 0, K = Q + 64 * HS * 2, E = K + 64 * HS * 2, P = E + 64 * HS * 2;
+    static constexpr int A = P + 64 * PS * 2, GL = A + 64 * PS * 2, BYTES = GL + DK * 4;
+};
 
 // Tiles t = wave, wave + 8, ... < NT of one product: fetch(t, a, b) loads the
 // NKB K-blocks of a tile's A and B fragments, epi(t, acc) consumes its
@@ -255,13 +261,6 @@ __device__ __attribute__((always_inline)) inline void grad_val_chunk(const GradV
     const Tg* wgt = static_cast<const Tg*>(a.w);
     Tg* dwg = static_cast<Tg*>(a.dw);
     bf* dvg = static_cast<bf*>(a.dv_out);
-    float* sc = a.gsc + ci * gradmf_scratch_floats(DK);
-    bf* s_dQh = reinterpret_cast<bf*>(sc);
-    bf* s_dKt = s_dQh + 64 * DK;
-    bf* s_dEh = s_dKt + 64 * DK;
-    bf* s_dP = s_dEh + 64 * DK;
-    bf* s_dA = s_dP + 4096;
-    float* s_dGL = sc + 96 * DK + 4096;
     const bool logits = (a.flags & kFlagGateLogits) != 0;
 
     // ---- phase 0: operands into LDS ----------------------------------------
@@ -420,6 +419,9 @@ __device__ __attribute__((always_inline)) inline void grad_val_chunk(const GradV
         for (int kb = 0; kb < NKV; ++kb) rb[m][kb] = fr(B, 16 * tn + l16, DV, kb, grp);
     }
     float glp[FUSE_GL ? NPW / 2 : 1];
+    // results for the key side, held until the end of this stage: per panel
+    // and row tile, 4 rows of 4 columns after a transpose inside each lane quad
+    bf16x4 hqk[NPW][4];
 #pragma unroll
     for (int m = 0; m < NPW; ++m) {
         const int p = wave + NW * m;
@@ -440,13 +442,12 @@ __device__ __attribute__((always_inline)) inline void grad_val_chunk(const GradV
 #pragma unroll
                 for (int i = 0; i < 4; ++i) dWl[(r + i) * ldk + c] = (bf)aw[i];
                 st_vec4(dWtl + c * LT + r, aw);
-                // rows of 4 columns after a transpose inside each lane quad
-                st_vec4(s_dQh + (r + (l16 & 3)) * DK + (c & ~3), quad_transpose4(aq));
+                hqk[m][tr] = IOB::pack4(quad_transpose4(aq));
             } else {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < NKV; ++kb) acc = IOB::mma(acc, fr(Dll, 16 * tr + l16, ldv, kb, grp), fb[kb]);
-                st_vec4(s_dKt + (r + (l16 & 3)) * DK + (c & ~3), quad_transpose4(acc));
+                hqk[m][tr] = IOB::pack4(quad_transpose4(acc));
             }
         }
         if constexpr (FUSE_GL) {
@@ -463,20 +464,19 @@ __device__ __attribute__((always_inline)) inline void grad_val_chunk(const GradV
         }
     }
     // ---- dP = mask(dO Delta^T) -------------------------------------------------------
-    tiles<NKV>(wave, 16,
-               [&](int t, bfrag (&fa)[NKV], bfrag (&fb)[NKV]) {
-                   const int tr = t >> 2, tn = t & 3;
+    constexpr int N64 = 16 / NW;                                    // 64 x 64 tiles per wave
+    bf16x4 hp[N64];
 #pragma unroll
-                   for (int kb = 0; kb < NKV; ++kb) {
-                       fa[kb] = fr(dOl, 16 * tr + l16, ldv, kb, grp);
-                       fb[kb] = fr(Dll, 16 * tn + l16, ldv, kb, grp);
-                   }
-               },
-               [&](int t, f32x4 acc) {
-                   const int r = 16 * (t >> 2) + 4 * grp, s = 16 * (t & 3) + l16;
+    for (int m = 0; m < N64; ++m) {
+        const int t = wave + NW * m, tr = t >> 2, tn = t & 3;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                   for (int i = 0; i < 4; ++i) s_dP[(r + i) * 64 + s] = (bf)(s <= r + i ? acc[i] : 0.f);
-               });
+        for (int kb = 0; kb < NKV; ++kb) acc = IOB::mma(acc, fr(dOl, 16 * tr + l16, ldv, kb, grp), fr(Dll, 16 * tn + l16, ldv, kb, grp));
+        const int r = 16 * tr + 4 * grp, s = 16 * tn + l16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = s <= r + i ? acc[i] : 0.f;
+        hp[m] = IOB::pack4(quad_transpose4(acc));
+    }
     // ---- du = T^T dDelta -> dw = du v, dv = du w;  u = w v ----------------------
     // A transpose inside each lane quad turns a du tile's accumulator into rows
     // of 4 consecutive columns (lane q: row 16 tr + 4 grp + q), so w and v are
@@ -545,20 +545,17 @@ __device__ __attribute__((always_inline)) inline void grad_val_chunk(const GradV
                      [&](int t, f32x4 acc) {
                          st_vec4(dTtl + (16 * (t & 3) + l16) * LT + 16 * (t >> 2) + 4 * grp, acc);
                      });
-    tiles<2>(wave, 4 * NTK,
-             [&](int t, bfrag (&fa)[2], bfrag (&fb)[2]) {
-                 const int tr = t / NTK, tn = t - tr * NTK;
+    constexpr int NEH = 4 * NTK / NW;                               // dEh tiles per wave
+    static_assert(4 * NTK % NW == 0, "dEh tiles");
+    bf16x4 he[NEH];
 #pragma unroll
-                 for (int kb = 0; kb < 2; ++kb) {
-                     fa[kb] = fr(Ttl, 16 * tr + l16, LT, kb, grp);
-                     fb[kb] = fr(dWtl, 16 * tn + l16, LT, kb, grp);
-                 }
-             },
-             [&](int t, f32x4 acc) {
-                 const int tr = t / NTK, tn = t - tr * NTK;
-                 const int r = 16 * tr + 4 * grp + (l16 & 3), c = 16 * tn + (l16 & ~3);
-                 st_vec4(s_dEh + r * DK + c, quad_transpose4(acc));
-             });
+    for (int m = 0; m < NEH; ++m) {
+        const int t = wave + NW * m, tr = t / NTK, tn = t - tr * NTK;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) acc = IOB::mma(acc, fr(Ttl, 16 * tr + l16, LT, kb, grp), fr(dWtl, 16 * tn + l16, LT, kb, grp));
+        he[m] = IOB::pack4(quad_transpose4(acc));
+    }
     __syncthreads();
     // ---- tmp = T^T dT -------------------------------------------------------------
     tiles<2>(wave, 16,
@@ -576,26 +573,58 @@ __device__ __attribute__((always_inline)) inline void grad_val_chunk(const GradV
              });
     __syncthreads();
     // ---- dA = mask(-tmp T^T) --------------------------------------------------------
-    tiles<2>(wave, 16,
-             [&](int t, bfrag (&fa)[2], bfrag (&fb)[2]) {
+    bf16x4 ha[N64];
 #pragma unroll
-                 for (int kb = 0; kb < 2; ++kb) {
-                     fa[kb] = fr(tmpl, 16 * (t >> 2) + l16, LT, kb, grp);
-                     fb[kb] = fr(Tl, 16 * (t & 3) + l16, LT, kb, grp);
-                 }
-             },
-             [&](int t, f32x4 acc) {
-                 const int r = 16 * (t >> 2) + 4 * grp, s = 16 * (t & 3) + l16;
+    for (int m = 0; m < N64; ++m) {
+        const int t = wave + NW * m, tr = t >> 2, tn = t & 3;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                 for (int i = 0; i < 4; ++i) s_dA[(r + i) * 64 + s] = (bf)(s < r + i ? -acc[i] : 0.f);
-             });
+        for (int kb = 0; kb < 2; ++kb) acc = IOB::mma(acc, fr(tmpl, 16 * tr + l16, LT, kb, grp), fr(Tl, 16 * tn + l16, LT, kb, grp));
+        const int r = 16 * tr + 4 * grp, s = 16 * tn + l16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = s < r + i ? -acc[i] : 0.f;
+        ha[m] = IOB::pack4(quad_transpose4(acc));
+    }
+    // ---- hand-over: every LDS region of this stage is free now ----------------
+    __syncthreads();
+    using HL = HandLds<DK>;
+    constexpr int HS = HL::HS, PS = HL::PS;
+    bf* hQ = reinterpret_cast<bf*>(sm + HL::Q);
+    bf* hK = reinterpret_cast<bf*>(sm + HL::K);
+    bf* hE = reinterpret_cast<bf*>(sm + HL::E);
+    bf* hP = reinterpret_cast<bf*>(sm + HL::P);
+    bf* hA = reinterpret_cast<bf*>(sm + HL::A);
+    float* hG = reinterpret_cast<float*>(sm + HL::GL);
+    const int rq = 4 * grp + (l16 & 3), cq = l16 & ~3;             // lane's row and column in a tile
+#pragma unroll
+    for (int m = 0; m < NPW; ++m) {
+        const int p = wave + NW * m;
+        if (p < 2 * NTK) {
+            const int tn = p < NTK ? p : p - NTK;
+            bf* dst = p < NTK ? hQ : hK;
+#pragma unroll
+            for (int tr = 0; tr < 4; ++tr)
+                *reinterpret_cast<bf16x4*>(dst + (16 * tr + rq) * HS + 16 * tn + cq) = hqk[m][tr];
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < NEH; ++m) {
+        const int t = wave + NW * m, tr = t / NTK, tn = t - tr * NTK;
+        *reinterpret_cast<bf16x4*>(hE + (16 * tr + rq) * HS + 16 * tn + cq) = he[m];
+    }
+#pragma unroll
+    for (int m = 0; m < N64; ++m) {
+        const int t = wave + NW * m, tr = t >> 2, tn = t & 3;
+        *reinterpret_cast<bf16x4*>(hP + (16 * tr + rq) * PS + 16 * tn + cq) = hp[m];
+        *reinterpret_cast<bf16x4*>(hA + (16 * tr + rq) * PS + 16 * tn + cq) = ha[m];
+    }
     if constexpr (FUSE_GL) {
         if (grp == 0) {
 #pragma unroll
-            for (int i = 0; i < NPW / 2; ++i) s_dGL[16 * (wave + NW * i) + l16] = glp[i];
+            for (int i = 0; i < NPW / 2; ++i) hG[16 * (wave + NW * i) + l16] = glp[i];
         }
     } else {
-        if (tid % TPR == 0 && tid < DK * TPR) s_dGL[tid / TPR] = dgl;
+        if (tid % TPR == 0 && tid < DK * TPR) hG[tid / TPR] = dgl;
     }
 }
 
@@ -686,15 +715,35 @@ __device__ __attribute__((always_inline)) inline void grad_key_chunk(const GradK
     const bf* kg = static_cast<const bf*>(a.k);
     const Tg* agt = static_cast<const Tg*>(a.alpha);
     const Tg* bgt = static_cast<const Tg*>(a.b);
-    const float* sc = a.gsc + ci * gradmf_scratch_floats(DK);
-    const bf* s_dQh = reinterpret_cast<const bf*>(sc);
-    const bf* s_dKt = s_dQh + 64 * DK;
-    const bf* s_dEh = s_dKt + 64 * DK;
-    const bf* s_dP = s_dEh + 64 * DK;
-    const bf* s_dA = s_dP + 4096;
-    const float* s_dGL = sc + 96 * DK + 4096;
     const bool logits = (a.flags & kFlagGateLogits) != 0, l2 = (a.flags & kFlagQkL2norm) != 0;
     const float bscale = (a.flags & kFlagNegEigval) ? 2.f : 1.f;
+
+    // ---- the value side's results, from the hand-over region of LDS -----------
+    // (the row pass's dQh, dEh, dKtil at this thread's key items; dA and dP in
+    // the 8 x 8 blocks of phase A; dGamma_L)
+    using HL = HandLds<DK>;
+    const int c0 = 4 * (tid % CG), r0 = (tid / CG) * R;
+    bf16x4 xqh[R], xeh[R], xkt[R];                                 // raw until used
+    bfrag xb[8];
+    const int bk = tid & 63, bR = bk >> 3, bS = bk & 7;
+    float dglv;
+    {
+        const bf* hQ = reinterpret_cast<const bf*>(sm + HL::Q);
+        const bf* hK = reinterpret_cast<const bf*>(sm + HL::K);
+        const bf* hE = reinterpret_cast<const bf*>(sm + HL::E);
+        const bf* bsrc = reinterpret_cast<const bf*>(sm + ((tid & 64) ? HL::P : HL::A));
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
+            const int r = r0 + rr;
+            xqh[rr] = *reinterpret_cast<const bf16x4*>(hQ + r * HL::HS + c0);
+            xeh[rr] = *reinterpret_cast<const bf16x4*>(hE + r * HL::HS + c0);
+            xkt[rr] = *reinterpret_cast<const bf16x4*>(hK + r * HL::HS + c0);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xb[e] = *reinterpret_cast<const bfrag*>(bsrc + (8 * bR + e) * HL::PS + 8 * bS);
+        dglv = reinterpret_cast<const float*>(sm + HL::GL)[tid < DK ? tid : 0];
+    }
+    __syncthreads();                                           // read: this stage's regions overwrite it
 
     // ---- phase A: loads (raw), then dA, dP, G, KY, EA, QA into LDS ----------
     // alpha, b, k, q stay in registers, raw, for the row pass and dalpha (the
@@ -703,16 +752,10 @@ __device__ __attribute__((always_inline)) inline void grad_key_chunk(const GradK
     gvec ax[NV], bx[NV];
     bf16x4 kx[NV], qx[NV];
     {
-        // dA and dP in 8 x 8 blocks: thread t < 128 takes block t mod 64 of dA
+        // dA and dP in 8 x 8 blocks: thread t < 128 holds block t mod 64 of dA
         // (t < 64) or dP, rows 8 (b / 8) .., columns 8 (b mod 8) ..; it writes
         // the block row-major and, transposed in registers, into the
-        // transposed copy (threads t >= 128 load the same blocks again and
-        // write nothing: every load is unconditional)
-        bfrag xb[8];
-        const int bk = tid & 63, bR = bk >> 3, bS = bk & 7;
-        const bf* bsrc = (tid & 64) ? s_dP : s_dA;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) xb[e] = *reinterpret_cast<const bfrag*>(bsrc + (8 * bR + e) * 64 + 8 * bS);
+        // transposed copy
         cld_load<DK, NTH>(ax, agt, row0, H, Ln);
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
@@ -779,17 +822,6 @@ __device__ __attribute__((always_inline)) inline void grad_key_chunk(const GradK
         }
     }
     __syncthreads();
-
-    // the row pass's scratch values, requested before the products
-    const int c0 = 4 * (tid % CG), r0 = (tid / CG) * R;
-    bf16x4 xqh[R], xeh[R], xkt[R];                                 // raw until used
-#pragma unroll
-    for (int rr = 0; rr < R; ++rr) {
-        const int r = r0 + rr;
-        xqh[rr] = *reinterpret_cast<const bf16x4*>(s_dQh + r * DK + c0);
-        xeh[rr] = *reinterpret_cast<const bf16x4*>(s_dEh + r * DK + c0);
-        xkt[rr] = *reinterpret_cast<const bf16x4*>(s_dKt + r * DK + c0);
-    }
 
     // ---- products on the matrix cores: column tiles ct = wave + NW m ---------
     f32x4 acc[CPW][4][4];                                      // [tile][row block][rowA rowP colA colP]
@@ -908,7 +940,7 @@ __device__ __attribute__((always_inline)) inline void grad_key_chunk(const GradK
     // dlog(alpha) = reverse cumulative sum of dG; the last token also carries
     // the uses of Gamma_L (the state decay over the chunk and Ktil)
     if (tid < DK) {
-        float x = s_dGL[tid] * __expf(G[63 * DK + tid]);
+        float x = dglv * __expf(G[63 * DK + tid]);
         for (int g = 0; g < NTH / CG; ++g) x += ext[g * DK + tid];
         dG[63 * RS + tid] += x;
     }
@@ -954,17 +986,19 @@ __device__ __attribute__((always_inline)) inline void grad_key_chunk(const GradK
 }
 
 // One workgroup per chunk runs the value side, then the key side of the same
-// chunk in the same LDS (the value side's results reach the key side through
-// the scratch block it has just written, from this XCD's L2).
+// chunk in the same LDS; the value side's results pass from one to the other
+// through LDS (HandLds), written when the value side's regions are free and
+// read before the key side's overwrite them.
 template <int DK, int DV, typename Tg>
 __global__ __launch_bounds__(kGvThreads, 1) void k_chunk_grad_mf(GradVArgs v, GradKArgs k)
 {
     static_assert(kGvThreads == kGkThreads, "one workgroup shape for both sides");
-    constexpr int BYTES = GvLds::BYTES > GkLds<DK>::BYTES ? GvLds::BYTES : GkLds<DK>::BYTES;
+    constexpr int B0 = GvLds::BYTES > GkLds<DK>::BYTES ? GvLds::BYTES : GkLds<DK>::BYTES;
+    constexpr int BYTES = B0 > HandLds<DK>::BYTES ? B0 : HandLds<DK>::BYTES;
     static_assert(BYTES <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(16))) char sm[BYTES];
     grad_val_chunk<DK, DV, Tg>(v, sm);
-    __syncthreads();                       // LDS reused; the scratch block written
+    __syncthreads();                       // the hand-over written
     grad_key_chunk<DK, Tg>(k, sm);
 }
 
@@ -1270,8 +1304,6 @@ __global__ __launch_bounds__(RsLds<DK>::THREADS, 1) void k_chunk_state_bwd_mf(Bw
         }
     }
 }
-
-int64_t gradmf_scratch_bytes(int dk, int64_t total) { return total * gradmf_scratch_floats(dk) * 4; }
 
 bool gradmf_supported(int dk, int dv, bool bf16)
 {

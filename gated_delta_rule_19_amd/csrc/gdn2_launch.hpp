@@ -74,26 +74,24 @@ struct GradArgs {
     int64_t B, T, H; int dk, dv, nt; int64_t total;
 };
 
-// Matrix-core per-chunk gradients (bf16 I/O; with the prologue flags the
-// gates are logits and q/k unnormalised, and the gradients are those of the
-// raw inputs): the value-side launch reads the
-// forward workspace (blocks of ws_block bytes with T at t_off), the
-// checkpoints S_chk/S_chkT and dSL/dSLT (bf16, [dk][dv] and [dv][dk] per
-// chunk), dO, v, w, b, k, alpha; writes dw, dv
-// and an fp32 scratch block per chunk that the key-side launch reads with q,
-// k, b, alpha to write dq, dk, db, dalpha.
+// Matrix-core per-chunk gradients, one launch of two stages (bf16 I/O; with
+// the prologue flags the gates are logits and q/k unnormalised, and the
+// gradients are those of the raw inputs): the value side reads the forward
+// workspace (blocks of ws_block bytes, the backward's extension at t_off),
+// the checkpoints S_chk/S_chkT and dSL/dSLT (bf16, [dk][dv] and [dv][dk] per
+// chunk), dO, v, w and writes dw, dv; the key side takes its results from
+// LDS and reads q, k, b, alpha to write dq, dk, db, dalpha.
 struct GradVArgs {
     const void* ws; int64_t ws_block, t_off;
     const void* k; const void* v; const void* alpha; const void* b; const void* w; const void* dO;
     const void* S_chk; const void* S_chkT; const void* dSL; const void* dSLT;
-    void* dw; void* dv_out; float* gsc;
+    void* dw; void* dv_out;
     int64_t B, T, H; int dk, dv, nt; int64_t total;
     int flags;              // prologue options applied in-kernel (gradients of the logits, raw q/k)
 };
 
 struct GradKArgs {
     const void* q; const void* k; const void* alpha; const void* b;
-    const float* gsc;
     void* dq; void* dk_out; void* dalpha; void* db;
     int64_t B, T, H; int dk, nt; int64_t total;
     int flags;
@@ -145,7 +143,6 @@ hipError_t launch_bwd_gate_map(const GateMapArgs& a, bool post, bool gbf16, hipS
 hipError_t launch_chunk_grad(const GradArgs& a, bool bf16, bool gbf16, hipStream_t s);
 hipError_t launch_chunk_grad_mf(const GradVArgs& v, const GradKArgs& k, bool gbf16, hipStream_t s);
 bool gradmf_supported(int dk, int dv, bool bf16);
-int64_t gradmf_scratch_bytes(int dk, int64_t total);
 // workgroups of the gradient launch and the bytes of its scratch
 int64_t grad_blocks(int64_t total);
 int64_t chunk_grad_scratch_bytes(int dk, int dv, int64_t total);
