@@ -305,7 +305,7 @@ int bwd_core(const gdn2_problem* p, const BwdLayout& l, const void* q, const voi
     if (nchunks(p) == 0) return GDN2_OK;
     float* gsc = reinterpret_cast<float*>(ws + l.scratch);
     if (l.mf) {
-        gdn2::GradVArgs va{ws, l.block, l.t_off, k, v, alpha, b, w, dO, chkIo, chkT, dslIo, dslT, dw, dv,
+        gdn2::GradVArgs va{ws, l.block, l.t_off, v, w, dO, chkIo, chkT, dslIo, dslT, dw, dv,
                            p->B, p->T, p->H, (int)p->dk, (int)p->dv, (int)nchunks(p), total, (int)p->flags};
         gdn2::GradKArgs ka{q, k, alpha, b, dq, dk, dalpha, db, p->B, p->T, p->H, (int)p->dk,
                            (int)nchunks(p), total, (int)p->flags};

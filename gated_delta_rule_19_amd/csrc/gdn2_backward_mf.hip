@@ -53,7 +53,6 @@ __device__ inline bfrag fr(const bf* base, int row, int64_t ld, int kb, int grp)
     return *reinterpret_cast<const bfrag*>(base + row * ld + kb * 32 + grp * 8);
 }
 
-template <typename T> __device__ inline float gf(const T* p, int64_t i) { return Io<T>::to_f(p[i]); }
 
 // sum over the N consecutive lanes that hold one row (N a power of two <= 32)
 template <int N>
@@ -70,7 +69,6 @@ __device__ __forceinline__ float row_rnorm(f32x4 x)
 {
     return __builtin_amdgcn_rsqf(lanes_sum<N>(x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3]) + kL2normEps);
 }
-template <typename T> __device__ inline void gs(T* p, int64_t i, float x) { p[i] = Io<T>::from_f(x); }
 
 }  // namespace
 
@@ -190,14 +188,14 @@ __device__ __attribute__((always_inline)) inline void tiles(int wave, int NT, FF
 }
 
 // Column panels p = wave, wave + 8, ... < NP of products whose B operand
-// (NKB K-blocks of one 16-column panel) comes from global memory: fetch(p, b)
-// loads it once, body(p, b) runs the panel's row tiles with A from LDS.  The
-// next panel's B is requested before the current panel's products.
+// (NKB K-blocks of one 16-column panel) comes from global memory: panel
+// p = wave has been requested into `first`, fetch(p, b) loads a later one,
+// body(p, b) runs the panel's row tiles with A from LDS.  The next panel's B
+// is requested before the current panel's products.
 template <int NKB, typename FF, typename FB>
 __device__ __attribute__((always_inline)) inline void panels_from(int wave, int NP, const bfrag (&first)[NKB], FF fetch,
                                                                   FB body)
 {
-    // the same, with panel p = wave already requested (into `first`)
     bfrag cb[NKB], nb[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) nb[kb] = first[kb];

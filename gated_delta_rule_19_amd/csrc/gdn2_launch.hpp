@@ -83,7 +83,7 @@ struct GradArgs {
 // LDS and reads q, k, b, alpha to write dq, dk, db, dalpha.
 struct GradVArgs {
     const void* ws; int64_t ws_block, t_off;
-    const void* k; const void* v; const void* alpha; const void* b; const void* w; const void* dO;
+    const void* v; const void* w; const void* dO;
     const void* S_chk; const void* S_chkT; const void* dSL; const void* dSLT;
     void* dw; void* dv_out;
     int64_t B, T, H; int dk, dv, nt; int64_t total;
