@@ -45,7 +45,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["recurrent", "chunked_wy", "rel_l2", "prologue", "sigmoid", "gated_rmsnorm", "NORM_EPS", "share_qk_heads", "varlen",
-           "FLAG_GATE_LOGITS", "FLAG_NEG_EIGVAL", "FLAG_QK_L2NORM"]
+           "FLAG_GATE_LOGITS", "FLAG_NEG_EIGVAL", "FLAG_QK_L2NORM", "short_conv", "short_conv_bwd", "CONV_SILU"]
 
 # prologue options (the library's GDN2_FLAG_* values)
 FLAG_GATE_LOGITS, FLAG_NEG_EIGVAL, FLAG_QK_L2NORM = 1, 2, 4
@@ -170,6 +170,69 @@ def gated_rmsnorm(o, g, weight, eps=NORM_EPS):
     o, g, weight = _f64(o), _f64(g), _f64(weight)
     rms = np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
     return o / rms * weight * (g * sigmoid(g))
+
+
+CONV_SILU = 1   # the library's GDN2_CONV_SILU
+
+
+def short_conv(x, weight, state=None, silu=False):
+    """The layer's short convolution before the core, fp64.
+
+    burn-gdn2 README, "Architecture" diagram: the projections go through a
+    ShortConv before the L2 norm; "Configuration": use_short_conv = true, a
+    depthwise convolution before the recurrence.  Its width and activation
+    are not on the page.  Reading taken: a causal depthwise convolution over
+    the token axis, one filter of K taps per channel,
+
+        z[t, c] = sum_{i=0}^{K-1} weight[c, i] * x[t - (K-1) + i, c],
+
+    y = z, or z * sigmoid(z) with the SiLU option.  Positions before the
+    first token are read from `state`, the last K-1 inputs before it (oldest
+    first; zeros when None), so that a sequence can be processed in pieces.
+
+    x: [B, T, C]; weight: [C, K]; state: [B, K-1, C] or None.
+    Returns fp64 y [B, T, C] and the state after the last token [B, K-1, C].
+    """
+    x, weight = _f64(x), _f64(weight)
+    B, T, C = x.shape
+    K = weight.shape[1]
+    st = np.zeros((B, K - 1, C)) if state is None else _f64(state)
+    xe = np.concatenate([st, x], axis=1)          # window: x at t - (K-1) + i is xe[t + i]
+    z = np.zeros((B, T, C))
+    for i in range(K):
+        z += weight[:, i] * xe[:, i:i + T, :]
+    y = z * sigmoid(z) if silu else z
+    return y, xe[:, T:, :]
+
+
+def short_conv_bwd(x, weight, dy, state=None, silu=False):
+    """Gradients of sum(dy * y), y = short_conv(x, weight, state, silu)[0], fp64.
+
+    With z the pre-activation and dz = dy (or dy * d silu/dz = dy * s (1 + z (1 - s)),
+    s = sigmoid(z)), every input of the window xe = [state, x] receives
+        d xe[p] = sum_i weight[:, i] * dz[p - i]      (dz = 0 outside [0, T)),
+    and every tap  d weight[c, i] = sum over b, t of dz[b, t, c] * xe[b, t + i, c].
+    Returns dx [B, T, C], dweight [C, K], dstate [B, K-1, C].
+    """
+    x, weight, dy = _f64(x), _f64(weight), _f64(dy)
+    B, T, C = x.shape
+    K = weight.shape[1]
+    st = np.zeros((B, K - 1, C)) if state is None else _f64(state)
+    xe = np.concatenate([st, x], axis=1)
+    z = np.zeros((B, T, C))
+    for i in range(K):
+        z += weight[:, i] * xe[:, i:i + T, :]
+    if silu:
+        s = sigmoid(z)
+        dz = dy * s * (1.0 + z * (1.0 - s))
+    else:
+        dz = dy
+    dxe = np.zeros_like(xe)
+    dw = np.zeros((C, K))
+    for i in range(K):
+        dxe[:, i:i + T, :] += weight[:, i] * dz
+        dw[:, i] = np.sum(dz * xe[:, i:i + T, :], axis=(0, 1))
+    return dxe[:, K - 1:, :], dw, dxe[:, :K - 1, :]
 
 
 def recurrent(q, k, v, alpha, b, w, S0=None):

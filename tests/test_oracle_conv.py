@@ -1,0 +1,156 @@
+"""Pins of the oracle's short convolution and its gradient (CPU only).
+
+burn-gdn2 README (docs.rs), "Architecture" diagram: the projections pass
+through a "ShortConv" before the L2 norm; "Configuration": use_short_conv =
+true, "Depthwise conv before recurrence".  The width and the activation are
+not on the page.  Reading: a causal depthwise convolution over tokens with K
+taps per channel, z[t] = sum_i weight[:, i] x[t - (K-1) + i], y = z or
+z * sigmoid(z), earlier positions read from a carried state of the last K-1
+inputs.  The pins fix it by special filters, numpy's own convolution, streaming
+in pieces, closed forms and central finite differences; planted slips show that
+each kind of mistake is caught.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle.reference import short_conv, short_conv_bwd, sigmoid
+
+
+def _rand(seed, B=2, T=9, C=5, K=4):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((B, T, C)), rng.standard_normal((C, K)),
+            rng.standard_normal((B, K - 1, C)), rng.standard_normal((B, T, C)))
+
+
+def check_identity_filter(f=short_conv):
+    """Only the newest tap set: y = x, whatever the state."""
+    x, _, st, _ = _rand(0)
+    w = np.zeros((5, 4))
+    w[:, 3] = 1.0
+    y, _ = f(x, w, st)
+    np.testing.assert_allclose(y, x, rtol=0, atol=0)
+
+
+def check_delay_filter(f=short_conv):
+    """Only the oldest tap set: y[t] = x[t - 3], the first three from the state."""
+    x, _, st, _ = _rand(1)
+    w = np.zeros((5, 4))
+    w[:, 0] = 1.0
+    y, _ = f(x, w, st)
+    np.testing.assert_allclose(y[:, 3:], x[:, :-3], rtol=0, atol=0)
+    np.testing.assert_allclose(y[:, :3], st, rtol=0, atol=0)
+
+
+def check_numpy_convolve(f=short_conv):
+    """Each channel equals numpy's 'valid' convolution of [state, x] with the reversed taps."""
+    x, w, st, _ = _rand(2)
+    y, _ = f(x, w, st)
+    for b in range(x.shape[0]):
+        for c in range(x.shape[2]):
+            xe = np.concatenate([st[b, :, c], x[b, :, c]])
+            np.testing.assert_allclose(y[b, :, c], np.convolve(xe, w[c, ::-1], mode="valid"), rtol=1e-13, atol=1e-13)
+
+
+def check_streaming(f=short_conv):
+    """Two pieces with the returned state carried = one call, outputs and final state (pieces
+    shorter than the window included)."""
+    x, w, st, _ = _rand(3, T=11)
+    y, s_end = f(x, w, st, silu=True)
+    for cut in (1, 2, 5, 10):
+        y1, s1 = f(x[:, :cut], w, st, silu=True)
+        y2, s2 = f(x[:, cut:], w, s1, silu=True)
+        np.testing.assert_allclose(np.concatenate([y1, y2], axis=1), y, rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(s2, s_end, rtol=0, atol=0)
+    np.testing.assert_allclose(s_end, x[:, -3:], rtol=0, atol=0)
+
+
+def check_zero_state(f=short_conv):
+    """No state = a zero state."""
+    x, w, _, _ = _rand(4)
+    y0, _ = f(x, w, None)
+    y1, _ = f(x, w, np.zeros((2, 3, 5)))
+    np.testing.assert_allclose(y0, y1, rtol=0, atol=0)
+
+
+def check_silu_closed_form(f=short_conv):
+    """Constant input c with a constant state: z = c * sum of taps; with the SiLU
+    option, z = ln 3 gives y = 0.75 ln 3."""
+    c = math.log(3.0)
+    w = np.full((3, 4), 0.25)
+    x = np.full((1, 6, 3), c)
+    st = np.full((1, 3, 3), c)
+    y, _ = f(x, w, st, silu=True)
+    np.testing.assert_allclose(y, 0.75 * math.log(3.0), rtol=1e-14, atol=0)
+    y, _ = f(x, 2.0 * w, st, silu=False)
+    np.testing.assert_allclose(y, 2.0 * c, rtol=1e-14, atol=0)
+
+
+PINS = [check_identity_filter, check_delay_filter, check_numpy_convolve, check_streaming, check_zero_state,
+        check_silu_closed_form]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
+def test_short_conv_pins(pin):
+    pin()
+
+
+@pytest.mark.parametrize("silu", [False, True])
+@pytest.mark.parametrize("K", [1, 2, 4])
+def test_short_conv_bwd_finite_differences(silu, K):
+    """dx, dweight and dstate against central differences of sum(dy * y) for every element."""
+    x, w, st, dy = _rand(5, B=2, T=6, C=3, K=K)
+    dx, dw, dst = short_conv_bwd(x, w, dy, st, silu)
+    loss = lambda x_, w_, s_: float(np.sum(dy * short_conv(x_, w_, s_, silu)[0]))
+    h = 1e-6
+    for arr, grad in ((x, dx), (w, dw), (st, dst)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + h
+            lp = loss(x, w, st)
+            arr[idx] = old - h
+            lm = loss(x, w, st)
+            arr[idx] = old
+            num[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-7)
+
+
+# ---- planted slips: each must fail at least one pin --------------------------------------
+def _slip_reversed(x, weight, state=None, silu=False):
+    return short_conv(x, np.asarray(weight)[:, ::-1], state, silu)
+
+
+def _slip_no_state(x, weight, state=None, silu=False):
+    return short_conv(x, weight, None, silu)
+
+
+def _slip_off_by_one(x, weight, state=None, silu=False):
+    y, s = short_conv(x, weight, state, silu)
+    return np.concatenate([y[:, :1], y[:, :-1]], axis=1), s
+
+
+def _slip_silu_on_input(x, weight, state=None, silu=False):
+    x = np.asarray(x, dtype=np.float64)
+    if silu:
+        x = x * sigmoid(x)
+        state = None if state is None else np.asarray(state) * sigmoid(np.asarray(state))
+    return short_conv(x, weight, state, False)
+
+
+def _slip_state_not_carried(x, weight, state=None, silu=False):
+    y, s = short_conv(x, weight, state, silu)
+    return y, np.zeros_like(s)
+
+
+@pytest.mark.parametrize("slip", [_slip_reversed, _slip_no_state, _slip_off_by_one, _slip_silu_on_input,
+                                  _slip_state_not_carried], ids=lambda f: f.__name__)
+def test_short_conv_slips_rejected(slip):
+    failed = 0
+    for pin in PINS:
+        try:
+            pin(slip)
+        except AssertionError:
+            failed += 1
+    assert failed >= 1
