@@ -3,7 +3,7 @@
 Python face of the C ABI in ``include/gdn2.h`` (``libgdn2.so`` in this
 directory): the chunked forward and the fused recurrent / decode step of the
 GDN-2 recurrence (also over packed variable-length batches and with grouped
-value heads), the output step, with hand-written HIP kernels doing all the
+value heads), the output step, the short convolution of the prologue, with hand-written HIP kernels doing all the
 arithmetic.
 The library is loaded on first use; a missing library raises.
 """
@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     FLAG_GATE_LOGITS,
     FLAG_NEG_EIGVAL,
     FLAG_QK_L2NORM,
+    CONV_SILU,
     Gdn2Error,
     Problem,
     abi_version,
@@ -28,5 +29,8 @@ from ._binding import (  # noqa: F401
     problem,
     recurrent_step,
     recurrent_varlen,
+    short_conv,
+    short_conv_bwd,
+    short_conv_bwd_workspace_size,
     status_str,
 )

@@ -16,15 +16,17 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn2.so")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 GDN2_F32, GDN2_BF16 = 0, 1
 FLAG_GATE_LOGITS, FLAG_NEG_EIGVAL, FLAG_QK_L2NORM = 1, 2, 4
+CONV_SILU = 1
 _STATUS = {0: "GDN2_OK", 1: "GDN2_ERR_NULL", 2: "GDN2_ERR_SHAPE", 3: "GDN2_ERR_DTYPE",
            4: "GDN2_ERR_ALIAS", 5: "GDN2_ERR_WORKSPACE", 6: "GDN2_ERR_DEVICE", 7: "GDN2_ERR_ALIGN"}
 EXPORTED = ("gdn2_abi_version", "gdn2_status_str", "gdn2_chunk_fwd_workspace_size",
             "gdn2_chunk_fwd", "gdn2_chunk_prep", "gdn2_chunk_state", "gdn2_recurrent_step",
             "gdn2_gated_rmsnorm", "gdn2_chunk_fwd_varlen_workspace_size", "gdn2_chunk_fwd_varlen",
-            "gdn2_recurrent_varlen", "gdn2_chunk_bwd_workspace_size", "gdn2_chunk_bwd")
+            "gdn2_recurrent_varlen", "gdn2_chunk_bwd_workspace_size", "gdn2_chunk_bwd",
+            "gdn2_short_conv", "gdn2_short_conv_bwd_workspace_size", "gdn2_short_conv_bwd")
 
 
 class Problem(ctypes.Structure):
@@ -83,6 +85,13 @@ def lib():
         L.gdn2_chunk_bwd_workspace_size.argtypes = [P]
         L.gdn2_chunk_bwd.restype = ctypes.c_int
         L.gdn2_chunk_bwd.argtypes = [P] + [vp] * 16 + [vp, sz, vp]
+        i64, i32 = ctypes.c_int64, ctypes.c_int32
+        L.gdn2_short_conv.restype = ctypes.c_int
+        L.gdn2_short_conv.argtypes = [i64] * 3 + [i32] * 3 + [vp] * 5 + [vp]
+        L.gdn2_short_conv_bwd_workspace_size.restype = sz
+        L.gdn2_short_conv_bwd_workspace_size.argtypes = [i64] * 3 + [i32]
+        L.gdn2_short_conv_bwd.restype = ctypes.c_int
+        L.gdn2_short_conv_bwd.argtypes = [i64] * 3 + [i32] * 3 + [vp] * 7 + [vp, sz, vp]
         if L.gdn2_abi_version() != ABI_VERSION:   # the Problem mirror must match the library's struct
             raise ImportError(f"{LIB_PATH} has ABI {L.gdn2_abi_version()}, this binding expects {ABI_VERSION}: "
                               "rebuild it")
@@ -332,3 +341,60 @@ def gated_rmsnorm(o, g, weight, *, out=None, inplace: bool = False):
     p = problem(B, T, H, 16, dv, o.dtype)
     _check(lib().gdn2_gated_rmsnorm(ctypes.byref(p), _ptr(o), _ptr(g), _ptr(weight), _ptr(y), _stream(dev)))
     return y
+
+
+def _conv_check(x, weight, state, what="x"):
+    if x.dim() != 3:
+        raise ValueError(f"{what} must be [B,T,C]")
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"{what} must be float32 or bfloat16")
+    B, T, C = x.shape
+    if weight.dim() != 2 or weight.shape[0] != C or weight.dtype != torch.float32:
+        raise ValueError(f"weight must be float32 [{C}, K]")
+    K = weight.shape[1]
+    if state is not None and (tuple(state.shape) != (B, K - 1, C) or state.dtype != x.dtype):
+        raise ValueError(f"state must be [{B}, {K - 1}, {C}] of the dtype of {what}")
+    dev = x.device
+    for name, t in ((what, x), ("weight", weight), ("state", state)):
+        if t is not None and (t.device != dev or dev.type != "cuda" or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous GPU tensor on {dev}")
+    return B, T, C, K, dev, (GDN2_BF16 if x.dtype == torch.bfloat16 else GDN2_F32)
+
+
+def short_conv(x, weight, state=None, *, silu: bool = False, want_state: bool = True, out=None,
+               state_out=None):
+    """Short convolution (``gdn2_short_conv``): causal depthwise over tokens,
+    y[t] = sum_i weight[:, i] * xe[t - (K-1) + i] (then z * sigmoid(z) with ``silu``),
+    xe reading ``state`` [B, K-1, C] before the first token (None = zeros).
+    x: [B, T, C] float32 or bfloat16 (C a multiple of 8); weight: [C, K] float32, K <= 8.
+    Returns (y, new state [B, K-1, C] or None); ``state_out=state`` updates it in place."""
+    B, T, C, K, dev, code = _conv_check(x, weight, state)
+    y = torch.empty_like(x) if out is None else out
+    so = None
+    if want_state:
+        so = state_out if state_out is not None else torch.empty((B, K - 1, C), dtype=x.dtype, device=dev)
+    _check(lib().gdn2_short_conv(B, T, C, K, CONV_SILU if silu else 0, code, _ptr(x), _ptr(weight), _ptr(state),
+                                 _ptr(y), _ptr(so) if K > 1 else None, _stream(dev)))
+    return y, so
+
+
+def short_conv_bwd_workspace_size(B, T, C, K) -> int:
+    return int(lib().gdn2_short_conv_bwd_workspace_size(B, T, C, K))
+
+
+def short_conv_bwd(x, weight, dy, state=None, *, silu: bool = False, want_dstate: bool = True, workspace=None):
+    """Gradient of :func:`short_conv` (``gdn2_short_conv_bwd``) given dy = dL/dy.
+    Returns (dx, dweight [C, K] float32, dstate [B, K-1, C] or None)."""
+    B, T, C, K, dev, code = _conv_check(x, weight, state)
+    if tuple(dy.shape) != (B, T, C) or dy.dtype != x.dtype or dy.device != dev or not dy.is_contiguous():
+        raise ValueError("dy must be a contiguous GPU tensor shaped and typed like x")
+    dx = torch.empty_like(x)
+    dw = torch.empty((C, K), dtype=torch.float32, device=dev)
+    ds = torch.empty((B, K - 1, C), dtype=x.dtype, device=dev) if want_dstate else None
+    need = short_conv_bwd_workspace_size(B, T, C, K)
+    if workspace is None:
+        workspace = alloc_workspace(need, dev)
+    _check(lib().gdn2_short_conv_bwd(B, T, C, K, CONV_SILU if silu else 0, code, _ptr(x), _ptr(weight), _ptr(state),
+                                     _ptr(dy), _ptr(dx), _ptr(dw), _ptr(ds) if K > 1 else None,
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev)))
+    return dx, dw, ds

@@ -21,7 +21,7 @@ OBJDIR = os.path.join(HERE, "_build")
 
 SOURCES = ["gdn2_api.cpp", "gdn2_recurrent.hip", "gdn2_chunk.hip", "gdn2_epilogue.hip", "gdn2_varlen.hip",
            "gdn2_backward.hip", "gdn2_backward_mf.hip",
-           "gdn2_backward_prologue.hip"]
+           "gdn2_backward_prologue.hip", "gdn2_conv.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",

@@ -639,4 +639,80 @@ int gdn2_gated_rmsnorm(const gdn2_problem* p, const void* o, const void* g, cons
     return launch_status(gdn2::launch_gated_rmsnorm(a, is_bf16(p), static_cast<hipStream_t>(stream)));
 }
 
+// sizes of the short convolution; a non-zero return is the status
+static int conv_check(int64_t B, int64_t T, int64_t C, int32_t K, int32_t flags, int32_t io_dtype)
+{
+    if (B < 0 || T < 0 || C <= 0 || B > kMaxDim || T > kMaxDim || C > kMaxDim) return GDN2_ERR_SHAPE;
+    if (C % 8 != 0 || K < 1 || K > 8 || (flags & ~GDN2_CONV_SILU) != 0) return GDN2_ERR_SHAPE;
+    // every element count and the forward's thread count must fit in 32 bits of workgroups
+    const double n = (double)B * (double)T * (double)C;
+    if (n > 1e15 || n / (gdn2::kConvTileF * 4) > 4.0e9) return GDN2_ERR_SHAPE;
+    if (io_dtype != GDN2_F32 && io_dtype != GDN2_BF16) return GDN2_ERR_DTYPE;
+    return GDN2_OK;
+}
+
+static int64_t conv_spans(int64_t T) { return T == 0 ? 1 : (T + gdn2::kConvSpan - 1) / gdn2::kConvSpan; }
+
+int gdn2_short_conv(int64_t B, int64_t T, int64_t C, int32_t K, int32_t flags, int32_t io_dtype,
+                    const void* x, const float* weight, const void* state_in,
+                    void* y, void* state_out, void* stream)
+{
+    int st = conv_check(B, T, C, K, flags, io_dtype);
+    if (st) return st;
+    if (K == 1) state_in = state_out = nullptr;
+    const int64_t es = io_dtype == GDN2_BF16 ? 2 : 4;
+    int64_t ntile = (T + gdn2::kConvTileF - 1) / gdn2::kConvTileF;
+    if (ntile == 0 && state_out != nullptr) ntile = 1;
+    if (B == 0 || ntile == 0) return GDN2_OK;
+    if (!weight) return GDN2_ERR_NULL;
+    if (T > 0 && (!x || !y)) return GDN2_ERR_NULL;
+    const int64_t xb = B * T * C * es, sb = B * (K - 1) * C * es;
+    const Range ins[3] = {range_of(x, xb), range_of(weight, C * K * 4), range_of(state_in, sb)};
+    const Range outs[2] = {range_of(y, xb), range_of(state_out, sb)};
+    st = check_alias(outs, 2, ins, 3, state_in, state_out, 2, 1);
+    if (st) return st;
+    st = check_align({x, weight, state_in, y, state_out});
+    if (st) return st;
+    st = device_ready();
+    if (st) return st;
+    gdn2::ConvArgs a{x, weight, state_in, y, state_out, B, T, C, ntile};
+    return launch_status(gdn2::launch_short_conv(a, K, (flags & GDN2_CONV_SILU) != 0, io_dtype == GDN2_BF16,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+size_t gdn2_short_conv_bwd_workspace_size(int64_t B, int64_t T, int64_t C, int32_t K)
+{
+    if (conv_check(B, T, C, K, 0, GDN2_F32) != GDN2_OK) return 0;
+    return (size_t)(B * conv_spans(T) * C * K) * sizeof(float);
+}
+
+int gdn2_short_conv_bwd(int64_t B, int64_t T, int64_t C, int32_t K, int32_t flags, int32_t io_dtype,
+                        const void* x, const float* weight, const void* state_in, const void* dy,
+                        void* dx, float* dweight, void* dstate_in,
+                        void* workspace, size_t workspace_bytes, void* stream)
+{
+    int st = conv_check(B, T, C, K, flags, io_dtype);
+    if (st) return st;
+    if (K == 1) state_in = dstate_in = nullptr;
+    if (!weight || !dweight) return GDN2_ERR_NULL;
+    if (B > 0 && T > 0 && (!x || !dy || !dx)) return GDN2_ERR_NULL;
+    const size_t need = gdn2_short_conv_bwd_workspace_size(B, T, C, K);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GDN2_ERR_WORKSPACE;
+    const int64_t es = io_dtype == GDN2_BF16 ? 2 : 4;
+    const int64_t xb = B * T * C * es, sb = B * (K - 1) * C * es;
+    const Range ins[4] = {range_of(x, xb), range_of(weight, C * K * 4), range_of(state_in, sb), range_of(dy, xb)};
+    const Range outs[4] = {range_of(dx, xb), range_of(dweight, C * K * 4), range_of(dstate_in, sb),
+                           range_of(workspace, (int64_t)need)};
+    st = check_alias(outs, 4, ins, 4, nullptr, nullptr, -1, -1);
+    if (st) return st;
+    st = check_align({x, weight, state_in, dy, dx, dweight, dstate_in, workspace});
+    if (st) return st;
+    st = device_ready();
+    if (st) return st;
+    gdn2::ConvBwdArgs a{x, weight, state_in, dy, dx, dweight, dstate_in, static_cast<float*>(workspace),
+                        B, T, C, conv_spans(T)};
+    return launch_status(gdn2::launch_short_conv_bwd(a, K, (flags & GDN2_CONV_SILU) != 0, io_dtype == GDN2_BF16,
+                                                     static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -126,12 +126,35 @@ struct NormArgs {
     int64_t rows; int dv; float inv_dv; float eps;
 };
 
+// short convolution: a forward tile is kConvTileF tokens of 4 channels a
+// lane; a backward workgroup takes a kConvSpan-token span of one sequence in
+// tiles of kConvTileB and writes one fp32 [C][K] row of weight partials
+constexpr int kConvTileF = 16;
+constexpr int kConvTileB = 8;
+constexpr int kConvSpan = 256;
+
+struct ConvArgs {
+    const void* x; const float* weight; const void* state_in; void* y; void* state_out;
+    int64_t B, T, C;
+    int64_t ntile;        // forward tiles a sequence (at least 1 when the state is written)
+};
+
+struct ConvBwdArgs {
+    const void* x; const float* weight; const void* state_in; const void* dy;
+    void* dx; float* dweight; void* dstate; float* part;
+    int64_t B, T, C;
+    int64_t nspan;        // spans a sequence (at least 1)
+};
+
 // Each returns hipSuccess or the launch error.  bf16 selects the I/O dtype,
 // gbf16 the gate dtype (bf16 gates only with bf16 I/O).
 hipError_t launch_chunk_prep(const PrepArgs& a, int dk, bool bf16, bool gbf16, hipStream_t s);
 hipError_t launch_chunk_state(const StateArgs& a, int dk, int vs, bool bf16, hipStream_t s);
 hipError_t launch_recurrent(const RecArgs& a, int dk, int vs, bool bf16, bool gbf16, hipStream_t s);
 hipError_t launch_gated_rmsnorm(const NormArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_short_conv(const ConvArgs& a, int K, bool silu, bool bf16, hipStream_t s);
+// the gradient launch, then the fixed-order sum of the weight partials
+hipError_t launch_short_conv_bwd(const ConvBwdArgs& a, int K, bool silu, bool bf16, hipStream_t s);
 hipError_t launch_varlen_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_chunk_state_bwd(const BwdStateArgs& a, bool bf16, hipStream_t s);
 // the same on the matrix-core path (bf16, dk in {32, 64, 128}, dv in {32, 64,

@@ -84,7 +84,7 @@
 extern "C" {
 #endif
 
-#define GDN2_ABI_VERSION 3
+#define GDN2_ABI_VERSION 4
 
 typedef enum {
     GDN2_OK = 0,
@@ -104,6 +104,8 @@ enum {
     GDN2_FLAG_NEG_EIGVAL = 2,    /* b = 2 * sigmoid(b) (requires GATE_LOGITS)     */
     GDN2_FLAG_QK_L2NORM = 4      /* L2-normalise q and k over dk in-kernel        */
 };
+
+enum { GDN2_CONV_SILU = 1 };     /* gdn2_short_conv: y = z * sigmoid(z)          */
 
 /* Problem description (plain old data; 64 bytes). */
 typedef struct {
@@ -282,6 +284,66 @@ int gdn2_chunk_bwd(const gdn2_problem* p,
  */
 int gdn2_gated_rmsnorm(const gdn2_problem* p, const void* o, const void* g, const float* weight,
                        void* y, void* stream);
+
+/*
+ * Short convolution of the layer's prologue (README "Architecture": the q, k
+ * and v projections pass through a "ShortConv" before the L2 norm;
+ * "Configuration": use_short_conv, a depthwise convolution before the
+ * recurrence).  The README gives neither the width nor the activation; this
+ * library reads it as a causal depthwise convolution over tokens with K taps
+ * per channel and an optional SiLU:
+ *
+ *     z[b,t,c] = sum_{i<K} weight[c,i] * xe[b, t-(K-1)+i, c]
+ *     y = z, or z * sigmoid(z) with GDN2_CONV_SILU
+ *
+ * where xe reads x at positions >= 0 and, at the K-1 positions before the
+ * first token, the carried state: xe[b, -(K-1)+j, c] = state_in[b, j, c]
+ * (zeros when state_in is NULL).  state_out, when not NULL, receives the
+ * last K-1 positions of xe (the window a following call continues from), so
+ * that calls on consecutive pieces of a sequence equal one call on the whole.
+ *
+ * Shapes and dtypes: x, y: [B, T, C]; state_in, state_out: [B, K-1, C],
+ * all in io_dtype (gdn2_dtype; the state holds inputs and is copied
+ * exactly); weight: [C, K] fp32.  All arithmetic is fp32.  B, T >= 0,
+ * C > 0 a multiple of 8, 1 <= K <= 8 (with K == 1 the state pointers are
+ * ignored); flags is 0 or GDN2_CONV_SILU.  A concatenated [B, T, C] tensor
+ * of the q, k and v projections is convolved in one call.
+ * Aliasing: y must not overlap any input (tiles read their neighbours'
+ * inputs); state_out may equal state_in exactly (in-place update), any
+ * other overlap is GDN2_ERR_ALIAS.  16-byte alignment, errors, streams and
+ * ownership as for every other call.  One launch on `stream`.
+ */
+int gdn2_short_conv(int64_t B, int64_t T, int64_t C, int32_t K, int32_t flags, int32_t io_dtype,
+                    const void* x, const float* weight, const void* state_in,
+                    void* y, void* state_out, void* stream);
+
+/*
+ * Bytes of workspace gdn2_short_conv_bwd needs (0 for invalid sizes): one
+ * fp32 [C, K] row of partial weight gradients per (sequence, 256-token span).
+ */
+size_t gdn2_short_conv_bwd_workspace_size(int64_t B, int64_t T, int64_t C, int32_t K);
+
+/*
+ * Gradient of gdn2_short_conv given dy = dL/dy (same shapes, dtypes and
+ * flags; state_in as in the forward, NULL = zeros):
+ *
+ *     dz = dy, or dy * s * (1 + z * (1 - s)), s = sigmoid(z)   (SiLU)
+ *     dxe[b,p,c] = sum_i weight[c,i] * dz[b, p+(K-1)-i, c]  over 0 <= p+(K-1)-i < T
+ *     dweight[c,i] = sum_{b,t} dz[b,t,c] * xe[b, t-(K-1)+i, c]
+ *
+ * dx = dxe at positions >= 0; dstate_in (NULL = not wanted) = dxe at the K-1
+ * positions before the first token, the gradient with respect to state_in
+ * (also when state_in is NULL, i.e. zero).  The loss is taken not to depend on
+ * state_out.  dx, dstate_in: io_dtype; dweight: fp32 [C, K], summed in a
+ * fixed order (the result does not depend on scheduling).  Outputs and the
+ * workspace (16-byte aligned, at least gdn2_short_conv_bwd_workspace_size
+ * bytes) must not overlap any input or each other.  Two launches on `stream`
+ * (gradients with per-span weight partials, then the fixed-order sum).
+ */
+int gdn2_short_conv_bwd(int64_t B, int64_t T, int64_t C, int32_t K, int32_t flags, int32_t io_dtype,
+                        const void* x, const float* weight, const void* state_in, const void* dy,
+                        void* dx, float* dweight, void* dstate_in,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }
