@@ -646,7 +646,7 @@ static int conv_check(int64_t B, int64_t T, int64_t C, int32_t K, int32_t flags,
     if (C % 8 != 0 || K < 1 || K > 8 || (flags & ~GDN2_CONV_SILU) != 0) return GDN2_ERR_SHAPE;
     // every element count and the forward's thread count must fit in 32 bits of workgroups
     const double n = (double)B * (double)T * (double)C;
-    if (n > 1e15 || n / (gdn2::kConvTileF * 4) > 4.0e9) return GDN2_ERR_SHAPE;
+    if (n > 1e15 || n / (32.0 * 256.0) > 2.0e9) return GDN2_ERR_SHAPE;
     if (io_dtype != GDN2_F32 && io_dtype != GDN2_BF16) return GDN2_ERR_DTYPE;
     return GDN2_OK;
 }
@@ -661,7 +661,8 @@ int gdn2_short_conv(int64_t B, int64_t T, int64_t C, int32_t K, int32_t flags, i
     if (st) return st;
     if (K == 1) state_in = state_out = nullptr;
     const int64_t es = io_dtype == GDN2_BF16 ? 2 : 4;
-    int64_t ntile = (T + gdn2::kConvTileF - 1) / gdn2::kConvTileF;
+    const int64_t span = gdn2::kConvSpanF(io_dtype == GDN2_BF16);
+    int64_t ntile = (T + span - 1) / span;
     if (ntile == 0 && state_out != nullptr) ntile = 1;
     if (B == 0 || ntile == 0) return GDN2_OK;
     if (!weight) return GDN2_ERR_NULL;

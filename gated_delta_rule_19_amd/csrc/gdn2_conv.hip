@@ -6,21 +6,21 @@
 //
 //   z[t, c] = sum_i w[c, i] xe[t - (K-1) + i, c],   y = z or z * sigmoid(z)
 //
-// Layout [B, T, C], channels fastest.  A lane takes 4 adjacent channels, so a
-// wave reads 256 channels of one token row per access (1 KB fp32, 512 B
-// bf16), and a tile of consecutive tokens together with the K-1 earlier
-// positions it also needs; a tile issues all its loads before the
-// arithmetic.  No contraction is large enough for the matrix cores (K <= 8
-// taps a channel): both directions are HBM-bound, x and y (forward) or x, dy
-// and dx (backward) crossing HBM once, the overlapping rows of neighbouring
-// tiles mostly hitting in L2.
+// Layout [B, T, C], channels fastest.  No contraction is large enough for the
+// matrix cores (K <= 8 taps a channel): both directions are HBM-bound, x and
+// y (forward) or x, dy and dx (backward) crossing HBM once.  A workgroup takes
+// a block of 256 channels over a span of tokens: it first stages the span's
+// rows (with the K-1 earlier positions, and for the backward the K-1 later
+// ones) into LDS in 16-byte pieces, every load of the span issued before the
+// first is used, so that a wave keeps many kilobytes in flight without
+// holding them in registers; then each lane takes 4 channels of a quarter of
+// the span from LDS.
 //
-// Backward: a workgroup takes 256 channels of one 256-token span of one
-// sequence; each wave walks 8 tiles of 8 tokens, recomputing z where the SiLU
-// needs it, and writes dx (and, for the first tile of a sequence, the
-// gradient of the carried state).  The weight gradient of a span is summed
-// over its waves in LDS in a fixed order and written as one partial row; a
-// second launch adds the rows in a fixed order, so dweight is reproducible.
+// Backward: a workgroup walks the sub-spans of a 128-token span, recomputing
+// z where the SiLU needs it, writes dx (and, at the start of a sequence, the
+// gradient of the carried state), and sums the span's weight gradient over
+// its waves in LDS in a fixed order into one partial row; a second launch
+// adds the rows in a fixed order, so dweight is reproducible.
 #include "gdn2_device.hpp"
 #include "gdn2_launch.hpp"
 
@@ -28,9 +28,13 @@ namespace gdn2 {
 
 constexpr int kConvCh = 4;                        // channels a lane
 constexpr int kConvWaves = kThreads / 64;
-constexpr int kConvTilesB = kConvSpan / (kConvWaves * kConvTileB);   // tiles a wave walks
+constexpr int kConvBlk = 64 * kConvCh;            // channels a workgroup
 
-static_assert(kConvTilesB * kConvWaves * kConvTileB == kConvSpan, "span must split into tiles");
+// rows of the channel block in LDS: 16-byte pieces of EPC elements
+template <typename Tio> struct ConvRow {
+    static constexpr int EPC = 16 / (int)sizeof(Tio);
+    static constexpr int CHR = kConvBlk / EPC;    // pieces a row
+};
 
 // row of xe at token position p for the 4 channels at x / st: x past the end
 // and a missing state read as zero
@@ -43,6 +47,57 @@ __device__ inline f32x4 conv_row(const Tio* x, const Tio* st, int64_t T, int64_t
         return ld_vec4(st + (p + K - 1) * C);
     }
     return f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// Stage NA rows of xe from position pa (x, the carried state before 0) and NB
+// rows of a second tensor from position pb (zero outside [0, T)) for channels
+// [c_lo, c_lo + 256) into LDS rows of 256 elements (zero past C).  Loads go
+// out in batches of up to kConvBatch 16-byte pieces a thread, every load of a
+// batch issued before its LDS writes.  x, st and y2 point at the sequence's
+// base.
+constexpr int kConvBatch = 10;
+
+template <typename Tio, int K, int NA, int NB>
+__device__ inline void conv_stage(Tio* lds, const Tio* x, const Tio* st, const Tio* y2, int64_t pa, int64_t pb,
+                                  int64_t T, int64_t C, int64_t c_lo)
+{
+    constexpr int CHR = ConvRow<Tio>::CHR, EPC = ConvRow<Tio>::EPC;
+    constexpr int N = (NA + NB) * CHR, PER = (N + kThreads - 1) / kThreads;
+    constexpr int NB_ = (PER + kConvBatch - 1) / kConvBatch, BATCH = (PER + NB_ - 1) / NB_;
+    typedef int __attribute__((ext_vector_type(4))) i32x4;
+#pragma unroll
+    for (int j0 = 0; j0 < PER; j0 += BATCH) {
+        i32x4 v[BATCH];
+#pragma unroll
+        for (int jj = 0; jj < BATCH; ++jj) {
+            const int id = threadIdx.x + (j0 + jj) * kThreads;
+            v[jj] = i32x4{0, 0, 0, 0};
+            const int row = id / CHR;
+            const int64_t ch = c_lo + (int64_t)(id % CHR) * EPC;
+            if (j0 + jj < PER && id < N && ch < C) {
+                const Tio* src = nullptr;
+                if (row < NA) {
+                    const int64_t p = pa + row;
+                    if (p >= 0) {
+                        if (p < T) src = x + p * C + ch;
+                    } else if (st != nullptr) {
+                        src = st + (p + K - 1) * C + ch;
+                    }
+                } else {
+                    const int64_t p = pb + (row - NA);
+                    if (p >= 0 && p < T) src = y2 + p * C + ch;
+                }
+                if (src != nullptr) v[jj] = *reinterpret_cast<const i32x4*>(src);
+            }
+        }
+#pragma unroll
+        for (int jj = 0; jj < BATCH; ++jj) {
+            const int id = threadIdx.x + (j0 + jj) * kThreads;
+            if (j0 + jj < PER && id < N) reinterpret_cast<i32x4*>(lds)[id] = v[jj];
+        }
+        // keep the next batch's loads (and their registers) after these writes
+        __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 // taps of the 4 channels from c0: w[i] holds tap i of each ([C][K] fp32 rows)
@@ -63,41 +118,49 @@ __device__ inline void conv_taps(const float* weight, int64_t c0, f32x4 (&w)[K])
 template <typename Tio, int K, bool SILU>
 __global__ __launch_bounds__(kThreads) void k_short_conv(ConvArgs a)
 {
-    constexpr int TT = kConvTileF;
-    constexpr int NR = TT + K - 1;
-    const int64_t C4 = a.C / kConvCh;
-    const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (gid >= a.B * a.ntile * C4) return;
-    const int64_t c0 = (gid % C4) * kConvCh;
-    const int64_t rest = gid / C4;
-    const int64_t tile = rest % a.ntile, b = rest / a.ntile;
-    const int64_t t0 = tile * TT, T = a.T, C = a.C;
-    const Tio* x = static_cast<const Tio*>(a.x) + b * T * C + c0;
-    const Tio* st = a.state_in ? static_cast<const Tio*>(a.state_in) + b * (K - 1) * C + c0 : nullptr;
+    constexpr int S = kConvSpanF(sizeof(Tio) == 2);   // tokens a workgroup
+    constexpr int TW = S / kConvWaves;                 // tokens a wave
+    constexpr int NR = S + K - 1;                      // staged rows from s0 - (K-1)
+    __shared__ __align__(16) Tio lds[NR * kConvBlk];
 
-    f32x4 r[NR];
-#pragma unroll
-    for (int j = 0; j < NR; ++j) r[j] = conv_row<Tio, K>(x, st, T, C, t0 - (K - 1) + j);
-    // the carried window for a following call: only the first tile of a
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t C4 = a.C / kConvCh, ncb = (C4 + 63) / 64;
+    int64_t blk = blockIdx.x;
+    const int64_t cb = blk % ncb;
+    blk /= ncb;
+    const int64_t span = blk % a.ntile, b = blk / a.ntile;
+    const int64_t T = a.T, C = a.C, s0 = span * S;
+    const int64_t c0 = (cb * 64 + lane) * kConvCh;
+    const bool active = c0 < C;
+    const Tio* x = static_cast<const Tio*>(a.x) + b * T * C;
+    const Tio* st = a.state_in ? static_cast<const Tio*>(a.state_in) + b * (K - 1) * C : nullptr;
+
+    conv_stage<Tio, K, NR, 0>(lds, x, st, nullptr, s0 - (K - 1), 0, T, C, cb * kConvBlk);
+    // the carried window for a following call: only the first span of a
     // sequence reads the state, so it alone writes the new one, after its reads
-    const bool keep = K > 1 && a.state_out != nullptr && tile == 0;
+    const bool keep = K > 1 && a.state_out != nullptr && span == 0 && wave == 0 && active;
     f32x4 so[K > 1 ? K - 1 : 1];
     if (keep) {
 #pragma unroll
-        for (int j = 0; j < K - 1; ++j) so[j] = conv_row<Tio, K>(x, st, T, C, T - (K - 1) + j);
+        for (int j = 0; j < K - 1; ++j)
+            so[j] = conv_row<Tio, K>(x + c0, st ? st + c0 : nullptr, T, C, T - (K - 1) + j);
     }
-    f32x4 w[K];
-    conv_taps<K>(a.weight, c0, w);
-
-    Tio* y = static_cast<Tio*>(a.y) + b * T * C + c0;
+    __syncthreads();
+    if (active) {
+        f32x4 w[K];
+        conv_taps<K>(a.weight, c0, w);
+        const Tio* row = lds + lane * kConvCh;
+        Tio* y = static_cast<Tio*>(a.y) + b * T * C + c0;
 #pragma unroll
-    for (int t = 0; t < TT; ++t) {
-        if (t0 + t < T) {
-            f32x4 z = w[0] * r[t];
+        for (int t = 0; t < TW; ++t) {
+            const int l = wave * TW + t;
+            if (s0 + l < T) {
+                f32x4 z = w[0] * ld_vec4(row + l * kConvBlk);
 #pragma unroll
-            for (int i = 1; i < K; ++i) z += w[i] * r[t + i];
-            if (SILU) z = z * sigmoid4(z);
-            st_vec4(y + (t0 + t) * C, z);
+                for (int i = 1; i < K; ++i) z += w[i] * ld_vec4(row + (l + i) * kConvBlk);
+                if (SILU) z = z * sigmoid4(z);
+                st_vec4(y + (s0 + l) * C, z);
+            }
         }
     }
     if (keep) {
@@ -108,11 +171,18 @@ __global__ __launch_bounds__(kThreads) void k_short_conv(ConvArgs a)
 }
 
 template <typename Tio, int K, bool SILU>
-__global__ __launch_bounds__(kThreads) void k_short_conv_bwd(ConvBwdArgs a)
+__global__ __launch_bounds__(kThreads, K <= 4 ? 2 : 1) void k_short_conv_bwd(ConvBwdArgs a)
 {
-    constexpr int TT = kConvTileB;
-    constexpr int NX = SILU ? TT + 2 * K - 2 : TT + K - 1;   // xe rows from t0 - (K-1)
-    constexpr int ND = TT + K - 1;                           // dz rows from t0
+    constexpr int S = 32;                              // tokens a sub-span
+    constexpr int NSUB = kConvSpan / S;
+    constexpr int TW = S / kConvWaves;                 // tokens a wave
+    constexpr int TT = 8;                              // tokens a pass
+    constexpr int XR = SILU ? S + 2 * K - 2 : S + K - 1;   // staged xe rows from s0 - (K-1)
+    constexpr int DR = S + K - 1;                          // staged dy rows from s0
+    constexpr int NX = SILU ? TT + 2 * K - 2 : TT + K - 1;
+    constexpr int ND = TT + K - 1;
+    static_assert(NSUB * S == kConvSpan && TW % TT == 0, "span must split into passes");
+    __shared__ __align__(16) Tio lds[(XR + DR) * kConvBlk];
     __shared__ f32x4 red[kConvWaves - 1][K][64];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -121,35 +191,38 @@ __global__ __launch_bounds__(kThreads) void k_short_conv_bwd(ConvBwdArgs a)
     const int64_t cb = blk % ncb;
     blk /= ncb;
     const int64_t span = blk % a.nspan, b = blk / a.nspan;
-    const int64_t c4 = cb * 64 + lane;
-    const bool active = c4 < C4;
-    const int64_t c0 = c4 * kConvCh, T = a.T, C = a.C;
+    const int64_t T = a.T, C = a.C;
+    const int64_t c0 = (cb * 64 + lane) * kConvCh;
+    const bool active = c0 < C;
+    const Tio* x = static_cast<const Tio*>(a.x) + b * T * C;
+    const Tio* st = a.state_in ? static_cast<const Tio*>(a.state_in) + b * (K - 1) * C : nullptr;
+    const Tio* dy = static_cast<const Tio*>(a.dy) + b * T * C;
 
-    // acc[i]: weight gradient of tap i for the 4 channels
-    f32x4 acc[K];
+    f32x4 w[K], acc[K];   // acc[i]: weight gradient of tap i for the 4 channels
 #pragma unroll
     for (int i = 0; i < K; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (active) conv_taps<K>(a.weight, c0, w);
 
-    if (active) {
-        f32x4 w[K];
-        conv_taps<K>(a.weight, c0, w);
-        const Tio* x = static_cast<const Tio*>(a.x) + b * T * C + c0;
-        const Tio* st = a.state_in ? static_cast<const Tio*>(a.state_in) + b * (K - 1) * C + c0 : nullptr;
-        const Tio* dy = static_cast<const Tio*>(a.dy) + b * T * C + c0;
-        Tio* dx = static_cast<Tio*>(a.dx) + b * T * C + c0;
+    const Tio* xrow = lds + lane * kConvCh;
+    const Tio* drow = lds + XR * kConvBlk + lane * kConvCh;
 #pragma unroll 1
-        for (int n = 0; n < kConvTilesB; ++n) {
-            const int64_t t0 = span * kConvSpan + (int64_t)(wave * kConvTilesB + n) * TT;
-            const bool first = t0 == 0;   // also runs when T == 0, for the state's gradient
-            if (t0 >= T && !first) break;
+    for (int n = 0; n < NSUB; ++n) {
+        const int64_t s0 = span * kConvSpan + (int64_t)n * S;
+        if (s0 >= T && s0 != 0) break;      // uniform over the workgroup; T == 0 still runs once
+        if (n > 0) __syncthreads();         // the previous sub-span's reads are done
+        conv_stage<Tio, K, XR, DR>(lds, x, st, dy, s0 - (K - 1), s0, T, C, cb * kConvBlk);
+        __syncthreads();
+        if (!active) continue;
+#pragma unroll 1
+        for (int pass = 0; pass < TW / TT; ++pass) {
+            const int l0 = wave * TW + pass * TT;
             f32x4 xr[NX], dz[ND];
 #pragma unroll
-            for (int j = 0; j < NX; ++j) xr[j] = conv_row<Tio, K>(x, st, T, C, t0 - (K - 1) + j);
+            for (int j = 0; j < NX; ++j) xr[j] = ld_vec4(xrow + (l0 + j) * kConvBlk);
 #pragma unroll
-            for (int j = 0; j < ND; ++j)
-                dz[j] = (t0 + j < T) ? ld_vec4(dy + (t0 + j) * C) : f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < ND; ++j) dz[j] = ld_vec4(drow + (l0 + j) * kConvBlk);
             if (SILU) {
-                // d(z sigmoid z)/dz = s (1 + z (1 - s))
+                // d(z sigmoid z)/dz = s (1 + z (1 - s)); rows past T hold dy = 0
 #pragma unroll
                 for (int j = 0; j < ND; ++j) {
                     f32x4 z = w[0] * xr[j];
@@ -164,16 +237,17 @@ __global__ __launch_bounds__(kThreads) void k_short_conv_bwd(ConvBwdArgs a)
 #pragma unroll
                 for (int i = 0; i < K; ++i) acc[i] += dz[t] * xr[t + i];
             }
+            Tio* dx = static_cast<Tio*>(a.dx) + b * T * C + c0;
 #pragma unroll
             for (int t = 0; t < TT; ++t) {
-                if (t0 + t < T) {
+                if (s0 + l0 + t < T) {
                     f32x4 g = w[K - 1] * dz[t];
 #pragma unroll
                     for (int i = 0; i < K - 1; ++i) g += w[i] * dz[t + K - 1 - i];
-                    st_vec4(dx + (t0 + t) * C, g);
+                    st_vec4(dx + (s0 + l0 + t) * C, g);
                 }
             }
-            if (K > 1 && first && a.dstate != nullptr) {
+            if (K > 1 && s0 + l0 == 0 && a.dstate != nullptr) {
                 // positions q - (K-1) before the first token: taps i <= q reach dz[q - i]
                 Tio* ds = static_cast<Tio*>(a.dstate) + b * (K - 1) * C + c0;
 #pragma unroll
@@ -227,9 +301,9 @@ namespace {
 template <typename Tio, int K>
 hipError_t conv_fwd_k(const ConvArgs& a, bool silu, hipStream_t s)
 {
-    const int64_t threads = a.B * a.ntile * (a.C / kConvCh);
-    if (threads == 0) return hipSuccess;
-    const dim3 grid((unsigned)((threads + kThreads - 1) / kThreads));
+    const int64_t blocks = a.B * a.ntile * ((a.C / kConvCh + 63) / 64);
+    if (blocks == 0) return hipSuccess;
+    const dim3 grid((unsigned)blocks);
     if (silu)
         hipLaunchKernelGGL((k_short_conv<Tio, K, true>), grid, dim3(kThreads), 0, s, a);
     else

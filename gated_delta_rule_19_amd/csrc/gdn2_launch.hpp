@@ -126,17 +126,17 @@ struct NormArgs {
     int64_t rows; int dv; float inv_dv; float eps;
 };
 
-// short convolution: a forward tile is kConvTileF tokens of 4 channels a
-// lane; a backward workgroup takes a kConvSpan-token span of one sequence in
-// tiles of kConvTileB and writes one fp32 [C][K] row of weight partials
-constexpr int kConvTileF = 16;
-constexpr int kConvTileB = 8;
-constexpr int kConvSpan = 256;
+// short convolution: a workgroup takes 256 channels of a span of tokens
+// staged through LDS; forward spans of kConvSpanF(bf16) tokens, backward
+// workgroups of kConvSpan tokens that each write one fp32 [C][K] row of
+// weight partials
+constexpr int kConvSpan = 128;
+constexpr int kConvSpanF(bool bf16) { return bf16 ? 64 : 32; }
 
 struct ConvArgs {
     const void* x; const float* weight; const void* state_in; void* y; void* state_out;
     int64_t B, T, C;
-    int64_t ntile;        // forward tiles a sequence (at least 1 when the state is written)
+    int64_t ntile;        // forward spans a sequence (at least 1 when the state is written)
 };
 
 struct ConvBwdArgs {

@@ -319,7 +319,7 @@ int gdn2_short_conv(int64_t B, int64_t T, int64_t C, int32_t K, int32_t flags, i
 
 /*
  * Bytes of workspace gdn2_short_conv_bwd needs (0 for invalid sizes): one
- * fp32 [C, K] row of partial weight gradients per (sequence, 256-token span).
+ * fp32 [C, K] row of partial weight gradients per (sequence, 128-token span).
  */
 size_t gdn2_short_conv_bwd_workspace_size(int64_t B, int64_t T, int64_t C, int32_t K);
 

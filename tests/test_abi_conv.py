@@ -124,9 +124,9 @@ def test_single_tap_ignores_the_state_pointers():
 
 def test_workspace():
     L = g.lib()
-    # one fp32 [C, K] row per (sequence, 256-token span)
-    assert L.gdn2_short_conv_bwd_workspace_size(4, 2048, 6144, 4) == 4 * 8 * 6144 * 4 * 4
-    assert L.gdn2_short_conv_bwd_workspace_size(2, 257, 16, 3) == 2 * 2 * 16 * 3 * 4
+    # one fp32 [C, K] row per (sequence, 128-token span)
+    assert L.gdn2_short_conv_bwd_workspace_size(4, 2048, 6144, 4) == 4 * 16 * 6144 * 4 * 4
+    assert L.gdn2_short_conv_bwd_workspace_size(2, 257, 16, 3) == 2 * 3 * 16 * 3 * 4
     assert L.gdn2_short_conv_bwd_workspace_size(2, 0, 16, 3) == 2 * 1 * 16 * 3 * 4
     assert L.gdn2_short_conv_bwd_workspace_size(0, 100, 16, 3) == 0
     assert L.gdn2_short_conv_bwd_workspace_size(2, 10, 12, 3) == 0      # invalid
