@@ -100,6 +100,52 @@ __device__ inline void conv_stage(Tio* lds, const Tio* x, const Tio* st, const T
     }
 }
 
+// The same rows held in registers between a fetch and a put, so that the
+// next sub-span's loads are in flight while the current one is computed.
+template <typename Tio, int K, int NA, int NB>
+struct ConvFetch {
+    static constexpr int CHR = ConvRow<Tio>::CHR, EPC = ConvRow<Tio>::EPC;
+    static constexpr int N = (NA + NB) * CHR, PER = (N + kThreads - 1) / kThreads;
+    typedef int __attribute__((ext_vector_type(4))) i32x4;
+    i32x4 v[PER];
+
+    __device__ inline void fetch(const Tio* x, const Tio* st, const Tio* y2, int64_t pa, int64_t pb, int64_t T,
+                                 int64_t C, int64_t c_lo)
+    {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int id = threadIdx.x + j * kThreads;
+            v[j] = i32x4{0, 0, 0, 0};
+            const int row = id / CHR;
+            const int64_t ch = c_lo + (int64_t)(id % CHR) * EPC;
+            if (id < N && ch < C) {
+                const Tio* src = nullptr;
+                if (row < NA) {
+                    const int64_t p = pa + row;
+                    if (p >= 0) {
+                        if (p < T) src = x + p * C + ch;
+                    } else if (st != nullptr) {
+                        src = st + (p + K - 1) * C + ch;
+                    }
+                } else {
+                    const int64_t p = pb + (row - NA);
+                    if (p >= 0 && p < T) src = y2 + p * C + ch;
+                }
+                if (src != nullptr) v[j] = *reinterpret_cast<const i32x4*>(src);
+            }
+        }
+    }
+
+    __device__ inline void put(Tio* lds) const
+    {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int id = threadIdx.x + j * kThreads;
+            if (id < N) reinterpret_cast<i32x4*>(lds)[id] = v[j];
+        }
+    }
+};
+
 // taps of the 4 channels from c0: w[i] holds tap i of each ([C][K] fp32 rows)
 template <int K>
 __device__ inline void conv_taps(const float* weight, int64_t c0, f32x4 (&w)[K])
@@ -171,19 +217,23 @@ __global__ __launch_bounds__(kThreads) void k_short_conv(ConvArgs a)
 }
 
 template <typename Tio, int K, bool SILU>
-__global__ __launch_bounds__(kThreads, K <= 4 ? 2 : 1) void k_short_conv_bwd(ConvBwdArgs a)
+__global__ __launch_bounds__(kThreads) void k_short_conv_bwd(ConvBwdArgs a)
 {
     constexpr int S = 32;                              // tokens a sub-span
     constexpr int NSUB = kConvSpan / S;
     constexpr int TW = S / kConvWaves;                 // tokens a wave
-    constexpr int TT = 8;                              // tokens a pass
     constexpr int XR = SILU ? S + 2 * K - 2 : S + K - 1;   // staged xe rows from s0 - (K-1)
     constexpr int DR = S + K - 1;                          // staged dy rows from s0
-    constexpr int NX = SILU ? TT + 2 * K - 2 : TT + K - 1;
-    constexpr int ND = TT + K - 1;
-    static_assert(NSUB * S == kConvSpan && TW % TT == 0, "span must split into passes");
-    __shared__ __align__(16) Tio lds[(XR + DR) * kConvBlk];
-    __shared__ f32x4 red[kConvWaves - 1][K][64];
+    // with the SiLU, dz = dy * d(z sigmoid z)/dz is formed once a row: in place
+    // of dy for fp32, in an fp32 area for bf16
+    constexpr bool SEP = SILU && sizeof(Tio) == 2;
+    constexpr int LDS_IO = (XR + DR) * kConvBlk * (int)sizeof(Tio);
+    constexpr int LDS_RED = (kConvWaves - 1) * K * 64 * 16;
+    constexpr int LDS_A = LDS_IO > LDS_RED ? LDS_IO : LDS_RED;
+    static_assert(NSUB * S == kConvSpan, "span must split into sub-spans");
+    __shared__ __align__(16) char lds_a[LDS_A];
+    __shared__ __align__(16) f32x4 dzs[SEP ? DR * 64 : 1];
+    Tio* lds = reinterpret_cast<Tio*>(lds_a);
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t C4 = a.C / kConvCh, ncb = (C4 + 63) / 64;
@@ -197,82 +247,99 @@ __global__ __launch_bounds__(kThreads, K <= 4 ? 2 : 1) void k_short_conv_bwd(Con
     const Tio* x = static_cast<const Tio*>(a.x) + b * T * C;
     const Tio* st = a.state_in ? static_cast<const Tio*>(a.state_in) + b * (K - 1) * C : nullptr;
     const Tio* dy = static_cast<const Tio*>(a.dy) + b * T * C;
+    Tio* dx = static_cast<Tio*>(a.dx) + b * T * C + c0;
 
     f32x4 w[K], acc[K];   // acc[i]: weight gradient of tap i for the 4 channels
 #pragma unroll
     for (int i = 0; i < K; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (active) conv_taps<K>(a.weight, c0, w);
 
-    const Tio* xrow = lds + lane * kConvCh;
-    const Tio* drow = lds + XR * kConvBlk + lane * kConvCh;
+    Tio* xrow = lds + lane * kConvCh;
+    Tio* drow = lds + XR * kConvBlk + lane * kConvCh;
+    // dz of staged row j (row j = position s0 + j)
+    auto dz_at = [&](int j) -> f32x4 {
+        if constexpr (SEP) return dzs[j * 64 + lane];
+        else return ld_vec4(drow + j * kConvBlk);
+    };
+    // bf16 rows are few enough a thread to be prefetched in registers
+    constexpr bool PIPE = sizeof(Tio) == 2;
+    ConvFetch<Tio, K, XR, DR> pf;
+    if constexpr (PIPE) pf.fetch(x, st, dy, span * kConvSpan - (K - 1), span * kConvSpan, T, C, cb * kConvBlk);
 #pragma unroll 1
     for (int n = 0; n < NSUB; ++n) {
         const int64_t s0 = span * kConvSpan + (int64_t)n * S;
         if (s0 >= T && s0 != 0) break;      // uniform over the workgroup; T == 0 still runs once
         if (n > 0) __syncthreads();         // the previous sub-span's reads are done
-        conv_stage<Tio, K, XR, DR>(lds, x, st, dy, s0 - (K - 1), s0, T, C, cb * kConvBlk);
-        __syncthreads();
+        if constexpr (PIPE) {
+            pf.put(lds);
+            __syncthreads();
+            const int64_t s1 = s0 + S;
+            if (n + 1 < NSUB && s1 < T) pf.fetch(x, st, dy, s1 - (K - 1), s1, T, C, cb * kConvBlk);
+        } else {
+            conv_stage<Tio, K, XR, DR>(lds, x, st, dy, s0 - (K - 1), s0, T, C, cb * kConvBlk);
+            __syncthreads();
+        }
+        if (SILU) {
+            // rows past T hold dy = 0, so their dz is 0
+            if (active) {
+#pragma unroll
+                for (int j = wave; j < DR; j += kConvWaves) {
+                    f32x4 z = w[0] * ld_vec4(xrow + j * kConvBlk);
+#pragma unroll
+                    for (int i = 1; i < K; ++i) z += w[i] * ld_vec4(xrow + (j + i) * kConvBlk);
+                    const f32x4 sg = sigmoid4(z);
+                    const f32x4 d = ld_vec4(drow + j * kConvBlk) * sg * (1.f + z * (1.f - sg));
+                    if constexpr (SEP) dzs[j * 64 + lane] = d;
+                    else st_vec4(drow + j * kConvBlk, d);
+                }
+            }
+            __syncthreads();
+        }
         if (!active) continue;
-#pragma unroll 1
-        for (int pass = 0; pass < TW / TT; ++pass) {
-            const int l0 = wave * TW + pass * TT;
-            f32x4 xr[NX], dz[ND];
+        const int l0 = wave * TW;
 #pragma unroll
-            for (int j = 0; j < NX; ++j) xr[j] = ld_vec4(xrow + (l0 + j) * kConvBlk);
+        for (int t = 0; t < TW; ++t) {
+            const f32x4 d = dz_at(l0 + t);
 #pragma unroll
-            for (int j = 0; j < ND; ++j) dz[j] = ld_vec4(drow + (l0 + j) * kConvBlk);
-            if (SILU) {
-                // d(z sigmoid z)/dz = s (1 + z (1 - s)); rows past T hold dy = 0
+            for (int i = 0; i < K; ++i) acc[i] += d * ld_vec4(xrow + (l0 + t + i) * kConvBlk);
+        }
 #pragma unroll
-                for (int j = 0; j < ND; ++j) {
-                    f32x4 z = w[0] * xr[j];
+        for (int t = 0; t < TW; ++t) {
+            if (s0 + l0 + t < T) {
+                f32x4 g = w[K - 1] * dz_at(l0 + t);
 #pragma unroll
-                    for (int i = 1; i < K; ++i) z += w[i] * xr[j + i];
-                    const f32x4 s = sigmoid4(z);
-                    dz[j] = dz[j] * s * (1.f + z * (1.f - s));
-                }
+                for (int i = 0; i < K - 1; ++i) g += w[i] * dz_at(l0 + t + K - 1 - i);
+                st_vec4(dx + (s0 + l0 + t) * C, g);
             }
+        }
+        if (K > 1 && s0 + l0 == 0 && a.dstate != nullptr) {
+            // positions q - (K-1) before the first token: taps i <= q reach dz[q - i]
+            Tio* ds = static_cast<Tio*>(a.dstate) + b * (K - 1) * C + c0;
 #pragma unroll
-            for (int t = 0; t < TT; ++t) {
+            for (int q = 0; q < K - 1; ++q) {
+                f32x4 g = w[q] * dz_at(0);
 #pragma unroll
-                for (int i = 0; i < K; ++i) acc[i] += dz[t] * xr[t + i];
-            }
-            Tio* dx = static_cast<Tio*>(a.dx) + b * T * C + c0;
-#pragma unroll
-            for (int t = 0; t < TT; ++t) {
-                if (s0 + l0 + t < T) {
-                    f32x4 g = w[K - 1] * dz[t];
-#pragma unroll
-                    for (int i = 0; i < K - 1; ++i) g += w[i] * dz[t + K - 1 - i];
-                    st_vec4(dx + (s0 + l0 + t) * C, g);
-                }
-            }
-            if (K > 1 && s0 + l0 == 0 && a.dstate != nullptr) {
-                // positions q - (K-1) before the first token: taps i <= q reach dz[q - i]
-                Tio* ds = static_cast<Tio*>(a.dstate) + b * (K - 1) * C + c0;
-#pragma unroll
-                for (int q = 0; q < K - 1; ++q) {
-                    f32x4 g = w[q] * dz[0];
-#pragma unroll
-                    for (int i = 0; i < q; ++i) g += w[i] * dz[q - i];
-                    st_vec4(ds + q * C, g);
-                }
+                for (int i = 0; i < q; ++i) g += w[i] * dz_at(q - i);
+                st_vec4(ds + q * C, g);
             }
         }
     }
 
-    // the span's weight gradient: waves 1.. hand theirs to wave 0, which adds
-    // them in wave order and writes one partial row [C][K]
+    // the span's weight gradient: waves 1.. hand theirs to wave 0 (in the
+    // staging area, once every wave is done with it), which adds them in wave
+    // order and writes one partial row [C][K]
+    f32x4* red = reinterpret_cast<f32x4*>(lds_a);   // [wave - 1][K][64]
+    __syncthreads();
     if (wave > 0) {
 #pragma unroll
-        for (int i = 0; i < K; ++i) red[wave - 1][i][lane] = acc[i];
+        for (int i = 0; i < K; ++i) red[((wave - 1) * K + i) * 64 + lane] = acc[i];
     }
     __syncthreads();
     if (wave == 0 && active) {
 #pragma unroll
         for (int v = 0; v < kConvWaves - 1; ++v) {
 #pragma unroll
-            for (int i = 0; i < K; ++i) acc[i] += red[v][i][lane];
+            for (int i = 0; i < K; ++i) acc[i] += red[(v * K + i) * 64 + lane];
         }
         float f[kConvCh * K];
 #pragma unroll
