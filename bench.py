@@ -80,7 +80,7 @@ def parse_args(argv=None):
     ap.add_argument("--pmc-summary", metavar="DIR", default=None)
     ap.add_argument("--copy-pmc", metavar="DIR", default=None)
     ap.add_argument("--util-summary", metavar="DIRS", default=None)
-    ap.add_argument("--no-prologue", action="store_true", help="skip the side legs (in-kernel prologue, grouped heads, packed batch, backward, output step)")
+    ap.add_argument("--no-prologue", action="store_true", help="skip the side legs (in-kernel prologue, grouped heads, packed batch, backward, output step, short convolution)")
     return ap.parse_args(argv)
 
 
@@ -363,6 +363,7 @@ def main(argv=None):
         result["chunk_fwd_varlen"] = varlen_leg(g, inputs, wl_c, dev, args)
         result["chunk_bwd"] = backward_leg(g, inputs, wl_c, dev, args)
         result["epilogue"] = epilogue_leg(g, outs, dev, args)
+        result["short_conv"] = short_conv_leg(g, dev, args)
 
     ok = bool(torch.isfinite(outs[0].float()).all() and torch.isfinite(states[0]).all()
               and torch.isfinite(douts[0].float()).all())
@@ -604,6 +605,54 @@ def epilogue_leg(g, outs, dev, args):
             "alg_bytes": int(nbytes),
             "roofline": {"kernel": "k_gated_rmsnorm", "bound": "hbm", "achieved": round(gbps, 1),
                          "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4)}}
+
+
+def short_conv_leg(g, dev, args, B=4, T=2048, C=3 * 16 * 128, K=4):
+    """The short convolution of the prologue on the concatenated q/k/v projections of the
+    chunked workload (B4 T2048, 3 x 16 heads x 128 = 6144 channels, bf16, K = 4 taps,
+    SiLU, carried state in and out), forward and gradient over rotated input sets.
+    Algorithmic bytes: x and y (forward); x, dy and dx (gradient), plus the states and
+    the [C, K] weights; the gradient's time covers both of its launches."""
+    import torch
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    dt = torch.bfloat16
+    n_sets = max(args.sets, 1)
+    xs = [torch.randn(B, T, C, generator=gen, device=dev).to(dt) for _ in range(n_sets)]
+    dys = [torch.randn(B, T, C, generator=gen, device=dev).to(dt) for _ in range(n_sets)]
+    sts = [torch.randn(B, K - 1, C, generator=gen, device=dev).to(dt) for _ in range(n_sets)]
+    wt = torch.randn(C, K, generator=gen, device=dev) * 0.5
+    ys = [torch.empty_like(x) for x in xs]
+    so = torch.empty(B, K - 1, C, dtype=dt, device=dev)
+    ws = g.alloc_workspace(g.short_conv_bwd_workspace_size(B, T, C, K), dev)
+    steps = max(args.steps // 2, 5)
+
+    def run(fn):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for i in range(args.warmup + steps):
+            ev = evs[i - args.warmup] if i >= args.warmup else None
+            if ev:
+                ev[0].record()
+            fn(i % n_sets)
+            if ev:
+                ev[1].record()
+        torch.cuda.synchronize()
+        return sorted(e[0].elapsed_time(e[1]) for e in evs)
+
+    t_f = run(lambda j: g.short_conv(xs[j], wt, sts[j], silu=True, out=ys[j], state_out=so))
+    t_b = run(lambda j: g.short_conv_bwd(xs[j], wt, dys[j], sts[j], silu=True, workspace=ws))
+    el, st_b, w_b = B * T * C * 2, B * (K - 1) * C * 2, C * K * 4
+    out = {"workload": f"short convolution B{B} T{T} C{C} (q/k/v of 16 heads x 128) K{K} SiLU bf16, state in/out"}
+    for name, t, nbytes, kern in (("forward", t_f, 2 * el + 2 * st_b + w_b, "k_short_conv"),
+                                  ("gradient", t_b, 3 * el + 2 * st_b + 2 * w_b,
+                                   "k_short_conv_bwd + k_conv_dw_sum (whole call)")):
+        ms = sum(t) / len(t)
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"us": round(ms * 1e3, 2), "median_us": round(t[len(t) // 2] * 1e3, 2),
+                     "alg_bytes": int(nbytes),
+                     "roofline": {"kernel": kern, "bound": "hbm", "achieved": round(gbps, 1),
+                                  "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4)}}
+    return out
 
 
 def device_copy_gbps(dev, nbytes=1 << 30, reps=5):

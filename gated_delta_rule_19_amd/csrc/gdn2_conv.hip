@@ -353,13 +353,25 @@ __global__ __launch_bounds__(kThreads) void k_short_conv_bwd(ConvBwdArgs a)
     }
 }
 
-// dweight[e] = sum over the partial rows r = 0, 1, ... of part[r][e]
-__global__ __launch_bounds__(kThreads) void k_conv_dw_sum(const float* part, float* dw, int64_t rows, int64_t n)
+// dweight[e] = sum over the partial rows r = 0, 1, ... of part[r][e], added
+// in row order; 16 rows' loads are in flight at a time
+constexpr int kConvSumThreads = 64;
+
+__global__ __launch_bounds__(kConvSumThreads) void k_conv_dw_sum(const float* part, float* dw, int64_t rows,
+                                                                 int64_t n)
 {
-    const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t e = (int64_t)blockIdx.x * kConvSumThreads + threadIdx.x;
     if (e >= n) return;
     float s = 0.f;
-    for (int64_t r = 0; r < rows; ++r) s += part[r * n + e];
+    int64_t r = 0;
+    for (; r + 16 <= rows; r += 16) {
+        float v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = part[(r + j) * n + e];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) s += v[j];
+    }
+    for (; r < rows; ++r) s += part[r * n + e];
     dw[e] = s;
 }
 
@@ -392,8 +404,8 @@ hipError_t conv_bwd_k(const ConvBwdArgs& a, bool silu, hipStream_t s)
         if (e != hipSuccess) return e;
     }
     const int64_t n = a.C * K;
-    hipLaunchKernelGGL(k_conv_dw_sum, dim3((unsigned)((n + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
-                       a.part, a.dweight, a.B * a.nspan, n);
+    hipLaunchKernelGGL(k_conv_dw_sum, dim3((unsigned)((n + kConvSumThreads - 1) / kConvSumThreads)),
+                       dim3(kConvSumThreads), 0, s, a.part, a.dweight, a.B * a.nspan, n);
     return hipGetLastError();
 }
 
