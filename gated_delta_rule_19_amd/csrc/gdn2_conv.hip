@@ -14,7 +14,8 @@
 // ones) into LDS in 16-byte pieces, every load of the span issued before the
 // first is used, so that a wave keeps many kilobytes in flight without
 // holding them in registers; then each lane takes 4 channels of a quarter of
-// the span from LDS.
+// the span from LDS.  A forward workgroup takes two consecutive spans, the
+// second one's rows fetched into registers while the first is computed.
 //
 // Backward: a workgroup walks the sub-spans of a 128-token span, recomputing
 // z where the SiLU needs it, writes dx (and, at the start of a sequence, the
@@ -29,6 +30,7 @@ namespace gdn2 {
 constexpr int kConvCh = 4;                        // channels a lane
 constexpr int kConvWaves = kThreads / 64;
 constexpr int kConvBlk = 64 * kConvCh;            // channels a workgroup
+constexpr int kConvSpansF = 2;                    // forward spans a workgroup
 
 // rows of the channel block in LDS: 16-byte pieces of EPC elements
 template <typename Tio> struct ConvRow {
@@ -164,39 +166,53 @@ __device__ inline void conv_taps(const float* weight, int64_t c0, f32x4 (&w)[K])
 template <typename Tio, int K, bool SILU>
 __global__ __launch_bounds__(kThreads) void k_short_conv(ConvArgs a)
 {
-    constexpr int S = kConvSpanF(sizeof(Tio) == 2);   // tokens a workgroup
+    constexpr int S = kConvSpanF(sizeof(Tio) == 2);   // tokens a span
     constexpr int TW = S / kConvWaves;                 // tokens a wave
     constexpr int NR = S + K - 1;                      // staged rows from s0 - (K-1)
     __shared__ __align__(16) Tio lds[NR * kConvBlk];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t C4 = a.C / kConvCh, ncb = (C4 + 63) / 64;
+    const int64_t ngrp = (a.ntile + kConvSpansF - 1) / kConvSpansF;
     int64_t blk = blockIdx.x;
     const int64_t cb = blk % ncb;
     blk /= ncb;
-    const int64_t span = blk % a.ntile, b = blk / a.ntile;
-    const int64_t T = a.T, C = a.C, s0 = span * S;
+    const int64_t grp = blk % ngrp, b = blk / ngrp;
+    const int64_t T = a.T, C = a.C;
     const int64_t c0 = (cb * 64 + lane) * kConvCh;
     const bool active = c0 < C;
     const Tio* x = static_cast<const Tio*>(a.x) + b * T * C;
     const Tio* st = a.state_in ? static_cast<const Tio*>(a.state_in) + b * (K - 1) * C : nullptr;
+    Tio* y = static_cast<Tio*>(a.y) + b * T * C + c0;
 
-    conv_stage<Tio, K, NR, 0>(lds, x, st, nullptr, s0 - (K - 1), 0, T, C, cb * kConvBlk);
+    // the spans of a group go one after the other, the next one's rows
+    // fetched into registers while the current one is computed
+    ConvFetch<Tio, K, NR, 0> pf;
+    pf.fetch(x, st, nullptr, grp * kConvSpansF * S - (K - 1), 0, T, C, cb * kConvBlk);
     // the carried window for a following call: only the first span of a
-    // sequence reads the state, so it alone writes the new one, after its reads
-    const bool keep = K > 1 && a.state_out != nullptr && span == 0 && wave == 0 && active;
+    // sequence reads the state, so its workgroup alone writes the new one,
+    // after its reads
+    const bool keep = K > 1 && a.state_out != nullptr && grp == 0 && wave == 0 && active;
     f32x4 so[K > 1 ? K - 1 : 1];
     if (keep) {
 #pragma unroll
         for (int j = 0; j < K - 1; ++j)
             so[j] = conv_row<Tio, K>(x + c0, st ? st + c0 : nullptr, T, C, T - (K - 1) + j);
     }
-    __syncthreads();
-    if (active) {
-        f32x4 w[K];
-        conv_taps<K>(a.weight, c0, w);
-        const Tio* row = lds + lane * kConvCh;
-        Tio* y = static_cast<Tio*>(a.y) + b * T * C + c0;
+    f32x4 w[K];
+    if (active) conv_taps<K>(a.weight, c0, w);
+    const Tio* row = lds + lane * kConvCh;
+#pragma unroll 1
+    for (int m = 0; m < kConvSpansF; ++m) {
+        const int64_t span = grp * kConvSpansF + m;
+        if (span >= a.ntile) break;         // uniform over the workgroup
+        const int64_t s0 = span * S;
+        if (m > 0) __syncthreads();         // the previous span's reads are done
+        pf.put(lds);
+        __syncthreads();
+        if (m + 1 < kConvSpansF && span + 1 < a.ntile)
+            pf.fetch(x, st, nullptr, s0 + S - (K - 1), 0, T, C, cb * kConvBlk);
+        if (!active) continue;
 #pragma unroll
         for (int t = 0; t < TW; ++t) {
             const int l = wave * TW + t;
@@ -380,7 +396,7 @@ namespace {
 template <typename Tio, int K>
 hipError_t conv_fwd_k(const ConvArgs& a, bool silu, hipStream_t s)
 {
-    const int64_t blocks = a.B * a.ntile * ((a.C / kConvCh + 63) / 64);
+    const int64_t blocks = a.B * ((a.ntile + kConvSpansF - 1) / kConvSpansF) * ((a.C / kConvCh + 63) / 64);
     if (blocks == 0) return hipSuccess;
     const dim3 grid((unsigned)blocks);
     if (silu)
