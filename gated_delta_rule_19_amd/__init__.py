@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     abi_version,
     alloc_workspace,
     chunk_bwd,
+    chunk_bwd_varlen,
     chunk_bwd_workspace_size,
     chunk_fwd,
     chunk_fwd_varlen,

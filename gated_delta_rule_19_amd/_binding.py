@@ -26,7 +26,8 @@ EXPORTED = ("gdn2_abi_version", "gdn2_status_str", "gdn2_chunk_fwd_workspace_siz
             "gdn2_chunk_fwd", "gdn2_chunk_prep", "gdn2_chunk_state", "gdn2_recurrent_step",
             "gdn2_gated_rmsnorm", "gdn2_chunk_fwd_varlen_workspace_size", "gdn2_chunk_fwd_varlen",
             "gdn2_recurrent_varlen", "gdn2_chunk_bwd_workspace_size", "gdn2_chunk_bwd",
-            "gdn2_short_conv", "gdn2_short_conv_bwd_workspace_size", "gdn2_short_conv_bwd")
+            "gdn2_short_conv", "gdn2_short_conv_bwd_workspace_size", "gdn2_short_conv_bwd",
+            "gdn2_chunk_bwd_varlen_workspace_size", "gdn2_chunk_bwd_varlen")
 
 
 class Problem(ctypes.Structure):
@@ -92,6 +93,10 @@ def lib():
         L.gdn2_short_conv_bwd_workspace_size.argtypes = [i64] * 3 + [i32]
         L.gdn2_short_conv_bwd.restype = ctypes.c_int
         L.gdn2_short_conv_bwd.argtypes = [i64] * 3 + [i32] * 3 + [vp] * 7 + [vp, sz, vp]
+        L.gdn2_chunk_bwd_varlen_workspace_size.restype = sz
+        L.gdn2_chunk_bwd_varlen_workspace_size.argtypes = [P, vp]
+        L.gdn2_chunk_bwd_varlen.restype = ctypes.c_int
+        L.gdn2_chunk_bwd_varlen.argtypes = [P, vp] + [vp] * 16 + [vp, sz, vp]
         if L.gdn2_abi_version() != ABI_VERSION:   # the Problem mirror must match the library's struct
             raise ImportError(f"{LIB_PATH} has ABI {L.gdn2_abi_version()}, this binding expects {ABI_VERSION}: "
                               "rebuild it")
@@ -318,6 +323,38 @@ def chunk_bwd(q, k, v, alpha, b, w, dO, S0=None, dS_T=None, *, want_dS0: bool = 
                                 _ptr(dO), _ptr(dS_T), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dalpha"]),
                                 _ptr(g["db"]), _ptr(g["dw"]), _ptr(g["dS0"]), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(dev)))
+    return g
+
+
+def chunk_bwd_varlen(q, k, v, alpha, b, w, dO, cu_seqlens, S0=None, dS_T=None, *, want_dS0: bool = True,
+                     workspace=None, flags: int = 0):
+    """Backward of :func:`chunk_fwd_varlen` (``gdn2_chunk_bwd_varlen``): tensors as there
+    ([1, T, heads, d]), states [N, Hv, dk, dv]; ``cu_seqlens`` as an int32 [N+1] tensor
+    (read on the host).  Returns a dict dq, dk, dv, dalpha, db, dw, dS0 as :func:`chunk_bwd`."""
+    cu_host = cu_seqlens.detach().to("cpu", torch.int32).contiguous()
+    p, dev = _problem_from(q, k, v, alpha, b, w, flags)
+    if p.B != 1:
+        raise ValueError("a packed batch is passed as [1, T, heads, d] tensors")
+    if cu_host.dim() != 1 or cu_host.numel() < 1:
+        raise ValueError("cu_seqlens must be an int32 [N+1] tensor")
+    p.B = cu_host.numel() - 1
+    _check_state(S0, p, dev, "S0")
+    _check_state(dS_T, p, dev, "dS_T")
+    if tuple(dO.shape) != tuple(v.shape) or dO.dtype != v.dtype or dO.device != dev or not dO.is_contiguous():
+        raise ValueError("dO must be a contiguous tensor like v")
+    g = {n: torch.empty_like(x) for n, x in (("dq", q), ("dk", k), ("dv", v), ("dalpha", alpha), ("db", b),
+                                            ("dw", w))}
+    g["dS0"] = (torch.empty((p.B, p.value_heads, p.dk, p.dv), dtype=torch.float32, device=dev)
+                if want_dS0 else None)
+    cu_p = ctypes.c_void_p(cu_host.data_ptr())
+    need = int(lib().gdn2_chunk_bwd_varlen_workspace_size(ctypes.byref(p), cu_p))
+    if workspace is None:
+        workspace = alloc_workspace(need, dev)
+    _check(lib().gdn2_chunk_bwd_varlen(ctypes.byref(p), cu_p, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b),
+                                       _ptr(w), _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(g["dq"]), _ptr(g["dk"]),
+                                       _ptr(g["dv"]), _ptr(g["dalpha"]), _ptr(g["db"]), _ptr(g["dw"]),
+                                       _ptr(g["dS0"]), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                       _stream(dev)))
     return g
 
 

@@ -716,4 +716,96 @@ int gdn2_short_conv_bwd(int64_t B, int64_t T, int64_t C, int32_t K, int32_t flag
                                                      static_cast<hipStream_t>(stream)));
 }
 
+// host offsets of a packed batch: rising from 0 to T
+static int check_cu_host(const gdn2_problem* p, const int32_t* cu)
+{
+    if (cu == nullptr) return GDN2_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(cu) & 3u) != 0) return GDN2_ERR_ALIGN;
+    if (cu[0] != 0 || cu[p->B] != p->T) return GDN2_ERR_SHAPE;
+    for (int64_t i = 0; i < p->B; ++i)
+        if (cu[i + 1] < cu[i]) return GDN2_ERR_SHAPE;
+    return GDN2_OK;
+}
+
+// the problem of sequence i of a packed batch, as a batch of one
+static gdn2_problem seq_problem(const gdn2_problem* p, const int32_t* cu, int64_t i)
+{
+    gdn2_problem q = *p;
+    q.B = 1;
+    q.T = cu[i + 1] - cu[i];
+    return q;
+}
+
+size_t gdn2_chunk_bwd_varlen_workspace_size(const gdn2_problem* p, const int32_t* cu_seqlens_host)
+{
+    if (check_problem(p, true, true) != GDN2_OK) return 0;
+    if (p->B == 0) return 0;
+    if (check_cu_host(p, cu_seqlens_host) != GDN2_OK) return 0;
+    size_t need = 0;
+    for (int64_t i = 0; i < p->B; ++i) {
+        const gdn2_problem q = seq_problem(p, cu_seqlens_host, i);
+        const size_t n = gdn2_chunk_bwd_workspace_size(&q);
+        if (n > need) need = n;
+    }
+    return need;
+}
+
+int gdn2_chunk_bwd_varlen(const gdn2_problem* p, const int32_t* cu_seqlens_host, const void* q, const void* k,
+                          const void* v, const void* alpha, const void* b, const void* w, const float* S0,
+                          const void* dO, const float* dS_T, void* dq, void* dk, void* dv, void* dalpha, void* db,
+                          void* dw, float* dS0, void* workspace, size_t workspace_bytes, void* stream)
+{
+    int st = check_problem(p, true, true);
+    if (st) return st;
+    if (p->B * nvh(p) == 0) return GDN2_OK;
+    st = check_cu_host(p, cu_seqlens_host);
+    if (st) return st;
+    // the packed tensors as a whole: one batch of T tokens, N states
+    gdn2_problem whole = *p;
+    whole.B = 1;
+    st = check_inputs(&whole, q, k, v, alpha, b, w, dO);
+    if (st) return st;
+    if (rows_nonempty(&whole) && (!dq || !dk || !dv || !dalpha || !db || !dw)) return GDN2_ERR_NULL;
+    const int64_t need = (int64_t)gdn2_chunk_bwd_varlen_workspace_size(p, cu_seqlens_host);
+    if (need > 0 && (workspace == nullptr || static_cast<int64_t>(workspace_bytes) < need))
+        return GDN2_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_WORKSPACE;
+    const Sizes z = sizes_of(&whole);
+    const int64_t states = z.state * p->B;
+    const Range ins[10] = {range_of(q, z.key),   range_of(k, z.key),  range_of(v, z.val),
+                           range_of(alpha, z.gk), range_of(b, z.gk),   range_of(w, z.gv),
+                           range_of(S0, states),  range_of(dO, z.val), range_of(dS_T, states),
+                           range_of(cu_seqlens_host, (p->B + 1) * 4)};
+    const Range outs[8] = {range_of(dq, z.key),   range_of(dk, z.key), range_of(dv, z.val),
+                           range_of(dalpha, z.gk), range_of(db, z.gk),  range_of(dw, z.gv),
+                           range_of(dS0, states),  range_of(workspace, need)};
+    st = check_alias(outs, 8, ins, 10, nullptr, nullptr, -1, -1);
+    if (st) return st;
+    st = check_align({q, k, v, alpha, b, w, S0, dO, dS_T, dq, dk, dv, dalpha, db, dw, dS0});
+    if (st) return st;
+    // sequences are independent: the backward of each slice in turn, all on
+    // `stream`, one workspace reused in stream order
+    const Sizes one = sizes_of(&whole);
+    const int64_t tok = whole.T > 0 ? whole.T : 1;
+    const int64_t key_tok = one.key / tok, val_tok = one.val / tok, gk_tok = one.gk / tok, gv_tok = one.gv / tok;
+    auto at = [](const void* base, int64_t bytes) -> const char* {
+        return base ? static_cast<const char*>(base) + bytes : nullptr;
+    };
+    auto atw = [](void* base, int64_t bytes) -> char* { return base ? static_cast<char*>(base) + bytes : nullptr; };
+    for (int64_t i = 0; i < p->B; ++i) {
+        const gdn2_problem qi = seq_problem(p, cu_seqlens_host, i);
+        const int64_t t0 = cu_seqlens_host[i];
+        const int64_t so = i * z.state;
+        st = gdn2_chunk_bwd(&qi, at(q, t0 * key_tok), at(k, t0 * key_tok), at(v, t0 * val_tok),
+                            at(alpha, t0 * gk_tok), at(b, t0 * gk_tok), at(w, t0 * gv_tok),
+                            reinterpret_cast<const float*>(at(S0, so)), at(dO, t0 * val_tok),
+                            reinterpret_cast<const float*>(at(dS_T, so)), atw(dq, t0 * key_tok),
+                            atw(dk, t0 * key_tok), atw(dv, t0 * val_tok), atw(dalpha, t0 * gk_tok),
+                            atw(db, t0 * gk_tok), atw(dw, t0 * gv_tok), reinterpret_cast<float*>(atw(dS0, so)),
+                            workspace, workspace_bytes, stream);
+        if (st) return st;
+    }
+    return GDN2_OK;
+}
+
 }  // extern "C"

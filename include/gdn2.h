@@ -266,6 +266,32 @@ int gdn2_chunk_bwd(const gdn2_problem* p,
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Backward of gdn2_chunk_fwd_varlen (packed batches, layouts and p->B = N,
+ * p->T = total tokens as described above).  The gradients and their
+ * meaning are those of gdn2_chunk_bwd, per sequence: dq, dk, dalpha, db,
+ * dw, dv in the packed layouts of the inputs, dS0 [N, Hv, dk, dv] (NULL =
+ * not wanted); S0 and dS_T [N, Hv, dk, dv] or NULL (zero).
+ * cu_seqlens_host: the N+1 offsets in HOST memory (4-byte aligned), checked
+ * on the host: they must rise from 0 to T (GDN2_ERR_SHAPE otherwise).
+ * Sequences are independent, so the call runs the chunked backward on each
+ * sequence's contiguous slice in turn, all launches on `stream` (those of
+ * gdn2_chunk_bwd, a sequence at a time; an empty sequence only passes dS_T
+ * through to dS0).  The workspace (256-byte aligned, at least
+ * gdn2_chunk_bwd_varlen_workspace_size(p, cu_seqlens_host) bytes, the
+ * largest single sequence's need) is reused by the sequences in stream
+ * order.  Aliasing and alignment are checked over the packed tensors as a
+ * whole; the offsets count as an input.
+ */
+size_t gdn2_chunk_bwd_varlen_workspace_size(const gdn2_problem* p, const int32_t* cu_seqlens_host);
+
+int gdn2_chunk_bwd_varlen(const gdn2_problem* p, const int32_t* cu_seqlens_host,
+                          const void* q, const void* k, const void* v,
+                          const void* alpha, const void* b, const void* w,
+                          const float* S0, const void* dO, const float* dS_T,
+                          void* dq, void* dk, void* dv, void* dalpha, void* db, void* dw, float* dS0,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Output step of the layer (README "Architecture": "Gated RMS Norm <- SiLU
  * Gate"; "Configuration": norm_eps = 1e-5).  For every (token, head) row of
  * dv channels
