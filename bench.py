@@ -80,6 +80,7 @@ def parse_args(argv=None):
     ap.add_argument("--pmc-summary", metavar="DIR", default=None)
     ap.add_argument("--copy-pmc", metavar="DIR", default=None)
     ap.add_argument("--util-summary", metavar="DIRS", default=None)
+    ap.add_argument("--no-long", action="store_true", help="skip the long-context and expanded-value workloads")
     ap.add_argument("--no-prologue", action="store_true", help="skip the side legs (in-kernel prologue, grouped heads, packed batch, backward, output step, short convolution)")
     return ap.parse_args(argv)
 
@@ -326,6 +327,13 @@ def main(argv=None):
         return r
 
     chunk_gbps = gbps(alg_chunk, chunk_ms)
+    tr_p, tr_s = load_traffic("prep"), load_traffic("state")
+    whole = {"kernel": "whole chunked forward call (k_chunk_prep + k_chunk_state)", "bound": "hbm",
+             "achieved": round(chunk_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+             "frac": round(chunk_gbps / PEAK_HBM_GBPS, 4),
+             "traffic": None if tr_p is None or tr_s is None else round(tr_p + tr_s),
+             "alg_bytes": int(alg_chunk), "us_per_launch": round(chunk_ms * 1e3, 2)}
+    whole.update(spread["chunk"])
     result = {
         "metric": "chunk-fwd tokens/s (B4 H16 T2048 d128) + decode-step HBM GB/s; % roofline",
         "value": round(tokens / (chunk_ms * 1e-3), 1),
@@ -343,8 +351,8 @@ def main(argv=None):
                                "decode step B256 H16 d128 (fp32 state in place) timed in a loop of its own",
                    "global_batch": B, "seq_len": T, "heads": H, "dk": dk, "dv": dv, "chunk": 64,
                    "parallelism": "single GPU", "rotated_input_sets": args.sets},
-        "roofline": roof(dom),
-        "chunk_fwd": {"us": round(chunk_ms * 1e3, 2), "prep_us": round(prep_ms * 1e3, 2),
+        "roofline": whole,
+        "chunk_fwd": {"dominant_kernel": KERNEL_NAMES[dom], "us": round(chunk_ms * 1e3, 2), "prep_us": round(prep_ms * 1e3, 2),
                       "state_us": round(state_ms * 1e3, 2), "alg_GBps": round(chunk_gbps, 1),
                       "frac_hbm_roofline": round(chunk_gbps / PEAK_HBM_GBPS, 4),
                       "useful_TFLOPs": round(flops / (chunk_ms * 1e-3) / 1e12, 2),
@@ -357,6 +365,10 @@ def main(argv=None):
                    "frac_of_device_copy": round(gbps(alg_dec, dec_ms) / copy_gbps, 4),
                    "roofline": roof("decode")},
     }
+    if not args.no_long:
+        del ws
+        result["chunk_fwd_long"] = workload_leg(g, inputs, 3, dev, args)
+        result["chunk_fwd_expand_v"] = workload_leg(g, inputs, 4, dev, args)
     if not args.no_prologue:
         result["chunk_fwd_prologue"] = prologue_leg(g, inputs, wl_c, dev, args)
         result["chunk_fwd_grouped"] = grouped_leg(g, inputs, wl_c, dev, args)
@@ -370,9 +382,22 @@ def main(argv=None):
     result["outputs_finite"] = ok
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(sets[0], args.cpu_chains, B, T, H, dk, dv)
+        cb, ref = cpu_baseline(sets[0], args.cpu_chains, B, T, H, dk, dv)
+        result["cpu_baseline"] = cb
+        # the timed outputs of input set 0 against the oracle's (all chains)
+        result["parity_relL2"] = parity_figures(outs[0], states[0], ref, cb["chains"], H)
         if "chunk_bwd" in result:
             result["chunk_bwd"]["cpu_baseline"] = cpu_baseline_backward(sets[0], B, T, H, dk, dv)
+        for key, wi in (("chunk_fwd_long", 3), ("chunk_fwd_expand_v", 4)):
+            if key in result:
+                leg = result[key]
+                x = leg.pop("_set0")
+                cbl, refl = cpu_baseline(x["inp"], 0, *x["shape"])
+                leg["cpu_baseline"] = cbl
+                leg["parity_relL2"] = parity_figures(x["o"], x["S"], refl, cbl["chains"], x["shape"][2])
+    for key in ("chunk_fwd_long", "chunk_fwd_expand_v"):
+        if key in result:
+            result[key].pop("_set0", None)
     print(json.dumps(result), flush=True)
     return 0
 
@@ -404,6 +429,62 @@ def _leg_times(prep, state, tot):
     return {"us": round(sum(tot) / n * 1e3, 2), "median_us": round(tot[n // 2] * 1e3, 2),
             "min_us": round(tot[0] * 1e3, 2), "prep_us": round(sum(prep) / n * 1e3, 2),
             "state_us": round(sum(state) / n * 1e3, 2)}
+
+
+def workload_leg(g, inputs, idx, dev, args, nsets=3):
+    """One of the other chunked workloads (long context B1 H16 T65536 with slow decay;
+    expanded values B8 H16 T4096 dk128 dv256 with b in (0, 2) and a nonzero initial state),
+    timed like the main workload: the whole forward call (prep + state pass) back to back
+    over `nsets` rotated input sets resident in HBM.  Algorithmic bytes: the inputs read,
+    o written, the initial state read when there is one and the final state written."""
+    import torch
+    wl = inputs.WORKLOADS[idx]
+    B, T, H, dk, dv = wl.B, wl.T, wl.H, wl.dk, wl.dv
+    sets = [inputs.make(wl, seed=1000 * idx + i, device=dev) for i in range(nsets)]
+    prob = g.problem(B, T, H, dk, dv, wl.io_dtype)
+    ws = g.alloc_workspace(g.chunk_fwd_workspace_size(B, T, H, dk, dv, wl.io_dtype), dev)
+    outs = [torch.empty_like(x["v"]) for x in sets]
+    sts = [torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev) for _ in sets]
+    A = lambda x: (x["q"], x["k"], x["v"], x["alpha"], x["b"], x["w"])
+    steps = max(args.steps // 3, 5)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(args.warmup + steps):
+        j = i % nsets
+        ev = evs[i - args.warmup] if i >= args.warmup else None
+        if ev:
+            ev[0].record()
+        g.chunk_prep(*A(sets[j]), ws)
+        if ev:
+            ev[1].record()
+        g.chunk_state(prob, ws, outs[j], sets[j]["S0"], sts[j])
+        if ev:
+            ev[2].record()
+    torch.cuda.synchronize()
+    prep = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    state = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    tot = sorted(e[0].elapsed_time(e[2]) for e in evs)
+    t = _leg_times(prep, state, tot)
+    ms = t["us"] * 1e-3
+    ht = B * T * H
+    alg = chunk_bytes_per_ht(dk, dv) * ht + B * H * dk * dv * 4 * (2 if wl.s0_std is not None else 1)
+    flops = chunk_flops_per_ht(dk, dv) * ht
+    ach = alg / (ms * 1e-3) / 1e9
+    t_roof = max(alg / (PEAK_HBM_GBPS * 1e9), flops / (PEAK_BF16_TFLOPS * 1e12))
+    finite = bool(all(torch.isfinite(o.float()).all() and torch.isfinite(S).all() for o, S in zip(outs, sts)))
+    out = {"workload": wl.note + f": B{B} H{H} T{T} dk{dk} dv{dv}, bf16 q/k/v, fp32 gates and state"
+                                 + (", S0 ~ N(0, 0.05)" if wl.s0_std is not None else ", zero initial state")
+                                 + (f", b = {wl.b_scale:g} sigmoid(N(0,1))" if wl.b_scale != 1.0 else "")
+                                 + f", alpha = sigmoid(N({wl.alpha_mu:g}, 1))",
+           "tokens_per_s": round(B * T / (ms * 1e-3), 1), **t, "alg_bytes": int(alg),
+           "useful_GFLOP": round(flops / 1e9, 2),
+           "roofline": {"kernel": "whole chunked forward call (k_chunk_prep + k_chunk_state)", "bound": "hbm",
+                        "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                        "frac": round(ach / PEAK_HBM_GBPS, 4), "t_roofline_us": round(t_roof * 1e6, 1)},
+           "frac_of_roofline_time": round(t_roof / (ms * 1e-3), 4),
+           "rotated_input_sets": nsets, "outputs_finite": finite,
+           "_set0": {"inp": sets[0], "o": outs[0], "S": sts[0], "shape": (B, T, H, dk, dv)}}
+    del ws
+    return out
 
 
 def prologue_leg(g, inputs, wl, dev, args):
@@ -685,52 +766,78 @@ def cpu_model():
     return "unknown"
 
 
+def host_threads():
+    """Threads the oracle may use: the process's CPU affinity, capped by OMP_NUM_THREADS when
+    set (the GPU host sets it to its per-GPU share of the cores).  Returns (threads, affinity)."""
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:
+        aff = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    n = min(aff, int(cap)) if cap.isdigit() and int(cap) > 0 else aff
+    return n, aff
+
+
 def cpu_baseline(inp, chains, B, T, H, dk, dv):
     """The fp64 C oracle on the first `chains` (batch, head) chains (0 = all), all T tokens,
-    timed on the host cores; tokens/s scaled by the share of chains run."""
+    timed on the host cores; tokens/s scaled by the share of chains run.  Returns the
+    record and the oracle's (o, S) for those chains."""
     import torch
 
     from oracle import c_oracle
     nch = B * H if chains <= 0 else max(1, min(chains, B * H))
     nb = (nch + H - 1) // H
-    f = lambda x: x[0:nb].detach().to("cpu", torch.float32).contiguous().numpy()
+    f = lambda x: None if x is None else x[0:nb].detach().to("cpu", torch.float32).contiguous().numpy()
     arrs = [f(inp[k_]) for k_ in ("q", "k", "v", "alpha", "b", "w")]
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count() or 1
-    cores = min(cores, 16)
+    cores, aff = host_threads()
     t0 = time.perf_counter()
-    c_oracle.recurrent(*arrs, None, nthreads=cores, col_block=16)
+    ref = c_oracle.recurrent(*arrs, f(inp["S0"]), nthreads=cores, col_block=16)
     dt = time.perf_counter() - t0
     frac = nb * H / float(B * H)
     tok_s = B * T / (dt / frac)
-    return {"value": round(tok_s, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu": cpu_model(),
+    return {"value": round(tok_s, 2), "unit": "tokens/s", "cores": cores, "affinity_cores": aff,
+            "kind": "oracle", "cpu": cpu_model(),
             "sample": f"fp64 C oracle (OpenMP over head x 16-column blocks) on {nb * H} of {B * H} "
                       f"(batch, head) chains x {T} tokens of the same inputs: {dt:.2f} s",
-            "seconds": round(dt, 3)}
+            "seconds": round(dt, 3), "chains": nb * H}, ref
 
 
-def cpu_baseline_backward(inp, B, T, H, dk, dv, chains=2):
-    """The fp64 backward oracle (numpy, reverse loop over tokens) on `chains` (batch, head)
-    chains of the inputs, all T tokens, output gradients dO ~ N(0,1) and dS_T ~ N(0,1);
-    tokens/s scaled by the share of chains run."""
+def parity_figures(o, S, ref, nchains, H):
+    """rel-L2 of the GPU's o and S against the oracle's on the first `nchains` chains:
+    whole tensors and the worst (batch, head) chain."""
+    import torch
+
+    from oracle.reference import rel_l2, rel_l2_chains
+    nb = nchains // H
+    on = o[0:nb].detach().to("cpu", torch.float32).numpy()
+    Sn = S[0:nb].detach().to("cpu", torch.float32).numpy()
+    ro, rS = ref
+    return {"o": round(rel_l2(on, ro), 7), "S": round(rel_l2(Sn, rS), 7),
+            "o_worst_chain": round(float(rel_l2_chains(on, ro, (0, 2)).max()), 7),
+            "S_worst_chain": round(float(rel_l2_chains(Sn, rS, (0, 1)).max()), 7),
+            "chains": nb * H, "tol": 2e-2}
+
+
+def cpu_baseline_backward(inp, B, T, H, dk, dv):
+    """The fp64 C backward oracle (token-by-token reverse of the recurrence, OpenMP over
+    chains) on the whole workload, output gradients dO ~ N(0,1) and dS_T ~ N(0,1)."""
     import numpy as np
     import torch
 
-    from oracle.backward import recurrent_bwd
-    f = lambda x, h: x[0:1, :, h:h + 1].detach().to("cpu", torch.float64).numpy()
+    from oracle import c_oracle
+    f = lambda x: x.detach().to("cpu", torch.float32).contiguous().numpy()
     rng = np.random.default_rng(5)
+    dO = rng.standard_normal((B, T, H, dv)).astype(np.float32)
+    dS = rng.standard_normal((B, H, dk, dv)).astype(np.float32)
+    cores, aff = host_threads()
     t0 = time.perf_counter()
-    for h in range(chains):
-        dO = rng.standard_normal((1, T, 1, dv))
-        dS = rng.standard_normal((1, 1, dk, dv))
-        recurrent_bwd(*(f(inp[k_], h) for k_ in ("q", "k", "v", "alpha", "b", "w")), None, dO, dS)
+    c_oracle.recurrent_bwd(*(f(inp[k_]) for k_ in ("q", "k", "v", "alpha", "b", "w")), None, dO, dS,
+                           nthreads=cores)
     dt = time.perf_counter() - t0
-    frac = chains / float(B * H)
-    return {"value": round(B * T / (dt / frac), 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"fp64 numpy backward oracle (reverse token loop) on {chains} of {B * H} (batch, head) "
-                      f"chains x {T} tokens of the forward's inputs: {dt:.2f} s",
+    return {"value": round(B * T / dt, 2), "unit": "tokens/s", "cores": cores, "affinity_cores": aff,
+            "kind": "oracle",
+            "sample": f"fp64 C backward oracle (OpenMP over chains, reverse token loop) on all {B * H} "
+                      f"(batch, head) chains x {T} tokens of the forward's inputs: {dt:.2f} s",
             "seconds": round(dt, 3)}
 
 

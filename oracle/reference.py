@@ -44,7 +44,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["recurrent", "chunked_wy", "rel_l2", "prologue", "sigmoid", "gated_rmsnorm", "NORM_EPS", "share_qk_heads", "varlen",
+__all__ = ["recurrent", "chunked_wy", "rel_l2", "rel_l2_chains", "prologue", "sigmoid", "gated_rmsnorm", "NORM_EPS", "share_qk_heads", "varlen",
            "FLAG_GATE_LOGITS", "FLAG_NEG_EIGVAL", "FLAG_QK_L2NORM", "short_conv", "short_conv_bwd", "CONV_SILU"]
 
 # prologue options (the library's GDN2_FLAG_* values)
@@ -332,8 +332,30 @@ def rel_l2(x, ref):
     """||x - ref||_2 / ||ref||_2 over the whole tensor in fp64 (max-abs if ref == 0)."""
     x = np.asarray(x, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
+    if x.shape != ref.shape:
+        raise ValueError(f"rel_l2: shapes differ, {x.shape} vs {ref.shape}")
     den = np.linalg.norm(ref.ravel())
     num = np.linalg.norm((x - ref).ravel())
     if den == 0.0:
         return float(np.max(np.abs(x - ref))) if x.size else 0.0
     return float(num / den)
+
+
+def rel_l2_chains(x, ref, chain_axes):
+    """rel_l2 of every chain: the sub-tensors indexed by ``chain_axes`` (e.g. (0, 2) for
+    o [B,T,H,dv], (0, 1) for S [B,H,dk,dv]), each over all its other elements.  Returns
+    an array shaped like those axes."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if x.shape != ref.shape:
+        raise ValueError(f"rel_l2_chains: shapes differ, {x.shape} vs {ref.shape}")
+    rest = [a for a in range(x.ndim) if a not in chain_axes]
+    xs = np.transpose(x, list(chain_axes) + rest)
+    rs = np.transpose(ref, list(chain_axes) + rest)
+    lead = xs.shape[:len(chain_axes)]
+    xs = xs.reshape(lead + (-1,))
+    rs = rs.reshape(lead + (-1,))
+    out = np.zeros(lead)
+    for idx in np.ndindex(*lead):
+        out[idx] = rel_l2(xs[idx], rs[idx])
+    return out

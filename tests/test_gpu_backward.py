@@ -5,7 +5,10 @@ with respect to q, k, v, alpha, b, w and S0; the oracle
 (``oracle.backward.recurrent_bwd``, pinned by finite differences of the
 forward) computes them in fp64 from the same inputs (bf16 widened exactly).
 Relative L2 error per gradient tensor: <= 1e-4 with fp32 I/O, <= 2e-2 with
-bf16 I/O (the forward's operands are bf16 there).  The bf16 cases with dk in
+bf16 I/O (the forward's operands are bf16 there).  The full-size cases compare
+every (batch, head) chain against the fp64 C backward oracle
+(``oracle.c_oracle.recurrent_bwd``, pinned by finite differences too) and hold
+the worst chain to the same bar.  The bf16 cases with dk in
 {32, 64, 128} and dv in {32, 64, 128} run the matrix-core gradient kernels,
 the others the vector-ALU ones.
 """
@@ -16,7 +19,7 @@ import torch
 import gated_delta_rule_19_amd as g
 from gated_delta_rule_19_amd import inputs
 from oracle.backward import recurrent_bwd
-from oracle.reference import rel_l2
+from oracle.reference import rel_l2, rel_l2_chains
 
 pytestmark = pytest.mark.gpu
 
@@ -61,8 +64,14 @@ def ref(inp, dO, dS_T, chains=None):
     return {n: np.stack(v) for n, v in out.items()}
 
 
-def check(what, got, want, tol):
+def check(what, got, want, tol, chains=False):
+    """rel-L2 per gradient tensor; with chains=True also the worst (batch, head) chain of each
+    ([B,T,H,*] tensors on axes 0, 2; dS0 [B,H,dk,dv] on axes 0, 1), held to the same bar."""
     errs = {n: rel_l2(got[n], want[n]) for n in NAMES}
+    if chains:
+        for n in NAMES:
+            ax = (0, 1) if n == "dS0" else (0, 2)
+            errs[n + "_worst_chain"] = float(np.max(rel_l2_chains(got[n], want[n], ax)))
     print(f"[parity] {what}: " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()) + f" (tol {tol:g})", flush=True)
     bad = {n: e for n, e in errs.items() if not e <= tol}
     assert not bad, f"{what}: {bad}"
@@ -104,15 +113,65 @@ def test_backward_small(dev, case):
     check(_id(case), gn, want, TOL[io])
 
 
-def test_backward_full_size_sampled(dev):
-    """B4 H16 T2048 d128 bf16 (the chunked workload), sampled (batch, head) chains."""
+def test_backward_full_size_all_chains(dev):
+    """B4 H16 T2048 d128 bf16 (the chunked workload): every (batch, head) chain against the
+    fp64 C backward oracle, the worst chain's error held to the same bar."""
+    from oracle import c_oracle
     B, T, H, dk, dv = 4, 2048, 16, 128, 128
     inp, dO, dS_T, got = run(dev, B, T, H, dk, dv, BF16, F32, None, True, seed=77)
-    chains = [(0, 0), (3, 15)]
-    want = ref(inp, dO, dS_T, chains)
-    gn = {n: _np(got[n]) for n in NAMES}
-    gs = {n: np.stack([gn[n][bi, :, hi] if n != "dS0" else gn[n][bi, hi] for bi, hi in chains]) for n in NAMES}
-    check("B4H16T2048 sampled", gs, want, 2e-2)
+    h = {n: _np(x) for n, x in inp.items()}
+    want = c_oracle.recurrent_bwd(h["q"], h["k"], h["v"], h["alpha"], h["b"], h["w"], None, _np(dO), _np(dS_T))
+    check("B4H16T2048 all chains", {n: _np(got[n]) for n in NAMES}, want, 2e-2, chains=True)
+
+
+FAST_CASES = [
+    # B, T, H, dk, dv, io, alpha_mu, b scale
+    (1, 260, 2, 128, 128, BF16, 0.0, 2.0),
+    (2, 200, 2, 64, 64, BF16, -2.0, 1.0),
+    (1, 210, 2, 32, 48, F32, -2.0, 2.0),      # fp32 I/O: every gradient within 1e-4
+]
+
+
+# The chunked backward forms dlog(alpha) as a reverse cumulative sum over the chunk of
+# per-token terms whose pairs inside [t, 64) cancel exactly in real arithmetic; with
+# bf16 matrix-core operands each side of such a pair carries ~2^-9 relative error, so the
+# error of dalpha = dlog(alpha) / alpha grows like 1/alpha.  Measured on the MI355X:
+# dalpha 3.3e-2 (mu 0), 0.25 (mu -2), 3.7e-2 (alpha 0.02 on some channels); every other
+# gradient stays at 1.4e-3 .. 6.8e-3.  These cases document that limit until the pair
+# sums are formed without the cancellation.
+DALPHA_FAST = pytest.mark.xfail(strict=True, reason="chunked backward: dalpha error grows like 1/alpha "
+                                "(cancelling bf16 pair terms in the reverse cumulative sum of dG)")
+
+
+@pytest.mark.parametrize("case", [pytest.param(c, marks=DALPHA_FAST) if c[5] == BF16 else c for c in FAST_CASES],
+                         ids=lambda c: f"B{c[0]}T{c[1]}H{c[2]}dk{c[3]}dv{c[4]}"
+                         f"{'bf16' if c[5] == BF16 else 'f32'}mu{c[6]:g}b{c[7]:g}")
+def test_backward_fast_decay(dev, case):
+    """alpha = sigmoid(N(mu, 1)) with mu = 0 or -2 (the workloads use 3), S0 and dS_T given."""
+    from oracle import c_oracle
+    B, T, H, dk, dv, io, mu, bs = case
+    inp = inputs.make_raw(B, T, H, dk, dv, io, T + dk, dev, s0_std=0.05, alpha_mu=mu, b_scale=bs)
+    dO, dS_T = inputs.make_out_grads(B, T, H, dk, dv, io, T + dk + 1, dev)
+    got = g.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["b"], inp["w"], dO, inp["S0"], dS_T)
+    torch.cuda.synchronize()
+    h = {n: _np(x) for n, x in inp.items()}
+    want = c_oracle.recurrent_bwd(h["q"], h["k"], h["v"], h["alpha"], h["b"], h["w"], h["S0"], _np(dO), _np(dS_T))
+    check(f"fast decay mu {mu}", {n: _np(got[n]) for n in NAMES}, want, TOL[io], chains=True)
+
+
+@DALPHA_FAST
+def test_backward_decay_002_on_some_channels(dev):
+    """alpha = 0.02 on every fifth key channel (0.02^16 = 6.6e-28 over a 16-token block)."""
+    from oracle import c_oracle
+    B, T, H, dk, dv = 1, 230, 2, 128, 64
+    inp = inputs.make_raw(B, T, H, dk, dv, BF16, 43, dev, s0_std=0.05, b_scale=2.0)
+    inp["alpha"][..., ::5] = 0.02
+    dO, dS_T = inputs.make_out_grads(B, T, H, dk, dv, BF16, 44, dev)
+    got = g.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["b"], inp["w"], dO, inp["S0"], dS_T)
+    torch.cuda.synchronize()
+    h = {n: _np(x) for n, x in inp.items()}
+    want = c_oracle.recurrent_bwd(h["q"], h["k"], h["v"], h["alpha"], h["b"], h["w"], h["S0"], _np(dO), _np(dS_T))
+    check("alpha 0.02 on some channels", {n: _np(got[n]) for n in NAMES}, want, 2e-2, chains=True)
 
 
 def test_backward_deterministic(dev):
@@ -190,10 +249,11 @@ def test_backward_grouped_heads_equal_widened_call(dev):
         assert rel_l2(_np(g1[n]), _np(s)) < 1e-2, n
 
 
-def test_backward_full_size_with_options_sampled(dev):
+def test_backward_full_size_with_options_all_chains(dev):
     """B4 H16 T2048 d128 bf16 with gate logits in bf16, negative eigenvalues and the
-    q/k norm: sampled (batch, head) chains against full_bwd."""
-    from oracle.backward import full_bwd
+    q/k norm: every (batch, head) chain against the fp64 C backward oracle with the same
+    options."""
+    from oracle import c_oracle
     B, T, H, dk, dv = 4, 2048, 16, 128, 128
     fl = LOG | NEG | L2
     inp = inputs.make_raw(B, T, H, dk, dv, BF16, 78, dev, gate_dtype=BF16, gate_logits=True, unit_qk=False)
@@ -201,14 +261,9 @@ def test_backward_full_size_with_options_sampled(dev):
     got = g.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["b"], inp["w"], dO, None, dS_T, flags=fl)
     torch.cuda.synchronize()
     h = {n: _np(x) for n, x in inp.items()}
-    dOn, dSn = _np(dO), _np(dS_T)
-    for bi, hi in [(0, 0), (3, 15)]:
-        sl = lambda x: x[bi:bi + 1, :, hi:hi + 1]
-        want = full_bwd(sl(h["q"]), sl(h["k"]), sl(h["v"]), sl(h["alpha"]), sl(h["b"]), sl(h["w"]), None,
-                        sl(dOn), dSn[bi:bi + 1, hi:hi + 1], flags=fl)
-        gs = {n: (_np(got[n])[bi:bi + 1, :, hi:hi + 1] if n != "dS0" else _np(got[n])[bi:bi + 1, hi:hi + 1])
-              for n in NAMES}
-        check(f"B4H16T2048 flags {fl} chain ({bi},{hi})", gs, want, 2e-2)
+    want = c_oracle.recurrent_bwd(h["q"], h["k"], h["v"], h["alpha"], h["b"], h["w"], None, _np(dO), _np(dS_T),
+                                  flags=fl)
+    check(f"B4H16T2048 flags {fl} all chains", {n: _np(got[n]) for n in NAMES}, want, 2e-2, chains=True)
 
 
 @pytest.mark.parametrize("flags", [0, LOG | NEG | L2])

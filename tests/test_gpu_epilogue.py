@@ -64,10 +64,14 @@ def test_gated_rmsnorm_in_place_after_the_chunked_forward(dev):
 
 
 def test_gated_rmsnorm_full_chunk_size(dev):
-    """The chunked workload's o (B4 H16 T2048 dv128), sampled rows against the oracle."""
+    """The chunked workload's o (B4 H16 T2048 dv128): the whole tensor against the oracle,
+    and the worst (token, head) row held to the same bar."""
     o, gt, wt = _draw(dev, (4, 2048, 16, 128), torch.bfloat16, seed=5)
     y = g.gated_rmsnorm(o, gt, wt)
     torch.cuda.synchronize()
-    idx = (np.array([0, 1, 3]), np.array([0, 1000, 2047]), np.array([0, 7, 15]))
-    ref = gated_rmsnorm(_np(o)[idx], _np(gt)[idx], _np(wt))
-    assert rel_l2(_np(y)[idx], ref) <= 2e-2
+    ref = gated_rmsnorm(_np(o), _np(gt), _np(wt))
+    yn = _np(y).astype(np.float64)
+    e = rel_l2(yn, ref)
+    rows = np.linalg.norm((yn - ref).reshape(-1, 128), axis=1) / np.linalg.norm(ref.reshape(-1, 128), axis=1)
+    print(f"[parity] gated_rmsnorm B4 H16 T2048: relL2 {e:.3e}, worst row {rows.max():.3e}", flush=True)
+    assert e <= 2e-2 and rows.max() <= 2e-2

@@ -4,9 +4,10 @@ Every comparison feeds both sides the same seeded inputs (bf16 inputs are
 widened exactly for the oracle) and measures the relative L2 error over the
 whole tensor, for o and for the final state separately:
     <= 1e-4 for fp32 I/O, <= 2e-2 for bf16 I/O with the fp32 state.
-Full-size workloads are compared on sampled (batch, head) chains, which the
-recurrence keeps independent, with the GPU run in exactly the launch
-configuration the benchmark times.
+Full-size workloads are compared on every (batch, head) chain against the
+fp64 C oracle, with the GPU run in exactly the launch configuration the
+benchmark times; the worst chain's error is reported beside the global one
+(and held to the same bar).
 """
 import numpy as np
 import pytest
@@ -15,7 +16,7 @@ import torch
 import gated_delta_rule_19_amd as g
 from gated_delta_rule_19_amd import inputs
 from oracle import c_oracle
-from oracle.reference import chunked_wy, rel_l2
+from oracle.reference import chunked_wy, rel_l2, rel_l2_chains
 
 pytestmark = pytest.mark.gpu
 
@@ -58,12 +59,22 @@ def pick(o, S, chains):
             np.stack([Sn[bi, hi] for bi, hi in chains]))
 
 
-def check(what, o, S, ref_o, ref_S, tol):
-    eo = rel_l2(_np(o) if torch.is_tensor(o) else o, ref_o)
-    eS = rel_l2(_np(S) if torch.is_tensor(S) else S, ref_S)
-    print(f"[parity] {what}: relL2 o={eo:.3e} S={eS:.3e} (tol {tol:g})", flush=True)
+def check(what, o, S, ref_o, ref_S, tol, chain_axes=((0, 2), (0, 1))):
+    """Whole-tensor rel-L2 of o and S, and the worst (batch, head) chain of each
+    (o [B,T,H,dv] chains on axes 0, 2; S [B,H,dk,dv] on axes 0, 1; pass chain_axes=None
+    for stacked per-chain arrays, whose chains are axis 0)."""
+    on = _np(o) if torch.is_tensor(o) else o
+    Sn = _np(S) if torch.is_tensor(S) else S
+    eo, eS = rel_l2(on, ref_o), rel_l2(Sn, ref_S)
+    ax_o, ax_S = chain_axes if chain_axes is not None else ((0,), (0,))
+    wo = float(np.max(rel_l2_chains(on, ref_o, ax_o))) if on.size else 0.0
+    wS = float(np.max(rel_l2_chains(Sn, ref_S, ax_S))) if Sn.size else 0.0
+    print(f"[parity] {what}: relL2 o={eo:.3e} S={eS:.3e}; worst chain o={wo:.3e} S={wS:.3e} (tol {tol:g})",
+          flush=True)
     assert eo <= tol, f"{what}: o rel-L2 {eo:.3e} > {tol}"
     assert eS <= tol, f"{what}: S rel-L2 {eS:.3e} > {tol}"
+    assert wo <= tol, f"{what}: worst chain o rel-L2 {wo:.3e} > {tol}"
+    assert wS <= tol, f"{what}: worst chain S rel-L2 {wS:.3e} > {tol}"
 
 
 def make(dev, B, T, H, dk, dv, dt, seed, s0=None, b_scale=1.0, alpha_mu=3.0):
@@ -270,7 +281,7 @@ def test_recall_invariant_gpu(dev):
 
 
 # ---------------------------------------------------------------------------
-# full-size workloads (sampled chains), launched exactly as the benchmark does
+# full-size workloads, every chain, launched exactly as the benchmark does
 # ---------------------------------------------------------------------------
 def _full(dev, idx, seed):
     wl = inputs.WORKLOADS[idx]
@@ -281,11 +292,8 @@ def test_full_chunk_B4_H16_T2048(dev):
     wl, inp = _full(dev, 1, seed=1)
     o, S = g.chunk_fwd(*args(inp), inp["S0"])
     torch.cuda.synchronize()
-    chains = [(0, 0), (1, 7), (2, 11), (3, 15)]
-    ro, rS = oracle(inp, chains=chains)
-    go, gS = pick(o, S, chains)
-    check("full chunk B4 H16 T2048 (4 heads)", go, gS, ro, rS, 2e-2)
-    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
+    ro, rS = oracle(inp)
+    check("full chunk B4 H16 T2048 (all 64 chains)", o, S, ro, rS, 2e-2)
 
 
 def test_full_decode_B256_H16(dev):
@@ -294,29 +302,65 @@ def test_full_decode_B256_H16(dev):
     ro, rS = oracle(inp)
     o, _ = g.recurrent_step(*args(inp), S, inplace=True)
     torch.cuda.synchronize()
-    check("full decode B256 H16 (all heads)", o, S, ro, rS, 2e-2)
+    check("full decode B256 H16 (all 4096 chains)", o, S, ro, rS, 2e-2)
 
 
 def test_full_chunk_B1_H16_T65536(dev):
     wl, inp = _full(dev, 3, seed=3)
     o, S = g.chunk_fwd(*args(inp), inp["S0"])
     torch.cuda.synchronize()
-    chains = [(0, 5)]
-    ro, rS = oracle(inp, chains=chains)
-    go, gS = pick(o, S, chains)
-    check("full chunk B1 H16 T65536 (1 head)", go, gS, ro, rS, 2e-2)
-    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
+    ro, rS = oracle(inp)
+    check("full chunk B1 H16 T65536 (all 16 chains)", o, S, ro, rS, 2e-2)
 
 
 def test_full_chunk_B8_H16_T4096_dv256(dev):
     wl, inp = _full(dev, 4, seed=4)
     o, S = g.chunk_fwd(*args(inp), inp["S0"])
     torch.cuda.synchronize()
-    chains = [(0, 3), (7, 12)]
-    ro, rS = oracle(inp, chains=chains)
-    go, gS = pick(o, S, chains)
-    check("full chunk B8 H16 T4096 dv256 (2 heads)", go, gS, ro, rS, 2e-2)
-    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
+    ro, rS = oracle(inp)
+    check("full chunk B8 H16 T4096 dv256 (all 128 chains)", o, S, ro, rS, 2e-2)
+
+
+# ---------------------------------------------------------------------------
+# fast decay (alpha well below the workloads' sigmoid(N(3, 1))), both modes
+# ---------------------------------------------------------------------------
+FAST = [
+    # B, T, H, dk, dv, dtype, alpha_mu, b scale
+    (1, 300, 2, 128, 128, torch.bfloat16, 0.0, 2.0),
+    (2, 257, 2, 128, 64, torch.bfloat16, -2.0, 1.0),
+    (1, 200, 3, 64, 32, torch.float32, 0.0, 2.0),
+    (1, 230, 2, 32, 48, torch.float32, -2.0, 2.0),
+]
+
+
+def _fid(c):
+    B, T, H, dk, dv, dt, mu, bs = c
+    return f"B{B}T{T}H{H}dk{dk}dv{dv}{'bf16' if dt == torch.bfloat16 else 'f32'}mu{mu:g}b{bs:g}"
+
+
+@pytest.mark.parametrize("case", FAST, ids=_fid)
+def test_fast_decay_both_modes(dev, case):
+    B, T, H, dk, dv, dt, mu, bs = case
+    inp = make(dev, B, T, H, dk, dv, dt, seed=T + 3, s0=0.05, b_scale=bs, alpha_mu=mu)
+    ro, rS = oracle(inp)
+    for fn in (g.chunk_fwd, g.recurrent_step):
+        o, S = fn(*args(inp), inp["S0"])
+        torch.cuda.synchronize()
+        check(f"fast decay {fn.__name__} {_fid(case)}", o, S, ro, rS, TOL[dt])
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32])
+def test_decay_002_on_some_channels(dev, dt):
+    """alpha = 0.02 on every fifth key channel for every token (the product over a
+    16-token block is 0.02^16 = 6.6e-28), the workload's draw elsewhere."""
+    B, T, H, dk, dv = 1, 260, 2, 128, 64
+    inp = make(dev, B, T, H, dk, dv, dt, seed=41, s0=0.05, b_scale=2.0)
+    inp["alpha"][..., ::5] = 0.02
+    ro, rS = oracle(inp)
+    for fn in (g.chunk_fwd, g.recurrent_step):
+        o, S = fn(*args(inp), inp["S0"])
+        torch.cuda.synchronize()
+        check(f"alpha 0.02 on some channels {fn.__name__} {dt}", o, S, ro, rS, TOL[dt])
 
 
 def test_tiny_fp32_workload_both_modes(dev):

@@ -189,3 +189,100 @@ def test_full_bwd_without_options_is_recurrent_bwd():
     g2 = full_bwd(*(x[m] for m in NAMES), dO, dS, flags=0)
     for n in g1:
         np.testing.assert_array_equal(g1[n], g2[n])
+
+
+# ---- the C backward oracle (gdn2_oracle_bwd_f64) ------------------------------------
+def _fp32_exact(x):
+    """Round every input to float32 (the C routine takes float32 and widens it exactly),
+    so that both sides differentiate at the same point."""
+    return {n: (None if a is None else a.astype(np.float32).astype(np.float64)) for n, a in x.items()}
+
+
+def _fd_subset(x, dO, dS, flags, picks, h=1e-6):
+    """Central differences of loss(prologue -> recurrence) at the listed (input, index) pairs."""
+    from oracle.reference import prologue
+
+    def fwd(y):
+        pq, pk, pa, pb, pw = prologue(y["q"], y["k"], y["alpha"], y["b"], y["w"], flags)
+        o, S = recurrent(pq, pk, y["v"], pa, pb, pw, y["S0"])
+        return loss(o, S, dO, dS)
+    out = []
+    for n, idx in picks:
+        vals = []
+        for s in (h, -h):
+            y = {m: a.copy() for m, a in x.items()}
+            y[n][idx] += s
+            vals.append(fwd(y))
+        out.append((vals[0] - vals[1]) / (2 * h))
+    return np.array(out)
+
+
+@pytest.mark.parametrize("T,flags", [(1, 0), (6, 0), (6, 1), (5, 3), (6, 4), (7, 7)])
+def test_c_bwd_matches_finite_differences(T, flags):
+    """Every element of every input, short sequences, each prologue option."""
+    from oracle import c_oracle
+    rng = np.random.default_rng(60 + T + flags)
+    x, dO, dS = _draw(rng, T=T, dk=3, dv=2)
+    if flags & 1:
+        x["alpha"] = rng.standard_normal(x["alpha"].shape) + 2
+        x["b"] = rng.standard_normal(x["b"].shape)
+        x["w"] = rng.standard_normal(x["w"].shape)
+    if flags & 4:
+        x["q"] = x["q"] * 2
+        x["k"] = rng.standard_normal(x["k"].shape)
+    x = _fp32_exact(x)
+    dO, dS = dO.astype(np.float32).astype(np.float64), dS.astype(np.float32).astype(np.float64)
+    g = c_oracle.recurrent_bwd(*(x[m] for m in NAMES), dO, dS, flags=flags)
+    picks = [(n, idx) for n in NAMES for idx in np.ndindex(*x[n].shape)]
+    fd = _fd_subset(x, dO, dS, flags, picks)
+    got = np.array([g["d" + n][idx] for n, idx in picks])
+    err = np.max(np.abs(got - fd)) / max(1.0, np.max(np.abs(fd)))
+    assert err < 1e-7, f"max error {err:.2e} against finite differences"
+
+
+def test_c_bwd_across_checkpoint_spans():
+    """A 140-token sequence (three 64-token replay spans, the last one ragged): the
+    elements at and around the span edges and a random sample elsewhere."""
+    from oracle import c_oracle
+    rng = np.random.default_rng(71)
+    x, dO, dS = _draw(rng, B=1, T=140, H=2, dk=3, dv=2)
+    x = _fp32_exact(x)
+    dO, dS = dO.astype(np.float32).astype(np.float64), dS.astype(np.float32).astype(np.float64)
+    g = c_oracle.recurrent_bwd(*(x[m] for m in NAMES), dO, dS)
+    picks = [("S0", (0, 1, 2, 1)), ("S0", (0, 0, 0, 0))]
+    for t in (0, 62, 63, 64, 65, 127, 128, 129, 139):
+        for n in ("q", "k", "alpha", "b"):
+            picks.append((n, (0, t, 1, t % 3)))
+        for n in ("v", "w"):
+            picks.append((n, (0, t, 0, t % 2)))
+    for _ in range(30):
+        n = NAMES[rng.integers(0, 6)]
+        picks.append((n, tuple(int(rng.integers(0, s)) for s in x[n].shape)))
+    fd = _fd_subset(x, dO, dS, 0, picks)
+    got = np.array([g["d" + n][idx] for n, idx in picks])
+    err = np.max(np.abs(got - fd)) / max(1.0, np.max(np.abs(fd)))
+    assert err < 1e-7, f"max error {err:.2e} against finite differences"
+
+
+@pytest.mark.parametrize("flags", [0, 1, 3, 4, 7])
+def test_c_bwd_equals_numpy_bwd(flags):
+    """The C routine and ``full_bwd`` on a larger shape (several chains, 150 tokens)."""
+    from oracle import c_oracle
+    from oracle.backward import full_bwd
+    rng = np.random.default_rng(80 + flags)
+    x, dO, dS = _draw(rng, B=2, T=150, H=3, dk=8, dv=5)
+    if flags & 1:
+        x["alpha"] = rng.standard_normal(x["alpha"].shape) + 3
+        x["b"] = rng.standard_normal(x["b"].shape)
+        x["w"] = rng.standard_normal(x["w"].shape)
+    x = _fp32_exact(x)
+    dO, dS = dO.astype(np.float32).astype(np.float64), dS.astype(np.float32).astype(np.float64)
+    g1 = c_oracle.recurrent_bwd(*(x[m] for m in NAMES), dO, dS, flags=flags)
+    g2 = full_bwd(*(x[m] for m in NAMES), dO, dS, flags=flags)
+    for n in g1:
+        assert rel_l2(g1[n], g2[n]) < 1e-12, n
+    # no initial state, no state gradient
+    g3 = c_oracle.recurrent_bwd(*(x[m] for m in NAMES[:6]), None, dO, None, flags=flags)
+    g4 = full_bwd(*(x[m] for m in NAMES[:6]), None, dO, None, flags=flags)
+    for n in g3:
+        assert rel_l2(g3[n], g4[n]) < 1e-12, n
