@@ -20,6 +20,8 @@ from ._binding import (  # noqa: F401
     chunk_bwd_varlen,
     chunk_bwd_workspace_size,
     chunk_fwd,
+    chunk_fwd_noalloc,
+    NOALLOC_SCRATCH_BYTES,
     chunk_fwd_varlen,
     chunk_fwd_varlen_workspace_size,
     chunk_fwd_workspace_size,

@@ -27,7 +27,8 @@ EXPORTED = ("gdn2_abi_version", "gdn2_status_str", "gdn2_chunk_fwd_workspace_siz
             "gdn2_gated_rmsnorm", "gdn2_chunk_fwd_varlen_workspace_size", "gdn2_chunk_fwd_varlen",
             "gdn2_recurrent_varlen", "gdn2_chunk_bwd_workspace_size", "gdn2_chunk_bwd",
             "gdn2_short_conv", "gdn2_short_conv_bwd_workspace_size", "gdn2_short_conv_bwd",
-            "gdn2_chunk_bwd_varlen_workspace_size", "gdn2_chunk_bwd_varlen")
+            "gdn2_chunk_bwd_varlen_workspace_size", "gdn2_chunk_bwd_varlen", "gdn2_chunk_fwd_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class Problem(ctypes.Structure):
@@ -68,6 +69,8 @@ def lib():
         L.gdn2_chunk_fwd_workspace_size.argtypes = [P]
         L.gdn2_chunk_fwd.restype = ctypes.c_int
         L.gdn2_chunk_fwd.argtypes = [P] + [vp] * 9 + [vp, sz, vp]
+        L.gdn2_chunk_fwd_noalloc.restype = ctypes.c_int
+        L.gdn2_chunk_fwd_noalloc.argtypes = [P] + [vp] * 9 + [vp]
         L.gdn2_chunk_prep.restype = ctypes.c_int
         L.gdn2_chunk_prep.argtypes = [P] + [vp] * 6 + [vp, sz, vp]
         L.gdn2_chunk_state.restype = ctypes.c_int
@@ -192,6 +195,20 @@ def chunk_fwd(q, k, v, alpha, b, w, S0=None, *, out_state: bool = True, o=None, 
     _check(lib().gdn2_chunk_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w),
                                 _ptr(S0), _ptr(o), _ptr(S_out), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(dev)))
+    return o, S_out
+
+
+def chunk_fwd_noalloc(q, k, v, alpha, b, w, S0=None, *, o, S_out=None, flags: int = 0):
+    """Chunked forward with the library's own fixed workspace (``gdn2_chunk_fwd_noalloc``):
+    the call allocates nothing, so the caller passes the outputs ``o`` (and ``S_out`` for
+    the final state).  Returns (o, S_out)."""
+    p, dev = _problem_from(q, k, v, alpha, b, w, flags)
+    _check_state(S0, p, dev, "S0")
+    _check_state(S_out, p, dev, "S_out")
+    if tuple(o.shape) != tuple(v.shape) or o.dtype != v.dtype or o.device != dev or not o.is_contiguous():
+        raise ValueError("o must be a contiguous tensor shaped and typed like v")
+    _check(lib().gdn2_chunk_fwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b),
+                                        _ptr(w), _ptr(S0), _ptr(o), _ptr(S_out), _stream(dev)))
     return o, S_out
 
 

@@ -423,6 +423,37 @@ int gdn2_chunk_fwd(const gdn2_problem* p, const void* q, const void* k, const vo
     return do_state(p, S0, o, S_out, workspace, s);
 }
 
+int gdn2_chunk_fwd_noalloc(const gdn2_problem* p, const void* q, const void* k, const void* v,
+                           const void* alpha, const void* b, const void* w, const float* S0, void* o,
+                           float* S_out, void* stream)
+{
+    int st = check_problem(p, true);
+    if (st) return st;
+    st = check_inputs(p, q, k, v, alpha, b, w, o);
+    if (st) return st;
+    const int64_t need = ws_bytes(p);
+    if (need > static_cast<int64_t>(GDN2_NOALLOC_SCRATCH_BYTES)) return GDN2_ERR_WORKSPACE;
+    const Sizes z = sizes_of(p);
+    const Range ins[7] = {range_of(q, z.key),  range_of(k, z.key),  range_of(v, z.val),
+                          range_of(alpha, z.gk), range_of(b, z.gk), range_of(w, z.gv),
+                          range_of(S0, z.state)};
+    const Range outs[2] = {range_of(o, z.val), range_of(S_out, z.state)};
+    st = check_alias(outs, 2, ins, 7, S0, S_out, 6, 1);
+    if (st) return st;
+    st = check_align({q, k, v, alpha, b, w, S0, o, S_out});
+    if (st) return st;
+    if (p->B * p->H == 0 || (nchunks(p) == 0 && S_out == S0)) return GDN2_OK;
+    st = device_ready();
+    if (st) return st;
+    // the device address of this GPU's copy of the library's scratch array
+    void* ws = need > 0 ? gdn2::noalloc_scratch() : nullptr;
+    if (need > 0 && ws == nullptr) return GDN2_ERR_DEVICE;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    st = do_prep(p, q, k, v, alpha, b, w, ws, s);
+    if (st) return st;
+    return do_state(p, S0, o, S_out, ws, s);
+}
+
 int gdn2_recurrent_step(const gdn2_problem* p, const void* q, const void* k, const void* v,
                         const void* alpha, const void* b, const void* w, const float* S_in, void* o,
                         float* S_out, void* stream)

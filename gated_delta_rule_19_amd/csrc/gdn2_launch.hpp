@@ -170,6 +170,11 @@ bool gradmf_supported(int dk, int dv, bool bf16);
 int64_t grad_blocks(int64_t total);
 int64_t chunk_grad_scratch_bytes(int dk, int dv, int64_t total);
 
+// gdn2_chunk_fwd_noalloc's workspace: the device address of the current
+// device's copy of the library's fixed scratch array (GDN2_NOALLOC_SCRATCH_BYTES),
+// looked up once per device; nullptr when there is no usable device.
+void* noalloc_scratch();
+
 // int32 words of the varlen plan ahead of its chunk table (kept even so the
 // 8-byte table entries stay aligned)
 __host__ __device__ inline int64_t plan_head_words(int64_t N) { return 2 * (N + 1); }

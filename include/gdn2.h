@@ -169,6 +169,27 @@ int gdn2_chunk_state(const gdn2_problem* p, const float* S0, void* o, float* S_o
                      const void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gdn2_chunk_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same computation, arguments (minus the workspace), checks and launches as
+ * gdn2_chunk_fwd; the workspace is a fixed device array inside the library
+ * (GDN2_NOALLOC_SCRATCH_BYTES, 64 MiB on every GPU the library runs on, held
+ * until the process ends), so the call allocates nothing.  A problem whose
+ * workspace (gdn2_chunk_fwd_workspace_size) is larger returns
+ * GDN2_ERR_WORKSPACE before anything runs; d128 bf16 needs 1,160 bytes per
+ * (token, value head), e.g. B1 T2048 H16 = 38 MB.  All calls on one GPU share
+ * that GPU's array: calls whose work overlaps in time on one GPU (other
+ * streams, other threads) race and give undefined results; calls in one
+ * stream's order are safe.  Nothing in the array needs to start at zero.
+ */
+#define GDN2_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+int gdn2_chunk_fwd_noalloc(const gdn2_problem* p,
+                           const void* q, const void* k, const void* v,
+                           const void* alpha, const void* b, const void* w,
+                           const float* S0, void* o, float* S_out, void* stream);
+
+/*
  * Fused recurrent forward (README: "Fused Recurrent", token-by-token
  * inference with a persistent state).  Processes the T tokens one after the
  * other from S_in (NULL = zero state), writes o for each token and, if

@@ -1,0 +1,63 @@
+"""gdn2_chunk_fwd_noalloc: the chunked forward with the library's fixed workspace.
+
+For callers that cannot allocate (graph capture, serving loops).  It runs the
+same kernels as gdn2_chunk_fwd with the workspace in a static device array, so
+its outputs must equal gdn2_chunk_fwd's bit for bit; two calls in a row (the
+second smaller) check that nothing from the first call leaks into the second.
+The host checks (a problem too large for the array) need no GPU.
+"""
+import ctypes
+
+import pytest
+import torch
+
+import gated_delta_rule_19_amd as g
+from gated_delta_rule_19_amd import _binding as bnd
+from gated_delta_rule_19_amd import inputs
+
+
+def _args(inp):
+    return inp["q"], inp["k"], inp["v"], inp["alpha"], inp["b"], inp["w"]
+
+
+def test_too_large_is_rejected_on_the_host():
+    # d128 bf16 needs 1,160 B per (token, value head): B1 T4096 H16 = 76 MB > 64 MiB
+    p = bnd.problem(1, 4096, 16, 128, 128, torch.bfloat16)
+    assert g.chunk_fwd_workspace_size(1, 4096, 16, 128, 128, torch.bfloat16) > g.NOALLOC_SCRATCH_BYTES
+    fake = ctypes.c_void_p(1 << 20)        # never dereferenced: the size check comes first
+    code = g.lib().gdn2_chunk_fwd_noalloc(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, fake,
+                                          None, None)
+    assert code == 5                       # GDN2_ERR_WORKSPACE
+    p2 = bnd.problem(1, 64, 16, 100, 128, torch.bfloat16)   # invalid dk: the shape error comes first
+    assert g.lib().gdn2_chunk_fwd_noalloc(ctypes.byref(p2), fake, fake, fake, fake, fake, fake, None, fake,
+                                          None, None) == 2
+
+
+@pytest.mark.gpu
+def test_noalloc_equals_chunk_fwd_two_calls():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    g.lib()
+    dev = torch.device("cuda:0")
+    # first call: B2 T1000 H12 d128 bf16 (2 x 12 x 16 chunks x 74,240 B = 28.5 MB of workspace)
+    big = inputs.make_raw(2, 1000, 12, 128, 128, torch.bfloat16, 31, dev, s0_std=0.05, b_scale=2.0)
+    # second call, smaller: B1 T300 H4 dk64 dv96, zero initial state
+    small = inputs.make_raw(1, 300, 4, 64, 96, torch.bfloat16, 32, dev)
+    for inp in (big, small):
+        o_ref, S_ref = g.chunk_fwd(*_args(inp), inp["S0"])
+        o = torch.full_like(o_ref, float("nan"))
+        S = torch.full_like(S_ref, float("nan"))
+        g.chunk_fwd_noalloc(*_args(inp), inp["S0"], o=o, S_out=S)
+        torch.cuda.synchronize()
+        print(f"[noalloc] {tuple(inp['v'].shape)}: equal o {torch.equal(o, o_ref)} S {torch.equal(S, S_ref)}",
+              flush=True)
+        assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
+    # the first shape again after the smaller one, and fp32 I/O
+    f32 = inputs.make_raw(1, 130, 2, 32, 48, torch.float32, 33, dev, s0_std=0.05)
+    for inp in (big, f32):
+        o_ref, S_ref = g.chunk_fwd(*_args(inp), inp["S0"])
+        o = torch.empty_like(o_ref)
+        S = torch.empty_like(S_ref)
+        g.chunk_fwd_noalloc(*_args(inp), inp["S0"], o=o, S_out=S)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
