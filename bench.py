@@ -38,7 +38,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 UTIL_FILE = os.path.join(ROOT, "profiles", "pmc_util.json")
 KERNEL_SOURCES = ["gated_delta_rule_19_amd/csrc/gdn2_chunk.hip", "gated_delta_rule_19_amd/csrc/gdn2_recurrent.hip",
                   "gated_delta_rule_19_amd/csrc/gdn2_device.hpp", "gated_delta_rule_19_amd/csrc/gdn2_layout.hpp"]
-KERNEL_NAMES = {"prep": "k_chunk_prep", "state": "k_chunk_state", "decode": "k_recurrent"}
+KERNEL_NAMES = {"prep": "k_chunk_prep", "state": "k_chunk_state", "decode": "k_decode"}
 
 
 def kernel_sha() -> str:
@@ -235,7 +235,6 @@ def main(argv=None):
     B, T, H, dk, dv = wl_c.B, wl_c.T, wl_c.H, wl_c.dk, wl_c.dv
     sets = [inputs.make(wl_c, seed=100 + i, device=dev) for i in range(args.sets)]
     dsets = [inputs.make(wl_d, seed=200 + i, device=dev) for i in range(args.sets)]
-    prob = g.problem(B, T, H, dk, dv, wl_c.io_dtype)
     ws = g.alloc_workspace(g.chunk_fwd_workspace_size(B, T, H, dk, dv, wl_c.io_dtype), dev)
     outs = [torch.empty_like(s["v"]) for s in sets]
     states = [torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev) for _ in sets]
@@ -247,12 +246,9 @@ def main(argv=None):
         s = i % len(sets)
         if ev is not None:
             ev[0].record()
-        g.chunk_prep(*A(sets[s]), ws)
+        g.chunk_fwd(*A(sets[s]), sets[s]["S0"], o=outs[s], S_out=states[s], workspace=ws)
         if ev is not None:
             ev[1].record()
-        g.chunk_state(prob, ws, outs[s], sets[s]["S0"], states[s])
-        if ev is not None:
-            ev[2].record()
 
     def decode(i, ev=None):
         d = i % len(dsets)
@@ -266,7 +262,7 @@ def main(argv=None):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -283,57 +279,69 @@ def main(argv=None):
     for i in range(args.steps):
         decode(args.warmup + i, dev_evs[i])
     torch.cuda.synchronize()
-    per_step = {"prep": sorted(e[0].elapsed_time(e[1]) for e in evs),
-                "state": sorted(e[1].elapsed_time(e[2]) for e in evs),
+    # the decode step with the layer's output step fused (gated RMS norm on the token's
+    # row), and the same as two launches (decode, then the separate output step)
+    gts = [torch.randn(d["v"].shape, device=dev).to(d["v"].dtype) for d in dsets]
+    nw = torch.ones(wl_d.dv, device=dev)
+    ys = [torch.empty_like(d["v"]) for d in dsets]
+    gated_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    sep_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for which, evl in ((0, gated_evs), (1, sep_evs)):
+        for i in range(args.warmup + args.steps):
+            d = i % len(dsets)
+            ev = evl[i - args.warmup] if i >= args.warmup else None
+            if ev:
+                ev[0].record()
+            if which == 0:
+                g.recurrent_step_gated(*A(dsets[d]), gts[d], nw, dsets[d]["S0"], y=ys[d], inplace=True)
+            else:
+                g.recurrent_step(*A(dsets[d]), dsets[d]["S0"], o=douts[d], inplace=True)
+                g.gated_rmsnorm(douts[d], gts[d], nw, out=ys[d])
+            if ev:
+                ev[1].record()
+    torch.cuda.synchronize()
+    per_step = {"chunk": sorted(e[0].elapsed_time(e[1]) for e in evs),
                 "decode": sorted(e[0].elapsed_time(e[1]) for e in dev_evs),
-                "chunk": sorted(e[0].elapsed_time(e[2]) for e in evs)}
-    prep_ms = sum(per_step["prep"]) / args.steps
-    state_ms = sum(per_step["state"]) / args.steps
+                "decode_gated": sorted(e[0].elapsed_time(e[1]) for e in gated_evs),
+                "decode_sep": sorted(e[0].elapsed_time(e[1]) for e in sep_evs)}
     dec_ms = sum(per_step["decode"]) / args.steps
     spread = {k_: {"median_us": round(v_[len(v_) // 2] * 1e3, 2), "min_us": round(v_[0] * 1e3, 2)}
               for k_, v_ in per_step.items()}
     copy_gbps = device_copy_gbps(dev)
-    chunk_ms = prep_ms + state_ms
+    chunk_ms = sum(per_step["chunk"]) / args.steps
+    # the two launches of the same call timed apart (prep, then the state pass)
+    split = split_leg(g, wl_c, sets, dev, args)
 
     ht = B * T * H
     tokens = B * T
     bpht = chunk_bytes_per_ht(dk, dv)
     alg_chunk = bpht * ht + B * H * dk * dv * 4                   # + final state written
-    alg_prep = (bpht - 2 * dv) * ht                               # inputs read
-    alg_state = 2 * dv * ht + B * H * dk * dv * 4                 # o + final state written
     alg_dec = decode_bytes(wl_d.B, wl_d.H, wl_d.dk, wl_d.dv)
     flops = chunk_flops_per_ht(dk, dv) * ht
     gbps = lambda byts, ms: byts / (ms * 1e-3) / 1e9
 
-    kern = {
-        "prep": dict(ms=prep_ms, alg=alg_prep),
-        "state": dict(ms=state_ms, alg=alg_state),
-        "decode": dict(ms=dec_ms, alg=alg_dec),
-    }
-    dom = max(("prep", "state"), key=lambda k_: kern[k_]["ms"])   # the timed step: the chunked forward
-
-    def roof(key):
-        k_ = kern[key]
-        ach = gbps(k_["alg"], k_["ms"])
+    def roof(key, alg, ms, sp):
+        ach = gbps(alg, ms)
         tr = load_traffic(key)
         r = {"kernel": KERNEL_NAMES[key], "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS,
              "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBPS, 4),
-             "traffic": None if tr is None else round(tr), "alg_bytes": int(k_["alg"]),
-             "us_per_launch": round(k_["ms"] * 1e3, 2)}
-        r.update(spread[key])
+             "traffic": None if tr is None else round(tr), "alg_bytes": int(alg),
+             "us_per_launch": round(ms * 1e3, 2)}
+        r.update(sp)
         u = load_util(key)
         if u is not None and "MfmaUtil" in u:
             r["mfma_busy_pct"] = round(u["MfmaUtil"], 2)
         return r
 
     chunk_gbps = gbps(alg_chunk, chunk_ms)
+    # the whole forward call (its two launches): algorithmic bytes over the call's time;
+    # traffic = both kernels' counter bytes
     tr_p, tr_s = load_traffic("prep"), load_traffic("state")
-    whole = {"kernel": "whole chunked forward call (k_chunk_prep + k_chunk_state)", "bound": "hbm",
-             "achieved": round(chunk_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-             "frac": round(chunk_gbps / PEAK_HBM_GBPS, 4),
-             "traffic": None if tr_p is None or tr_s is None else round(tr_p + tr_s),
-             "alg_bytes": int(alg_chunk), "us_per_launch": round(chunk_ms * 1e3, 2)}
-    whole.update(spread["chunk"])
+    whole_roof = {"kernel": "k_chunk_prep + k_chunk_state (the whole chunked forward call)", "bound": "hbm",
+                  "achieved": round(chunk_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                  "frac": round(chunk_gbps / PEAK_HBM_GBPS, 4),
+                  "traffic": None if tr_p is None or tr_s is None else round(tr_p + tr_s),
+                  "alg_bytes": int(alg_chunk), "us_per_launch": round(chunk_ms * 1e3, 2), **spread["chunk"]}
     result = {
         "metric": "chunk-fwd tokens/s (B4 H16 T2048 d128) + decode-step HBM GB/s; % roofline",
         "value": round(tokens / (chunk_ms * 1e-3), 1),
@@ -351,22 +359,35 @@ def main(argv=None):
                                "decode step B256 H16 d128 (fp32 state in place) timed in a loop of its own",
                    "global_batch": B, "seq_len": T, "heads": H, "dk": dk, "dv": dv, "chunk": 64,
                    "parallelism": "single GPU", "rotated_input_sets": args.sets},
-        "roofline": whole,
-        "chunk_fwd": {"dominant_kernel": KERNEL_NAMES[dom], "us": round(chunk_ms * 1e3, 2), "prep_us": round(prep_ms * 1e3, 2),
-                      "state_us": round(state_ms * 1e3, 2), "alg_GBps": round(chunk_gbps, 1),
+        "roofline": whole_roof,
+        "chunk_fwd": {"kernels": "k_chunk_prep (per-chunk factors to a workspace), then k_chunk_state "
+                                 "(the chunks in order, state in matrix-core accumulators)",
+                      "us": round(chunk_ms * 1e3, 2), "alg_GBps": round(chunk_gbps, 1),
                       "frac_hbm_roofline": round(chunk_gbps / PEAK_HBM_GBPS, 4),
                       "useful_TFLOPs": round(flops / (chunk_ms * 1e-3) / 1e12, 2),
                       "frac_bf16_mfma_peak": round(flops / (chunk_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                       "median_us": spread["chunk"]["median_us"], "min_us": spread["chunk"]["min_us"],
-                      "roofline_prep": roof("prep"), "roofline_state": roof("state")},
+                      "stages": {**split,
+                                 "roofline_prep": roof("prep", (bpht - 2 * dv) * ht, split["prep_us"] * 1e-3,
+                                                       {"median_us": split["prep_median_us"]}),
+                                 "roofline_state": roof("state", 2 * dv * ht + B * H * dk * dv * 4,
+                                                        split["state_us"] * 1e-3,
+                                                        {"median_us": split["state_median_us"]})}},
         "decode": {"us": round(dec_ms * 1e3, 2), "GBps": round(gbps(alg_dec, dec_ms), 1),
                    "frac_hbm_peak": round(gbps(alg_dec, dec_ms) / PEAK_HBM_GBPS, 4),
                    "device_copy_GBps": round(copy_gbps, 1),
                    "frac_of_device_copy": round(gbps(alg_dec, dec_ms) / copy_gbps, 4),
-                   "roofline": roof("decode")},
+                   "roofline": roof("decode", alg_dec, dec_ms, spread["decode"]),
+                   "with_output_step": {
+                       "workload": "the same step with the layer's output step (gated RMS norm, SiLU gate) "
+                                   "fused into its output write: reads g, writes y instead of o",
+                       "us": round(sum(per_step["decode_gated"]) / args.steps * 1e3, 2),
+                       "median_us": spread["decode_gated"]["median_us"],
+                       "GBps": round(gbps(alg_dec + wl_d.B * wl_d.H * wl_d.dv * 2, sum(per_step["decode_gated"]) / args.steps), 1),
+                       "separate_launches_us": round(sum(per_step["decode_sep"]) / args.steps * 1e3, 2),
+                       "separate_launches_median_us": spread["decode_sep"]["median_us"]}},
     }
     if not args.no_long:
-        del ws
         result["chunk_fwd_long"] = workload_leg(g, inputs, 3, dev, args)
         result["chunk_fwd_expand_v"] = workload_leg(g, inputs, 4, dev, args)
     if not args.no_prologue:
@@ -402,8 +423,26 @@ def main(argv=None):
     return 0
 
 
-def _time_chunk(g, sets, prob, ws, outs, st, flags, steps, warmup):
-    """Time prep and state launches of the chunked forward over rotating input sets;
+def _time_fwd(g, sets, outs, sts, flags, steps, warmup):
+    """Time gdn2_chunk_fwd calls back to back over rotating input sets; returns the sorted
+    milliseconds per call."""
+    import torch
+    A = lambda x: (x["q"], x["k"], x["v"], x["alpha"], x["b"], x["w"])
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(warmup + steps):
+        j = i % len(sets)
+        ev = evs[i - warmup] if i >= warmup else None
+        if ev:
+            ev[0].record()
+        g.chunk_fwd(*A(sets[j]), sets[j]["S0"], o=outs[j], S_out=sts[j], flags=flags)
+        if ev:
+            ev[1].record()
+    torch.cuda.synchronize()
+    return sorted(e[0].elapsed_time(e[1]) for e in evs)
+
+
+def _time_split(g, sets, prob, ws, outs, st, flags, steps, warmup):
+    """Time the two stages (prep, state pass) over rotating input sets;
     returns (prep, state, total) lists of milliseconds, sorted."""
     import torch
     A = lambda x: (x["q"], x["k"], x["v"], x["alpha"], x["b"], x["w"])
@@ -416,12 +455,37 @@ def _time_chunk(g, sets, prob, ws, outs, st, flags, steps, warmup):
         g.chunk_prep(*A(x), ws, flags=flags)
         if ev:
             ev[1].record()
-        g.chunk_state(prob, ws, outs[i % len(sets)], None, st)
+        g.chunk_state(prob, ws, outs[i % len(sets)], x["S0"], st)
         if ev:
             ev[2].record()
     torch.cuda.synchronize()
     return (sorted(e[0].elapsed_time(e[1]) for e in evs), sorted(e[1].elapsed_time(e[2]) for e in evs),
             sorted(e[0].elapsed_time(e[2]) for e in evs))
+
+
+def _fwd_times(t):
+    n = len(t)
+    return {"us": round(sum(t) / n * 1e3, 2), "median_us": round(t[n // 2] * 1e3, 2), "min_us": round(t[0] * 1e3, 2)}
+
+
+def split_leg(g, wl, sets, dev, args):
+    """The main workload's two launches timed apart: k_chunk_prep writes every chunk's
+    factors to a workspace (1,160 B per head-token at d = 128), k_chunk_state reads them
+    back."""
+    import torch
+    B, T, H, dk, dv = wl.B, wl.T, wl.H, wl.dk, wl.dv
+    prob = g.problem(B, T, H, dk, dv, wl.io_dtype)
+    ws = g.alloc_workspace(g.chunk_prep_workspace_size(B, T, H, dk, dv, wl.io_dtype), dev)
+    outs = [torch.empty_like(x["v"]) for x in sets]
+    st = torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev)
+    steps = max(args.steps // 2, 5)
+    prep, state, tot = _time_split(g, sets, prob, ws, outs, st, 0, steps, args.warmup)
+    t = _leg_times(prep, state, tot)
+    t["prep_median_us"] = round(prep[len(prep) // 2] * 1e3, 2)
+    t["state_median_us"] = round(state[len(state) // 2] * 1e3, 2)
+    t["tokens_per_s"] = round(B * T / (t["us"] * 1e-6), 1)
+    del ws
+    return t
 
 
 def _leg_times(prep, state, tot):
@@ -434,36 +498,17 @@ def _leg_times(prep, state, tot):
 def workload_leg(g, inputs, idx, dev, args, nsets=3):
     """One of the other chunked workloads (long context B1 H16 T65536 with slow decay;
     expanded values B8 H16 T4096 dk128 dv256 with b in (0, 2) and a nonzero initial state),
-    timed like the main workload: the whole forward call (prep + state pass) back to back
-    over `nsets` rotated input sets resident in HBM.  Algorithmic bytes: the inputs read,
+    timed like the main workload: gdn2_chunk_fwd calls back to back over `nsets` rotated
+    input sets resident in HBM.  Algorithmic bytes: the inputs read,
     o written, the initial state read when there is one and the final state written."""
     import torch
     wl = inputs.WORKLOADS[idx]
     B, T, H, dk, dv = wl.B, wl.T, wl.H, wl.dk, wl.dv
     sets = [inputs.make(wl, seed=1000 * idx + i, device=dev) for i in range(nsets)]
-    prob = g.problem(B, T, H, dk, dv, wl.io_dtype)
-    ws = g.alloc_workspace(g.chunk_fwd_workspace_size(B, T, H, dk, dv, wl.io_dtype), dev)
     outs = [torch.empty_like(x["v"]) for x in sets]
     sts = [torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev) for _ in sets]
-    A = lambda x: (x["q"], x["k"], x["v"], x["alpha"], x["b"], x["w"])
     steps = max(args.steps // 3, 5)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    for i in range(args.warmup + steps):
-        j = i % nsets
-        ev = evs[i - args.warmup] if i >= args.warmup else None
-        if ev:
-            ev[0].record()
-        g.chunk_prep(*A(sets[j]), ws)
-        if ev:
-            ev[1].record()
-        g.chunk_state(prob, ws, outs[j], sets[j]["S0"], sts[j])
-        if ev:
-            ev[2].record()
-    torch.cuda.synchronize()
-    prep = sorted(e[0].elapsed_time(e[1]) for e in evs)
-    state = sorted(e[1].elapsed_time(e[2]) for e in evs)
-    tot = sorted(e[0].elapsed_time(e[2]) for e in evs)
-    t = _leg_times(prep, state, tot)
+    t = _fwd_times(_time_fwd(g, sets, outs, sts, 0, steps, args.warmup))
     ms = t["us"] * 1e-3
     ht = B * T * H
     alg = chunk_bytes_per_ht(dk, dv) * ht + B * H * dk * dv * 4 * (2 if wl.s0_std is not None else 1)
@@ -477,13 +522,12 @@ def workload_leg(g, inputs, idx, dev, args, nsets=3):
                                  + f", alpha = sigmoid(N({wl.alpha_mu:g}, 1))",
            "tokens_per_s": round(B * T / (ms * 1e-3), 1), **t, "alg_bytes": int(alg),
            "useful_GFLOP": round(flops / 1e9, 2),
-           "roofline": {"kernel": "whole chunked forward call (k_chunk_prep + k_chunk_state)", "bound": "hbm",
+           "roofline": {"kernel": "k_chunk_prep + k_chunk_state (the whole chunked forward call)", "bound": "hbm",
                         "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                         "frac": round(ach / PEAK_HBM_GBPS, 4), "t_roofline_us": round(t_roof * 1e6, 1)},
            "frac_of_roofline_time": round(t_roof / (ms * 1e-3), 4),
            "rotated_input_sets": nsets, "outputs_finite": finite,
            "_set0": {"inp": sets[0], "o": outs[0], "S": sts[0], "shape": (B, T, H, dk, dv)}}
-    del ws
     return out
 
 
@@ -496,25 +540,21 @@ def prologue_leg(g, inputs, wl, dev, args):
     flags = g.FLAG_GATE_LOGITS | g.FLAG_NEG_EIGVAL | g.FLAG_QK_L2NORM
     sets = [inputs.make_raw(B, T, H, dk, dv, wl.io_dtype, 300 + i, dev, gate_logits=True, unit_qk=False,
                             gate_dtype=torch.bfloat16) for i in range(args.sets)]
-    prob = g.problem(B, T, H, dk, dv, wl.io_dtype, gate_dtype=torch.bfloat16, flags=flags)
-    ws = g.alloc_workspace(g.chunk_fwd_workspace_size(B, T, H, dk, dv, wl.io_dtype), dev)
     outs = [torch.empty_like(x["v"]) for x in sets]
-    st = torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev)
+    sts = [torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev) for _ in sets]
+    st = sts[0]
     steps = max(args.steps // 2, 5)
-    prep, state, tot = _time_chunk(g, sets, prob, ws, outs, st, flags, steps, args.warmup)
-    t = _leg_times(prep, state, tot)
-    ms, prep_ms = t["us"] * 1e-3, t["prep_us"] * 1e-3
+    t = _fwd_times(_time_fwd(g, sets, outs, sts, flags, steps, args.warmup))
+    ms = t["us"] * 1e-3
     ht = B * T * H
     per_ht = 2 * (2 * dk + dv) + 2 * (2 * dk + dv) + 2 * dv
     alg = per_ht * ht + B * H * dk * dv * 4
-    alg_prep = (2 * (2 * dk + dv) + 2 * (2 * dk + dv)) * ht
     gbps = alg / (ms * 1e-3) / 1e9
     return {"workload": "chunk fwd B4 H16 T2048 d128, bf16 q/k/v and bf16 gate logits, flags gate-logits | "
                         "b x 2 | q/k L2 norm (prologue in-kernel), zero initial state",
             "tokens_per_s": round(B * T / (ms * 1e-3), 1), **t,
             "alg_bytes_per_head_token": per_ht,
             "alg_GBps": round(gbps, 1), "frac_hbm_roofline": round(gbps / PEAK_HBM_GBPS, 4),
-            "prep_alg_GBps": round(alg_prep / (prep_ms * 1e-3) / 1e9, 1),
             "outputs_finite": bool(torch.isfinite(outs[0].float()).all() and torch.isfinite(st).all())}
 
 
@@ -526,13 +566,11 @@ def grouped_leg(g, inputs, wl, dev, args, H=4):
     import torch
     B, T, Hv, dk, dv = wl.B, wl.T, wl.H, wl.dk, wl.dv
     sets = [inputs.make_raw(B, T, H, dk, dv, wl.io_dtype, 500 + i, dev, Hv=Hv) for i in range(args.sets)]
-    prob = g.problem(B, T, H, dk, dv, wl.io_dtype, Hv=Hv)
-    ws = g.alloc_workspace(g.chunk_fwd_workspace_size(B, T, H, dk, dv, wl.io_dtype, Hv=Hv), dev)
     outs = [torch.empty_like(x["v"]) for x in sets]
-    st = torch.empty(B, Hv, dk, dv, dtype=torch.float32, device=dev)
+    sts = [torch.empty(B, Hv, dk, dv, dtype=torch.float32, device=dev) for _ in sets]
+    st = sts[0]
     steps = max(args.steps // 2, 5)
-    prep, state, tot = _time_chunk(g, sets, prob, ws, outs, st, 0, steps, args.warmup)
-    t = _leg_times(prep, state, tot)
+    t = _fwd_times(_time_fwd(g, sets, outs, sts, 0, steps, args.warmup))
     ms = t["us"] * 1e-3
     vht = B * T * Hv
     per_vht = 2 * 2 * dk * H // Hv + 2 * dv + 4 * (2 * dk + dv) + 2 * dv

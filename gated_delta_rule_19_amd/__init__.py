@@ -26,11 +26,13 @@ from ._binding import (  # noqa: F401
     chunk_fwd_varlen_workspace_size,
     chunk_fwd_workspace_size,
     chunk_prep,
+    chunk_prep_workspace_size,
     chunk_state,
     gated_rmsnorm,
     lib,
     problem,
     recurrent_step,
+    recurrent_step_gated,
     recurrent_varlen,
     short_conv,
     short_conv_bwd,

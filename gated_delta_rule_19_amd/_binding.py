@@ -16,7 +16,7 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn2.so")
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 GDN2_F32, GDN2_BF16 = 0, 1
 FLAG_GATE_LOGITS, FLAG_NEG_EIGVAL, FLAG_QK_L2NORM = 1, 2, 4
 CONV_SILU = 1
@@ -27,7 +27,8 @@ EXPORTED = ("gdn2_abi_version", "gdn2_status_str", "gdn2_chunk_fwd_workspace_siz
             "gdn2_gated_rmsnorm", "gdn2_chunk_fwd_varlen_workspace_size", "gdn2_chunk_fwd_varlen",
             "gdn2_recurrent_varlen", "gdn2_chunk_bwd_workspace_size", "gdn2_chunk_bwd",
             "gdn2_short_conv", "gdn2_short_conv_bwd_workspace_size", "gdn2_short_conv_bwd",
-            "gdn2_chunk_bwd_varlen_workspace_size", "gdn2_chunk_bwd_varlen", "gdn2_chunk_fwd_noalloc")
+            "gdn2_chunk_bwd_varlen_workspace_size", "gdn2_chunk_bwd_varlen", "gdn2_chunk_fwd_noalloc",
+            "gdn2_chunk_prep_workspace_size", "gdn2_recurrent_step_gated")
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -67,6 +68,8 @@ def lib():
         L.gdn2_status_str.argtypes = [ctypes.c_int]
         L.gdn2_chunk_fwd_workspace_size.restype = sz
         L.gdn2_chunk_fwd_workspace_size.argtypes = [P]
+        L.gdn2_chunk_prep_workspace_size.restype = sz
+        L.gdn2_chunk_prep_workspace_size.argtypes = [P]
         L.gdn2_chunk_fwd.restype = ctypes.c_int
         L.gdn2_chunk_fwd.argtypes = [P] + [vp] * 9 + [vp, sz, vp]
         L.gdn2_chunk_fwd_noalloc.restype = ctypes.c_int
@@ -75,6 +78,8 @@ def lib():
         L.gdn2_chunk_prep.argtypes = [P] + [vp] * 6 + [vp, sz, vp]
         L.gdn2_chunk_state.restype = ctypes.c_int
         L.gdn2_chunk_state.argtypes = [P, vp, vp, vp, vp, sz, vp]
+        L.gdn2_recurrent_step_gated.restype = ctypes.c_int
+        L.gdn2_recurrent_step_gated.argtypes = [P] + [vp] * 11 + [vp]
         L.gdn2_recurrent_step.restype = ctypes.c_int
         L.gdn2_recurrent_step.argtypes = [P] + [vp] * 9 + [vp]
         L.gdn2_gated_rmsnorm.restype = ctypes.c_int
@@ -173,6 +178,11 @@ def chunk_fwd_workspace_size(B, T, H, dk, dv, io_dtype: torch.dtype, Hv: int = 0
     return int(lib().gdn2_chunk_fwd_workspace_size(ctypes.byref(problem(B, T, H, dk, dv, io_dtype, Hv=Hv))))
 
 
+def chunk_prep_workspace_size(B, T, H, dk, dv, io_dtype: torch.dtype, Hv: int = 0) -> int:
+    """Workspace of the two stages ``chunk_prep`` / ``chunk_state`` (every shape)."""
+    return int(lib().gdn2_chunk_prep_workspace_size(ctypes.byref(problem(B, T, H, dk, dv, io_dtype, Hv=Hv))))
+
+
 def alloc_workspace(nbytes: int, device) -> torch.Tensor:
     # torch's caching allocator returns blocks aligned to at least 512 bytes
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
@@ -250,6 +260,32 @@ def recurrent_step(q, k, v, alpha, b, w, S_in=None, *, o=None, S_out=None, out_s
     _check(lib().gdn2_recurrent_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w),
                                      _ptr(S_in), _ptr(o), _ptr(S_out), _stream(dev)))
     return o, S_out
+
+
+def recurrent_step_gated(q, k, v, alpha, b, w, g, norm_weight, S_in=None, *, y=None, S_out=None,
+                         out_state: bool = True, inplace: bool = False, flags: int = 0):
+    """Recurrent forward with the output step fused (``gdn2_recurrent_step_gated``):
+    returns (y, S_final or None), y = o / sqrt(mean(o^2) + 1e-5) * norm_weight * g * sigmoid(g)."""
+    p, dev = _problem_from(q, k, v, alpha, b, w, flags)
+    _check_state(S_in, p, dev, "S_in")
+    if tuple(g.shape) != tuple(v.shape) or g.dtype != v.dtype or g.device != dev or not g.is_contiguous():
+        raise ValueError("g must be a contiguous tensor shaped and typed like v")
+    if (tuple(norm_weight.shape) != (p.dv,) or norm_weight.dtype != torch.float32 or norm_weight.device != dev
+            or not norm_weight.is_contiguous()):
+        raise ValueError(f"norm_weight must be a contiguous float32 [{p.dv}] tensor on {dev}")
+    if y is None:
+        y = torch.empty(v.shape, dtype=v.dtype, device=dev)
+    if inplace:
+        if S_in is None:
+            raise ValueError("inplace needs S_in")
+        S_out = S_in
+    elif S_out is None and out_state:
+        S_out = torch.empty((p.B, p.value_heads, p.dk, p.dv), dtype=torch.float32, device=dev)
+    _check_state(S_out, p, dev, "S_out")
+    _check(lib().gdn2_recurrent_step_gated(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b),
+                                           _ptr(w), _ptr(S_in), _ptr(g), _ptr(norm_weight), _ptr(y), _ptr(S_out),
+                                           _stream(dev)))
+    return y, S_out
 
 
 def _varlen_problem(q, k, v, alpha, b, w, cu_seqlens, flags):

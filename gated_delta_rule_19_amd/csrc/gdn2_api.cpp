@@ -84,6 +84,9 @@ int64_t ws_block_bytes(const gdn2_problem* p)
 
 int64_t ws_bytes(const gdn2_problem* p) { return p->B * nvh(p) * nchunks(p) * ws_block_bytes(p); }
 
+// workspace gdn2_chunk_fwd needs: the two stages' factor blocks
+int64_t fwd_ws_bytes(const gdn2_problem* p) { return ws_bytes(p); }
+
 // packed batches: the chunk plan, then one block per (value head, chunk slot)
 int64_t varlen_ncmax(const gdn2_problem* p) { return nchunks(p) + p->B; }
 int64_t varlen_plan_bytes(const gdn2_problem* p)
@@ -340,6 +343,12 @@ const char* gdn2_status_str(int status)
 size_t gdn2_chunk_fwd_workspace_size(const gdn2_problem* p)
 {
     if (check_problem(p, true) != GDN2_OK) return 0;
+    return static_cast<size_t>(fwd_ws_bytes(p));
+}
+
+size_t gdn2_chunk_prep_workspace_size(const gdn2_problem* p)
+{
+    if (check_problem(p, true) != GDN2_OK) return 0;
     return static_cast<size_t>(ws_bytes(p));
 }
 
@@ -401,7 +410,7 @@ int gdn2_chunk_fwd(const gdn2_problem* p, const void* q, const void* k, const vo
     if (st) return st;
     st = check_inputs(p, q, k, v, alpha, b, w, o);
     if (st) return st;
-    const int64_t need = ws_bytes(p);
+    const int64_t need = fwd_ws_bytes(p);
     if (need > 0 && (workspace == nullptr || static_cast<int64_t>(workspace_bytes) < need))
         return GDN2_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_WORKSPACE;
@@ -431,7 +440,7 @@ int gdn2_chunk_fwd_noalloc(const gdn2_problem* p, const void* q, const void* k, 
     if (st) return st;
     st = check_inputs(p, q, k, v, alpha, b, w, o);
     if (st) return st;
-    const int64_t need = ws_bytes(p);
+    const int64_t need = fwd_ws_bytes(p);
     if (need > static_cast<int64_t>(GDN2_NOALLOC_SCRATCH_BYTES)) return GDN2_ERR_WORKSPACE;
     const Sizes z = sizes_of(p);
     const Range ins[7] = {range_of(q, z.key),  range_of(k, z.key),  range_of(v, z.val),
@@ -446,9 +455,9 @@ int gdn2_chunk_fwd_noalloc(const gdn2_problem* p, const void* q, const void* k, 
     st = device_ready();
     if (st) return st;
     // the device address of this GPU's copy of the library's scratch array
+    const hipStream_t s = static_cast<hipStream_t>(stream);
     void* ws = need > 0 ? gdn2::noalloc_scratch() : nullptr;
     if (need > 0 && ws == nullptr) return GDN2_ERR_DEVICE;
-    const hipStream_t s = static_cast<hipStream_t>(stream);
     st = do_prep(p, q, k, v, alpha, b, w, ws, s);
     if (st) return st;
     return do_state(p, S0, o, S_out, ws, s);
@@ -480,6 +489,38 @@ int gdn2_recurrent_step(const gdn2_problem* p, const void* q, const void* k, con
     gdn2::RecArgs a{q, k, v, alpha, b, w, S_in, o, S_out, p->B, p->T, nvh(p), p->H, (int)p->dv,
                     (int)(p->dv / vs), (int)p->flags, nullptr};
     return launch_status(gdn2::launch_recurrent(a, (int)p->dk, vs, is_bf16(p), gates_bf16(p),
+                                                static_cast<hipStream_t>(stream)));
+}
+
+int gdn2_recurrent_step_gated(const gdn2_problem* p, const void* q, const void* k, const void* v,
+                              const void* alpha, const void* b, const void* w, const float* S_in,
+                              const void* g, const float* norm_weight, void* y, float* S_out, void* stream)
+{
+    int st = check_problem(p, false);
+    if (st) return st;
+    // whole rows in one workgroup: dv one of the widths the kernel is built for
+    if (p->dv != 16 && p->dv != 32 && p->dv != 64 && p->dv != 128 && p->dv != 256) return GDN2_ERR_SHAPE;
+    st = check_inputs(p, q, k, v, alpha, b, w, y);
+    if (st) return st;
+    if (rows_nonempty(p) && (g == nullptr || norm_weight == nullptr)) return GDN2_ERR_NULL;
+    const Sizes z = sizes_of(p);
+    const Range ins[9] = {range_of(q, z.key),  range_of(k, z.key),  range_of(v, z.val),
+                          range_of(alpha, z.gk), range_of(b, z.gk), range_of(w, z.gv),
+                          range_of(S_in, z.state), range_of(g, z.val), range_of(norm_weight, p->dv * 4)};
+    const Range outs[2] = {range_of(y, z.val), range_of(S_out, z.state)};
+    st = check_alias(outs, 2, ins, 9, S_in, S_out, 6, 1);
+    if (st) return st;
+    st = check_align({q, k, v, alpha, b, w, S_in, y, S_out, g, norm_weight});
+    if (st) return st;
+    const int64_t nch = p->B * nvh(p);
+    if (nch == 0) return GDN2_OK;
+    if (p->T == 0 && S_out == S_in) return GDN2_OK;
+    st = device_ready();
+    if (st) return st;
+    // one workgroup holds whole value rows, so the row statistic is local
+    gdn2::RecArgs a{q, k, v, alpha, b, w, S_in, y, S_out, p->B, p->T, nvh(p), p->H, (int)p->dv,
+                    1, (int)p->flags, nullptr, g, norm_weight, 1e-5f};
+    return launch_status(gdn2::launch_recurrent(a, (int)p->dk, (int)p->dv, is_bf16(p), gates_bf16(p),
                                                 static_cast<hipStream_t>(stream)));
 }
 

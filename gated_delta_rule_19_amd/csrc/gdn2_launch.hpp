@@ -40,12 +40,17 @@ struct StateArgs {
 
 // cu (null for equal-length batches): the N+1 caller offsets of a packed
 // batch, each clamped into [0, T] before use
+// With norm_g set (whole value rows per workgroup: nslices == 1), the output
+// written to o is the layer's output step applied to the token's row,
+// o / sqrt(mean(o^2) + norm_eps) * norm_w * g * sigmoid(g), g [.., Hv, dv] in
+// the I/O dtype, norm_w [dv] fp32.
 struct RecArgs {
     const void* q; const void* k; const void* v;
     const void* alpha; const void* b; const void* w;
     const float* S_in; void* o; float* S_out;
     int64_t B, T, H, Hk; int dv; int nslices; int flags;
     const int* cu;
+    const void* norm_g; const float* norm_w; float norm_eps;
 };
 
 // Backward (equal-length batches, H value heads = query/key heads).  Reverse
@@ -151,6 +156,7 @@ struct ConvBwdArgs {
 hipError_t launch_chunk_prep(const PrepArgs& a, int dk, bool bf16, bool gbf16, hipStream_t s);
 hipError_t launch_chunk_state(const StateArgs& a, int dk, int vs, bool bf16, hipStream_t s);
 hipError_t launch_recurrent(const RecArgs& a, int dk, int vs, bool bf16, bool gbf16, hipStream_t s);
+
 hipError_t launch_gated_rmsnorm(const NormArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_short_conv(const ConvArgs& a, int K, bool silu, bool bf16, hipStream_t s);
 // the gradient launch, then the fixed-order sum of the weight partials

@@ -31,11 +31,13 @@
 
 namespace gdn2 {
 
-// Tg = gate dtype (alpha, b, w): float, or __bf16 with bf16 I/O
-template <typename Tio, int DK, int VS, typename Tg>
-__global__ __launch_bounds__(kThreads) void k_recurrent(RecArgs a)
+// Tg = gate dtype (alpha, b, w): float, or __bf16 with bf16 I/O; NT threads
+// (256, or 512 for whole rows of 256 columns)
+template <typename Tio, int DK, int VS, typename Tg, int NT = kThreads>
+__global__ __launch_bounds__(NT, NT == 512 ? 3 : 1) void k_recurrent(RecArgs a)
 {
     using IO = Io<Tio>;
+    constexpr int kThreads = NT;
     constexpr int NJ = VS / 4;                          // column groups (4 columns each)
     constexpr int NR = (kThreads / NJ) < DK ? (kThreads / NJ) : DK;   // row groups
     constexpr int NTH = NJ * NR;                        // threads holding state (multiple of 64)
@@ -201,7 +203,25 @@ __global__ __launch_bounds__(kThreads) void k_recurrent(RecArgs a)
                 QK *= rq * rk;
             }
             const f32x4 delta = u - R;
-            if (rg == 0) st_vec4(o + rowv, M + QK * delta);
+            const f32x4 ov = M + QK * delta;
+            if (a.norm_g == nullptr) {
+                if (rg == 0) st_vec4(o + rowv, ov);
+            } else {
+                // output step on the whole row (threads rg == 0, lanes 0..NJ-1 of
+                // wave 0): sum of squares across the row, then the gated norm
+                float ss = rg == 0 ? ov[0] * ov[0] + ov[1] * ov[1] + ov[2] * ov[2] + ov[3] * ov[3] : 0.f;
+#pragma unroll
+                for (int off = 1; off < NJ; off <<= 1) ss += __shfl_xor(ss, off, 64);
+                if (rg == 0) {
+                    const float rn = __builtin_amdgcn_rsqf(ss * (1.f / (float)VS) + a.norm_eps);
+                    const f32x4 z = ld_vec4(static_cast<const Tio*>(a.norm_g) + rowv);
+                    const f32x4 wn = *reinterpret_cast<const f32x4*>(a.norm_w + jc);
+                    f32x4 y;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) y[e] = ov[e] * rn * wn[e] * (z[e] * sigmoid_f(z[e]));
+                    st_vec4(o + rowv, y);
+                }
+            }
             const f32x4 kd = rk * delta;
 #pragma unroll
             for (int i = 0; i < RPT; ++i) S[i] += kreg[i] * kd;
@@ -212,6 +232,161 @@ __global__ __launch_bounds__(kThreads) void k_recurrent(RecArgs a)
 #pragma unroll
         for (int i = 0; i < RPT; ++i)
             __builtin_nontemporal_store(S[i], reinterpret_cast<f32x4*>(a.S_out + (chain * DK + rg + NR * i) * dv + jc));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_decode: the same step for one token (T == 1, equal-length batches), built
+// for streaming the state.  Every byte of the state is read once and written
+// once, so the step is bound by how much state the CUs keep in flight and by
+// how long each wave holds it without a request outstanding.  Each wave owns
+// whole columns of the slice (all dk rows of VS / waves columns), so its
+// reductions over the key axis stay inside the wave: no workgroup barrier,
+// each wave reads the token's key-axis vectors into its own LDS rows.  Those
+// vectors and w, v are requested before the state (so waiting for them never
+// waits for the state), and k is read back from LDS for the update instead
+// of being held per row, which keeps few registers beside the state.
+// ---------------------------------------------------------------------------
+template <typename Tio, int DK, int VS, typename Tg, int NT, int MINW>
+__global__ __launch_bounds__(NT, MINW) void k_decode(RecArgs a)
+{
+    using IO = Io<Tio>;
+    constexpr int NW = NT / 64;
+    constexpr int WC = VS / NW;                         // columns per wave
+    constexpr int NJ = WC / 4;                          // column groups of a wave
+    constexpr int NR = 64 / NJ;                         // row groups of a wave
+    constexpr int RPT = DK / NR;                        // rows per thread
+    static_assert(VS % NW == 0 && WC % 4 == 0 && 64 % NJ == 0 && NR <= DK && DK % NR == 0, "thread layout");
+    constexpr int VPL = 4 * DK / 64;                    // vector elements a lane loads
+
+    __shared__ __attribute__((aligned(16))) float vec[NW][4][DK];   // per wave: alpha, b, k, q
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int jg = lane % NJ, rg = lane / NJ;
+    const int64_t chain = blockIdx.x / a.nslices;
+    const int slice = (int)(blockIdx.x - chain * a.nslices);
+    const int64_t bb = chain / a.H, hh = chain - bb * a.H;
+    const int64_t hk = hh / (a.H / a.Hk);
+    const int dv = a.dv;
+    const int jc = slice * VS + wave * WC + 4 * jg;
+    const bool logits = (a.flags & kFlagGateLogits) != 0;
+    const bool l2norm = (a.flags & kFlagQkL2norm) != 0;
+    const float bscale = (a.flags & kFlagNegEigval) ? 2.f : 1.f;
+    const Tg* galpha = static_cast<const Tg*>(a.alpha);
+    const Tg* gb = static_cast<const Tg*>(a.b);
+    const Tg* gw = static_cast<const Tg*>(a.w);
+    const Tio* q = static_cast<const Tio*>(a.q);
+    const Tio* k = static_cast<const Tio*>(a.k);
+    float* vw = &vec[wave][0][0];
+
+    // 1. the token's key-axis vectors (this wave's copy) and the thread's w, v, before the state
+    const int64_t rowk = (bb * a.H + hh) * DK, rowq = (bb * a.Hk + hk) * DK;
+    float kv[VPL];
+#pragma unroll
+    for (int u = 0; u < VPL; ++u) {
+        const int e = lane + 64 * u;
+        const int which = e / DK, c = e - which * DK;   // which is uniform per u when DK >= 64
+        float x;
+        if (which == 0) x = gate_f(galpha[rowk + c]);
+        else if (which == 1) x = gate_f(gb[rowk + c]);
+        else if (which == 2) x = IO::to_f(k[rowq + c]);
+        else x = IO::to_f(q[rowq + c]);
+        kv[u] = x;
+    }
+    const int64_t rowv = (bb * a.H + hh) * dv + jc;
+    const auto wraw = *reinterpret_cast<const typename GateVec<Tg>::type*>(gw + rowv);
+    const auto vraw = *reinterpret_cast<const typename IO::vec4*>(static_cast<const Tio*>(a.v) + rowv);
+    // 2. the state
+    f32x4 S[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (a.S_in != nullptr)
+            S[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.S_in + (chain * DK + rg + NR * i) * dv + jc));
+    }
+    // 3. the vectors into this wave's LDS rows (read back by the same wave: no barrier)
+#pragma unroll
+    for (int u = 0; u < VPL; ++u) {
+        const int e = lane + 64 * u;
+        const int which = e / DK;
+        float x = kv[u];
+        if (logits && which == 0) x = sigmoid_f(x);
+        if (logits && which == 1) x = sigmoid_f(x) * bscale;
+        vw[e] = x;
+    }
+    __builtin_amdgcn_wave_barrier();
+    // 4. decay and the reductions over the key axis (row groups of the wave)
+    f32x4 r = {0.f, 0.f, 0.f, 0.f}, m = r;
+    float qk = 0.f, k2 = 0.f, q2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int c = rg + NR * i;
+        const float al = vw[c], kk = vw[2 * DK + c], qq = vw[3 * DK + c];
+        const float e = vw[DK + c] * kk;
+        S[i] *= al;
+        r += e * S[i];
+        m += qq * S[i];
+        qk += qq * kk;
+        k2 += kk * kk;
+        q2 += qq * qq;
+    }
+#pragma unroll
+    for (int off = NJ; off < 64; off <<= 1) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            r[jj] += __shfl_xor(r[jj], off, 64);
+            m[jj] += __shfl_xor(m[jj], off, 64);
+        }
+        qk += __shfl_xor(qk, off, 64);
+        if (l2norm) {
+            k2 += __shfl_xor(k2, off, 64);
+            q2 += __shfl_xor(q2, off, 64);
+        }
+    }
+    float rk = 1.f;
+    if (l2norm) {
+        rk = __builtin_amdgcn_rsqf(k2 + kL2normEps);
+        const float rq = __builtin_amdgcn_rsqf(q2 + kL2normEps);
+        r *= rk;
+        m *= rq;
+        qk *= rq * rk;
+    }
+    f32x4 w4 = widen4(wraw);
+    if (logits) w4 = sigmoid4(w4);
+    const f32x4 delta = w4 * IO::unpack4(vraw) - r;
+    // 5. the state update, streamed out
+    const f32x4 kd = rk * delta;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        S[i] += vw[2 * DK + rg + NR * i] * kd;
+        if (a.S_out != nullptr)
+            __builtin_nontemporal_store(S[i], reinterpret_cast<f32x4*>(a.S_out + (chain * DK + rg + NR * i) * dv + jc));
+    }
+    // 6. the output row (optionally through the output step, whose row sum
+    // spans the waves: one barrier, taken only then)
+    const f32x4 ov = m + qk * delta;
+    Tio* o = static_cast<Tio*>(a.o);
+    if (a.norm_g == nullptr) {
+        if (rg == 0) st_vec4(o + rowv, ov);
+    } else {
+        __shared__ float ssw[NW];
+        float ss = rg == 0 ? ov[0] * ov[0] + ov[1] * ov[1] + ov[2] * ov[2] + ov[3] * ov[3] : 0.f;
+#pragma unroll
+        for (int off = 1; off < NJ; off <<= 1) ss += __shfl_xor(ss, off, 64);
+        if (lane == 0) ssw[wave] = ss;
+        __syncthreads();
+        float tot = 0.f;
+#pragma unroll
+        for (int wv = 0; wv < NW; ++wv) tot += ssw[wv];
+        if (rg == 0) {
+            const float rn = __builtin_amdgcn_rsqf(tot * (1.f / (float)VS) + a.norm_eps);
+            const f32x4 z = ld_vec4(static_cast<const Tio*>(a.norm_g) + rowv);
+            const f32x4 wn = *reinterpret_cast<const f32x4*>(a.norm_w + jc);
+            f32x4 y;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = ov[e] * rn * wn[e] * (z[e] * sigmoid_f(z[e]));
+            st_vec4(o + rowv, y);
+        }
     }
 }
 
@@ -232,7 +407,23 @@ template <typename Tio, int DK, int VS, typename Tg>
 static hipError_t rec_v(const RecArgs& a, hipStream_t s)
 {
     const int64_t nblk = a.B * a.H * (int64_t)a.nslices;
-    hipLaunchKernelGGL((k_recurrent<Tio, DK, VS, Tg>), dim3((unsigned)nblk), dim3(kThreads), 0, s, a);
+    if constexpr (VS == 256) {
+        // whole rows of 256 columns (the output step over dv = 256): 512 threads
+        if (a.T == 1 && a.cu == nullptr)
+            hipLaunchKernelGGL((k_decode<Tio, DK, VS, Tg, 256, 2>), dim3((unsigned)nblk), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_recurrent<Tio, DK, VS, Tg, 512>), dim3((unsigned)nblk), dim3(512), 0, s, a);
+    } else {
+        // every lane holds state rows: 64 / (columns per wave / 4) row groups at most dk
+        constexpr bool fits = VS % 16 == 0 && VS >= 16 && (64 / (VS / 16)) <= DK && DK >= 64;
+        if (fits && a.T == 1 && a.cu == nullptr) {
+            if constexpr (fits)
+                hipLaunchKernelGGL((k_decode<Tio, DK, VS, Tg, kThreads, (DK * VS >= 128 * 128 ? 4 : 8)>),
+                                   dim3((unsigned)nblk), dim3(kThreads), 0, s, a);
+        } else {
+            hipLaunchKernelGGL((k_recurrent<Tio, DK, VS, Tg>), dim3((unsigned)nblk), dim3(kThreads), 0, s, a);
+        }
+    }
     return hipGetLastError();
 }
 
@@ -244,6 +435,7 @@ static hipError_t rec_dk(const RecArgs& a, int vs, hipStream_t s)
         case 32: return rec_v<Tio, DK, 32, Tg>(a, s);
         case 64: return rec_v<Tio, DK, 64, Tg>(a, s);
         case 128: return rec_v<Tio, DK, 128, Tg>(a, s);
+        case 256: return rec_v<Tio, DK, 256, Tg>(a, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -84,7 +84,7 @@
 extern "C" {
 #endif
 
-#define GDN2_ABI_VERSION 4
+#define GDN2_ABI_VERSION 5
 
 typedef enum {
     GDN2_OK = 0,
@@ -131,6 +131,13 @@ const char* gdn2_status_str(int status);
  * undefined between calls, and it must be 256-byte aligned.
  */
 size_t gdn2_chunk_fwd_workspace_size(const gdn2_problem* p);
+
+/*
+ * Bytes of workspace the two stages gdn2_chunk_prep and gdn2_chunk_state
+ * (declared below) need for problem *p when called on their own (0 if *p is
+ * invalid); in this version the same as gdn2_chunk_fwd_workspace_size.
+ */
+size_t gdn2_chunk_prep_workspace_size(const gdn2_problem* p);
 
 /*
  * Chunked forward (README: "chunked WY decomposition", chunk_size 64).
@@ -200,6 +207,29 @@ int gdn2_recurrent_step(const gdn2_problem* p,
                         const void* q, const void* k, const void* v,
                         const void* alpha, const void* b, const void* w,
                         const float* S_in, void* o, float* S_out, void* stream);
+
+/*
+ * The recurrent forward with the layer's output step fused into its output
+ * write (README "Architecture": the core's output passes through "Gated RMS
+ * Norm <- SiLU Gate"; "Configuration": norm_eps = 1e-5): for every token and
+ * value head, with o the row gdn2_recurrent_step would write,
+ *
+ *     y = o / sqrt(mean(o^2) + 1e-5) * norm_weight * g * sigmoid(g)
+ *
+ * (the reading of gdn2_gated_rmsnorm below), computed from o in fp32 before
+ * it is rounded.  One workgroup holds whole value rows, so dv must be one of
+ * 16, 32, 64, 128, 256 (else GDN2_ERR_SHAPE).  g: [B, T, Hv, dv] io_dtype,
+ * norm_weight: [dv] fp32, y: [B, T, Hv, dv] io_dtype.  Everything else
+ * (sizes, dtypes, flags, grouped heads, S_in/S_out, in-place state, checks)
+ * is as for gdn2_recurrent_step; y must not overlap any input.  T == 1 is
+ * the decode step with its output step, one launch, the layer's o never
+ * written to memory.
+ */
+int gdn2_recurrent_step_gated(const gdn2_problem* p,
+                              const void* q, const void* k, const void* v,
+                              const void* alpha, const void* b, const void* w,
+                              const float* S_in, const void* g, const float* norm_weight,
+                              void* y, float* S_out, void* stream);
 
 /*
  * Packed variable-length batches.  The recurrence runs per sequence and each

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert g.abi_version() == 4
+    assert g.abi_version() == 5
     for code in range(8):
         assert g.status_str(code).startswith(bnd._STATUS[code])
     assert "unknown" in g.status_str(99)
@@ -62,7 +62,7 @@ class Call:
         sizes = dict(q=rows * dk * es, k=rows * dk * es, v=vrows * dv * es, alpha=vrows * dk * gs,
                      b=vrows * dk * gs, w=vrows * dv * gs, S0=nv * dk * dv * 4, o=vrows * dv * es,
                      S_out=nv * dk * dv * 4)
-        sizes["ws"] = g.lib().gdn2_chunk_fwd_workspace_size(ctypes.byref(self.p)) or 256
+        sizes["ws"] = g.lib().gdn2_chunk_prep_workspace_size(ctypes.byref(self.p)) or 256
         self.size = sizes
         addr = BASE
         self.ptr = {}
@@ -95,11 +95,18 @@ def test_valid_call_reaches_the_device_check():
 
 
 def test_workspace_size():
-    p = bnd.problem(4, 2048, 16, 128, 128, __import__("torch").bfloat16)
-    n = g.lib().gdn2_chunk_fwd_workspace_size(ctypes.byref(p))
+    torch = __import__("torch")
+    p = bnd.problem(4, 2048, 16, 128, 128, torch.bfloat16)
     # one 256-aligned block per (batch, head, chunk); bf16 block = 74,240 bytes at dk = dv = 128
-    assert n == 4 * 16 * 32 * 74240
+    assert g.lib().gdn2_chunk_fwd_workspace_size(ctypes.byref(p)) == 4 * 16 * 32 * 74240
+    # the stages on their own need the same
+    for shape in ((4, 2048, 16, 128, 128, torch.bfloat16), (4, 2048, 16, 64, 64, torch.bfloat16),
+                  (1, 100, 2, 128, 128, torch.float32), (1, 100, 2, 128, 48, torch.bfloat16)):
+        p2 = bnd.problem(*shape)
+        n = g.lib().gdn2_chunk_fwd_workspace_size(ctypes.byref(p2))
+        assert n == g.lib().gdn2_chunk_prep_workspace_size(ctypes.byref(p2)) > 0
     assert g.lib().gdn2_chunk_fwd_workspace_size(None) == 0
+    assert g.lib().gdn2_chunk_prep_workspace_size(None) == 0
     bad = bnd.Problem(1, 1, 1, 100, 16, 64, 1, 0, 0)
     assert g.lib().gdn2_chunk_fwd_workspace_size(ctypes.byref(bad)) == 0
 
@@ -157,7 +164,7 @@ def test_grouped_heads_are_sized_per_tensor():
     assert c.fwd(o=c.ptr["alpha"] + 512) == DEVICE
     one = bnd.problem(2, 300, 4, 128, 128, __import__("torch").bfloat16)
     four = bnd.problem(2, 300, 4, 128, 128, __import__("torch").bfloat16, Hv=16)
-    ws = lambda p: g.lib().gdn2_chunk_fwd_workspace_size(ctypes.byref(p))
+    ws = lambda p: g.lib().gdn2_chunk_prep_workspace_size(ctypes.byref(p))
     assert ws(four) == 4 * ws(one) > 0                  # one workspace block per value head and chunk
 
 

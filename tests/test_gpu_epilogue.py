@@ -75,3 +75,53 @@ def test_gated_rmsnorm_full_chunk_size(dev):
     rows = np.linalg.norm((yn - ref).reshape(-1, 128), axis=1) / np.linalg.norm(ref.reshape(-1, 128), axis=1)
     print(f"[parity] gated_rmsnorm B4 H16 T2048: relL2 {e:.3e}, worst row {rows.max():.3e}", flush=True)
     assert e <= 2e-2 and rows.max() <= 2e-2
+
+
+# ---- the output step fused into the recurrent forward -----------------------------
+GATED = [
+    # B, T, H, Hv, dk, dv, io dtype, flags
+    (256, 1, 16, 16, 128, 128, torch.bfloat16, 0),     # the decode workload's shape
+    (8, 1, 4, 8, 128, 256, torch.bfloat16, 0),
+    (4, 1, 2, 2, 64, 64, torch.float32, 0),
+    (2, 37, 2, 4, 128, 128, torch.bfloat16, 7),        # several tokens, prologue flags, grouped heads
+    (3, 5, 2, 2, 32, 32, torch.float32, 1),
+    (2, 9, 1, 1, 16, 16, torch.bfloat16, 4),
+]
+
+
+@pytest.mark.parametrize("case", GATED, ids=lambda c: f"B{c[0]}T{c[1]}H{c[2]}Hv{c[3]}dk{c[4]}dv{c[5]}"
+                         f"{'bf16' if c[6] == torch.bfloat16 else 'f32'}fl{c[7]}")
+def test_recurrent_with_output_step(dev, case):
+    """gdn2_recurrent_step_gated against the oracle chain gated_rmsnorm(recurrent(...)) (the output
+    step taken on the fp64 o), and the state against the plain recurrence; both modes' state updated
+    in place."""
+    from gated_delta_rule_19_amd import inputs
+    from oracle import c_oracle
+    from oracle.reference import share_qk_heads
+    B, T, H, Hv, dk, dv, dt, fl = case
+    inp = inputs.make_raw(B, T, H, dk, dv, dt, B + T + dv + fl, dev, s0_std=0.05, Hv=Hv,
+                          gate_logits=bool(fl & 1), unit_qk=not fl & 4)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(B * T + dv)
+    gt = torch.randn(inp["v"].shape, generator=gen, device=dev).to(dt)
+    wt = torch.randn(dv, generator=gen, device=dev) * 0.5 + 1.0
+    a = (inp["q"], inp["k"], inp["v"], inp["alpha"], inp["b"], inp["w"])
+    h = {k_: (None if v_ is None else _np(v_)) for k_, v_ in inp.items()}
+    qw, kw = share_qk_heads(h["q"], h["k"], Hv)
+    ro, rS = c_oracle.recurrent(qw, kw, h["v"], h["alpha"], h["b"], h["w"], h["S0"], flags=fl)
+    ry = gated_rmsnorm(ro, _np(gt), _np(wt))
+    S = inp["S0"].clone()
+    y, _ = g.recurrent_step_gated(*a, gt, wt, S, inplace=True, flags=fl)
+    torch.cuda.synchronize()
+    tol = 1e-4 if dt == torch.float32 else 2e-2
+    ey, eS = rel_l2(_np(y), ry), rel_l2(_np(S), rS)
+    print(f"[parity] recurrent + output step {case}: relL2 y={ey:.3e} S={eS:.3e}", flush=True)
+    assert ey <= tol and eS <= tol
+    # the state equals the plain recurrent step's up to the order of its fp32 sums (whole-row
+    # workgroups here, slices there); y equals the separate output step within one rounding of o
+    S2 = inp["S0"].clone()
+    o2, _ = g.recurrent_step(*a, S2, inplace=True, flags=fl)
+    y2 = g.gated_rmsnorm(o2, gt, wt)
+    torch.cuda.synchronize()
+    assert rel_l2(_np(S), _np(S2)) <= 1e-5
+    assert rel_l2(_np(y), _np(y2)) <= (1e-5 if dt == torch.float32 else 1e-2)

@@ -153,7 +153,7 @@ def test_chunk_prep_intermediates(dev, dt):
     (Gamma*q, W = T(Gamma*b*k), Ktil, P, U = T(w*v), Gamma_L)."""
     B, T, H, dk, dv = 1, 100, 2, 64, 32
     inp = make(dev, B, T, H, dk, dv, dt, seed=5, b_scale=2.0)
-    nbytes = g.chunk_fwd_workspace_size(B, T, H, dk, dv, dt)
+    nbytes = g.chunk_prep_workspace_size(B, T, H, dk, dv, dt)
     ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
     g.chunk_prep(*args(inp), ws)
     torch.cuda.synchronize()
@@ -370,3 +370,81 @@ def test_tiny_fp32_workload_both_modes(dev):
         o, S = fn(*args(inp), inp["S0"])
         torch.cuda.synchronize()
         check(f"tiny fp32 {fn.__name__}", o, S, ro, rS, 1e-4)
+
+
+# ---------------------------------------------------------------------------
+# the chunked forward at d128 bf16: tails, every value width, the stages
+# called one by one, prologue options with grouped heads, decay extremes
+# ---------------------------------------------------------------------------
+def _split(inp, flags=0):
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    B, T, H, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    ws = g.alloc_workspace(g.chunk_prep_workspace_size(B, T, H, dk, dv, q.dtype, Hv=Hv), q.device)
+    prob = g.problem(B, T, H, dk, dv, q.dtype, gate_dtype=inp["alpha"].dtype, flags=flags, Hv=Hv)
+    g.chunk_prep(*args(inp), ws, flags=flags)
+    o = torch.empty_like(v)
+    S = torch.empty(B, Hv, dk, dv, dtype=torch.float32, device=q.device)
+    g.chunk_state(prob, ws, o, inp["S0"], S)
+    return o, S
+
+
+FUSED = [
+    # B, T, H, dk, dv, S0 std, b scale
+    (1, 1, 2, 128, 128, 0.05, 1.0),
+    (2, 63, 2, 128, 32, None, 2.0),
+    (1, 64, 3, 128, 64, 0.05, 1.0),
+    (1, 65, 2, 128, 96, 0.05, 2.0),
+    (2, 129, 2, 128, 128, None, 1.0),
+    (1, 300, 4, 128, 256, 0.05, 2.0),
+]
+
+
+@pytest.mark.parametrize("case", FUSED, ids=lambda c: f"B{c[0]}T{c[1]}H{c[2]}dv{c[4]}{'S0' if c[5] else ''}b{c[6]:g}")
+def test_chunk_d128_against_oracle_and_stages(dev, case):
+    B, T, H, dk, dv, s0, bs = case
+    inp = make(dev, B, T, H, dk, dv, torch.bfloat16, seed=T * 13 + dv, s0=s0, b_scale=bs)
+    o, S = g.chunk_fwd(*args(inp), inp["S0"])
+    o2, S2 = _split(inp)
+    torch.cuda.synchronize()
+    ro, rS = oracle(inp)
+    check(f"chunk_fwd B{B}T{T}H{H}dv{dv}", o, S, ro, rS, 2e-2)
+    check(f"prep + state B{B}T{T}H{H}dv{dv}", o2, S2, ro, rS, 2e-2)
+
+
+@pytest.mark.parametrize("flags", [1, 3, 4, 7])
+def test_chunk_d128_prologue_flags_and_grouped_heads(dev, flags):
+    """In-kernel prologue (gate logits in bf16, b x 2, q/k L2 norm) and 2 value heads per
+    query/key head at d128, against the oracle with the same options."""
+    from oracle.reference import share_qk_heads
+    B, T, H, Hv, dk, dv = 2, 150, 2, 4, 128, 64
+    inp = inputs.make_raw(B, T, H, dk, dv, torch.bfloat16, 70 + flags, dev, s0_std=0.05, Hv=Hv,
+                          gate_logits=bool(flags & 1), unit_qk=not flags & 4,
+                          gate_dtype=torch.bfloat16 if flags & 1 else torch.float32)
+    o, S = g.chunk_fwd(*args(inp), inp["S0"], flags=flags)
+    o2, S2 = _split(inp, flags)
+    torch.cuda.synchronize()
+    h = {k_: _np(v_) for k_, v_ in inp.items()}
+    qw, kw = share_qk_heads(h["q"], h["k"], Hv)
+    ro, rS = c_oracle.recurrent(qw, kw, h["v"], h["alpha"], h["b"], h["w"], h["S0"], flags=flags)
+    check(f"chunk_fwd flags {flags} Hv {Hv}", o, S, ro, rS, 2e-2)
+    check(f"prep + state flags {flags} Hv {Hv}", o2, S2, ro, rS, 2e-2)
+
+
+def test_chunk_d128_split_resume_bitwise(dev):
+    """Two calls split at a chunk boundary equal one call bit for bit (the state crosses
+    the boundary in fp32 either way), and the state may be updated in place."""
+    T = 320
+    inp = make(dev, 1, T, 4, 128, 128, torch.bfloat16, seed=88, s0=0.05, b_scale=2.0)
+    o, S = g.chunk_fwd(*args(inp), inp["S0"])
+    a1 = [x[:, :192].contiguous() for x in args(inp)]
+    a2 = [x[:, 192:].contiguous() for x in args(inp)]
+    o1, S1 = g.chunk_fwd(*a1, inp["S0"])
+    o2, S2 = g.chunk_fwd(*a2, S1)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([o1, o2], 1), o) and torch.equal(S2, S)
+    # in place: S_out == S0
+    Sp = inp["S0"].clone()
+    o3, _ = g.chunk_fwd(*args(inp), Sp, S_out=Sp)
+    torch.cuda.synchronize()
+    assert torch.equal(o3, o) and torch.equal(Sp, S)

@@ -113,7 +113,9 @@ def test_varlen_equal_lengths_match_the_batched_call(dev):
 
 
 def test_varlen_one_token_sequences_are_decode_steps(dev):
-    """256 one-token sequences updated in place = one batched decode step."""
+    """256 one-token sequences updated in place = one batched decode step, up to the order
+    of the fp32 sums (the batched step runs the decode kernel, the packed batch the general
+    recurrent kernel): the states agree to fp32 rounding, the bf16 outputs to one rounding."""
     N, H, dk, dv = 256, 16, 128, 128
     inp = make(dev, [1] * N, H, H, dk, dv, BF16, BF16, LOG | L2, seed=12, s0=0.05)
     S1 = inp["S0"].clone()
@@ -122,7 +124,10 @@ def test_varlen_one_token_sequences_are_decode_steps(dev):
     unpack = lambda x: x.reshape(N, 1, *x.shape[2:]).contiguous()
     o2, _ = g.recurrent_step(*(unpack(x) for x in args(inp)), S2, inplace=True, flags=LOG | L2)
     torch.cuda.synchronize()
-    assert torch.equal(unpack(o1), o2) and torch.equal(S1, S2)
+    eS = rel_l2(_np(S1), _np(S2))
+    eo = rel_l2(_np(unpack(o1)), _np(o2))
+    print(f"[parity] varlen one-token vs batched decode: S {eS:.2e}, o {eo:.2e}", flush=True)
+    assert eS <= 1e-6 and eo <= 4e-3
 
 
 def test_varlen_full_size_sampled(dev):

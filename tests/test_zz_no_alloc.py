@@ -28,7 +28,7 @@ def test_too_large_is_rejected_on_the_host():
     code = g.lib().gdn2_chunk_fwd_noalloc(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, fake,
                                           None, None)
     assert code == 5                       # GDN2_ERR_WORKSPACE
-    p2 = bnd.problem(1, 64, 16, 100, 128, torch.bfloat16)   # invalid dk: the shape error comes first
+    p2 = bnd.problem(1, 64, 16, 100, 64, torch.bfloat16)    # invalid dk: the shape error comes first
     assert g.lib().gdn2_chunk_fwd_noalloc(ctypes.byref(p2), fake, fake, fake, fake, fake, fake, None, fake,
                                           None, None) == 2
 
@@ -39,8 +39,10 @@ def test_noalloc_equals_chunk_fwd_two_calls():
         pytest.skip("no GPU")
     g.lib()
     dev = torch.device("cuda:0")
-    # first call: B2 T1000 H12 d128 bf16 (2 x 12 x 16 chunks x 74,240 B = 28.5 MB of workspace)
-    big = inputs.make_raw(2, 1000, 12, 128, 128, torch.bfloat16, 31, dev, s0_std=0.05, b_scale=2.0)
+    # first call: B2 T1000 H12 dk64 dv128 bf16 (2 x 12 x 16 chunks of 49,664 B = 19 MB of workspace
+    # in the library's array)
+    big = inputs.make_raw(2, 1000, 12, 64, 128, torch.bfloat16, 31, dev, s0_std=0.05, b_scale=2.0)
+    assert g.chunk_fwd_workspace_size(2, 1000, 12, 64, 128, torch.bfloat16) > 16 << 20
     # second call, smaller: B1 T300 H4 dk64 dv96, zero initial state
     small = inputs.make_raw(1, 300, 4, 64, 96, torch.bfloat16, 32, dev)
     for inp in (big, small):
@@ -52,9 +54,10 @@ def test_noalloc_equals_chunk_fwd_two_calls():
         print(f"[noalloc] {tuple(inp['v'].shape)}: equal o {torch.equal(o, o_ref)} S {torch.equal(S, S_ref)}",
               flush=True)
         assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
-    # the first shape again after the smaller one, and fp32 I/O
+    # the first shape again after the smaller one, fp32 I/O, and a d128 shape
     f32 = inputs.make_raw(1, 130, 2, 32, 48, torch.float32, 33, dev, s0_std=0.05)
-    for inp in (big, f32):
+    fused = inputs.make_raw(2, 200, 4, 128, 128, torch.bfloat16, 34, dev, s0_std=0.05)
+    for inp in (big, f32, fused):
         o_ref, S_ref = g.chunk_fwd(*_args(inp), inp["S0"])
         o = torch.empty_like(o_ref)
         S = torch.empty_like(S_ref)
