@@ -19,16 +19,23 @@
 // k_chunk_state (one workgroup per (batch, head, value slice)) runs the
 // chunks in order with the fp32 state held in matrix-core accumulators.
 //
-// Decay ratios inside matrix products.  Gamma_r/Gamma_s is split over the four
-// 16-token blocks of the chunk: with g_r the running product of alpha from the
-// start of r's block (so g <= 1) and Z_K the product over block K,
-//   same block:   Gamma_r/Gamma_s = g_r * (1/g_s)
-//   block I > J:  Gamma_r/Gamma_s = g_r * (1/g_s) * prod_{K=J}^{I-1} Z_K
-// so one row-side operand (e*g, q*g) and one column-side operand (k/g) serve
-// every block pair; the off-diagonal factor is applied per channel to the
-// column operand on load.  Only 1/g_s can exceed 1, by at most the inverse
-// decay of 16 tokens.  No exp/log is evaluated: all factors are running
-// products of alpha.
+// Decay ratios inside matrix products.  The chunk's 64 tokens form eight
+// half-blocks of 8 tokens; half h takes its 4th token m_h as reference.  With
+//   rho_r   = Gamma_r / Gamma_m,   sigma_s = Gamma_m / Gamma_s   (r, s in half h),
+//   lambda_h, tau_h = the products of alpha over the first / last 4 tokens of h,
+//   Z_h = lambda_h tau_h,
+// a pair inside one half has Gamma_r/Gamma_s = rho_r sigma_s, and a pair with r
+// in a later half hr than s's half hs has
+//   Gamma_r/Gamma_s = (rho_r lambda_hr) * prod_{hs<h<hr} Z_h * (sigma_s tau_hs).
+// rho and sigma are running products of at most 4 alphas or their inverses,
+// so every operand of these products is bounded by the inverse product of 4
+// consecutive alphas, and every correction factor is at most 1 (no exp/log is
+// evaluated).  One row operand (e rho, q rho) and one column operand (k sigma)
+// are stored; the per-(half, channel) corrections are applied to a fragment
+// when it is loaded.  A 16x16 tile spans two halves on each side: an
+// off-diagonal tile takes one product with both operands corrected, a
+// diagonal tile two (same-half pairs plain, second-half rows against
+// first-half columns corrected).
 #include <type_traits>
 
 #include "gdn2_device.hpp"
@@ -75,10 +82,12 @@ struct PrepSmem {
     static constexpr int R1 = align16(imax(imax(SZ_X, SZ_F), SZ_U));
     static constexpr int R2 = align16(imax(SZ_X, SZ_T + SZ_TD));
     static constexpr int O1 = R0, O2 = O1 + R1, OF = O2 + R2;
-    // Fs [7][KPAD]: rows 0..5 the per-channel decay factors of the block pairs
-    // (1,0) (2,1) (3,2) (2,0) (3,1) (3,0); rows 0..2 double as the block
-    // totals Z_0..Z_2 and row 6 holds Z_3
-    static constexpr int BYTES = OF + 7 * KPAD * 4;
+    // fp32 [.][KPAD] tables of the decay corrections: lambda [8], tau [8] per
+    // half; the row correction of off-diagonal tiles per half [8]; the column
+    // correction per off-diagonal tile (1,0) (2,1) (3,2) (2,0) (3,1) (3,0) and
+    // half of its column block [12]
+    static constexpr int TL = 0, TT = 8, TRS = 16, TCS = 24, NTAB = 36;
+    static constexpr int BYTES = OF + NTAB * KPAD * 4;
     // workgroups per CU the LDS and register budgets are sized for
     static constexpr int MINB = BYTES * 3 <= 160 * 1024 ? 3 : (BYTES * 2 <= 160 * 1024 ? 2 : 1);
 };
@@ -246,29 +255,39 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
         }
     }
 
-    // ---- 1a. running decay products inside each 16-token block -------------
-    // g[i] = prod of alpha from the start of the 16-token block to row i; the
-    // second 8-token half multiplies in the first half's total (lane +- NQ).
-    f32x4 g[8];
-    f32x4 zblk;
+    // ---- 1a. decay products inside the thread's half (its 8 tokens) ----------
+    // suf[i] = prod_{i<j<=7} alpha_j, inc[i] = prod_{j<=i} alpha_j; lambda and
+    // tau are the products over tokens 0..3 and 4..7; rho, sigma relative to
+    // token 3 (the half's 4th): P_i = prod_{i<j<=3} alpha_j (i <= 3),
+    // Q_i = prod_{4<=j<=i} alpha_j (i >= 4).
+    f32x4 suf[8], rho[8], sig[8];
+    f32x4 lam, tau;
     {
-        f32x4 run = {1.f, 1.f, 1.f, 1.f};
+        suf[7] = f32x4{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            run *= al[i];
-            g[i] = run;
+        for (int i = 6; i >= 0; --i) suf[i] = suf[i + 1] * al[i + 1];
+        f32x4 pp = {1.f, 1.f, 1.f, 1.f};                // P_i, i = 3 down to 0
+#pragma unroll
+        for (int i = 3; i >= 0; --i) {
+            if (i < 3) pp *= al[i + 1];
+            sig[i] = pp;
+            rho[i] = f32x4{fast_rcp(pp[0]), fast_rcp(pp[1]), fast_rcp(pp[2]), fast_rcp(pp[3])};
         }
-        f32x4 other;
+        lam = pp * al[0];
+        f32x4 qp = {1.f, 1.f, 1.f, 1.f};                // Q_i, i = 4 up to 7
 #pragma unroll
-        for (int e = 0; e < 4; ++e) other[e] = __shfl_xor(run[e], NQ, 64);
-        if (half) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) g[i] *= other;
+        for (int i = 4; i < 8; ++i) {
+            qp *= al[i];
+            rho[i] = qp;
+            sig[i] = f32x4{fast_rcp(qp[0]), fast_rcp(qp[1]), fast_rcp(qp[2]), fast_rcp(qp[3])};
         }
-        zblk = run * other;
-        if (kact && half == 0) *reinterpret_cast<f32x4*>(Fs + (p < 3 ? p : 6) * KPAD + c0) = zblk;
+        tau = qp;
+        if (kact) {
+            *reinterpret_cast<f32x4*>(Fs + (SM::TL + rg) * KPAD + c0) = lam;
+            *reinterpret_cast<f32x4*>(Fs + (SM::TT + rg) * KPAD + c0) = tau;
+        }
     }
-    if constexpr (KPAD > DK) {   // zero the K padding of the operand arrays
+    if constexpr (KPAD > DK) {   // zero the K padding of the operand arrays and tables
         for (int e = tid; e < 64 * (KPAD - DK); e += kThreads) {
             const int r = e / (KPAD - DK), c = DK + e % (KPAD - DK);
             Xe[xo(r, c)] = IO::from_f(0.f);
@@ -277,45 +296,63 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
             qh_out[r * KPAD + c] = IO::from_f(0.f);
             wwy_out[r * KPAD + c] = IO::from_f(0.f);
         }
-        for (int e = tid; e < 6 * (KPAD - DK); e += kThreads)
+        for (int e = tid; e < SM::NTAB * (KPAD - DK); e += kThreads)
             Fs[(e / (KPAD - DK)) * KPAD + DK + e % (KPAD - DK)] = 0.f;
     }
     __syncthreads();
 
-    // ---- 1b. block factors, decay-scaled operands ---------------------------
+    // ---- 1b. products over the other halves, corrections, operands ----------
     // The (Gamma e)^T fragments are kept in registers and written to LDS after
     // the solve, when the space of A is free.
     constexpr int NEF = 8 / EPL;
     frag ehf[4][NEF];
     if (kact) {
-        f32x4 z[4];
+        f32x4 pre = {1.f, 1.f, 1.f, 1.f}, post = pre, gaml = pre, zprev = pre, znext = pre;
+        f32x4 zb[4];                                      // whole 16-token blocks
 #pragma unroll
-        for (int K = 0; K < 4; ++K) z[K] = *reinterpret_cast<const f32x4*>(Fs + (K < 3 ? K : 6) * KPAD + c0);
-        if (rg == 0) {   // rows 0..2 (pairs (1,0) (2,1) (3,2)) already hold Z_0..Z_2
-            *reinterpret_cast<f32x4*>(Fs + 3 * KPAD + c0) = z[0] * z[1];          // pair (2,0)
-            *reinterpret_cast<f32x4*>(Fs + 4 * KPAD + c0) = z[1] * z[2];          // pair (3,1)
-            *reinterpret_cast<f32x4*>(Fs + 5 * KPAD + c0) = z[0] * z[1] * z[2];   // pair (3,0)
-            *reinterpret_cast<f32x4*>(gaml_out + c0) = z[0] * z[1] * z[2] * z[3];
-        }
-        f32x4 pre = {1.f, 1.f, 1.f, 1.f}, post = pre;
+        for (int K = 0; K < 4; ++K) zb[K] = pre;
 #pragma unroll
-        for (int K = 0; K < 4; ++K) {
-            if (K < p) pre *= z[K];
-            if (K > p) post *= z[K];
+        for (int h = 0; h < 8; ++h) {
+            const f32x4 z = *reinterpret_cast<const f32x4*>(Fs + (SM::TL + h) * KPAD + c0) *
+                            *reinterpret_cast<const f32x4*>(Fs + (SM::TT + h) * KPAD + c0);
+            if (h < rg) pre *= z;
+            if (h > rg) post *= z;
+            if (h == rg - 1) zprev = z;
+            if (h == rg + 1) znext = z;
+            zb[h >> 1] *= z;
+            gaml *= z;
         }
+        // row correction of off-diagonal tiles for rows in this half; column
+        // corrections of the tiles (I, J), J = rg / 2 < I, for columns in this half
+        *reinterpret_cast<f32x4*>(Fs + (SM::TRS + rg) * KPAD + c0) = (rg & 1) ? lam * zprev : lam;
+        {
+            const int J = rg >> 1;
+            f32x4 F = (rg & 1) ? tau : tau * znext;
+#pragma unroll
+            for (int I = 1; I < 4; ++I) {
+                if (I > J) {
+                    const int pair = I - J == 1 ? J : (I - J == 2 ? 3 + J : 5);
+                    *reinterpret_cast<f32x4*>(Fs + (SM::TCS + 2 * pair + (rg & 1)) * KPAD + c0) = F;
+                    F *= zb[I];                           // the tile (I+1, J) also spans block I
+                }
+            }
+        }
+        if (rg == 0) *reinterpret_cast<f32x4*>(gaml_out + c0) = gaml;
         Tio kt[4][8], qt[4][8];
+        f32x4 inc = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int r = 8 * rg + i;
+            inc *= al[i];
             const f32x4 kv = IO::unpack4(kk[i]) * sk[i], qv = IO::unpack4(qq[i]) * sq[i];
-            const f32x4 ig = {fast_rcp(g[i][0]), fast_rcp(g[i][1]), fast_rcp(g[i][2]), fast_rcp(g[i][3])};
-            const f32x4 xe = bt[i] * kv * g[i], xq = qv * g[i];
-            st_vec4(Xe + xo(r, c0), xe);
-            st_vec4(Xq + xo(r, c0), xq);
-            st_vec4(Yd + xo(r, c0), kv * ig);
-            const f32x4 qhv = xq * pre;
+            const f32x4 ev = bt[i] * kv;
+            st_vec4(Xe + xo(r, c0), ev * rho[i]);
+            st_vec4(Xq + xo(r, c0), qv * rho[i]);
+            st_vec4(Yd + xo(r, c0), kv * sig[i]);
+            const f32x4 gam = pre * inc;                  // Gamma_r
+            const f32x4 qhv = qv * gam;
             if constexpr (!TOUT) st_vec4(qh_out + r * KPAD + c0, qhv);
-            const f32x4 ehv = xe * pre, ktv = kv * (zblk * ig) * post;
+            const f32x4 ehv = ev * gam, ktv = kv * suf[i] * post;
             if constexpr (TOUT) {
                 st_vec4(kn_out + r * DK + c0, ktv);
                 st_vec4(eh_out + r * DK + c0, ehv);
@@ -369,6 +406,10 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
     // ---- 2. A^T and P^T tiles on the matrix cores ---------------------------
     // tile (J, I): rows s of block J, columns r of block I,
     // D[s][r] = sum_c Y[s][c] (f_IJ[c]) X[r][c]
+    // Lane l16 supplies row s = 16J + l16 of the column operand and row
+    // r = 16I + l16 of the row operands; a diagonal tile adds a second product
+    // with the corrections of second-half rows against first-half columns and
+    // keeps it where the lane's element pairs those halves.
     f32x4 accA[3], accP[3];
 #pragma unroll
     for (int pi = 0; pi < 3; ++pi) {
@@ -377,16 +418,38 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
         const int pr = wave + 4 * pi;
         if (pr < 10) {
             const int I = unpack2(kPairI, pr), J = unpack2(kPairJ, pr);
+            const int hl = l16 >> 3;
+            const bool diag = pr < 4;
+            // corrections: off-diagonal rows by half 2I + hl, columns by (tile, half 2J + hl);
+            // the diagonal's second product rows by lambda of half 2I+1, columns by tau of half 2I
+            const float* rsc = Fs + (diag ? SM::TL + 2 * I + 1 : SM::TRS + 2 * I + hl) * KPAD;
+            const float* csc = Fs + (diag ? SM::TT + 2 * I : SM::TCS + 2 * (pr - 4) + hl) * KPAD;
+            f32x4 a1 = {0.f, 0.f, 0.f, 0.f}, p1 = a1;
 #pragma unroll
             for (int kb = 0; kb < KPAD / KB; ++kb) {
                 const int ko = kb * KB + grp * EPL;
-                typename IO::frag y = ld_frag(Yd + xo(16 * J + l16, ko));
-                if (pr >= 4) y = IO::scale(y, Fs + (pr - 4) * KPAD + ko);
+                const typename IO::frag y = ld_frag(Yd + xo(16 * J + l16, ko));
                 const typename IO::frag xe = ld_frag(Xe + xo(16 * I + l16, ko));
                 const typename IO::frag xq = ld_frag(Xq + xo(16 * I + l16, ko));
-                accA[pi] = IO::mma(accA[pi], y, xe);
-                if constexpr (TOUT) accP[pi] = IO::mma(accP[pi], xq, y);   // D[r][s]
-                else accP[pi] = IO::mma(accP[pi], y, xq);
+                const typename IO::frag ys = IO::scale(y, csc + ko);
+                const typename IO::frag xes = IO::scale(xe, rsc + ko);
+                const typename IO::frag xqs = IO::scale(xq, rsc + ko);
+                if (diag) {
+                    accA[pi] = IO::mma(accA[pi], y, xe);
+                    if constexpr (TOUT) accP[pi] = IO::mma(accP[pi], xq, y);   // D[r][s]
+                    else accP[pi] = IO::mma(accP[pi], y, xq);
+                }
+                a1 = IO::mma(a1, ys, xes);
+                if constexpr (TOUT) p1 = IO::mma(p1, xqs, ys);
+                else p1 = IO::mma(p1, ys, xqs);
+            }
+            // accumulator element e: D[s = 4grp + e][r = l16] (TOUT's P: D[r = 4grp + e][s = l16])
+            if (!diag) {
+                accA[pi] = a1;
+                accP[pi] = p1;
+            } else {
+                if (l16 >= 8 && grp < 2) accA[pi] = a1;            // r second half, s first half
+                if (TOUT ? (l16 < 8 && grp >= 2) : (l16 >= 8 && grp < 2)) accP[pi] = p1;
             }
         }
     }

@@ -58,11 +58,16 @@
  *   {16, 32, 64, 128}; dv a multiple of 16 in [16, 256]; chunk == 64 for the
  *   chunked mode.
  * Domain.  alpha in (0, 1] (after the sigmoid with GATE_LOGITS).  The
- *   chunked mode rescales keys by partial decay products inside 16-token
- *   blocks, so within any 16 consecutive tokens of a chunk the product of
- *   alpha in one key channel must stay above ~1e-30 (fp32 range); the
- *   recurrent mode has no such limit.  b, w, q, k, v are any finite values
- *   (b in (0, 2) is the README's negative-eigenvalue option, "b x 2").
+ *   chunked forward rescales keys and queries by decay products of at most
+ *   4 consecutive tokens (and their inverses), so the product of alpha over
+ *   any 4 consecutive tokens of one key channel must stay above ~1e-30 (fp32
+ *   range); every other decay factor it forms is a product of alphas (<= 1),
+ *   so faster decay than that only underflows terms that are negligible.
+ *   The chunked backward rescales by products inside 16-token blocks: there
+ *   the product over any 16 consecutive tokens of a chunk must stay above
+ *   ~1e-30.  The recurrent mode has no such limit.  b, w, q, k, v are any
+ *   finite values (b in (0, 2) is the README's negative-eigenvalue option,
+ *   "b x 2").
  * Alignment.  Every tensor pointer is 16-byte aligned (the kernels use
  *   16-byte vector accesses); the workspace is 256-byte aligned.
  * Aliasing.  Inputs are never written.  Outputs (o, S_out, workspace) must

@@ -412,6 +412,39 @@ def test_chunk_d128_against_oracle_and_stages(dev, case):
     check(f"prep + state B{B}T{T}H{H}dv{dv}", o2, S2, ro, rS, 2e-2)
 
 
+@pytest.mark.parametrize("mu", [-6.0, -12.0])
+def test_chunk_decay_far_below_the_workloads(dev, mu):
+    """alpha = sigmoid(N(mu, 1)): at mu = -12 the product over 16 tokens (~1e-83) is far
+    outside the fp32 range; the chunked form's operands are bounded by products of 4 alphas
+    (~1e-21) and it stays at the bf16 bar in both output and state."""
+    inp = make(dev, 2, 200, 2, 128, 64, torch.bfloat16, seed=int(-mu) + 50, s0=0.05, b_scale=2.0,
+               alpha_mu=mu)
+    o, S = g.chunk_fwd(*args(inp), inp["S0"])
+    torch.cuda.synchronize()
+    ro, rS = oracle(inp)
+    check(f"chunk alpha_mu {mu}", o, S, ro, rS, 2e-2)
+
+
+def test_chunk_decay_fp32_far_below(dev):
+    """The fp32 operand path (dk 64, dv 48) at alpha = sigmoid(N(-8, 1)), against the fp32 bar."""
+    inp = make(dev, 1, 230, 2, 64, 48, torch.float32, seed=71, s0=0.05, b_scale=2.0, alpha_mu=-8.0)
+    o, S = g.chunk_fwd(*args(inp), inp["S0"])
+    torch.cuda.synchronize()
+    ro, rS = oracle(inp)
+    check("chunk fp32 alpha_mu -8", o, S, ro, rS, 1e-4)
+
+
+def test_chunk_decay_mix_and_exact_one(dev):
+    """alpha = 1 exactly on some channels (no decay), 1e-3 on others, the draw elsewhere."""
+    inp = make(dev, 1, 260, 3, 128, 128, torch.bfloat16, seed=61, s0=0.05, b_scale=2.0)
+    inp["alpha"][..., ::7] = 1.0
+    inp["alpha"][..., 3::7] = 1e-3
+    o, S = g.chunk_fwd(*args(inp), inp["S0"])
+    torch.cuda.synchronize()
+    ro, rS = oracle(inp)
+    check("chunk alpha mix", o, S, ro, rS, 2e-2)
+
+
 @pytest.mark.parametrize("flags", [1, 3, 4, 7])
 def test_chunk_d128_prologue_flags_and_grouped_heads(dev, flags):
     """In-kernel prologue (gate logits in bf16, b x 2, q/k L2 norm) and 2 value heads per
