@@ -69,7 +69,8 @@
  *   finite values (b in (0, 2) is the README's negative-eigenvalue option,
  *   "b x 2").
  * Alignment.  Every tensor pointer is 16-byte aligned (the kernels use
- *   16-byte vector accesses); the workspace is 256-byte aligned.
+ *   16-byte vector accesses); the workspace is 256-byte aligned (a workspace
+ *   that is not is GDN2_ERR_WORKSPACE).
  * Aliasing.  Inputs are never written.  Outputs (o, S_out, workspace) must
  *   not overlap any input or each other, except that S_out may equal S0 /
  *   S_in exactly (in-place state update).  Any other overlap is an error.
@@ -97,7 +98,7 @@ typedef enum {
     GDN2_ERR_SHAPE = 2,      /* unsupported or inconsistent sizes               */
     GDN2_ERR_DTYPE = 3,      /* unsupported dtype pair                          */
     GDN2_ERR_ALIAS = 4,      /* an output overlaps an input or another output   */
-    GDN2_ERR_WORKSPACE = 5,  /* workspace missing or smaller than required      */
+    GDN2_ERR_WORKSPACE = 5,  /* workspace missing, too small or not 256-B aligned */
     GDN2_ERR_DEVICE = 6,     /* no usable GPU, or a launch failed               */
     GDN2_ERR_ALIGN = 7       /* a pointer is misaligned (16 B; cu_seqlens 4 B)  */
 } gdn2_status;
