@@ -397,6 +397,7 @@ def main(argv=None):
         result["chunk_bwd"] = backward_leg(g, inputs, wl_c, dev, args)
         result["epilogue"] = epilogue_leg(g, outs, dev, args)
         result["short_conv"] = short_conv_leg(g, dev, args)
+        result["conv_fused"] = conv_fused_leg(g, inputs, wl_c, dev, args)
 
     ok = bool(torch.isfinite(outs[0].float()).all() and torch.isfinite(states[0]).all()
               and torch.isfinite(douts[0].float()).all())
@@ -771,6 +772,101 @@ def short_conv_leg(g, dev, args, B=4, T=2048, C=3 * 16 * 128, K=4):
                      "alg_bytes": int(nbytes),
                      "roofline": {"kernel": kern, "bound": "hbm", "achieved": round(gbps, 1),
                                   "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4)}}
+    return out
+
+
+def conv_fused_leg(g, inputs, wl, dev, args, K=4):
+    """The prologue's short convolution fused into the chunked forward and into the decode
+    step, against the unfused chain (the standalone convolution on the concatenated
+    [q | k | v] projection, its three parts made contiguous, then the core call).  Both
+    with bf16 gate logits and unnormalised q/k (flags gate-logits | b x 2 | L2 norm),
+    K = 4 taps with SiLU and the window carried in and out.  The fused chunked call reads
+    each input once: algorithmic bytes = q, k, v and the gates in bf16 + o per head-token,
+    plus the [C, K] taps and the windows."""
+    import torch
+    B, T, H, dk, dv = wl.B, wl.T, wl.H, wl.dk, wl.dv
+    flags = g.FLAG_GATE_LOGITS | g.FLAG_NEG_EIGVAL | g.FLAG_QK_L2NORM
+    C = 2 * H * dk + H * dv
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(21)
+    n_sets = max(args.sets, 1)
+    sets = [inputs.make_raw(B, T, H, dk, dv, wl.io_dtype, 400 + i, dev, gate_logits=True, unit_qk=False,
+                            gate_dtype=torch.bfloat16) for i in range(n_sets)]
+    wt = torch.randn(C, K, generator=gen, device=dev) * 0.5
+    wins = [(torch.randn(B, K - 1, C, generator=gen, device=dev) * 0.5).to(wl.io_dtype) for _ in range(n_sets)]
+    xcat = [torch.cat([x["q"].reshape(B, T, -1), x["k"].reshape(B, T, -1), x["v"].reshape(B, T, -1)], -1)
+            .contiguous() for x in sets]
+    outs = [torch.empty_like(x["v"]) for x in sets]
+    S = torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev)
+    wout = torch.empty(B, K - 1, C, dtype=wl.io_dtype, device=dev)
+    ws = g.alloc_workspace(g.chunk_fwd_workspace_size(B, T, H, dk, dv, wl.io_dtype), dev)
+    steps = max(args.steps // 2, 5)
+
+    def run(fn, nsteps=steps):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nsteps)]
+        for i in range(args.warmup + nsteps):
+            ev = evs[i - args.warmup] if i >= args.warmup else None
+            if ev:
+                ev[0].record()
+            fn(i % n_sets)
+            if ev:
+                ev[1].record()
+        torch.cuda.synchronize()
+        t = sorted(e[0].elapsed_time(e[1]) for e in evs)
+        return {"us": round(sum(t) / len(t) * 1e3, 2), "median_us": round(t[len(t) // 2] * 1e3, 2)}
+
+    A = lambda x: (x["q"], x["k"], x["v"], x["alpha"], x["b"], x["w"])
+
+    def fused(j):
+        g.chunk_fwd_conv(*A(sets[j]), wt, wins[j], None, conv_silu=True, conv_state_out=wout, o=outs[j],
+                         S_out=S, workspace=ws, flags=flags)
+
+    def unfused(j):
+        y, _ = g.short_conv(xcat[j], wt, wins[j], silu=True, state_out=wout)
+        q = y[..., :H * dk].reshape(B, T, H, dk).contiguous()
+        k = y[..., H * dk:2 * H * dk].reshape(B, T, H, dk).contiguous()
+        v = y[..., 2 * H * dk:].reshape(B, T, H, dv).contiguous()
+        x = sets[j]
+        g.chunk_fwd(q, k, v, x["alpha"], x["b"], x["w"], None, o=outs[j], S_out=S, workspace=ws, flags=flags)
+
+    tf, tu = run(fused), run(unfused)
+    per_ht = 2 * (2 * dk + dv) + 2 * (2 * dk + dv) + 2 * dv
+    alg = per_ht * B * T * H + B * H * dk * dv * 4 + C * K * 4 + 2 * B * (K - 1) * C * 2
+    gbps = alg / (tf["us"] * 1e-6) / 1e9
+    out = {"workload": f"chunk fwd B{B} H{H} T{T} d{dk}, bf16, gate logits | b x 2 | q/k L2 norm, "
+                       f"short convolution K{K} SiLU fused (window in/out)",
+           "fused": {**tf, "tokens_per_s": round(B * T / (tf["us"] * 1e-6), 1),
+                     "alg_bytes": int(alg), "alg_GBps": round(gbps, 1), "frac_hbm_roofline": round(gbps / PEAK_HBM_GBPS, 4)},
+           "unfused_chain": {**tu, "tokens_per_s": round(B * T / (tu["us"] * 1e-6), 1),
+                             "calls": "gdn2_short_conv + 3 contiguous copies + gdn2_chunk_fwd"},
+           "speedup": round(tu["us"] / tf["us"], 3)}
+
+    # the decode step with its window: B 256, H 16, one token
+    Bd = 256
+    dsets = [inputs.make_raw(Bd, 1, H, dk, dv, wl.io_dtype, 500 + i, dev, s0_std=0.05, gate_logits=True,
+                             unit_qk=False, gate_dtype=torch.bfloat16) for i in range(n_sets)]
+    dwin = [(torch.randn(Bd, K - 1, C, generator=gen, device=dev) * 0.5).to(wl.io_dtype) for _ in range(2)]
+    dS = torch.empty(Bd, H, dk, dv, dtype=torch.float32, device=dev)
+    dout = torch.empty_like(dsets[0]["v"])
+    dxcat = [torch.cat([x["q"].reshape(Bd, 1, -1), x["k"].reshape(Bd, 1, -1), x["v"].reshape(Bd, 1, -1)], -1)
+             .contiguous() for x in dsets]
+
+    def dfused(j):
+        g.recurrent_step_conv(*A(dsets[j]), wt, dwin[j % 2], dsets[j]["S0"], conv_silu=True,
+                              conv_state_out=dwin[(j + 1) % 2], o=dout, S_out=dS, flags=flags)
+
+    def dunfused(j):
+        y, _ = g.short_conv(dxcat[j], wt, dwin[j % 2], silu=True, state_out=dwin[(j + 1) % 2])
+        q = y[..., :H * dk].reshape(Bd, 1, H, dk).contiguous()
+        k = y[..., H * dk:2 * H * dk].reshape(Bd, 1, H, dk).contiguous()
+        v = y[..., 2 * H * dk:].reshape(Bd, 1, H, dv).contiguous()
+        x = dsets[j]
+        g.recurrent_step(q, k, v, x["alpha"], x["b"], x["w"], x["S0"], o=dout, S_out=dS, flags=flags)
+
+    df, du = run(dfused), run(dunfused)
+    out["decode"] = {"workload": f"decode step B{Bd} H{H} d{dk} bf16 with its window (K{K} SiLU)",
+                     "fused": df, "unfused_chain": {**du, "calls": "gdn2_short_conv + 3 copies + gdn2_recurrent_step"},
+                     "speedup": round(du["us"] / df["us"], 3)}
     return out
 
 

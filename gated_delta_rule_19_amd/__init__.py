@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     FLAG_NEG_EIGVAL,
     FLAG_QK_L2NORM,
     CONV_SILU,
+    Conv,
     Gdn2Error,
     Problem,
     abi_version,
@@ -20,6 +21,7 @@ from ._binding import (  # noqa: F401
     chunk_bwd_varlen,
     chunk_bwd_workspace_size,
     chunk_fwd,
+    chunk_fwd_conv,
     chunk_fwd_noalloc,
     NOALLOC_SCRATCH_BYTES,
     chunk_fwd_varlen,
@@ -32,6 +34,7 @@ from ._binding import (  # noqa: F401
     lib,
     problem,
     recurrent_step,
+    recurrent_step_conv,
     recurrent_step_gated,
     recurrent_varlen,
     short_conv,

@@ -16,7 +16,7 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn2.so")
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 GDN2_F32, GDN2_BF16 = 0, 1
 FLAG_GATE_LOGITS, FLAG_NEG_EIGVAL, FLAG_QK_L2NORM = 1, 2, 4
 CONV_SILU = 1
@@ -28,7 +28,8 @@ EXPORTED = ("gdn2_abi_version", "gdn2_status_str", "gdn2_chunk_fwd_workspace_siz
             "gdn2_recurrent_varlen", "gdn2_chunk_bwd_workspace_size", "gdn2_chunk_bwd",
             "gdn2_short_conv", "gdn2_short_conv_bwd_workspace_size", "gdn2_short_conv_bwd",
             "gdn2_chunk_bwd_varlen_workspace_size", "gdn2_chunk_bwd_varlen", "gdn2_chunk_fwd_noalloc",
-            "gdn2_chunk_prep_workspace_size", "gdn2_recurrent_step_gated")
+            "gdn2_chunk_prep_workspace_size", "gdn2_recurrent_step_gated", "gdn2_chunk_fwd_conv",
+            "gdn2_recurrent_step_conv")
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -42,6 +43,12 @@ class Problem(ctypes.Structure):
     @property
     def value_heads(self) -> int:
         return self.Hv if self.Hv else self.H
+
+
+class Conv(ctypes.Structure):
+    """Mirror of ``gdn2_conv`` (include/gdn2.h): the short convolution fused into the prologue."""
+    _fields_ = [("weight", ctypes.c_void_p), ("state_in", ctypes.c_void_p), ("state_out", ctypes.c_void_p),
+                ("K", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 class Gdn2Error(RuntimeError):
@@ -82,6 +89,11 @@ def lib():
         L.gdn2_recurrent_step_gated.argtypes = [P] + [vp] * 11 + [vp]
         L.gdn2_recurrent_step.restype = ctypes.c_int
         L.gdn2_recurrent_step.argtypes = [P] + [vp] * 9 + [vp]
+        CP = ctypes.POINTER(Conv)
+        L.gdn2_chunk_fwd_conv.restype = ctypes.c_int
+        L.gdn2_chunk_fwd_conv.argtypes = [P, CP] + [vp] * 9 + [vp, sz, vp]
+        L.gdn2_recurrent_step_conv.restype = ctypes.c_int
+        L.gdn2_recurrent_step_conv.argtypes = [P, CP] + [vp] * 9 + [vp]
         L.gdn2_gated_rmsnorm.restype = ctypes.c_int
         L.gdn2_gated_rmsnorm.argtypes = [P, vp, vp, vp, vp, vp]
         L.gdn2_chunk_fwd_varlen_workspace_size.restype = sz
@@ -260,6 +272,80 @@ def recurrent_step(q, k, v, alpha, b, w, S_in=None, *, o=None, S_out=None, out_s
     _check(lib().gdn2_recurrent_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b), _ptr(w),
                                      _ptr(S_in), _ptr(o), _ptr(S_out), _stream(dev)))
     return o, S_out
+
+
+def _conv_from(p: Problem, dev, weight, state, state_out, K, silu):
+    """The fused convolution's descriptor; checks shapes ([C, K] fp32 taps, [B, K-1, C] windows
+    in the I/O dtype, C = 2 H dk + Hv dv)."""
+    C = 2 * p.H * p.dk + p.value_heads * p.dv
+    K = int(weight.shape[1]) if K is None else int(K)
+    if tuple(weight.shape) != (C, K) or weight.dtype != torch.float32 or weight.device != dev \
+            or not weight.is_contiguous():
+        raise ValueError(f"conv weight must be a contiguous float32 [{C}, {K}] tensor on {dev}")
+    io = torch.bfloat16 if p.io_dtype == GDN2_BF16 else torch.float32
+    for name, t in (("conv state", state), ("conv state_out", state_out)):
+        if t is not None and (tuple(t.shape) != (p.B, K - 1, C) or t.dtype != io or t.device != dev
+                              or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous [{p.B}, {K - 1}, {C}] {io} tensor on {dev}")
+    return Conv(_ptr(weight), _ptr(state), _ptr(state_out), K, CONV_SILU if silu else 0)
+
+
+def chunk_fwd_conv(q, k, v, alpha, b, w, conv_weight, conv_state=None, S0=None, *, conv_silu: bool = False,
+                   want_conv_state: bool = True, conv_state_out=None, out_state: bool = True, o=None,
+                   S_out=None, workspace=None, flags: int = 0):
+    """Chunked forward with the short convolution fused into its prologue
+    (``gdn2_chunk_fwd_conv``): equals :func:`short_conv` on the concatenated [q | k | v]
+    followed by :func:`chunk_fwd` on the three parts.  ``conv_weight``: [C, K] float32,
+    C = 2 H dk + Hv dv; ``conv_state``: [B, K-1, C] window before the first token (None =
+    zeros); ``conv_state_out=conv_state`` updates it in place.
+    Returns (o, S_final or None, conv window after the last token or None)."""
+    p, dev = _problem_from(q, k, v, alpha, b, w, flags)
+    _check_state(S0, p, dev, "S0")
+    K = int(conv_weight.shape[1])
+    C = 2 * p.H * p.dk + p.value_heads * p.dv
+    if conv_state_out is None and want_conv_state and K > 1:
+        conv_state_out = torch.empty((p.B, K - 1, C), dtype=v.dtype, device=dev)
+    cv = _conv_from(p, dev, conv_weight, conv_state, conv_state_out, K, conv_silu)
+    if o is None:
+        o = torch.empty(v.shape, dtype=v.dtype, device=dev)
+    if S_out is None and out_state:
+        S_out = torch.empty((p.B, p.value_heads, p.dk, p.dv), dtype=torch.float32, device=dev)
+    _check_state(S_out, p, dev, "S_out")
+    need = int(lib().gdn2_chunk_fwd_workspace_size(ctypes.byref(p)))
+    if workspace is None:
+        workspace = alloc_workspace(need, dev)
+    _check(lib().gdn2_chunk_fwd_conv(ctypes.byref(p), ctypes.byref(cv), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                     _ptr(b), _ptr(w), _ptr(S0), _ptr(o), _ptr(S_out), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(dev)))
+    return o, S_out, (conv_state_out if K > 1 else None)
+
+
+def recurrent_step_conv(q, k, v, alpha, b, w, conv_weight, conv_state=None, S_in=None, *, conv_silu: bool = False,
+                        want_conv_state: bool = True, conv_state_out=None, o=None, S_out=None,
+                        out_state: bool = True, inplace: bool = False, flags: int = 0):
+    """Recurrent forward with the short convolution fused (``gdn2_recurrent_step_conv``);
+    T == 1 is the decode step with its window.  ``conv_state_out`` must be a different
+    buffer from ``conv_state``.  Returns (o, S_final or None, window or None)."""
+    p, dev = _problem_from(q, k, v, alpha, b, w, flags)
+    _check_state(S_in, p, dev, "S_in")
+    K = int(conv_weight.shape[1])
+    C = 2 * p.H * p.dk + p.value_heads * p.dv
+    if conv_state_out is None and want_conv_state and K > 1:
+        conv_state_out = torch.empty((p.B, K - 1, C), dtype=v.dtype, device=dev)
+    cv = _conv_from(p, dev, conv_weight, conv_state, conv_state_out, K, conv_silu)
+    if o is None:
+        o = torch.empty(v.shape, dtype=v.dtype, device=dev)
+    if inplace:
+        if S_in is None:
+            raise ValueError("inplace needs S_in")
+        S_out = S_in
+    elif S_out is None and out_state:
+        S_out = torch.empty((p.B, p.value_heads, p.dk, p.dv), dtype=torch.float32, device=dev)
+    _check_state(S_out, p, dev, "S_out")
+    _check(lib().gdn2_recurrent_step_conv(ctypes.byref(p), ctypes.byref(cv), _ptr(q), _ptr(k), _ptr(v),
+                                          _ptr(alpha), _ptr(b), _ptr(w), _ptr(S_in), _ptr(o), _ptr(S_out),
+                                          _stream(dev)))
+    return o, S_out, (conv_state_out if K > 1 else None)
 
 
 def recurrent_step_gated(q, k, v, alpha, b, w, g, norm_weight, S_in=None, *, y=None, S_out=None,

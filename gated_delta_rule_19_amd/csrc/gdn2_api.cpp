@@ -165,24 +165,77 @@ int device_ready()
 
 int launch_status(hipError_t e) { return e == hipSuccess ? GDN2_OK : GDN2_ERR_DEVICE; }
 
+// channels of the fused short convolution: q | k | v of the concatenated projection
+int64_t conv_channels(const gdn2_problem* p) { return 2 * p->H * p->dk + nvh(p) * p->dv; }
+
+// the fused convolution's window moves only when it has taps before the
+// current token and somewhere new to go
+bool conv_window_moves(const gdn2_conv* c)
+{
+    return c != nullptr && c->K > 1 && c->state_out != nullptr && c->state_out != c->state_in;
+}
+
 int do_prep(const gdn2_problem* p, const void* q, const void* k, const void* v, const void* alpha,
-            const void* b, const void* w, void* ws, hipStream_t s)
+            const void* b, const void* w, void* ws, hipStream_t s, const gdn2_conv* conv = nullptr)
 {
     if (p->B * nvh(p) * nchunks(p) == 0) return GDN2_OK;
     gdn2::PrepArgs a{q, k, v, alpha, b, w, ws, ws_block_bytes(p), p->B, p->T, nvh(p), p->H,
                      (int)p->dv, (int)nchunks(p), (int)p->flags, nullptr, 0};
+    if (conv != nullptr) {
+        a.conv_w = conv->weight;
+        a.conv_in = conv->K > 1 ? conv->state_in : nullptr;
+        a.conv_C = conv_channels(p);
+        a.conv_K = conv->K;
+        a.conv_silu = (conv->flags & GDN2_CONV_SILU) != 0;
+    }
     return launch_status(gdn2::launch_chunk_prep(a, (int)p->dk, is_bf16(p), gates_bf16(p), s));
 }
 
-int do_state(const gdn2_problem* p, const float* S0, void* o, float* S_out, const void* ws, hipStream_t s)
+// conv (optional): the fused convolution whose window after the last token
+// the first slice of each chain writes (q, k, v: the raw inputs)
+int do_state(const gdn2_problem* p, const float* S0, void* o, float* S_out, const void* ws, hipStream_t s,
+             const gdn2_conv* conv = nullptr, const void* q = nullptr, const void* k = nullptr,
+             const void* v = nullptr)
 {
     const int64_t nch = p->B * nvh(p);
     if (nch == 0) return GDN2_OK;
-    if (nchunks(p) == 0 && S_out == S0) return GDN2_OK;   // nothing to compute or copy
+    const bool window = conv != nullptr && conv->K > 1 && conv->state_out != nullptr;
+    if (nchunks(p) == 0 && S_out == S0 && !conv_window_moves(conv)) return GDN2_OK;   // nothing to do
     const int vs = gdn2::chunk_state_slice(nch, (int)p->dv, (int)p->dk, (int)io_size(p));
     gdn2::StateArgs a{ws, ws_block_bytes(p), S0, o, S_out, p->B, p->T, nvh(p), (int)p->dv,
                       (int)nchunks(p), (int)(p->dv / vs), nullptr, 0};
+    if (window) {
+        a.cq = q;
+        a.ck = k;
+        a.cv = v;
+        a.conv_in = conv->state_in;
+        a.conv_out = conv->state_out;
+        a.conv_C = conv_channels(p);
+        a.Hk = p->H;
+        a.conv_K = conv->K;
+    }
     return launch_status(gdn2::launch_chunk_state(a, (int)p->dk, vs, is_bf16(p), s));
+}
+
+// the fused convolution's descriptor: taps, option, weights present and
+// aligned; equal-length batches only
+int check_conv(const gdn2_problem* p, const gdn2_conv* c)
+{
+    if (c == nullptr || c->weight == nullptr) return GDN2_ERR_NULL;
+    if (c->K < 1 || c->K > 4) return GDN2_ERR_SHAPE;
+    if (c->flags != 0 && c->flags != GDN2_CONV_SILU) return GDN2_ERR_SHAPE;
+    (void)p;
+    return GDN2_OK;
+}
+
+// ranges of the convolution's weights and windows
+Range conv_weight_range(const gdn2_problem* p, const gdn2_conv* c)
+{
+    return range_of(c->weight, conv_channels(p) * c->K * 4);
+}
+Range conv_state_range(const gdn2_problem* p, const gdn2_conv* c, const void* ptr)
+{
+    return range_of(c->K > 1 ? ptr : nullptr, p->B * (c->K - 1) * conv_channels(p) * io_size(p));
 }
 
 // backward workspace: forward factors | chunk entry states | chunk exit
@@ -463,6 +516,45 @@ int gdn2_chunk_fwd_noalloc(const gdn2_problem* p, const void* q, const void* k, 
     return do_state(p, S0, o, S_out, ws, s);
 }
 
+int gdn2_chunk_fwd_conv(const gdn2_problem* p, const gdn2_conv* conv, const void* q, const void* k,
+                        const void* v, const void* alpha, const void* b, const void* w, const float* S0,
+                        void* o, float* S_out, void* workspace, size_t workspace_bytes, void* stream)
+{
+    int st = check_problem(p, true);
+    if (st) return st;
+    st = check_conv(p, conv);
+    if (st) return st;
+    st = check_inputs(p, q, k, v, alpha, b, w, o);
+    if (st) return st;
+    const int64_t need = fwd_ws_bytes(p);
+    if (need > 0 && (workspace == nullptr || static_cast<int64_t>(workspace_bytes) < need))
+        return GDN2_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_WORKSPACE;
+    const Sizes z = sizes_of(p);
+    const Range cin = conv_state_range(p, conv, conv->state_in), cout = conv_state_range(p, conv, conv->state_out);
+    const Range ins[9] = {range_of(q, z.key),  range_of(k, z.key),  range_of(v, z.val),
+                          range_of(alpha, z.gk), range_of(b, z.gk), range_of(w, z.gv),
+                          range_of(S0, z.state), conv_weight_range(p, conv), cin};
+    const Range outs[4] = {range_of(o, z.val), range_of(S_out, z.state), range_of(workspace, need), cout};
+    // the window may be updated in place (equal pointers), like the state
+    st = check_alias(outs, 3, ins, 9, S0, S_out, 6, 1);
+    if (st) return st;
+    for (int j = 0; j < 8; ++j)
+        if (overlap(cout, ins[j])) return GDN2_ERR_ALIAS;
+    if (overlap(cout, cin) && conv->state_out != conv->state_in) return GDN2_ERR_ALIAS;
+    for (int j = 0; j < 3; ++j)
+        if (overlap(cout, outs[j])) return GDN2_ERR_ALIAS;
+    st = check_align({q, k, v, alpha, b, w, S0, o, S_out, conv->weight, conv->state_in, conv->state_out});
+    if (st) return st;
+    if (p->B * p->H == 0 || (nchunks(p) == 0 && S_out == S0 && !conv_window_moves(conv))) return GDN2_OK;
+    st = device_ready();
+    if (st) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    st = do_prep(p, q, k, v, alpha, b, w, workspace, s, conv);
+    if (st) return st;
+    return do_state(p, S0, o, S_out, workspace, s, conv, q, k, v);
+}
+
 int gdn2_recurrent_step(const gdn2_problem* p, const void* q, const void* k, const void* v,
                         const void* alpha, const void* b, const void* w, const float* S_in, void* o,
                         float* S_out, void* stream)
@@ -488,6 +580,47 @@ int gdn2_recurrent_step(const gdn2_problem* p, const void* q, const void* k, con
     const int vs = gdn2::recurrent_slice(nch, p->T, (int)p->dv);
     gdn2::RecArgs a{q, k, v, alpha, b, w, S_in, o, S_out, p->B, p->T, nvh(p), p->H, (int)p->dv,
                     (int)(p->dv / vs), (int)p->flags, nullptr};
+    return launch_status(gdn2::launch_recurrent(a, (int)p->dk, vs, is_bf16(p), gates_bf16(p),
+                                                static_cast<hipStream_t>(stream)));
+}
+
+int gdn2_recurrent_step_conv(const gdn2_problem* p, const gdn2_conv* conv, const void* q, const void* k,
+                             const void* v, const void* alpha, const void* b, const void* w,
+                             const float* S_in, void* o, float* S_out, void* stream)
+{
+    int st = check_problem(p, false);
+    if (st) return st;
+    st = check_conv(p, conv);
+    if (st) return st;
+    st = check_inputs(p, q, k, v, alpha, b, w, o);
+    if (st) return st;
+    const Sizes z = sizes_of(p);
+    const Range cout = conv_state_range(p, conv, conv->state_out);
+    const Range ins[9] = {range_of(q, z.key),  range_of(k, z.key),  range_of(v, z.val),
+                          range_of(alpha, z.gk), range_of(b, z.gk), range_of(w, z.gv),
+                          range_of(S_in, z.state), conv_weight_range(p, conv),
+                          conv_state_range(p, conv, conv->state_in)};
+    const Range outs[3] = {range_of(o, z.val), range_of(S_out, z.state), cout};
+    // the state may be updated in place; the window not (workgroups of one
+    // sequence read it while the first of them writes)
+    st = check_alias(outs, 3, ins, 9, S_in, S_out, 6, 1);
+    if (st) return st;
+    st = check_align({q, k, v, alpha, b, w, S_in, o, S_out, conv->weight, conv->state_in, conv->state_out});
+    if (st) return st;
+    const int64_t nch = p->B * nvh(p);
+    if (nch == 0) return GDN2_OK;
+    if (p->T == 0 && S_out == S_in && !conv_window_moves(conv)) return GDN2_OK;
+    st = device_ready();
+    if (st) return st;
+    const int vs = gdn2::recurrent_slice(nch, p->T, (int)p->dv);
+    gdn2::RecArgs a{q, k, v, alpha, b, w, S_in, o, S_out, p->B, p->T, nvh(p), p->H, (int)p->dv,
+                    (int)(p->dv / vs), (int)p->flags, nullptr};
+    a.conv_w = conv->weight;
+    a.conv_in = conv->K > 1 ? conv->state_in : nullptr;
+    a.conv_out = conv->K > 1 ? conv->state_out : nullptr;
+    a.conv_C = conv_channels(p);
+    a.conv_K = conv->K;
+    a.conv_silu = (conv->flags & GDN2_CONV_SILU) != 0;
     return launch_status(gdn2::launch_recurrent(a, (int)p->dk, vs, is_bf16(p), gates_bf16(p),
                                                 static_cast<hipStream_t>(stream)));
 }

@@ -88,8 +88,9 @@ struct PrepSmem {
     // half of its column block [12]
     static constexpr int TL = 0, TT = 8, TRS = 16, TCS = 24, NTAB = 36;
     static constexpr int BYTES = OF + NTAB * KPAD * 4;
-    // workgroups per CU the LDS and register budgets are sized for
-    static constexpr int MINB = BYTES * 3 <= 160 * 1024 ? 3 : (BYTES * 2 <= 160 * 1024 ? 2 : 1);
+    // workgroups per CU the LDS and register budgets are sized for (at most 2
+    // below dk 64, whose register use does not fit the budget of 3)
+    static constexpr int MINB = (BYTES * 3 <= 160 * 1024 && DK >= 64) ? 3 : (BYTES * 2 <= 160 * 1024 ? 2 : 1);
 };
 
 // block pairs (I >= J) of the 64x64 lower triangle, diagonal first; the
@@ -112,8 +113,58 @@ __device__ inline int unpack2(unsigned p, int i) { return (int)((p >> (2 * i)) &
 // Tg = gate dtype (alpha, b, w): float, or __bf16 with bf16 I/O
 // TOUT: the backward's layout of the block (bf16, KPAD = DK): Qh^T and P^T in
 // place of Qh and P, and T, Ktil, W^T and Eh appended from a.t_off on (BwdExt)
-template <typename Tio, int DK, int NUI, typename Tg, bool TOUT = false>
-__global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2)) void k_chunk_prep(PrepArgs a)
+// ---- fused short convolution ---------------------------------------------
+// Taps of 4 consecutive channels c..c+3 (weight [C][K] fp32), right-aligned
+// in 4 slots: w[m][e] = weight[c+e][m-(4-K)] for m >= 4-K, else 0, so that
+// z[t] = sum_m w[m] * x[t-3+m] for any K in 1..4.
+__device__ inline void conv_taps(const PrepArgs& a, int64_t c, f32x4 (&w)[4])
+{
+    const int K = a.conv_K;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[m][e] = m >= 4 - K ? a.conv_w[(c + e) * K + m - (4 - K)] : 0.f;
+}
+// the 4 inputs x[p, c..c+3] at position p of sequence seq: from the tensor
+// row `row` when p >= 0, from the carried window conv_in (rows p + K - 1)
+// for -(K-1) <= p < 0 (zeros when it is null), zeros before that (their taps
+// are zero)
+template <typename Tio>
+__device__ inline typename Io<Tio>::vec4 conv_hist(const PrepArgs& a, const Tio* row, int64_t p, int64_t seq, int64_t c)
+{
+    using IO = Io<Tio>;
+    const int K = a.conv_K;
+    if (p >= 0) return *reinterpret_cast<const typename IO::vec4*>(row);
+    if (p >= -(K - 1) && a.conv_in != nullptr)
+        return *reinterpret_cast<const typename IO::vec4*>(static_cast<const Tio*>(a.conv_in) +
+                                                            (seq * (K - 1) + K - 1 + p) * a.conv_C + c);
+    return IO::pack4(f32x4{0.f, 0.f, 0.f, 0.f});
+}
+// x[0..7] <- conv(x) over the window (h[0..2], x[0..7]) with the taps w, in
+// fp32, (optionally) through SiLU, rounded to the I/O type as a stored
+// convolution output would be; tokens last to first so that x is read raw
+template <typename Tio>
+__device__ inline void conv8(typename Io<Tio>::vec4 (&x)[8], const typename Io<Tio>::vec4 (&h)[3], const f32x4 (&w)[4], int silu)
+{
+    using IO = Io<Tio>;
+#pragma unroll
+    for (int i = 7; i >= 0; --i) {
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int j = i - 3 + m;
+            z += w[m] * IO::unpack4(j >= 0 ? x[j] : h[j + 3]);
+        }
+        if (silu) z = z * sigmoid4(z);
+        x[i] = IO::pack4(z);
+    }
+}
+
+// CONV: the short convolution fused into the prologue (PrepArgs conv_*)
+// (workgroups per CU: as LDS allows, at most 2 for wide values or the convolution)
+template <typename Tio, int DK, int NUI, typename Tg, bool TOUT = false, bool CONV = false>
+__global__ __launch_bounds__(kThreads, (((NUI <= 8 && !CONV) || (PrepSmem<Tio, DK>::MINB < 2)) ? PrepSmem<Tio, DK>::MINB : 2))
+void k_chunk_prep(PrepArgs a)
 {
     using IO = Io<Tio>;
     using SM = PrepSmem<Tio, DK>;
@@ -146,15 +197,16 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
     // first token, length L, workspace block chi
     const int64_t chi = blockIdx.x;
     int64_t hh, tok0;
+    int64_t seq = 0, t0 = 0;                             // sequence and first position (equal lengths)
     int L;
     if (a.plan == nullptr) {
         const int64_t chain = chi / a.nt;
         const int n = (int)(chi - chain * a.nt);
-        const int64_t bb = chain / a.H;
-        hh = chain - bb * a.H;
-        const int64_t t0 = (int64_t)n * kChunk;
+        seq = chain / a.H;
+        hh = chain - seq * a.H;
+        t0 = (int64_t)n * kChunk;
         L = (int)((a.T - t0) < kChunk ? (a.T - t0) : kChunk);
-        tok0 = bb * a.T + t0;
+        tok0 = seq * a.T + t0;
     } else {
         hh = chi / a.ncmax;
         const int64_t gc = chi - hh * a.ncmax;
@@ -212,6 +264,24 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
         btr[i] = __builtin_nontemporal_load(reinterpret_cast<const gvec*>(gb + off));
         kk[i] = __builtin_nontemporal_load(reinterpret_cast<const typename IO::vec4*>(k + offk));
         qq[i] = __builtin_nontemporal_load(reinterpret_cast<const typename IO::vec4*>(q + offk));
+    }
+    if constexpr (CONV) {
+        // the short convolution of q and k over the thread's 8 tokens, from the
+        // 3 inputs before them (before the sequence: the carried window)
+        const int64_t cq = (hh / (H / Hk)) * DK + c0, ck = Hk * DK + cq;
+        typename IO::vec4 hq[3], hk3[3];
+        f32x4 wq[4], wk[4];
+        conv_taps(a, cq, wq);
+        conv_taps(a, ck, wk);
+#pragma unroll
+        for (int m = 0; m < 3; ++m) {
+            const int r = 8 * rg - 3 + m;
+            const int rr = r < L ? r : L - 1;
+            hq[m] = conv_hist<Tio>(a, q + (row0k + (int64_t)rr * Hk) * DK + c0, t0 + r, seq, cq);
+            hk3[m] = conv_hist<Tio>(a, k + (row0k + (int64_t)rr * Hk) * DK + c0, t0 + r, seq, ck);
+        }
+        conv8<Tio>(qq, hq, wq, a.conv_silu);
+        conv8<Tio>(kk, hk3, wk, a.conv_silu);
     }
     // prologue: gate activations, q/k L2 norms (sum of squares over the NQ
     // lanes that hold one token's channels)
@@ -387,6 +457,8 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
     constexpr int NIT = NUI <= 8 ? 1 : 2;     // items per thread: 8 * dv/4 <= 256 * NIT
     gvec wr[NIT][8];
     typename IO::vec4 vr[NIT][8];
+    typename IO::vec4 vh[CONV ? NIT : 1][3];      // (CONV) the 3 inputs before the item's tokens
+    f32x4 wv[CONV ? NIT : 1][4];                  // (CONV) its columns' taps
     const Tg* gw = static_cast<const Tg*>(a.w);
     const int nvq = a.dv / 4;
 #pragma unroll
@@ -399,6 +471,16 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
             const int64_t off = (row0 + (s < L ? s : L - 1) * H) * a.dv + 4 * jq;
             wr[it][i] = __builtin_nontemporal_load(reinterpret_cast<const gvec*>(gw + off));
             vr[it][i] = __builtin_nontemporal_load(reinterpret_cast<const typename IO::vec4*>(v + off));
+        }
+        if constexpr (CONV) {
+            const int64_t cv = 2 * Hk * DK + hh * a.dv + 4 * jq;
+            conv_taps(a, cv, wv[it]);
+#pragma unroll
+            for (int m = 0; m < 3; ++m) {
+                const int r = 8 * sg - 3 + m;
+                const int rr = r < L ? r : L - 1;
+                vh[it][m] = conv_hist<Tio>(a, v + (row0 + (int64_t)rr * H) * a.dv + 4 * jq, t0 + r, seq, cv);
+            }
         }
     }
     __syncthreads();
@@ -579,6 +661,10 @@ __global__ __launch_bounds__(kThreads, (NUI <= 8 ? PrepSmem<Tio, DK>::MINB : 2))
     // ---- 5. U = T (w * v), stored transposed, in column blocks of 64 --------
     // (w*v) of tokens past the sequence end is zero
     frag uf[NIT][4][8 / EPL];      // per item and column: the 8 tokens as fragments
+    if constexpr (CONV) {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) conv8<Tio>(vr[it], vh[it], wv[it], a.conv_silu);
+    }
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
         const int sg = ((tid + it * kThreads) / nvq) & 7;
@@ -697,6 +783,53 @@ inline int state_lds_bytes(int dk, int vs, int es)
     return 0;
 }
 
+// The fused short convolution's window after the last token (StateArgs
+// conv_*, equal-length batches): the first slice of each chain copies the
+// last conv_K-1 inputs of its value head's columns, and of its query/key
+// head when it is the group's first value head, into conv_out.  The state
+// pass runs after the prep has read every input it needs, and here all reads
+// come before all writes (a barrier between), so conv_out may be conv_in.
+// Called by every thread of the workgroup.
+template <typename Tio, int DK>
+__device__ void conv_window_out(const StateArgs& a, int64_t bb, int64_t hh)
+{
+    using IO = Io<Tio>;
+    constexpr int MAXE = 4;                       // elements per thread (3 rows of 2 dk + dv <= 768)
+    const int K1 = a.conv_K - 1, nt = blockDim.x, tid = threadIdx.x;
+    const int64_t G = a.H / a.Hk, hk = hh / G;
+    const int nqk = (hh % G) == 0 ? 2 * DK : 0, nch = nqk + a.dv;
+    Tio val[MAXE];
+    int64_t dst[MAXE];
+#pragma unroll
+    for (int m = 0; m < MAXE; ++m) {
+        const int e = tid + m * nt;
+        dst[m] = -1;
+        if (e < K1 * nch) {
+            const int j = e / nch, ch = e - j * nch;
+            const int64_t p = a.T - K1 + j;       // position of row j of the window
+            int64_t c;
+            const Tio* src;
+            if (ch < nqk) {
+                const int which = ch / DK, cc = ch - which * DK;
+                c = which * a.Hk * DK + hk * DK + cc;
+                src = static_cast<const Tio*>(which == 0 ? a.cq : a.ck) + ((bb * a.T + p) * a.Hk + hk) * DK + cc;
+            } else {
+                const int col = ch - nqk;
+                c = 2 * a.Hk * DK + hh * a.dv + col;
+                src = static_cast<const Tio*>(a.cv) + ((bb * a.T + p) * a.H + hh) * a.dv + col;
+            }
+            if (p >= 0) val[m] = *src;
+            else if (a.conv_in != nullptr) val[m] = static_cast<const Tio*>(a.conv_in)[(bb * K1 + K1 + p) * a.conv_C + c];
+            else val[m] = IO::from_f(0.f);
+            dst[m] = (bb * K1 + j) * a.conv_C + c;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < MAXE; ++m)
+        if (dst[m] >= 0) static_cast<Tio*>(a.conv_out)[dst[m]] = val[m];
+}
+
 // value columns per compute wave and threads per workgroup of the state pass
 
 // CHK: write the state entering every chunk (the checkpoints of StateArgs)
@@ -751,6 +884,7 @@ __global__ __launch_bounds__(state_threads(VS, (int)sizeof(Tio)), 1) void k_chun
     const int j0 = slice * VS;
     const int64_t bb = chain / a.H, hh = chain - bb * a.H;   // sequence, value head
     const int dv = a.dv;
+    if (a.conv_out != nullptr && a.conv_K > 1 && slice == 0) conv_window_out<Tio, DK>(a, bb, hh);
     // the sequence's first packed token, its length, chunk count and first
     // workspace block
     int64_t tok0, tlen;
@@ -1127,6 +1261,16 @@ static hipError_t prep_dk(const PrepArgs& a, hipStream_t s)
         } else {
             return hipErrorInvalidValue;
         }
+    }
+    if (a.conv_w != nullptr) {                   // fused short convolution (equal-length batches)
+        if (a.plan != nullptr || a.conv_K < 1 || a.conv_K > 4) return hipErrorInvalidValue;
+        if (a.dv <= 64)
+            hipLaunchKernelGGL((k_chunk_prep<Tio, DK, 4, Tg, false, true>), dim3((unsigned)nblk), dim3(kThreads), 0, s, a);
+        else if (a.dv <= 128)
+            hipLaunchKernelGGL((k_chunk_prep<Tio, DK, 8, Tg, false, true>), dim3((unsigned)nblk), dim3(kThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_chunk_prep<Tio, DK, 16, Tg, false, true>), dim3((unsigned)nblk), dim3(kThreads), 0, s, a);
+        return hipGetLastError();
     }
     if (a.dv <= 64)
         hipLaunchKernelGGL((k_chunk_prep<Tio, DK, 4, Tg>), dim3((unsigned)nblk), dim3(kThreads), 0, s, a);

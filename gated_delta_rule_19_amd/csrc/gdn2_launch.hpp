@@ -24,6 +24,12 @@ struct PrepArgs {
     int64_t B, T, H, Hk; int dv; int nt; int flags;
     const int* plan; int64_t ncmax;
     int64_t t_off;          // backward: byte offset of T in each block (0 = not written)
+    // short convolution fused into the prologue (equal-length batches): conv_w
+    // [conv_C][conv_K] fp32 over the concatenated channels q | k | v (q/k head
+    // h channel c = h*DK + c and Hk*DK + h*DK + c, value head h column j =
+    // 2*Hk*DK + h*dv + j); conv_in [B][conv_K-1][conv_C] holds the inputs
+    // before each sequence (null = zeros); conv_w null = no convolution
+    const float* conv_w; const void* conv_in; int64_t conv_C; int conv_K; int conv_silu;
 };
 
 // Checkpoints (optional, equal-length batches only): the state entering every
@@ -36,6 +42,12 @@ struct StateArgs {
     int64_t B, T, H; int dv; int nt; int nslices;
     const int* plan; int64_t ncmax;
     float* S_chk; void* S_chkT; void* S_chkIo;
+    // the fused short convolution's carried window: the first slice of each
+    // chain writes conv_out [B][conv_K-1][conv_C] = the last conv_K-1 inputs
+    // (from cq/ck/cv and conv_in, as PrepArgs) of its value head's columns,
+    // and of its query/key head when it is the group's first value head
+    const void* cq; const void* ck; const void* cv; const void* conv_in; void* conv_out;
+    int64_t conv_C, Hk; int conv_K;
 };
 
 // cu (null for equal-length batches): the N+1 caller offsets of a packed
@@ -51,6 +63,9 @@ struct RecArgs {
     int64_t B, T, H, Hk; int dv; int nslices; int flags;
     const int* cu;
     const void* norm_g; const float* norm_w; float norm_eps;
+    // fused short convolution (as PrepArgs); conv_out receives the window
+    // after the last token and must not overlap conv_in
+    const float* conv_w; const void* conv_in; void* conv_out; int64_t conv_C; int conv_K; int conv_silu;
 };
 
 // Backward (equal-length batches, H value heads = query/key heads).  Reverse

@@ -33,7 +33,10 @@ namespace gdn2 {
 
 // Tg = gate dtype (alpha, b, w): float, or __bf16 with bf16 I/O; NT threads
 // (256, or 512 for whole rows of 256 columns)
-template <typename Tio, int DK, int VS, typename Tg, int NT = kThreads>
+// CONV: the short convolution fused into the prologue (RecArgs conv_*):
+// every thread keeps the last 3 raw inputs of the q/k channels it fetches
+// and of its 4 value columns, and convolves each new token with them
+template <typename Tio, int DK, int VS, typename Tg, int NT = kThreads, bool CONV = false>
 __global__ __launch_bounds__(NT, NT == 512 ? 3 : 1) void k_recurrent(RecArgs a)
 {
     using IO = Io<Tio>;
@@ -87,6 +90,61 @@ __global__ __launch_bounds__(NT, NT == 512 ? 3 : 1) void k_recurrent(RecArgs a)
 
     // key-axis vectors of a token -> registers (cooperative, coalesced)
     constexpr int VPT = (4 * DK + kThreads - 1) / kThreads;
+
+    // fused convolution: taps right-aligned in 4 slots (zero below 4-K) and
+    // the window of the 3 inputs before the next token (from conv_in before
+    // the sequence), per fetched q/k element and per value column
+    const int K = CONV ? a.conv_K : 1;
+    const int64_t Hk = a.Hk;
+    float kw[CONV ? VPT : 1][4], kh[CONV ? VPT : 1][3];
+    f32x4 vw[4], vh[3];
+    auto conv_tap = [&](int64_t c, int m) { return m >= 4 - K ? a.conv_w[c * K + m - (4 - K)] : 0.f; };
+    auto conv_in = [&](int64_t c, int m) {   // input at position m - 3 < 0
+        const int p = m - 3;
+        if (p < -(K - 1) || a.conv_in == nullptr) return 0.f;
+        return IO::to_f(static_cast<const Tio*>(a.conv_in)[(bb * (K - 1) + K - 1 + p) * a.conv_C + c]);
+    };
+    auto qk_chan = [&](int e) {   // conv channel of fetched element e (which 1, 2: k; 3: q)
+        const int which = e / DK, c = e - which * DK;
+        return which == 3 ? hk * DK + c : Hk * DK + hk * DK + c;
+    };
+    const int64_t vchan = 2 * Hk * DK + hh * a.dv + jc;
+    if constexpr (CONV) {
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const int e = tid + u * kThreads;
+            if (e >= DK && e < 4 * DK) {
+                const int64_t c = qk_chan(e);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) kw[u][m] = conv_tap(c, m);
+#pragma unroll
+                for (int m = 0; m < 3; ++m) kh[u][m] = conv_in(c, m);
+            }
+        }
+        if (holder) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vw[m][e] = conv_tap(vchan + e, m);
+#pragma unroll
+            for (int m = 0; m < 3; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vh[m][e] = conv_in(vchan + e, m);
+        }
+    }
+    // one step of the window: the convolution at the new input x (fp32, SiLU
+    // when asked, rounded to the I/O type as a stored convolution output)
+    auto conv1 = [&](float (&h)[3], const float (&w)[4], float x) {
+        float z = w[3] * x;
+#pragma unroll
+        for (int m = 0; m < 3; ++m) z += w[m] * h[m];
+        h[0] = h[1];
+        h[1] = h[2];
+        h[2] = x;
+        if (a.conv_silu) z *= sigmoid_f(z);
+        return IO::to_f(IO::from_f(z));
+    };
+
     auto fetch = [&](int64_t t, float (&st)[VPT]) {
         const int64_t rowk = ((tok0 + t) * a.H + hh) * DK;                    // gates: value head
         const int64_t rowq = ((tok0 + t) * a.Hk + hk) * DK;                   // q, k: its key head
@@ -102,10 +160,17 @@ __global__ __launch_bounds__(NT, NT == 512 ? 3 : 1) void k_recurrent(RecArgs a)
                 } else if (which == 1) {
                     float g = gate_f(gb[rowk + c]);
                     if (logits) g = sigmoid_f(g) * bscale;
-                    x = g * IO::to_f(k[rowq + c]);
+                    if constexpr (CONV) x = g * conv1(kh[u], kw[u], IO::to_f(k[rowq + c]));
+                    else x = g * IO::to_f(k[rowq + c]);
                 }
-                else if (which == 2) x = IO::to_f(k[rowq + c]);
-                else x = IO::to_f(q[rowq + c]);
+                else if (which == 2) {
+                    if constexpr (CONV) x = conv1(kh[u], kw[u], IO::to_f(k[rowq + c]));
+                    else x = IO::to_f(k[rowq + c]);
+                }
+                else {
+                    if constexpr (CONV) x = conv1(kh[u], kw[u], IO::to_f(q[rowq + c]));
+                    else x = IO::to_f(q[rowq + c]);
+                }
             }
             st[u] = x;
         }
@@ -138,7 +203,19 @@ __global__ __launch_bounds__(NT, NT == 512 ? 3 : 1) void k_recurrent(RecArgs a)
         if (holder) {
             f32x4 w4 = ld_gate4(gw + rowv);
             if (logits) w4 = sigmoid4(w4);
-            u = w4 * ld_vec4(v + rowv);
+            if constexpr (CONV) {
+                const f32x4 v4 = ld_vec4(v + rowv);
+                f32x4 z = vw[3] * v4;
+#pragma unroll
+                for (int j = 0; j < 3; ++j) z += vw[j] * vh[j];
+                vh[0] = vh[1];
+                vh[1] = vh[2];
+                vh[2] = v4;
+                if (a.conv_silu) z = z * sigmoid4(z);
+                u = w4 * IO::unpack4(IO::pack4(z));
+            } else {
+                u = w4 * ld_vec4(v + rowv);
+            }
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
                 const int c = rg + NR * i;
@@ -232,6 +309,31 @@ __global__ __launch_bounds__(NT, NT == 512 ? 3 : 1) void k_recurrent(RecArgs a)
 #pragma unroll
         for (int i = 0; i < RPT; ++i)
             __builtin_nontemporal_store(S[i], reinterpret_cast<f32x4*>(a.S_out + (chain * DK + rg + NR * i) * dv + jc));
+    }
+    if constexpr (CONV) {
+        // the window after the last token: the last K-1 inputs; q/k channels
+        // by the first slice of the group's first value head, value columns
+        // by row group 0 (conv_out does not overlap conv_in: other workgroups
+        // may still be reading it)
+        if (a.conv_out != nullptr && K > 1) {
+            Tio* out = static_cast<Tio*>(a.conv_out) + bb * (K - 1) * a.conv_C;
+            if (slice == 0 && hh % (a.H / a.Hk) == 0) {
+#pragma unroll
+                for (int u = 0; u < VPT; ++u) {
+                    const int e = tid + u * kThreads;
+                    if (e >= 2 * DK && e < 4 * DK) {   // the k and q elements
+                        const int64_t c = qk_chan(e);
+                        for (int j = 0; j < K - 1; ++j) out[j * a.conv_C + c] = IO::from_f(kh[u][3 - (K - 1) + j]);
+                    }
+                }
+            }
+            if (holder && rg == 0) {
+                for (int j = 0; j < K - 1; ++j) {
+                    const int m = 3 - (K - 1) + j;
+                    st_vec4(out + j * a.conv_C + vchan, vh[m]);
+                }
+            }
+        }
     }
 }
 
@@ -407,6 +509,14 @@ template <typename Tio, int DK, int VS, typename Tg>
 static hipError_t rec_v(const RecArgs& a, hipStream_t s)
 {
     const int64_t nblk = a.B * a.H * (int64_t)a.nslices;
+    if (a.conv_w != nullptr) {   // fused short convolution (equal-length batches)
+        if (a.cu != nullptr || a.conv_K < 1 || a.conv_K > 4) return hipErrorInvalidValue;
+        if constexpr (VS == 256)
+            hipLaunchKernelGGL((k_recurrent<Tio, DK, VS, Tg, 512, true>), dim3((unsigned)nblk), dim3(512), 0, s, a);
+        else
+            hipLaunchKernelGGL((k_recurrent<Tio, DK, VS, Tg, kThreads, true>), dim3((unsigned)nblk), dim3(kThreads), 0, s, a);
+        return hipGetLastError();
+    }
     if constexpr (VS == 256) {
         // whole rows of 256 columns (the output step over dv = 256): 512 threads
         if (a.T == 1 && a.cu == nullptr)

@@ -90,7 +90,7 @@
 extern "C" {
 #endif
 
-#define GDN2_ABI_VERSION 5
+#define GDN2_ABI_VERSION 6
 
 typedef enum {
     GDN2_OK = 0,
@@ -427,6 +427,62 @@ int gdn2_short_conv_bwd(int64_t B, int64_t T, int64_t C, int32_t K, int32_t flag
                         const void* x, const float* weight, const void* state_in, const void* dy,
                         void* dx, float* dweight, void* dstate_in,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The short convolution fused into the core's prologue (README "Architecture":
+ * the projections pass through the ShortConv, then the L2 norm, into the
+ * recurrence; "Configuration": use_short_conv).  The two calls below compute
+ * exactly what gdn2_short_conv on the concatenated projection followed by
+ * gdn2_chunk_fwd / gdn2_recurrent_step on its three parts computes, in one
+ * pass that writes no convolved tensor:
+ *
+ *   x = [q | k | v] per token, C = 2 H dk + Hv dv channels: query/key head h
+ *       channel c of q is h dk + c, of k is H dk + h dk + c; value head h
+ *       column j of v is 2 H dk + h dv + j;
+ *   (q', k', v') = gdn2_short_conv(x, weight, state_in, flags), each rounded
+ *       to io_dtype as that call stores it;
+ *   o, S_out as the core computes them from q', k', v' and the gates.
+ *
+ * weight [C, K] fp32 and the windows [B, K-1, C] (io_dtype) have the layout
+ * gdn2_short_conv takes for the concatenated projection, so a caller can move
+ * between the two forms.  1 <= K <= 4; flags 0 or GDN2_CONV_SILU; with K == 1
+ * the window pointers are ignored.  state_in NULL = zeros; state_out NULL =
+ * not written.  Equal-length batches only (no packed-batch form).  Everything
+ * else (sizes, dtypes, flags of the problem, alignment, errors, streams) is as
+ * for the unfused calls; weight and the windows count as inputs and outputs
+ * for the aliasing rule.
+ */
+typedef struct {
+    const float* weight;     /* [C, K] fp32                                    */
+    const void* state_in;    /* [B, K-1, C] io_dtype, or NULL (zeros)           */
+    void* state_out;         /* [B, K-1, C] io_dtype, or NULL (not written)     */
+    int32_t K;               /* taps, 1..4                                       */
+    int32_t flags;           /* 0 or GDN2_CONV_SILU                              */
+} gdn2_conv;
+
+/*
+ * gdn2_chunk_fwd with the fused convolution.  Same workspace
+ * (gdn2_chunk_fwd_workspace_size) and two launches; state_out may equal
+ * state_in exactly (the window is written by the second launch, after the
+ * first has read every input it needs).
+ */
+int gdn2_chunk_fwd_conv(const gdn2_problem* p, const gdn2_conv* conv,
+                        const void* q, const void* k, const void* v,
+                        const void* alpha, const void* b, const void* w,
+                        const float* S0, void* o, float* S_out,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gdn2_recurrent_step with the fused convolution (T == 1: the decode step
+ * with its convolution window).  One launch.  state_out must not overlap
+ * state_in (GDN2_ERR_ALIAS): the workgroups of one sequence read the window
+ * while the first of them writes the next one, so a serving loop alternates
+ * two window buffers.
+ */
+int gdn2_recurrent_step_conv(const gdn2_problem* p, const gdn2_conv* conv,
+                             const void* q, const void* k, const void* v,
+                             const void* alpha, const void* b, const void* w,
+                             const float* S_in, void* o, float* S_out, void* stream);
 
 #ifdef __cplusplus
 }

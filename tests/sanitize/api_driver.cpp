@@ -173,6 +173,51 @@ void recurrent_cases()
            gdn2_gated_rmsnorm(&p, t.o, t.g, t.norm_w, static_cast<char*>(t.o) + 16, nullptr), GDN2_ERR_ALIAS);
 }
 
+void fused_conv_cases()
+{
+    for (int K : {1, 4}) {
+        Tensors t = make(2, 100, 2, 4, 64, 32, GDN2_BF16, GDN2_F32, GDN2_FLAG_QK_L2NORM);
+        const gdn2_problem& p = t.p;
+        const int64_t C = 2 * 2 * 64 + 4 * 32;
+        float* wt = static_cast<float*>(stub::dev_alloc(C * K * 4));
+        void* sin = stub::dev_alloc(2 * 3 * C * 2);
+        void* sout = stub::dev_alloc(2 * 3 * C * 2);
+        gdn2_conv c{wt, sin, sout, K, GDN2_CONV_SILU};
+        auto cf = [&](const gdn2_conv* cc, void* o) {
+            return gdn2_chunk_fwd_conv(&p, cc, t.q, t.k, t.v, t.alpha, t.b, t.w, t.S0, o, t.S_out, t.ws, t.ws_bytes,
+                                       nullptr);
+        };
+        auto rf = [&](const gdn2_conv* cc) {
+            return gdn2_recurrent_step_conv(&p, cc, t.q, t.k, t.v, t.alpha, t.b, t.w, t.S0, t.o, t.S_out, nullptr);
+        };
+        expect("chunk conv valid", cf(&c, t.o), GDN2_OK, 2, 2);
+        expect("recurrent conv valid", rf(&c), GDN2_OK, 1, 1);
+        gdn2_conv inplace = c;
+        inplace.state_out = sin;
+        expect("chunk conv window in place", cf(&inplace, t.o), GDN2_OK, 2, 2);
+        expect("recurrent conv window in place", rf(&inplace), K > 1 ? GDN2_ERR_ALIAS : GDN2_OK, 1, 1);
+        expect("chunk conv null descriptor", cf(nullptr, t.o), GDN2_ERR_NULL);
+        gdn2_conv bad = c;
+        bad.weight = nullptr;
+        expect("chunk conv null weight", cf(&bad, t.o), GDN2_ERR_NULL);
+        bad = c;
+        bad.K = 5;
+        expect("conv K 5", rf(&bad), GDN2_ERR_SHAPE);
+        bad = c;
+        bad.flags = 2;
+        expect("conv flag 2", cf(&bad, t.o), GDN2_ERR_SHAPE);
+        bad = c;
+        bad.state_out = t.q;
+        if (K > 1) expect("conv window over q", cf(&bad, t.o), GDN2_ERR_ALIAS);
+        expect("chunk conv o over weight", cf(&c, wt), GDN2_ERR_ALIAS);
+        // no tokens: the window and the state are only carried over
+        gdn2_problem e = p;
+        e.T = 0;
+        expect("chunk conv T 0", gdn2_chunk_fwd_conv(&e, &c, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, t.S0,
+                                                     nullptr, t.S_out, nullptr, 0, nullptr), GDN2_OK, 1, 1);
+    }
+}
+
 void varlen_cases()
 {
     // four packed sequences, 300 tokens in all
@@ -312,6 +357,7 @@ int main()
     chunk_forward_cases();
     recurrent_cases();
     varlen_cases();
+    fused_conv_cases();
     backward_cases();
     conv_cases();
     query_cases();

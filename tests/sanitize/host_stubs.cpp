@@ -101,6 +101,11 @@ hipError_t launch_chunk_prep(const PrepArgs& a, int, bool, bool, hipStream_t)
     for (const void* p : {a.q, a.k, a.v, a.alpha, a.b, a.w}) in_buf(h, "input", p, 0, true);
     in_buf(h, "workspace blocks", a.ws, prep_blocks(a) * a.ws_block, true);
     in_buf(h, "plan", a.plan, 0);
+    if (a.conv_w != nullptr) {
+        if (a.conv_K < 1 || a.conv_K > 4 || a.plan != nullptr) fail(h, "conv taps / packed batch");
+        in_buf(h, "conv weight", a.conv_w, a.conv_C * a.conv_K * 4, true);
+        in_buf(h, "conv window", a.conv_in, a.B * (a.conv_K - 1) * a.conv_C * 2);
+    }
     return hipSuccess;
 }
 
@@ -118,6 +123,11 @@ hipError_t launch_chunk_state(const StateArgs& a, int dk, int vs, bool, hipStrea
     in_buf(h, "S_chk", a.S_chk, a.B * a.H * a.nt * dk * a.dv * 4);
     in_buf(h, "S_chkT", a.S_chkT, 0);
     in_buf(h, "S_chkIo", a.S_chkIo, 0);
+    if (a.conv_out != nullptr) {
+        for (const void* p : {a.cq, a.ck, a.cv}) in_buf(h, "conv input", p, 0, a.T > 0);   // read only at positions >= 0
+        in_buf(h, "conv window in", a.conv_in, a.B * (a.conv_K - 1) * a.conv_C * 2);
+        in_buf(h, "conv window out", a.conv_out, a.B * (a.conv_K - 1) * a.conv_C * 2, true);
+    }
     return hipSuccess;
 }
 
@@ -134,6 +144,11 @@ hipError_t launch_recurrent(const RecArgs& a, int dk, int vs, bool, bool, hipStr
     in_buf(h, "cu", a.cu, 4 * (a.B + 1));
     in_buf(h, "norm_g", a.norm_g, 0);
     in_buf(h, "norm_w", a.norm_w, 4 * a.dv);
+    if (a.conv_w != nullptr) {
+        in_buf(h, "conv weight", a.conv_w, a.conv_C * a.conv_K * 4, true);
+        in_buf(h, "conv window in", a.conv_in, a.B * (a.conv_K - 1) * a.conv_C * 2);
+        in_buf(h, "conv window out", a.conv_out, a.B * (a.conv_K - 1) * a.conv_C * 2);
+    }
     return hipSuccess;
 }
 
