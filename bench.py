@@ -211,7 +211,7 @@ def main(argv=None):
     args = parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
               "every (batch, head) chain is independent, so more GPUs would each run their own share "
               "without communication -- see the sharding notes in the design document.", file=sys.stderr)
         return 2

@@ -114,31 +114,27 @@ __device__ inline int unpack2(unsigned p, int i) { return (int)((p >> (2 * i)) &
 // TOUT: the backward's layout of the block (bf16, KPAD = DK): Qh^T and P^T in
 // place of Qh and P, and T, Ktil, W^T and Eh appended from a.t_off on (BwdExt)
 // ---- fused short convolution ---------------------------------------------
-// Taps of 4 consecutive channels c..c+3 (weight [C][K] fp32), right-aligned
-// in 4 slots: w[m][e] = weight[c+e][m-(4-K)] for m >= 4-K, else 0, so that
-// z[t] = sum_m w[m] * x[t-3+m] for any K in 1..4.
-__device__ inline void conv_taps(const PrepArgs& a, int64_t c, f32x4 (&w)[4])
-{
-    const int K = a.conv_K;
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[m][e] = m >= 4 - K ? a.conv_w[(c + e) * K + m - (4 - K)] : 0.f;
-}
-// the 4 inputs x[p, c..c+3] at position p of sequence seq: from the tensor
-// row `row` when p >= 0, from the carried window conv_in (rows p + K - 1)
-// for -(K-1) <= p < 0 (zeros when it is null), zeros before that (their taps
-// are zero)
+// Its loads are issued with the other input loads, unconditionally (taps:
+// conv_taps4_load / conv_taps4_pick; window rows: conv_hist_src, clamped
+// addresses, values dropped afterwards with keep_or_zero).
+// Source of the 4 inputs x[p, c..c+3] at position p of sequence seq: the
+// tensor row `row` when p >= 0, the carried window conv_in (row p + K - 1)
+// for -(K-1) <= p < 0 when it is given; else `safe` (any readable row of the
+// tensor), whose value conv_hist_keep then drops (zeros: no window, or
+// positions whose taps are zero).
 template <typename Tio>
-__device__ inline typename Io<Tio>::vec4 conv_hist(const PrepArgs& a, const Tio* row, int64_t p, int64_t seq, int64_t c)
+__device__ inline const Tio* conv_hist_src(const PrepArgs& a, const Tio* row, const Tio* safe, int64_t p, int64_t seq,
+                                           int64_t c)
 {
-    using IO = Io<Tio>;
     const int K = a.conv_K;
-    if (p >= 0) return *reinterpret_cast<const typename IO::vec4*>(row);
-    if (p >= -(K - 1) && a.conv_in != nullptr)
-        return *reinterpret_cast<const typename IO::vec4*>(static_cast<const Tio*>(a.conv_in) +
-                                                            (seq * (K - 1) + K - 1 + p) * a.conv_C + c);
-    return IO::pack4(f32x4{0.f, 0.f, 0.f, 0.f});
+    const bool win = p < 0 && p >= -(K - 1) && a.conv_in != nullptr;
+    return p >= 0 ? row
+         : win    ? static_cast<const Tio*>(a.conv_in) + (seq * (K - 1) + K - 1 + p) * a.conv_C + c
+                  : safe;
+}
+__device__ inline bool conv_hist_keep(const PrepArgs& a, int64_t p)
+{
+    return p >= 0 || (p >= -(a.conv_K - 1) && a.conv_in != nullptr);
 }
 // x[0..7] <- conv(x) over the window (h[0..2], x[0..7]) with the taps w, in
 // fp32, (optionally) through SiLU, rounded to the I/O type as a stored
@@ -255,6 +251,25 @@ void k_chunk_prep(PrepArgs a)
     const Tg* gb = static_cast<const Tg*>(a.b);
     gvec alr[8], btr[8];
     typename IO::vec4 kk[8], qq[8];
+    // (CONV) the 3 inputs before the thread's 8 tokens (before the sequence:
+    // the carried window) and its channels' raw taps, requested first
+    typename IO::vec4 hq[CONV ? 3 : 1], hk3[CONV ? 3 : 1];
+    f32x4 tq[CONV ? 4 : 1], tk[CONV ? 4 : 1];
+    if constexpr (CONV) {
+        const int64_t ccq = (hh / (H / Hk)) * DK + c0, cck = Hk * DK + ccq;
+        conv_taps4_load(a.conv_w, ccq, a.conv_K, tq);
+        conv_taps4_load(a.conv_w, cck, a.conv_K, tk);
+#pragma unroll
+        for (int m = 0; m < 3; ++m) {
+            // r < 0 reads the previous chunk's rows (t0 + r >= 0) or the window;
+            // before the sequence the row index is clamped to the chunk's first row
+            const int r = 8 * rg - 3 + m;
+            const int rr = r < L ? (t0 + r >= 0 ? r : 0) : L - 1;
+            const int64_t rowq = (row0k + (int64_t)rr * Hk) * DK + c0, safe = row0k * DK + c0;
+            hq[m] = *reinterpret_cast<const typename IO::vec4*>(conv_hist_src<Tio>(a, q + rowq, q + safe, t0 + r, seq, ccq));
+            hk3[m] = *reinterpret_cast<const typename IO::vec4*>(conv_hist_src<Tio>(a, k + rowq, k + safe, t0 + r, seq, cck));
+        }
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int r = 8 * rg + i;
@@ -266,19 +281,15 @@ void k_chunk_prep(PrepArgs a)
         qq[i] = __builtin_nontemporal_load(reinterpret_cast<const typename IO::vec4*>(q + offk));
     }
     if constexpr (CONV) {
-        // the short convolution of q and k over the thread's 8 tokens, from the
-        // 3 inputs before them (before the sequence: the carried window)
-        const int64_t cq = (hh / (H / Hk)) * DK + c0, ck = Hk * DK + cq;
-        typename IO::vec4 hq[3], hk3[3];
+        // the short convolution of q and k over the thread's 8 tokens
         f32x4 wq[4], wk[4];
-        conv_taps(a, cq, wq);
-        conv_taps(a, ck, wk);
+        conv_taps4_pick(a.conv_K, tq, wq);
+        conv_taps4_pick(a.conv_K, tk, wk);
 #pragma unroll
         for (int m = 0; m < 3; ++m) {
-            const int r = 8 * rg - 3 + m;
-            const int rr = r < L ? r : L - 1;
-            hq[m] = conv_hist<Tio>(a, q + (row0k + (int64_t)rr * Hk) * DK + c0, t0 + r, seq, cq);
-            hk3[m] = conv_hist<Tio>(a, k + (row0k + (int64_t)rr * Hk) * DK + c0, t0 + r, seq, ck);
+            const bool keep = conv_hist_keep(a, t0 + 8 * rg - 3 + m);
+            hq[m] = keep_or_zero(hq[m], keep);
+            hk3[m] = keep_or_zero(hk3[m], keep);
         }
         conv8<Tio>(qq, hq, wq, a.conv_silu);
         conv8<Tio>(kk, hk3, wk, a.conv_silu);
@@ -458,29 +469,30 @@ void k_chunk_prep(PrepArgs a)
     gvec wr[NIT][8];
     typename IO::vec4 vr[NIT][8];
     typename IO::vec4 vh[CONV ? NIT : 1][3];      // (CONV) the 3 inputs before the item's tokens
-    f32x4 wv[CONV ? NIT : 1][4];                  // (CONV) its columns' taps
+    f32x4 wv[CONV ? NIT : 1][4];                  // (CONV) its columns' raw taps, then picked
     const Tg* gw = static_cast<const Tg*>(a.w);
     const int nvq = a.dv / 4;
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
         const int q = tid + it * kThreads;
         const int jq = q % nvq, sg = (q / nvq) & 7;
+        if constexpr (CONV) {
+            conv_taps4_load(a.conv_w, 2 * Hk * DK + hh * a.dv + 4 * jq, a.conv_K, wv[it]);
+#pragma unroll
+            for (int m = 0; m < 3; ++m) {
+                const int r = 8 * sg - 3 + m;
+                const int rr = r < L ? (t0 + r >= 0 ? r : 0) : L - 1;
+                vh[it][m] = *reinterpret_cast<const typename IO::vec4*>(conv_hist_src<Tio>(
+                    a, v + (row0 + (int64_t)rr * H) * a.dv + 4 * jq, v + row0 * a.dv + 4 * jq, t0 + r, seq,
+                    2 * Hk * DK + hh * a.dv + 4 * jq));
+            }
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int s = 8 * sg + i;
             const int64_t off = (row0 + (s < L ? s : L - 1) * H) * a.dv + 4 * jq;
             wr[it][i] = __builtin_nontemporal_load(reinterpret_cast<const gvec*>(gw + off));
             vr[it][i] = __builtin_nontemporal_load(reinterpret_cast<const typename IO::vec4*>(v + off));
-        }
-        if constexpr (CONV) {
-            const int64_t cv = 2 * Hk * DK + hh * a.dv + 4 * jq;
-            conv_taps(a, cv, wv[it]);
-#pragma unroll
-            for (int m = 0; m < 3; ++m) {
-                const int r = 8 * sg - 3 + m;
-                const int rr = r < L ? r : L - 1;
-                vh[it][m] = conv_hist<Tio>(a, v + (row0 + (int64_t)rr * H) * a.dv + 4 * jq, t0 + r, seq, cv);
-            }
         }
     }
     __syncthreads();
@@ -663,7 +675,14 @@ void k_chunk_prep(PrepArgs a)
     frag uf[NIT][4][8 / EPL];      // per item and column: the 8 tokens as fragments
     if constexpr (CONV) {
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) conv8<Tio>(vr[it], vh[it], wv[it], a.conv_silu);
+        for (int it = 0; it < NIT; ++it) {
+            const int sg = ((tid + it * kThreads) / nvq) & 7;
+            f32x4 wp[4];
+            conv_taps4_pick(a.conv_K, wv[it], wp);
+#pragma unroll
+            for (int m = 0; m < 3; ++m) vh[it][m] = keep_or_zero(vh[it][m], conv_hist_keep(a, t0 + 8 * sg - 3 + m));
+            conv8<Tio>(vr[it], vh[it], wp, a.conv_silu);
+        }
     }
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {

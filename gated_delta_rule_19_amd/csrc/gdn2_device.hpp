@@ -177,4 +177,69 @@ __device__ inline f32x4 sigmoid4(f32x4 x)
     return f32x4{sigmoid_f(x[0]), sigmoid_f(x[1]), sigmoid_f(x[2]), sigmoid_f(x[3])};
 }
 
+// ---- short convolution taps (weight [C][K] fp32, 1 <= K <= 4) -------------
+// Taps are right-aligned in 4 slots, w[m] = weight[c][m - (4 - K)] for
+// m >= 4 - K and 0 below, so that z[t] = sum_m w[m] x[t - 3 + m] for any K.
+// Every load is unconditional (indices clamped into the row) and the slots
+// are chosen afterwards with bit masks: a load under a branch, or a value
+// picked by one, would drain the vector-memory counter together with every
+// other load in flight.
+// The 4K weights of 4 consecutive channels c..c+3 (c % 4 == 0) are contiguous
+// and 16-byte aligned: K vector loads, then conv_taps4_pick.
+__device__ inline void conv_taps4_load(const float* weight, int64_t c, int K, f32x4 (&f)[4])
+{
+    const f32x4* src = reinterpret_cast<const f32x4*>(weight + c * K);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f[j] = src[j < K ? j : K - 1];
+}
+__device__ inline void conv_taps4_pick(int K, const f32x4 (&f)[4], f32x4 (&w)[4])
+{
+    const unsigned m4 = 0u - (unsigned)(K == 4), m3 = 0u - (unsigned)(K == 3);
+    const unsigned m2 = 0u - (unsigned)(K == 2), m1 = 0u - (unsigned)(K == 1);
+    auto at = [&](int i) { return __float_as_uint(f[i / 4][i % 4]); };   // weight[c + i / K][i % K]
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            unsigned u = at(4 * e + m) & m4;
+            if (m >= 1) u |= at(3 * e + m - 1) & m3;
+            if (m >= 2) u |= at(2 * e + m - 2) & m2;
+            if (m == 3) u |= at(e) & m1;
+            w[m][e] = __uint_as_float(u);
+        }
+}
+// the taps of one channel c
+__device__ inline void conv_taps1(const float* weight, int64_t c, int K, float (&w)[4])
+{
+    float f[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f[j] = weight[c * K + (j < K ? j : K - 1)];
+    const unsigned m4 = 0u - (unsigned)(K == 4), m3 = 0u - (unsigned)(K == 3);
+    const unsigned m2 = 0u - (unsigned)(K == 2), m1 = 0u - (unsigned)(K == 1);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        unsigned u = __float_as_uint(f[m]) & m4;
+        if (m >= 1) u |= __float_as_uint(f[m - 1]) & m3;
+        if (m >= 2) u |= __float_as_uint(f[m - 2]) & m2;
+        if (m == 3) u |= __float_as_uint(f[0]) & m1;
+        w[m] = __uint_as_float(u);
+    }
+}
+// x where keep holds, else all-zero bits (no branch)
+template <typename V>
+__device__ inline V keep_or_zero(V x, bool keep)
+{
+    static_assert(sizeof(V) % 4 == 0, "whole 32-bit words");
+    const unsigned mk = 0u - (unsigned)keep;
+    V r;
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(V) / 4); ++i)
+        reinterpret_cast<unsigned*>(&r)[i] = reinterpret_cast<const unsigned*>(&x)[i] & mk;
+    return r;
+}
+__device__ inline float keep_or_zero(float x, bool keep)
+{
+    return __uint_as_float(__float_as_uint(x) & (0u - (unsigned)keep));
+}
+
 }  // namespace gdn2

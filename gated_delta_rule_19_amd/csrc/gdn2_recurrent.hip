@@ -348,8 +348,17 @@ __global__ __launch_bounds__(NT, NT == 512 ? 3 : 1) void k_recurrent(RecArgs a)
 // vectors and w, v are requested before the state (so waiting for them never
 // waits for the state), and k is read back from LDS for the update instead
 // of being held per row, which keeps few registers beside the state.
+// CONV: the short convolution fused into the prologue (RecArgs conv_*).  The
+// workgroup convolves the token once: thread t takes channel t % dk of
+// (alpha, k) or (b, q) and column t of the slice, requests their taps and
+// window rows with the vectors (unconditionally: clamped addresses, values
+// dropped by mask) and writes the results to one copy in LDS shared by the
+// waves -- one workgroup barrier, after the state is requested.  The window
+// after the token (the last K - 1 inputs) is written by the first slice of
+// each key head's first value head (q/k channels) and by every slice (its
+// columns).
 // ---------------------------------------------------------------------------
-template <typename Tio, int DK, int VS, typename Tg, int NT, int MINW>
+template <typename Tio, int DK, int VS, typename Tg, int NT, int MINW, bool CONV = false>
 __global__ __launch_bounds__(NT, MINW) void k_decode(RecArgs a)
 {
     using IO = Io<Tio>;
@@ -361,7 +370,8 @@ __global__ __launch_bounds__(NT, MINW) void k_decode(RecArgs a)
     static_assert(VS % NW == 0 && WC % 4 == 0 && 64 % NJ == 0 && NR <= DK && DK % NR == 0, "thread layout");
     constexpr int VPL = 4 * DK / 64;                    // vector elements a lane loads
 
-    __shared__ __attribute__((aligned(16))) float vec[NW][4][DK];   // per wave: alpha, b, k, q
+    __shared__ __attribute__((aligned(16))) float vec[CONV ? 1 : NW][4][DK];   // per wave (CONV: shared): alpha, b, k, q
+    __shared__ __attribute__((aligned(16))) float vconv[CONV ? VS : 1];       // (CONV) the convolved values
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int jg = lane % NJ, rg = lane / NJ;
@@ -379,13 +389,13 @@ __global__ __launch_bounds__(NT, MINW) void k_decode(RecArgs a)
     const Tg* gw = static_cast<const Tg*>(a.w);
     const Tio* q = static_cast<const Tio*>(a.q);
     const Tio* k = static_cast<const Tio*>(a.k);
-    float* vw = &vec[wave][0][0];
+    float* vw = &vec[CONV ? 0 : wave][0][0];
 
     // 1. the token's key-axis vectors (this wave's copy) and the thread's w, v, before the state
     const int64_t rowk = (bb * a.H + hh) * DK, rowq = (bb * a.Hk + hk) * DK;
-    float kv[VPL];
+    float kv[CONV ? 1 : VPL];
 #pragma unroll
-    for (int u = 0; u < VPL; ++u) {
+    for (int u = 0; u < (CONV ? 0 : VPL); ++u) {
         const int e = lane + 64 * u;
         const int which = e / DK, c = e - which * DK;   // which is uniform per u when DK >= 64
         float x;
@@ -398,6 +408,36 @@ __global__ __launch_bounds__(NT, MINW) void k_decode(RecArgs a)
     const int64_t rowv = (bb * a.H + hh) * dv + jc;
     const auto wraw = *reinterpret_cast<const typename GateVec<Tg>::type*>(gw + rowv);
     const auto vraw = *reinterpret_cast<const typename IO::vec4*>(static_cast<const Tio*>(a.v) + rowv);
+    // (CONV) thread t: channel c of pair P (0: alpha and k, 1: b and q) and
+    // column ct of the slice; window row K-4+m holds the input at position
+    // m - 3 (kept when that row exists and a window is given)
+    const int K = CONV ? a.conv_K : 1;
+    const Tio* cin = static_cast<const Tio*>(a.conv_in);
+    const int t2 = tid < 2 * DK ? tid : 2 * DK - 1;
+    const int P = __builtin_amdgcn_readfirstlane(t2 / DK), c = t2 - P * DK;   // P: wave-uniform (dk % 64 == 0)
+    const int ct = tid < VS ? tid : VS - 1;
+    const int64_t cch = P == 0 ? (a.Hk + hk) * DK + c : hk * DK + c;   // channel of k / q
+    const int64_t vch = 2 * a.Hk * DK + hh * dv + slice * VS + ct;     // channel of the column
+    float cg = 0.f, cx = 0.f, cv = 0.f, ctap[4], vtap[4], chis[3], vhis[3];
+    bool keep[3];
+    if constexpr (CONV) {
+        static_assert(NT >= 2 * DK && NT >= VS, "one q/k element and one column per thread");
+        cg = gate_f((P == 0 ? galpha : gb)[rowk + c]);
+        cx = IO::to_f((P == 0 ? k : q)[rowq + c]);
+        cv = IO::to_f(static_cast<const Tio*>(a.v)[(bb * a.H + hh) * dv + slice * VS + ct]);
+        conv_taps1(a.conv_w, cch, K, ctap);
+        conv_taps1(a.conv_w, vch, K, vtap);
+        // dropped values are read from the weights (readable, and no value
+        // the compiler already holds)
+        const Tio* safe = reinterpret_cast<const Tio*>(a.conv_w);
+#pragma unroll
+        for (int m = 0; m < 3; ++m) {
+            keep[m] = K - 4 + m >= 0 && cin != nullptr;
+            const int64_t wrow = (bb * (K - 1) + K - 4 + m) * a.conv_C;
+            chis[m] = IO::to_f(*(keep[m] ? cin + wrow + cch : safe + cch));
+            vhis[m] = IO::to_f(*(keep[m] ? cin + wrow + vch : safe + vch));
+        }
+    }
     // 2. the state
     f32x4 S[RPT];
 #pragma unroll
@@ -407,16 +447,44 @@ __global__ __launch_bounds__(NT, MINW) void k_decode(RecArgs a)
             S[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.S_in + (chain * DK + rg + NR * i) * dv + jc));
     }
     // 3. the vectors into this wave's LDS rows (read back by the same wave: no barrier)
+    if constexpr (CONV) {
+        // the convolution (fp32, SiLU when asked, rounded to the I/O type as
+        // a stored convolution output would be) into the shared copy
 #pragma unroll
-    for (int u = 0; u < VPL; ++u) {
-        const int e = lane + 64 * u;
-        const int which = e / DK;
-        float x = kv[u];
-        if (logits && which == 0) x = sigmoid_f(x);
-        if (logits && which == 1) x = sigmoid_f(x) * bscale;
-        vw[e] = x;
+        for (int m = 0; m < 3; ++m) {
+            chis[m] = keep_or_zero(chis[m], keep[m]);
+            vhis[m] = keep_or_zero(vhis[m], keep[m]);
+        }
+        float zq = ctap[3] * cx, zv = vtap[3] * cv;
+#pragma unroll
+        for (int m = 0; m < 3; ++m) {
+            zq += ctap[m] * chis[m];
+            zv += vtap[m] * vhis[m];
+        }
+        if (a.conv_silu) {
+            zq *= sigmoid_f(zq);
+            zv *= sigmoid_f(zv);
+        }
+        float g = cg;
+        if (logits) g = P == 0 ? sigmoid_f(g) : sigmoid_f(g) * bscale;
+        if (tid < 2 * DK) {
+            vw[P * DK + c] = g;
+            vw[(2 + P) * DK + c] = IO::to_f(IO::from_f(zq));
+        }
+        if (tid < VS) vconv[tid] = IO::to_f(IO::from_f(zv));
+        __syncthreads();
+    } else {
+#pragma unroll
+        for (int u = 0; u < VPL; ++u) {
+            const int e = lane + 64 * u;
+            const int which = e / DK;
+            float x = kv[u];
+            if (logits && which == 0) x = sigmoid_f(x);
+            if (logits && which == 1) x = sigmoid_f(x) * bscale;
+            vw[e] = x;
+        }
+        __builtin_amdgcn_wave_barrier();
     }
-    __builtin_amdgcn_wave_barrier();
     // 4. decay and the reductions over the key axis (row groups of the wave)
     f32x4 r = {0.f, 0.f, 0.f, 0.f}, m = r;
     float qk = 0.f, k2 = 0.f, q2 = 0.f;
@@ -455,7 +523,10 @@ __global__ __launch_bounds__(NT, MINW) void k_decode(RecArgs a)
     }
     f32x4 w4 = widen4(wraw);
     if (logits) w4 = sigmoid4(w4);
-    const f32x4 delta = w4 * IO::unpack4(vraw) - r;
+    f32x4 v4;
+    if constexpr (CONV) v4 = *reinterpret_cast<const f32x4*>(&vconv[wave * WC + 4 * jg]);
+    else v4 = IO::unpack4(vraw);
+    const f32x4 delta = w4 * v4 - r;
     // 5. the state update, streamed out
     const f32x4 kd = rk * delta;
 #pragma unroll
@@ -490,6 +561,19 @@ __global__ __launch_bounds__(NT, MINW) void k_decode(RecArgs a)
             st_vec4(o + rowv, y);
         }
     }
+    if constexpr (CONV) {
+        // 7. the window after the token: row j < K-1 holds the input at
+        // position j - (K-2), slot 4-(K-1)+j of (h0, h1, h2, x)
+        if (a.conv_out != nullptr && K > 1) {
+            Tio* out = static_cast<Tio*>(a.conv_out) + bb * (K - 1) * a.conv_C;
+            const bool qk = tid < 2 * DK && slice == 0 && hh % (a.H / a.Hk) == 0;
+            for (int j = 0; j < K - 1; ++j) {
+                const int sl = 4 - (K - 1) + j;   // 1..3
+                if (qk) out[j * a.conv_C + cch] = IO::from_f(sl == 1 ? chis[1] : (sl == 2 ? chis[2] : cx));
+                if (tid < VS) out[j * a.conv_C + vch] = IO::from_f(sl == 1 ? vhis[1] : (sl == 2 ? vhis[2] : cv));
+            }
+        }
+    }
 }
 
 int recurrent_slice(int64_t nchains, int64_t T, int dv)
@@ -511,6 +595,18 @@ static hipError_t rec_v(const RecArgs& a, hipStream_t s)
     const int64_t nblk = a.B * a.H * (int64_t)a.nslices;
     if (a.conv_w != nullptr) {   // fused short convolution (equal-length batches)
         if (a.cu != nullptr || a.conv_K < 1 || a.conv_K > 4) return hipErrorInvalidValue;
+        // the decode step: k_decode where its layout fits (dk >= 64)
+        constexpr bool dec = DK >= 64 && (VS == 256 || (VS % 16 == 0 && VS >= 16 && (64 / (VS / 16)) <= DK));
+        if constexpr (dec) {
+            if (a.T == 1) {
+                if constexpr (VS == 256)
+                    hipLaunchKernelGGL((k_decode<Tio, DK, VS, Tg, 256, 2, true>), dim3((unsigned)nblk), dim3(256), 0, s, a);
+                else
+                    hipLaunchKernelGGL((k_decode<Tio, DK, VS, Tg, kThreads, (DK * VS >= 128 * 128 ? 4 : 8), true>),
+                                       dim3((unsigned)nblk), dim3(kThreads), 0, s, a);
+                return hipGetLastError();
+            }
+        }
         if constexpr (VS == 256)
             hipLaunchKernelGGL((k_recurrent<Tio, DK, VS, Tg, 512, true>), dim3((unsigned)nblk), dim3(512), 0, s, a);
         else

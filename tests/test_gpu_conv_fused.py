@@ -167,6 +167,41 @@ def test_fused_conv_decode_steps_with_alternating_windows(dev):
     check("decode x5 with conv window", io, torch.cat(outs, 1), S, bufs[T % 2], ro, rS, rwin)
 
 
+DECODE_CASES = [
+    # B, H, Hv, dk, dv, io, gate, flags, K, silu, carried window, initial state
+    (4, 2, 2, 64, 64, F32, F32, L2, 4, True, True, True),
+    (3, 2, 4, 128, 256, BF16, BF16, LOG | NEG | L2, 3, False, True, True),
+    (2, 4, 4, 128, 128, BF16, F32, 0, 2, True, False, True),
+    (5, 1, 2, 64, 128, BF16, F32, LOG | L2, 1, False, True, False),
+    (2, 2, 2, 128, 32, F32, F32, L2, 4, True, False, True),
+    (7, 2, 2, 128, 128, BF16, BF16, LOG | L2, 4, True, True, True),
+    (3, 2, 2, 64, 256, F32, F32, NEG | LOG, 3, True, True, False),
+]
+
+
+def _did(c):
+    B, H, Hv, dk, dv, io, gate, flags, K, silu, win, s0 = c
+    return (f"B{B}H{H}Hv{Hv}dk{dk}dv{dv}{'bf16' if io == BF16 else 'f32'}g{'bf16' if gate == BF16 else 'f32'}"
+            f"fl{flags}K{K}{'silu' if silu else ''}{'win' if win else 'nowin'}{'S0' if s0 else 'zero'}")
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=_did)
+def test_fused_conv_decode_step(dev, case):
+    """One token per sequence (the decode kernel's layout, dk >= 64): o, the
+    state and the window after the token against the oracle chain."""
+    B, H, Hv, dk, dv, io, gate, flags, K, silu, win, s0 = case
+    inp, weight, state = make(dev, B, 1, H, Hv, dk, dv, io, gate, flags, K, seed=400 + dk + dv + K, wscale=0.5)
+    if not win:
+        state = None
+    S0 = inp["S0"] if s0 else None
+    out = torch.empty(B, K - 1, weight.shape[0], dtype=io, device=dev) if K > 1 else None
+    o, S, w = run("recurrent", inp, weight, state, silu, flags, S0=S0, state_out=out)
+    torch.cuda.synchronize()
+    ro, rS, rwin = oracle_chain(inp, weight, state, silu, flags,
+                                S0=None if s0 else torch.zeros_like(inp["S0"]))
+    check(f"decode conv {_did(case)}", io, o, S, w, ro, rS, rwin)
+
+
 def test_fused_conv_chunked_window_in_place(dev):
     B, T, H, Hv, dk, dv, io, K = 2, 140, 2, 2, 64, 128, BF16, 3
     inp, weight, state = make(dev, B, T, H, Hv, dk, dv, io, F32, L2, K, seed=13, wscale=0.5)
