@@ -1257,13 +1257,16 @@ __global__ __launch_bounds__(state_threads(VS, (int)sizeof(Tio)), 1) void k_chun
 int chunk_state_slice(int64_t nchains, int dv, int dk, int esize)
 {
     // widest slice that still gives every CU a workgroup and fits in LDS:
-    // wider slices copy each chunk's factors into fewer workgroups
+    // wider slices copy each chunk's factors into fewer workgroups.  When no
+    // width fills the chip (few long chains), the narrowest: a chunk's
+    // latency in the serial loop barely depends on the width, its work does
+    // (B1 H16 T65536 d128: 16 columns 1216 us, 32 columns 1389 us)
     static const int widths[3] = {64, 32, 16};
     for (int i = 0; i < 3; ++i) {
         const int w = widths[i];
         if (dv % w == 0 && nchains * (dv / w) >= 256 && state_lds_bytes(dk, w, esize) > 0) return w;
     }
-    for (int i = 1; i < 3; ++i)
+    for (int i = 2; i >= 1; --i)
         if (dv % widths[i] == 0 && state_lds_bytes(dk, widths[i], esize) > 0) return widths[i];
     return 16;
 }
