@@ -16,7 +16,7 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn2.so")
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 GDN2_F32, GDN2_BF16 = 0, 1
 FLAG_GATE_LOGITS, FLAG_NEG_EIGVAL, FLAG_QK_L2NORM = 1, 2, 4
 CONV_SILU = 1
@@ -112,7 +112,7 @@ def lib():
         L.gdn2_short_conv_bwd_workspace_size.restype = sz
         L.gdn2_short_conv_bwd_workspace_size.argtypes = [i64] * 3 + [i32]
         L.gdn2_short_conv_bwd.restype = ctypes.c_int
-        L.gdn2_short_conv_bwd.argtypes = [i64] * 3 + [i32] * 3 + [vp] * 7 + [vp, sz, vp]
+        L.gdn2_short_conv_bwd.argtypes = [i64] * 3 + [i32] * 3 + [vp] * 8 + [vp, sz, vp]
         L.gdn2_chunk_bwd_varlen_workspace_size.restype = sz
         L.gdn2_chunk_bwd_varlen_workspace_size.argtypes = [P, vp]
         L.gdn2_chunk_bwd_varlen.restype = ctypes.c_int
@@ -558,12 +558,18 @@ def short_conv_bwd_workspace_size(B, T, C, K) -> int:
     return int(lib().gdn2_short_conv_bwd_workspace_size(B, T, C, K))
 
 
-def short_conv_bwd(x, weight, dy, state=None, *, silu: bool = False, want_dstate: bool = True, workspace=None):
-    """Gradient of :func:`short_conv` (``gdn2_short_conv_bwd``) given dy = dL/dy.
+def short_conv_bwd(x, weight, dy, state=None, *, silu: bool = False, want_dstate: bool = True, workspace=None,
+                   dstate_out=None):
+    """Gradient of :func:`short_conv` (``gdn2_short_conv_bwd``) given dy = dL/dy and,
+    optionally, dstate_out = dL/dstate_out [B, K-1, C] (the gradient of the window after
+    the last token, e.g. the next piece's dstate).
     Returns (dx, dweight [C, K] float32, dstate [B, K-1, C] or None)."""
     B, T, C, K, dev, code = _conv_check(x, weight, state)
     if tuple(dy.shape) != (B, T, C) or dy.dtype != x.dtype or dy.device != dev or not dy.is_contiguous():
         raise ValueError("dy must be a contiguous GPU tensor shaped and typed like x")
+    if dstate_out is not None and (tuple(dstate_out.shape) != (B, K - 1, C) or dstate_out.dtype != x.dtype
+                                   or dstate_out.device != dev or not dstate_out.is_contiguous()):
+        raise ValueError("dstate_out must be a contiguous [B, K-1, C] GPU tensor typed like x")
     dx = torch.empty_like(x)
     dw = torch.empty((C, K), dtype=torch.float32, device=dev)
     ds = torch.empty((B, K - 1, C), dtype=x.dtype, device=dev) if want_dstate else None
@@ -571,6 +577,7 @@ def short_conv_bwd(x, weight, dy, state=None, *, silu: bool = False, want_dstate
     if workspace is None:
         workspace = alloc_workspace(need, dev)
     _check(lib().gdn2_short_conv_bwd(B, T, C, K, CONV_SILU if silu else 0, code, _ptr(x), _ptr(weight), _ptr(state),
-                                     _ptr(dy), _ptr(dx), _ptr(dw), _ptr(ds) if K > 1 else None,
+                                     _ptr(dy), _ptr(dstate_out) if K > 1 else None, _ptr(dx), _ptr(dw),
+                                     _ptr(ds) if K > 1 else None,
                                      _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev)))
     return dx, dw, ds

@@ -894,29 +894,33 @@ size_t gdn2_short_conv_bwd_workspace_size(int64_t B, int64_t T, int64_t C, int32
 
 int gdn2_short_conv_bwd(int64_t B, int64_t T, int64_t C, int32_t K, int32_t flags, int32_t io_dtype,
                         const void* x, const float* weight, const void* state_in, const void* dy,
-                        void* dx, float* dweight, void* dstate_in,
+                        const void* dstate_out, void* dx, float* dweight, void* dstate_in,
                         void* workspace, size_t workspace_bytes, void* stream)
 {
     int st = conv_check(B, T, C, K, flags, io_dtype);
     if (st) return st;
-    if (K == 1) state_in = dstate_in = nullptr;
+    if (K == 1) {
+        state_in = dstate_out = nullptr;
+        dstate_in = nullptr;
+    }
     if (!weight || !dweight) return GDN2_ERR_NULL;
     if (B > 0 && T > 0 && (!x || !dy || !dx)) return GDN2_ERR_NULL;
     const size_t need = gdn2_short_conv_bwd_workspace_size(B, T, C, K);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return GDN2_ERR_WORKSPACE;
     const int64_t es = io_dtype == GDN2_BF16 ? 2 : 4;
     const int64_t xb = B * T * C * es, sb = B * (K - 1) * C * es;
-    const Range ins[4] = {range_of(x, xb), range_of(weight, C * K * 4), range_of(state_in, sb), range_of(dy, xb)};
+    const Range ins[5] = {range_of(x, xb), range_of(weight, C * K * 4), range_of(state_in, sb), range_of(dy, xb),
+                          range_of(dstate_out, sb)};
     const Range outs[4] = {range_of(dx, xb), range_of(dweight, C * K * 4), range_of(dstate_in, sb),
                            range_of(workspace, (int64_t)need)};
-    st = check_alias(outs, 4, ins, 4, nullptr, nullptr, -1, -1);
+    st = check_alias(outs, 4, ins, 5, nullptr, nullptr, -1, -1);
     if (st) return st;
-    st = check_align({x, weight, state_in, dy, dx, dweight, dstate_in, workspace});
+    st = check_align({x, weight, state_in, dy, dstate_out, dx, dweight, dstate_in, workspace});
     if (st) return st;
     st = device_ready();
     if (st) return st;
     gdn2::ConvBwdArgs a{x, weight, state_in, dy, dx, dweight, dstate_in, static_cast<float*>(workspace),
-                        B, T, C, conv_spans(T)};
+                        dstate_out, B, T, C, conv_spans(T)};
     return launch_status(gdn2::launch_short_conv_bwd(a, K, (flags & GDN2_CONV_SILU) != 0, io_dtype == GDN2_BF16,
                                                      static_cast<hipStream_t>(stream)));
 }

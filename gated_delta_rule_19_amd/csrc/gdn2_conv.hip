@@ -321,11 +321,15 @@ __global__ __launch_bounds__(kThreads) void k_short_conv_bwd(ConvBwdArgs a)
         }
 #pragma unroll
         for (int t = 0; t < TW; ++t) {
-            if (s0 + l0 + t < T) {
+            const int64_t p = s0 + l0 + t;
+            if (p < T) {
                 f32x4 g = w[K - 1] * dz_at(l0 + t);
 #pragma unroll
                 for (int i = 0; i < K - 1; ++i) g += w[i] * dz_at(l0 + t + K - 1 - i);
-                st_vec4(dx + (s0 + l0 + t) * C, g);
+                // the window after the last token holds positions T-(K-1)..T-1
+                if (K > 1 && a.dstate_out != nullptr && p >= T - (K - 1))
+                    g += ld_vec4(static_cast<const Tio*>(a.dstate_out) + (b * (K - 1) + p - T + K - 1) * C + c0);
+                st_vec4(dx + p * C, g);
             }
         }
         if (K > 1 && s0 + l0 == 0 && a.dstate != nullptr) {
@@ -336,6 +340,10 @@ __global__ __launch_bounds__(kThreads) void k_short_conv_bwd(ConvBwdArgs a)
                 f32x4 g = w[q] * dz_at(0);
 #pragma unroll
                 for (int i = 0; i < q; ++i) g += w[i] * dz_at(q - i);
+                // with T < K-1 the window after the last token still holds
+                // state inputs: position q-(K-1) is its row q - T
+                if (a.dstate_out != nullptr && q >= T)
+                    g += ld_vec4(static_cast<const Tio*>(a.dstate_out) + (b * (K - 1) + q - T) * C + c0);
                 st_vec4(ds + q * C, g);
             }
         }

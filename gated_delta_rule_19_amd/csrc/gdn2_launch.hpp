@@ -162,6 +162,7 @@ struct ConvArgs {
 struct ConvBwdArgs {
     const void* x; const float* weight; const void* state_in; const void* dy;
     void* dx; float* dweight; void* dstate; float* part;
+    const void* dstate_out;   // gradient of the window after the last token (null = zeros)
     int64_t B, T, C;
     int64_t nspan;        // spans a sequence (at least 1)
 };

@@ -90,7 +90,7 @@
 extern "C" {
 #endif
 
-#define GDN2_ABI_VERSION 6
+#define GDN2_ABI_VERSION 7
 
 typedef enum {
     GDN2_OK = 0,
@@ -330,6 +330,10 @@ int gdn2_chunk_bwd(const gdn2_problem* p,
  * not wanted); S0 and dS_T [N, Hv, dk, dv] or NULL (zero).
  * cu_seqlens_host: the N+1 offsets in HOST memory (4-byte aligned), checked
  * on the host: they must rise from 0 to T (GDN2_ERR_SHAPE otherwise).
+ * NOTE: this differs from gdn2_chunk_fwd_varlen, whose cu_seqlens is in
+ * DEVICE memory: pass the backward a host copy of the forward's offsets
+ * (the backward sizes its workspace and launches per sequence from them);
+ * a device pointer here would be read by the host.
  * Sequences are independent, so the call runs the chunked backward on each
  * sequence's contiguous slice in turn, all launches on `stream` (those of
  * gdn2_chunk_bwd, a sequence at a time; an empty sequence only passes dS_T
@@ -414,10 +418,14 @@ size_t gdn2_short_conv_bwd_workspace_size(int64_t B, int64_t T, int64_t C, int32
  *     dxe[b,p,c] = sum_i weight[c,i] * dz[b, p+(K-1)-i, c]  over 0 <= p+(K-1)-i < T
  *     dweight[c,i] = sum_{b,t} dz[b,t,c] * xe[b, t-(K-1)+i, c]
  *
+ * dstate_out [B, K-1, C] (io_dtype; NULL = zeros) is the gradient with
+ * respect to the forward's state_out, the last K-1 positions of xe: it is
+ * added to dxe there, so that a sequence processed in pieces is
+ * differentiated piece by piece, last first, each piece's dstate_in handed
+ * to the piece before it as dstate_out (the pieces' dweight summed).
  * dx = dxe at positions >= 0; dstate_in (NULL = not wanted) = dxe at the K-1
  * positions before the first token, the gradient with respect to state_in
- * (also when state_in is NULL, i.e. zero).  The loss is taken not to depend on
- * state_out.  dx, dstate_in: io_dtype; dweight: fp32 [C, K], summed in a
+ * (also when state_in is NULL, i.e. zero).  dx, dstate_in: io_dtype; dweight: fp32 [C, K], summed in a
  * fixed order (the result does not depend on scheduling).  Outputs and the
  * workspace (16-byte aligned, at least gdn2_short_conv_bwd_workspace_size
  * bytes) must not overlap any input or each other.  Two launches on `stream`
@@ -425,7 +433,7 @@ size_t gdn2_short_conv_bwd_workspace_size(int64_t B, int64_t T, int64_t C, int32
  */
 int gdn2_short_conv_bwd(int64_t B, int64_t T, int64_t C, int32_t K, int32_t flags, int32_t io_dtype,
                         const void* x, const float* weight, const void* state_in, const void* dy,
-                        void* dx, float* dweight, void* dstate_in,
+                        const void* dstate_out, void* dx, float* dweight, void* dstate_in,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*

@@ -205,13 +205,17 @@ def short_conv(x, weight, state=None, silu=False):
     return y, xe[:, T:, :]
 
 
-def short_conv_bwd(x, weight, dy, state=None, silu=False):
-    """Gradients of sum(dy * y), y = short_conv(x, weight, state, silu)[0], fp64.
+def short_conv_bwd(x, weight, dy, state=None, silu=False, dstate_out=None):
+    """Gradients of sum(dy * y) + sum(dstate_out * state_out), where
+    (y, state_out) = short_conv(x, weight, state, silu), fp64.
 
     With z the pre-activation and dz = dy (or dy * d silu/dz = dy * s (1 + z (1 - s)),
     s = sigmoid(z)), every input of the window xe = [state, x] receives
         d xe[p] = sum_i weight[:, i] * dz[p - i]      (dz = 0 outside [0, T)),
     and every tap  d weight[c, i] = sum over b, t of dz[b, t, c] * xe[b, t + i, c].
+    state_out is the last K-1 entries of xe, so dstate_out (None = zeros) is
+    added to d xe there: the gradient a following piece's backward hands back
+    when a sequence is processed in pieces.
     Returns dx [B, T, C], dweight [C, K], dstate [B, K-1, C].
     """
     x, weight, dy = _f64(x), _f64(weight), _f64(dy)
@@ -232,6 +236,8 @@ def short_conv_bwd(x, weight, dy, state=None, silu=False):
     for i in range(K):
         dxe[:, i:i + T, :] += weight[:, i] * dz
         dw[:, i] = np.sum(dz * xe[:, i:i + T, :], axis=(0, 1))
+    if dstate_out is not None:
+        dxe[:, T:, :] += _f64(dstate_out)
     return dxe[:, K - 1:, :], dw, dxe[:, :K - 1, :]
 
 

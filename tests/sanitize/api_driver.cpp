@@ -317,12 +317,20 @@ void conv_cases()
         void* dx = stub::dev_alloc(B * T * C * es);
         float* dwt = static_cast<float*>(stub::dev_alloc(C * 4 * 4));
         void* dsin = stub::dev_alloc(B * 3 * C * es);
+        void* dsout = stub::dev_alloc(B * 3 * C * es);
         const size_t wsb = gdn2_short_conv_bwd_workspace_size(B, T, C, 4);
         void* ws = stub::dev_alloc(wsb);
         auto cb = [&](void* dxx, size_t n) {
-            return gdn2_short_conv_bwd(B, T, C, 4, GDN2_CONV_SILU, io, x, wt, sin, dy, dxx, dwt, dsin, ws, n, nullptr);
+            return gdn2_short_conv_bwd(B, T, C, 4, GDN2_CONV_SILU, io, x, wt, sin, dy, dsout, dxx, dwt, dsin, ws, n,
+                                       nullptr);
         };
         expect("conv bwd valid", cb(dx, wsb), GDN2_OK, 1, 1000);
+        expect("conv bwd no dstate_out",
+               gdn2_short_conv_bwd(B, T, C, 4, 0, io, x, wt, sin, dy, nullptr, dx, dwt, dsin, ws, wsb, nullptr), GDN2_OK,
+               1, 1000);
+        expect("conv bwd dstate over dstate_out",
+               gdn2_short_conv_bwd(B, T, C, 4, 0, io, x, wt, sin, dy, dsout, dx, dwt, dsout, ws, wsb, nullptr),
+               GDN2_ERR_ALIAS);
         expect("conv bwd dx over dy", cb(dy, wsb), GDN2_ERR_ALIAS);
         expect("conv bwd workspace short", cb(dx, wsb - 1), GDN2_ERR_WORKSPACE);
     }

@@ -187,6 +187,7 @@ hipError_t launch_short_conv_bwd(const ConvBwdArgs& a, int K, bool, bool bf16, h
     in_buf(h, "dweight", a.dweight, a.C * K * 4, true);
     in_buf(h, "state_in", a.state_in, a.B * (K - 1) * a.C * es);
     in_buf(h, "dstate", a.dstate, a.B * (K - 1) * a.C * es);
+    in_buf(h, "dstate_out", a.dstate_out, a.B * (K - 1) * a.C * es);
     in_buf(h, "partials", a.part, a.B * a.nspan * a.C * K * 4, true);
     return hipSuccess;
 }

@@ -24,6 +24,7 @@ class Conv:
         sizes = {"x": B * T * C * es, "weight": C * K * 4, "state": B * (K - 1) * C * es,
                  "y": B * T * C * es, "state_out": B * (K - 1) * C * es, "dy": B * T * C * es,
                  "dx": B * T * C * es, "dweight": C * K * 4, "dstate": B * (K - 1) * C * es,
+                 "dstate_out": B * (K - 1) * C * es,
                  "ws": max(g.lib().gdn2_short_conv_bwd_workspace_size(B, T, C, K), 1)}
         self.ptr, at = {}, BASE
         for name, n in sizes.items():
@@ -45,8 +46,8 @@ class Conv:
         a = {k: kw.pop(k) for k in ("B", "T", "C", "K", "flags", "io") if k in kw}
         return g.lib().gdn2_short_conv_bwd(a.get("B", self.B), a.get("T", self.T), a.get("C", self.C),
                                            a.get("K", self.K), a.get("flags", self.flags), a.get("io", self.io),
-                                           *(self._p(kw, n) for n in ("x", "weight", "state", "dy", "dx",
-                                                                      "dweight", "dstate", "ws")),
+                                           *(self._p(kw, n) for n in ("x", "weight", "state", "dy", "dstate_out",
+                                                                      "dx", "dweight", "dstate", "ws")),
                                            self.ws_bytes if ws_bytes is None else ws_bytes, None)
 
 
@@ -59,6 +60,7 @@ def test_valid_calls_reach_the_device_check(io, K, flags):
     assert c.bwd() == DEVICE
     assert c.fwd(state=None, state_out=None) == DEVICE
     assert c.bwd(state=None, dstate=None) == DEVICE
+    assert c.bwd(dstate_out=None) == DEVICE
 
 
 @pytest.mark.parametrize("field,value", [("C", 12), ("C", 0), ("C", -8), ("K", 0), ("K", 9), ("flags", 2),
@@ -106,20 +108,23 @@ def test_alias_errors():
     assert c.bwd(ws=p["x"]) == ALIAS
     assert c.bwd(dweight=p["weight"]) == ALIAS
     assert c.bwd(dweight=p["dx"]) == ALIAS
+    assert c.bwd(dx=p["dstate_out"]) == ALIAS           # dstate_out is an input
+    assert c.bwd(dstate=p["dstate_out"]) == ALIAS
+    assert c.bwd(dstate_out=p["state"]) == DEVICE       # inputs may share memory
 
 
 def test_alignment_errors():
     c = Conv()
     for name in ("x", "weight", "state", "y", "state_out"):
         assert c.fwd(**{name: c.ptr[name] + 8}) == ALIGN
-    for name in ("dy", "dx", "dweight", "dstate", "ws"):
+    for name in ("dy", "dstate_out", "dx", "dweight", "dstate", "ws"):
         assert c.bwd(**{name: c.ptr[name] + 8}) == ALIGN
 
 
 def test_single_tap_ignores_the_state_pointers():
     c = Conv(K=1)
     assert c.fwd(state=c.ptr["state"] + 8, state_out=c.ptr["x"]) == DEVICE
-    assert c.bwd(state=c.ptr["state"] + 8, dstate=c.ptr["dy"]) == DEVICE
+    assert c.bwd(state=c.ptr["state"] + 8, dstate=c.ptr["dy"], dstate_out=c.ptr["dx"] + 8) == DEVICE
 
 
 def test_workspace():

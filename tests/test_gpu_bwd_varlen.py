@@ -4,7 +4,13 @@ fix that: isolation of sequences, equal lengths = an ordinary batch), so the exp
 gradients are ``oracle.backward.recurrent_bwd`` of each sequence on its own, laid back to
 back.  Same bars as the chunked backward: rel-L2 <= 1e-4 (fp32 I/O), <= 2e-2 (bf16).
 Lengths include empty sequences, one-token sequences and ragged last chunks; both the
-matrix-core (bf16, d 128) and the vector-ALU (fp32) gradient paths run.
+matrix-core (bf16, d 128) and the vector-ALU (fp32) gradient paths run.  With grouped
+value heads (Hv = 2H) and the in-kernel prologue (gate logits, b x 2, q/k L2 norm) the
+expected gradients are ``oracle.backward.full_bwd`` of each sequence (pinned by finite
+differences of the whole forward with its prologue).
+
+The offsets are read on the host (``cu_seqlens`` is copied there by the binding), unlike
+the packed forward, which takes them in device memory.
 """
 import numpy as np
 import pytest
@@ -66,6 +72,51 @@ def test_packed_backward_matches_per_sequence_oracle(dev, lengths, H, dk, dv, io
         got_n = _np(got[n])
         if ref.size == 0:
             assert got_n.size == 0
+            continue
+        err = rel_l2(got_n, ref)
+        print(f"  {n}: {err:.2e}", flush=True)
+        assert err <= tol, n
+
+
+LOG, NEG, L2 = g.FLAG_GATE_LOGITS, g.FLAG_NEG_EIGVAL, g.FLAG_QK_L2NORM
+
+
+@pytest.mark.parametrize("lengths,H,Hv,dk,dv,io,gate,flags,tol", [
+    ((70, 0, 129, 1, 64), 2, 4, 128, 128, BF16, BF16, LOG | NEG | L2, 2e-2),
+    ((90, 3, 65), 1, 2, 128, 128, BF16, F32, LOG | L2, 2e-2),
+    ((33, 100, 0), 2, 4, 64, 32, F32, F32, LOG | NEG | L2, 1e-4),
+])
+def test_packed_backward_grouped_heads_and_prologue(dev, lengths, H, Hv, dk, dv, io, gate, flags, tol):
+    from oracle.backward import full_bwd
+    print(f"bwd varlen lengths={lengths} H={H} Hv={Hv} dk={dk} dv={dv} {io} gates {gate} flags {flags}", flush=True)
+    N, T = len(lengths), sum(lengths)
+    inp = inputs.make_packed(lengths, H, dk, dv, io, 15, dev, s0_std=0.05, Hv=Hv, gate_dtype=gate,
+                             gate_logits=bool(flags & LOG), unit_qk=not flags & L2)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(16)
+    dO = torch.randn(1, T, Hv, dv, generator=gen, device=dev).to(io)
+    dS_T = torch.randn(N, Hv, dk, dv, generator=gen, device=dev)
+    got = g.chunk_bwd_varlen(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["b"], inp["w"], dO, inp["cu"],
+                             inp["S0"], dS_T, flags=flags)
+    torch.cuda.synchronize()
+    h = {n: _np(inp[n]) for n in ("q", "k", "v", "alpha", "b", "w", "S0")}
+    dOn, dSn = _np(dO), _np(dS_T)
+    want = {n: [] for n in NAMES}
+    cu = [0]
+    for n in lengths:
+        cu.append(cu[-1] + n)
+    for i in range(N):
+        a, e = cu[i], cu[i + 1]
+        sl = lambda x: x[:, a:e]
+        r = full_bwd(sl(h["q"]), sl(h["k"]), sl(h["v"]), sl(h["alpha"]), sl(h["b"]), sl(h["w"]),
+                     h["S0"][i:i + 1], sl(dOn), dSn[i:i + 1], flags=flags)
+        for n in NAMES:
+            want[n].append(r[n] if n == "dS0" else r[n].reshape(1, e - a, *r[n].shape[2:]))
+    for n in NAMES:
+        ref = np.concatenate(want[n], axis=0 if n == "dS0" else 1)
+        got_n = _np(got[n])
+        assert got_n.shape == ref.shape, n
+        if ref.size == 0:
             continue
         err = rel_l2(got_n, ref)
         print(f"  {n}: {err:.2e}", flush=True)

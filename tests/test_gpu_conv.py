@@ -7,8 +7,12 @@ norm; "Configuration": use_short_conv).  Both sides get the same seeded x, dy,
 state (bf16 widened exactly) and fp32 weights.  Bars: rel-L2 <= 1e-4 with fp32
 I/O, <= 2e-2 for bf16 outputs (rounded once); the fp32 weight gradient <= 1e-4 in
 both; the returned state is a copy, compared bit for bit.  Shapes span several
-tiles (16 tokens forward, 8 backward, 256-token spans) with ragged tails, channel
+of the kernels' token spans (forward: 32 tokens fp32, 64 bf16, two a workgroup;
+backward: 128-token spans of 32-token sub-spans) with ragged tails, channel
 counts that leave a wave partly idle, T of 1 and 0, and every K from 1 to 8.
+The backward also takes a gradient of the window after the last token
+(dstate_out), checked against the oracle and by chaining the backward over the
+pieces of a sequence.
 """
 import numpy as np
 import pytest
@@ -137,3 +141,56 @@ def test_full_size_sampled_channels(dev):
     assert rel_l2(_np(sel(ds)), rds) <= 2e-2
     assert rel_l2(_np(sel(dw)), rdw) <= 1e-4
     np.testing.assert_array_equal(_np(sel(so)), rso)
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("K,T", [(4, 70), (4, 2), (3, 0), (8, 5), (2, 129), (5, 300)])
+def test_window_gradient(dev, K, T, dt):
+    """dstate_out (the gradient of the window after the last token) reaches dx at the
+    last K-1 positions and dstate when the sequence is shorter than the window."""
+    B, C = 2, 72
+    print(f"conv bwd with dstate_out B={B} T={T} C={C} K={K} {dt}", flush=True)
+    x, w, st, dy = _draw(dev, B, T, C, K, dt, 40 + K + T)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(77 + T)
+    dso = torch.randn(B, K - 1, C, generator=gen, device=dev).to(dt)
+    dx, dw, ds = g.short_conv_bwd(x, w, dy, st, silu=True, dstate_out=dso)
+    torch.cuda.synchronize()
+    rdx, rdw, rds = short_conv_bwd(_np(x), _np(w), _np(dy), _np(st), True, dstate_out=_np(dso))
+    tol = _tol(dt)
+    if T > 0:
+        assert rel_l2(_np(dx), rdx) <= tol
+        assert rel_l2(_np(dw), rdw) <= 1e-4
+    assert rel_l2(_np(ds), rds) <= tol
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_backward_over_pieces_equals_whole(dev, dt):
+    """A sequence in pieces: forwards with the state carried, then backwards last
+    piece first, each piece's dstate handed to the piece before as dstate_out.  The
+    pieces' dx, the summed dweight and the first piece's dstate equal one backward
+    over the whole sequence."""
+    B, T, C, K = 2, 300, 96, 4
+    x, w, st, dy = _draw(dev, B, T, C, K, dt, 55)
+    dx_all, dw_all, ds_all = g.short_conv_bwd(x, w, dy, st, silu=True)
+    cuts = (0, 3, 130, 131, 300)
+    states = [st]
+    for lo, hi in zip(cuts[:-1], cuts[1:]):
+        _, so = g.short_conv(x[:, lo:hi].contiguous(), w, states[-1], silu=True)
+        states.append(so)
+    dxs, dw_sum, dso = [], torch.zeros_like(dw_all), None
+    for i in reversed(range(len(cuts) - 1)):
+        lo, hi = cuts[i], cuts[i + 1]
+        dxp, dwp, dsp = g.short_conv_bwd(x[:, lo:hi].contiguous(), w, dy[:, lo:hi].contiguous(), states[i],
+                                         silu=True, dstate_out=dso)
+        dxs.insert(0, dxp)
+        dw_sum += dwp
+        dso = dsp
+    torch.cuda.synchronize()
+    tol = 1e-6 if dt == torch.float32 else 2e-2
+    assert rel_l2(_np(torch.cat(dxs, 1)), _np(dx_all)) <= tol
+    assert rel_l2(_np(dso), _np(ds_all)) <= tol
+    assert rel_l2(_np(dw_sum), _np(dw_all)) <= 1e-5
+    rdx, rdw, rds = short_conv_bwd(_np(x), _np(w), _np(dy), _np(st), True)
+    assert rel_l2(_np(torch.cat(dxs, 1)), rdx) <= _tol(dt)
+    assert rel_l2(_np(dso), rds) <= _tol(dt)

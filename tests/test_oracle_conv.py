@@ -117,6 +117,73 @@ def test_short_conv_bwd_finite_differences(silu, K):
         np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-7)
 
 
+@pytest.mark.parametrize("silu", [False, True])
+@pytest.mark.parametrize("K,T", [(4, 6), (4, 2), (3, 0), (2, 1)])
+def test_short_conv_bwd_state_out_finite_differences(silu, K, T):
+    """With a gradient on the window after the last token: dx, dweight and dstate
+    against central differences of sum(dy * y) + sum(dso * state_out), also for
+    sequences shorter than the window (state_out then holds state inputs)."""
+    x, w, st, _ = _rand(11 + K + T, B=2, T=T, C=3, K=K)
+    rng = np.random.default_rng(100 + K + T)
+    dy = rng.standard_normal((2, T, 3))
+    dso = rng.standard_normal((2, K - 1, 3))
+    dx, dw, dst = short_conv_bwd(x, w, dy, st, silu, dstate_out=dso)
+
+    def loss(x_, w_, s_):
+        y, so = short_conv(x_, w_, s_, silu)
+        return float(np.sum(dy * y) + np.sum(dso * so))
+
+    h = 1e-6
+    for arr, grad in ((x, dx), (w, dw), (st, dst)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + h
+            lp = loss(x, w, st)
+            arr[idx] = old - h
+            lm = loss(x, w, st)
+            arr[idx] = old
+            num[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-7)
+
+
+def check_bwd_pieces(f=short_conv_bwd):
+    """The backward over a sequence split in two pieces, the second piece's dstate
+    handed to the first as dstate_out, equals the backward over the whole (dweight:
+    the sum of the pieces')."""
+    x, w, st, dy = _rand(21, B=2, T=11, C=4, K=4)
+    for silu in (False, True):
+        dx, dw, dst = f(x, w, dy, st, silu)
+        T1 = 5
+        _, st1 = short_conv(x[:, :T1], w, st, silu)
+        dx2, dw2, dst2 = f(x[:, T1:], w, dy[:, T1:], st1, silu)
+        dx1, dw1, dst1 = f(x[:, :T1], w, dy[:, :T1], st, silu, dstate_out=dst2)
+        np.testing.assert_allclose(np.concatenate([dx1, dx2], axis=1), dx, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dw1 + dw2, dw, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(dst1, dst, rtol=1e-12, atol=1e-12)
+
+
+def test_short_conv_bwd_pieces():
+    check_bwd_pieces()
+
+
+def _bslip_state_out_ignored(x, weight, dy, state=None, silu=False, dstate_out=None):
+    return short_conv_bwd(x, weight, dy, state, silu)
+
+
+def _bslip_state_out_shifted(x, weight, dy, state=None, silu=False, dstate_out=None):
+    if dstate_out is None:
+        return short_conv_bwd(x, weight, dy, state, silu)
+    d = np.concatenate([np.asarray(dstate_out)[:, 1:], np.zeros_like(np.asarray(dstate_out)[:, :1])], axis=1)
+    return short_conv_bwd(x, weight, dy, state, silu, dstate_out=d)
+
+
+@pytest.mark.parametrize("slip", [_bslip_state_out_ignored, _bslip_state_out_shifted], ids=lambda f: f.__name__)
+def test_short_conv_bwd_slips_rejected(slip):
+    with pytest.raises(AssertionError):
+        check_bwd_pieces(slip)
+
+
 # ---- planted slips: each must fail at least one pin --------------------------------------
 def _slip_reversed(x, weight, state=None, silu=False):
     return short_conv(x, np.asarray(weight)[:, ::-1], state, silu)
