@@ -11,6 +11,7 @@
 #include <stdint.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "gdn2_launch.hpp"
 #include "gdn2_layout.hpp"
@@ -455,6 +456,103 @@ int gdn2_chunk_state(const gdn2_problem* p, const float* S0, void* o, float* S_o
     return do_state(p, S0, o, S_out, workspace, static_cast<hipStream_t>(stream));
 }
 
+// ---- long single sequences: the prep of the next piece beside the state pass
+// With few chains the serial state pass holds at most half of the CUs (one
+// workgroup each) for a long time while the rest idle.  The sequence is then
+// cut into pieces of whole chunks: piece i's state pass runs on the caller's
+// stream while the preps of the pieces after it run on a second stream on
+// the other CUs.  Each piece has its own part of the workspace (the same
+// bytes in all), the state is carried through S_out, and the pieces are
+// ordered only by events (no workgroup waits for another).
+namespace {
+constexpr int kMaxPieces = 8;
+constexpr int kMaxDevices = 64;
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t start = nullptr, done[kMaxPieces] = {};
+    bool ok = false, tried = false;
+};
+SideStream g_side[kMaxDevices];
+std::mutex g_side_mu;   // one call's fork and join are enqueued as a whole
+
+// pieces for this problem (1 = one prep and one state pass, as usual)
+int64_t chunk_pieces(const gdn2_problem* p)
+{
+    const int64_t nt = nchunks(p), nch = p->B * nvh(p);
+    if (p->B != 1 || nt < 256) return 1;
+    const int vs = gdn2::chunk_state_slice(nch, (int)p->dv, (int)p->dk, (int)io_size(p));
+    if (nch * (p->dv / vs) > 128) return 1;   // the state pass would hold more than half of the CUs
+    const int64_t k = nt / 128;
+    return k < 2 ? 2 : (k > kMaxPieces ? kMaxPieces : k);
+}
+
+SideStream* side_stream(int dev)
+{
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    SideStream& x = g_side[dev];
+    if (!x.tried) {
+        x.tried = true;
+        bool ok = hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking) == hipSuccess;
+        ok = ok && hipEventCreateWithFlags(&x.start, hipEventDisableTiming) == hipSuccess;
+        for (int i = 0; i < kMaxPieces && ok; ++i)
+            ok = hipEventCreateWithFlags(&x.done[i], hipEventDisableTiming) == hipSuccess;
+        x.ok = ok;
+    }
+    return x.ok ? &x : nullptr;
+}
+
+// the forward in npc pieces (B == 1): pointers of piece i are offset by its
+// first token; its workspace blocks follow the previous pieces'
+int chunk_fwd_pieces(const gdn2_problem* p, int64_t npc, const void* q, const void* k, const void* v,
+                     const void* alpha, const void* b, const void* w, const float* S0, void* o, float* S_out,
+                     void* workspace, hipStream_t s)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GDN2_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream* side = side_stream(dev);
+    if (side == nullptr) return GDN2_ERR_DEVICE;
+    const int64_t nt = nchunks(p), per = (nt + npc - 1) / npc;
+    const int64_t es = io_size(p), gs = gates_bf16(p) ? 2 : 4, Hv = nvh(p);
+    const int64_t blk = ws_block_bytes(p);
+    auto piece = [&](int64_t i, gdn2_problem* pp, int64_t* t0, int64_t* wsoff) {
+        const int64_t c0 = i * per, c1 = (i + 1) * per < nt ? (i + 1) * per : nt;
+        *pp = *p;
+        *t0 = c0 * 64;
+        pp->T = (c1 * 64 < p->T ? c1 * 64 : p->T) - *t0;
+        *wsoff = c0 * Hv * blk;   // blocks of the pieces before, B == 1
+    };
+    auto at = [](const void* x, int64_t bytes) { return static_cast<const char*>(x) + bytes; };
+    // the side stream starts after everything already on the caller's stream
+    if (hipEventRecord(side->start, s) != hipSuccess || hipStreamWaitEvent(side->s, side->start, 0) != hipSuccess)
+        return GDN2_ERR_DEVICE;
+    for (int64_t i = 0; i < npc; ++i) {
+        gdn2_problem pp;
+        int64_t t0, wso;
+        piece(i, &pp, &t0, &wso);
+        if (pp.T <= 0) break;
+        const int64_t tk = t0 * p->H * p->dk, tg = t0 * Hv * p->dk, tv = t0 * Hv * p->dv;
+        const hipStream_t ps = i == 0 ? s : side->s;
+        int st = do_prep(&pp, at(q, tk * es), at(k, tk * es), at(v, tv * es), at(alpha, tg * gs), at(b, tg * gs),
+                         at(w, tv * gs), static_cast<char*>(workspace) + wso, ps);
+        if (st) return st;
+        if (i > 0 && hipEventRecord(side->done[i], side->s) != hipSuccess) return GDN2_ERR_DEVICE;
+    }
+    for (int64_t i = 0; i < npc; ++i) {
+        gdn2_problem pp;
+        int64_t t0, wso;
+        piece(i, &pp, &t0, &wso);
+        if (pp.T <= 0) break;
+        if (i > 0 && hipStreamWaitEvent(s, side->done[i], 0) != hipSuccess) return GDN2_ERR_DEVICE;
+        const int64_t tv = t0 * Hv * p->dv;
+        int st = do_state(&pp, i == 0 ? S0 : S_out, static_cast<char*>(o) + tv * es, S_out,
+                          static_cast<char*>(workspace) + wso, s);
+        if (st) return st;
+    }
+    return GDN2_OK;
+}
+}  // namespace
+
 int gdn2_chunk_fwd(const gdn2_problem* p, const void* q, const void* k, const void* v,
                    const void* alpha, const void* b, const void* w, const float* S0, void* o,
                    float* S_out, void* workspace, size_t workspace_bytes, void* stream)
@@ -480,6 +578,11 @@ int gdn2_chunk_fwd(const gdn2_problem* p, const void* q, const void* k, const vo
     st = device_ready();
     if (st) return st;
     const hipStream_t s = static_cast<hipStream_t>(stream);
+    // pieces only outside stream capture (no stream is created or forked then)
+    const int64_t npc = chunk_pieces(p);
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (npc > 1 && S_out != nullptr && hipStreamIsCapturing(s, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone)
+        return chunk_fwd_pieces(p, npc, q, k, v, alpha, b, w, S0, o, S_out, workspace, s);
     st = do_prep(p, q, k, v, alpha, b, w, workspace, s);
     if (st) return st;
     return do_state(p, S0, o, S_out, workspace, s);

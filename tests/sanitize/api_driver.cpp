@@ -75,6 +75,18 @@ int fwd(const Tensors& t, const gdn2_problem* p, const void* q, void* o, const f
 
 void chunk_forward_cases()
 {
+    // a long single sequence with few chains: run in pieces (prep of the next
+    // piece beside the state pass); every piece's pointers must stay inside
+    // the tensors and its workspace blocks inside the workspace
+    for (int io = 0; io < 2; ++io) {
+        Tensors t = make(1, 256 * 64 + 37, 2, 4, 16, 16, io, io ? GDN2_BF16 : GDN2_F32, 0);
+        const gdn2_problem& p = t.p;
+        expect("fwd long sequence in pieces", fwd(t, &p, t.q, t.o, t.S0, t.S_out, t.ws, t.ws_bytes), GDN2_OK, 4, 4);
+        expect("fwd long sequence in pieces, in place", fwd(t, &p, t.q, t.o, t.S0, t.S0, t.ws, t.ws_bytes), GDN2_OK,
+               4, 4);
+        expect("fwd long sequence, no final state", fwd(t, &p, t.q, t.o, t.S0, nullptr, t.ws, t.ws_bytes), GDN2_OK,
+               2, 2);
+    }
     for (int io = 0; io < 2; ++io) {
         Tensors t = make(2, 100, 2, 4, 64, 32, io, GDN2_F32, io ? GDN2_FLAG_GATE_LOGITS | GDN2_FLAG_QK_L2NORM : 0);
         const gdn2_problem& p = t.p;

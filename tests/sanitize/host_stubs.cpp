@@ -89,16 +89,50 @@ extern "C" hipError_t hipGetDevice(int* d)
     return hipSuccess;
 }
 
+// the side stream and events of the piecewise chunked forward: opaque handles
+static int g_handles[64];
+static int g_nhandles = 0;
+extern "C" hipError_t hipStreamCreateWithFlags(hipStream_t* s, unsigned int)
+{
+    *s = reinterpret_cast<hipStream_t>(&g_handles[g_nhandles++ % 64]);
+    return hipSuccess;
+}
+extern "C" hipError_t hipEventCreateWithFlags(hipEvent_t* e, unsigned int)
+{
+    *e = reinterpret_cast<hipEvent_t>(&g_handles[g_nhandles++ % 64]);
+    return hipSuccess;
+}
+extern "C" hipError_t hipEventRecord(hipEvent_t e, hipStream_t)
+{
+    return e != nullptr ? hipSuccess : hipErrorInvalidValue;
+}
+extern "C" hipError_t hipStreamIsCapturing(hipStream_t, hipStreamCaptureStatus* c)
+{
+    *c = hipStreamCaptureStatusNone;
+    return hipSuccess;
+}
+extern "C" hipError_t hipStreamWaitEvent(hipStream_t, hipEvent_t e, unsigned int)   // null stream: the default one
+{
+    return e != nullptr ? hipSuccess : hipErrorInvalidValue;
+}
+
 // ---- launch hooks ----------------------------------------------------------
 namespace gdn2 {
 
 static int64_t prep_blocks(const PrepArgs& a) { return a.plan ? a.H * a.ncmax : a.B * a.H * a.nt; }
 
-hipError_t launch_chunk_prep(const PrepArgs& a, int, bool, bool, hipStream_t)
+hipError_t launch_chunk_prep(const PrepArgs& a, int dk, bool bf16, bool gbf16, hipStream_t)
 {
     ++g_launches;
     const char* h = "launch_chunk_prep";
-    for (const void* p : {a.q, a.k, a.v, a.alpha, a.b, a.w}) in_buf(h, "input", p, 0, true);
+    // whole extents of the token tensors (equal-length batches: B sequences of T)
+    const int64_t es = bf16 ? 2 : 4, gs = gbf16 ? 2 : 4, tok = a.plan ? a.T : a.B * a.T;
+    in_buf(h, "q", a.q, tok * a.Hk * dk * es, true);
+    in_buf(h, "k", a.k, tok * a.Hk * dk * es, true);
+    in_buf(h, "v", a.v, tok * a.H * a.dv * es, true);
+    in_buf(h, "alpha", a.alpha, tok * a.H * dk * gs, true);
+    in_buf(h, "b", a.b, tok * a.H * dk * gs, true);
+    in_buf(h, "w", a.w, tok * a.H * a.dv * gs, true);
     in_buf(h, "workspace blocks", a.ws, prep_blocks(a) * a.ws_block, true);
     in_buf(h, "plan", a.plan, 0);
     if (a.conv_w != nullptr) {

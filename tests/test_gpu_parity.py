@@ -481,3 +481,45 @@ def test_chunk_d128_split_resume_bitwise(dev):
     o3, _ = g.chunk_fwd(*args(inp), Sp, S_out=Sp)
     torch.cuda.synchronize()
     assert torch.equal(o3, o) and torch.equal(Sp, S)
+
+
+# ---------------------------------------------------------------------------
+# a long single sequence with few chains runs in pieces (the prep of later
+# pieces on a second stream beside the state pass); chunk boundaries are
+# bitwise resumable, so the pieces must equal the two stages called once
+# ---------------------------------------------------------------------------
+PIECES = [
+    # T, H, Hv, dk, dv, dtype, gate dtype, flags, S0 std
+    (256 * 64 + 37, 2, 2, 64, 64, torch.float32, torch.float32, 0, 0.05),
+    (300 * 64, 1, 2, 128, 128, torch.bfloat16, torch.bfloat16,
+     g.FLAG_GATE_LOGITS | g.FLAG_NEG_EIGVAL | g.FLAG_QK_L2NORM, None),
+    (1024 * 64 + 1, 2, 2, 128, 128, torch.bfloat16, torch.float32, 0, 0.05),
+]
+
+
+@pytest.mark.parametrize("case", PIECES, ids=lambda c: f"T{c[0]}H{c[1]}Hv{c[2]}dk{c[3]}dv{c[4]}fl{c[7]}")
+def test_long_sequence_in_pieces(dev, case):
+    T, H, Hv, dk, dv, dt, gt, flags, s0 = case
+    print(f"pieces T={T} H={H} Hv={Hv} dk={dk} dv={dv} {dt} flags {flags}", flush=True)
+    inp = inputs.make_raw(1, T, H, dk, dv, dt, 61 + dk, dev, s0_std=s0, Hv=Hv, gate_dtype=gt,
+                          gate_logits=bool(flags & g.FLAG_GATE_LOGITS), unit_qk=not flags & g.FLAG_QK_L2NORM)
+    o, S = g.chunk_fwd(*args(inp), inp["S0"], flags=flags)
+    o2, S2 = _split(inp, flags)
+    # in place: S_out is the initial state's buffer
+    S_io = inp["S0"].clone() if inp["S0"] is not None else None
+    o3 = torch.empty_like(o)
+    if S_io is not None:
+        g.chunk_fwd(*args(inp), S_io, flags=flags, o=o3, S_out=S_io)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(S, S2), "pieces differ from the single pass"
+    if S_io is not None:
+        assert torch.equal(o3, o) and torch.equal(S_io, S), "in-place pieces differ"
+    if T <= 300 * 64:
+        from oracle.reference import share_qk_heads
+        f = lambda x: None if x is None else x.detach().to("cpu", torch.float32).numpy()
+        qq, kk = f(inp["q"]), f(inp["k"])
+        if Hv != H:
+            qq, kk = (np.ascontiguousarray(x, dtype=np.float32) for x in share_qk_heads(qq, kk, Hv))
+        ro, rS = c_oracle.recurrent(qq, kk, f(inp["v"]), f(inp["alpha"]), f(inp["b"]), f(inp["w"]), f(inp["S0"]),
+                                    flags=flags)
+        check(f"pieces T{T}", o, S, ro, rS, 1e-4 if dt == torch.float32 else 2e-2)
