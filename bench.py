@@ -71,7 +71,8 @@ def parse_args(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps first: the GPU needs ~15 ms of work to reach its steady clocks")
     ap.add_argument("--sets", type=int, default=3, help="rotated input sets (>= 3 defeats the 256 MB MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-chains", type=int, default=0,
