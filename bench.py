@@ -367,6 +367,8 @@ def main(argv=None):
                       "frac_hbm_roofline": round(chunk_gbps / PEAK_HBM_GBPS, 4),
                       "useful_TFLOPs": round(flops / (chunk_ms * 1e-3) / 1e12, 2),
                       "frac_bf16_mfma_peak": round(flops / (chunk_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                      "frac_bf16_mfma_peak_at_roofline": round(
+                          flops / (alg_chunk / (PEAK_HBM_GBPS * 1e9)) / 1e12 / PEAK_BF16_TFLOPS, 4),
                       "median_us": spread["chunk"]["median_us"], "min_us": spread["chunk"]["min_us"],
                       "stages": {**split,
                                  "roofline_prep": roof("prep", (bpht - 2 * dv) * ht, split["prep_us"] * 1e-3,
@@ -524,6 +526,10 @@ def workload_leg(g, inputs, idx, dev, args, nsets=3):
                                  + f", alpha = sigmoid(N({wl.alpha_mu:g}, 1))",
            "tokens_per_s": round(B * T / (ms * 1e-3), 1), **t, "alg_bytes": int(alg),
            "useful_GFLOP": round(flops / 1e9, 2),
+           "useful_TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
+           "frac_bf16_mfma_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           # the useful-MFMA fraction a call at the HBM roofline would reach (its ceiling)
+           "frac_bf16_mfma_peak_at_roofline": round(flops / t_roof / 1e12 / PEAK_BF16_TFLOPS, 4),
            "roofline": {"kernel": "k_chunk_prep + k_chunk_state (the whole chunked forward call)", "bound": "hbm",
                         "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                         "frac": round(ach / PEAK_HBM_GBPS, 4), "t_roofline_us": round(t_roof * 1e6, 1)},
