@@ -523,3 +523,27 @@ def test_long_sequence_in_pieces(dev, case):
         ro, rS = c_oracle.recurrent(qq, kk, f(inp["v"]), f(inp["alpha"]), f(inp["b"]), f(inp["w"]), f(inp["S0"]),
                                     flags=flags)
         check(f"pieces T{T}", o, S, ro, rS, 1e-4 if dt == torch.float32 else 2e-2)
+
+
+def test_long_sequence_under_graph_capture(dev):
+    """A forward that runs in pieces when called eagerly (second stream) is captured into a
+    graph as one stream's work; replays, with eager work and synchronisations between them,
+    equal the eager result bit for bit."""
+    T, H, dk, dv = 256 * 64 + 5, 2, 64, 64
+    inp = inputs.make_raw(1, T, H, dk, dv, torch.bfloat16, 71, dev, s0_std=0.05)
+    o_ref, S_ref = g.chunk_fwd(*args(inp), inp["S0"])
+    ws = g.alloc_workspace(g.chunk_fwd_workspace_size(1, T, H, dk, dv, torch.bfloat16), dev)
+    o = torch.empty_like(o_ref)
+    S = torch.empty_like(S_ref)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g.chunk_fwd(*args(inp), inp["S0"], o=o, S_out=S, workspace=ws)
+    for rep in range(4):
+        o.zero_()
+        S.fill_(1.0)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(S, S_ref), f"replay {rep}"
+        g.chunk_fwd(*args(inp), inp["S0"], o=torch.empty_like(o), workspace=ws)   # eager work between replays
+        torch.cuda.synchronize()
