@@ -398,6 +398,7 @@ def main(argv=None):
         result["chunk_fwd_grouped"] = grouped_leg(g, inputs, wl_c, dev, args)
         result["chunk_fwd_varlen"] = varlen_leg(g, inputs, wl_c, dev, args)
         result["chunk_bwd"] = backward_leg(g, inputs, wl_c, dev, args)
+        result["chunk_bwd_varlen"] = bwd_varlen_leg(g, inputs, wl_c, dev, args)
         result["epilogue"] = epilogue_leg(g, outs, dev, args)
         result["short_conv"] = short_conv_leg(g, dev, args)
         result["conv_fused"] = conv_fused_leg(g, inputs, wl_c, dev, args)
@@ -700,6 +701,48 @@ def backward_leg(g, inputs, wl, dev, args):
             "grad_kernel_useful_GFLOP": round(flops / 1e9, 2),
             "with_prologue_flags": {"workload": "the same with bf16 gate logits, b x 2 and the q/k L2 norm",
                                     "us": round(msf * 1e3, 2), "median_us": round(tf[len(tf) // 2] * 1e3, 2)},
+            "outputs_finite": bool(finite)}
+
+
+def bwd_varlen_leg(g, inputs, wl, dev, args):
+    """Backward of the packed batch the forward's varlen leg runs (the chunked workload's
+    8,192 tokens per head in sequences of mixed length, zero initial states), offsets in
+    device memory: the whole call (chunk plan, forward recompute, reverse pass, gradients)
+    timed.  Algorithmic bytes as for the equal-length backward."""
+    import torch
+    H, dk, dv = wl.H, wl.dk, wl.dv
+    lens = inputs.length_mix(wl.B * wl.T, seed=1)
+    N, T = len(lens), sum(lens)
+    sets = [inputs.make_packed(lens, H, dk, dv, wl.io_dtype, 800 + i, dev) for i in range(2)]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(850)
+    grads = [(torch.randn(1, T, H, dv, generator=gen, device=dev).to(wl.io_dtype),
+              torch.randn(N, H, dk, dv, generator=gen, device=dev)) for _ in range(2)]
+    ws = g.alloc_workspace(g.chunk_bwd_varlen_workspace_size(N, T, H, dk, dv, wl.io_dtype), dev)
+    steps = max(args.steps // 5, 3)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    out = None
+    for i in range(args.warmup + steps):
+        x, (dO, dS) = sets[i % 2], grads[i % 2]
+        ev = evs[i - args.warmup] if i >= args.warmup else None
+        if ev:
+            ev[0].record()
+        out = g.chunk_bwd_varlen(x["q"], x["k"], x["v"], x["alpha"], x["b"], x["w"], dO, x["cu"], None, dS,
+                                 workspace=ws)
+        if ev:
+            ev[1].record()
+    torch.cuda.synchronize()
+    t = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    ms = sum(t) / steps
+    per_ht = 2 * (2 * dk + 2 * dv) + 4 * (2 * dk + dv) + 2 * (2 * dk + dv) + 4 * (2 * dk + dv)
+    alg = per_ht * T * H + 2 * N * H * dk * dv * 4
+    ach = alg / (ms * 1e-3) / 1e9
+    finite = all(torch.isfinite(v.float()).all() for v in out.values() if v is not None)
+    return {"workload": f"backward of a packed batch of {N} sequences, {T} tokens (lengths log-uniform in "
+                        f"[16, 4096], seed 1), H{H} d{dk}, bf16 q/k/v/dO, fp32 gates, dS_T given",
+            "tokens_per_s": round(T / (ms * 1e-3), 1), "us": round(ms * 1e3, 2),
+            "median_us": round(t[len(t) // 2] * 1e3, 2), "min_us": round(t[0] * 1e3, 2),
+            "alg_GBps": round(ach, 1), "frac_hbm_roofline": round(ach / PEAK_HBM_GBPS, 4),
             "outputs_finite": bool(finite)}
 
 

@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     alloc_workspace,
     chunk_bwd,
     chunk_bwd_varlen,
+    chunk_bwd_varlen_workspace_size,
     chunk_bwd_workspace_size,
     chunk_fwd,
     chunk_fwd_conv,

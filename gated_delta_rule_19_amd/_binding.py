@@ -16,7 +16,7 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn2.so")
 
-ABI_VERSION = 7
+ABI_VERSION = 8
 GDN2_F32, GDN2_BF16 = 0, 1
 FLAG_GATE_LOGITS, FLAG_NEG_EIGVAL, FLAG_QK_L2NORM = 1, 2, 4
 CONV_SILU = 1
@@ -114,7 +114,7 @@ def lib():
         L.gdn2_short_conv_bwd.restype = ctypes.c_int
         L.gdn2_short_conv_bwd.argtypes = [i64] * 3 + [i32] * 3 + [vp] * 8 + [vp, sz, vp]
         L.gdn2_chunk_bwd_varlen_workspace_size.restype = sz
-        L.gdn2_chunk_bwd_varlen_workspace_size.argtypes = [P, vp]
+        L.gdn2_chunk_bwd_varlen_workspace_size.argtypes = [P]
         L.gdn2_chunk_bwd_varlen.restype = ctypes.c_int
         L.gdn2_chunk_bwd_varlen.argtypes = [P, vp] + [vp] * 16 + [vp, sz, vp]
         if L.gdn2_abi_version() != ABI_VERSION:   # the Problem mirror must match the library's struct
@@ -465,18 +465,19 @@ def chunk_bwd(q, k, v, alpha, b, w, dO, S0=None, dS_T=None, *, want_dS0: bool = 
     return g
 
 
+def chunk_bwd_varlen_workspace_size(N, T, H, dk, dv, io_dtype: torch.dtype, Hv: int = 0, flags: int = 0,
+                                    gate_dtype: torch.dtype = torch.float32) -> int:
+    """Workspace bytes of ``chunk_bwd_varlen`` for N sequences of T packed tokens in all."""
+    p = problem(N, T, H, dk, dv, io_dtype, gate_dtype=gate_dtype, flags=flags, Hv=Hv)
+    return int(lib().gdn2_chunk_bwd_varlen_workspace_size(ctypes.byref(p)))
+
+
 def chunk_bwd_varlen(q, k, v, alpha, b, w, dO, cu_seqlens, S0=None, dS_T=None, *, want_dS0: bool = True,
                      workspace=None, flags: int = 0):
-    """Backward of :func:`chunk_fwd_varlen` (``gdn2_chunk_bwd_varlen``): tensors as there
-    ([1, T, heads, d]), states [N, Hv, dk, dv]; ``cu_seqlens`` as an int32 [N+1] tensor
-    (read on the host).  Returns a dict dq, dk, dv, dalpha, db, dw, dS0 as :func:`chunk_bwd`."""
-    cu_host = cu_seqlens.detach().to("cpu", torch.int32).contiguous()
-    p, dev = _problem_from(q, k, v, alpha, b, w, flags)
-    if p.B != 1:
-        raise ValueError("a packed batch is passed as [1, T, heads, d] tensors")
-    if cu_host.dim() != 1 or cu_host.numel() < 1:
-        raise ValueError("cu_seqlens must be an int32 [N+1] tensor")
-    p.B = cu_host.numel() - 1
+    """Backward of :func:`chunk_fwd_varlen` (``gdn2_chunk_bwd_varlen``): tensors and the
+    int32 [N+1] offsets on the GPU as there ([1, T, heads, d]), states [N, Hv, dk, dv].
+    Returns a dict dq, dk, dv, dalpha, db, dw, dS0 as :func:`chunk_bwd`."""
+    p, dev = _varlen_problem(q, k, v, alpha, b, w, cu_seqlens, flags)
     _check_state(S0, p, dev, "S0")
     _check_state(dS_T, p, dev, "dS_T")
     if tuple(dO.shape) != tuple(v.shape) or dO.dtype != v.dtype or dO.device != dev or not dO.is_contiguous():
@@ -485,13 +486,12 @@ def chunk_bwd_varlen(q, k, v, alpha, b, w, dO, cu_seqlens, S0=None, dS_T=None, *
                                             ("dw", w))}
     g["dS0"] = (torch.empty((p.B, p.value_heads, p.dk, p.dv), dtype=torch.float32, device=dev)
                 if want_dS0 else None)
-    cu_p = ctypes.c_void_p(cu_host.data_ptr())
-    need = int(lib().gdn2_chunk_bwd_varlen_workspace_size(ctypes.byref(p), cu_p))
+    need = int(lib().gdn2_chunk_bwd_varlen_workspace_size(ctypes.byref(p)))
     if workspace is None:
         workspace = alloc_workspace(need, dev)
-    _check(lib().gdn2_chunk_bwd_varlen(ctypes.byref(p), cu_p, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(b),
-                                       _ptr(w), _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(g["dq"]), _ptr(g["dk"]),
-                                       _ptr(g["dv"]), _ptr(g["dalpha"]), _ptr(g["db"]), _ptr(g["dw"]),
+    _check(lib().gdn2_chunk_bwd_varlen(ctypes.byref(p), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                       _ptr(b), _ptr(w), _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(g["dq"]),
+                                       _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dalpha"]), _ptr(g["db"]), _ptr(g["dw"]),
                                        _ptr(g["dS0"]), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                        _stream(dev)))
     return g

@@ -249,12 +249,13 @@ Range conv_state_range(const gdn2_problem* p, const gdn2_conv* c, const void* pt
 struct BwdLayout {
     bool mf;
     int64_t block, t_off;                 // factor block stride, offset of T in it
+    int64_t blk;                          // offset of the first factor block
     int64_t chk, chkT, dsl, dslT, scratch, total;
 };
 
-BwdLayout bwd_layout(const gdn2_problem* p)
+// nblk: the factor blocks (B*H*nchunks, or H*ncmax for a packed batch)
+BwdLayout bwd_layout(const gdn2_problem* p, int64_t nblk)
 {
-    const int64_t nblk = p->B * p->H * nchunks(p);
     const int64_t states = nblk * p->dk * p->dv * 4;
     auto up = [](int64_t x) { return (x + 255) & ~int64_t(255); };
     BwdLayout l{};
@@ -278,18 +279,32 @@ BwdLayout bwd_layout(const gdn2_problem* p)
 // with no flags and one query/key row per value head on inputs materialised in
 // workspace after its own (activated gates as fp32; q/k rows normalised and
 // widened to the value heads), and its gradients of those are mapped back.
+// A packed batch (varlen: B sequences, T packed tokens) puts its chunk plan
+// first and gives every value head ncmax blocks.
 struct BwdWrap {
     gdn2_problem core;     // the problem the core backward sees
-    BwdLayout l;           // its workspace layout
+    BwdLayout l;           // its workspace layout, from `base` on
     bool qk, gates;        // q/k rows materialised; gates activated
+    int64_t base;          // bytes of the chunk plan ahead of the layout (0: equal lengths)
+    int64_t ncmax;         // block slots per value head (packed batches)
+    int64_t tok;           // token rows of the tensors: B*T, or T packed
     int64_t qh, kh, dqh, dkh, ga, gb, gw, dga, dgb, dgw, total;
 };
 
-BwdWrap bwd_wrap(const gdn2_problem* p)
+BwdWrap bwd_wrap(const gdn2_problem* p, bool varlen = false)
 {
     BwdWrap w{};
     w.core = *p;
-    w.l = bwd_layout(p);
+    w.base = varlen ? varlen_plan_bytes(p) : 0;
+    w.ncmax = varlen ? varlen_ncmax(p) : 0;
+    w.tok = varlen ? p->T : p->B * p->T;
+    auto blocks = [&](const gdn2_problem* c) { return varlen ? c->H * w.ncmax : c->B * c->H * nchunks(c); };
+    auto shift = [&](BwdLayout l) {       // the layout's offsets from the start of the workspace
+        l.blk += w.base; l.chk += w.base; l.chkT += w.base; l.dsl += w.base; l.dslT += w.base;
+        l.scratch += w.base; l.total += w.base;
+        return l;
+    };
+    w.l = shift(bwd_layout(p, blocks(p)));
     // the matrix-core kernels apply the prologue options themselves; shared
     // query/key heads still need q/k widened to the value heads (and their
     // gradients summed per group, through the norm when it is on), and the
@@ -306,14 +321,14 @@ BwdWrap bwd_wrap(const gdn2_problem* p)
     w.core.H = nvh(p);
     w.core.Hv = 0;
     if (w.gates) w.core.gate_dtype = GDN2_F32;
-    w.l = bwd_layout(&w.core);
+    w.l = shift(bwd_layout(&w.core, blocks(&w.core)));
     int64_t off = w.l.total;
     auto take = [&off](int64_t bytes) {
         const int64_t o = (off + 255) & ~int64_t(255);
         off = o + bytes;
         return o;
     };
-    const int64_t vrows = p->B * p->T * nvh(p);
+    const int64_t vrows = w.tok * nvh(p);
     if (w.qk) {
         const int64_t bytes = vrows * p->dk * io_size(p);
         w.qh = take(bytes); w.kh = take(bytes); w.dqh = take(bytes); w.dkh = take(bytes);
@@ -328,12 +343,15 @@ BwdWrap bwd_wrap(const gdn2_problem* p)
 }
 
 // the core backward: H value heads = query/key heads; prologue flags only on
-// the matrix-core path
-int bwd_core(const gdn2_problem* p, const BwdLayout& l, const void* q, const void* k, const void* v,
-             const void* alpha, const void* b, const void* w, const float* S0, const void* dO, const float* dS_T,
-             void* dq, void* dk, void* dv, void* dalpha, void* db, void* dw, float* dS0, char* ws, hipStream_t s)
+// the matrix-core path.  plan (null for equal-length batches): the packed
+// batch's chunk plan, already written, with ncmax block slots per head.
+int bwd_core(const gdn2_problem* p, const BwdLayout& l, const int* plan, int64_t ncmax, const void* q,
+             const void* k, const void* v, const void* alpha, const void* b, const void* w, const float* S0,
+             const void* dO, const float* dS_T, void* dq, void* dk, void* dv, void* dalpha, void* db, void* dw,
+             float* dS0, char* ws, hipStream_t s)
 {
     int st = GDN2_OK;
+    char* blocks = ws + l.blk;
     float* chk = l.mf ? nullptr : reinterpret_cast<float*>(ws + l.chk);     // fp32 checkpoints
     float* dsl = l.mf ? nullptr : reinterpret_cast<float*>(ws + l.dsl);
     void* chkIo = l.mf ? ws + l.chk : nullptr;                                // bf16, both layouts
@@ -341,36 +359,95 @@ int bwd_core(const gdn2_problem* p, const BwdLayout& l, const void* q, const voi
     void* chkT = l.mf ? ws + l.chkT : nullptr;
     void* dslT = l.mf ? ws + l.dslT : nullptr;
     const int64_t nch = p->B * p->H;
-    const int64_t total = nch * nchunks(p);
+    const int nt = plan ? 0 : (int)nchunks(p);               // per chain; a plan gives each its own
+    const int64_t total = plan ? p->H * ncmax : nch * nchunks(p);   // block slots
     if (p->flags != 0 && !l.mf) return GDN2_ERR_SHAPE;   // never reached: the mappings clear the flags
     if (nchunks(p) > 0) {
-        gdn2::PrepArgs pa{q, k, v, alpha, b, w, ws, l.block, p->B, p->T, p->H, p->H,
-                          (int)p->dv, (int)nchunks(p), (int)p->flags, nullptr, 0, l.t_off};
+        gdn2::PrepArgs pa{q, k, v, alpha, b, w, blocks, l.block, p->B, p->T, p->H, p->H,
+                          (int)p->dv, nt, (int)p->flags, plan, ncmax, l.t_off};
         st = launch_status(gdn2::launch_chunk_prep(pa, (int)p->dk, is_bf16(p), gates_bf16(p), s));
         if (st) return st;
         const int vs = gdn2::chunk_state_slice(nch, (int)p->dv, (int)p->dk, (int)io_size(p));
-        gdn2::StateArgs fa{ws, l.block, S0, nullptr, nullptr, p->B, p->T, p->H, (int)p->dv,
-                           (int)nchunks(p), (int)(p->dv / vs), nullptr, 0, chk, chkT, chkIo};
+        gdn2::StateArgs fa{blocks, l.block, S0, nullptr, nullptr, p->B, p->T, p->H, (int)p->dv,
+                           nt, (int)(p->dv / vs), plan, ncmax, chk, chkT, chkIo};
         st = launch_status(gdn2::launch_chunk_state(fa, (int)p->dk, vs, is_bf16(p), s));
         if (st) return st;
     }
     const int bvs = l.mf ? 32 : gdn2::state_bwd_slice((int)p->dv);
-    gdn2::BwdStateArgs ba{ws, l.block, dO, dS_T, dsl, dS0, p->B, p->T, p->H, (int)p->dk, (int)p->dv,
-                          (int)nchunks(p), (int)(p->dv / bvs), bvs, dslT, dslIo, l.t_off};
+    gdn2::BwdStateArgs ba{blocks, l.block, dO, dS_T, dsl, dS0, p->B, p->T, p->H, (int)p->dk, (int)p->dv,
+                          nt, (int)(p->dv / bvs), bvs, dslT, dslIo, l.t_off, plan, ncmax};
     st = launch_status(l.mf ? gdn2::launch_chunk_state_bwd_mf(ba, s) : gdn2::launch_chunk_state_bwd(ba, is_bf16(p), s));
     if (st) return st;
     if (nchunks(p) == 0) return GDN2_OK;
     float* gsc = reinterpret_cast<float*>(ws + l.scratch);
     if (l.mf) {
-        gdn2::GradVArgs va{ws, l.block, l.t_off, v, w, dO, chkIo, chkT, dslIo, dslT, dw, dv,
-                           p->B, p->T, p->H, (int)p->dk, (int)p->dv, (int)nchunks(p), total, (int)p->flags};
+        gdn2::GradVArgs va{blocks, l.block, l.t_off, v, w, dO, chkIo, chkT, dslIo, dslT, dw, dv,
+                           p->B, p->T, p->H, (int)p->dk, (int)p->dv, nt, total, (int)p->flags, plan, ncmax};
         gdn2::GradKArgs ka{q, k, alpha, b, dq, dk, dalpha, db, p->B, p->T, p->H, (int)p->dk,
-                           (int)nchunks(p), total, (int)p->flags};
+                           nt, total, (int)p->flags, plan, ncmax};
         return launch_status(gdn2::launch_chunk_grad_mf(va, ka, gates_bf16(p), s));
     }
     gdn2::GradArgs ga{q, k, v, alpha, b, w, dO, chk, dsl, dq, dk, dv, dalpha, db, dw, gsc, p->B, p->T, p->H,
-                      (int)p->dk, (int)p->dv, (int)nchunks(p), total};
+                      (int)p->dk, (int)p->dv, nt, total, plan, ncmax};
     return launch_status(gdn2::launch_chunk_grad(ga, is_bf16(p), gates_bf16(p), s));
+}
+
+// The backward once every argument has passed its checks: the prologue
+// mappings (kernels over the token rows, wr.tok of them) around the core.
+// A packed batch's plan is written first, into the workspace's head.
+int bwd_run(const gdn2_problem* p, const BwdWrap& wr, const int32_t* cu_seqlens, const void* q, const void* k,
+            const void* v, const void* alpha, const void* b, const void* w, const float* S0, const void* dO,
+            const float* dS_T, void* dq, void* dk, void* dv, void* dalpha, void* db, void* dw, float* dS0,
+            char* ws, hipStream_t s)
+{
+    int st = GDN2_OK;
+    const int* plan = nullptr;
+    if (cu_seqlens != nullptr) {
+        int* pl = reinterpret_cast<int*>(ws);
+        st = launch_status(gdn2::launch_varlen_plan(gdn2::PlanArgs{cu_seqlens, pl, p->B, p->T, wr.ncmax}, s));
+        if (st) return st;
+        plan = pl;
+    }
+    if (nchunks(p) == 0 || (!wr.qk && !wr.gates))   // no token to map: the core alone
+        return bwd_core(&wr.core, wr.l, plan, wr.ncmax, q, k, v, alpha, b, w, S0, dO, dS_T, dq, dk, dv, dalpha,
+                        db, dw, dS0, ws, s);
+    const void *cq = q, *ck = k, *ca = alpha, *cb = b, *cw = w;
+    void *cdq = dq, *cdk = dk, *cda = dalpha, *cdb = db, *cdw = dw;
+    const int G = (int)(nvh(p) / p->H);
+    const gdn2::QkMapArgs qa{q, k, ws + wr.qh, ws + wr.kh, ws + wr.dqh, ws + wr.dkh, dq, dk,
+                             wr.tok * p->H, G, (int)p->dk, (p->flags & GDN2_FLAG_QK_L2NORM) != 0};
+    if (wr.qk) {
+        st = launch_status(gdn2::launch_bwd_qk_map(qa, false, is_bf16(p), s));
+        if (st) return st;
+        cq = ws + wr.qh; ck = ws + wr.kh; cdq = ws + wr.dqh; cdk = ws + wr.dkh;
+    }
+    const int64_t vrows = wr.tok * nvh(p);
+    const float bscale = (p->flags & GDN2_FLAG_NEG_EIGVAL) ? 2.f : 1.f;
+    float* ga[3] = {reinterpret_cast<float*>(ws + wr.ga), reinterpret_cast<float*>(ws + wr.gb),
+                    reinterpret_cast<float*>(ws + wr.gw)};
+    float* dga[3] = {reinterpret_cast<float*>(ws + wr.dga), reinterpret_cast<float*>(ws + wr.dgb),
+                     reinterpret_cast<float*>(ws + wr.dgw)};
+    if (wr.gates) {
+        const gdn2::GateMapArgs pre{{alpha, b, w}, {nullptr, nullptr, nullptr}, {ga[0], ga[1], ga[2]},
+                                    {vrows * p->dk, vrows * p->dk, vrows * p->dv}, {1.f, bscale, 1.f}};
+        st = launch_status(gdn2::launch_bwd_gate_map(pre, false, gates_bf16(p), s));
+        if (st) return st;
+        ca = ga[0]; cb = ga[1]; cw = ga[2];
+        cda = dga[0]; cdb = dga[1]; cdw = dga[2];
+    }
+    st = bwd_core(&wr.core, wr.l, plan, wr.ncmax, cq, ck, v, ca, cb, cw, S0, dO, dS_T, cdq, cdk, dv, cda, cdb,
+                  cdw, dS0, ws, s);
+    if (st) return st;
+    if (wr.qk) {
+        st = launch_status(gdn2::launch_bwd_qk_map(qa, true, is_bf16(p), s));
+        if (st) return st;
+    }
+    if (wr.gates) {
+        const gdn2::GateMapArgs post{{alpha, b, w}, {dga[0], dga[1], dga[2]}, {dalpha, db, dw},
+                                     {vrows * p->dk, vrows * p->dk, vrows * p->dv}, {1.f, bscale, 1.f}};
+        st = launch_status(gdn2::launch_bwd_gate_map(post, true, gates_bf16(p), s));
+    }
+    return st;
 }
 
 }  // namespace
@@ -883,47 +960,8 @@ int gdn2_chunk_bwd(const gdn2_problem* p, const void* q, const void* k, const vo
     if (nchunks(p) == 0 && dS0 == nullptr) return GDN2_OK;
     st = device_ready();
     if (st) return st;
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    char* ws = static_cast<char*>(workspace);
-    if (nchunks(p) == 0 || (!wr.qk && !wr.gates))   // no token to map: the core alone
-        return bwd_core(&wr.core, wr.l, q, k, v, alpha, b, w, S0, dO, dS_T, dq, dk, dv, dalpha, db, dw, dS0,
-                        ws, s);
-    const void *cq = q, *ck = k, *ca = alpha, *cb = b, *cw = w;
-    void *cdq = dq, *cdk = dk, *cda = dalpha, *cdb = db, *cdw = dw;
-    const int G = (int)(nvh(p) / p->H);
-    const gdn2::QkMapArgs qa{q, k, ws + wr.qh, ws + wr.kh, ws + wr.dqh, ws + wr.dkh, dq, dk,
-                             p->B * p->T * p->H, G, (int)p->dk, (p->flags & GDN2_FLAG_QK_L2NORM) != 0};
-    if (wr.qk) {
-        st = launch_status(gdn2::launch_bwd_qk_map(qa, false, is_bf16(p), s));
-        if (st) return st;
-        cq = ws + wr.qh; ck = ws + wr.kh; cdq = ws + wr.dqh; cdk = ws + wr.dkh;
-    }
-    const int64_t vrows = p->B * p->T * nvh(p);
-    const float bscale = (p->flags & GDN2_FLAG_NEG_EIGVAL) ? 2.f : 1.f;
-    float* ga[3] = {reinterpret_cast<float*>(ws + wr.ga), reinterpret_cast<float*>(ws + wr.gb),
-                    reinterpret_cast<float*>(ws + wr.gw)};
-    float* dga[3] = {reinterpret_cast<float*>(ws + wr.dga), reinterpret_cast<float*>(ws + wr.dgb),
-                     reinterpret_cast<float*>(ws + wr.dgw)};
-    if (wr.gates) {
-        const gdn2::GateMapArgs pre{{alpha, b, w}, {nullptr, nullptr, nullptr}, {ga[0], ga[1], ga[2]},
-                                    {vrows * p->dk, vrows * p->dk, vrows * p->dv}, {1.f, bscale, 1.f}};
-        st = launch_status(gdn2::launch_bwd_gate_map(pre, false, gates_bf16(p), s));
-        if (st) return st;
-        ca = ga[0]; cb = ga[1]; cw = ga[2];
-        cda = dga[0]; cdb = dga[1]; cdw = dga[2];
-    }
-    st = bwd_core(&wr.core, wr.l, cq, ck, v, ca, cb, cw, S0, dO, dS_T, cdq, cdk, dv, cda, cdb, cdw, dS0, ws, s);
-    if (st) return st;
-    if (wr.qk) {
-        st = launch_status(gdn2::launch_bwd_qk_map(qa, true, is_bf16(p), s));
-        if (st) return st;
-    }
-    if (wr.gates) {
-        const gdn2::GateMapArgs post{{alpha, b, w}, {dga[0], dga[1], dga[2]}, {dalpha, db, dw},
-                                     {vrows * p->dk, vrows * p->dk, vrows * p->dv}, {1.f, bscale, 1.f}};
-        st = launch_status(gdn2::launch_bwd_gate_map(post, true, gates_bf16(p), s));
-    }
-    return st;
+    return bwd_run(p, wr, nullptr, q, k, v, alpha, b, w, S0, dO, dS_T, dq, dk, dv, dalpha, db, dw, dS0,
+                   static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
 }
 
 int gdn2_gated_rmsnorm(const gdn2_problem* p, const void* o, const void* g, const float* weight, void* y,
@@ -1028,96 +1066,51 @@ int gdn2_short_conv_bwd(int64_t B, int64_t T, int64_t C, int32_t K, int32_t flag
                                                      static_cast<hipStream_t>(stream)));
 }
 
-// host offsets of a packed batch: rising from 0 to T
-static int check_cu_host(const gdn2_problem* p, const int32_t* cu)
-{
-    if (cu == nullptr) return GDN2_ERR_NULL;
-    if ((reinterpret_cast<uintptr_t>(cu) & 3u) != 0) return GDN2_ERR_ALIGN;
-    if (cu[0] != 0 || cu[p->B] != p->T) return GDN2_ERR_SHAPE;
-    for (int64_t i = 0; i < p->B; ++i)
-        if (cu[i + 1] < cu[i]) return GDN2_ERR_SHAPE;
-    return GDN2_OK;
-}
-
-// the problem of sequence i of a packed batch, as a batch of one
-static gdn2_problem seq_problem(const gdn2_problem* p, const int32_t* cu, int64_t i)
-{
-    gdn2_problem q = *p;
-    q.B = 1;
-    q.T = cu[i + 1] - cu[i];
-    return q;
-}
-
-size_t gdn2_chunk_bwd_varlen_workspace_size(const gdn2_problem* p, const int32_t* cu_seqlens_host)
+size_t gdn2_chunk_bwd_varlen_workspace_size(const gdn2_problem* p)
 {
     if (check_problem(p, true, true) != GDN2_OK) return 0;
-    if (p->B == 0) return 0;
-    if (check_cu_host(p, cu_seqlens_host) != GDN2_OK) return 0;
-    size_t need = 0;
-    for (int64_t i = 0; i < p->B; ++i) {
-        const gdn2_problem q = seq_problem(p, cu_seqlens_host, i);
-        const size_t n = gdn2_chunk_bwd_workspace_size(&q);
-        if (n > need) need = n;
-    }
-    return need;
+    if (p->B * nvh(p) == 0) return 0;
+    return static_cast<size_t>(bwd_wrap(p, true).total);
 }
 
-int gdn2_chunk_bwd_varlen(const gdn2_problem* p, const int32_t* cu_seqlens_host, const void* q, const void* k,
+int gdn2_chunk_bwd_varlen(const gdn2_problem* p, const int32_t* cu_seqlens, const void* q, const void* k,
                           const void* v, const void* alpha, const void* b, const void* w, const float* S0,
                           const void* dO, const float* dS_T, void* dq, void* dk, void* dv, void* dalpha, void* db,
                           void* dw, float* dS0, void* workspace, size_t workspace_bytes, void* stream)
 {
     int st = check_problem(p, true, true);
     if (st) return st;
-    if (p->B * nvh(p) == 0) return GDN2_OK;
-    st = check_cu_host(p, cu_seqlens_host);
+    st = check_cu(p, cu_seqlens);
     if (st) return st;
-    // the packed tensors as a whole: one batch of T tokens, N states
-    gdn2_problem whole = *p;
-    whole.B = 1;
-    st = check_inputs(&whole, q, k, v, alpha, b, w, dO);
-    if (st) return st;
-    if (rows_nonempty(&whole) && (!dq || !dk || !dv || !dalpha || !db || !dw)) return GDN2_ERR_NULL;
-    const int64_t need = (int64_t)gdn2_chunk_bwd_varlen_workspace_size(p, cu_seqlens_host);
+    const bool any = p->B * nvh(p) > 0;
+    if (any) {
+        st = check_inputs(p, q, k, v, alpha, b, w, dO);
+        if (st) return st;
+        if (rows_nonempty(p) && (!dq || !dk || !dv || !dalpha || !db || !dw)) return GDN2_ERR_NULL;
+    }
+    const BwdWrap wr = bwd_wrap(p, true);
+    const int64_t need = any ? wr.total : 0;
     if (need > 0 && (workspace == nullptr || static_cast<int64_t>(workspace_bytes) < need))
         return GDN2_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return GDN2_ERR_WORKSPACE;
-    const Sizes z = sizes_of(&whole);
-    const int64_t states = z.state * p->B;
+    const Sizes z = sizes_of(p, true);
     const Range ins[10] = {range_of(q, z.key),   range_of(k, z.key),  range_of(v, z.val),
                            range_of(alpha, z.gk), range_of(b, z.gk),   range_of(w, z.gv),
-                           range_of(S0, states),  range_of(dO, z.val), range_of(dS_T, states),
-                           range_of(cu_seqlens_host, (p->B + 1) * 4)};
+                           range_of(S0, z.state), range_of(dO, z.val), range_of(dS_T, z.state),
+                           range_of(cu_seqlens, any ? 4 * (p->B + 1) : 0)};
     const Range outs[8] = {range_of(dq, z.key),   range_of(dk, z.key), range_of(dv, z.val),
                            range_of(dalpha, z.gk), range_of(db, z.gk),  range_of(dw, z.gv),
-                           range_of(dS0, states),  range_of(workspace, need)};
+                           range_of(dS0, z.state), range_of(workspace, need)};
     st = check_alias(outs, 8, ins, 10, nullptr, nullptr, -1, -1);
     if (st) return st;
     st = check_align({q, k, v, alpha, b, w, S0, dO, dS_T, dq, dk, dv, dalpha, db, dw, dS0});
     if (st) return st;
-    // sequences are independent: the backward of each slice in turn, all on
-    // `stream`, one workspace reused in stream order
-    const Sizes one = sizes_of(&whole);
-    const int64_t tok = whole.T > 0 ? whole.T : 1;
-    const int64_t key_tok = one.key / tok, val_tok = one.val / tok, gk_tok = one.gk / tok, gv_tok = one.gv / tok;
-    auto at = [](const void* base, int64_t bytes) -> const char* {
-        return base ? static_cast<const char*>(base) + bytes : nullptr;
-    };
-    auto atw = [](void* base, int64_t bytes) -> char* { return base ? static_cast<char*>(base) + bytes : nullptr; };
-    for (int64_t i = 0; i < p->B; ++i) {
-        const gdn2_problem qi = seq_problem(p, cu_seqlens_host, i);
-        const int64_t t0 = cu_seqlens_host[i];
-        const int64_t so = i * z.state;
-        st = gdn2_chunk_bwd(&qi, at(q, t0 * key_tok), at(k, t0 * key_tok), at(v, t0 * val_tok),
-                            at(alpha, t0 * gk_tok), at(b, t0 * gk_tok), at(w, t0 * gv_tok),
-                            reinterpret_cast<const float*>(at(S0, so)), at(dO, t0 * val_tok),
-                            reinterpret_cast<const float*>(at(dS_T, so)), atw(dq, t0 * key_tok),
-                            atw(dk, t0 * key_tok), atw(dv, t0 * val_tok), atw(dalpha, t0 * gk_tok),
-                            atw(db, t0 * gk_tok), atw(dw, t0 * gv_tok), reinterpret_cast<float*>(atw(dS0, so)),
-                            workspace, workspace_bytes, stream);
-        if (st) return st;
-    }
-    return GDN2_OK;
+    if (!any) return GDN2_OK;
+    if (p->T == 0 && dS0 == nullptr) return GDN2_OK;
+    st = device_ready();
+    if (st) return st;
+    return bwd_run(p, wr, cu_seqlens, q, k, v, alpha, b, w, S0, dO, dS_T, dq, dk, dv, dalpha, db, dw, dS0,
+                   static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -202,7 +202,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_state_bwd(BwdStateArgs a)
     const Tio* dOs = reinterpret_cast<const Tio*>(img + IMG);          // [64][VS]
 
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4, wave = tid >> 6;
-    const int dv = a.dv, nt = a.nt;
+    const int dv = a.dv;
     f32x4 accD = {0.f, 0.f, 0.f, 0.f};
     // the slices of one head get block ids congruent mod 8 (one XCD, one L2
     // for the head's factors)
@@ -220,12 +220,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_state_bwd(BwdStateArgs a)
     const int j0 = slice * VS;
     const int64_t bb = chain / a.H, hh = chain - bb * a.H;
     const Tio* dO = static_cast<const Tio*>(a.dO);
+    // the sequence's tokens, chunk count and first block
+    const ChainSpan sp = chain_span(a.plan, a.ncmax, a.B, a.T, a.H, a.nt, bb, hh);
+    const int nt = sp.nt;
 
     f32x4 pre[NPT];
     auto fetch = [&](int n) {
-        const char* blk = static_cast<const char*>(a.ws) + (chain * nt + n) * a.ws_block;
+        const char* blk = static_cast<const char*>(a.ws) + (sp.blk0 + n) * a.ws_block;
         const int64_t t0 = (int64_t)n * kChunk;
-        const int L = (int)(a.T - t0 < kChunk ? a.T - t0 : kChunk);
+        const int L = (int)(sp.tlen - t0 < kChunk ? sp.tlen - t0 : kChunk);
 #pragma unroll
         for (int i = 0; i < NPT; ++i) {
             const int gi = tid + i * kThreads;
@@ -236,7 +239,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_state_bwd(BwdStateArgs a)
                 const int r = (gi - IMG / 16) / GROW, g = (gi - IMG / 16) % GROW;
                 if (r < L)
                     x = *reinterpret_cast<const f32x4*>(
-                        dO + ((bb * a.T + t0 + r) * a.H + hh) * dv + j0 + g * (16 / ES));
+                        dO + ((sp.tok0 + t0 + r) * a.H + hh) * dv + j0 + g * (16 / ES));
             }
             pre[i] = x;
         }
@@ -259,7 +262,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_state_bwd(BwdStateArgs a)
         stash();
         // the gradient this chunk's exit state receives
         if (a.dSL != nullptr) {
-            float* dsl = a.dSL + (chain * nt + n) * (int64_t)DK * dv + j0;
+            float* dsl = a.dSL + (sp.blk0 + n) * (int64_t)DK * dv + j0;
             for (int i = tid; i < DK * VS / 4; i += kThreads) {
                 const int c = i / NCG, g = i - c * NCG;
                 *reinterpret_cast<f32x4*>(dsl + (int64_t)c * dv + 4 * g) = *reinterpret_cast<const f32x4*>(&dS[c * VS + 4 * g]);
@@ -267,7 +270,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_state_bwd(BwdStateArgs a)
         }
         if (a.dSLIo != nullptr) {
             // the same in the I/O dtype
-            Tio* dsl = static_cast<Tio*>(a.dSLIo) + (chain * nt + n) * (int64_t)DK * dv + j0;
+            Tio* dsl = static_cast<Tio*>(a.dSLIo) + (sp.blk0 + n) * (int64_t)DK * dv + j0;
             for (int i = tid; i < DK * VS / 4; i += kThreads) {
                 const int c = i / NCG, g = i - c * NCG;
                 st_vec4(dsl + (int64_t)c * dv + 4 * g, *reinterpret_cast<const f32x4*>(&dS[c * VS + 4 * g]));
@@ -275,7 +278,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_chunk_state_bwd(BwdStateArgs a)
         }
         if (a.dSLT != nullptr) {
             // and transposed, [dv][dk] in the I/O dtype
-            Tio* dslT = static_cast<Tio*>(a.dSLT) + (chain * nt + n) * (int64_t)DK * dv;
+            Tio* dslT = static_cast<Tio*>(a.dSLT) + (sp.blk0 + n) * (int64_t)DK * dv;
             for (int i = tid; i < DK * VS / 4; i += kThreads) {
                 const int j = i / (DK / 4), c4 = 4 * (i - j * (DK / 4));
                 const f32x4 x = {dS[c4 * VS + j], dS[(c4 + 1) * VS + j], dS[(c4 + 2) * VS + j], dS[(c4 + 3) * VS + j]};
@@ -363,7 +366,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_grad(GradArgs a)
 {
     __shared__ GemmLds gl;
     const int tid = threadIdx.x;
-    const int dk = a.dk, dv = a.dv, nt = a.nt;
+    const int dk = a.dk, dv = a.dv;
     const int KA = 64 * dk, VA = 64 * dv, QA = 64 * 64;
     float* sc = a.scratch + blockIdx.x * grad_scratch_floats(dk, dv);
     // 64 x dk arrays
@@ -390,13 +393,11 @@ __global__ __launch_bounds__(kThreads) void k_chunk_grad(GradArgs a)
     Tg* db = static_cast<Tg*>(a.db);
     Tg* dw = static_cast<Tg*>(a.dw);
 
-    for (int64_t ci = blockIdx.x; ci < a.total; ci += gridDim.x) {
-        const int64_t chain = ci / nt;
-        const int n = (int)(ci - chain * nt);
-        const int64_t bb = chain / a.H, hh = chain - bb * a.H;
-        const int64_t t0 = (int64_t)n * kChunk;
-        const int L = (int)(a.T - t0 < kChunk ? a.T - t0 : kChunk);
-        const int64_t row0 = (bb * a.T + t0) * a.H + hh;        // row of token t0
+    for (int64_t ci = blockIdx.x; ci < a.total; ci += gridDim.x) {   // ci: workspace block
+        ChunkPos cp;
+        if (!chunk_pos(a.plan, a.ncmax, a.B, a.T, a.H, a.nt, ci, cp)) continue;   // past a packed batch's chunks
+        const int L = cp.len;
+        const int64_t row0 = cp.tok0 * a.H + cp.hh;             // row of the chunk's first token
         const int64_t H = a.H;
         const float* S0 = a.S_chk + ci * (int64_t)dk * dv;      // [dk][dv]
         const float* dSL = a.dSL + ci * (int64_t)dk * dv;

@@ -233,15 +233,13 @@ __device__ __attribute__((always_inline)) inline void grad_val_chunk(const GradV
 
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
     const int wave = tid >> 6;
-    const int nt = a.nt;
-    const int64_t ci = blockIdx.x;
-    const int64_t chain = ci / nt;
-    const int n = (int)(ci - chain * nt);
-    const int64_t bb = chain / a.H, hh = chain - bb * a.H;
-    const int64_t t0 = (int64_t)n * kChunk;
-    const int Ln = (int)(a.T - t0 < kChunk ? a.T - t0 : kChunk);
+    const int64_t ci = blockIdx.x;                   // workspace block (valid: checked by the kernel)
+    ChunkPos cp;
+    chunk_pos(a.plan, a.ncmax, a.B, a.T, a.H, a.nt, ci, cp);
+    const int64_t hh = cp.hh;
+    const int Ln = cp.len;
     const int64_t H = a.H;
-    const int64_t row0 = (bb * a.T + t0) * H + hh;
+    const int64_t row0 = cp.tok0 * H + hh;
     constexpr WsLayout LY = ws_layout(DK, DV, 2, 32);
     const char* blk = static_cast<const char*>(a.ws) + ci * a.ws_block;
     const bf* Tg_ = reinterpret_cast<const bf*>(blk + a.t_off);         // T [64][64]
@@ -700,15 +698,13 @@ __device__ __attribute__((always_inline)) inline void grad_key_chunk(const GradK
 
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
     const int wave = tid >> 6;
-    const int nt = a.nt;
-    const int64_t ci = blockIdx.x;
-    const int64_t chain = ci / nt;
-    const int n = (int)(ci - chain * nt);
-    const int64_t bb = chain / a.H, hh = chain - bb * a.H;
-    const int64_t t0 = (int64_t)n * kChunk;
-    const int Ln = (int)(a.T - t0 < kChunk ? a.T - t0 : kChunk);
+    const int64_t ci = blockIdx.x;                   // workspace block (valid: checked by the kernel)
+    ChunkPos cp;
+    chunk_pos(a.plan, a.ncmax, a.B, a.T, a.H, a.nt, ci, cp);
+    const int64_t hh = cp.hh;
+    const int Ln = cp.len;
     const int64_t H = a.H;
-    const int64_t row0 = (bb * a.T + t0) * H + hh;
+    const int64_t row0 = cp.tok0 * H + hh;
     const bf* qg = static_cast<const bf*>(a.q);
     const bf* kg = static_cast<const bf*>(a.k);
     const Tg* agt = static_cast<const Tg*>(a.alpha);
@@ -995,6 +991,8 @@ __global__ __launch_bounds__(kGvThreads, 1) void k_chunk_grad_mf(GradVArgs v, Gr
     constexpr int BYTES = B0 > HandLds<DK>::BYTES ? B0 : HandLds<DK>::BYTES;
     static_assert(BYTES <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(16))) char sm[BYTES];
+    ChunkPos cp;
+    if (!chunk_pos(v.plan, v.ncmax, v.B, v.T, v.H, v.nt, blockIdx.x, cp)) return;   // past a packed batch's chunks
     grad_val_chunk<DK, DV, Tg>(v, sm);
     __syncthreads();                       // the hand-over written
     grad_key_chunk<DK, Tg>(k, sm);
@@ -1066,7 +1064,7 @@ __global__ __launch_bounds__(RsLds<DK>::THREADS, 1) void k_chunk_state_bwd_mf(Bw
 
     const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int dv = a.dv, nt = a.nt;
+    const int dv = a.dv;
     const int64_t nch = a.B * a.H, x = blockIdx.x;
     const int ns = a.nslices;
     int64_t chain;
@@ -1080,6 +1078,9 @@ __global__ __launch_bounds__(RsLds<DK>::THREADS, 1) void k_chunk_state_bwd_mf(Bw
     }
     const int j0 = slice * VS;
     const int64_t bb = chain / a.H, hh = chain - bb * a.H;
+    // the sequence's tokens, chunk count and first block
+    const ChainSpan sp = chain_span(a.plan, a.ncmax, a.B, a.T, a.H, a.nt, bb, hh);
+    const int nt = sp.nt;
 
     if (wave >= NCW) {
         // ---------------- loader waves ------------------------------------
@@ -1130,11 +1131,11 @@ __global__ __launch_bounds__(RsLds<DK>::THREADS, 1) void k_chunk_state_bwd_mf(Bw
         // the end load chunk 0 again (every step issues the same loads)
         auto fetch = [&](int i, bfrag* rs, int m0, int m1) {
             const int n = nt - 1 - i < 0 ? 0 : nt - 1 - i;
-            const char* blk = static_cast<const char*>(a.ws) + (chain * nt + n) * a.ws_block;
+            const char* blk = static_cast<const char*>(a.ws) + (sp.blk0 + n) * a.ws_block;
             const int64_t t0 = (int64_t)n * kChunk;
-            const int Ln = (int)(a.T - t0 < kChunk ? a.T - t0 : kChunk);
+            const int Ln = (int)(sp.tlen - t0 < kChunk ? sp.tlen - t0 : kChunk);
             const int rc = dr < Ln ? dr : Ln - 1;
-            const char* pd = reinterpret_cast<const char*>(dO + ((bb * a.T + t0 + rc) * a.H + hh) * dv + j0 + dc);
+            const char* pd = reinterpret_cast<const char*>(dO + ((sp.tok0 + t0 + rc) * a.H + hh) * dv + j0 + dc);
 #pragma unroll
             for (int m = 0; m < LPL; ++m)
                 if (m >= m0 && m < m1)
@@ -1148,7 +1149,7 @@ __global__ __launch_bounds__(RsLds<DK>::THREADS, 1) void k_chunk_state_bwd_mf(Bw
                     if (m == 0 && dol) {                    // dO^T, zero past the end
                         const int n = nt - 1 - i < 0 ? 0 : nt - 1 - i;
                         const int64_t t0 = (int64_t)n * kChunk;
-                        const int Ln = (int)(a.T - t0 < kChunk ? a.T - t0 : kChunk);
+                        const int Ln = (int)(sp.tlen - t0 < kChunk ? sp.tlen - t0 : kChunk);
                         bf* ot = reinterpret_cast<bf*>(b0 + L::OT);
 #pragma unroll
                         for (int e = 0; e < 8; ++e) ot[(dc + e) * RP + dr] = dr < Ln ? rs[0][e] : (bf)0.f;
@@ -1162,7 +1163,7 @@ __global__ __launch_bounds__(RsLds<DK>::THREADS, 1) void k_chunk_state_bwd_mf(Bw
         // (dS^T rows [dv][dk], dS rows [dk][dv]): granule q < G_CK of dS^T,
         // then of dS
         auto ckpt = [&](int i) {
-            const int64_t cb = (chain * nt + (nt - 1 - i)) * (int64_t)DK * dv;
+            const int64_t cb = (sp.blk0 + (nt - 1 - i)) * (int64_t)DK * dv;
 #pragma unroll
             for (int q0 = 0; q0 < 2 * L::G_CK; q0 += L::NLD) {
                 const int q = q0 + lw * 64 + lane;

@@ -905,22 +905,11 @@ __global__ __launch_bounds__(state_threads(VS, (int)sizeof(Tio)), 1) void k_chun
     const int dv = a.dv;
     if (a.conv_out != nullptr && a.conv_K > 1 && slice == 0) conv_window_out<Tio, DK>(a, bb, hh);
     // the sequence's first packed token, its length, chunk count and first
-    // workspace block
-    int64_t tok0, tlen;
-    int nt;
-    const char* wsbase;
-    if (a.plan == nullptr) {
-        tok0 = bb * a.T;
-        tlen = a.T;
-        nt = a.nt;
-        wsbase = static_cast<const char*>(a.ws) + chain * (int64_t)nt * a.ws_block;
-    } else {
-        const int* first = a.plan + (a.B + 1);
-        tok0 = a.plan[bb];
-        tlen = a.plan[bb + 1] - tok0;
-        nt = first[bb + 1] - first[bb];
-        wsbase = static_cast<const char*>(a.ws) + (hh * a.ncmax + first[bb]) * a.ws_block;
-    }
+    // workspace block (checkpoints follow the blocks)
+    const ChainSpan sp = chain_span(a.plan, a.ncmax, a.B, a.T, a.H, a.nt, bb, hh);
+    const int64_t tok0 = sp.tok0, tlen = sp.tlen, blk0 = sp.blk0;
+    const int nt = sp.nt;
+    const char* wsbase = static_cast<const char*>(a.ws) + blk0 * a.ws_block;
 
     if (loader) {
         // ---------------- loader waves ------------------------------------
@@ -993,7 +982,7 @@ __global__ __launch_bounds__(state_threads(VS, (int)sizeof(Tio)), 1) void k_chun
             if constexpr (CKL) {
                 constexpr int GR = DK * ES / 16, GN = VS * ES / 16, EG = 16 / ES;
                 constexpr int G1 = VS * GR, G2 = DK * GN;
-                const int64_t cb = (chain * (int64_t)nt + n) * DK * dv;
+                const int64_t cb = (blk0 + n) * DK * dv;
 #pragma unroll
                 for (int q0 = 0; q0 < G1 + G2; q0 += L::NLD) {
                     const int q = q0 + (wave - NCW) * 64 + lane;
@@ -1104,7 +1093,7 @@ __global__ __launch_bounds__(state_threads(VS, (int)sizeof(Tio)), 1) void k_chun
             // transpose inside each lane quad gives every lane 4 consecutive
             // columns of one row, written as one vector.
             if (a.S_chk != nullptr) {
-                const int64_t base = (chain * (int64_t)nt + n) * DK * dv + j0 + jc + (l16 & ~3);
+                const int64_t base = (blk0 + n) * DK * dv + j0 + jc + (l16 & ~3);
 #pragma unroll
                 for (int i = 0; i < SPW; ++i) {
                     const int rt = tb * SPW + i;

@@ -242,4 +242,57 @@ __device__ inline float keep_or_zero(float x, bool keep)
     return __uint_as_float(__float_as_uint(x) & (0u - (unsigned)keep));
 }
 
+// ---------------------------------------------------------------------------
+// Where chunks lie in the token tensors and the workspace.  Equal-length
+// batches (plan == nullptr): chain (sequence bb, value head hh) owns tokens
+// bb*T .. bb*T+T-1 and blocks (bb*H + hh)*nt .. +nt-1.  Packed batches: the
+// table k_varlen_plan writes, clamped offsets cu[B+1], first chunks
+// first[B+1] (first[B] = the chunk count), then from word 2(B+1) one
+// {first token, length} pair per chunk; chunk c of head hh owns block
+// hh*ncmax + c.  Every per-chunk array (factors, checkpoints, exit
+// gradients) is indexed by that block number.
+// ---------------------------------------------------------------------------
+struct ChainSpan {
+    int64_t tok0;   // packed index of the sequence's first token
+    int64_t tlen;   // its token count
+    int64_t blk0;   // block of its first chunk
+    int nt;         // its chunk count
+};
+
+__device__ inline ChainSpan chain_span(const int* plan, int64_t ncmax, int64_t B, int64_t T, int64_t H, int nt,
+                                       int64_t bb, int64_t hh)
+{
+    if (plan == nullptr) return ChainSpan{bb * T, T, (bb * H + hh) * nt, nt};
+    const int* first = plan + (B + 1);
+    return ChainSpan{plan[bb], (int64_t)plan[bb + 1] - plan[bb], hh * ncmax + first[bb], first[bb + 1] - first[bb]};
+}
+
+// block ci of a launch with one workgroup per block: its value head, the
+// packed index of its first token and its token count; false for the blocks
+// of a packed batch past its last chunk
+struct ChunkPos {
+    int64_t hh, tok0;
+    int len;
+};
+
+__device__ inline bool chunk_pos(const int* plan, int64_t ncmax, int64_t B, int64_t T, int64_t H, int nt, int64_t ci,
+                                 ChunkPos& c)
+{
+    if (plan == nullptr) {
+        const int64_t chain = ci / nt, bb = chain / H;
+        const int64_t t0 = (ci - chain * nt) * (int64_t)kChunk;
+        c.hh = chain - bb * H;
+        c.tok0 = bb * T + t0;
+        c.len = (int)(T - t0 < kChunk ? T - t0 : kChunk);
+        return true;
+    }
+    c.hh = ci / ncmax;
+    const int64_t gc = ci - c.hh * ncmax;
+    if (gc >= plan[2 * B + 1]) return false;
+    const int2 e = reinterpret_cast<const int2*>(plan + 2 * (B + 1))[gc];
+    c.tok0 = e.x;
+    c.len = e.y;
+    return true;
+}
+
 }  // namespace gdn2

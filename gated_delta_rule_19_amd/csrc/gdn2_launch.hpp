@@ -32,9 +32,9 @@ struct PrepArgs {
     const float* conv_w; const void* conv_in; int64_t conv_C; int conv_K; int conv_silu;
 };
 
-// Checkpoints (optional, equal-length batches only): the state entering every
-// chunk, [B*H][nt][dk][dv] in fp32 (S_chk) or in the I/O dtype (S_chkIo), and
-// its transpose in the I/O dtype, S_chkT [B*H][nt][dv][dk]; each may be null.
+// Checkpoints (optional): the state entering every chunk, [dk][dv] per
+// workspace block in fp32 (S_chk) or in the I/O dtype (S_chkIo), and its
+// transpose in the I/O dtype, S_chkT [dv][dk] per block; each may be null.
 // o may be null when only states are wanted.
 struct StateArgs {
     const void* ws; int64_t ws_block;
@@ -68,23 +68,27 @@ struct RecArgs {
     const float* conv_w; const void* conv_in; void* conv_out; int64_t conv_C; int conv_K; int conv_silu;
 };
 
-// Backward (equal-length batches, H value heads = query/key heads).  Reverse
-// state pass: per (batch, head, slice of vs value columns), reads the forward
-// workspace, dO and dS_T (nullable), writes the gradient each chunk's exit
-// state receives, [B*H][nt][dk][dv] in fp32 (dSL) and/or in the I/O dtype
-// (dSLIo), each nullable, and dS0 (nullable).
+// Backward (H value heads = query/key heads; equal-length batches, or a
+// packed batch through `plan` and ncmax as for the forward, each chunk's
+// per-chunk arrays at its workspace block number).  Reverse state pass: per
+// (sequence, head, slice of vs value columns), reads the forward workspace,
+// dO and dS_T (nullable), writes the gradient each chunk's exit state
+// receives, [dk][dv] per block in fp32 (dSL) and/or in the I/O dtype (dSLIo),
+// each nullable, and dS0 (nullable).
 struct BwdStateArgs {
     const void* ws; int64_t ws_block;
     const void* dO; const float* dS_T; float* dSL; float* dS0;
     int64_t B, T, H; int dk, dv, nt, nslices, vs;
-    void* dSLT;             // optional: the same transposed, [B*H][nt][dv][dk], I/O dtype
+    void* dSLT;             // optional: the same transposed, [dv][dk] per block, I/O dtype
     void* dSLIo;
     int64_t t_off;          // matrix-core pass: the blocks' backward extension (BwdExt) starts here
+    const int* plan; int64_t ncmax;
 };
 
 // Per-chunk gradients: inputs, dO, the chunk entry states S_chk and exit
-// gradients dSL ([B*H][nt][dk][dv] fp32); writes dq, dk, dv (I/O dtype) and
-// dalpha, db, dw (gate dtype).  scratch: fp32 per workgroup.
+// gradients dSL ([dk][dv] fp32 per block); writes dq, dk, dv (I/O dtype) and
+// dalpha, db, dw (gate dtype).  scratch: fp32 per workgroup.  total = the
+// block count (B*H*nt, or H*ncmax with a plan).
 struct GradArgs {
     const void* q; const void* k; const void* v;
     const void* alpha; const void* b; const void* w; const void* dO;
@@ -92,6 +96,7 @@ struct GradArgs {
     void* dq; void* dk_out; void* dv_out; void* dalpha; void* db; void* dw;
     float* scratch;
     int64_t B, T, H; int dk, dv, nt; int64_t total;
+    const int* plan; int64_t ncmax;
 };
 
 // Matrix-core per-chunk gradients, one launch of two stages (bf16 I/O; with
@@ -108,6 +113,7 @@ struct GradVArgs {
     void* dw; void* dv_out;
     int64_t B, T, H; int dk, dv, nt; int64_t total;
     int flags;              // prologue options applied in-kernel (gradients of the logits, raw q/k)
+    const int* plan; int64_t ncmax;
 };
 
 struct GradKArgs {
@@ -115,6 +121,7 @@ struct GradKArgs {
     void* dq; void* dk_out; void* dalpha; void* db;
     int64_t B, T, H; int dk, nt; int64_t total;
     int flags;
+    const int* plan; int64_t ncmax;
 };
 
 // Prologue options in the backward.  Query/key rows (rows = B*T*Hk of dk

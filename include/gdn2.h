@@ -90,7 +90,7 @@
 extern "C" {
 #endif
 
-#define GDN2_ABI_VERSION 7
+#define GDN2_ABI_VERSION 8
 
 typedef enum {
     GDN2_OK = 0,
@@ -323,29 +323,28 @@ int gdn2_chunk_bwd(const gdn2_problem* p,
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Backward of gdn2_chunk_fwd_varlen (packed batches, layouts and p->B = N,
- * p->T = total tokens as described above).  The gradients and their
+ * Backward of gdn2_chunk_fwd_varlen (packed batches, layouts, p->B = N,
+ * p->T = total tokens and cu_seqlens in DEVICE memory exactly as for that
+ * call, the same offsets clamped the same way).  The gradients and their
  * meaning are those of gdn2_chunk_bwd, per sequence: dq, dk, dalpha, db,
  * dw, dv in the packed layouts of the inputs, dS0 [N, Hv, dk, dv] (NULL =
- * not wanted); S0 and dS_T [N, Hv, dk, dv] or NULL (zero).
- * cu_seqlens_host: the N+1 offsets in HOST memory (4-byte aligned), checked
- * on the host: they must rise from 0 to T (GDN2_ERR_SHAPE otherwise).
- * NOTE: this differs from gdn2_chunk_fwd_varlen, whose cu_seqlens is in
- * DEVICE memory: pass the backward a host copy of the forward's offsets
- * (the backward sizes its workspace and launches per sequence from them);
- * a device pointer here would be read by the host.
- * Sequences are independent, so the call runs the chunked backward on each
- * sequence's contiguous slice in turn, all launches on `stream` (those of
- * gdn2_chunk_bwd, a sequence at a time; an empty sequence only passes dS_T
- * through to dS0).  The workspace (256-byte aligned, at least
- * gdn2_chunk_bwd_varlen_workspace_size(p, cu_seqlens_host) bytes, the
- * largest single sequence's need) is reused by the sequences in stream
- * order.  Aliasing and alignment are checked over the packed tensors as a
- * whole; the offsets count as an input.
+ * not wanted); S0 and dS_T [N, Hv, dk, dv] or NULL (zero).  An empty
+ * sequence passes its dS_T through to dS0.
+ * The whole batch runs in the launches of gdn2_chunk_bwd plus the
+ * one-workgroup plan of gdn2_chunk_fwd_varlen, written into the head of the
+ * workspace: every per-chunk kernel takes one workgroup per (value head,
+ * chunk slot) and finds its sequence and tokens in the plan, and every
+ * state pass one workgroup per (sequence, value head, column slice), so
+ * the launch count does not grow with N.  The workspace (256-byte aligned,
+ * at least gdn2_chunk_bwd_varlen_workspace_size(p) bytes, which depends on
+ * N and T only) holds the plan and gdn2_chunk_bwd's arrays for
+ * ceil(T/64) + N chunk slots per value head.  Aliasing and alignment are
+ * checked over the packed tensors as a whole; the offsets count as an
+ * input.
  */
-size_t gdn2_chunk_bwd_varlen_workspace_size(const gdn2_problem* p, const int32_t* cu_seqlens_host);
+size_t gdn2_chunk_bwd_varlen_workspace_size(const gdn2_problem* p);
 
-int gdn2_chunk_bwd_varlen(const gdn2_problem* p, const int32_t* cu_seqlens_host,
+int gdn2_chunk_bwd_varlen(const gdn2_problem* p, const int32_t* cu_seqlens,
                           const void* q, const void* k, const void* v,
                           const void* alpha, const void* b, const void* w,
                           const float* S0, const void* dO, const float* dS_T,

@@ -287,26 +287,37 @@ void backward_cases()
             expect("bwd dq over dk", bwd(dkk, ws, wsb), GDN2_ERR_ALIAS);
             expect("bwd dq over q", bwd(t.q, ws, wsb), GDN2_ERR_ALIAS);
             expect("bwd workspace short", bwd(dq, ws, wsb - 1), GDN2_ERR_WORKSPACE);
-            // packed batch with host offsets: 3 sequences of 40, 0 and 220 tokens
+            // packed batch: 3 sequences of 40, 0 and 220 tokens, offsets in
+            // (stand-in) device memory
             gdn2_problem pv = p;
             pv.B = 3;
             pv.T = 260;
-            const int32_t cu_host[4] = {0, 40, 40, 260};
-            const size_t wsv = gdn2_chunk_bwd_varlen_workspace_size(&pv, cu_host);
+            int32_t* cu = static_cast<int32_t*>(stub::dev_alloc(16));
+            const size_t wsv = gdn2_chunk_bwd_varlen_workspace_size(&pv);
+            if (wsv == 0) {
+                std::fprintf(stderr, "FAIL bwd varlen workspace size 0\n");
+                ++g_bad;
+            }
             void* wsvp = stub::dev_alloc(wsv);
             float* S0v = static_cast<float*>(stub::dev_alloc(3 * hv * dk * dv * 4));
             float* dSTv = static_cast<float*>(stub::dev_alloc(3 * hv * dk * dv * 4));
             float* dS0v = static_cast<float*>(stub::dev_alloc(3 * hv * dk * dv * 4));
-            auto bv = [&](const int32_t* c, size_t n) {
-                return gdn2_chunk_bwd_varlen(&pv, c, t.q, t.k, t.v, t.alpha, t.b, t.w, S0v, dO, dSTv, dq, dkk, dvv,
+            auto bv = [&](const gdn2_problem* pp, const int32_t* c, void* dqx, size_t n) {
+                return gdn2_chunk_bwd_varlen(pp, c, t.q, t.k, t.v, t.alpha, t.b, t.w, S0v, dO, dSTv, dqx, dkk, dvv,
                                              da, db, dw, dS0v, wsvp, n, nullptr);
             };
-            expect("bwd varlen valid", bv(cu_host, wsv), GDN2_OK, 3, 1000);
-            const int32_t decreasing[4] = {0, 50, 40, 260};
-            expect("bwd varlen decreasing offsets", bv(decreasing, wsv), GDN2_ERR_SHAPE);
-            const int32_t past_end[4] = {0, 40, 40, 261};
-            expect("bwd varlen offsets past T", bv(past_end, wsv), GDN2_ERR_SHAPE);
-            expect("bwd varlen null offsets", bv(nullptr, wsv), GDN2_ERR_NULL);
+            expect("bwd varlen valid", bv(&pv, cu, dq, wsv), GDN2_OK, 4, 1000);
+            expect("bwd varlen workspace short", bv(&pv, cu, dq, wsv - 1), GDN2_ERR_WORKSPACE);
+            expect("bwd varlen offsets over dq", bv(&pv, reinterpret_cast<const int32_t*>(dq), dq, wsv),
+                   GDN2_ERR_ALIAS);
+            expect("bwd varlen offsets misaligned",
+                   bv(&pv, reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(cu) + 2), dq, wsv),
+                   GDN2_ERR_ALIGN);
+            // no tokens: the plan and the reverse pass (dS_T through to dS0)
+            gdn2_problem p0 = pv;
+            p0.T = 0;
+            expect("bwd varlen no tokens", bv(&p0, cu, dq, gdn2_chunk_bwd_varlen_workspace_size(&p0)), GDN2_OK, 2, 2);
+            expect("bwd varlen null offsets", bv(&pv, nullptr, dq, wsv), GDN2_ERR_NULL);
         }
     }
 }

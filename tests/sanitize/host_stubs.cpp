@@ -143,20 +143,23 @@ hipError_t launch_chunk_prep(const PrepArgs& a, int dk, bool bf16, bool gbf16, h
     return hipSuccess;
 }
 
-hipError_t launch_chunk_state(const StateArgs& a, int dk, int vs, bool, hipStream_t)
+hipError_t launch_chunk_state(const StateArgs& a, int dk, int vs, bool bf16, hipStream_t)
 {
     ++g_launches;
     const char* h = "launch_chunk_state";
     if (vs <= 0 || a.dv % vs != 0 || a.nslices * vs != a.dv) fail(h, "value slices");
     const int64_t nblk = a.plan ? a.H * a.ncmax : a.B * a.H * a.nt;
-    if (a.nt > 0) in_buf(h, "workspace blocks", a.ws, nblk * a.ws_block, true);
+    const bool any = a.plan ? a.T > 0 : a.nt > 0;
+    if (any) in_buf(h, "workspace blocks", a.ws, nblk * a.ws_block, true);
+    in_buf(h, "plan", a.plan, 0);
     const int64_t st = a.B * a.H * dk * a.dv * 4;   // B counts sequences in a packed batch
     in_buf(h, "S0", a.S0, st);
     in_buf(h, "S_out", a.S_out, st);
     in_buf(h, "o", a.o, 0);
-    in_buf(h, "S_chk", a.S_chk, a.B * a.H * a.nt * dk * a.dv * 4);
-    in_buf(h, "S_chkT", a.S_chkT, 0);
-    in_buf(h, "S_chkIo", a.S_chkIo, 0);
+    // checkpoints: one [dk][dv] per workspace block
+    in_buf(h, "S_chk", a.S_chk, nblk * dk * a.dv * 4);
+    in_buf(h, "S_chkT", a.S_chkT, nblk * dk * a.dv * (bf16 ? 2 : 4));
+    in_buf(h, "S_chkIo", a.S_chkIo, nblk * dk * a.dv * (bf16 ? 2 : 4));
     if (a.conv_out != nullptr) {
         for (const void* p : {a.cq, a.ck, a.cv}) in_buf(h, "conv input", p, 0, a.T > 0);   // read only at positions >= 0
         in_buf(h, "conv window in", a.conv_in, a.B * (a.conv_K - 1) * a.conv_C * 2);
@@ -234,14 +237,21 @@ hipError_t launch_varlen_plan(const PlanArgs& a, hipStream_t)
     return hipSuccess;
 }
 
-hipError_t launch_chunk_state_bwd(const BwdStateArgs& a, bool, hipStream_t)
+hipError_t launch_chunk_state_bwd(const BwdStateArgs& a, bool bf16, hipStream_t)
 {
     ++g_launches;
-    in_buf("launch_chunk_state_bwd", "workspace blocks", a.ws, a.B * a.H * a.nt * a.ws_block, a.nt > 0);
-    in_buf("launch_chunk_state_bwd", "dO", a.dO, 0, a.nt > 0);
-    in_buf("launch_chunk_state_bwd", "dSL", a.dSL, a.B * a.H * a.nt * a.dk * a.dv * 4);
-    in_buf("launch_chunk_state_bwd", "dS0", a.dS0, a.B * a.H * a.dk * a.dv * 4);
-    in_buf("launch_chunk_state_bwd", "dS_T", a.dS_T, a.B * a.H * a.dk * a.dv * 4);
+    const char* h = "launch_chunk_state_bwd";
+    const int64_t nblk = a.plan ? a.H * a.ncmax : a.B * a.H * a.nt;
+    const bool any = a.plan ? a.T > 0 : a.nt > 0;
+    if (a.plan != nullptr && a.nt != 0) fail(h, "chunk count with a plan");
+    in_buf(h, "plan", a.plan, 4 * plan_head_words(a.B) + 8 * a.ncmax);
+    in_buf(h, "workspace blocks", a.ws, nblk * a.ws_block, any);
+    in_buf(h, "dO", a.dO, 0, any);
+    in_buf(h, "dSL", a.dSL, nblk * a.dk * a.dv * 4);
+    in_buf(h, "dSLIo", a.dSLIo, nblk * a.dk * a.dv * (bf16 ? 2 : 4));
+    in_buf(h, "dSLT", a.dSLT, nblk * a.dk * a.dv * (bf16 ? 2 : 4));
+    in_buf(h, "dS0", a.dS0, a.B * a.H * a.dk * a.dv * 4);
+    in_buf(h, "dS_T", a.dS_T, a.B * a.H * a.dk * a.dv * 4);
     return hipSuccess;
 }
 
@@ -285,6 +295,8 @@ hipError_t launch_chunk_grad(const GradArgs& a, bool, bool, hipStream_t)
     const char* h = "launch_chunk_grad";
     for (const void* p : {a.q, a.k, a.v, a.alpha, a.b, a.w, a.dO}) in_buf(h, "input", p, 0, true);
     for (void* p : {a.dq, a.dk_out, a.dv_out, a.dalpha, a.db, a.dw}) in_buf(h, "output", p, 0, true);
+    if (a.total != (a.plan ? a.H * a.ncmax : a.B * a.H * a.nt)) fail(h, "block count");
+    in_buf(h, "plan", a.plan, 4 * plan_head_words(a.B) + 8 * a.ncmax);
     in_buf(h, "S_chk", a.S_chk, a.total * a.dk * a.dv * 4, true);
     in_buf(h, "dSL", a.dSL, a.total * a.dk * a.dv * 4, true);
     in_buf(h, "scratch", a.scratch, chunk_grad_scratch_bytes(a.dk, a.dv, a.total), true);
@@ -295,8 +307,13 @@ hipError_t launch_chunk_grad_mf(const GradVArgs& v, const GradKArgs& k, bool, hi
 {
     ++g_launches;
     const char* h = "launch_chunk_grad_mf";
+    if (v.total != (v.plan ? v.H * v.ncmax : v.B * v.H * v.nt) || k.total != v.total || k.plan != v.plan ||
+        k.ncmax != v.ncmax)
+        fail(h, "block count");
+    in_buf(h, "plan", v.plan, 4 * plan_head_words(v.B) + 8 * v.ncmax);
     in_buf(h, "workspace blocks", v.ws, v.total * v.ws_block, true);
-    for (const void* p : {v.v, v.w, v.dO, v.S_chk, v.S_chkT, v.dSL, v.dSLT}) in_buf(h, "input", p, 0, true);
+    for (const void* p : {v.S_chk, v.S_chkT, v.dSL, v.dSLT}) in_buf(h, "checkpoint", p, v.total * v.dk * v.dv * 2, true);
+    for (const void* p : {v.v, v.w, v.dO}) in_buf(h, "input", p, 0, true);
     for (const void* p : {k.q, k.k, k.alpha, k.b}) in_buf(h, "input", p, 0, true);
     for (void* p : {v.dw, v.dv_out, k.dq, k.dk_out, k.dalpha, k.db}) in_buf(h, "output", p, 0, true);
     return hipSuccess;

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert g.abi_version() == 7
+    assert g.abi_version() == 8
     for code in range(8):
         assert g.status_str(code).startswith(bnd._STATUS[code])
     assert "unknown" in g.status_str(99)

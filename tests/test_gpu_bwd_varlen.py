@@ -9,8 +9,11 @@ value heads (Hv = 2H) and the in-kernel prologue (gate logits, b x 2, q/k L2 nor
 expected gradients are ``oracle.backward.full_bwd`` of each sequence (pinned by finite
 differences of the whole forward with its prologue).
 
-The offsets are read on the host (``cu_seqlens`` is copied there by the binding), unlike
-the packed forward, which takes them in device memory.
+The call takes the offsets in device memory, as the packed forward does, and runs the whole
+batch from the chunk plan in a fixed number of launches.  A batch of equal lengths must give
+the equal-length backward's gradients bit for bit (same per-chunk arithmetic, blocks found
+through the plan instead of by position), and a batch of many short sequences of mixed
+lengths is compared with the oracle sequence by sequence.
 """
 import numpy as np
 import pytest
@@ -121,3 +124,63 @@ def test_packed_backward_grouped_heads_and_prologue(dev, lengths, H, Hv, dk, dv,
         err = rel_l2(got_n, ref)
         print(f"  {n}: {err:.2e}", flush=True)
         assert err <= tol, n
+
+
+@pytest.mark.parametrize("N,T,io,flags", [
+    (3, 200, BF16, 0),
+    (2, 128, BF16, LOG | NEG | L2),
+    (3, 70, F32, 0),
+])
+def test_equal_lengths_equal_the_batched_backward_bitwise(dev, N, T, io, flags):
+    print(f"bwd varlen equal lengths N={N} T={T} {io} flags {flags}", flush=True)
+    H, dk, dv = 2, 64, 64
+    inp = inputs.make_packed([T] * N, H, dk, dv, io, 25, dev, s0_std=0.05, gate_logits=bool(flags & LOG),
+                             unit_qk=not flags & L2)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(26)
+    dO = torch.randn(1, N * T, H, dv, generator=gen, device=dev).to(io)
+    dS_T = torch.randn(N, H, dk, dv, generator=gen, device=dev)
+    got = g.chunk_bwd_varlen(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["b"], inp["w"], dO, inp["cu"],
+                             inp["S0"], dS_T, flags=flags)
+    bat = lambda x: x.reshape(N, T, *x.shape[2:])
+    ref = g.chunk_bwd(bat(inp["q"]), bat(inp["k"]), bat(inp["v"]), bat(inp["alpha"]), bat(inp["b"]),
+                      bat(inp["w"]), bat(dO), inp["S0"], dS_T, flags=flags)
+    torch.cuda.synchronize()
+    for n in NAMES:
+        a, b = got[n], ref[n]
+        assert torch.equal(a.reshape(b.shape), b), n
+
+
+def test_many_short_sequences(dev):
+    rng = np.random.default_rng(41)
+    lengths = [int(x) for x in rng.integers(0, 90, size=150)]
+    lengths[:4] = [0, 1, 64, 65]
+    H, dk, dv = 2, 64, 64
+    N, T = len(lengths), sum(lengths)
+    print(f"bwd varlen {N} sequences, {T} tokens", flush=True)
+    inp = inputs.make_packed(lengths, H, dk, dv, BF16, 35, dev, s0_std=0.05)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(36)
+    dO = torch.randn(1, T, H, dv, generator=gen, device=dev).to(BF16)
+    dS_T = torch.randn(N, H, dk, dv, generator=gen, device=dev)
+    got = g.chunk_bwd_varlen(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["b"], inp["w"], dO, inp["cu"],
+                             inp["S0"], dS_T)
+    torch.cuda.synchronize()
+    h = {n: _np(inp[n]) for n in ("q", "k", "v", "alpha", "b", "w", "S0")}
+    dOn, dSn = _np(dO), _np(dS_T)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    worst = {n: 0.0 for n in NAMES}
+    gotn = {n: _np(got[n]) for n in NAMES}
+    for i in range(N):
+        a, e = int(cu[i]), int(cu[i + 1])
+        sl = lambda x: x[:, a:e]
+        r = recurrent_bwd(sl(h["q"]), sl(h["k"]), sl(h["v"]), sl(h["alpha"]), sl(h["b"]), sl(h["w"]),
+                          h["S0"][i:i + 1], sl(dOn), dSn[i:i + 1])
+        for n in NAMES:
+            mine = gotn[n][i:i + 1] if n == "dS0" else gotn[n][:, a:e]
+            if mine.size == 0:
+                continue
+            worst[n] = max(worst[n], rel_l2(mine, r[n].reshape(mine.shape)))
+    print("  worst per sequence: " + ", ".join(f"{n} {v:.2e}" for n, v in worst.items()), flush=True)
+    for n, v in worst.items():
+        assert v <= 2e-2, n
