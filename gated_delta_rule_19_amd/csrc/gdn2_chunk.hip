@@ -242,10 +242,10 @@ void k_chunk_prep(PrepArgs a)
     // and replaced by identity tokens afterwards): a load under a branch would
     // be waited for at the join.  16-byte accesses keep the count of loads per
     // lane under the 63 the counter can track.
-    // Key-axis item = (4 channels c0..c0+3, 8-token group rg); block p = rg/2.
+    // Key-axis item = (4 channels c0..c0+3, 8-token group rg).
     constexpr int NQ = DK / 4;
     const bool kact = tid < 2 * DK;
-    const int cq = tid % NQ, rg = (tid / NQ) & 7, p = rg >> 1, half = rg & 1, c0 = 4 * cq;
+    const int cq = tid % NQ, rg = (tid / NQ) & 7, c0 = 4 * cq;
     typedef typename GateVec<Tg>::type gvec;
     const Tg* galpha = static_cast<const Tg*>(a.alpha);
     const Tg* gb = static_cast<const Tg*>(a.b);

@@ -494,6 +494,9 @@ PIECES = [
     (300 * 64, 1, 2, 128, 128, torch.bfloat16, torch.bfloat16,
      g.FLAG_GATE_LOGITS | g.FLAG_NEG_EIGVAL | g.FLAG_QK_L2NORM, None),
     (1024 * 64 + 1, 2, 2, 128, 128, torch.bfloat16, torch.float32, 0, 0.05),
+    (256 * 64 + 9, 1, 1, 128, 256, torch.bfloat16, torch.float32, 0, 0.05),
+    (384 * 64 + 63, 3, 3, 64, 128, torch.bfloat16, torch.float32, 0, 0.05),
+    (256 * 64 + 17, 2, 2, 64, 64, torch.bfloat16, torch.float32, 0, 0.05),
 ]
 
 
