@@ -153,7 +153,17 @@ size_t gdn2_chunk_prep_workspace_size(const gdn2_problem* p);
  *
  * Runs as two launches on `stream`: gdn2_chunk_prep followed by
  * gdn2_chunk_state (declared below), which callers may also issue
- * themselves, e.g. to time them apart.
+ * themselves, e.g. to time them apart.  One case differs: a single long
+ * sequence whose state pass would leave most of the GPU idle (B == 1, at
+ * least 256 chunks, few value heads) with S_out != NULL, on a stream that is
+ * not being captured, runs in up to 8 pieces of whole chunks, the prep of
+ * each later piece on a second stream the library keeps per device (default
+ * priority), ordered by events.  The call's work is still ordered on
+ * `stream` as a whole (it starts after what `stream` already holds and
+ * whatever is enqueued on `stream` afterwards sees o and S_out), results
+ * are bit-identical to the two launches, and concurrent calls on one device
+ * serialise their enqueueing.  Under stream capture the two launches are
+ * always used.
  */
 int gdn2_chunk_fwd(const gdn2_problem* p,
                    const void* q, const void* k, const void* v,
