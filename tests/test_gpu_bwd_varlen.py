@@ -184,3 +184,28 @@ def test_many_short_sequences(dev):
     print("  worst per sequence: " + ", ".join(f"{n} {v:.2e}" for n, v in worst.items()), flush=True)
     for n, v in worst.items():
         assert v <= 2e-2, n
+
+
+@pytest.mark.parametrize("io", [BF16, F32])
+def test_offsets_are_clamped_as_in_the_forward(dev, io):
+    """Offsets that break the rules (negative, decreasing, past T) go through the forward's
+    chunk plan, which clamps them into [0, T] and raises each to the running maximum: the
+    gradients equal those for the clamped offsets, bit for bit."""
+    lens = [50, 30, 120]
+    H, dk, dv = 2, 64, 64
+    T = sum(lens)
+    print(f"bwd varlen clamped offsets {io}", flush=True)
+    inp = inputs.make_packed(lens, H, dk, dv, io, 45, dev, s0_std=0.05)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(46)
+    dO = torch.randn(1, T, H, dv, generator=gen, device=dev).to(io)
+    dS_T = torch.randn(len(lens), H, dk, dv, generator=gen, device=dev)
+    raw = torch.tensor([-5, 40, 20, T + 90], dtype=torch.int32, device=dev)
+    clamped = torch.tensor([0, 40, 40, T], dtype=torch.int32, device=dev)
+    x = (inp["q"], inp["k"], inp["v"], inp["alpha"], inp["b"], inp["w"], dO)
+    a = g.chunk_bwd_varlen(*x, raw, inp["S0"], dS_T)
+    b = g.chunk_bwd_varlen(*x, clamped, inp["S0"], dS_T)
+    torch.cuda.synchronize()
+    for n in NAMES:
+        assert torch.equal(a[n], b[n]), n
+    assert all(torch.isfinite(a[n].float()).all() for n in NAMES)
