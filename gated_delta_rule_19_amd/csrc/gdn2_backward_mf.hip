@@ -645,14 +645,6 @@ __device__ __attribute__((always_inline)) inline void grad_val_chunk(const GradV
 // sum of dG.  Every phase issues its global loads before using any of them.
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ bfrag scale8(bfrag x, float f)
-{
-    bfrag r;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = (bf)((float)x[e] * f);
-    return r;
-}
-
 constexpr int kGkThreads = 512;                    // 8 waves per key-side workgroup
 
 template <int DK>
@@ -829,25 +821,37 @@ __device__ __attribute__((always_inline)) inline void grad_key_chunk(const GradK
             for (int qd = 0; qd < 4; ++qd) acc[m][I][qd] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (ct >= NCT) continue;
             const float gI = G[16 * I * DK + c];
+            // One product per pair of 16-token blocks: the A operand keeps only
+            // the lanes whose 8 tokens lie in the other block (a K-block holds
+            // two), and the block pair's decay factor F (per column) scales the
+            // fp32 sum.  Every pair term dA[r][s] KY_s EA_r then enters the row
+            // sums and the column sums with the same bf16 factors, which lets
+            // them cancel in dlog(alpha) (below) down to fp32 rounding.
             // row side: s over blocks 0..I (dA, dP are zero for s >= r)
 #pragma unroll
-            for (int kb = 0; kb < (I + 2) / 2; ++kb) {
-                const int s0 = kb * 32 + grp * 8, J = s0 >> 4;
+            for (int J = 0; J <= I; ++J) {
+                const int kb = J >> 1;
+                const bool mine = (grp >> 1) == (J & 1);
+                const bfrag bk = fr(KYTl, c, LT, kb, grp);
+                f32x4 ta = {0.f, 0.f, 0.f, 0.f}, tp = ta;
+                ta = IOB::mma(ta, keep_or_zero(fr(dAl, 16 * I + l16, LT, kb, grp), mine), bk);
+                tp = IOB::mma(tp, keep_or_zero(fr(dPl, 16 * I + l16, LT, kb, grp), mine), bk);
                 const float f = J < I ? __expf(gI - G[16 * J * DK + c]) : 1.f;
-                const bfrag bk = scale8(fr(KYTl, c, LT, kb, grp), f);
-                acc[m][I][0] = IOB::mma(acc[m][I][0], fr(dAl, 16 * I + l16, LT, kb, grp), bk);
-                acc[m][I][1] = IOB::mma(acc[m][I][1], fr(dPl, 16 * I + l16, LT, kb, grp), bk);
+                acc[m][I][0] += f * ta;
+                acc[m][I][1] += f * tp;
             }
             // column side: r over blocks I..3 (dA[r][s] is zero for r <= s)
 #pragma unroll
-            for (int kb = I / 2; kb < 2; ++kb) {
-                const int r0 = kb * 32 + grp * 8, Ir = r0 >> 4;
-                const float f = Ir > I ? __expf(G[16 * Ir * DK + c] - gI) : 1.f;
+            for (int Ir = I; Ir < 4; ++Ir) {
+                const int kb = Ir >> 1;
+                const bool mine = (grp >> 1) == (Ir & 1);
                 const int s = 16 * I + l16;
-                const bfrag be = scale8(fr(EATl, c, LT, kb, grp), f);
-                const bfrag bq = scale8(fr(QATl, c, LT, kb, grp), f);
-                acc[m][I][2] = IOB::mma(acc[m][I][2], fr(dATl, s, LT, kb, grp), be);
-                acc[m][I][3] = IOB::mma(acc[m][I][3], fr(dPTl, s, LT, kb, grp), bq);
+                f32x4 ta = {0.f, 0.f, 0.f, 0.f}, tp = ta;
+                ta = IOB::mma(ta, keep_or_zero(fr(dATl, s, LT, kb, grp), mine), fr(EATl, c, LT, kb, grp));
+                tp = IOB::mma(tp, keep_or_zero(fr(dPTl, s, LT, kb, grp), mine), fr(QATl, c, LT, kb, grp));
+                const float f = Ir > I ? __expf(G[16 * Ir * DK + c] - gI) : 1.f;
+                acc[m][I][2] += f * ta;
+                acc[m][I][3] += f * tp;
             }
         }
     }
@@ -859,15 +863,13 @@ __device__ __attribute__((always_inline)) inline void grad_key_chunk(const GradK
         const int c = 16 * ct + l16;
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
-            const float gI = G[16 * I * DK + c];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
+                // the sums before their row factors (the per-row pass applies them)
                 const int r = 16 * I + 4 * grp + i;
-                const float d = G[r * DK + c] - gI;            // <= 0
-                const float xr = __expf(d), y = __expf(-d);
-                deAl[r * RS + c] = acc[m][I][0][i] * xr;
-                dqPl[r * RS + c] = acc[m][I][1][i] * xr;
-                kakl[r * RS + c] = (acc[m][I][2][i] + acc[m][I][3][i]) * y;
+                deAl[r * RS + c] = acc[m][I][0][i];
+                dqPl[r * RS + c] = acc[m][I][1][i];
+                kakl[r * RS + c] = acc[m][I][2][i] + acc[m][I][3][i];
             }
         }
     }
@@ -894,21 +896,28 @@ __device__ __attribute__((always_inline)) inline void grad_key_chunk(const GradK
                 q4 = q4 * nq;
                 k4 = k4 * nk;
             }
-            const f32x4 deA = *reinterpret_cast<const f32x4*>(&deAl[r * RS + c0]);
-            const f32x4 dqP = *reinterpret_cast<const f32x4*>(&dqPl[r * RS + c0]);
-            const f32x4 kak = *reinterpret_cast<const f32x4*>(&kakl[r * RS + c0]);
+            const f32x4 sA = *reinterpret_cast<const f32x4*>(&deAl[r * RS + c0]);
+            const f32x4 sP = *reinterpret_cast<const f32x4*>(&dqPl[r * RS + c0]);
+            const f32x4 sC = *reinterpret_cast<const f32x4*>(&kakl[r * RS + c0]);
             f32x4 oq, okk, ob, dg;
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) {
                 const int c = c0 + cc;
                 const float g = G[r * DK + c], gam = __expf(g), kt = __expf(G[63 * DK + c] - g);
+                const float gI = G[(r & ~15) * DK + c];
+                const float xr = __expf(g - gI), y = __expf(gI - g);   // as phase A forms EA, QA, KY
                 const float qv = ok ? q4[cc] : 0.f, kv = ok ? k4[cc] : 0.f, bv = ok ? b4[cc] : 0.f, ev = bv * kv;
-                const float de = gam * dEh[cc] + deA[cc];
-                oq[cc] = gam * dQh[cc] + dqP[cc];
-                okk[cc] = kt * dKt[cc] + de * bv + kak[cc];
+                const float deA = sA[cc] * xr, dqP = sP[cc] * xr, kak = sC[cc] * y;
+                const float de = gam * dEh[cc] + deA;
+                oq[cc] = gam * dQh[cc] + dqP;
+                okk[cc] = kt * dKt[cc] + de * bv + kak;
                 ob[cc] = de * kv;
-                dg[cc] = dQh[cc] * gam * qv + dEh[cc] * gam * ev - dKt[cc] * kv * kt + ev * deA[cc] +
-                         qv * dqP[cc] - kv * kak[cc];
+                // the pair terms of A and P with the bf16 EA, QA, KY the products
+                // used, so that the pairs of dG inside [t, 64) cancel in the
+                // reverse sum below
+                const float eab = (float)(bf)(ev * xr), qab = (float)(bf)(qv * xr), kyb = (float)(bf)(kv * y);
+                dg[cc] = dQh[cc] * gam * qv + dEh[cc] * gam * ev - dKt[cc] * kv * kt + sA[cc] * eab +
+                         sP[cc] * qab - sC[cc] * kyb;
                 ex[cc] += dKt[cc] * kv * kt;
             }
             *reinterpret_cast<f32x4*>(&dG[r * RS + c0]) = dg;

@@ -11,9 +11,7 @@ oracle on the same inputs (q/k shared by the value heads of a group as
 <= 2e-2 with bf16, whole tensor and worst (batch, head) chain.
 Decay levels stay inside each call's documented domain (include/gdn2.h): the
 forward down to alpha ~ sigma(N(-6, 1)) (4-token products), the backward
-down to sigma(N(-2, 1)) (16-token products), and with bf16 I/O the backward
-at the workloads' level sigma(N(3, 1)): with faster decay its dalpha error
-grows like 1/alpha (tests/test_gpu_backward.py, DALPHA_FAST).
+down to sigma(N(-2, 1)) (16-token products).
 """
 import numpy as np
 import pytest
@@ -48,8 +46,7 @@ def case(i, small=False):
         gate=BF16 if io == BF16 and r.random() < 0.4 else F32,
         flags=flags,
         s0=0.05 if r.random() < 0.5 else None,
-        alpha_mu=float(r.choice([3.0, 3.0, 0.0, -2.0, -6.0] if not small else
-                                ([3.0] if io == BF16 else [3.0, 0.0, -2.0]))),
+        alpha_mu=float(r.choice([3.0, 3.0, 0.0, -2.0, -6.0] if not small else [3.0, 0.0, -2.0])),
         b_scale=2.0 if (flags & LOG) == 0 and r.random() < 0.3 else 1.0,
         seed=int(r.integers(1, 1 << 30)),
     )
