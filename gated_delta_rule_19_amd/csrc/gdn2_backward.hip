@@ -28,11 +28,11 @@
 //               dalpha from the reverse cumulative sum of the latter.
 //
 // Decay ratios Gamma_r / Gamma_s (s <= r) inside A, P and their gradients
-// are split at the first token j0 of s's 16-token block:
-// exp(G_r - G_s) = exp(G_r - G_j0) * exp(G_j0 - G_s), the first factor <= 1
-// on the row side, the second >= 1 but bounded by the decay domain of the
-// chunked mode (products of alpha over 16 tokens above ~1e-30) on the
-// column side, so every one of them is a plain product per column block.
+// are split at the reference token m = 8h + 3 of s's 8-token half h, as in
+// the forward: exp(G_r - G_s) = exp(G_r - G_m) * exp(G_m - G_s), each factor
+// a product of decays or, within one half, the inverse of a product of at
+// most 4 (bounded by the chunked mode's decay domain), so every one of them
+// is a plain product per column half.
 //
 // This first version computes with fp32 vector FMAs: a generic product on
 // 256 threads stages K-slices of both operands in LDS and keeps 4x4 output
@@ -424,7 +424,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_grad(GradArgs a)
             Qh[i] = gam * qv;
             Eh[i] = gam * bv * kv;
             Kt[i] = kv * __expf(G[63 * dk + c] - g);
-            KY[i] = kv * __expf(G[(r & ~15) * dk + c] - g);
+            KY[i] = kv * __expf(G[((r & ~7) | 3) * dk + c] - g);   // referred to the half's token 3
             deA[i] = dqP[i] = dkA[i] = dkP[i] = 0.f;
         }
         for (int i = tid; i < VA; i += kThreads) {
@@ -437,15 +437,16 @@ __global__ __launch_bounds__(kThreads) void k_chunk_grad(GradArgs a)
         for (int i = tid; i < QA; i += kThreads) A[i] = P[i] = Tm[i] = 0.f;
         __syncthreads();
 
-        // ---- A (s < r) and P (s <= r), one 16-column block at a time
-        for (int J = 0; J < 4; ++J) {
-            const int j0 = 16 * J;
-            gemm<true, false>(gl, 64 - j0, 16, dk,
-                 [&](int m, int c) { return ef[(j0 + m) * dk + c] * __expf(G[(j0 + m) * dk + c] - G[j0 * dk + c]); },
+        // ---- A (s < r) and P (s <= r), one 8-column half at a time (rows from
+        // the half's first token on; reference token j0 + 3)
+        for (int J = 0; J < 8; ++J) {
+            const int j0 = 8 * J, jm = j0 + 3;
+            gemm<true, false>(gl, 64 - j0, 8, dk,
+                 [&](int m, int c) { return ef[(j0 + m) * dk + c] * __expf(G[(j0 + m) * dk + c] - G[jm * dk + c]); },
                  [&](int c, int s) { return KY[(j0 + s) * dk + c]; },
                  [&](int m, int s, float x) { if (s < m) A[(j0 + m) * 64 + j0 + s] = x; });
-            gemm<true, false>(gl, 64 - j0, 16, dk,
-                 [&](int m, int c) { return qf[(j0 + m) * dk + c] * __expf(G[(j0 + m) * dk + c] - G[j0 * dk + c]); },
+            gemm<true, false>(gl, 64 - j0, 8, dk,
+                 [&](int m, int c) { return qf[(j0 + m) * dk + c] * __expf(G[(j0 + m) * dk + c] - G[jm * dk + c]); },
                  [&](int c, int s) { return KY[(j0 + s) * dk + c]; },
                  [&](int m, int s, float x) { if (s <= m) P[(j0 + m) * 64 + j0 + s] = x; });
         }
@@ -536,39 +537,39 @@ __global__ __launch_bounds__(kThreads) void k_chunk_grad(GradArgs a)
         gemm<true, false>(gl, 64, 64, 64, [&](int m, int j) { return tmp[m * 64 + j]; }, [&](int j, int s) { return Tm[s * 64 + j]; },
              [&](int m, int s, float x) { dA[m * 64 + s] = s < m ? -x : 0.f; });
 
-        // ---- through A and P: row side (rows r >= j0 of column block J) and
-        // column side (columns s of block J)
-        for (int J = 0; J < 4; ++J) {
-            const int j0 = 16 * J;
-            gemm<true, true>(gl, 64 - j0, dk, 16, [&](int m, int s) { return dA[(j0 + m) * 64 + j0 + s]; },
+        // ---- through A and P: row side (rows r >= j0 of column half J) and
+        // column side (columns s of half J), reference token j0 + 3
+        for (int J = 0; J < 8; ++J) {
+            const int j0 = 8 * J, jm = j0 + 3;
+            gemm<true, true>(gl, 64 - j0, dk, 8, [&](int m, int s) { return dA[(j0 + m) * 64 + j0 + s]; },
                  [&](int s, int c) { return KY[(j0 + s) * dk + c]; },
                  [&](int m, int c, float x) {
                      const int r = j0 + m;
-                     deA[r * dk + c] += x * __expf(G[r * dk + c] - G[j0 * dk + c]);
+                     deA[r * dk + c] += x * __expf(G[r * dk + c] - G[jm * dk + c]);
                  });
-            gemm<true, true>(gl, 64 - j0, dk, 16, [&](int m, int s) { return dP[(j0 + m) * 64 + j0 + s]; },
+            gemm<true, true>(gl, 64 - j0, dk, 8, [&](int m, int s) { return dP[(j0 + m) * 64 + j0 + s]; },
                  [&](int s, int c) { return KY[(j0 + s) * dk + c]; },
                  [&](int m, int c, float x) {
                      const int r = j0 + m;
-                     dqP[r * dk + c] += x * __expf(G[r * dk + c] - G[j0 * dk + c]);
+                     dqP[r * dk + c] += x * __expf(G[r * dk + c] - G[jm * dk + c]);
                  });
-            gemm<false, true>(gl, 16, dk, 64 - j0, [&](int m, int rr) { return dA[(j0 + rr) * 64 + j0 + m]; },
+            gemm<false, true>(gl, 8, dk, 64 - j0, [&](int m, int rr) { return dA[(j0 + rr) * 64 + j0 + m]; },
                  [&](int rr, int c) {
                      const int r = j0 + rr;
-                     return ef[r * dk + c] * __expf(G[r * dk + c] - G[j0 * dk + c]);
+                     return ef[r * dk + c] * __expf(G[r * dk + c] - G[jm * dk + c]);
                  },
                  [&](int m, int c, float x) {
                      const int s = j0 + m;
-                     dkA[s * dk + c] += x * __expf(G[j0 * dk + c] - G[s * dk + c]);
+                     dkA[s * dk + c] += x * __expf(G[jm * dk + c] - G[s * dk + c]);
                  });
-            gemm<false, true>(gl, 16, dk, 64 - j0, [&](int m, int rr) { return dP[(j0 + rr) * 64 + j0 + m]; },
+            gemm<false, true>(gl, 8, dk, 64 - j0, [&](int m, int rr) { return dP[(j0 + rr) * 64 + j0 + m]; },
                  [&](int rr, int c) {
                      const int r = j0 + rr;
-                     return qf[r * dk + c] * __expf(G[r * dk + c] - G[j0 * dk + c]);
+                     return qf[r * dk + c] * __expf(G[r * dk + c] - G[jm * dk + c]);
                  },
                  [&](int m, int c, float x) {
                      const int s = j0 + m;
-                     dkP[s * dk + c] += x * __expf(G[j0 * dk + c] - G[s * dk + c]);
+                     dkP[s * dk + c] += x * __expf(G[jm * dk + c] - G[s * dk + c]);
                  });
         }
 

@@ -626,16 +626,18 @@ __device__ __attribute__((always_inline)) inline void grad_val_chunk(const GradV
 
 // ---------------------------------------------------------------------------
 // key side: one workgroup per chunk.  The contractions of dA and dP with the
-// decay ratios run on bf16 matrix cores, split at the chunk's 16-token blocks
-// as in the forward: for rows r in block I and columns s in block J,
-//   exp(G_r - G_s) = exp(G_r - G_16I) * exp(G_16I - G_16J) * exp(G_16J - G_s),
-// every factor bounded (the last two inverse decays stay inside one block);
-// the middle one, per (I, J, channel), scales a whole B fragment.
-//   row side    deA[r,c] = exp(G_r - G_16I) sum_s dA[r,s] F_IJ[c] KY[s,c]
-//               (and dqP with dP),   KY[s,c] = k_s exp(G_16J - G_s)
-//   column side kak[s,c] = exp(G_16J - G_s) sum_r dA[r,s] F_IJ[c] EA[r,c]
-//               + the same with dP and QA,  EA = e_r exp(G_r - G_16I),
-//               QA = q_r exp(G_r - G_16I)
+// decay ratios run on bf16 matrix cores, split at the chunk's 8-token halves,
+// each referred to its token 3 (m_h = 8h + 3) as in the forward: for rows r
+// in half hr and columns s in half hs,
+//   exp(G_r - G_s) = exp(G_r - G_m(hr)) * exp(G_m(hr) - G_m(hs)) * exp(G_m(hs) - G_s),
+// the outer factors products of at most 4 decays or their inverses, the
+// middle one (<= 1 for hr >= hs) per (hr, hs, channel) scaling the fp32 sum of
+// that pair of halves.
+//   row side    deA[r,c] = exp(G_r - G_m(hr)) sum_hs F[c] sum_{s in hs} dA[r,s] KY[s,c]
+//               (and dqP with dP),   KY[s,c] = k_s exp(G_m(hs) - G_s)
+//   column side kak[s,c] = exp(G_m(hs) - G_s) sum_hr F[c] sum_{r in hr} dA[r,s] EA[r,c]
+//               + the same with dP and QA,  EA = e_r exp(G_r - G_m(hr)),
+//               QA = q_r exp(G_r - G_m(hr))
 // Every operand is stored in LDS with its contraction index contiguous:
 // dA and dP row-major and transposed, KY, EA and QA transposed ([channel]
 // [token]), written element by element from registers in phase A, so that
@@ -777,7 +779,7 @@ __device__ __attribute__((always_inline)) inline void grad_key_chunk(const GradK
             int r, c4;
             key_item<DK, NTH>(u, r, c4);
             const f32x4 g4 = *reinterpret_cast<const f32x4*>(&G[r * DK + c4]);
-            const f32x4 gj = *reinterpret_cast<const f32x4*>(&G[(r & ~15) * DK + c4]);
+            const f32x4 gj = *reinterpret_cast<const f32x4*>(&G[((r & ~7) | 3) * DK + c4]);   // half's midpoint
             const bool ok = r < Ln;
             f32x4 k4 = IOB::unpack4(kx[u]), q4 = IOB::unpack4(qx[u]);
             const f32x4 b4 = logits ? sigmoid4(widen4(bx[u])) * bscale : widen4(bx[u]);
@@ -788,7 +790,7 @@ __device__ __attribute__((always_inline)) inline void grad_key_chunk(const GradK
             f32x4 ky, ea, qa;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float up = __expf(g4[e] - gj[e]);        // <= 1
+                const float up = __expf(g4[e] - gj[e]);        // a product of at most 4 decays or its inverse
                 ky[e] = ok ? k4[e] * __expf(gj[e] - g4[e]) : 0.f;
                 ea[e] = ok ? b4[e] * k4[e] * up : 0.f;
                 qa[e] = ok ? q4[e] * up : 0.f;
@@ -820,36 +822,41 @@ __device__ __attribute__((always_inline)) inline void grad_key_chunk(const GradK
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) acc[m][I][qd] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (ct >= NCT) continue;
-            const float gI = G[16 * I * DK + c];
-            // One product per pair of 16-token blocks: the A operand keeps only
-            // the lanes whose 8 tokens lie in the other block (a K-block holds
-            // two), and the block pair's decay factor F (per column) scales the
-            // fp32 sum.  Every pair term dA[r][s] KY_s EA_r then enters the row
-            // sums and the column sums with the same bf16 factors, which lets
-            // them cancel in dlog(alpha) (below) down to fp32 rounding.
-            // row side: s over blocks 0..I (dA, dP are zero for s >= r)
+            // One product per pair of 8-token halves: the A operand keeps only
+            // the lanes whose 8 tokens form the other half (a K-block holds
+            // four), and the decay between the two halves' reference tokens
+            // (token 3 of each half; <= 1) scales the fp32 sum.  With KY, EA,
+            // QA referred to their own half's reference token, every factor
+            // stays within a product of 4 decays or its inverse, and every pair
+            // term dA[r][s] KY_s EA_r enters the row sums and the column sums
+            // with the same bf16 factors, which lets them cancel in dlog(alpha)
+            // (below) down to fp32 rounding.  A lane's accumulator rows
+            // 4 grp .. 4 grp + 3 lie in half 2 I + grp / 2 of the tile's rows.
+            const int hown = 2 * I + (grp >> 1);
+            const float gown = G[(8 * hown + 3) * DK + c];
+            // row side: source halves 0 .. 2I+1 (dA, dP are zero for s >= r)
 #pragma unroll
-            for (int J = 0; J <= I; ++J) {
-                const int kb = J >> 1;
-                const bool mine = (grp >> 1) == (J & 1);
+            for (int hs = 0; hs <= 2 * I + 1; ++hs) {
+                const int kb = hs >> 2;
+                const bool mine = grp == (hs & 3);
                 const bfrag bk = fr(KYTl, c, LT, kb, grp);
                 f32x4 ta = {0.f, 0.f, 0.f, 0.f}, tp = ta;
                 ta = IOB::mma(ta, keep_or_zero(fr(dAl, 16 * I + l16, LT, kb, grp), mine), bk);
                 tp = IOB::mma(tp, keep_or_zero(fr(dPl, 16 * I + l16, LT, kb, grp), mine), bk);
-                const float f = J < I ? __expf(gI - G[16 * J * DK + c]) : 1.f;
+                const float f = hs <= hown ? __expf(gown - G[(8 * hs + 3) * DK + c]) : 0.f;   // 0: above the diagonal
                 acc[m][I][0] += f * ta;
                 acc[m][I][1] += f * tp;
             }
-            // column side: r over blocks I..3 (dA[r][s] is zero for r <= s)
+            // column side: r over halves 2I .. 7 (dA[r][s] is zero for r <= s)
 #pragma unroll
-            for (int Ir = I; Ir < 4; ++Ir) {
-                const int kb = Ir >> 1;
-                const bool mine = (grp >> 1) == (Ir & 1);
+            for (int hr = 2 * I; hr < 8; ++hr) {
+                const int kb = hr >> 2;
+                const bool mine = grp == (hr & 3);
                 const int s = 16 * I + l16;
                 f32x4 ta = {0.f, 0.f, 0.f, 0.f}, tp = ta;
                 ta = IOB::mma(ta, keep_or_zero(fr(dATl, s, LT, kb, grp), mine), fr(EATl, c, LT, kb, grp));
                 tp = IOB::mma(tp, keep_or_zero(fr(dPTl, s, LT, kb, grp), mine), fr(QATl, c, LT, kb, grp));
-                const float f = Ir > I ? __expf(G[16 * Ir * DK + c] - gI) : 1.f;
+                const float f = hr >= hown ? __expf(G[(8 * hr + 3) * DK + c] - gown) : 0.f;
                 acc[m][I][2] += f * ta;
                 acc[m][I][3] += f * tp;
             }
@@ -904,7 +911,7 @@ __device__ __attribute__((always_inline)) inline void grad_key_chunk(const GradK
             for (int cc = 0; cc < 4; ++cc) {
                 const int c = c0 + cc;
                 const float g = G[r * DK + c], gam = __expf(g), kt = __expf(G[63 * DK + c] - g);
-                const float gI = G[(r & ~15) * DK + c];
+                const float gI = G[((r & ~7) | 3) * DK + c];            // the half's reference token
                 const float xr = __expf(g - gI), y = __expf(gI - g);   // as phase A forms EA, QA, KY
                 const float qv = ok ? q4[cc] : 0.f, kv = ok ? k4[cc] : 0.f, bv = ok ? b4[cc] : 0.f, ev = bv * kv;
                 const float deA = sA[cc] * xr, dqP = sP[cc] * xr, kak = sC[cc] * y;

@@ -63,9 +63,8 @@
  *   any 4 consecutive tokens of one key channel must stay above ~1e-30 (fp32
  *   range); every other decay factor it forms is a product of alphas (<= 1),
  *   so faster decay than that only underflows terms that are negligible.
- *   The chunked backward rescales by products inside 16-token blocks: there
- *   the product over any 16 consecutive tokens of a chunk must stay above
- *   ~1e-30.  The recurrent mode has no such limit.  b, w, q, k, v are any
+ *   The chunked backward splits its decay ratios the same way and has the
+ *   same domain.  The recurrent mode has no such limit.  b, w, q, k, v are any
  *   finite values (b in (0, 2) is the README's negative-eigenvalue option,
  *   "b x 2").
  * Alignment.  Every tensor pointer is 16-byte aligned (the kernels use

@@ -64,16 +64,20 @@ def ref(inp, dO, dS_T, chains=None):
     return {n: np.stack(v) for n, v in out.items()}
 
 
-def check(what, got, want, tol, chains=False):
+def check(what, got, want, tol, chains=False, tol_for=None):
     """rel-L2 per gradient tensor; with chains=True also the worst (batch, head) chain of each
-    ([B,T,H,*] tensors on axes 0, 2; dS0 [B,H,dk,dv] on axes 0, 1), held to the same bar."""
+    ([B,T,H,*] tensors on axes 0, 2; dS0 [B,H,dk,dv] on axes 0, 1), held to the same bar
+    (tol_for: a different bar for some gradients, by name)."""
+    tol_for = tol_for or {}
     errs = {n: rel_l2(got[n], want[n]) for n in NAMES}
     if chains:
         for n in NAMES:
             ax = (0, 1) if n == "dS0" else (0, 2)
             errs[n + "_worst_chain"] = float(np.max(rel_l2_chains(got[n], want[n], ax)))
-    print(f"[parity] {what}: " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()) + f" (tol {tol:g})", flush=True)
-    bad = {n: e for n, e in errs.items() if not e <= tol}
+    extra = "".join(f", {n} {t:g}" for n, t in tol_for.items())
+    print(f"[parity] {what}: " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()) + f" (tol {tol:g}{extra})",
+          flush=True)
+    bad = {n: e for n, e in errs.items() if not e <= tol_for.get(n.replace("_worst_chain", ""), tol)}
     assert not bad, f"{what}: {bad}"
 
 
@@ -170,6 +174,61 @@ def test_backward_decay_002_on_some_channels(dev):
     check("alpha 0.02 on some channels", {n: _np(got[n]) for n in NAMES}, want, 2e-2, chains=True)
 
 
+LOG, NEG, L2 = g.FLAG_GATE_LOGITS, g.FLAG_NEG_EIGVAL, g.FLAG_QK_L2NORM
+
+# Decay inside the forward's domain (4-token products above ~1e-30) but far past a
+# 16-token one: both backward paths refer their decay ratios to 8-token halves
+# (products of at most 4 decays or their inverses), as the forward does.
+DOMAIN_CASES = [
+    # B, T, H, Hv, dk, dv, io, gate dtype, flags, alpha_mu
+    (1, 200, 2, 2, 128, 128, BF16, F32, 0, -6.0),
+    (2, 150, 2, 2, 64, 64, BF16, BF16, LOG | NEG | L2, -6.0),
+    (1, 130, 1, 2, 32, 32, BF16, F32, LOG, -8.0),
+    (1, 170, 2, 2, 16, 48, F32, F32, 0, -6.0),            # vector-ALU path
+    (2, 90, 1, 2, 64, 32, F32, F32, LOG | L2, -8.0),
+    (1, 120, 2, 2, 32, 48, BF16, F32, 0, -6.0),           # bf16 on the vector-ALU path (dv 48)
+]
+
+
+@pytest.mark.parametrize("case", DOMAIN_CASES,
+                         ids=lambda c: f"B{c[0]}T{c[1]}H{c[2]}Hv{c[3]}dk{c[4]}dv{c[5]}"
+                         f"{'bf16' if c[6] == BF16 else 'f32'}fl{c[8]}mu{c[9]:g}")
+def test_backward_fast_decay_domain(dev, case):
+    """alpha = sigmoid(N(mu, 1)) with mu = -6 or -8: 16-token products far below 1e-30, 4-token
+    products above it; every gradient at the usual bar against full_bwd (prologue and grouped
+    heads included)."""
+    from oracle.backward import full_bwd
+    B, T, H, Hv, dk, dv, io, gt, flags, mu = case
+    inp = inputs.make_raw(B, T, H, dk, dv, io, 3 * T + dk, dev, s0_std=0.05, alpha_mu=mu, Hv=Hv,
+                          gate_dtype=gt, gate_logits=bool(flags & LOG), unit_qk=not flags & L2)
+    dO, dS_T = inputs.make_out_grads(B, T, Hv, dk, dv, io, 3 * T + dk + 1, dev)
+    got = g.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["b"], inp["w"], dO, inp["S0"], dS_T,
+                      flags=flags)
+    torch.cuda.synchronize()
+    h = {n: _np(x) for n, x in inp.items()}
+    want = full_bwd(h["q"], h["k"], h["v"], h["alpha"], h["b"], h["w"], h["S0"], _np(dO), _np(dS_T), flags=flags)
+    # fp32: the vector-ALU path takes its decay factors from fp32 cumulative log sums, whose
+    # absolute error grows with |G| (~64 |mu| here); dalpha, a reverse sum of nearly
+    # cancelling terms, then lands at 3-5e-4 (every other gradient stays near 1e-7)
+    tol_for = {"dalpha": 1e-3} if io == F32 and mu <= -6 else None
+    check(f"backward, mu {mu}", {n: _np(got[n]) for n in NAMES}, want, TOL[io], chains=True, tol_for=tol_for)
+
+
+@pytest.mark.parametrize("io,dk,dv", [(BF16, 128, 64), (F32, 64, 48)])
+def test_backward_alpha_1e3_on_some_channels(dev, io, dk, dv):
+    """alpha = 1e-3 on every third key channel (1e-3^16 = 1e-48 over 16 tokens)."""
+    from oracle import c_oracle
+    B, T, H = 1, 200, 2
+    inp = inputs.make_raw(B, T, H, dk, dv, io, 53, dev, s0_std=0.05, b_scale=2.0)
+    inp["alpha"][..., ::3] = 1e-3
+    dO, dS_T = inputs.make_out_grads(B, T, H, dk, dv, io, 54, dev)
+    got = g.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["b"], inp["w"], dO, inp["S0"], dS_T)
+    torch.cuda.synchronize()
+    h = {n: _np(x) for n, x in inp.items()}
+    want = c_oracle.recurrent_bwd(h["q"], h["k"], h["v"], h["alpha"], h["b"], h["w"], h["S0"], _np(dO), _np(dS_T))
+    check("alpha 1e-3 on some channels", {n: _np(got[n]) for n in NAMES}, want, TOL[io], chains=True)
+
+
 def test_backward_deterministic(dev):
     inp, dO, dS_T, g1 = run(dev, 1, 150, 2, 64, 64, BF16, F32, 0.05, True, seed=5)
     g2 = g.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["b"], inp["w"], dO, inp["S0"], dS_T)
@@ -179,7 +238,6 @@ def test_backward_deterministic(dev):
 
 
 # ---- prologue options and grouped value heads -------------------------------------
-LOG, NEG, L2 = g.FLAG_GATE_LOGITS, g.FLAG_NEG_EIGVAL, g.FLAG_QK_L2NORM
 
 FULL_CASES = [
     # B, T, H, Hv, dk, dv, io, gate dtype, flags, S0 std

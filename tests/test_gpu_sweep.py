@@ -9,9 +9,9 @@ oracle on the same inputs (q/k shared by the value heads of a group as
 ``oracle.reference.share_qk_heads`` states), and the chunked backward with
 ``oracle.backward.full_bwd``, at the usual bars: rel-L2 <= 1e-4 with fp32 I/O,
 <= 2e-2 with bf16, whole tensor and worst (batch, head) chain.
-Decay levels stay inside each call's documented domain (include/gdn2.h): the
-forward down to alpha ~ sigma(N(-6, 1)) (4-token products), the backward
-down to sigma(N(-2, 1)) (16-token products).
+Decay levels stay inside the chunked mode's documented domain (include/gdn2.h;
+products over 4 consecutive tokens above ~1e-30): down to alpha ~
+sigma(N(-6, 1)) in the forward and the backward alike.
 """
 import numpy as np
 import pytest
@@ -46,7 +46,7 @@ def case(i, small=False):
         gate=BF16 if io == BF16 and r.random() < 0.4 else F32,
         flags=flags,
         s0=0.05 if r.random() < 0.5 else None,
-        alpha_mu=float(r.choice([3.0, 3.0, 0.0, -2.0, -6.0] if not small else [3.0, 0.0, -2.0])),
+        alpha_mu=float(r.choice([3.0, 3.0, 0.0, -2.0, -6.0])),
         b_scale=2.0 if (flags & LOG) == 0 and r.random() < 0.3 else 1.0,
         seed=int(r.integers(1, 1 << 30)),
     )
@@ -114,4 +114,6 @@ def test_sweep_backward(dev, i):
     for n in NAMES:
         gn = _np(got[n])
         assert gn.shape == ref[n].shape, n
-        _check(n, gn, ref[n], tol, (0, 1) if n == "dS0" else (0, 2))
+        # fp32 dalpha under very fast decay: 1e-3 (tests/test_gpu_backward.py, fast-decay domain)
+        t = 1e-3 if n == "dalpha" and c["io"] == F32 and c["alpha_mu"] <= -6 else tol
+        _check(n, gn, ref[n], t, (0, 1) if n == "dS0" else (0, 2))
