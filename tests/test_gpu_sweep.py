@@ -117,3 +117,39 @@ def test_sweep_backward(dev, i):
         # fp32 dalpha under very fast decay: 1e-3 (tests/test_gpu_backward.py, fast-decay domain)
         t = 1e-3 if n == "dalpha" and c["io"] == F32 and c["alpha_mu"] <= -6 else tol
         _check(n, gn, ref[n], t, (0, 1) if n == "dS0" else (0, 2))
+
+
+def conv_case(i):
+    """Case i of the fused-convolution sweep (equal-length batches, K <= 4)."""
+    r = np.random.default_rng(9000 + i)
+    io = BF16 if r.random() < 0.6 else F32
+    H = int(r.integers(1, 3))
+    # q/k are convolved before the recurrence: without the L2 option their rows
+    # leave the unit sphere, so the weights stay small there
+    flags = int(r.choice([L2, LOG | L2, LOG | NEG | L2, 0, LOG]))
+    return dict(B=int(r.integers(1, 3)), T=int(r.integers(1, 260)), H=H, Hv=H * int(r.choice([1, 2])),
+                dk=int(r.choice([32, 64, 128])), dv=int(r.choice([32, 64, 128])), io=io,
+                gate=BF16 if io == BF16 and r.random() < 0.4 else F32, flags=flags,
+                K=int(r.integers(1, 5)), silu=bool(r.random() < 0.5),
+                wscale=0.5 if flags & L2 else 0.25, alpha_mu=float(r.choice([3.0, 0.0, -4.0])),
+                mode=str(r.choice(["chunk", "recurrent"])), seed=int(r.integers(1, 1 << 30)))
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_sweep_fused_conv(dev, i):
+    """Both forward modes with the short convolution fused in, against the oracle chain
+    short_conv -> split -> shared q/k heads -> recurrence (tests/test_gpu_conv_fused.py)."""
+    from test_gpu_conv_fused import check as conv_check, oracle_chain, run as conv_run
+    c = conv_case(i)
+    print(f"sweep fused conv {i}: {c}", flush=True)
+    inp = inputs.make_raw(c["B"], c["T"], c["H"], c["dk"], c["dv"], c["io"], c["seed"], dev, s0_std=0.05,
+                          alpha_mu=c["alpha_mu"], gate_logits=bool(c["flags"] & LOG), unit_qk=True,
+                          gate_dtype=c["gate"], Hv=c["Hv"])
+    C = 2 * c["H"] * c["dk"] + c["Hv"] * c["dv"]
+    gen = torch.Generator().manual_seed(c["seed"] + 7)
+    weight = (torch.randn(C, c["K"], generator=gen) * c["wscale"]).to(dev)
+    state = (torch.randn(c["B"], c["K"] - 1, C, generator=gen) * 0.5).to(c["io"]).to(dev) if c["K"] > 1 else None
+    o, S, win = conv_run(c["mode"], inp, weight, state, c["silu"], c["flags"])
+    torch.cuda.synchronize()
+    ro, rS, rwin = oracle_chain(inp, weight, state, c["silu"], c["flags"])
+    conv_check(f"sweep conv {i}", c["io"], o, S, win, ro, rS, rwin)
