@@ -27,6 +27,16 @@
 //               through the definitions of Qh, Eh, Ktil, A and P, and
 //               dalpha from the reverse cumulative sum of the latter.
 //
+// dlog(alpha_t) gathers every term that depends on alpha_t.  Each pair (r, s)
+// of A or P enters token r's row sum and token s's column sum, and the pairs
+// with r, s >= t cancel in the reverse sum.  P's diagonal pairs carry no
+// decay ratio and cancel inside their own token, so they are left out of
+// both sums (dq and dk take them apart): every pair that is left carries a
+// ratio Gamma_r / Gamma_s with s < r, of the size of what survives, and the
+// fp32 sums keep their relative accuracy at fast decay.  Likewise Ktil_s
+// depends on alpha_t for s < t, so its terms are summed forward from the
+// chunk's first token rather than taken from a total at its last.
+//
 // Decay ratios Gamma_r / Gamma_s (s <= r) inside A, P and their gradients
 // are split at the reference token m = 8h + 3 of s's 8-token half h, as in
 // the forward: exp(G_r - G_s) = exp(G_r - G_m) * exp(G_m - G_s), each factor
@@ -547,7 +557,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_grad(GradArgs a)
                      const int r = j0 + m;
                      deA[r * dk + c] += x * __expf(G[r * dk + c] - G[jm * dk + c]);
                  });
-            gemm<true, true>(gl, 64 - j0, dk, 8, [&](int m, int s) { return dP[(j0 + m) * 64 + j0 + s]; },
+            gemm<true, true>(gl, 64 - j0, dk, 8, [&](int m, int s) { return m == s ? 0.f : dP[(j0 + m) * 64 + j0 + s]; },
                  [&](int s, int c) { return KY[(j0 + s) * dk + c]; },
                  [&](int m, int c, float x) {
                      const int r = j0 + m;
@@ -562,7 +572,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_grad(GradArgs a)
                      const int s = j0 + m;
                      dkA[s * dk + c] += x * __expf(G[jm * dk + c] - G[s * dk + c]);
                  });
-            gemm<false, true>(gl, 8, dk, 64 - j0, [&](int m, int rr) { return dP[(j0 + rr) * 64 + j0 + m]; },
+            gemm<false, true>(gl, 8, dk, 64 - j0, [&](int m, int rr) { return m == rr ? 0.f : dP[(j0 + rr) * 64 + j0 + m]; },
                  [&](int rr, int c) {
                      const int r = j0 + rr;
                      return qf[r * dk + c] * __expf(G[r * dk + c] - G[jm * dk + c]);
@@ -573,36 +583,41 @@ __global__ __launch_bounds__(kThreads) void k_chunk_grad(GradArgs a)
                  });
         }
 
-        // ---- gradients of q, k, b and of G (dG kept in deA's place)
+        // ---- gradients of q, k, b and of G (dG kept in deA's place; P's
+        // diagonal, left out of dqP and dkP, added to dq and dk here)
         for (int i = tid; i < KA; i += kThreads) {
             const int r = i / dk, c = i - r * dk;
             const float g = G[i], gam = __expf(g);
             const float de = gam * dEh[i] + deA[i];
-            const float kv = kf[i];
+            const float kv = kf[i], pd = dP[r * 64 + r];
             const bool ok = r < L;
             const int64_t o = (row0 + r * H) * dk + c;
             const float bv = ok ? ldf(bg, o) : 0.f;
-            const float dG = dQh[i] * Qh[i] + dEh[i] * Eh[i] - dKt[i] * Kt[i] + ef[i] * deA[i] + qf[i] * dqP[i] -
+            const float dG = dQh[i] * Qh[i] + dEh[i] * Eh[i] + ef[i] * deA[i] + qf[i] * dqP[i] -
                              kv * (dkA[i] + dkP[i]);
             if (ok) {
-                stf(dq, o, gam * dQh[i] + dqP[i]);
-                stf(dk_out, o, __expf(G[63 * dk + c] - g) * dKt[i] + dkA[i] + dkP[i] + de * bv);
+                stf(dq, o, gam * dQh[i] + dqP[i] + pd * kv);
+                stf(dk_out, o, __expf(G[63 * dk + c] - g) * dKt[i] + dkA[i] + dkP[i] + pd * qf[i] + de * bv);
                 stf(db, o, de * kv);
             }
             deA[i] = dG;
         }
         __syncthreads();
-        // dG at the last token also carries Gamma_L's uses; dlog(alpha) is the
-        // reverse cumulative sum of dG
+        // dlog(alpha_t): the reverse sum of dG from t on, Gamma_L's uses, and
+        // the forward sum of Ktil's terms over the tokens before t
         for (int c = tid; c < dk; c += kThreads) {
-            float extra = dGamL[c] * __expf(G[63 * dk + c]);
-            for (int r = 0; r < 64; ++r) extra += dKt[r * dk + c] * Kt[r * dk + c];
-            float acc = extra;
+            float pre = 0.f;
+            for (int r = 0; r < 64; ++r) {
+                const float x = dKt[r * dk + c] * Kt[r * dk + c];
+                dKt[r * dk + c] = pre;
+                pre += x;
+            }
+            float acc = dGamL[c] * __expf(G[63 * dk + c]);
             for (int r = 63; r >= 0; --r) {
                 acc += deA[r * dk + c];
                 if (r < L) {
                     const int64_t o = (row0 + r * H) * dk + c;
-                    stf(dalpha, o, acc / ldf(alpha, o));
+                    stf(dalpha, o, (acc + dKt[r * dk + c]) / ldf(alpha, o));
                 }
             }
         }

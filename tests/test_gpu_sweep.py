@@ -114,9 +114,7 @@ def test_sweep_backward(dev, i):
     for n in NAMES:
         gn = _np(got[n])
         assert gn.shape == ref[n].shape, n
-        # fp32 dalpha under very fast decay: 1e-3 (tests/test_gpu_backward.py, fast-decay domain)
-        t = 1e-3 if n == "dalpha" and c["io"] == F32 and c["alpha_mu"] <= -6 else tol
-        _check(n, gn, ref[n], t, (0, 1) if n == "dS0" else (0, 2))
+        _check(n, gn, ref[n], tol, (0, 1) if n == "dS0" else (0, 2))
 
 
 def conv_case(i):
