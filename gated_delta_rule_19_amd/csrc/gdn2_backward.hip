@@ -416,7 +416,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_grad(GradArgs a)
         for (int c = tid; c < dk; c += kThreads) {
             float g = 0.f;
             for (int r = 0; r < 64; ++r) {
-                if (r < L) g += __logf(ldf(alpha, (row0 + r * H) * dk + c));
+                if (r < L) g += __logf(fmaxf(ldf(alpha, (row0 + r * H) * dk + c), kAlphaFloor));
                 G[r * dk + c] = g;
             }
         }
@@ -617,7 +617,10 @@ __global__ __launch_bounds__(kThreads) void k_chunk_grad(GradArgs a)
                 acc += deA[r * dk + c];
                 if (r < L) {
                     const int64_t o = (row0 + r * H) * dk + c;
-                    stf(dalpha, o, (acc + dKt[r * dk + c]) / ldf(alpha, o));
+                    {   // a decay below the floor was raised to it: its gradient is 0
+                        const float al = ldf(alpha, o);
+                        stf(dalpha, o, al < kAlphaFloor ? 0.f : (acc + dKt[r * dk + c]) / al);
+                    }
                 }
             }
         }

@@ -113,7 +113,7 @@ __device__ __attribute__((always_inline)) inline void cld_scan(float* G, float* 
     for (int u = 0; u < NV; ++u) {
         int r, c4;
         key_item<DK, NTH>(u, r, c4);
-        const f32x4 a = logits ? sigmoid4(widen4(x[u])) : widen4(x[u]);
+        const f32x4 a = alpha_floor4(logits ? sigmoid4(widen4(x[u])) : widen4(x[u]));
         f32x4 l;
 #pragma unroll
         for (int e = 0; e < 4; ++e) l[e] = r < Ln ? __logf(a[e]) : 0.f;   // alpha = 1 past the end
@@ -981,13 +981,15 @@ __device__ __attribute__((always_inline)) inline void grad_key_chunk(const GradK
                 const int64_t o = (row0 + r * H) * DK + c4;
                 const f32x4 a4 = widen4(ax[u]), g4 = *reinterpret_cast<const f32x4*>(&dG[r * RS + c4]);
                 f32x4 d4;
+                // a decay below the floor was raised to it: the forward does not
+                // depend on it there, and its gradient is 0
                 if (logits) {   // d logit = (dG / alpha) alpha (1 - alpha), alpha = sigmoid(logit)
                     const f32x4 s4 = sigmoid4(a4);
 #pragma unroll
-                    for (int cc = 0; cc < 4; ++cc) d4[cc] = g4[cc] * (1.f - s4[cc]);
+                    for (int cc = 0; cc < 4; ++cc) d4[cc] = s4[cc] < kAlphaFloor ? 0.f : g4[cc] * (1.f - s4[cc]);
                 } else {
 #pragma unroll
-                    for (int cc = 0; cc < 4; ++cc) d4[cc] = g4[cc] / a4[cc];
+                    for (int cc = 0; cc < 4; ++cc) d4[cc] = a4[cc] < kAlphaFloor ? 0.f : g4[cc] / a4[cc];
                 }
                 st_vec4(dalpha + o, d4);
             }

@@ -307,6 +307,7 @@ void k_chunk_prep(PrepArgs a)
             al[i] = sigmoid4(al[i]);
             bt[i] = sigmoid4(bt[i]) * bscale;
         }
+        al[i] = alpha_floor4(al[i]);
     }
     float sk[8], sq[8];
 #pragma unroll

@@ -151,6 +151,16 @@ __device__ inline f32x4 quad_transpose4(f32x4 v)
 // ---------------------------------------------------------------------------
 constexpr int kFlagGateLogits = 1, kFlagNegEigval = 2, kFlagQkL2norm = 4;
 constexpr float kL2normEps = 1e-6f;
+// Smallest decay the chunked mode uses: alpha below it (zero included) is
+// raised to it, so that a product of 4 consecutive decays stays >= 2^-80 and
+// its inverse stays finite in fp32 and bf16.  A raised alpha keeps at most a
+// 2^-20 share of the state it should have erased.
+constexpr float kAlphaFloor = 0x1p-20f;
+__device__ inline f32x4 alpha_floor4(f32x4 a)
+{
+    return f32x4{fmaxf(a[0], kAlphaFloor), fmaxf(a[1], kAlphaFloor), fmaxf(a[2], kAlphaFloor),
+                 fmaxf(a[3], kAlphaFloor)};
+}
 
 __device__ inline float gate_f(float x) { return x; }
 __device__ inline float gate_f(__bf16 x) { return (float)x; }

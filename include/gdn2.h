@@ -57,16 +57,19 @@
  *   state copy described below); Hv = 0 or a positive multiple of H; dk in
  *   {16, 32, 64, 128}; dv a multiple of 16 in [16, 256]; chunk == 64 for the
  *   chunked mode.
- * Domain.  alpha in (0, 1] (after the sigmoid with GATE_LOGITS).  The
+ * Domain.  alpha in [0, 1] (after the sigmoid with GATE_LOGITS).  The
  *   chunked forward rescales keys and queries by decay products of at most
- *   4 consecutive tokens (and their inverses), so the product of alpha over
- *   any 4 consecutive tokens of one key channel must stay above ~1e-30 (fp32
- *   range); every other decay factor it forms is a product of alphas (<= 1),
- *   so faster decay than that only underflows terms that are negligible.
- *   The chunked backward splits its decay ratios the same way and has the
- *   same domain.  The recurrent mode has no such limit.  b, w, q, k, v are any
- *   finite values (b in (0, 2) is the README's negative-eigenvalue option,
- *   "b x 2").
+ *   4 consecutive tokens (and their inverses), so it raises every alpha
+ *   below 2^-20 (zero included) to 2^-20: those products then stay >= 2^-80
+ *   and their inverses finite, and a raised decay keeps at most a 2^-20
+ *   share of the state it should have erased (a relative change far below
+ *   either parity bar); every other decay factor it forms is a product of
+ *   alphas (<= 1), so fast decay only underflows negligible terms.  The
+ *   chunked backward raises alpha the same way and returns the gradient of
+ *   that forward: where alpha < 2^-20 the forward does not depend on alpha,
+ *   and dalpha (d logit with GATE_LOGITS) is 0 there.
+ *   The recurrent mode uses alpha as given.  b, w, q, k, v are any finite
+ *   values (b in (0, 2) is the README's negative-eigenvalue option, "b x 2").
  * Alignment.  Every tensor pointer is 16-byte aligned (the kernels use
  *   16-byte vector accesses); the workspace is 256-byte aligned (a workspace
  *   that is not is GDN2_ERR_WORKSPACE).
