@@ -158,7 +158,7 @@ size_t gdn2_chunk_prep_workspace_size(const gdn2_problem* p);
  * themselves, e.g. to time them apart.  One case differs: a single long
  * sequence whose state pass would leave most of the GPU idle (B == 1, at
  * least 256 chunks, few value heads) with S_out != NULL, on a stream that is
- * not being captured, runs in up to 8 pieces of whole chunks, the prep of
+ * not being captured, runs in pieces of 32 chunks (at most 256), the prep of
  * each later piece on a second stream the library keeps per device (default
  * priority), ordered by events.  The call's work is still ordered on
  * `stream` as a whole (it starts after what `stream` already holds and
